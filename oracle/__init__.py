@@ -1,0 +1,270 @@
+"""CPU oracle for the block-scaled 4-bit (E2M1) linear-layer path.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, ``__graft_entry__.smoke()``
+and the CPU-baseline leg of ``bench.py`` may import this package.  The product
+path (the HIP library and its binding) never imports, links or calls it, and
+it shares no code with that path.
+
+The arithmetic lives in ``mxfp4_oracle.c`` (plain C, fp64, one obvious loop
+per definition); this module is a ctypes veneer that moves numpy arrays in and
+out.  Source passages for every definition are listed in ``mxfp4_oracle.h``.
+
+Tolerance rules for the GEMM (``gemm_fp32_ok`` / ``gemm_bf16_ok``) restate
+the parity bar fixed for this path: per element
+``|gpu - y| <= 1e-5 * sum_k |a_k b_k|`` for fp32 output, and at most one bf16
+ulp (ordered-bit distance, +0 == -0) from RNE_bf16(y) for bf16 output.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import pathlib
+import subprocess
+
+import numpy as np
+
+_DIR = pathlib.Path(__file__).resolve().parent
+_SRC = _DIR / "mxfp4_oracle.c"
+_LIB_PATH = _DIR / "_liboracle.so"
+_lib = None
+
+GEMM_FP32_RTOL = 1e-5
+
+
+def build() -> pathlib.Path:
+    """Compile the oracle with the host gcc (no GPU toolchain involved)."""
+    cmd = [
+        "gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-ffp-contract=off",
+        "-fno-fast-math", "-fopenmp", "-shared", "-fPIC", str(_SRC),
+        "-o", str(_LIB_PATH) + ".tmp", "-lm",
+    ]
+    subprocess.run(cmd, check=True)
+    os.replace(str(_LIB_PATH) + ".tmp", _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not _LIB_PATH.exists():
+        build()
+    lib = ctypes.CDLL(str(_LIB_PATH))
+    P = ctypes.c_void_p
+    I = ctypes.c_int64
+    lib.orc_e2m1_value.restype = ctypes.c_double
+    lib.orc_e2m1_value.argtypes = [ctypes.c_uint]
+    lib.orc_e4m3_value.restype = ctypes.c_double
+    lib.orc_e4m3_value.argtypes = [ctypes.c_uint]
+    lib.orc_e8m0_value.restype = ctypes.c_double
+    lib.orc_e8m0_value.argtypes = [ctypes.c_uint]
+    lib.orc_bf16_value.restype = ctypes.c_double
+    lib.orc_bf16_value.argtypes = [ctypes.c_uint16]
+    lib.orc_bf16_from_double.restype = ctypes.c_uint16
+    lib.orc_bf16_from_double.argtypes = [ctypes.c_double]
+    lib.orc_e2m1_encode.restype = ctypes.c_uint
+    lib.orc_e2m1_encode.argtypes = [ctypes.c_double]
+    lib.orc_shared_exponent.restype = ctypes.c_uint
+    lib.orc_shared_exponent.argtypes = [ctypes.c_double]
+    lib.orc_mx_quantize_block.restype = None
+    lib.orc_mx_quantize_block.argtypes = [P, P, P]
+    lib.orc_nvfp4_dequant.restype = None
+    lib.orc_nvfp4_dequant.argtypes = [P, P, ctypes.c_float, I, I, ctypes.c_int, P]
+    lib.orc_requant.restype = None
+    lib.orc_requant.argtypes = [P, P, P, I, I, I, ctypes.c_int, P, P]
+    lib.orc_quantize_act.restype = None
+    lib.orc_quantize_act.argtypes = [P, I, P, I, I, P, P]
+    lib.orc_gemm.restype = None
+    lib.orc_gemm.argtypes = [P, P, P, P, I, I, I, P, P]
+    lib.orc_gemm_at.restype = None
+    lib.orc_gemm_at.argtypes = [P, P, P, P, I, I, I, P, P, I, P, P]
+    lib.orc_grouped_gemm.restype = None
+    lib.orc_grouped_gemm.argtypes = [P, P, P, P, P, I, I, I, P, P]
+    lib.orc_bf16_from_double_array.restype = None
+    lib.orc_bf16_from_double_array.argtypes = [P, I, P]
+    lib.orc_num_threads.restype = ctypes.c_int
+    lib.orc_num_threads.argtypes = []
+    _lib = lib
+    return lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def num_threads() -> int:
+    return int(_load().orc_num_threads())
+
+
+# ---- scalar codecs (for the pins) ----------------------------------------
+def e2m1_value(code: int) -> float:
+    return float(_load().orc_e2m1_value(int(code)))
+
+
+def e4m3_value(byte: int) -> float:
+    return float(_load().orc_e4m3_value(int(byte)))
+
+
+def e8m0_value(byte: int) -> float:
+    return float(_load().orc_e8m0_value(int(byte)))
+
+
+def bf16_value(bits: int) -> float:
+    return float(_load().orc_bf16_value(int(bits)))
+
+
+def bf16_from_double(v: float) -> int:
+    return int(_load().orc_bf16_from_double(float(v)))
+
+
+def bf16_from_double_array(v) -> np.ndarray:
+    v = _c(v, np.float64)
+    out = np.empty(v.shape, dtype=np.uint16)
+    _load().orc_bf16_from_double_array(_ptr(v), v.size, _ptr(out))
+    return out
+
+
+def e2m1_encode(q: float) -> int:
+    return int(_load().orc_e2m1_encode(float(q)))
+
+
+def shared_exponent(amax: float) -> int:
+    return int(_load().orc_shared_exponent(float(amax)))
+
+
+def mx_quantize_block(v) -> tuple[np.ndarray, int]:
+    v = _c(v, np.float64)
+    assert v.shape == (32,)
+    codes = np.empty(16, dtype=np.uint8)
+    scale = np.empty(1, dtype=np.uint8)
+    _load().orc_mx_quantize_block(_ptr(v), _ptr(codes), _ptr(scale))
+    return codes, int(scale[0])
+
+
+# ---- the operations of the path -------------------------------------------
+def nvfp4_dequant(codes, scales, g, bf16_intermediate=False) -> np.ndarray:
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.uint8)
+    N, K = codes.shape[0], codes.shape[1] * 2
+    assert scales.shape == (N, K // 16)
+    out = np.empty((N, K), dtype=np.float32)
+    _load().orc_nvfp4_dequant(_ptr(codes), _ptr(scales), float(np.float32(g)), N, K,
+                              int(bool(bf16_intermediate)), _ptr(out))
+    return out
+
+
+def requant(nv_codes, nv_scales, nv_global, bf16_intermediate=False):
+    """NVFP4 [T,N,K/2] + [T,N,K/16] + g[T] -> MXFP4 codes [T,N,K/2], E8M0 [T,N,K/32]."""
+    nv_codes = _c(nv_codes, np.uint8)
+    nv_scales = _c(nv_scales, np.uint8)
+    squeeze = nv_codes.ndim == 2
+    if squeeze:
+        nv_codes = nv_codes[None]
+        nv_scales = nv_scales[None]
+    g = _c(np.atleast_1d(nv_global), np.float32)
+    T, N, Kh = nv_codes.shape
+    K = 2 * Kh
+    assert K % 32 == 0 and nv_scales.shape == (T, N, K // 16) and g.shape == (T,)
+    codes = np.empty((T, N, K // 2), dtype=np.uint8)
+    scales = np.empty((T, N, K // 32), dtype=np.uint8)
+    _load().orc_requant(_ptr(nv_codes), _ptr(nv_scales), _ptr(g), T, N, K,
+                        int(bool(bf16_intermediate)), _ptr(codes), _ptr(scales))
+    if squeeze:
+        return codes[0], scales[0]
+    return codes, scales
+
+
+def quantize_act(x_bits, K=None, row_index=None):
+    """bf16 bit patterns (uint16) [R, ldx] -> codes [M, K/2], E8M0 [M, K/32]."""
+    x_bits = _c(x_bits, np.uint16)
+    R, ldx = x_bits.shape
+    K = ldx if K is None else int(K)
+    assert K % 32 == 0 and K <= ldx
+    if row_index is not None:
+        row_index = _c(row_index, np.int32)
+        M = row_index.shape[0]
+        assert M == 0 or (row_index.min() >= 0 and row_index.max() < R)
+    else:
+        M = R
+    codes = np.empty((M, K // 2), dtype=np.uint8)
+    scales = np.empty((M, K // 32), dtype=np.uint8)
+    if M:
+        _load().orc_quantize_act(_ptr(x_bits), ldx, _ptr(row_index), M, K,
+                                 _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+def _gemm_operands(a_codes, a_scales, b_codes, b_scales):
+    a_codes = _c(a_codes, np.uint8)
+    a_scales = _c(a_scales, np.uint8)
+    b_codes = _c(b_codes, np.uint8)
+    b_scales = _c(b_scales, np.uint8)
+    M, K = a_codes.shape[0], a_codes.shape[1] * 2
+    N = b_codes.shape[-2]
+    assert K % 32 == 0 and b_codes.shape[-1] * 2 == K
+    assert a_scales.shape == (M, K // 32) and b_scales.shape[-1] == K // 32
+    return a_codes, a_scales, b_codes, b_scales, M, N, K
+
+
+def gemm(a_codes, a_scales, b_codes, b_scales):
+    """Returns (y, s): fp64 [M,N] result and sum_k |a_k b_k|."""
+    a_codes, a_scales, b_codes, b_scales, M, N, K = _gemm_operands(
+        a_codes, a_scales, b_codes, b_scales)
+    y = np.empty((M, N), dtype=np.float64)
+    s = np.empty((M, N), dtype=np.float64)
+    _load().orc_gemm(_ptr(a_codes), _ptr(a_scales), _ptr(b_codes), _ptr(b_scales),
+                     M, N, K, _ptr(y), _ptr(s))
+    return y, s
+
+
+def gemm_at(a_codes, a_scales, b_codes, b_scales, pm, pn):
+    a_codes, a_scales, b_codes, b_scales, M, N, K = _gemm_operands(
+        a_codes, a_scales, b_codes, b_scales)
+    pm = _c(pm, np.int64)
+    pn = _c(pn, np.int64)
+    assert pm.shape == pn.shape and pm.ndim == 1
+    assert (pm >= 0).all() and (pm < M).all() and (pn >= 0).all() and (pn < N).all()
+    y = np.empty(pm.shape, dtype=np.float64)
+    s = np.empty(pm.shape, dtype=np.float64)
+    _load().orc_gemm_at(_ptr(a_codes), _ptr(a_scales), _ptr(b_codes), _ptr(b_scales),
+                        M, N, K, _ptr(pm), _ptr(pn), pm.shape[0], _ptr(y), _ptr(s))
+    return y, s
+
+
+def grouped_gemm(a_codes, a_scales, b_codes, b_scales, offsets):
+    """A [total_M, K/2] expert-sorted, B [E, N, K/2], offsets [E+1]."""
+    a_codes, a_scales, b_codes, b_scales, M, N, K = _gemm_operands(
+        a_codes, a_scales, b_codes, b_scales)
+    offsets = _c(offsets, np.int32)
+    E = offsets.shape[0] - 1
+    assert b_codes.shape == (E, N, K // 2) and b_scales.shape == (E, N, K // 32)
+    assert offsets[0] == 0 and offsets[-1] == M and (np.diff(offsets) >= 0).all()
+    y = np.zeros((M, N), dtype=np.float64)
+    s = np.zeros((M, N), dtype=np.float64)
+    _load().orc_grouped_gemm(_ptr(a_codes), _ptr(a_scales), _ptr(b_codes),
+                             _ptr(b_scales), _ptr(offsets), E, N, K, _ptr(y), _ptr(s))
+    return y, s
+
+
+# ---- parity bar for the GEMM ------------------------------------------------
+def gemm_fp32_ok(gpu, y, s, rtol=GEMM_FP32_RTOL) -> np.ndarray:
+    """Elementwise: |gpu - y| <= rtol * s (s == 0 requires gpu == 0)."""
+    gpu = np.asarray(gpu, dtype=np.float64)
+    return np.abs(gpu - y) <= rtol * s
+
+
+def _bf16_ordered(bits):
+    b = np.asarray(bits, dtype=np.uint16).astype(np.int64)
+    mag = b & 0x7FFF
+    return np.where(b & 0x8000, -mag, mag)
+
+
+def gemm_bf16_ok(gpu_bits, y, max_ulp=1) -> np.ndarray:
+    """Elementwise: ordered-bit distance between the GPU's bf16 output and
+    RNE_bf16(y) is at most max_ulp (+0 and -0 are the same point)."""
+    ref = bf16_from_double_array(y)
+    return np.abs(_bf16_ordered(gpu_bits) - _bf16_ordered(ref)) <= max_ulp

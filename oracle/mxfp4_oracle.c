@@ -1,0 +1,383 @@
+/*
+ * mxfp4_oracle.c -- plain CPU oracle (TEST INFRASTRUCTURE ONLY; see the
+ * header for the source passages and the readings R1-R5).
+ *
+ * Written for clarity, not speed: each value is decoded from its bit fields,
+ * every rounding is spelled out, fp64 is used wherever the method does not
+ * itself fix a narrower type.  Rows are independent, so the outer loops carry
+ * an OpenMP pragma; nothing else is reordered.
+ *
+ * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -fopenmp -shared
+ *        -fPIC mxfp4_oracle.c -o _liboracle.so -lm
+ */
+#include "mxfp4_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ---------------------------------------------------------------------- */
+/* Scalar codecs                                                           */
+/* ---------------------------------------------------------------------- */
+
+/* E2M1 ([P2] Overview: float4_e2m1fn): 1 sign bit, 2 exponent bits with
+   bias 1, 1 mantissa bit; exponent field 0 is subnormal (0.5 * mantissa).
+   The magnitudes are therefore {0, 0.5, 1, 1.5, 2, 3, 4, 6}; max 6 as the
+   single-scale section of [P2] states. */
+double orc_e2m1_value(unsigned code)
+{
+    unsigned sign = (code >> 3) & 1u;
+    unsigned exp  = (code >> 1) & 3u;
+    unsigned man  = code & 1u;
+    double mag;
+    if (exp == 0)
+        mag = 0.5 * (double)man;
+    else
+        mag = ldexp(1.0 + 0.5 * (double)man, (int)exp - 1);
+    return sign ? -mag : mag;
+}
+
+/* float8_e4m3fn ([P3] section 4: the NVFP4 per-16 group scale type):
+   1 sign, 4 exponent bits (bias 7), 3 mantissa bits, no infinities,
+   S.1111.111 is NaN, max finite 448. */
+double orc_e4m3_value(unsigned byte)
+{
+    unsigned sign = (byte >> 7) & 1u;
+    unsigned exp  = (byte >> 3) & 15u;
+    unsigned man  = byte & 7u;
+    double mag;
+    if (exp == 15 && man == 7)
+        return NAN;
+    if (exp == 0)
+        mag = ldexp((double)man / 8.0, -6);
+    else
+        mag = ldexp(1.0 + (double)man / 8.0, (int)exp - 7);
+    return sign ? -mag : mag;
+}
+
+/* float8_e8m0fnu ([P2] Overview; Validation and Notes item 4: raw bytes):
+   an unsigned biased exponent, value 2^(b-127), 0xFF is NaN. */
+double orc_e8m0_value(unsigned byte)
+{
+    if ((byte & 0xFFu) == 0xFFu)
+        return NAN;
+    return ldexp(1.0, (int)(byte & 0xFFu) - 127);
+}
+
+double orc_bf16_value(uint16_t bits)
+{
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* Round a double to the nearest bfloat16 (8 significant bits, exponent range
+   of fp32, subnormals down to 2^-133), ties to even, overflow to infinity. */
+uint16_t orc_bf16_from_double(double v)
+{
+    if (isnan(v))
+        return 0x7FC0u;
+    int neg = signbit(v) ? 1 : 0;
+    double a = fabs(v);
+    double r;
+    if (isinf(a)) {
+        r = INFINITY;
+    } else if (a == 0.0) {
+        r = 0.0;
+    } else {
+        int x;
+        frexp(a, &x);                 /* a = f * 2^x, f in [0.5, 1)      */
+        int e = x - 1;                /* floor(log2 a)                    */
+        int quantum_exp = (e < -126) ? -133 : e - 7;
+        double n = nearbyint(ldexp(a, -quantum_exp));   /* half-to-even */
+        r = ldexp(n, quantum_exp);
+        if (r >= ldexp(1.0, 128))
+            r = INFINITY;
+    }
+    float f = (float)r;               /* exact: r is bf16-representable  */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    uint16_t bits = (uint16_t)(u >> 16);
+    return neg ? (uint16_t)(bits | 0x8000u) : bits;
+}
+
+uint16_t orc_bf16_from_float(float v) { return orc_bf16_from_double((double)v); }
+
+/* R4 -- element encode ([P2] single-scale section: round_mode="rint", E2M1
+   maximum 6).  The E2M1 value nearest to q is chosen; when q lies exactly
+   half-way between two neighbours the one with the even code (mantissa bit
+   0) wins.  Values beyond 6 are nearest to 6, so saturation falls out of the
+   nearest-value rule.  The sign bit is copied from q.  Distances are exact in
+   fp64 for every q the path produces (q has at most 24 significant bits and
+   |q| < 8), so no false ties arise. */
+unsigned orc_e2m1_encode(double q)
+{
+    static const double grid[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+    double a = fabs(q);
+    unsigned best = 0;
+    double bestd = a;
+    for (unsigned i = 1; i < 8; ++i) {
+        double d = fabs(a - grid[i]);
+        if (d < bestd || (d == bestd && (i % 2u) == 0u)) {
+            best = i;
+            bestd = d;
+        }
+    }
+    return (signbit(q) ? 8u : 0u) | best;
+}
+
+/* R3 -- shared exponent of an OCP MX block ([P2] single-scale section:
+   setting 0 = OCP MX; Overview: one E8M0 exponent per 32 K-elements).  The
+   block scale is 2^(floor(log2 amax) - emax) with emax = 2, the exponent of
+   the largest E2M1 binade (6 = 1.5 * 2^2), clamped to E8M0's range. */
+unsigned orc_shared_exponent(double amax)
+{
+    if (isnan(amax) || isinf(amax))
+        return 0xFFu;
+    int e;
+    if (amax == 0.0) {
+        e = -127;
+    } else {
+        int x;
+        frexp(amax, &x);
+        e = (x - 1) - 2;
+    }
+    if (e < -127) e = -127;
+    if (e > 127) e = 127;
+    return (unsigned)(e + 127);
+}
+
+/* R3 + R4 on one block of 32 values, packed per R1. */
+void orc_mx_quantize_block(const double v[32], uint8_t codes[16], uint8_t* scale)
+{
+    double amax = 0.0;
+    int bad = 0;
+    for (int i = 0; i < 32; ++i) {
+        if (isnan(v[i]) || isinf(v[i]))
+            bad = 1;
+        else if (fabs(v[i]) > amax)
+            amax = fabs(v[i]);
+    }
+    unsigned b = bad ? 0xFFu : orc_shared_exponent(amax);
+    *scale = (uint8_t)b;
+    if (b == 0xFFu) {
+        memset(codes, 0, 16);
+        return;
+    }
+    int e = (int)b - 127;
+    for (int j = 0; j < 16; ++j) {
+        unsigned lo = orc_e2m1_encode(ldexp(v[2 * j], -e));
+        unsigned hi = orc_e2m1_encode(ldexp(v[2 * j + 1], -e));
+        codes[j] = (uint8_t)(lo | (hi << 4));
+    }
+}
+
+/* ---------------------------------------------------------------------- */
+/* NVFP4 dequantization (R2)                                               */
+/* ---------------------------------------------------------------------- */
+
+static unsigned nibble(const uint8_t* row, int64_t k)
+{
+    uint8_t byte = row[k / 2];
+    return (k % 2 == 0) ? (byte & 15u) : (byte >> 4);
+}
+
+/* [P1] introduction: NVFP4 = packed E2M1, an FP8 scale per block, an FP32
+   per-tensor scale.  [P3] sections 3-4: codes [N, K/2], E4M3 scales
+   [N, K/16], fp32 global.  The product code * block scale is exact in fp32
+   (at most 6 significant bits); multiplying by g rounds once (RNE). */
+static void nvfp4_dequant_row(const uint8_t* codes_row, const uint8_t* scales_row,
+                              float g, int64_t K, int bf16_intermediate, float* out)
+{
+    for (int64_t k = 0; k < K; ++k) {
+        double cs = orc_e2m1_value(nibble(codes_row, k)) *
+                    orc_e4m3_value(scales_row[k / 16]);
+        float p = (float)cs;          /* exact                              */
+        float w = p * g;              /* one IEEE fp32 rounding             */
+        if (bf16_intermediate) {
+            uint32_t u = (uint32_t)orc_bf16_from_float(w) << 16;
+            memcpy(&w, &u, sizeof w);
+        }
+        out[k] = w;
+    }
+}
+
+void orc_nvfp4_dequant(const uint8_t* codes, const uint8_t* scales, float g,
+                       int64_t N, int64_t K, int bf16_intermediate, float* out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n)
+        nvfp4_dequant_row(codes + n * (K / 2), scales + n * (K / 16), g, K,
+                          bf16_intermediate, out + n * K);
+}
+
+/* ---------------------------------------------------------------------- */
+/* The four operations                                                     */
+/* ---------------------------------------------------------------------- */
+
+/* [P1] pipeline section: dequantize a layer, quantize the intermediate to
+   MXFP4, write it into the preallocated destination.  MX block j along K
+   covers NVFP4 blocks 2j and 2j+1. */
+void orc_requant(const uint8_t* nv_codes, const uint8_t* nv_scales,
+                 const float* nv_global, int64_t T, int64_t N, int64_t K,
+                 int bf16_intermediate, uint8_t* mx_codes, uint8_t* mx_scales)
+{
+    for (int64_t t = 0; t < T; ++t) {
+#pragma omp parallel
+        {
+            float* row = (float*)malloc((size_t)K * sizeof(float));
+            double blk[32];
+#pragma omp for schedule(static)
+            for (int64_t n = 0; n < N; ++n) {
+                int64_t r = t * N + n;
+                nvfp4_dequant_row(nv_codes + r * (K / 2), nv_scales + r * (K / 16),
+                                  nv_global[t], K, bf16_intermediate, row);
+                for (int64_t j = 0; j < K / 32; ++j) {
+                    for (int i = 0; i < 32; ++i)
+                        blk[i] = (double)row[32 * j + i];
+                    orc_mx_quantize_block(blk, mx_codes + r * (K / 2) + 16 * j,
+                                          mx_scales + r * (K / 32) + j);
+                }
+            }
+            free(row);
+        }
+    }
+}
+
+/* [P1] closing list: activations are quantized to MXFP4 per batch, with no
+   stored scales; [P2] single-scale section: axis=-1, block 32. */
+void orc_quantize_act(const uint16_t* x, int64_t ldx, const int32_t* row_index,
+                      int64_t M, int64_t K, uint8_t* codes, uint8_t* scales)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        int64_t src = row_index ? (int64_t)row_index[m] : m;
+        const uint16_t* xr = x + src * ldx;
+        double blk[32];
+        for (int64_t j = 0; j < K / 32; ++j) {
+            for (int i = 0; i < 32; ++i)
+                blk[i] = orc_bf16_value(xr[32 * j + i]);
+            orc_mx_quantize_block(blk, codes + m * (K / 2) + 16 * j,
+                                  scales + m * (K / 32) + j);
+        }
+    }
+}
+
+/* Dequantized MXFP4 element: e2m1(code) * 2^(byte - 127), exact in fp64. */
+static double mx_value(const uint8_t* codes, const uint8_t* scales, int64_t row,
+                       int64_t K, int64_t k)
+{
+    return orc_e2m1_value(nibble(codes + row * (K / 2), k)) *
+           orc_e8m0_value(scales[row * (K / 32) + k / 32]);
+}
+
+static void mx_row(const uint8_t* codes, const uint8_t* scales, int64_t row,
+                   int64_t K, double* out)
+{
+    for (int64_t k = 0; k < K; ++k)
+        out[k] = mx_value(codes, scales, row, K, k);
+}
+
+static void dot_row(const double* a, const double* b, int64_t K, double* y, double* s)
+{
+    double acc = 0.0, mag = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+        double p = a[k] * b[k];
+        acc += p;
+        mag += fabs(p);
+    }
+    *y = acc;
+    *s = mag;
+}
+
+/* [P1] closing list: both GEMM operands are MXFP4; FP32 accumulation is the
+   hardware's, the oracle sums the exact products in fp64 (R5). */
+void orc_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
+              const uint8_t* b_codes, const uint8_t* b_scales,
+              int64_t M, int64_t N, int64_t K, double* y, double* s)
+{
+    double* bd = (double*)malloc((size_t)(N * K) * sizeof(double));
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n)
+        mx_row(b_codes, b_scales, n, K, bd + n * K);
+#pragma omp parallel
+    {
+        double* ad = (double*)malloc((size_t)K * sizeof(double));
+#pragma omp for schedule(static)
+        for (int64_t m = 0; m < M; ++m) {
+            mx_row(a_codes, a_scales, m, K, ad);
+            for (int64_t n = 0; n < N; ++n) {
+                double yy, ss;
+                dot_row(ad, bd + n * K, K, &yy, &ss);
+                if (y) y[m * N + n] = yy;
+                if (s) s[m * N + n] = ss;
+            }
+        }
+        free(ad);
+    }
+    free(bd);
+}
+
+void orc_gemm_at(const uint8_t* a_codes, const uint8_t* a_scales,
+                 const uint8_t* b_codes, const uint8_t* b_scales,
+                 int64_t M, int64_t N, int64_t K,
+                 const int64_t* pm, const int64_t* pn, int64_t P,
+                 double* y, double* s)
+{
+    (void)M; (void)N;
+#pragma omp parallel
+    {
+        double* ad = (double*)malloc((size_t)K * sizeof(double));
+        double* bd = (double*)malloc((size_t)K * sizeof(double));
+#pragma omp for schedule(static)
+        for (int64_t p = 0; p < P; ++p) {
+            mx_row(a_codes, a_scales, pm[p], K, ad);
+            mx_row(b_codes, b_scales, pn[p], K, bd);
+            double yy, ss;
+            dot_row(ad, bd, K, &yy, &ss);
+            if (y) y[p] = yy;
+            if (s) s[p] = ss;
+        }
+        free(ad);
+        free(bd);
+    }
+}
+
+/* [P1] closing list: MoE experts run on MXFP4 kernels; one GEMM per expert
+   over its contiguous block of (already expert-sorted) rows. */
+void orc_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
+                      const uint8_t* b_codes, const uint8_t* b_scales,
+                      const int32_t* offsets, int64_t E, int64_t N, int64_t K,
+                      double* y, double* s)
+{
+    for (int64_t e = 0; e < E; ++e) {
+        int64_t r0 = offsets[e], r1 = offsets[e + 1];
+        if (r1 <= r0)
+            continue;
+        orc_gemm(a_codes + r0 * (K / 2), a_scales + r0 * (K / 32),
+                 b_codes + e * N * (K / 2), b_scales + e * N * (K / 32),
+                 r1 - r0, N, K,
+                 y ? y + r0 * N : NULL, s ? s + r0 * N : NULL);
+    }
+}
+
+/* Elementwise helper for the tests: RNE of n doubles to bf16 bit patterns. */
+void orc_bf16_from_double_array(const double* v, int64_t n, uint16_t* out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = orc_bf16_from_double(v[i]);
+}
+
+int orc_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

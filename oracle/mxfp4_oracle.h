@@ -1,0 +1,103 @@
+/*
+ * mxfp4_oracle.h -- plain, slow, obviously-correct CPU oracle for the
+ * block-scaled 4-bit (E2M1) linear-layer path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path links, loads or
+ * calls this library: only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg do.  It shares no code, header, table or
+ * constant generator with the HIP library.
+ *
+ * All arithmetic that is not exact integer work is carried out in fp64 (or,
+ * where the method itself fixes fp32, in IEEE fp32 with contraction off).
+ * Every function names the passage of the source pages it follows:
+ *
+ *   [P1] AMD blog "Efficiently Serving NVFP4 Models on AMD Instinct
+ *        MI350X/MI355X Accelerators via Online NVFP4 to Quark MXFP4
+ *        Requantization" -- introduction (NVFP4 = packed E2M1 + FP8 per-block
+ *        scale + FP32 per-tensor scale), the pipeline section under Figure 1
+ *        (dequantize one layer, quantize to MXFP4, write into a preallocated
+ *        destination), and the closing list (dynamic per-batch activation
+ *        quantization; both GEMM operands MXFP4 on the scaled MFMA).
+ *   [P2] vLLM-Omni user guide "W4A4 MXFP4 Quantization" -- Overview (OCP MX:
+ *        32 K-elements share one float8_e8m0fnu exponent, E2M1 packed two per
+ *        byte), "mxfp4 -- Single-Scale Block Scaling (OCP / UOS)" (setting 0 =
+ *        OCP MX, axis=-1, block_size=32, round_mode="rint", E2M1 max 6),
+ *        "Validation and Notes" item 4 (scale bytes are raw E8M0 bytes).
+ *   [P3] SGLang FP4 post ("[SGLang] FP4 ..."), sections 3-4: NVFP4 weight
+ *        layout weight_packed [N, K/2] u8, weight_scale [N, K/16]
+ *        float8_e4m3fn, fp32 global scale.
+ *
+ * Readings where the pages are silent (each is listed in the design notes):
+ *   R1 nibble order: element 2j in bits 3:0 of byte j, element 2j+1 in 7:4.
+ *   R2 NVFP4 value = fl32( fl32(e2m1 * e4m3) * g ), g multiplies on dequant.
+ *      The requant's materialised intermediate is fp32 unless the caller asks
+ *      for bf16 (RNE of that fp32 value).
+ *   R3 shared exponent (OCP MX): e = floor(log2(amax)) - 2, clamped to
+ *      [-127, 127]; byte = e + 127.  amax NaN/Inf -> byte 0xFF, codes 0.
+ *   R4 element encode: round-half-to-even onto the E2M1 grid, saturating at
+ *      +-6, sign bit copied from the input (so -0.1 * 2^e encodes as 0x8).
+ *   R5 GEMM output: fp64 sum of exact products, rounded once (RNE) to the
+ *      output type.
+ */
+#ifndef MXFP4_ORACLE_H
+#define MXFP4_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- scalar codecs ---------------------------------------------------- */
+double   orc_e2m1_value(unsigned code);          /* code in [0,15]          */
+double   orc_e4m3_value(unsigned byte);          /* float8_e4m3fn           */
+double   orc_e8m0_value(unsigned byte);          /* float8_e8m0fnu          */
+double   orc_bf16_value(uint16_t bits);
+uint16_t orc_bf16_from_double(double v);         /* RNE, NaN -> 0x7FC0      */
+uint16_t orc_bf16_from_float(float v);           /* RNE, NaN -> 0x7FC0      */
+unsigned orc_e2m1_encode(double q);              /* R4                      */
+unsigned orc_shared_exponent(double amax);       /* R3, amax >= 0 or NaN    */
+
+/* ---- MX quantization of one 32-element block (R3 + R4) ---------------- */
+void orc_mx_quantize_block(const double v[32], uint8_t codes[16], uint8_t* scale);
+
+/* ---- NVFP4 dequantization of one tensor into fp32 (R2) ---------------- */
+void orc_nvfp4_dequant(const uint8_t* codes, const uint8_t* scales, float g,
+                       int64_t N, int64_t K, int bf16_intermediate, float* out);
+
+/* ---- the four operations of the path ---------------------------------- */
+/* NVFP4 -> MXFP4 requant of T same-shape tensors [T][N][K]. */
+void orc_requant(const uint8_t* nv_codes, const uint8_t* nv_scales,
+                 const float* nv_global, int64_t T, int64_t N, int64_t K,
+                 int bf16_intermediate, uint8_t* mx_codes, uint8_t* mx_scales);
+
+/* bf16 [*, ldx] -> MXFP4 codes [M][K/2] + E8M0 [M][K/32]; optional gather. */
+void orc_quantize_act(const uint16_t* x, int64_t ldx, const int32_t* row_index,
+                      int64_t M, int64_t K, uint8_t* codes, uint8_t* scales);
+
+/* y[m][n] = sum_k A[m,k] * B[n,k] over dequantized MXFP4 (fp64), and
+   s[m][n] = sum_k |A[m,k] * B[n,k]|.  Either output may be NULL. */
+void orc_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
+              const uint8_t* b_codes, const uint8_t* b_scales,
+              int64_t M, int64_t N, int64_t K, double* y, double* s);
+
+/* The same quantities at P sampled (m, n) positions only. */
+void orc_gemm_at(const uint8_t* a_codes, const uint8_t* a_scales,
+                 const uint8_t* b_codes, const uint8_t* b_scales,
+                 int64_t M, int64_t N, int64_t K,
+                 const int64_t* pm, const int64_t* pn, int64_t P,
+                 double* y, double* s);
+
+/* Per expert e, rows [off[e], off[e+1]) times expert e's weights. */
+void orc_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
+                      const uint8_t* b_codes, const uint8_t* b_scales,
+                      const int32_t* offsets, int64_t E, int64_t N, int64_t K,
+                      double* y, double* s);
+
+void orc_bf16_from_double_array(const double* v, int64_t n, uint16_t* out);
+int  orc_num_threads(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

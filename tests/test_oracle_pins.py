@@ -1,0 +1,428 @@
+"""Pins for the CPU oracle: each check ties the oracle to something other than
+itself -- torch's fp8/bf16 decode tables, numpy's half-to-even ``rint``,
+brute-force searches over whole domains, hand-worked fixtures under
+``tests/golden/`` (each cites its source passage), exact round trips and
+closed forms.  CPU only."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from conftest import parse_float, parse_sparse, read_table
+
+
+def e2m1_table():
+    rows = []
+    for line in (__import__("conftest").GOLDEN / "e2m1_values.txt").read_text().splitlines():
+        line = line.strip()
+        if line and not line.startswith("#"):
+            c, v = line.split()
+            rows.append((int(c), float(v)))
+    assert [c for c, _ in rows] == list(range(16))
+    return np.array([v for _, v in rows], dtype=np.float64)
+
+
+E2M1 = e2m1_table()
+
+
+# ---- scalar decoders -----------------------------------------------------
+def test_e2m1_decode_matches_value_table():
+    for c in range(16):
+        v = oracle.e2m1_value(c)
+        assert v == E2M1[c]
+        assert math.copysign(1.0, v) == math.copysign(1.0, E2M1[c])
+    assert max(oracle.e2m1_value(c) for c in range(16)) == 6.0
+
+
+def test_e4m3_decode_matches_torch_all_bytes():
+    b = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = b.view(torch.float8_e4m3fn).to(torch.float32).double().numpy()
+    got = np.array([oracle.e4m3_value(i) for i in range(256)])
+    assert np.array_equal(np.isnan(ref), np.isnan(got))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(ref[ok], got[ok])
+    assert np.array_equal(np.signbit(ref[ok]), np.signbit(got[ok]))
+    assert got[0x7E] == 448.0 and np.isnan(got[0x7F]) and got[0x01] == 2.0 ** -9
+
+
+def test_e8m0_decode_matches_torch_all_bytes():
+    b = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = b.view(torch.float8_e8m0fnu).to(torch.float32).double().numpy()
+    got = np.array([oracle.e8m0_value(i) for i in range(256)])
+    assert np.isnan(got[255]) and np.isnan(ref[255])
+    assert np.array_equal(ref[:255], got[:255])
+    assert got[127] == 1.0 and got[0] == 2.0 ** -127 and got[254] == 2.0 ** 127
+
+
+def test_bf16_decode_matches_torch_all_patterns():
+    bits = np.arange(65536, dtype=np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).float().double().numpy()
+    got = np.array([oracle.bf16_value(int(b)) for b in bits[::7]])
+    r = ref[::7]
+    assert np.array_equal(np.isnan(r), np.isnan(got))
+    ok = ~np.isnan(r)
+    assert np.array_equal(r[ok], got[ok])
+
+
+# ---- bf16 rounding -------------------------------------------------------
+def test_bf16_rounding_matches_torch_on_fp32_values():
+    rng = np.random.default_rng(5)
+    bits = rng.integers(0, 2 ** 32, size=200_000, dtype=np.uint64).astype(np.uint32)
+    # add every bf16 midpoint family explicitly: low 16 bits == 0x8000
+    mids = (rng.integers(0, 2 ** 16, size=20_000, dtype=np.uint32) << 16) | 0x8000
+    bits = np.concatenate([bits, mids.astype(np.uint32)])
+    f = bits.view(np.float32)
+    f = f[np.isfinite(f)]
+    ref = torch.from_numpy(f.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = oracle.bf16_from_double_array(f.astype(np.float64))
+    assert np.array_equal(ref, got)
+
+
+def test_bf16_rounding_from_double_single_rounding():
+    # 1 + 2^-8 is the midpoint between bf16 1.0 and 1.0078125: ties-to-even -> 1.0;
+    # a hair above it must round up (no double rounding through fp32).
+    assert oracle.bf16_from_double(1.0 + 2.0 ** -8) == 0x3F80
+    assert oracle.bf16_from_double(1.0 + 2.0 ** -8 + 2.0 ** -40) == 0x3F81
+    assert oracle.bf16_from_double(-(1.0 + 2.0 ** -8 + 2.0 ** -40)) == 0xBF81
+    # largest finite bf16 and overflow
+    assert oracle.bf16_from_double(float.fromhex("0x1.fep127")) == 0x7F7F
+    assert oracle.bf16_from_double(float.fromhex("0x1.ffp127")) == 0x7F80
+    assert oracle.bf16_from_double(2.0 ** -133) == 0x0001
+    assert oracle.bf16_from_double(2.0 ** -134) == 0x0000       # tie -> even (0)
+    assert oracle.bf16_from_double(-0.0) == 0x8000
+    assert oracle.bf16_from_double(float("nan")) == 0x7FC0
+
+
+# ---- E2M1 encoder ----------------------------------------------------------
+def rint_reference(q):
+    """E2M1 RNE written region by region with numpy's half-to-even rint:
+    spacing 0.5 below 2, 1 in [2, 4), 2 in [4, 6]; saturate at 6."""
+    a = np.abs(q)
+    v = np.where(a < 2, np.rint(a * 2) / 2, np.where(a < 4, np.rint(a), 2 * np.rint(a / 2)))
+    return np.minimum(v, 6.0)
+
+
+def test_e2m1_encode_matches_regionwise_rint():
+    rng = np.random.default_rng(7)
+    grid = np.arange(0, 8.0, 1.0 / 64)           # every tie point and more
+    rand = rng.uniform(-8, 8, size=50_000)
+    q = np.concatenate([grid, -grid, rand, [6.0, 6.5, 7.0, 7.99, 1e-30, -1e-30]])
+    codes = np.array([oracle.e2m1_encode(x) for x in q])
+    assert np.array_equal(np.abs(E2M1[codes]), rint_reference(q))
+    assert np.array_equal(codes >= 8, np.signbit(q))
+
+
+def test_e2m1_encode_roundtrip_all_codes():
+    for c in range(16):
+        assert oracle.e2m1_encode(E2M1[c]) == c
+
+
+# ---- shared exponent ---------------------------------------------------------
+def brute_force_byte(amax):
+    """The unique E8M0 byte b with 4 <= amax / 2^(b-127) < 8 (the block max
+    lands in E2M1's top binade), clamped to [0, 254] at the ends."""
+    if amax < 4 * 2.0 ** -127:
+        return 0
+    for b in range(255):
+        r = amax / 2.0 ** (b - 127)
+        if 4 <= r < 8:
+            return b
+    raise AssertionError(amax)
+
+
+def test_shared_exponent_bruteforce_all_bf16():
+    bits = np.arange(1, 0x7F80, dtype=np.uint16)         # positive finite bf16
+    vals = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).float().double().numpy()
+    for v in vals[::3]:
+        assert oracle.shared_exponent(v) == brute_force_byte(v), v
+
+
+def test_shared_exponent_fp32_sweep_and_specials():
+    rng = np.random.default_rng(3)
+    for e in range(-149, 128):
+        for m in (1.0, 1.5, 1.999999, float(rng.uniform(1, 2))):
+            v = float(np.float32(m * 2.0 ** e))
+            if v > 0 and math.isfinite(v):
+                assert oracle.shared_exponent(v) == brute_force_byte(v), v
+    assert oracle.shared_exponent(0.0) == 0
+    assert oracle.shared_exponent(float("nan")) == 255
+    assert oracle.shared_exponent(float("inf")) == 255
+
+
+# ---- hand-worked block fixtures -------------------------------------------------
+@pytest.mark.parametrize("row", read_table("mx_block_examples.txt"), ids=lambda r: r[0])
+def test_mx_block_examples(row):
+    name, inputs, byte, codes = row
+    v = np.zeros(32)
+    for i, x in parse_sparse(inputs, parse_float).items():
+        v[i] = x
+    want = np.zeros(32, dtype=np.int64)
+    for i, c in parse_sparse(codes, int).items():
+        want[i] = c
+    got_codes, got_byte = oracle.mx_quantize_block(v)
+    assert got_byte == int(byte)
+    unpacked = np.empty(32, dtype=np.int64)
+    unpacked[0::2] = got_codes & 15
+    unpacked[1::2] = got_codes >> 4
+    assert np.array_equal(unpacked, want)
+
+
+@pytest.mark.parametrize("row", read_table("requant_examples.txt"), ids=lambda r: r[0])
+def test_requant_examples(row):
+    name, gbits, s0, s1, codes, bf16, byte, mx = row
+    g = np.array([int(gbits, 16)], dtype=np.uint32).view(np.float32)
+    nib = np.zeros(32, dtype=np.uint8)
+    for i, c in parse_sparse(codes, int).items():
+        nib[i] = c
+    packed = (nib[0::2] | (nib[1::2] << 4)).reshape(1, 16)
+    scales = np.array([[int(s0, 16), int(s1, 16)]], dtype=np.uint8)
+    out_codes, out_scales = oracle.requant(packed, scales, g, bf16_intermediate=bool(int(bf16)))
+    assert out_scales.shape == (1, 1) and int(out_scales[0, 0]) == int(byte)
+    want = np.zeros(32, dtype=np.uint8)
+    for i, c in parse_sparse(mx, int).items():
+        want[i] = c
+    got = np.empty(32, dtype=np.uint8)
+    got[0::2] = out_codes[0] & 15
+    got[1::2] = out_codes[0] >> 4
+    assert np.array_equal(got, want)
+
+
+# ---- round trips and exactness ---------------------------------------------------
+def canonical_blocks(rows, K, seed, lo=2, hi=252):
+    """MXFP4 tensors whose blocks re-quantize to themselves: each non-zero block's
+    largest |code| is 6 or 7 (4 or 6), scale bytes keep values normal in bf16;
+    all-zero blocks carry byte 0."""
+    rng = np.random.default_rng(seed)
+    nib = rng.integers(0, 16, size=(rows, K), dtype=np.uint8)
+    nb = K // 32
+    blk = nib.reshape(rows, nb, 32)
+    pos = rng.integers(0, 32, size=(rows, nb))
+    top = rng.choice(np.array([6, 7, 14, 15], dtype=np.uint8), size=(rows, nb))
+    np.put_along_axis(blk, pos[..., None], top[..., None], axis=2)
+    scales = rng.integers(lo, hi + 1, size=(rows, nb), dtype=np.uint8)
+    zero = rng.random((rows, nb)) < 0.05
+    blk[zero] = rng.choice(np.array([0, 8], dtype=np.uint8), size=(int(zero.sum()), 32))
+    scales[zero] = 0
+    nib = blk.reshape(rows, K)
+    packed = nib[:, 0::2] | (nib[:, 1::2] << 4)
+    return nib, packed, scales
+
+
+def dequant_to_bf16_bits(nib, scales):
+    vals = E2M1[nib] * np.ldexp(1.0, np.repeat(scales.astype(np.int64) - 127, 32, axis=1))
+    f = vals.astype(np.float32)
+    assert np.array_equal(f.astype(np.float64), vals)          # exact
+    b = f.view(np.uint32)
+    assert not (b & 0xFFFF).any()                             # exact in bf16
+    return (b >> 16).astype(np.uint16)
+
+
+def test_quantize_act_roundtrip_canonical():
+    nib, packed, scales = canonical_blocks(64, 1024, seed=11)
+    x = dequant_to_bf16_bits(nib, scales)
+    codes, sc = oracle.quantize_act(x)
+    assert np.array_equal(sc, scales)
+    assert np.array_equal(codes, packed)
+
+
+def test_quantize_act_gather_equals_quantize_then_index():
+    rng = np.random.default_rng(4)
+    x = torch.randn(40, 256, generator=torch.Generator().manual_seed(9)).to(torch.bfloat16)
+    xb = x.view(torch.int16).numpy().view(np.uint16)
+    idx = rng.integers(0, 40, size=77).astype(np.int32)
+    c_all, s_all = oracle.quantize_act(xb)
+    c_g, s_g = oracle.quantize_act(xb, row_index=idx)
+    assert np.array_equal(c_g, c_all[idx]) and np.array_equal(s_g, s_all[idx])
+    # ldx > K: only the first K columns are read
+    wide = np.concatenate([xb, np.full((40, 64), 0x7FC0, dtype=np.uint16)], axis=1)
+    c_w, s_w = oracle.quantize_act(wide, K=256)
+    assert np.array_equal(c_w, c_all) and np.array_equal(s_w, s_all)
+
+
+def test_requant_exact_on_representable_input():
+    rng = np.random.default_rng(21)
+    N, K = 48, 512
+    nib, packed, _ = canonical_blocks(N, K, seed=22)
+    # both 16-halves of a 32-block share one power-of-two E4M3 scale 2^p
+    p = rng.integers(-9, 9, size=(N, K // 32))
+    def e4m3_pow2(pp):
+        if pp >= -6:
+            return (pp + 7) << 3
+        return {-7: 0x04, -8: 0x02, -9: 0x01}[pp]
+    e4 = np.vectorize(e4m3_pow2)(p).astype(np.uint8)
+    nv_scales = np.repeat(e4, 2, axis=1)
+    for q in (-3, 0, 5):
+        g = np.float32(2.0 ** q)
+        codes, scales = oracle.requant(packed, nv_scales, g)
+        blk_nonzero = (nib.reshape(N, K // 32, 32) & 7).any(axis=2)
+        want_scales = np.where(blk_nonzero, p + q + 127, 0)
+        assert np.array_equal(scales, want_scales.astype(np.uint8))
+        assert np.array_equal(codes, packed)       # signed zeros included
+
+
+def test_nvfp4_dequant_matches_numpy_fp32():
+    rng = np.random.default_rng(8)
+    N, K = 16, 256
+    codes = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    scales = rng.integers(0, 0x7F, size=(N, K // 16), dtype=np.uint8)   # finite, >= 0
+    g = np.float32(rng.uniform(1e-5, 3.0))
+    nib = np.empty((N, K), dtype=np.uint8)
+    nib[:, 0::2] = codes & 15
+    nib[:, 1::2] = codes >> 4
+    s = torch.from_numpy(scales).view(torch.float8_e4m3fn).float().numpy()
+    p = (E2M1[nib].astype(np.float32) * np.repeat(s, 16, axis=1)).astype(np.float32)
+    want = p * g                                              # numpy IEEE fp32
+    got = oracle.nvfp4_dequant(codes, scales, g)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    got_b = oracle.nvfp4_dequant(codes, scales, g, bf16_intermediate=True)
+    want_b = torch.from_numpy(want).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(got_b.view(np.uint32), want_b.view(np.uint32))
+
+
+def test_requant_bf16_path_equals_act_quant_of_dequant():
+    """With the bf16 intermediate, requant == act-quant of the dequantized tensor."""
+    rng = np.random.default_rng(12)
+    N, K = 32, 512
+    codes = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    scales = rng.integers(0, 0x7F, size=(N, K // 16), dtype=np.uint8)
+    g = np.float32(0.000123)
+    deq = oracle.nvfp4_dequant(codes, scales, g, bf16_intermediate=True)
+    xb = (deq.view(np.uint32) >> 16).astype(np.uint16)
+    c1, s1 = oracle.requant(codes, scales, g, bf16_intermediate=True)
+    c2, s2 = oracle.quantize_act(xb)
+    assert np.array_equal(c1, c2) and np.array_equal(s1, s2)
+
+
+def test_requant_fp32_path_equals_blockwise_quantization():
+    rng = np.random.default_rng(13)
+    N, K = 6, 256
+    codes = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    scales = rng.integers(0, 0x7F, size=(N, K // 16), dtype=np.uint8)
+    g = np.float32(0.37)
+    deq = oracle.nvfp4_dequant(codes, scales, g)
+    c1, s1 = oracle.requant(codes, scales, g)
+    for n in range(N):
+        for j in range(K // 32):
+            cb, sb = oracle.mx_quantize_block(deq[n, 32 * j:32 * j + 32].astype(np.float64))
+            assert sb == s1[n, j]
+            assert np.array_equal(cb, c1[n, 16 * j:16 * j + 16])
+
+
+# ---- GEMM ------------------------------------------------------------------------
+def dequant(codes, scales):
+    K = codes.shape[-1] * 2
+    nib = np.empty(codes.shape[:-1] + (K,), dtype=np.uint8)
+    nib[..., 0::2] = codes & 15
+    nib[..., 1::2] = codes >> 4
+    sc = np.ldexp(1.0, scales.astype(np.int64) - 127)
+    return E2M1[nib] * np.repeat(sc, 32, axis=-1)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 32), (7, 5, 64), (33, 17, 544), (16, 256, 512)])
+def test_gemm_matches_numpy_fp64_matmul(M, N, K):
+    rng = np.random.default_rng(M * 1000 + N)
+    a = rng.integers(0, 256, size=(M, K // 2), dtype=np.uint8)
+    sa = rng.integers(110, 140, size=(M, K // 32), dtype=np.uint8)
+    b = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    sb = rng.integers(110, 140, size=(N, K // 32), dtype=np.uint8)
+    y, s = oracle.gemm(a, sa, b, sb)
+    A, B = dequant(a, sa), dequant(b, sb)
+    ref = A @ B.T
+    S = np.abs(A) @ np.abs(B).T
+    assert np.all(np.abs(y - ref) <= 1e-12 * S + 1e-300)
+    assert np.allclose(s, S, rtol=1e-12, atol=0)
+
+
+def test_gemm_unit_scales_is_integer_product():
+    rng = np.random.default_rng(1)
+    M, N, K = 9, 11, 320
+    a = rng.integers(0, 256, size=(M, K // 2), dtype=np.uint8)
+    b = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    ones_a = np.full((M, K // 32), 127, dtype=np.uint8)
+    ones_b = np.full((N, K // 32), 127, dtype=np.uint8)
+    y, _ = oracle.gemm(a, ones_a, b, ones_b)
+    def twice(c):          # 2 * e2m1 value as an integer, from the table fixture
+        nib = np.empty((c.shape[0], K), dtype=np.uint8)
+        nib[:, 0::2] = c & 15
+        nib[:, 1::2] = c >> 4
+        return (2 * E2M1[nib]).astype(np.int64)
+    ref = twice(a) @ twice(b).T
+    assert np.array_equal(y * 4, ref.astype(np.float64))
+
+
+def test_gemm_one_hot_reproduces_dequantized_column():
+    rng = np.random.default_rng(2)
+    N, K = 13, 96
+    b = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    sb = rng.integers(100, 150, size=(N, K // 32), dtype=np.uint8)
+    B = dequant(b, sb)
+    for k0 in (0, 1, 31, 32, 95):
+        a = np.zeros((1, K // 2), dtype=np.uint8)
+        a[0, k0 // 2] = 2 << (4 * (k0 % 2))      # code 2 = 1.0
+        sa = np.full((1, K // 32), 127, dtype=np.uint8)
+        y, s = oracle.gemm(a, sa, b, sb)
+        assert np.array_equal(y[0], B[:, k0])
+        assert np.array_equal(s[0], np.abs(B[:, k0]))
+
+
+def test_gemm_nan_scale_propagates():
+    a = np.zeros((1, 16), dtype=np.uint8)
+    sa = np.array([[255]], dtype=np.uint8)
+    b = np.zeros((2, 16), dtype=np.uint8)
+    sb = np.full((2, 1), 127, dtype=np.uint8)
+    y, _ = oracle.gemm(a, sa, b, sb)
+    assert np.isnan(y).all()
+
+
+def test_gemm_at_matches_full():
+    rng = np.random.default_rng(6)
+    M, N, K = 20, 30, 128
+    a = rng.integers(0, 256, size=(M, K // 2), dtype=np.uint8)
+    sa = rng.integers(120, 134, size=(M, K // 32), dtype=np.uint8)
+    b = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    sb = rng.integers(120, 134, size=(N, K // 32), dtype=np.uint8)
+    y, s = oracle.gemm(a, sa, b, sb)
+    pm = rng.integers(0, M, size=50)
+    pn = rng.integers(0, N, size=50)
+    yp, sp = oracle.gemm_at(a, sa, b, sb, pm, pn)
+    assert np.array_equal(yp, y[pm, pn]) and np.array_equal(sp, s[pm, pn])
+
+
+def test_grouped_gemm_equals_per_expert_gemm():
+    rng = np.random.default_rng(10)
+    E, N, K = 5, 24, 96
+    counts = np.array([3, 0, 7, 1, 0])
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    M = int(offsets[-1])
+    a = rng.integers(0, 256, size=(M, K // 2), dtype=np.uint8)
+    sa = rng.integers(120, 134, size=(M, K // 32), dtype=np.uint8)
+    b = rng.integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)
+    sb = rng.integers(120, 134, size=(E, N, K // 32), dtype=np.uint8)
+    y, s = oracle.grouped_gemm(a, sa, b, sb, offsets)
+    for e in range(E):
+        r0, r1 = offsets[e], offsets[e + 1]
+        if r1 > r0:
+            ye, se = oracle.gemm(a[r0:r1], sa[r0:r1], b[e], sb[e])
+            assert np.array_equal(y[r0:r1], ye) and np.array_equal(s[r0:r1], se)
+
+
+# ---- the tolerance rules themselves ----------------------------------------------
+def test_tolerance_rules_accept_one_ulp_reject_two():
+    rng = np.random.default_rng(0)
+    y = rng.standard_normal(2000) * 10.0 ** rng.integers(-5, 5, 2000)
+    ref = oracle.bf16_from_double_array(y)
+    def step(bits, k):
+        b = bits.astype(np.int64)
+        mag = (b & 0x7FFF) + k
+        return ((b & 0x8000) | mag).astype(np.uint16)
+    assert oracle.gemm_bf16_ok(ref, y).all()
+    assert oracle.gemm_bf16_ok(step(ref, 1), y).all()
+    assert not oracle.gemm_bf16_ok(step(ref, 2), y).any()
+    assert oracle.gemm_bf16_ok(np.array([0x8000], dtype=np.uint16), np.array([0.0])).all()
+    s = np.abs(y) * 3
+    assert oracle.gemm_fp32_ok(y + 0.9e-5 * s, y, s).all()
+    assert not oracle.gemm_fp32_ok(y + 1.1e-5 * s, y, s).any()
+    assert oracle.gemm_fp32_ok(np.array([0.0]), np.array([0.0]), np.array([0.0])).all()
+    assert not oracle.gemm_fp32_ok(np.array([1e-30]), np.array([0.0]), np.array([0.0])).any()
