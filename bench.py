@@ -1,0 +1,414 @@
+#!/usr/bin/env python3
+"""Benchmark of the MXFP4 W4A4 linear-layer path on one MI355X.
+
+Default workload (the decode-shaped dense linear): an NVFP4 weight
+[N=12288, K=4096] from bf16 N(0, 0.02) is requantized to MXFP4, then for each
+M in {1, 8, 32, 64} bf16 activations [M, 4096] ~ N(0, 1) with 1% outlier
+channels (x50) are quantized to MXFP4 and multiplied with the weight (bf16
+out).  One step = requant + the four (act-quant, GEMM) pairs.  Weight sources
+and destinations rotate over copies totalling > 768 MiB so that the bytes
+come from HBM, not the 256 MiB Infinity Cache.
+
+Other workloads (``--workload prefill|moe|layerwise``) print their own JSON
+line; they are measurements of the remaining configurations.
+
+Prints ONE JSON line.  ``value`` = GEMM TFLOP/s including activation
+quantization (sum of 2MNK over sum of act-quant + GEMM time); requant GB/s
+and roofline fractions are extra fields.  Every kernel is timed with HIP
+events recorded on the stream the kernels run on.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import pathlib
+import sys
+import time
+
+ROOT = pathlib.Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+METRIC = "MXFP4 W4A4 GEMM TFLOP/s (incl. act quant) + requant GB/s, % of roofline"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+MXFP4_PEAK_TFLOPS = 10100.0     # MI355X dense MXFP4 MFMA
+ROTATE_BYTES = 1 << 30          # > 3x the 256 MiB MALL
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="decode",
+                   choices=["decode", "prefill", "moe", "layerwise"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+# ---- algorithmic bytes (per launch) ---------------------------------------------
+def requant_bytes(T, N, K):          # codes+E4M3 in, codes+E8M0 out, one g per tensor
+    return T * N * K * (0.5 + 1 / 16 + 0.5 + 1 / 32) + 4 * T
+
+
+def act_quant_bytes(M, K):           # bf16 in, codes + E8M0 out
+    return M * K * (2 + 0.5 + 1 / 32)
+
+
+def gemm_bytes(M, N, K, out_bytes=2):  # both MXFP4 operands in, Y out
+    return (M + N) * K * (0.5 + 1 / 32) + M * N * out_bytes
+
+
+def kernel_source_digest():
+    h = hashlib.sha256()
+    for f in sorted((ROOT / "w4a4_mxfp4_gemm_amd" / "csrc").glob("*")):
+        h.update(f.read_bytes())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(kernel_tag):
+    """HBM bytes per dispatch measured by rocprofv3 PMC runs (profiles/), valid
+    only while the kernel sources hash to the digest stored with them."""
+    f = ROOT / "profiles" / f"{kernel_tag}_traffic.txt"
+    if not f.exists():
+        return None
+    kv = {}
+    for line in f.read_text().splitlines():
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_dispatch"])
+    except (KeyError, ValueError):
+        return None
+
+
+class Timeline:
+    """Per-kernel HIP events on the current stream; durations summed per tag."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.marks = []
+
+    def mark(self, tag=None):
+        ev = self.torch.cuda.Event(enable_timing=True)
+        ev.record()
+        self.marks.append((tag, ev))
+
+    def totals(self):
+        out = {}
+        for (_, e0), (tag, e1) in zip(self.marks, self.marks[1:]):
+            if tag is None:
+                continue
+            ms = e0.elapsed_time(e1)
+            t = out.setdefault(tag, [0.0, 0])
+            t[0] += ms
+            t[1] += 1
+        return out
+
+
+# ---- workloads ------------------------------------------------------------------------
+def decode_workload(torch, mx, synth):
+    N, K, Ms = 12288, 4096, (1, 8, 32, 64)
+    d = torch.device("cuda:0")
+    w = synth.bf16_normal((N, K), 0.02, seed=11, device=d)
+    codes, scales, g = synth.nvfp4_from_bf16(w)
+    g = g.reshape(1)
+    per_copy = requant_bytes(1, N, K)
+    R = max(2, math.ceil(ROTATE_BYTES / per_copy))
+    src = [(codes.clone(), scales.clone(), g.clone()) for _ in range(R)]
+    dst = [(torch.empty((N, K // 2), dtype=torch.uint8, device=d),
+            torch.empty((N, K // 32), dtype=torch.uint8, device=d)) for _ in range(R)]
+    x = synth.activations(64, K, seed=12, outlier_seed=13, device="cpu").to(d)
+    xs = {M: x[:M].contiguous() for M in Ms}
+    xq = {M: (torch.empty((M, K // 2), dtype=torch.uint8, device=d),
+              torch.empty((M, K // 32), dtype=torch.uint8, device=d)) for M in Ms}
+    ys = {M: torch.empty((M, N), dtype=torch.bfloat16, device=d) for M in Ms}
+    state = {"i": 0}
+
+    def step(tl):
+        r = state["i"] % R
+        state["i"] += 1
+        c, s, gg = src[r]
+        mc, ms = dst[r]
+        tl.mark()
+        mx.mxfp4_requant_from_nvfp4(c, s, gg, mc, ms)
+        tl.mark("requant")
+        for M in Ms:
+            mx.mxfp4_quantize_act(xs[M], *xq[M])
+            tl.mark(f"act_quant_M{M}")
+            mx.mxfp4_gemm(xq[M][0], xq[M][1], mc, ms, ys[M])
+            tl.mark(f"gemm_M{M}")
+
+    def report(tot, steps):
+        t_req = tot["requant"][0] / steps
+        flops = sum(2 * M * N * K for M in Ms)
+        t_aq = sum(tot[f"act_quant_M{M}"][0] for M in Ms) / steps
+        t_gemm = sum(tot[f"gemm_M{M}"][0] for M in Ms) / steps
+        value = flops / ((t_aq + t_gemm) * 1e-3) / 1e12
+        gb_req = requant_bytes(1, N, K) / (t_req * 1e-3) / 1e9
+        gemm_b = sum(gemm_bytes(M, N, K) for M in Ms)
+        gemm_gbps = gemm_b / (t_gemm * 1e-3) / 1e9
+        per_m = {}
+        for M in Ms:
+            ta = tot[f"act_quant_M{M}"][0] / steps
+            tg = tot[f"gemm_M{M}"][0] / steps
+            per_m[str(M)] = {
+                "act_quant_us": round(ta * 1e3, 2), "gemm_us": round(tg * 1e3, 2),
+                "gemm_GBps": round(gemm_bytes(M, N, K) / (tg * 1e-3) / 1e9, 1),
+                "gemm_frac_hbm": round(gemm_bytes(M, N, K) / (tg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                "TFLOPs_incl_act_quant": round(2 * M * N * K / ((ta + tg) * 1e-3) / 1e12, 3),
+            }
+        traffic = recorded_traffic("gemm_decode")
+        roof = {"kernel": "gemm (decode, M=1,8,32,64)", "bound": "hbm",
+                "achieved": round(gemm_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(gemm_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                "algorithmic_bytes_per_launch": round(gemm_b / len(Ms)),
+                "avg_launch_us": round(t_gemm / len(Ms) * 1e3, 3)}
+        extra = {"requant_GBps": round(gb_req, 1),
+                 "requant_frac_hbm": round(gb_req / HBM_PEAK_GBPS, 4),
+                 "requant_us": round(t_req * 1e3, 2), "per_M": per_m,
+                 "weight_copies_rotated": R}
+        cfg = {"workload": "decode-shaped dense linear: NVFP4->MXFP4 requant of W "
+                           "[12288,4096] + act-quant + W4A4 GEMM for M in {1,8,32,64}, bf16 out",
+               "N": N, "K": K, "M": list(Ms)}
+        return value, "TFLOP/s", roof, extra, cfg
+
+    def cpu_baseline():
+        import numpy as np
+        import oracle
+        rows = 1536                      # bounded sample: first rows of W (1/8 of N)
+        wc, ws, gg = codes[:rows].cpu().numpy(), scales[:rows].cpu().numpy(), g.cpu().numpy()
+        xb = x.cpu().view(torch.int16).numpy().view(np.uint16)
+        t0 = time.perf_counter()
+        oc, os_ = oracle.requant(wc, ws, gg)
+        t1 = time.perf_counter()
+        for M in Ms:
+            ac, as_ = oracle.quantize_act(xb[:M])
+            oracle.gemm(ac, as_, oc, os_)
+        t2 = time.perf_counter()
+        flops = sum(2 * M * rows * K for M in Ms)
+        return {"value": round(flops / (t2 - t1) / 1e12, 6), "unit": "TFLOP/s",
+                "cores": oracle.num_threads(), "kind": "oracle",
+                "sample": f"W rows 0..{rows - 1} of {N} (1/8 of the GEMM work) for M in "
+                          f"{{1,8,32,64}}: oracle act-quant + fp64 GEMM; requant of the same rows "
+                          f"{requant_bytes(1, rows, K) / (t1 - t0) / 1e9:.3f} GB/s",
+                "seconds": round(t2 - t0, 2)}
+
+    return step, report, cpu_baseline
+
+
+def prefill_workload(torch, mx, synth):
+    M = 4096
+    shapes = [(4096, 4096), (28672, 4096), (4096, 14336)]
+    d = torch.device("cuda:0")
+    data = []
+    for (N, K), ws, xs_, os_ in zip(shapes, (21, 22, 23), (24, 24, 25), (26, 26, 27)):
+        w = synth.bf16_normal((N, K), 0.02, seed=ws, device=d)
+        c, s, g = synth.nvfp4_from_bf16(w)
+        del w
+        wc, wsc = mx.mxfp4_requant_from_nvfp4(c, s, g.reshape(1))
+        x = synth.activations(M, K, seed=xs_, outlier_seed=os_, device=d)
+        xq = (torch.empty((M, K // 2), dtype=torch.uint8, device=d),
+              torch.empty((M, K // 32), dtype=torch.uint8, device=d))
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=d)
+        data.append((N, K, wc, wsc, x, xq, y))
+
+    def step(tl):
+        tl.mark()
+        for N, K, wc, wsc, x, xq, y in data:
+            mx.mxfp4_quantize_act(x, *xq)
+            tl.mark(f"aq_{N}x{K}")
+            mx.mxfp4_gemm(xq[0], xq[1], wc, wsc, y)
+            tl.mark(f"gemm_{N}x{K}")
+
+    def report(tot, steps):
+        flops = sum(2 * M * N * K for N, K in shapes)
+        t = sum(v[0] for v in tot.values()) / steps
+        value = flops / (t * 1e-3) / 1e12
+        per = {}
+        tg_all = 0.0
+        for N, K in shapes:
+            ta = tot[f"aq_{N}x{K}"][0] / steps
+            tg = tot[f"gemm_{N}x{K}"][0] / steps
+            tg_all += tg
+            per[f"{N}x{K}"] = {"act_quant_us": round(ta * 1e3, 2), "gemm_us": round(tg * 1e3, 2),
+                               "gemm_TFLOPs": round(2 * M * N * K / (tg * 1e-3) / 1e12, 1),
+                               "TFLOPs_incl_act_quant": round(2 * M * N * K / ((ta + tg) * 1e-3) / 1e12, 1),
+                               "act_quant_GBps": round(act_quant_bytes(M, K) / (ta * 1e-3) / 1e9, 1)}
+        gflops = sum(2 * M * N * K for N, K in shapes)
+        ach = gflops / (tg_all * 1e-3) / 1e12
+        roof = {"kernel": "gemm (prefill)", "bound": "mfma", "achieved": round(ach, 1),
+                "peak": MXFP4_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / MXFP4_PEAK_TFLOPS, 4),
+                "traffic": recorded_traffic("gemm_prefill")}
+        cfg = {"workload": "prefill dense linears M=4096, (N,K) in (4096,4096),(28672,4096),"
+                           "(4096,14336): act-quant + W4A4 GEMM, bf16 out"}
+        return value, "TFLOP/s", roof, {"per_shape": per}, cfg
+
+    return step, report, None
+
+
+def moe_workload(torch, mx, synth):
+    E, T, TOPK = 128, 2048, 8
+    d = torch.device("cuda:0")
+    perm, offsets = synth.route_topk(T, E, TOPK, seed=34, device="cpu")
+    perm, offsets = perm.to(d), offsets.to(d)
+    tokens = synth.activations(T, 4096, seed=33, device=d)
+    down_in = synth.activations(T * TOPK, 1024, seed=35, device=d)
+    W = {}
+    for name, (N, K), seed in (("gate_up", (2048, 4096), 31), ("down", (4096, 1024), 32)):
+        wc = torch.empty((E, N, K // 2), dtype=torch.uint8, device=d)
+        ws = torch.empty((E, N, K // 32), dtype=torch.uint8, device=d)
+        for e in range(E):
+            w = synth.bf16_normal((N, K), 0.02, seed=seed * 1000 + e, device=d)
+            c, s, g = synth.nvfp4_from_bf16(w)
+            mx.mxfp4_requant_from_nvfp4(c, s, g.reshape(1), wc[e], ws[e])
+        W[name] = (N, K, wc, ws)
+    Mtot = T * TOPK
+    aq1 = (torch.empty((Mtot, 2048), dtype=torch.uint8, device=d),
+           torch.empty((Mtot, 128), dtype=torch.uint8, device=d))
+    aq2 = (torch.empty((Mtot, 512), dtype=torch.uint8, device=d),
+           torch.empty((Mtot, 32), dtype=torch.uint8, device=d))
+    y1 = torch.empty((Mtot, 2048), dtype=torch.bfloat16, device=d)
+    y2 = torch.empty((Mtot, 4096), dtype=torch.bfloat16, device=d)
+
+    def step(tl):
+        tl.mark()
+        mx.mxfp4_quantize_act(tokens, *aq1, row_index=perm)
+        tl.mark("aq_gate_up")
+        _, _, wc, ws = W["gate_up"]
+        mx.mxfp4_grouped_gemm(aq1[0], aq1[1], wc, ws, offsets, y1)
+        tl.mark("gemm_gate_up")
+        mx.mxfp4_quantize_act(down_in, *aq2)
+        tl.mark("aq_down")
+        _, _, wc, ws = W["down"]
+        mx.mxfp4_grouped_gemm(aq2[0], aq2[1], wc, ws, offsets, y2)
+        tl.mark("gemm_down")
+
+    def report(tot, steps):
+        flops = 2 * Mtot * (2048 * 4096 + 4096 * 1024)
+        t = sum(v[0] for v in tot.values()) / steps
+        value = flops / (t * 1e-3) / 1e12
+        tg = (tot["gemm_gate_up"][0] + tot["gemm_down"][0]) / steps
+        mx4 = 0.5 + 1 / 32
+        gb = (E * 2048 * 4096 * mx4 + Mtot * 4096 * mx4 + Mtot * 2048 * 2 +
+              E * 4096 * 1024 * mx4 + Mtot * 1024 * mx4 + Mtot * 4096 * 2)
+        ach = gb / (tg * 1e-3) / 1e9
+        per = {k: round(v[0] / steps * 1e3, 2) for k, v in tot.items()}
+        roof = {"kernel": "grouped gemm (gate_up + down)", "bound": "hbm", "achieved": round(ach, 1),
+                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
+                "traffic": recorded_traffic("grouped_gemm_moe"),
+                "gemm_TFLOPs": round(flops / (tg * 1e-3) / 1e12, 1)}
+        cfg = {"workload": "MoE 128 experts, 2048 tokens top-8: gather act-quant + grouped "
+                           "GEMM gate_up [2048,4096], act-quant + grouped GEMM down [4096,1024]"}
+        return value, "TFLOP/s", roof, {"per_kernel_us": per}, cfg
+
+    return step, report, None
+
+
+def layerwise_workload(torch, mx, synth):
+    """One MoE layer's NVFP4 tensors resident in a one-layer scratch buffer,
+    requantized into a 48-layer preallocated destination, layer after layer
+    (kernel time only; 5% of tensors excluded and skipped)."""
+    E, L = 128, 48
+    d = torch.device("cuda:0")
+    gen = torch.Generator().manual_seed(42)
+    excluded = torch.rand((L, 2, E), generator=gen) < 0.05
+    shapes = {0: (2048, 4096), 1: (4096, 1024)}
+    src = {}
+    for k, (N, K) in shapes.items():
+        w = synth.bf16_normal((E, N, K), 0.02, seed=41 + k, device=d)
+        src[k] = synth.nvfp4_from_bf16(w)
+        del w
+    dst = {k: (torch.empty((L, E, N, K // 2), dtype=torch.uint8, device=d),
+               torch.empty((L, E, N, K // 32), dtype=torch.uint8, device=d))
+           for k, (N, K) in shapes.items()}
+    runs = []
+    for l in range(L):
+        for k in shapes:
+            keep = (~excluded[l, k]).nonzero().flatten().tolist()
+            i = 0
+            while i < len(keep):          # contiguous runs of non-excluded experts
+                j = i
+                while j + 1 < len(keep) and keep[j + 1] == keep[j] + 1:
+                    j += 1
+                runs.append((l, k, keep[i], keep[j] + 1))
+                i = j + 1
+    n_tensors = sum(b - a for _, _, a, b in runs)
+
+    def step(tl):
+        tl.mark()
+        for l, k, a, b in runs:
+            c, s, g = src[k]
+            mc, ms = dst[k]
+            mx.mxfp4_requant_from_nvfp4(c[a:b], s[a:b], g[a:b], mc[l, a:b], ms[l, a:b])
+        tl.mark("requant_all_layers")
+
+    def report(tot, steps):
+        t = tot["requant_all_layers"][0] / steps
+        b = sum(requant_bytes(bb - a, *shapes[k]) for _, k, a, bb in runs)
+        gbps = b / (t * 1e-3) / 1e9
+        roof = {"kernel": "requant", "bound": "hbm", "achieved": round(gbps, 1),
+                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                "traffic": recorded_traffic("requant_layer")}
+        cfg = {"workload": "layerwise load: 48 MoE layers x 128 experts x ([2048,4096] + "
+                           "[4096,1024]) NVFP4 -> MXFP4, 5% of tensors excluded",
+               "tensors_requantized": n_tensors, "launches": len(runs)}
+        return gbps, "GB/s", roof, {"ms_all_layers": round(t, 3)}, cfg
+
+    return step, report, None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this path has no multi-GPU mode "
+              f"(--gpus {args.gpus} requested). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU", file=sys.stderr)
+        sys.exit(2)
+    import synth
+    import w4a4_mxfp4_gemm_amd as mx
+
+    make = {"decode": decode_workload, "prefill": prefill_workload, "moe": moe_workload,
+            "layerwise": layerwise_workload}[args.workload]
+    step, report, cpu_baseline = make(torch, mx, synth)
+    torch.cuda.synchronize()
+    warm = Timeline(torch)
+    for _ in range(args.warmup):
+        step(warm)
+    torch.cuda.synchronize()
+
+    tl = Timeline(torch)
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for _ in range(args.steps):
+        step(tl)
+    t_end.record()
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    value, unit, roof, extra, cfg = report(tl.totals(), args.steps)
+
+    out = {"metric": METRIC, "value": round(value, 4), "unit": unit, "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(total_ms / args.steps, 4), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "mxfp4 (e2m1 x e8m0, fp32 acc)",
+           "data": "synthetic (seeded; NVFP4 weights from bf16 N(0,0.02), bf16 activations "
+                   "N(0,1) with 1% outlier channels x50)",
+           "config": cfg, "roofline": roof, **extra,
+           "kernel_source_digest": kernel_source_digest()}
+    if cpu_baseline is not None and not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

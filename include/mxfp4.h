@@ -1,0 +1,158 @@
+/*
+ * mxfp4.h -- C ABI of the MI355X (gfx950) block-scaled 4-bit linear-layer
+ * library: NVFP4 -> MXFP4 weight requant, dynamic MXFP4 activation
+ * quantization, and the MXFP4 x MXFP4 GEMM (dense and grouped by expert).
+ *
+ * Formats (shared by every call):
+ *   E2M1 code   4 bits: sign | 2-bit exponent (bias 1) | 1-bit mantissa;
+ *               magnitudes {0, 0.5, 1, 1.5, 2, 3, 4, 6}.  Two codes per
+ *               byte, the even K-index in bits 3:0, the odd one in bits 7:4.
+ *   MXFP4       codes [rows][K/2] u8 plus one E8M0 scale byte per 32
+ *               consecutive K-elements, [rows][K/32] u8, value 2^(b-127),
+ *               0xFF = NaN (vLLM-Omni "W4A4 MXFP4 Quantization", Overview;
+ *               "Validation and Notes": raw uint8 scale bytes).
+ *   NVFP4       codes [rows][K/2] u8 plus one float8_e4m3fn scale per 16
+ *               K-elements, [rows][K/16] u8, plus one fp32 per-tensor scale
+ *               (AMD blog "Efficiently Serving NVFP4 Models on AMD Instinct
+ *               MI350X/MI355X ...", introduction; SGLang FP4 post, sections
+ *               3-4: weight_packed / weight_scale / weight_global_scale).
+ *
+ * Conventions:
+ *   - Every tensor pointer is a DEVICE pointer to row-major memory owned by
+ *     the caller.  The library never allocates, frees or synchronises; all
+ *     work is enqueued on `stream`.  It keeps no global state.
+ *   - Every call returns MXFP4_OK or a negative mxfp4_status.  Arguments are
+ *     checked before anything is enqueued; on an error nothing is launched.
+ *   - K must be a positive multiple of 32 (whole MX blocks).  A zero row
+ *     count (M == 0, total_M == 0, T == 0) is a no-op returning MXFP4_OK.
+ *   - Code pointers (u8 [rows][K/2]) and bf16 activation pointers must be
+ *     16-byte aligned; scale pointers have no alignment requirement; fp32
+ *     outputs must be 4-byte and bf16 outputs 2-byte aligned.
+ *   - Results are bitwise reproducible from run to run (no atomics, fixed
+ *     reduction order).
+ */
+#ifndef MXFP4_H
+#define MXFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MXFP4_OK = 0,
+    MXFP4_EINVAL = -1,       /* bad size, null pointer, unknown flag/dtype    */
+    MXFP4_EALIGN = -2,       /* a pointer or leading dimension misaligned     */
+    MXFP4_EUNSUPPORTED = -3, /* valid request this build does not implement   */
+    MXFP4_EHIP = -4          /* the HIP runtime refused a launch              */
+} mxfp4_status;
+
+enum { MXFP4_OUT_BF16 = 0, MXFP4_OUT_FP32 = 1 };        /* out_dtype            */
+enum { MXFP4_REQ_INTERMEDIATE_BF16 = 1u << 0 };         /* requant flags        */
+
+/*
+ * NVFP4 -> MXFP4 requant of T same-shape weight tensors, the load-time step
+ * of the AMD blog's pipeline section (Figure 1): dequantize, quantize to
+ * MXFP4, write into a preallocated destination.  Per element the NVFP4 value
+ * is v = fl32(fl32(e2m1(code) * e4m3(scale16)) * nv_global[t]) (one fp32
+ * rounding; the product code*scale is exact), rounded once more to bf16 (RNE)
+ * when MXFP4_REQ_INTERMEDIATE_BF16 is set.  Each 32-element block along K
+ * (NVFP4 blocks 2j and 2j+1) is then quantized by the OCP MX rule (vLLM-Omni
+ * guide, "Single-Scale Block Scaling", setting 0): scale byte =
+ * floor(log2 amax) - 2 + 127 clamped to [0, 254]; codes = round-half-to-even
+ * of v / 2^(byte-127) onto E2M1, saturating at +-6, sign kept.  A block
+ * holding a NaN or Inf gets scale 0xFF and all-zero codes.
+ *
+ *   nv_codes   [T][N][K/2]  u8, device, read        (16-byte aligned)
+ *   nv_scales  [T][N][K/16] u8 (float8_e4m3fn bits), device, read
+ *   nv_global  [T] fp32, device, read: the multiplier applied on dequant
+ *              (a checkpoint that stores a divisor passes its reciprocal)
+ *   mx_codes   [T][N][K/2]  u8, device, written     (16-byte aligned)
+ *   mx_scales  [T][N][K/32] u8 (E8M0 bits), device, written
+ *   flags      0 or MXFP4_REQ_INTERMEDIATE_BF16
+ * Tensors a loader keeps in high precision are simply not passed (the blog's
+ * note on producer excludes).  Source and destination must not overlap.
+ */
+int mxfp4_requant_from_nvfp4(const uint8_t* nv_codes, const uint8_t* nv_scales,
+                             const float* nv_global, int64_t T, int64_t N, int64_t K,
+                             uint8_t* mx_codes, uint8_t* mx_scales,
+                             uint32_t flags, hipStream_t stream);
+
+/*
+ * Dynamic per-call MXFP4 quantization of bf16 activations (AMD blog, closing
+ * list: activations are quantized for each batch, no stored scales).  Row i
+ * of the output is the OCP MX quantization (rule as above, amax over the 32
+ * bf16 values of each block) of input row row_index[i], or of row i when
+ * row_index is NULL (the gather serves expert-sorted MoE inputs).
+ *
+ *   x_bf16     [*][ldx] bf16, device, read; ldx >= K, ldx % 8 == 0,
+ *              16-byte aligned.  Only the first K columns are read.
+ *   row_index  [M] int32, device, read, or NULL.  Every entry must index an
+ *              existing row of x (not checked: reading it would need a sync).
+ *   codes      [M][K/2] u8, device, written   (16-byte aligned)
+ *   scales     [M][K/32] u8, device, written
+ *   flags      must be 0
+ */
+int mxfp4_quantize_act(const void* x_bf16, int64_t ldx, const int32_t* row_index,
+                       int64_t M, int64_t K, uint8_t* codes, uint8_t* scales,
+                       uint32_t flags, hipStream_t stream);
+
+/*
+ * Y = A * B^T over MXFP4 operands with fp32 accumulation on gfx950's
+ * block-scaled MFMA (AMD blog, closing list: both operands MXFP4, no
+ * separate dequantize step).  y[m][n] = sum_k A[m,k] * B[n,k] where
+ * A[m,k] = e2m1 * 2^(a_scale - 127), likewise B.  Both operands are K-major.
+ *
+ *   a_codes, a_scales   [M][K/2], [M][K/32] u8, device, read
+ *   b_codes, b_scales   [N][K/2], [N][K/32] u8, device, read
+ *   y                   [M][N] bf16 (MXFP4_OUT_BF16, RNE of the fp32
+ *                       accumulator) or fp32 (MXFP4_OUT_FP32), device, written
+ *   workspace           reserved: the current kernels need none; pass NULL
+ *                       and 0 (mxfp4_gemm_workspace_size returns 0)
+ *   flags               must be 0
+ */
+int mxfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
+               const uint8_t* b_codes, const uint8_t* b_scales,
+               int64_t M, int64_t N, int64_t K, void* y, int out_dtype,
+               void* workspace, size_t workspace_bytes,
+               uint32_t flags, hipStream_t stream);
+
+/*
+ * Grouped GEMM for MoE experts (AMD blog, closing list: MoE experts run on
+ * MXFP4 kernels).  For each expert e and each row r in [offsets[e],
+ * offsets[e+1]): y[r][:] = A[r] * B_e^T.  A is expert-sorted.
+ *
+ *   a_codes, a_scales   [total_M][K/2], [total_M][K/32] u8, device, read
+ *   b_codes, b_scales   [E][N][K/2], [E][N][K/32] u8, device, read
+ *   offsets             [E+1] int32, device, read: non-decreasing,
+ *                       offsets[0] = 0, offsets[E] = total_M.  Empty experts
+ *                       are allowed.  The table is not checked on the host;
+ *                       the kernel clamps every row range to [0, total_M), so
+ *                       a bad table can give wrong rows but never a write
+ *                       outside y.
+ *   y                   [total_M][N] bf16 or fp32, device, written
+ *   workspace, flags    as for mxfp4_gemm
+ */
+int mxfp4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
+                       const uint8_t* b_codes, const uint8_t* b_scales,
+                       const int32_t* offsets, int64_t E, int64_t total_M,
+                       int64_t N, int64_t K, void* y, int out_dtype,
+                       void* workspace, size_t workspace_bytes,
+                       uint32_t flags, hipStream_t stream);
+
+/* Workspace bytes mxfp4_gemm / mxfp4_grouped_gemm need (currently 0). */
+size_t mxfp4_gemm_workspace_size(int64_t M, int64_t N, int64_t K);
+
+/* Static description of a status code; never NULL. */
+const char* mxfp4_status_string(int status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int mxfp4_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

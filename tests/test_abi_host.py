@@ -1,0 +1,107 @@
+"""Host-side checks of the C-ABI library: it loads without a GPU, exports every
+function include/mxfp4.h declares, and rejects malformed arguments before
+anything would be launched.  No compute call is made."""
+import ctypes
+import pathlib
+import re
+
+import pytest
+
+ROOT = pathlib.Path(__file__).resolve().parent.parent
+HEADER = ROOT / "include" / "mxfp4.h"
+
+
+def declared_functions():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mxfp4_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import w4a4_mxfp4_gemm_amd as m
+    return m.library()
+
+
+def test_header_declares_the_four_calls():
+    names = declared_functions()
+    for n in ("mxfp4_requant_from_nvfp4", "mxfp4_quantize_act", "mxfp4_gemm",
+              "mxfp4_grouped_gemm"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    import w4a4_mxfp4_gemm_amd as m
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert name in m.EXPORTED_SYMBOLS
+    assert m.LIBRARY_PATH.exists()
+
+
+def test_status_strings_and_version(lib):
+    import w4a4_mxfp4_gemm_amd as m
+    for s in (0, -1, -2, -3, -4, 7):
+        assert isinstance(m.mxfp4_status_string(s), str) and m.mxfp4_status_string(s)
+    assert m.mxfp4_version() >= 100
+    assert m.mxfp4_gemm_workspace_size(64, 12288, 4096) == 0
+
+
+# Arguments that are rejected before any HIP call (so these run without a GPU).
+FAKE = 0x1000            # 16-byte aligned, never dereferenced
+ODD = 0x1001
+
+
+def call_gemm(lib, **kw):
+    a = dict(a=FAKE, sa=FAKE, b=FAKE, sb=FAKE, M=16, N=16, K=64, y=FAKE, dt=0,
+             ws=None, wsb=0, flags=0)
+    a.update(kw)
+    return lib.mxfp4_gemm(a["a"], a["sa"], a["b"], a["sb"], a["M"], a["N"], a["K"], a["y"],
+                          a["dt"], a["ws"], a["wsb"], a["flags"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=48), -1), (dict(K=0), -1), (dict(K=-32), -1), (dict(N=0), -1), (dict(M=-1), -1),
+    (dict(dt=2), -1), (dict(flags=1), -1), (dict(wsb=64), -1), (dict(a=None), -1),
+    (dict(y=None), -1), (dict(a=ODD), -2), (dict(b=ODD), -2), (dict(y=ODD), -2),
+    (dict(M=0), 0),
+])
+def test_gemm_argument_checks(lib, kw, status):
+    assert call_gemm(lib, **kw) == status
+
+
+def test_grouped_gemm_argument_checks(lib):
+    f = lib.mxfp4_grouped_gemm
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, 4, 64, 32, 64, FAKE, 0, None, 0, 0, None]
+    bad_e = list(args); bad_e[5] = 0
+    assert f(*bad_e) == -1
+    no_off = list(args); no_off[4] = None
+    assert f(*no_off) == -1
+    odd_off = list(args); odd_off[4] = ODD
+    assert f(*odd_off) == -2
+    empty = list(args); empty[6] = 0
+    assert f(*empty) == 0
+    badk = list(args); badk[8] = 40
+    assert f(*badk) == -1
+
+
+def test_quantize_act_argument_checks(lib):
+    f = lib.mxfp4_quantize_act
+    assert f(FAKE, 32, None, 4, 64, FAKE, FAKE, 0, None) == -1           # ldx < K
+    assert f(FAKE, 64, None, 4, 48, FAKE, FAKE, 0, None) == -1           # K % 32
+    assert f(FAKE, 64, None, 4, 64, FAKE, FAKE, 1, None) == -1           # flags
+    assert f(FAKE, 68, None, 4, 64, FAKE, FAKE, 0, None) == -2           # ldx % 8
+    assert f(ODD, 64, None, 4, 64, FAKE, FAKE, 0, None) == -2            # x alignment
+    assert f(FAKE, 64, ODD, 4, 64, FAKE, FAKE, 0, None) == -2            # row_index
+    assert f(None, 64, None, 4, 64, FAKE, FAKE, 0, None) == -1
+    assert f(FAKE, 64, None, 0, 64, FAKE, FAKE, 0, None) == 0            # M == 0
+
+
+def test_requant_argument_checks(lib):
+    f = lib.mxfp4_requant_from_nvfp4
+    assert f(FAKE, FAKE, FAKE, 1, 16, 48, FAKE, FAKE, 0, None) == -1     # K % 32
+    assert f(FAKE, FAKE, FAKE, 1, 16, 64, FAKE, FAKE, 2, None) == -1     # flags
+    assert f(FAKE, FAKE, FAKE, 1, 0, 64, FAKE, FAKE, 0, None) == -1      # N
+    assert f(None, FAKE, FAKE, 1, 16, 64, FAKE, FAKE, 0, None) == -1
+    assert f(ODD, FAKE, FAKE, 1, 16, 64, FAKE, FAKE, 0, None) == -2
+    assert f(FAKE, ODD, FAKE, 1, 16, 64, FAKE, FAKE, 0, None) == -2      # u16 scale loads
+    assert f(FAKE, FAKE, FAKE, 0, 16, 64, FAKE, FAKE, 0, None) == 0      # T == 0

@@ -1,0 +1,258 @@
+"""GPU parity of the MXFP4 GEMM calls against the CPU oracle.
+
+Bar: fp32 output within 1e-5 * sum_k |a_k b_k| per element; bf16 output at
+most one bf16 ulp (ordered-bit distance) from the oracle's exact result
+rounded to bf16.  Operands of the dense/grouped pipelines are produced on each
+side by that side's own requant / act-quant from the same seeded inputs."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import (Guarded, assert_gemm_bf16, assert_gemm_fp32, bf16_bits, dev, f32, say,
+                      u8)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mx():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import w4a4_mxfp4_gemm_amd as m
+    return m
+
+
+def to_dev(*ts):
+    return [t.to(dev()) if isinstance(t, torch.Tensor) else torch.from_numpy(t).to(dev())
+            for t in ts]
+
+
+# ---- random operands, every tile edge ------------------------------------------------
+SHAPES = [(1, 1, 32), (1, 300, 4096), (7, 17, 96), (16, 256, 512), (33, 200, 544),
+          (64, 129, 1024), (65, 260, 1056), (100, 64, 4096), (130, 131, 2080)]
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_gemm_random_operands_fp32(mx, M, N, K):
+    say(f"gemm random M={M} N={N} K={K}")
+    a, sa = synth.canonical_mxfp4(M, K, seed=M * 7 + K)
+    b, sb = synth.canonical_mxfp4(N, K, seed=N * 11 + K + 1)
+    y, s = oracle.gemm(u8(a), u8(sa), u8(b), u8(sb))
+    A, SA, B, SB = to_dev(a, sa, b, sb)
+    gy = Guarded((M, N), torch.float32)
+    mx.mxfp4_gemm(A, SA, B, SB, gy.view)
+    yb = mx.mxfp4_gemm(A, SA, B, SB, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert gy.intact(), "write outside y"
+    assert_gemm_fp32(gy.view, y, s, f"{M}x{N}x{K}")
+    # the bf16 epilogue is the RNE of the same fp32 accumulator
+    assert np.array_equal(bf16_bits(yb), bf16_bits(gy.view.to(torch.bfloat16)))
+
+
+def test_gemm_wide_scale_range(mx):
+    """E8M0 bytes over most of the range that keeps products fp32-normal."""
+    say("gemm wide scale range")
+    M, N, K = 40, 72, 512
+    a, sa = synth.canonical_mxfp4(M, K, seed=1, scale_lo=64, scale_hi=190)
+    b, sb = synth.canonical_mxfp4(N, K, seed=2, scale_lo=64, scale_hi=190)
+    y, s = oracle.gemm(u8(a), u8(sa), u8(b), u8(sb))
+    A, SA, B, SB = to_dev(a, sa, b, sb)
+    out = mx.mxfp4_gemm(A, SA, B, SB, out_dtype=torch.float32)
+    assert_gemm_fp32(out, y, s, "wide scales")
+
+
+def test_gemm_deterministic_and_finite(mx):
+    say("gemm determinism / finiteness over mixed M")
+    K, N = 1024, 384
+    b, sb = synth.canonical_mxfp4(N, K, seed=5)
+    B, SB = to_dev(b, sb)
+    for M in (1, 3, 16, 31, 64, 65, 200):
+        a, sa = synth.canonical_mxfp4(M, K, seed=M)
+        A, SA = to_dev(a, sa)
+        y1 = mx.mxfp4_gemm(A, SA, B, SB, out_dtype=torch.float32)
+        y2 = mx.mxfp4_gemm(A, SA, B, SB, out_dtype=torch.float32)
+        assert torch.equal(y1, y2)
+        assert torch.isfinite(y1).all()
+
+
+# ---- the pipeline: requant + act-quant + GEMM on each side ------------------------------
+def pipeline_weight(N, K, seed):
+    """NVFP4 weight from bf16 N(0, 0.02); GPU requant on the device, oracle requant
+    on the host, each from the same NVFP4 bytes."""
+    w = synth.bf16_normal((N, K), 0.02, seed=seed)
+    codes, scales, g = synth.nvfp4_from_bf16(w)
+    oc, os_ = oracle.requant(u8(codes), u8(scales), np.atleast_1d(g.numpy()))
+    return (codes, scales, g), (oc, os_)
+
+
+def gpu_weight(mx, nv):
+    codes, scales, g = nv
+    C, S, G = to_dev(codes, scales, g.reshape(1))
+    return mx.mxfp4_requant_from_nvfp4(C, S, G)
+
+
+@pytest.fixture(scope="module")
+def decode_weight(mx):
+    say("building decode weight [12288,4096] seed 11")
+    nv, (oc, os_) = pipeline_weight(12288, 4096, seed=11)
+    wc, ws = gpu_weight(mx, nv)
+    return (wc, ws), (oc, os_)
+
+
+def test_gemm_tiny_pipeline(mx):
+    say("tiny pipeline 16x256x512")
+    nv, (oc, os_) = pipeline_weight(256, 512, seed=1)
+    wc, ws = gpu_weight(mx, nv)
+    x = synth.activations(16, 512, seed=2)
+    xc, xs = mx.mxfp4_quantize_act(x.to(dev()))
+    yg = mx.mxfp4_gemm(xc, xs, wc, ws, out_dtype=torch.bfloat16)
+    ac, as_ = oracle.quantize_act(bf16_bits(x))
+    y, s = oracle.gemm(ac, as_, oc, os_)
+    assert_gemm_bf16(yg, y, "tiny bf16")
+    yf = mx.mxfp4_gemm(xc, xs, wc, ws, out_dtype=torch.float32)
+    assert_gemm_fp32(yf, y, s, "tiny fp32")
+
+
+@pytest.mark.parametrize("M", [1, 8, 32, 64])
+def test_gemm_decode_pipeline_full(mx, decode_weight, M):
+    say(f"decode pipeline M={M} N=12288 K=4096 (all outputs)")
+    (wc, ws), (oc, os_) = decode_weight
+    x = synth.activations(64, 4096, seed=12, outlier_seed=13)[:M].contiguous()
+    xc, xs = mx.mxfp4_quantize_act(x.to(dev()))
+    yg = mx.mxfp4_gemm(xc, xs, wc, ws, out_dtype=torch.bfloat16)
+    yf = mx.mxfp4_gemm(xc, xs, wc, ws, out_dtype=torch.float32)
+    ac, as_ = oracle.quantize_act(bf16_bits(x))
+    y, s = oracle.gemm(ac, as_, oc, os_)
+    assert_gemm_bf16(yg, y, f"decode M={M} bf16")
+    assert_gemm_fp32(yf, y, s, f"decode M={M} fp32")
+
+
+def sample_positions(M, N, seed, n_random=3000):
+    rng = np.random.default_rng(seed)
+    pm = [rng.integers(0, M, n_random)]
+    pn = [rng.integers(0, N, n_random)]
+    for m in (0, 1, 15, 16, 127, 128, 255, 256, M - 1):       # whole rows at tile edges
+        cols = np.unique(np.concatenate([np.arange(0, min(N, 300)), rng.integers(0, N, 200),
+                                         [N - 1]]))
+        pm.append(np.full(cols.size, m))
+        pn.append(cols)
+    return np.concatenate(pm), np.concatenate(pn)
+
+
+@pytest.mark.parametrize("N,K,wseed,xseed,oseed", [(4096, 4096, 21, 24, 26),
+                                                   (28672, 4096, 22, 24, 26),
+                                                   (4096, 14336, 23, 25, 27)])
+def test_gemm_prefill_pipeline_sampled(mx, N, K, wseed, xseed, oseed):
+    M = 4096
+    say(f"prefill pipeline M={M} N={N} K={K} (sampled outputs)")
+    nv, (oc, os_) = pipeline_weight(N, K, seed=wseed)
+    wc, ws = gpu_weight(mx, nv)
+    x = synth.activations(M, K, seed=xseed, outlier_seed=oseed)
+    xc, xs = mx.mxfp4_quantize_act(x.to(dev()))
+    yg = mx.mxfp4_gemm(xc, xs, wc, ws, out_dtype=torch.bfloat16)
+    ac, as_ = oracle.quantize_act(bf16_bits(x))
+    pm, pn = sample_positions(M, N, seed=N + K)
+    y, s = oracle.gemm_at(ac, as_, oc, os_, pm, pn)
+    got = bf16_bits(yg)[pm, pn]
+    ok = oracle.gemm_bf16_ok(got, y)
+    assert ok.all(), f"{int((~ok).sum())} of {ok.size} sampled outputs off by >1 bf16 ulp"
+    assert torch.isfinite(yg.float()).all()
+
+
+# ---- grouped GEMM -------------------------------------------------------------------
+def test_grouped_gemm_ragged_and_empty_experts(mx):
+    say("grouped gemm ragged/empty experts")
+    E, N, K = 6, 72, 544
+    counts = np.array([5, 0, 37, 1, 0, 70])
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    M = int(offsets[-1])
+    a, sa = synth.canonical_mxfp4(M, K, seed=1)
+    b, sb = synth.canonical_mxfp4(E * N, K, seed=2)
+    b, sb = b.reshape(E, N, K // 2), sb.reshape(E, N, K // 32)
+    y, s = oracle.grouped_gemm(u8(a), u8(sa), u8(b), u8(sb), offsets)
+    A, SA, B, SB, OFF = to_dev(a, sa, b, sb, offsets)
+    gy = Guarded((M, N), torch.float32)
+    mx.mxfp4_grouped_gemm(A, SA, B, SB, OFF, gy.view)
+    torch.cuda.synchronize()
+    assert gy.intact()
+    assert_gemm_fp32(gy.view, y, s, "grouped")
+
+
+def test_grouped_gemm_bad_offsets_stay_inside_y(mx):
+    """A malformed offset table (decreasing, negative, past total_M) may give wrong
+    rows, but the kernel clamps every range: nothing outside y is written."""
+    say("grouped gemm malformed offsets")
+    E, N, K, M = 4, 32, 64, 50
+    a, sa = synth.canonical_mxfp4(M, K, seed=3)
+    b, sb = synth.canonical_mxfp4(E * N, K, seed=4)
+    A, SA, B, SB = to_dev(a, sa, b.reshape(E, N, K // 2), sb.reshape(E, N, K // 32))
+    for table in ([0, 60, 10, -5, 50], [-100, 0, 1000, 20, 50], [0, 0, 0, 0, 0]):
+        OFF = torch.tensor(table, dtype=torch.int32, device=dev())
+        gy = Guarded((M, N), torch.float32)
+        mx.mxfp4_grouped_gemm(A, SA, B, SB, OFF, gy.view)
+        torch.cuda.synchronize()
+        assert gy.intact(), table
+
+
+@pytest.fixture(scope="module")
+def moe_setup(mx):
+    """MoE layer: 128 experts, gate_up [2048,4096], down [4096,1024], 2048 tokens,
+    top-8 softmax routing.  Weights are generated, NVFP4-encoded and requantized
+    on the GPU; the oracle side rebuilds the sampled experts on the host."""
+    say("building MoE layer (128 experts)")
+    E, T, TOPK = 128, 2048, 8
+    d = dev()
+    perm, offsets = synth.route_topk(T, E, TOPK, seed=34)
+    tokens = synth.activations(T, 4096, seed=33)
+    down_in = synth.activations(T * TOPK, 1024, seed=35)
+    nv = {}
+    mxw = {}
+    for name, (N, K), seed in (("gate_up", (2048, 4096), 31), ("down", (4096, 1024), 32)):
+        codes = torch.empty((E, N, K // 2), dtype=torch.uint8, device=d)
+        scales = torch.empty((E, N, K // 16), dtype=torch.uint8, device=d)
+        gs = torch.empty((E,), dtype=torch.float32, device=d)
+        for e in range(E):
+            w = synth.bf16_normal((N, K), 0.02, seed=seed * 1000 + e, device=d)
+            c, s, g = synth.nvfp4_from_bf16(w)
+            codes[e], scales[e], gs[e] = c, s, g
+        nv[name] = (codes, scales, gs)
+        mxw[name] = mx.mxfp4_requant_from_nvfp4(codes, scales, gs)
+    torch.cuda.synchronize()
+    return dict(perm=perm, offsets=offsets, tokens=tokens, down_in=down_in, nv=nv, mxw=mxw)
+
+
+@pytest.mark.parametrize("which", ["gate_up", "down"])
+def test_grouped_gemm_moe_pipeline_sampled(mx, moe_setup, which):
+    say(f"MoE pipeline {which} (sampled experts)")
+    st = moe_setup
+    perm, offsets = st["perm"], st["offsets"]
+    codes, scales, gs = st["nv"][which]
+    wc, ws = st["mxw"][which]
+    E = codes.shape[0]
+    if which == "gate_up":
+        x, ri = st["tokens"], perm
+    else:
+        x, ri = st["down_in"], None
+    xc, xs = mx.mxfp4_quantize_act(x.to(dev()), row_index=None if ri is None else ri.to(dev()))
+    yg = mx.mxfp4_grouped_gemm(xc, xs, wc, ws, offsets.to(dev()), out_dtype=torch.bfloat16)
+    ybits = bf16_bits(yg)
+    ac, as_ = oracle.quantize_act(bf16_bits(x), row_index=None if ri is None else ri.numpy())
+    off = offsets.numpy()
+    rng = np.random.default_rng(7)
+    experts = sorted(set(rng.choice(E, 10, replace=False).tolist()) | {0, E - 1})
+    N = codes.shape[1]
+    for e in experts:
+        r0, r1 = int(off[e]), int(off[e + 1])
+        if r1 == r0:
+            continue
+        oc, os_ = oracle.requant(u8(codes[e]), u8(scales[e]), np.atleast_1d(u8(gs[e:e + 1])))
+        rows = np.unique(np.concatenate([[r0, r1 - 1], rng.integers(r0, r1, 4)]))
+        pm = np.repeat(rows - r0, N)
+        pn = np.tile(np.arange(N), rows.size)
+        y, _ = oracle.gemm_at(ac[r0:r1], as_[r0:r1], oc, os_, pm, pn)
+        got = ybits[np.repeat(rows, N), pn]
+        ok = oracle.gemm_bf16_ok(got, y)
+        assert ok.all(), f"{which} expert {e}: {int((~ok).sum())} outputs off by >1 bf16 ulp"
+    assert torch.isfinite(yg.float()).all()

@@ -1,0 +1,218 @@
+"""GPU parity of the two quantization calls against the CPU oracle: every code
+byte and every scale byte must match exactly."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import Guarded, bf16_bits, dev, oracle_requant_from_bf16, say, u8
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mx():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import w4a4_mxfp4_gemm_amd as m
+    return m
+
+
+def act_quant_both(mx, x_cpu, row_index=None, K=None):
+    """GPU and oracle act-quant of the same bf16 input; canary-guarded outputs."""
+    xg = x_cpu.to(dev())
+    M = x_cpu.shape[0] if row_index is None else row_index.shape[0]
+    K = x_cpu.shape[1] if K is None else K
+    gc = Guarded((M, K // 2), torch.uint8)
+    gs = Guarded((M, K // 32), torch.uint8)
+    ri = None if row_index is None else torch.from_numpy(row_index).to(dev())
+    mx.mxfp4_quantize_act(xg, gc.view, gs.view, row_index=ri, K=K)
+    torch.cuda.synchronize()
+    assert gc.intact() and gs.intact(), "write outside the output"
+    oc, os_ = oracle.quantize_act(bf16_bits(x_cpu), K=K, row_index=row_index)
+    return (u8(gc.view), u8(gs.view)), (oc, os_)
+
+
+def assert_same(gpu, ref, what):
+    (gc, gs), (oc, os_) = gpu, ref
+    if not np.array_equal(gs, os_):
+        i = tuple(np.argwhere(gs != os_)[0])
+        raise AssertionError(f"{what}: scale byte mismatch at {i}: gpu {gs[i]} oracle {os_[i]}")
+    if not np.array_equal(gc, oc):
+        i = tuple(np.argwhere(gc != oc)[0])
+        raise AssertionError(f"{what}: code byte mismatch at {i}: gpu {gc[i]:#04x} "
+                             f"oracle {oc[i]:#04x}")
+
+
+# ---- activation quantization --------------------------------------------------
+def test_act_quant_tiny(mx):
+    say("act_quant tiny [16,512] seed 2")
+    x = synth.activations(16, 512, seed=2)
+    g, o = act_quant_both(mx, x)
+    assert_same(g, o, "tiny")
+
+
+@pytest.mark.parametrize("M,K", [(1, 32), (37, 544), (5, 4096), (64, 4096)])
+def test_act_quant_ragged_with_outliers(mx, M, K):
+    say(f"act_quant M={M} K={K} with outliers")
+    x = synth.activations(M, K, seed=12, outlier_seed=13)
+    g, o = act_quant_both(mx, x)
+    assert_same(g, o, f"M={M} K={K}")
+
+
+def test_act_quant_gather_and_wide_rows(mx):
+    say("act_quant gather, ldx > K")
+    x = synth.activations(50, 1024, seed=3, outlier_seed=4)
+    rng = np.random.default_rng(0)
+    idx = rng.integers(0, 50, size=131).astype(np.int32)
+    g, o = act_quant_both(mx, x, row_index=idx)
+    assert_same(g, o, "gather")
+    g, o = act_quant_both(mx, x, K=512)
+    assert_same(g, o, "ldx>K")
+
+
+def test_act_quant_special_values(mx):
+    say("act_quant NaN/Inf/subnormal/ties")
+    rng = np.random.default_rng(1)
+    K = 256
+    bits = (rng.integers(0, 2 ** 16, size=(64, K), dtype=np.uint32)).astype(np.uint16)
+    # rows 0-7: random bit patterns (NaN, Inf, subnormals all appear)
+    # rows 8-15: subnormal-only blocks; rows 16-23: zeros of both signs
+    bits[8:16] = rng.integers(0, 0x80, size=(8, K)).astype(np.uint16) | \
+        (rng.integers(0, 2, size=(8, K)).astype(np.uint16) << 15)
+    bits[16:24] = rng.choice(np.array([0, 0x8000], dtype=np.uint16), size=(8, K))
+    # rows 24-31: exact E2M1 tie points times powers of two
+    ties = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 4.0], dtype=np.float32)
+    for r in range(24, 32):
+        v = rng.choice(ties, size=K) * np.float32(2.0 ** rng.integers(-20, 20))
+        v[::32] = 4.0 * np.float32(2.0 ** rng.integers(-20, 20))
+        v *= rng.choice(np.array([-1, 1], dtype=np.float32), size=K)
+        bits[r] = (v.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    x = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16)
+    g, o = act_quant_both(mx, x)
+    assert_same(g, o, "specials")
+
+
+def exhaustive_encode_input():
+    """Every bf16 magnitude p (both signs) paired with every scale byte b it can
+    meet: blocks whose element 0 is the anchor 4 * 2^(b-127) and whose other 31
+    elements are bf16 values below 8 * 2^(b-127), so every block's amax lies in
+    [4, 8) * 2^(b-127) and its scale byte is b."""
+    vals = []
+    for b in range(0, 253):
+        anchor = (b + 2) << 7                            # bf16 bits of 2^(b-125)
+        mags = np.arange(0, (b + 3) << 7, dtype=np.uint32)
+        v = np.concatenate([mags, mags | 0x8000]).astype(np.uint16)
+        nblk = -(-v.size // 31)
+        pad = np.zeros(nblk * 31 - v.size, dtype=np.uint16)
+        body = np.concatenate([v, pad]).reshape(nblk, 31)
+        head = np.full((nblk, 1), anchor, dtype=np.uint16)
+        head[1::2] |= 0x8000
+        vals.append(np.concatenate([head, body], axis=1))
+    blocks = np.concatenate(vals)
+    per_row = 128
+    nrow = -(-blocks.shape[0] // per_row)
+    pad = np.zeros((nrow * per_row - blocks.shape[0], 32), dtype=np.uint16)
+    return np.concatenate([blocks, pad]).reshape(nrow, per_row * 32)
+
+
+def test_act_quant_exhaustive_encoder(mx):
+    say("act_quant exhaustive: all bf16 magnitudes x all scale bytes")
+    bits = exhaustive_encode_input()
+    x = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16)
+    g, o = act_quant_both(mx, x)
+    assert_same(g, o, "exhaustive")
+
+
+@pytest.mark.parametrize("M,K", [(4096, 4096), (4096, 14336)])
+def test_act_quant_prefill_full_size(mx, M, K):
+    say(f"act_quant prefill [{M},{K}] full compare")
+    x = synth.activations(M, K, seed=24 if K == 4096 else 25,
+                          outlier_seed=26 if K == 4096 else 27)
+    g, o = act_quant_both(mx, x)
+    assert_same(g, o, f"prefill {M}x{K}")
+
+
+def test_act_quant_deterministic(mx):
+    x = synth.activations(256, 4096, seed=5).to(dev())
+    c1, s1 = mx.mxfp4_quantize_act(x)
+    c2, s2 = mx.mxfp4_quantize_act(x)
+    assert torch.equal(c1, c2) and torch.equal(s1, s2)
+
+
+# ---- NVFP4 -> MXFP4 requant ------------------------------------------------------
+def requant_both(mx, codes, scales, g, bf16_intermediate=False):
+    T = 1 if codes.dim() == 2 else codes.shape[0]
+    N, K = codes.shape[-2], codes.shape[-1] * 2
+    shape_c = (T, N, K // 2) if codes.dim() == 3 else (N, K // 2)
+    shape_s = (T, N, K // 32) if codes.dim() == 3 else (N, K // 32)
+    gc = Guarded(shape_c, torch.uint8)
+    gs = Guarded(shape_s, torch.uint8)
+    mx.mxfp4_requant_from_nvfp4(codes.to(dev()), scales.to(dev()),
+                                g.reshape(-1).to(torch.float32).to(dev()),
+                                gc.view, gs.view, bf16_intermediate=bf16_intermediate)
+    torch.cuda.synchronize()
+    assert gc.intact() and gs.intact(), "write outside the destination"
+    oc, os_ = oracle.requant(u8(codes), u8(scales), g.reshape(-1).numpy().astype(np.float32),
+                             bf16_intermediate=bf16_intermediate)
+    return (u8(gc.view), u8(gs.view)), (oc.reshape(shape_c), os_.reshape(shape_s))
+
+
+@pytest.mark.parametrize("bf16_intermediate", [False, True])
+def test_requant_tiny(mx, bf16_intermediate):
+    say(f"requant tiny [256,512] seed 1 bf16={bf16_intermediate}")
+    w = synth.bf16_normal((256, 512), 0.02, seed=1)
+    codes, scales, g = synth.nvfp4_from_bf16(w)
+    gpu, ref = requant_both(mx, codes, scales, g, bf16_intermediate)
+    assert_same(gpu, ref, "tiny requant")
+
+
+@pytest.mark.parametrize("bf16_intermediate", [False, True])
+def test_requant_random_bytes_many_globals(mx, bf16_intermediate):
+    """Arbitrary NVFP4 bytes (every E4M3 byte incl. NaN and subnormals) under
+    global scales from 2^-140 to 2^120, so fp32 denormals, overflow to Inf and
+    NaN blocks all occur; ragged K (17 MX blocks)."""
+    say(f"requant random bytes T=12 N=37 K=544 bf16={bf16_intermediate}")
+    rng = np.random.default_rng(3)
+    T, N, K = 12, 37, 544
+    codes = torch.from_numpy(rng.integers(0, 256, size=(T, N, K // 2), dtype=np.uint8))
+    scales = torch.from_numpy(rng.integers(0, 256, size=(T, N, K // 16), dtype=np.uint8))
+    g = torch.tensor([2.0 ** e for e in (-140, -130, -126, -120, -60, -20, -7, 0, 3, 30, 100,
+                                         120)], dtype=torch.float32)
+    gpu, ref = requant_both(mx, codes, scales, g, bf16_intermediate)
+    assert_same(gpu, ref, "random requant")
+    g2 = torch.from_numpy(rng.uniform(1e-6, 1e-2, size=T).astype(np.float32))
+    gpu, ref = requant_both(mx, codes, scales, g2, bf16_intermediate)
+    assert_same(gpu, ref, "random requant, non-power-of-two g")
+
+
+def test_requant_decode_weight_full_size(mx):
+    say("requant W [12288,4096] seed 11 full compare")
+    w = synth.bf16_normal((12288, 4096), 0.02, seed=11)
+    codes, scales, g = synth.nvfp4_from_bf16(w)
+    gpu, ref = requant_both(mx, codes, scales, g)
+    assert_same(gpu, ref, "decode weight")
+
+
+def test_requant_layer_shaped_batch(mx):
+    """A batch of expert tensors of both MoE shapes, as the layerwise load
+    passes them (one call per shape, T tensors each)."""
+    for shape, seed in (((6, 2048, 4096), 41), ((6, 4096, 1024), 42)):
+        say(f"requant layer batch {shape}")
+        w = synth.bf16_normal(shape, 0.02, seed=seed)
+        codes, scales, g = synth.nvfp4_from_bf16(w)
+        gpu, ref = requant_both(mx, codes, scales, g)
+        assert_same(gpu, ref, f"layer batch {shape}")
+
+
+def test_requant_rerun_is_identical(mx):
+    """Re-running a layer's requant into the same destination gives identical
+    bytes (a reload can restart from any layer)."""
+    w = synth.bf16_normal((3, 512, 1024), 0.02, seed=7).to(dev())
+    codes, scales, g = synth.nvfp4_from_bf16(w)
+    c1, s1 = mx.mxfp4_requant_from_nvfp4(codes, scales, g.reshape(-1))
+    c2 = torch.full_like(c1, 0x5A)
+    s2 = torch.full_like(s1, 0x5A)
+    mx.mxfp4_requant_from_nvfp4(codes, scales, g.reshape(-1), c2, s2)
+    assert torch.equal(c1, c2) and torch.equal(s1, s2)

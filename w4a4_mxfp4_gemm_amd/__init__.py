@@ -1,0 +1,231 @@
+"""Python binding of the gfx950 MXFP4 library (``libmxfp4_cdna4.so``).
+
+The functions below carry the C ABI's names (``include/mxfp4.h``) and do
+argument marshalling only: torch tensors supply device memory, the current
+torch stream supplies the HIP stream, and every step of the computation runs
+in the library's HIP kernels.  There is no fallback: if the shared library is
+missing and cannot be built, importing this package raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import pathlib
+
+import torch
+
+_PKG = pathlib.Path(__file__).resolve().parent
+LIBRARY_PATH = _PKG / "libmxfp4_cdna4.so"
+
+MXFP4_OUT_BF16 = 0
+MXFP4_OUT_FP32 = 1
+MXFP4_REQ_INTERMEDIATE_BF16 = 1
+
+_STATUS_NAMES = {0: "MXFP4_OK", -1: "MXFP4_EINVAL", -2: "MXFP4_EALIGN",
+                 -3: "MXFP4_EUNSUPPORTED", -4: "MXFP4_EHIP"}
+
+
+class Mxfp4Error(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: {_STATUS_NAMES.get(status, status)} "
+                         f"({mxfp4_status_string(status)})")
+
+
+def _load_library() -> ctypes.CDLL:
+    if not LIBRARY_PATH.exists():
+        from . import build as _build
+        _build.build()
+    lib = ctypes.CDLL(str(LIBRARY_PATH))
+    P, I, U32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32, ctypes.c_size_t
+    lib.mxfp4_requant_from_nvfp4.argtypes = [P, P, P, I, I, I, P, P, U32, P]
+    lib.mxfp4_requant_from_nvfp4.restype = ctypes.c_int
+    lib.mxfp4_quantize_act.argtypes = [P, I, P, I, I, P, P, U32, P]
+    lib.mxfp4_quantize_act.restype = ctypes.c_int
+    lib.mxfp4_gemm.argtypes = [P, P, P, P, I, I, I, P, ctypes.c_int, P, SZ, U32, P]
+    lib.mxfp4_gemm.restype = ctypes.c_int
+    lib.mxfp4_grouped_gemm.argtypes = [P, P, P, P, P, I, I, I, I, P, ctypes.c_int, P, SZ, U32, P]
+    lib.mxfp4_grouped_gemm.restype = ctypes.c_int
+    lib.mxfp4_gemm_workspace_size.argtypes = [I, I, I]
+    lib.mxfp4_gemm_workspace_size.restype = SZ
+    lib.mxfp4_status_string.argtypes = [ctypes.c_int]
+    lib.mxfp4_status_string.restype = ctypes.c_char_p
+    lib.mxfp4_version.argtypes = []
+    lib.mxfp4_version.restype = ctypes.c_int
+    return lib
+
+
+_lib = _load_library()
+
+EXPORTED_SYMBOLS = ("mxfp4_requant_from_nvfp4", "mxfp4_quantize_act", "mxfp4_gemm",
+                    "mxfp4_grouped_gemm", "mxfp4_gemm_workspace_size",
+                    "mxfp4_status_string", "mxfp4_version")
+
+
+def library() -> ctypes.CDLL:
+    return _lib
+
+
+def mxfp4_status_string(status: int) -> str:
+    return _lib.mxfp4_status_string(int(status)).decode()
+
+
+def mxfp4_version() -> int:
+    return int(_lib.mxfp4_version())
+
+
+def mxfp4_gemm_workspace_size(M: int, N: int, K: int) -> int:
+    return int(_lib.mxfp4_gemm_workspace_size(M, N, K))
+
+
+# ---- marshalling helpers -------------------------------------------------------
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t, name, dtype, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check(fn, status):
+    if status != 0:
+        raise Mxfp4Error(fn, status)
+
+
+# ---- the four calls ---------------------------------------------------------------
+def mxfp4_requant_from_nvfp4(nv_codes, nv_scales, nv_global, mx_codes=None, mx_scales=None,
+                             *, bf16_intermediate=False, stream=None):
+    """NVFP4 ([T,]N,K/2 codes, [T,]N,K/16 E4M3 bytes, fp32 global [T]) -> MXFP4
+    ([T,]N,K/2 codes, [T,]N,K/32 E8M0 bytes), written into mx_codes/mx_scales
+    (allocated when None).  Returns (mx_codes, mx_scales)."""
+    _need(nv_codes, "nv_codes", torch.uint8)
+    dev = nv_codes.device
+    _need(nv_scales, "nv_scales", torch.uint8, dev)
+    _need(nv_global, "nv_global", torch.float32, dev)
+    lead = nv_codes.shape[:-2]
+    N, K = nv_codes.shape[-2], nv_codes.shape[-1] * 2
+    T = int(torch.tensor(lead).prod().item()) if len(lead) else 1
+    if nv_scales.shape != (*lead, N, K // 16):
+        raise ValueError(f"nv_scales shape {tuple(nv_scales.shape)} != {(*lead, N, K // 16)}")
+    if nv_global.numel() != T:
+        raise ValueError(f"nv_global has {nv_global.numel()} entries, expected {T}")
+    if mx_codes is None:
+        mx_codes = torch.empty((*lead, N, K // 2), dtype=torch.uint8, device=dev)
+    if mx_scales is None:
+        mx_scales = torch.empty((*lead, N, K // 32), dtype=torch.uint8, device=dev)
+    _need(mx_codes, "mx_codes", torch.uint8, dev)
+    _need(mx_scales, "mx_scales", torch.uint8, dev)
+    if mx_codes.shape != (*lead, N, K // 2) or mx_scales.shape != (*lead, N, K // 32):
+        raise ValueError("destination shapes do not match the source")
+    flags = MXFP4_REQ_INTERMEDIATE_BF16 if bf16_intermediate else 0
+    _check("mxfp4_requant_from_nvfp4", _lib.mxfp4_requant_from_nvfp4(
+        _ptr(nv_codes), _ptr(nv_scales), _ptr(nv_global), T, N, K,
+        _ptr(mx_codes), _ptr(mx_scales), flags, _stream(stream, dev)))
+    return mx_codes, mx_scales
+
+
+def mxfp4_quantize_act(x, codes=None, scales=None, *, row_index=None, K=None, stream=None):
+    """bf16 x [R, ldx] -> MXFP4 codes [M, K/2] and E8M0 bytes [M, K/32] where
+    M = R, or len(row_index) with output row i taken from x[row_index[i]].
+    K defaults to x's row length; x may have extra columns (ldx >= K)."""
+    _need(x, "x", torch.bfloat16)
+    dev = x.device
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [rows, ldx]")
+    ldx = x.shape[1]
+    K = ldx if K is None else int(K)
+    if row_index is not None:
+        _need(row_index, "row_index", torch.int32, dev)
+        M = row_index.shape[0]
+    else:
+        M = x.shape[0]
+    if codes is None:
+        codes = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
+    _need(codes, "codes", torch.uint8, dev)
+    _need(scales, "scales", torch.uint8, dev)
+    if codes.shape != (M, K // 2) or scales.shape != (M, K // 32):
+        raise ValueError("output shapes do not match [M, K/2] / [M, K/32]")
+    _check("mxfp4_quantize_act", _lib.mxfp4_quantize_act(
+        _ptr(x), ldx, _ptr(row_index), M, K, _ptr(codes), _ptr(scales), 0,
+        _stream(stream, dev)))
+    return codes, scales
+
+
+def _out_dtype(dtype):
+    if dtype == torch.bfloat16:
+        return MXFP4_OUT_BF16
+    if dtype == torch.float32:
+        return MXFP4_OUT_FP32
+    raise TypeError("out dtype must be torch.bfloat16 or torch.float32")
+
+
+def mxfp4_gemm(a_codes, a_scales, b_codes, b_scales, y=None, *, out_dtype=torch.bfloat16,
+               stream=None):
+    """y [M, N] = A [M, K] * B [N, K]^T over MXFP4 operands."""
+    _need(a_codes, "a_codes", torch.uint8)
+    dev = a_codes.device
+    for t, n in ((a_scales, "a_scales"), (b_codes, "b_codes"), (b_scales, "b_scales")):
+        _need(t, n, torch.uint8, dev)
+    M, K = a_codes.shape[0], a_codes.shape[1] * 2
+    N = b_codes.shape[0]
+    if b_codes.shape != (N, K // 2) or a_scales.shape != (M, K // 32) or \
+            b_scales.shape != (N, K // 32):
+        raise ValueError("operand shapes disagree")
+    if y is None:
+        y = torch.empty((M, N), dtype=out_dtype, device=dev)
+    _need(y, "y", y.dtype, dev)
+    if y.shape != (M, N):
+        raise ValueError("y must be [M, N]")
+    _check("mxfp4_gemm", _lib.mxfp4_gemm(
+        _ptr(a_codes), _ptr(a_scales), _ptr(b_codes), _ptr(b_scales), M, N, K,
+        _ptr(y), _out_dtype(y.dtype), None, 0, 0, _stream(stream, dev)))
+    return y
+
+
+def mxfp4_grouped_gemm(a_codes, a_scales, b_codes, b_scales, offsets, y=None, *,
+                       out_dtype=torch.bfloat16, stream=None):
+    """For each expert e: y[off[e]:off[e+1]] = A[off[e]:off[e+1]] * B[e]^T.
+    A [total_M, K/2] expert-sorted, B [E, N, K/2], offsets int32 [E+1]."""
+    _need(a_codes, "a_codes", torch.uint8)
+    dev = a_codes.device
+    for t, n in ((a_scales, "a_scales"), (b_codes, "b_codes"), (b_scales, "b_scales")):
+        _need(t, n, torch.uint8, dev)
+    _need(offsets, "offsets", torch.int32, dev)
+    total_M, K = a_codes.shape[0], a_codes.shape[1] * 2
+    E, N = b_codes.shape[0], b_codes.shape[1]
+    if offsets.shape != (E + 1,):
+        raise ValueError("offsets must have E+1 entries")
+    if b_codes.shape != (E, N, K // 2) or b_scales.shape != (E, N, K // 32) or \
+            a_scales.shape != (total_M, K // 32):
+        raise ValueError("operand shapes disagree")
+    if y is None:
+        y = torch.empty((total_M, N), dtype=out_dtype, device=dev)
+    _need(y, "y", y.dtype, dev)
+    if y.shape != (total_M, N):
+        raise ValueError("y must be [total_M, N]")
+    _check("mxfp4_grouped_gemm", _lib.mxfp4_grouped_gemm(
+        _ptr(a_codes), _ptr(a_scales), _ptr(b_codes), _ptr(b_scales), _ptr(offsets),
+        E, total_M, N, K, _ptr(y), _out_dtype(y.dtype), None, 0, 0, _stream(stream, dev)))
+    return y
+
+
+__all__ = ["mxfp4_requant_from_nvfp4", "mxfp4_quantize_act", "mxfp4_gemm",
+           "mxfp4_grouped_gemm", "mxfp4_gemm_workspace_size", "mxfp4_status_string",
+           "mxfp4_version", "Mxfp4Error", "LIBRARY_PATH", "EXPORTED_SYMBOLS",
+           "MXFP4_OUT_BF16", "MXFP4_OUT_FP32", "MXFP4_REQ_INTERMEDIATE_BF16"]

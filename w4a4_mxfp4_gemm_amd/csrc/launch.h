@@ -1,0 +1,30 @@
+// launch.h -- host-side launchers shared between the kernel translation units
+// and the C ABI.  Arguments reaching these functions are already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mx {
+
+hipError_t launch_act_quant(const uint16_t* x, int64_t ldx, const int32_t* row_index,
+                            int64_t M, int64_t K, uint8_t* codes, uint8_t* scales,
+                            hipStream_t stream);
+
+hipError_t launch_requant(const uint8_t* nv_codes, const uint8_t* nv_scales,
+                          const float* nv_global, int64_t T, int64_t N, int64_t K,
+                          uint8_t* mx_codes, uint8_t* mx_scales, bool bf16_intermediate,
+                          hipStream_t stream);
+
+hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
+                       const uint8_t* b_codes, const uint8_t* b_scales,
+                       int64_t M, int64_t N, int64_t K, void* y, bool out_bf16,
+                       hipStream_t stream);
+
+hipError_t launch_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
+                               const uint8_t* b_codes, const uint8_t* b_scales,
+                               const int32_t* offsets, int64_t E, int64_t total_M,
+                               int64_t N, int64_t K, void* y, bool out_bf16,
+                               hipStream_t stream);
+
+}  // namespace mx

@@ -1,0 +1,79 @@
+// mx_device.h -- gfx950 device helpers for E2M1 / E4M3 / E8M0 / bf16 codes.
+//
+// Everything here is integer or exactly-rounded fp32 work, so results do not
+// depend on FMA contraction or the order of evaluation.  fp32 denormals are
+// kept (the kernels are built with the default IEEE denormal mode).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mx {
+
+// bf16 bit pattern (low 16 bits of b) -> fp32, exact.
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) {
+    return __uint_as_float(b << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return ((u >> 16) | 0x40u) & 0xFFFFu;
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// float8_e4m3fn byte -> fp32 (exact): bias 7, exponent field 0 subnormal,
+// S.1111.111 NaN, no infinities.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+    uint32_t e = (b >> 3) & 15u, m = b & 7u;
+    float mag;
+    if (e == 0) mag = (float)m * 0.001953125f;                 // m * 2^-9
+    else mag = __uint_as_float(((e + 120u) << 23) | (m << 20));
+    if (e == 15u && m == 7u) mag = __uint_as_float(0x7FC00000u);
+    return (b & 0x80u) ? -mag : mag;
+}
+
+// E2M1 code (low 4 bits) -> fp32 (exact).
+__device__ __forceinline__ float e2m1_to_f32(uint32_t c) {
+    uint32_t e = (c >> 1) & 3u, m = c & 1u;
+    float mag = e ? __uint_as_float(((e + 126u) << 23) | (m << 22)) : 0.5f * (float)m;
+    return (c & 8u) ? -mag : mag;
+}
+
+// OCP MX shared-exponent byte from the fp32 bit pattern of a block's amax
+// (sign bit clear).  floor(log2 amax) - 2 + 127 is the biased exponent field
+// minus 2, clamped at 0; NaN or Inf anywhere in the block gives 0xFF.
+__device__ __forceinline__ uint32_t mx_scale_from_amax_bits(uint32_t amax_bits) {
+    uint32_t E = amax_bits >> 23;
+    if (E >= 255u) return 255u;
+    return E >= 2u ? E - 2u : 0u;
+}
+
+// E2M1 magnitude code (0..7) of q >= 0: the nearest of {0, .5, 1, 1.5, 2, 3,
+// 4, 6}, exact half-way points going to the even code, anything past 5
+// saturating to 6.  Each term counts one decision threshold: strict '>' where
+// the tie belongs to the lower (even) neighbour, '>=' where it belongs to the
+// upper one.
+__device__ __forceinline__ uint32_t e2m1_mag_rne(float q) {
+    return (uint32_t)(q > 0.25f) + (uint32_t)(q >= 0.75f) + (uint32_t)(q > 1.25f) +
+           (uint32_t)(q >= 1.75f) + (uint32_t)(q > 2.5f) + (uint32_t)(q >= 3.5f) +
+           (uint32_t)(q > 5.0f);
+}
+
+// E2M1 code of v under the block scale 2^(byte-127) (byte != 0xFF).
+// v * 2^(127-byte) is exact whenever it is at least 2^-126; smaller results
+// round to code 0 either way.  The sign bit of v is kept.
+__device__ __forceinline__ uint32_t e2m1_encode(float v, int neg_exp) {
+    float q = __builtin_amdgcn_ldexpf(__builtin_fabsf(v), neg_exp);
+    return e2m1_mag_rne(q) | ((__float_as_uint(v) >> 28) & 8u);
+}
+
+// Max over the 4 lanes of an aligned quad (DPP quad permutations).
+__device__ __forceinline__ uint32_t quad_max_u32(uint32_t v) {
+    uint32_t x = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);  // [1,0,3,2]
+    v = v > x ? v : x;
+    x = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);           // [2,3,0,1]
+    return v > x ? v : x;
+}
+
+}  // namespace mx

@@ -1,0 +1,108 @@
+// mxfp4_abi.cpp -- the extern "C" entry points declared in include/mxfp4.h:
+// argument validation, then one launch on the caller's stream.  Nothing here
+// allocates, synchronises or keeps state.
+#include "../../include/mxfp4.h"
+#include "launch.h"
+
+#include <stdint.h>
+
+namespace {
+
+constexpr int kVersion = 100;   // 0.1.0
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int from_hip(hipError_t e) { return e == hipSuccess ? MXFP4_OK : MXFP4_EHIP; }
+
+int check_k(int64_t K) { return (K > 0 && K % 32 == 0) ? MXFP4_OK : MXFP4_EINVAL; }
+
+int check_gemm_common(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
+                      const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, void* y,
+                      int out_dtype, void* workspace, size_t workspace_bytes, uint32_t flags) {
+    if (M < 0 || N <= 0 || check_k(K) != MXFP4_OK) return MXFP4_EINVAL;
+    if (out_dtype != MXFP4_OUT_BF16 && out_dtype != MXFP4_OUT_FP32) return MXFP4_EINVAL;
+    if (flags != 0) return MXFP4_EINVAL;
+    if (workspace_bytes != 0 && workspace == nullptr) return MXFP4_EINVAL;
+    if (M == 0) return MXFP4_OK;
+    if (!a_codes || !a_scales || !b_codes || !b_scales || !y) return MXFP4_EINVAL;
+    if (!aligned(a_codes, 16) || !aligned(b_codes, 16)) return MXFP4_EALIGN;
+    if (!aligned(y, out_dtype == MXFP4_OUT_FP32 ? 4 : 2)) return MXFP4_EALIGN;
+    return MXFP4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mxfp4_requant_from_nvfp4(const uint8_t* nv_codes, const uint8_t* nv_scales,
+                             const float* nv_global, int64_t T, int64_t N, int64_t K,
+                             uint8_t* mx_codes, uint8_t* mx_scales, uint32_t flags,
+                             hipStream_t stream) {
+    if (T < 0 || N <= 0 || check_k(K) != MXFP4_OK) return MXFP4_EINVAL;
+    if ((flags & ~(uint32_t)MXFP4_REQ_INTERMEDIATE_BF16) != 0) return MXFP4_EINVAL;
+    if (T == 0) return MXFP4_OK;
+    if (!nv_codes || !nv_scales || !nv_global || !mx_codes || !mx_scales) return MXFP4_EINVAL;
+    if (!aligned(nv_codes, 16) || !aligned(mx_codes, 16) || !aligned(nv_scales, 2) ||
+        !aligned(nv_global, 4))
+        return MXFP4_EALIGN;
+    return from_hip(mx::launch_requant(nv_codes, nv_scales, nv_global, T, N, K, mx_codes,
+                                       mx_scales, (flags & MXFP4_REQ_INTERMEDIATE_BF16) != 0,
+                                       stream));
+}
+
+int mxfp4_quantize_act(const void* x_bf16, int64_t ldx, const int32_t* row_index, int64_t M,
+                       int64_t K, uint8_t* codes, uint8_t* scales, uint32_t flags,
+                       hipStream_t stream) {
+    if (M < 0 || check_k(K) != MXFP4_OK || ldx < K) return MXFP4_EINVAL;
+    if (flags != 0) return MXFP4_EINVAL;
+    if (M == 0) return MXFP4_OK;
+    if (!x_bf16 || !codes || !scales) return MXFP4_EINVAL;
+    if (!aligned(x_bf16, 16) || ldx % 8 != 0 || !aligned(codes, 16)) return MXFP4_EALIGN;
+    if (row_index && !aligned(row_index, 4)) return MXFP4_EALIGN;
+    return from_hip(mx::launch_act_quant(static_cast<const uint16_t*>(x_bf16), ldx, row_index,
+                                         M, K, codes, scales, stream));
+}
+
+int mxfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
+               const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, void* y,
+               int out_dtype, void* workspace, size_t workspace_bytes, uint32_t flags,
+               hipStream_t stream) {
+    const int st = check_gemm_common(a_codes, a_scales, b_codes, b_scales, M, N, K, y, out_dtype,
+                                     workspace, workspace_bytes, flags);
+    if (st != MXFP4_OK || M == 0) return st;
+    return from_hip(mx::launch_gemm(a_codes, a_scales, b_codes, b_scales, M, N, K, y,
+                                    out_dtype == MXFP4_OUT_BF16, stream));
+}
+
+int mxfp4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
+                       const uint8_t* b_scales, const int32_t* offsets, int64_t E,
+                       int64_t total_M, int64_t N, int64_t K, void* y, int out_dtype,
+                       void* workspace, size_t workspace_bytes, uint32_t flags,
+                       hipStream_t stream) {
+    if (E <= 0) return MXFP4_EINVAL;
+    const int st = check_gemm_common(a_codes, a_scales, b_codes, b_scales, total_M, N, K, y,
+                                     out_dtype, workspace, workspace_bytes, flags);
+    if (st != MXFP4_OK || total_M == 0) return st;
+    if (!offsets) return MXFP4_EINVAL;
+    if (!aligned(offsets, 4)) return MXFP4_EALIGN;
+    return from_hip(mx::launch_grouped_gemm(a_codes, a_scales, b_codes, b_scales, offsets, E,
+                                            total_M, N, K, y, out_dtype == MXFP4_OUT_BF16,
+                                            stream));
+}
+
+size_t mxfp4_gemm_workspace_size(int64_t, int64_t, int64_t) { return 0; }
+
+const char* mxfp4_status_string(int status) {
+    switch (status) {
+        case MXFP4_OK: return "ok";
+        case MXFP4_EINVAL: return "invalid argument (size, null pointer, flag or dtype)";
+        case MXFP4_EALIGN: return "misaligned pointer or leading dimension";
+        case MXFP4_EUNSUPPORTED: return "unsupported request";
+        case MXFP4_EHIP: return "HIP runtime error at launch";
+        default: return "unknown status";
+    }
+}
+
+int mxfp4_version(void) { return kVersion; }
+
+}  // extern "C"
