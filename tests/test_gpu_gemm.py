@@ -52,15 +52,36 @@ def test_gemm_random_operands_fp32(mx, M, N, K):
 
 
 def test_gemm_wide_scale_range(mx):
-    """E8M0 bytes over most of the range that keeps products fp32-normal."""
+    """E8M0 bytes over most of the range that keeps every product fp32-normal
+    (byte sums >= 130) and every partial sum finite (byte sums <= 366 at K=512)."""
     say("gemm wide scale range")
     M, N, K = 40, 72, 512
-    a, sa = synth.canonical_mxfp4(M, K, seed=1, scale_lo=64, scale_hi=190)
-    b, sb = synth.canonical_mxfp4(N, K, seed=2, scale_lo=64, scale_hi=190)
+    a, sa = synth.canonical_mxfp4(M, K, seed=1, scale_lo=65, scale_hi=183)
+    b, sb = synth.canonical_mxfp4(N, K, seed=2, scale_lo=65, scale_hi=183)
     y, s = oracle.gemm(u8(a), u8(sa), u8(b), u8(sb))
+    assert s.max() < 3.0e38
     A, SA, B, SB = to_dev(a, sa, b, sb)
     out = mx.mxfp4_gemm(A, SA, B, SB, out_dtype=torch.float32)
     assert_gemm_fp32(out, y, s, "wide scales")
+
+
+def test_gemm_overflow_saturates_to_inf(mx):
+    """When every product has the same sign and the exact sum exceeds the fp32
+    range, the fp32 result is +-inf (the RNE image of an overflowing value)."""
+    say("gemm fp32 overflow")
+    K = 256
+    a = torch.full((2, K // 2), 0x77, dtype=torch.uint8)          # all codes 6.0
+    sa = torch.full((2, K // 32), 250, dtype=torch.uint8)
+    b = torch.full((3, K // 2), 0x77, dtype=torch.uint8)
+    b[1] = 0xFF                                                    # all codes -6.0
+    sb = torch.full((3, K // 32), 127, dtype=torch.uint8)
+    sb[2] = 1                                                      # tiny: finite result
+    y, s = oracle.gemm(u8(a), u8(sa), u8(b), u8(sb))
+    A, SA, B, SB = to_dev(a, sa, b, sb)
+    out = f32(mx.mxfp4_gemm(A, SA, B, SB, out_dtype=torch.float32))
+    assert np.all(out[:, 0] == np.inf) and np.all(out[:, 1] == -np.inf)
+    assert np.all(np.isfinite(out[:, 2]))
+    assert oracle.gemm_fp32_ok(out[:, 2].astype(np.float64), y[:, 2], s[:, 2]).all()
 
 
 def test_gemm_deterministic_and_finite(mx):
