@@ -27,4 +27,11 @@ hipError_t launch_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
                                int64_t N, int64_t K, void* y, bool out_bf16,
                                hipStream_t stream);
 
+bool tiled_gemm_supported(int64_t M, int64_t N, int64_t K, const void* a_scales,
+                          const void* b_scales);
+
+hipError_t launch_gemm_tiled(const uint8_t* a_codes, const uint8_t* a_scales,
+                             const uint8_t* b_codes, const uint8_t* b_scales, int64_t M,
+                             int64_t N, int64_t K, void* y, bool out_bf16, hipStream_t stream);
+
 }  // namespace mx

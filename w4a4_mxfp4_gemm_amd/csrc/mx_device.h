@@ -22,6 +22,13 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Two fp32 -> packed bf16 (RNE; gfx950 v_cvt_pk_bf16_f32), a in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    const __bf16 lo = (__bf16)a, hi = (__bf16)b;
+    return (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+}
+
 // float8_e4m3fn byte -> fp32 (exact): bias 7, exponent field 0 subnormal,
 // S.1111.111 NaN, no infinities.
 __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
