@@ -43,6 +43,8 @@
 #include "mx_device.h"
 #include "launch.h"
 
+#include <type_traits>
+
 namespace mx {
 namespace tiled {
 
@@ -228,19 +230,57 @@ __device__ __forceinline__ void settle(Half& f, Scales& sc) {
                       "+v"(sc.x[1]), "+v"(sc.x[2]), "+v"(sc.x[3]));
 }
 
-// MFMAs of K-steps 2H, 2H+1 (scale bytes 2H, 2H+1 of each word).
-template <int H>
-__device__ __forceinline__ void mfma_half(const Half& f, const Scales& sc, v16f (&acc)[4][4]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            acc[i][j] = mfma<2 * H>(f.w[i][0], f.x[j][0], acc[i][j], sc.w[i], sc.x[j]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            acc[i][j] = mfma<2 * H + 1>(f.w[i][1], f.x[j][1], acc[i][j], sc.w[i], sc.x[j]);
+// One operand load of a stage, selected by index: 0-7 weight codes, 8-15
+// activation codes, 16 the stage's scale half-chunk.
+template <int Q>
+__device__ __forceinline__ void load_op(lds_u8* lds, const Operands& op, const LoadOffsets& o,
+                                        int buf, int kt, bool scale_w, int chunk) {
+    const int wave = threadIdx.x >> 6;
+    if constexpr (Q < 8) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            op.w, AS_LDS(lds + buf * CODE_STAGE + (wave * 8 + Q) * 1024), 16, o.w[Q],
+            (uint32_t)kt * BKB, 0, 0);
+    } else if constexpr (Q < 16) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            op.x, AS_LDS(lds + buf * CODE_STAGE + CODE_OPERAND + (wave * 8 + Q - 8) * 1024), 16,
+            o.x[Q - 8], (uint32_t)kt * BKB, 0, 0);
+    } else {
+        load_scales(lds, op, o, scale_w, chunk);
+    }
+}
+
+// One LDS read of a half-stage (index 0-15: K-step s = Q / 8, operand
+// Q % 8 / 4, block Q % 4), or for Q 16-23 one scale word.
+template <int H, int Q>
+__device__ __forceinline__ void read_op(Half& f, Scales& sc, uint32_t codes, uint32_t scales,
+                                        const ReadOffsets& ro) {
+    if constexpr (Q < 16) {
+        constexpr int s = Q / 8, opnd = (Q % 8) / 4, blk = Q % 4;
+        if constexpr (opnd == 0)
+            ds_read_b128<blk * 32 * BKB>(f.w[blk][s], codes + ro.w[2 * H + s]);
+        else
+            ds_read_b128<blk * 32 * BKB>(f.x[blk][s], codes + ro.x[2 * H + s]);
+    } else if constexpr (Q < 20) {
+        ds_read_b32<(Q - 16) * 32 * 16>(sc.w[Q - 16], scales + ro.ws);
+    } else {
+        ds_read_b32<(Q - 20) * 32 * 16>(sc.x[Q - 20], scales + ro.xs);
+    }
+}
+
+// The 32 MFMAs of K-steps 2H, 2H+1 (scale bytes 2H, 2H+1 of each word), with
+// the other pipes' work threaded between them: after MFMA q, `step<q>()`
+// issues that slot's loads / LDS reads, so the texture unit and LDS work
+// while the matrix core is busy instead of in bursts.
+template <int H, int Q = 0, typename Step>
+__device__ __forceinline__ void mfma_half(const Half& f, const Scales& sc, v16f (&acc)[4][4],
+                                          Step&& step) {
+    if constexpr (Q < 32) {
+        constexpr int t = Q / 16, i = (Q / 4) % 4, j = Q % 4;
+        acc[i][j] = mfma<2 * H + t>(f.w[i][t], f.x[j][t], acc[i][j], sc.w[i], sc.x[j]);
+        step(std::integral_constant<int, Q>{});
+        __builtin_amdgcn_sched_barrier(0);   // keep this slot's order
+        mfma_half<H, Q + 1>(f, sc, acc, step);
+    }
 }
 
 // XCD-aware tile order: workgroup ids are dealt to the 8 XCDs round-robin, so
@@ -366,19 +406,36 @@ __device__ __forceinline__ void tile_gemm(lds_u8* lds, const uint8_t* __restrict
     settle(h0, sc_cur);
 
     for (int kt = 0; kt < nkt; ++kt) {
-        read_half<1>(h1, code_addr(kt), ro);
-        mfma_half<0>(h0, sc_cur, acc);
-        settle(h1);
-
+        // first half: MFMAs on stage kt's K-steps 0-1, reads of its K-steps 2-3
+        {
+            const uint32_t codes = code_addr(kt);
+            Scales unused;
+            mfma_half<0>(h0, sc_cur, acc, [&](auto q) {
+                constexpr int Q = decltype(q)::value;
+                if constexpr (Q < 16) read_op<1, Q>(h1, unused, codes, 0, ro);
+            });
+            settle(h1);
+        }
         // stage kt+1 landed for every wave; every wave is done reading stage kt
         wait_vm<0>();
         __builtin_amdgcn_s_barrier();
-        issue(kt + 2);
-        read_half<0>(h0, code_addr(kt + 1), ro);
-        read_scales(sc_nxt, scale_addr(kt + 1), ro);
-        mfma_half<1>(h1, sc_cur, acc);
-        settle(h0, sc_nxt);
-        sc_cur = sc_nxt;
+        // second half: MFMAs on K-steps 2-3, loads of stage kt+2 into stage
+        // kt's buffer, reads of stage kt+1's K-steps 0-1 and scales
+        {
+            const int s2 = kt + 2;
+            const int ks = s2 < nkt ? s2 : nkt - 1;
+            const int c = s2 / 2 + 1;
+            const int chunk = c <= last_chunk ? c : last_chunk;
+            const bool scale_w = (s2 & 1) == 0;
+            const uint32_t codes = code_addr(kt + 1), scales = scale_addr(kt + 1);
+            mfma_half<1>(h1, sc_cur, acc, [&](auto q) {
+                constexpr int Q = decltype(q)::value;
+                if constexpr (Q < 17) load_op<Q>(lds, op, o, s2 & 1, ks, scale_w, chunk);
+                if constexpr (Q >= 4 && Q < 28) read_op<0, Q - 4>(h0, sc_nxt, codes, scales, ro);
+            });
+            settle(h0, sc_nxt);
+            sc_cur = sc_nxt;
+        }
     }
     // drain the surplus loads before the workgroup's LDS can be reused
     wait_vm<0>();
