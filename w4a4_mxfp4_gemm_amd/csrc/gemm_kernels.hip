@@ -226,6 +226,9 @@ static hipError_t launch_dense(const uint8_t* a, const uint8_t* as, const uint8_
 hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
                        const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, void* y,
                        bool out_bf16, hipStream_t stream) {
+    if (skinny_gemm_supported(M, N, K, a_codes, a_scales, b_scales))
+        return launch_gemm_skinny(a_codes, a_scales, b_codes, b_scales, M, N, K, y, out_bf16,
+                                  stream);
     if (tiled_gemm_supported(M, N, K, a_scales, b_scales))
         return launch_gemm_tiled(a_codes, a_scales, b_codes, b_scales, M, N, K, y, out_bf16,
                                  stream);
