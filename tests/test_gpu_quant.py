@@ -187,6 +187,26 @@ def test_requant_random_bytes_many_globals(mx, bf16_intermediate):
     assert_same(gpu, ref, "random requant, non-power-of-two g")
 
 
+@pytest.mark.parametrize("bf16_intermediate", [False, True])
+def test_requant_limited_code_range(mx, bf16_intermediate):
+    """Each NVFP4 block draws its codes from magnitudes 0..c_max with c_max
+    itself random (so the block's largest code varies from 0 to 6), under
+    E4M3 scales and global scales of both signs, including zero."""
+    say(f"requant limited code range T=8 N=64 K=1024 bf16={bf16_intermediate}")
+    rng = np.random.default_rng(17)
+    T, N, K = 8, 64, 1024
+    cmax = rng.integers(0, 8, size=(T, N, K // 16, 1))
+    mag = np.minimum(rng.integers(0, 8, size=(T, N, K // 16, 16)), cmax)
+    nib = (mag | (rng.integers(0, 2, size=mag.shape) << 3)).reshape(T, N, K)
+    codes = torch.from_numpy((nib[..., 0::2] | (nib[..., 1::2] << 4)).astype(np.uint8))
+    sc = rng.integers(0, 0x7F, size=(T, N, K // 16)) | (rng.integers(0, 2, size=(T, N, K // 16)) << 7)
+    scales = torch.from_numpy(sc.astype(np.uint8))
+    g = torch.tensor([1e-3, -2.5e-4, 0.0, -0.0, 3.0e-41, -7.0, 1.0e30, 2.0 ** -149],
+                     dtype=torch.float32)
+    gpu, ref = requant_both(mx, codes, scales, g, bf16_intermediate)
+    assert_same(gpu, ref, "limited code range")
+
+
 def test_requant_decode_weight_full_size(mx):
     say("requant W [12288,4096] seed 11 full compare")
     w = synth.bf16_normal((12288, 4096), 0.02, seed=11)

@@ -3,115 +3,200 @@
 //
 // Both are streaming kernels bound by HBM bandwidth: every byte is read once
 // with 16-byte loads that are contiguous across a wavefront and written once
-// with contiguous stores.  No LDS, no atomics.
+// with contiguous stores.  No LDS, no atomics.  The E2M1 rounding itself is
+// done by gfx950's scaled FP4 converter (two values per instruction), which
+// matches the exact round-half-to-even rule of the OCP MX format.
 #include "mx_device.h"
 #include "launch.h"
 
 namespace mx {
 
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
 // ---------------------------------------------------------------------------
-// Activation quantization.  One thread owns 8 consecutive bf16 values (one
-// 16-byte load); the 4 lanes of an aligned quad own one 32-element MX block
-// and share its amax through DPP.  Quads are laid out row-major over
-// (row, block), so a wavefront reads 1 KiB of one row contiguously.
+// Activation quantization.  One thread owns 8 consecutive bf16 values of a
+// row (one 16-byte load); the 4 lanes of an aligned quad own one 32-element
+// MX block and share its amax through DPP.  Threads along x walk one row's K,
+// so a wavefront reads 1 KiB of a row contiguously; blockIdx.y walks rows,
+// ROWS rows per thread per pass with every load issued before any math.
 // ---------------------------------------------------------------------------
+template <int ROWS>
 __global__ __launch_bounds__(256) void act_quant_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const int32_t* __restrict__ row_index,
     int64_t M, int64_t K, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
-    const int64_t quarters_per_row = K / 8;
-    const int64_t total = M * quarters_per_row;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += stride) {
-        const int64_t m = t / quarters_per_row;
-        const int64_t kq = t - m * quarters_per_row;          // which 8-element group
-        const int64_t src = row_index ? (int64_t)row_index[m] : m;
-        const uint4 raw = *reinterpret_cast<const uint4*>(x + src * ldx + kq * 8);
-        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-
-        // amax over the 8 values as bf16 magnitudes (monotone as integers);
-        // NaN and Inf patterns sort above every finite value.
-        uint32_t amax = 0;
+    const int64_t chunks = K / 8;                     // 16-byte chunks per row; multiple of 4
+    const int64_t kq = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (kq >= chunks) return;                         // whole quads leave together
+    for (int64_t m0 = (int64_t)blockIdx.y * ROWS; m0 < M; m0 += (int64_t)gridDim.y * ROWS) {
+        uint4 raw[ROWS];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            uint32_t lo = w[i] & 0x7FFFu, hi = (w[i] >> 16) & 0x7FFFu;
-            amax = max(amax, max(lo, hi));
-        }
-        amax = quad_max_u32(amax);
-        const uint32_t byte = mx_scale_from_amax_bits(amax << 16);
-        const int neg_exp = 127 - (int)byte;
-
-        uint32_t packed = 0;
-        if (byte != 255u) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                uint32_t c0 = e2m1_encode(bf16_to_f32(w[i] & 0xFFFFu), neg_exp);
-                uint32_t c1 = e2m1_encode(bf16_to_f32(w[i] >> 16), neg_exp);
-                packed |= (c0 | (c1 << 4)) << (8 * i);
+        for (int r = 0; r < ROWS; ++r) {
+            const int64_t m = m0 + r;
+            if (m < M) {
+                const int64_t src = row_index ? (int64_t)row_index[m] : m;
+                raw[r] = *reinterpret_cast<const uint4*>(x + src * ldx + kq * 8);
             }
         }
-        *reinterpret_cast<uint32_t*>(codes + m * (K / 2) + kq * 4) = packed;
-        if ((kq & 3) == 0) scales[m * (K / 32) + kq / 4] = (uint8_t)byte;
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r) {
+            const int64_t m = m0 + r;
+            if (m >= M) break;                        // uniform across the workgroup
+            const uint32_t w[4] = {raw[r].x, raw[r].y, raw[r].z, raw[r].w};
+            // amax over the 8 values as bf16 magnitudes (monotone as integers;
+            // NaN and Inf patterns sort above every finite value).
+            u16x2 a = __builtin_bit_cast(u16x2, w[0] & 0x7FFF7FFFu);
+#pragma unroll
+            for (int i = 1; i < 4; ++i)
+                a = __builtin_elementwise_max(a, __builtin_bit_cast(u16x2, w[i] & 0x7FFF7FFFu));
+            const uint32_t amax = quad_max_u32(max((uint32_t)a[0], (uint32_t)a[1]));
+            const uint32_t byte = mx_scale_from_amax_bits(amax << 16);
+            const float scale = e8m0_to_f32(byte);
+            uint32_t packed = cvt_fp4x2_bf16<0>(0u, w[0], scale);
+            packed = cvt_fp4x2_bf16<1>(packed, w[1], scale);
+            packed = cvt_fp4x2_bf16<2>(packed, w[2], scale);
+            packed = cvt_fp4x2_bf16<3>(packed, w[3], scale);
+            if (byte == 255u) packed = 0u;            // NaN/Inf block: codes are zero
+            *reinterpret_cast<uint32_t*>(codes + m * (K / 2) + kq * 4) = packed;
+            if ((kq & 3) == 0) scales[m * (K / 32) + kq / 4] = (uint8_t)byte;
+        }
     }
 }
 
 // ---------------------------------------------------------------------------
 // NVFP4 -> MXFP4 requant.  One thread owns one 32-element MX block: 16 code
-// bytes (one 16-byte load), the two E4M3 scales of NVFP4 blocks 2j and 2j+1,
-// and the tensor's fp32 global scale.  Values are materialised in registers
-// only: v = fl32(fl32(e2m1 * e4m3) * g), optionally rounded to bf16.
+// bytes (one 16-byte load) and the E4M3 scales of its two NVFP4 blocks.
+//
+// Inside an NVFP4 block every element is v = fl32(fl32(e2m1 * s) * g), a
+// function of its 4-bit code alone, and |v| grows with the code's magnitude
+// (rounding is monotone).  So per half-block the thread
+//   1. forms the 8 magnitudes |v(c)|, c = 0..7 (the sign of v is the code's
+//      sign bit xor the signs of s and g, also for zeros),
+//   2. finds the largest code magnitude present; the MX block's amax is the
+//      larger of the two halves' |v(cmax)|, which gives the E8M0 byte,
+//   3. encodes the 8 magnitudes once with the hardware converter into an
+//      8-entry byte table, and
+//   4. maps every code through that table with byte permutes (v_perm_b32),
+//      eight codes per two permutes, restoring the sign bits afterwards.
+// A NaN or Inf anywhere in the NVFP4 block shows up in |v(cmax)| (0 * Inf,
+// NaN scales and Inf products all surface there), giving byte 0xFF and zero
+// codes.
 // ---------------------------------------------------------------------------
+template <bool BF16_INTERMEDIATE>
+__device__ __forceinline__ float nv_mag(float e2m1_mag, float s_abs, float g_abs) {
+    float v = (e2m1_mag * s_abs) * g_abs;    // first product exact, second rounded once
+    if (BF16_INTERMEDIATE) v = bf16_to_f32(f32_to_bf16_rne(v));
+    return v;
+}
+
+// Bytes 0..7 of {hi:lo} hold one-hot masks 1 << c: permuting by code
+// magnitudes marks which magnitudes occur.
+constexpr uint32_t ONEHOT_LO = 0x08040201u, ONEHOT_HI = 0x80402010u;
+
+template <bool BF16_INTERMEDIATE>
+__device__ __forceinline__ void requant_block(uint4 raw, uint32_t sc, float g_abs,
+                                              uint32_t g_sign, uint4& out, uint32_t& byte_out) {
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    uint32_t sel_lo[4], sel_hi[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        sel_lo[i] = w[i] & 0x07070707u;            // even elements' code magnitudes
+        sel_hi[i] = (w[i] >> 4) & 0x07070707u;     // odd elements'
+    }
+    float tab_mag[2][8];
+    uint32_t amax_bits = 0;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint32_t s8 = (sc >> (8 * h)) & 0xFFu;
+        const float s_abs = e4m3_to_f32(s8 & 0x7Fu);
+        constexpr float E[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+#pragma unroll
+        for (int c = 0; c < 8; ++c) tab_mag[h][c] = nv_mag<BF16_INTERMEDIATE>(E[c], s_abs, g_abs);
+        uint32_t seen = 0;
+#pragma unroll
+        for (int i = 2 * h; i < 2 * h + 2; ++i)
+            seen |= byte_perm(ONEHOT_HI, ONEHOT_LO, sel_lo[i]) |
+                    byte_perm(ONEHOT_HI, ONEHOT_LO, sel_hi[i]);
+        seen |= seen >> 16;
+        seen |= seen >> 8;
+        const uint32_t cmax = 31u - (uint32_t)__builtin_clz(seen & 0xFFu);
+        const float top = nv_mag<BF16_INTERMEDIATE>(e2m1_to_f32(cmax), s_abs, g_abs);
+        amax_bits = max(amax_bits, __float_as_uint(top) & 0x7FFFFFFFu);
+    }
+    const uint32_t byte = mx_scale_from_amax_bits(amax_bits);
+    const float scale = e8m0_to_f32(byte);
+    uint32_t res[4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const float* m = tab_mag[h];
+        uint32_t t = cvt_fp4x2<0>(0u, m[0], m[4], scale);
+        t = cvt_fp4x2<1>(t, m[1], m[5], scale);
+        t = cvt_fp4x2<2>(t, m[2], m[6], scale);
+        t = cvt_fp4x2<3>(t, m[3], m[7], scale);
+        const uint32_t tab_lo = t & 0x0F0F0F0Fu;          // codes of magnitudes 0..3
+        const uint32_t tab_hi = (t >> 4) & 0x0F0F0F0Fu;   // codes of magnitudes 4..7
+        const uint32_t s8 = (sc >> (8 * h)) & 0xFFu;
+        const uint32_t flip = ((s8 >> 7) ^ g_sign) ? 0x88888888u : 0u;
+#pragma unroll
+        for (int i = 2 * h; i < 2 * h + 2; ++i)
+            res[i] = byte_perm(tab_hi, tab_lo, sel_lo[i]) |
+                     (byte_perm(tab_hi, tab_lo, sel_hi[i]) << 4) |
+                     ((w[i] ^ flip) & 0x88888888u);
+    }
+    if (byte == 255u) res[0] = res[1] = res[2] = res[3] = 0u;
+    out = make_uint4(res[0], res[1], res[2], res[3]);
+    byte_out = byte;
+}
+
+// Grid: x walks the MX blocks of one tensor, 2 * 256 per workgroup pass;
+// y walks tensors (each with its own global scale).
 template <bool BF16_INTERMEDIATE>
 __global__ __launch_bounds__(256) void requant_kernel(
     const uint8_t* __restrict__ nv_codes, const uint8_t* __restrict__ nv_scales,
-    const float* __restrict__ nv_global, int64_t T, int64_t N, int64_t K,
+    const float* __restrict__ nv_global, int64_t T, int64_t blocks_per_tensor,
     uint8_t* __restrict__ mx_codes, uint8_t* __restrict__ mx_scales) {
-    const int64_t blocks_per_tensor = N * (K / 32);
-    const int64_t total = T * blocks_per_tensor;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < total; b += stride) {
-        const int64_t t = b / blocks_per_tensor;
+    constexpr int UNROLL = 2;
+    for (int64_t t = blockIdx.y; t < T; t += gridDim.y) {
         const float g = nv_global[t];
-        const uint4 raw = *reinterpret_cast<const uint4*>(nv_codes + b * 16);
-        const uint32_t sc = *reinterpret_cast<const uint16_t*>(nv_scales + b * 2);
-        const float s0 = e4m3_to_f32(sc & 0xFFu), s1 = e4m3_to_f32(sc >> 8);
-        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-
-        float v[32];
-        uint32_t amax = 0;
+        const float g_abs = __builtin_fabsf(g);
+        const uint32_t g_sign = __float_as_uint(g) >> 31;
+        const int64_t base = t * blocks_per_tensor;
+        for (int64_t b0 = (int64_t)blockIdx.x * (UNROLL * 256) + threadIdx.x;
+             b0 < blocks_per_tensor; b0 += (int64_t)gridDim.x * (UNROLL * 256)) {
+            uint4 raw[UNROLL];
+            uint32_t sc[UNROLL];
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            const uint32_t c = (w[i / 8] >> (4 * (i % 8))) & 15u;
-            const float p = e2m1_to_f32(c) * (i < 16 ? s0 : s1);   // exact
-            float x = p * g;                                         // one rounding
-            if (BF16_INTERMEDIATE) x = bf16_to_f32(f32_to_bf16_rne(x));
-            v[i] = x;
-            amax = max(amax, __float_as_uint(x) & 0x7FFFFFFFu);
-        }
-        const uint32_t byte = mx_scale_from_amax_bits(amax);
-        const int neg_exp = 127 - (int)byte;
-        uint32_t out[4] = {0, 0, 0, 0};
-        if (byte != 255u) {
+            for (int u = 0; u < UNROLL; ++u) {
+                const int64_t b = b0 + u * 256;
+                if (b < blocks_per_tensor) {
+                    raw[u] = *reinterpret_cast<const uint4*>(nv_codes + (base + b) * 16);
+                    sc[u] = *reinterpret_cast<const uint16_t*>(nv_scales + (base + b) * 2);
+                }
+            }
 #pragma unroll
-            for (int i = 0; i < 32; ++i) out[i / 8] |= e2m1_encode(v[i], neg_exp) << (4 * (i % 8));
+            for (int u = 0; u < UNROLL; ++u) {
+                const int64_t b = b0 + u * 256;
+                if (b < blocks_per_tensor) {
+                    uint4 out;
+                    uint32_t byte;
+                    requant_block<BF16_INTERMEDIATE>(raw[u], sc[u], g_abs, g_sign, out, byte);
+                    *reinterpret_cast<uint4*>(mx_codes + (base + b) * 16) = out;
+                    mx_scales[base + b] = (uint8_t)byte;
+                }
+            }
         }
-        *reinterpret_cast<uint4*>(mx_codes + b * 16) = make_uint4(out[0], out[1], out[2], out[3]);
-        mx_scales[b] = (uint8_t)byte;
     }
-}
-
-static int grid_for(int64_t threads_needed) {
-    int64_t blocks = (threads_needed + 255) / 256;
-    const int64_t cap = 256 * 64;     // enough waves to cover 256 CUs many times over
-    if (blocks > cap) blocks = cap;
-    return (int)(blocks < 1 ? 1 : blocks);
 }
 
 hipError_t launch_act_quant(const uint16_t* x, int64_t ldx, const int32_t* row_index,
                             int64_t M, int64_t K, uint8_t* codes, uint8_t* scales,
                             hipStream_t stream) {
-    const int64_t threads = M * (K / 8);
-    hipLaunchKernelGGL(act_quant_kernel, dim3(grid_for(threads)), dim3(256), 0, stream,
-                       x, ldx, row_index, M, K, codes, scales);
+    constexpr int ROWS = 2;
+    const int64_t chunks = K / 8;
+    const int64_t gx = (chunks + 255) / 256;
+    int64_t gy = (M + ROWS - 1) / ROWS;
+    if (gy > 65535) gy = 65535;
+    hipLaunchKernelGGL(act_quant_kernel<ROWS>, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0,
+                       stream, x, ldx, row_index, M, K, codes, scales);
     return hipGetLastError();
 }
 
@@ -119,13 +204,17 @@ hipError_t launch_requant(const uint8_t* nv_codes, const uint8_t* nv_scales,
                           const float* nv_global, int64_t T, int64_t N, int64_t K,
                           uint8_t* mx_codes, uint8_t* mx_scales, bool bf16_intermediate,
                           hipStream_t stream) {
-    const int64_t threads = T * N * (K / 32);
+    const int64_t bpt = N * (K / 32);
+    int64_t gx = (bpt + 511) / 512;
+    if (gx > 8192) gx = 8192;
+    const int64_t gy = T > 65535 ? 65535 : T;
+    const dim3 grid((unsigned)gx, (unsigned)gy);
     if (bf16_intermediate)
-        hipLaunchKernelGGL(requant_kernel<true>, dim3(grid_for(threads)), dim3(256), 0, stream,
-                           nv_codes, nv_scales, nv_global, T, N, K, mx_codes, mx_scales);
+        hipLaunchKernelGGL(requant_kernel<true>, grid, dim3(256), 0, stream, nv_codes, nv_scales,
+                           nv_global, T, bpt, mx_codes, mx_scales);
     else
-        hipLaunchKernelGGL(requant_kernel<false>, dim3(grid_for(threads)), dim3(256), 0, stream,
-                           nv_codes, nv_scales, nv_global, T, N, K, mx_codes, mx_scales);
+        hipLaunchKernelGGL(requant_kernel<false>, grid, dim3(256), 0, stream, nv_codes,
+                           nv_scales, nv_global, T, bpt, mx_codes, mx_scales);
     return hipGetLastError();
 }
 
