@@ -217,6 +217,62 @@ def test_grouped_gemm_bad_offsets_stay_inside_y(mx):
         assert gy.intact(), table
 
 
+def grouped_case(mx, counts, N, K, seed, out_dtype):
+    E = len(counts)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    M = int(offsets[-1])
+    a, sa = synth.canonical_mxfp4(M, K, seed=seed)
+    b, sb = synth.canonical_mxfp4(E * N, K, seed=seed + 1)
+    b, sb = b.reshape(E, N, K // 2), sb.reshape(E, N, K // 32)
+    y, s = oracle.grouped_gemm(u8(a), u8(sa), u8(b), u8(sb), offsets)
+    A, SA, B, SB, OFF = to_dev(a, sa, b, sb, offsets)
+    gy = Guarded((M, N), out_dtype)
+    mx.mxfp4_grouped_gemm(A, SA, B, SB, OFF, gy.view)
+    torch.cuda.synchronize()
+    assert gy.intact(), "write outside y"
+    return gy.view, y, s
+
+
+def test_grouped_gemm_tiled_row_blocks(mx):
+    """Expert sizes that end in each 32-row block of a 128-row tile, span
+    several tiles, or are empty; N with a partial 256-row weight tile.  The
+    bf16 output is the RNE of the same fp32 accumulator (random scales make
+    cancellation common, so the oracle bound is the fp32 one)."""
+    counts = [0, 1, 31, 32, 33, 97, 128, 129, 257, 300, 0]
+    say(f"grouped tiled row blocks counts={counts} N=300 K=1024")
+    gy, y, s = grouped_case(mx, counts, 300, 1024, 51, torch.float32)
+    assert_gemm_fp32(gy, y, s, "grouped tiled")
+    yb, _, _ = grouped_case(mx, counts, 300, 1024, 51, torch.bfloat16)
+    assert np.array_equal(bf16_bits(yb), bf16_bits(gy.to(torch.bfloat16)))
+
+
+def test_grouped_gemm_tiled_many_small_experts(mx):
+    """More experts than a wavefront has lanes (the offset table is scanned in
+    pieces), most of them tiny or empty."""
+    rng = np.random.default_rng(5)
+    counts = rng.integers(0, 6, size=150)
+    counts[rng.random(150) < 0.3] = 0
+    counts[77] = 140
+    say(f"grouped tiled 150 experts total {counts.sum()} N=256 K=512")
+    gy, y, s = grouped_case(mx, counts, 256, 512, 61, torch.float32)
+    assert_gemm_fp32(gy, y, s, "grouped tiled small experts")
+
+
+def test_grouped_gemm_tiled_bad_offsets_stay_inside_y(mx):
+    say("grouped tiled gemm malformed offsets")
+    E, N, K, M = 4, 256, 512, 300
+    a, sa = synth.canonical_mxfp4(M, K, seed=13)
+    b, sb = synth.canonical_mxfp4(E * N, K, seed=14)
+    A, SA, B, SB = to_dev(a, sa, b.reshape(E, N, K // 2), sb.reshape(E, N, K // 32))
+    for table in ([0, 400, 10, -5, 300], [-100, 0, 1000, 20, 300], [0, 0, 0, 0, 0],
+                  [0, 300, 300, 300, 300]):
+        OFF = torch.tensor(table, dtype=torch.int32, device=dev())
+        gy = Guarded((M, N), torch.float32)
+        mx.mxfp4_grouped_gemm(A, SA, B, SB, OFF, gy.view)
+        torch.cuda.synchronize()
+        assert gy.intact(), table
+
+
 @pytest.fixture(scope="module")
 def moe_setup(mx):
     """MoE layer: 128 experts, gate_up [2048,4096], down [4096,1024], 2048 tokens,

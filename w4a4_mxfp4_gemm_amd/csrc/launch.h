@@ -34,6 +34,15 @@ hipError_t launch_gemm_tiled(const uint8_t* a_codes, const uint8_t* a_scales,
                              const uint8_t* b_codes, const uint8_t* b_scales, int64_t M,
                              int64_t N, int64_t K, void* y, bool out_bf16, hipStream_t stream);
 
+bool grouped_tiled_supported(int64_t E, int64_t total_M, int64_t N, int64_t K,
+                             const void* a_scales, const void* b_scales);
+
+hipError_t launch_grouped_gemm_tiled(const uint8_t* a_codes, const uint8_t* a_scales,
+                                     const uint8_t* b_codes, const uint8_t* b_scales,
+                                     const int32_t* offsets, int64_t E, int64_t total_M,
+                                     int64_t N, int64_t K, void* y, bool out_bf16,
+                                     hipStream_t stream);
+
 bool skinny_gemm_supported(int64_t M, int64_t N, int64_t K, const void* x, const void* x_scales,
                            const void* w_scales);
 
