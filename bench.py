@@ -63,16 +63,29 @@ def gemm_bytes(M, N, K, out_bytes=2):  # both MXFP4 operands in, Y out
     return (M + N) * K * (0.5 + 1 / 32) + M * N * out_bytes
 
 
-def kernel_source_digest():
+# The source files each measured kernel is built from (its traffic record is
+# valid only while these hash to the digest stored with it).
+KERNEL_SOURCES = {
+    "requant": ("quant_kernels.hip", "mx_device.h"),
+    "act_quant": ("quant_kernels.hip", "mx_device.h"),
+    "gemm_decode": ("gemm_skinny.hip", "mx_device.h"),
+    "gemm_prefill": ("gemm_tiled.hip", "mx_device.h"),
+    "grouped_gemm_moe": ("gemm_tiled.hip", "mx_device.h"),
+}
+
+
+def kernel_source_digest(tag=None):
+    csrc = ROOT / "w4a4_mxfp4_gemm_amd" / "csrc"
+    files = ([csrc / n for n in KERNEL_SOURCES[tag]] if tag else sorted(csrc.glob("*")))
     h = hashlib.sha256()
-    for f in sorted((ROOT / "w4a4_mxfp4_gemm_amd" / "csrc").glob("*")):
+    for f in files:
         h.update(f.read_bytes())
     return h.hexdigest()[:16]
 
 
 def recorded_traffic(kernel_tag):
     """HBM bytes per dispatch measured by rocprofv3 PMC runs (profiles/), valid
-    only while the kernel sources hash to the digest stored with them."""
+    only while the kernel's sources hash to the digest stored with them."""
     f = ROOT / "profiles" / f"{kernel_tag}_traffic.txt"
     if not f.exists():
         return None
@@ -81,7 +94,7 @@ def recorded_traffic(kernel_tag):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_digest") != kernel_source_digest():
+    if kv.get("kernel_source_digest") != kernel_source_digest(kernel_tag):
         return None
     try:
         return float(kv["hbm_bytes_per_dispatch"])
@@ -401,7 +414,7 @@ def layerwise_workload(torch, mx, synth):
         gbps = b / (tt * 1e-3) / 1e9
         roof = {"kernel": "mxfp4_requant_from_nvfp4", "bound": "hbm", "achieved": round(gbps, 1),
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
-                "traffic": recorded_traffic("requant_layer")}
+                "traffic": recorded_traffic("requant")}
         cfg = {"workload": "layerwise load: 48 MoE layers x 128 experts x ([2048,4096] + "
                            "[4096,1024]) NVFP4 -> MXFP4, 5% of tensors excluded",
                "tensors_requantized": n_tensors, "launches": len(runs)}
