@@ -46,8 +46,9 @@
 //   read half 0 of stage kt+1;  MFMAs on half 1;  wait for the reads
 // The compiler cannot tell which buffer an LDS read touches while loads into
 // the other are in flight, and would drain every load before each read, so
-// the operand reads are ds_read instructions in inline assembly with explicit
-// lgkmcnt waits.
+// the LDS-DMA loads are issued from inline assembly (invisible to its wait
+// insertion) and ordered by the kernel's own vmcnt waits and barriers; the
+// LDS reads are ordinary loads whose lgkmcnt waits the compiler places.
 #include "mx_device.h"
 #include "launch.h"
 
@@ -92,21 +93,33 @@ typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
 __device__ __forceinline__ uint32_t lds_addr(const lds_u8* p) { return (uint32_t)(uintptr_t)p; }
 
-// Raw buffer descriptor over [base, base + bytes): loads past the end read 0.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                             0x00020000);
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor over [base, base + bytes) (stride 0; loads past the
+// end read 0): base address, num_records, and the gfx950 format word.
+__device__ __forceinline__ v4i make_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    return v4i{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xFFFFu), (int)bytes, 0x00020000};
 }
 
 struct Operands {
-    __amdgpu_buffer_rsrc_t w, ws, x, xs;
+    v4i w, ws, x, xs;
 };
 
 // One 16-byte-per-lane buffer load into LDS: the wavefront's 64 lanes fill
-// 1 KiB of LDS starting at `dst` (lane order), each from its own voffset.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, lds_u8* dst, uint32_t voff,
-                                      uint32_t soff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, AS_LDS(dst), 16, voff, soff, 0, 0);
+// 1 KiB of LDS starting at `dst` (lane order, M0 = dst), each lane from its
+// own voffset.  Written as inline assembly on purpose: the compiler then
+// does not see these LDS writes, so it does not drain them before every LDS
+// read (it cannot tell the buffers apart); the kernel orders them itself
+// with explicit vmcnt waits and barriers.
+__device__ __forceinline__ void dma16(v4i r, lds_u8* dst, uint32_t voff, uint32_t soff) {
+    const v4i rs = {__builtin_amdgcn_readfirstlane(r[0]), __builtin_amdgcn_readfirstlane(r[1]),
+                    __builtin_amdgcn_readfirstlane(r[2]), __builtin_amdgcn_readfirstlane(r[3])};
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(lds_addr(dst))), "v"(voff), "s"(rs),
+                   "s"(__builtin_amdgcn_readfirstlane(soff))
+                 : "memory", "m0");
 }
 
 // Per-lane byte offsets of this thread's loads (constant over K; the K
@@ -156,15 +169,56 @@ __device__ __forceinline__ void load_codes(lds_u8* lds, const Operands& op,
         dma16(op.x, x + (wave * S::XLOADS + i) * 1024, o.x[i], k);
 }
 
-// One operand's scales for chunk c (stages 2c, 2c+1): 16 bytes per row, 256
-// rows (an activation tile of fewer rows repeats its last row).
+// One operand's scales for chunk c (stages 2c, 2c+1) into ring slot `slot`:
+// 16 bytes per row, 256 rows (an activation tile of fewer rows repeats its
+// last row).
 template <class S>
 __device__ __forceinline__ void load_scales(lds_u8* lds, const Operands& op,
-                                            const LoadOffsets<S>& o, bool weights, int c) {
+                                            const LoadOffsets<S>& o, bool weights, int c,
+                                            int slot) {
     const int wave = threadIdx.x >> 6;
-    lds_u8* dst = lds + S::SCALE_BASE + (c % 3) * SCALE_CHUNK + (weights ? 0 : SCALE_OPERAND) +
+    lds_u8* dst = lds + S::SCALE_BASE + slot * SCALE_CHUNK + (weights ? 0 : SCALE_OPERAND) +
                   wave * 1024;
     dma16(weights ? op.ws : op.xs, dst, weights ? o.ws : o.xs, (uint32_t)c * 16);
+}
+
+// Everything a thread needs to fetch one output tile's operands.
+template <class S>
+struct TileSrc {
+    Operands op;
+    LoadOffsets<S> o;
+};
+
+template <class S>
+__device__ __forceinline__ TileSrc<S> tile_src(const uint8_t* x, const uint8_t* xs,
+                                               const uint8_t* w, const uint8_t* ws, int64_t m0,
+                                               int64_t m_end, int64_t n0, int64_t N, int64_t K) {
+    const int64_t ldc = K / 2, lds_ = K / 32;
+    TileSrc<S> t;
+    t.op = Operands{make_rsrc(w, (uint32_t)(N * ldc)), make_rsrc(ws, (uint32_t)(N * lds_)),
+                    make_rsrc(x, (uint32_t)(m_end * ldc)), make_rsrc(xs, (uint32_t)(m_end * lds_))};
+    t.o = load_offsets<S>(n0, N, m0, m_end, ldc, lds_);
+    return t;
+}
+
+// Field-wise uniform select between two tiles' sources.
+template <class S>
+__device__ __forceinline__ TileSrc<S> pick(bool p, const TileSrc<S>& a, const TileSrc<S>& b) {
+    TileSrc<S> t;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        t.op.w[k] = p ? a.op.w[k] : b.op.w[k];
+        t.op.ws[k] = p ? a.op.ws[k] : b.op.ws[k];
+        t.op.x[k] = p ? a.op.x[k] : b.op.x[k];
+        t.op.xs[k] = p ? a.op.xs[k] : b.op.xs[k];
+    }
+#pragma unroll
+    for (int i = 0; i < S::WLOADS; ++i) t.o.w[i] = p ? a.o.w[i] : b.o.w[i];
+#pragma unroll
+    for (int i = 0; i < S::XLOADS; ++i) t.o.x[i] = p ? a.o.x[i] : b.o.x[i];
+    t.o.ws = p ? a.o.ws : b.o.ws;
+    t.o.xs = p ? a.o.xs : b.o.xs;
+    return t;
 }
 
 // vmcnt wait with the count packed into bits 3:0 and 15:14 (expcnt and
@@ -196,13 +250,16 @@ struct Scales {
     uint32_t w[S::NB], x[S::MB];
 };
 
+// Plain LDS reads: the compiler tracks their lgkmcnt itself.
+typedef __attribute__((address_space(3))) const v4u lds_v4u;
+typedef __attribute__((address_space(3))) const uint32_t lds_u32;
 template <int OFF>
 __device__ __forceinline__ void ds_read_b128(v4u& r, uint32_t addr) {
-    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+    r = *reinterpret_cast<lds_v4u*>((uintptr_t)(addr + OFF));
 }
 template <int OFF>
 __device__ __forceinline__ void ds_read_b32(uint32_t& r, uint32_t addr) {
-    asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+    r = *reinterpret_cast<lds_u32*>((uintptr_t)(addr + OFF));
 }
 
 // Lane-constant LDS offsets.  Row r32 of block i sits at
@@ -228,42 +285,29 @@ __device__ __forceinline__ ReadOffsets read_offsets(int wn, int wm) {
     return r;
 }
 
-// Wait for this wave's LDS reads and make the fragment registers depend on
-// the wait, so no use of them can be scheduled before it.
+// End of a half-stage's reads.  The reads are ordinary loads, so the
+// compiler places the lgkmcnt waits before the first use of each fragment.
 template <class S>
-__device__ __forceinline__ void settle(Half<S>& f) {
-    static_assert(S::NB >= 2, "the wait is tied to the first two weight blocks");
-    asm volatile("s_waitcnt lgkmcnt(0)"
-                 : "+v"(f.w[0][0]), "+v"(f.w[0][1]), "+v"(f.w[1][0]), "+v"(f.w[1][1]));
-#pragma unroll
-    for (int i = 2; i < S::NB; ++i) asm volatile("" : "+v"(f.w[i][0]), "+v"(f.w[i][1]));
-#pragma unroll
-    for (int j = 0; j < S::MB; ++j) asm volatile("" : "+v"(f.x[j][0]), "+v"(f.x[j][1]));
-}
+__device__ __forceinline__ void settle(Half<S>&) {}
 template <class S>
-__device__ __forceinline__ void settle(Half<S>& f, Scales<S>& sc) {
-    settle(f);
-#pragma unroll
-    for (int i = 0; i < S::NB; ++i) asm volatile("" : "+v"(sc.w[i]));
-#pragma unroll
-    for (int j = 0; j < S::MB; ++j) asm volatile("" : "+v"(sc.x[j]));
-}
+__device__ __forceinline__ void settle(Half<S>&, Scales<S>&) {}
 
 // One operand load of a stage, selected by index: weight codes, then
-// activation codes, then the stage's scale half-chunk.
+// activation codes (both from `cs`), then the stage's scale half-chunk
+// (from `ss`: chunk `chunk` of that tile into ring slot `slot`).
 template <class S, int Q>
-__device__ __forceinline__ void load_op(lds_u8* lds, const Operands& op, const LoadOffsets<S>& o,
-                                        int buf, int kt, bool scale_w, int chunk) {
+__device__ __forceinline__ void load_op(lds_u8* lds, const TileSrc<S>& cs, const TileSrc<S>& ss,
+                                        int buf, int kt, bool scale_w, int chunk, int slot) {
     const int wave = threadIdx.x >> 6;
     if constexpr (Q < S::WLOADS) {
-        dma16(op.w, lds + buf * S::CODE_STAGE + (wave * S::WLOADS + Q) * 1024, o.w[Q],
+        dma16(cs.op.w, lds + buf * S::CODE_STAGE + (wave * S::WLOADS + Q) * 1024, cs.o.w[Q],
               (uint32_t)kt * BKB);
     } else if constexpr (Q < S::WLOADS + S::XLOADS) {
         constexpr int i = Q - S::WLOADS;
-        dma16(op.x, lds + buf * S::CODE_STAGE + S::W_OPERAND + (wave * S::XLOADS + i) * 1024,
-              o.x[i], (uint32_t)kt * BKB);
+        dma16(cs.op.x, lds + buf * S::CODE_STAGE + S::W_OPERAND + (wave * S::XLOADS + i) * 1024,
+              cs.o.x[i], (uint32_t)kt * BKB);
     } else {
-        load_scales<S>(lds, op, o, scale_w, chunk);
+        load_scales<S>(lds, ss.op, ss.o, scale_w, chunk, slot);
     }
 }
 
@@ -370,73 +414,76 @@ constexpr int second_half_read(int q) {
     return v < 0 ? 0 : (v > R ? R : v);
 }
 
-// The pipelined main loop for one output tile: x rows [m0, min(m0+BM, m_end))
-// of the activations (row m_end - 1 is the last one the operand may touch),
-// w rows [n0, n0+BN) of the weights.  Only the first JL 32-row activation
-// blocks of each wave are multiplied (the caller guarantees the rest are
-// past m_end).
-template <class S, int JL, bool OUT_BF16>
-__device__ __forceinline__ void tile_gemm(lds_u8* lds, const uint8_t* __restrict__ x,
-                                          const uint8_t* __restrict__ xs,
-                                          const uint8_t* __restrict__ w,
-                                          const uint8_t* __restrict__ ws, int64_t m0,
-                                          int64_t m_end, int64_t n0, int64_t N, int64_t K,
-                                          void* __restrict__ y) {
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wn = wave % S::WGN, wm = wave / S::WGN;
-    const int64_t ldc = K / 2, lds_ = K / 32;
-    const int nkt = (int)(K / 256);           // even: K % 512 == 0
-    const int last_chunk = nkt / 2 - 1;
-
-    v16f acc[S::NB][S::MB];
-#pragma unroll
-    for (int i = 0; i < S::NB; ++i)
-#pragma unroll
-        for (int j = 0; j < S::MB; ++j) acc[i][j] = v16f{};
-
-    const Operands op{make_rsrc(w, (uint32_t)(N * ldc)), make_rsrc(ws, (uint32_t)(N * lds_)),
-                      make_rsrc(x, (uint32_t)(m_end * ldc)),
-                      make_rsrc(xs, (uint32_t)(m_end * lds_))};
-    const LoadOffsets<S> o = load_offsets<S>(n0, N, m0, m_end, ldc, lds_);
-    const ReadOffsets ro = read_offsets<S>(wn, wm);
-    const uint32_t lds0 = lds_addr(lds);
-
-    // Loads of stage s >= 2 also bring half of scale chunk s/2 + 1 (weights
-    // for even s, activations for odd s); chunk c is complete once stage
-    // 2c-1's loads land and is first used by stage 2c.  Loads past the last
-    // stage or chunk are clamped to it (they land in buffers nobody reads
-    // again), so every stage issues the same number of loads.
-    auto code_addr = [&](int s) { return lds0 + (uint32_t)((s & 1) * S::CODE_STAGE); };
-    auto scale_addr = [&](int s) {
-        return lds0 + (uint32_t)(S::SCALE_BASE + ((s / 2) % 3) * SCALE_CHUNK + (s & 1) * 8);
-    };
-
-    // Prologue: stage 0 with chunks 0 and 1, stage 1; then stage 0's first half.
-    load_codes<S>(lds, op, o, 0, 0);
-    load_scales<S>(lds, op, o, true, 0);
-    load_scales<S>(lds, op, o, false, 0);
-    load_scales<S>(lds, op, o, true, last_chunk >= 1 ? 1 : 0);
-    load_scales<S>(lds, op, o, false, last_chunk >= 1 ? 1 : 0);
-    load_codes<S>(lds, op, o, 1, nkt > 1 ? 1 : 0);
-    wait_vm<S::WLOADS + S::XLOADS>();
-    __builtin_amdgcn_s_barrier();
-
+// Pipeline registers of one wavefront: two half-stages of fragments and the
+// scale words of the current and the next stage.
+template <class S>
+struct Pipe {
     Half<S> h0, h1;
     Scales<S> sc_cur, sc_nxt;
-    read_range<S, 0, 0, S::CODE_READS + S::SCALE_READS>(h0, sc_cur, code_addr(0),
-                                                        scale_addr(0), ro);
-    settle(h0, sc_cur);
+};
 
+__device__ __forceinline__ uint32_t code_addr(uint32_t lds0, int s, int code_stage) {
+    return lds0 + (uint32_t)((s & 1) * code_stage);
+}
+// Scale words of stage s of a tile whose chunk 0 sits in ring slot cbase % 3.
+template <class S>
+__device__ __forceinline__ uint32_t scale_addr(uint32_t lds0, int cbase, int s) {
+    return lds0 + (uint32_t)(S::SCALE_BASE + ((cbase + s / 2) % 3) * SCALE_CHUNK + (s & 1) * 8);
+}
+
+// Stage loads and their scale halves.  Stage s of a tile (nkt stages, chunks
+// 0..nkt/2-1, chunk 0 in ring slot cbase % 3) brings half s&1 (weights, then
+// activations) of chunk s/2 + 1; chunk 0 is loaded on its own before stage 0.
+// When that chunk does not exist (the last two stages), the slot carries
+// chunk 0 of the next tile if one is being prefetched, else it reloads the
+// tile's last chunk (the same bytes, harmless).
+//
+// Prologue: chunk 0, stage 0, stage 1; wait for stage 0; read its first half.
+template <class S>
+__device__ __forceinline__ void prologue(lds_u8* lds, const TileSrc<S>& src, int nkt, int cbase,
+                                         Pipe<S>& pp, const ReadOffsets& ro) {
+    const int last_chunk = nkt / 2 - 1;
+    const int c1 = last_chunk >= 1 ? 1 : 0;
+    load_codes<S>(lds, src.op, src.o, 0, 0);
+    load_scales<S>(lds, src.op, src.o, true, 0, cbase % 3);
+    load_scales<S>(lds, src.op, src.o, false, 0, cbase % 3);
+    load_scales<S>(lds, src.op, src.o, true, c1, (cbase + c1) % 3);
+    load_scales<S>(lds, src.op, src.o, false, c1, (cbase + c1) % 3);
+    load_codes<S>(lds, src.op, src.o, 1, nkt > 1 ? 1 : 0);
+    wait_vm<S::WLOADS + S::XLOADS>();
+    __builtin_amdgcn_s_barrier();
+    const uint32_t lds0 = lds_addr(lds);
+    read_range<S, 0, 0, S::CODE_READS + S::SCALE_READS>(
+        pp.h0, pp.sc_cur, code_addr(lds0, 0, S::CODE_STAGE), scale_addr<S>(lds0, cbase, 0), ro);
+    settle(pp.h0, pp.sc_cur);
+}
+
+// The pipelined main loop of one output tile (its stages 0 and 1 are loaded
+// and stage 0's first half is in pp.h0 / pp.sc_cur).  Only the first JL
+// 32-row activation blocks of each wave are multiplied.  With PREFETCH, the
+// loads of stages nkt and nkt+1 are the next tile's stages 0 and 1 (and its
+// scale chunks 0 and 1), and the loop ends with the next tile's stage 0
+// first half in pp.h0 / pp.sc_cur: the next tile needs no prologue.
+// PREFETCH needs nkt >= 4.  Per stage kt (one barrier per stage):
+//   read half 1 of stage kt;  MFMAs on half 0;  wait for the reads
+//   wait for stage kt+1's loads; barrier; load stage kt+2 (+ one scale half-chunk)
+//   read half 0 of stage kt+1;  MFMAs on half 1;  wait for the reads
+template <class S, int JL, bool PREFETCH>
+__device__ __forceinline__ void main_loop(lds_u8* lds, const TileSrc<S>& cur,
+                                          const TileSrc<S>& nxt, int nkt, int cbase, Pipe<S>& pp,
+                                          v16f (&acc)[S::NB][S::MB], const ReadOffsets& ro) {
+    const int last_chunk = nkt / 2 - 1;
+    const uint32_t lds0 = lds_addr(lds);
     for (int kt = 0; kt < nkt; ++kt) {
         // first half: MFMAs on stage kt's K-steps 0-1, reads of its K-steps 2-3
         {
-            const uint32_t codes = code_addr(kt);
+            const uint32_t codes = code_addr(lds0, kt, S::CODE_STAGE);
             Scales<S> unused;
-            mfma_half<S, JL, 0>(h0, sc_cur, acc, [&](auto q) {
+            mfma_half<S, JL, 0>(pp.h0, pp.sc_cur, acc, [&](auto q) {
                 constexpr int Q = decltype(q)::value;
-                if constexpr (Q < S::CODE_READS) read_op<S, 1, Q>(h1, unused, codes, 0, ro);
+                if constexpr (Q < S::CODE_READS) read_op<S, 1, Q>(pp.h1, unused, codes, 0, ro);
             });
-            settle(h1);
+            settle(pp.h1);
         }
         // stage kt+1 landed for every wave; every wave is done reading stage kt
         wait_vm<0>();
@@ -445,26 +492,45 @@ __device__ __forceinline__ void tile_gemm(lds_u8* lds, const uint8_t* __restrict
         // kt's buffer, reads of stage kt+1's K-steps 0-1 and scales
         {
             const int s2 = kt + 2;
-            const int ks = s2 < nkt ? s2 : nkt - 1;
+            const bool code_next = PREFETCH && s2 >= nkt;
+            const int ks = s2 < nkt ? s2 : (PREFETCH ? s2 - nkt : nkt - 1);
             const int c = s2 / 2 + 1;
-            const int chunk = c <= last_chunk ? c : last_chunk;
+            bool scale_next = false;
+            int chunk = c, slot = (cbase + c) % 3;
+            if (c > last_chunk) {
+                if (PREFETCH) {
+                    scale_next = true;
+                    chunk = s2 < nkt ? 0 : 1;
+                    slot = (cbase + last_chunk + 1 + chunk) % 3;
+                } else {
+                    chunk = last_chunk;
+                    slot = (cbase + last_chunk) % 3;
+                }
+            }
             const bool scale_w = (s2 & 1) == 0;
-            const uint32_t codes = code_addr(kt + 1), scales = scale_addr(kt + 1);
-            mfma_half<S, JL, 1>(h1, sc_cur, acc, [&](auto q) {
+            const uint32_t codes = code_addr(lds0, kt + 1, S::CODE_STAGE);
+            const uint32_t scales = scale_addr<S>(lds0, cbase, kt + 1);
+            const TileSrc<S> cs = PREFETCH ? pick(code_next, nxt, cur) : cur;
+            const TileSrc<S> ss = PREFETCH ? pick(scale_next, nxt, cur) : cur;
+            mfma_half<S, JL, 1>(pp.h1, pp.sc_cur, acc, [&](auto q) {
                 constexpr int Q = decltype(q)::value;
                 if constexpr (Q < S::LOADS_PER_STAGE)
-                    load_op<S, Q>(lds, op, o, s2 & 1, ks, scale_w, chunk);
+                    load_op<S, Q>(lds, cs, ss, s2 & 1, ks, scale_w, chunk, slot);
                 read_range<S, 0, second_half_read<S>(Q), second_half_read<S>(Q + 1)>(
-                    h0, sc_nxt, codes, scales, ro);
+                    pp.h0, pp.sc_nxt, codes, scales, ro);
             });
-            settle(h0, sc_nxt);
-            sc_cur = sc_nxt;
+            settle(pp.h0, pp.sc_nxt);
+            pp.sc_cur = pp.sc_nxt;
         }
     }
-    // drain the surplus loads before the workgroup's LDS can be reused
-    wait_vm<0>();
+}
 
-    store_tile<S, OUT_BF16>(acc, y, m0, m_end, n0, N, wn, wm);
+template <class S>
+__device__ __forceinline__ void zero_acc(v16f (&acc)[S::NB][S::MB]) {
+#pragma unroll
+    for (int i = 0; i < S::NB; ++i)
+#pragma unroll
+        for (int j = 0; j < S::MB; ++j) acc[i][j] = v16f{};
 }
 
 // XCD-aware tile order: workgroup ids are dealt to the 8 XCDs round-robin, so
@@ -498,22 +564,38 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(
     const int tiles_n = (int)((N + S::BN - 1) / S::BN);
     int tm, tn;
     if (!tile_coords(tiles_m, tiles_n, gm, tm, tn)) return;
-    tile_gemm<S, S::MB, OUT_BF16>((lds_u8*)smem, x, xs, w, ws, (int64_t)tm * S::BM, M,
-                                  (int64_t)tn * S::BN, N, K, y);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wn = wave % S::WGN, wm = wave / S::WGN;
+    const int64_t m0 = (int64_t)tm * S::BM, n0 = (int64_t)tn * S::BN;
+    const int nkt = (int)(K / 256);           // even: K % 512 == 0
+    lds_u8* lds = (lds_u8*)smem;
+    const TileSrc<S> src = tile_src<S>(x, xs, w, ws, m0, M, n0, N, K);
+    const ReadOffsets ro = read_offsets<S>(wn, wm);
+    v16f acc[S::NB][S::MB];
+    zero_acc<S>(acc);
+    Pipe<S> pp;
+    prologue<S>(lds, src, nkt, 0, pp, ro);
+    main_loop<S, S::MB, false>(lds, src, src, nkt, 0, pp, acc, ro);
+    wait_vm<0>();                             // drain the surplus loads
+    store_tile<S, OUT_BF16>(acc, y, m0, M, n0, N, wn, wm);
 }
 
 // ---------------------------------------------------------------------------
-// Grouped (MoE) GEMM.  Work items are (expert e, weight tile tn, activation
-// tile mt) with mt < ceil(rows_e / BM), ordered by e, then tn, then mt, and
-// numbered 0..total-1.  Every workgroup derives the numbering from the
-// offset table itself (one wavefront scans it), then takes item
-//   t = xcd * ceil(total / 8) + local      (xcd = id % 8, local = id / 8),
-// so each XCD walks a contiguous run: the activation tiles of one weight tile
-// run back to back on one XCD (the weight rows are fetched from HBM once and
-// re-read from its L2), and an expert's rows stay in that L2 across its
-// weight tiles.  The grid is sized for the worst case; surplus workgroups
-// exit at once.
+// Grouped (MoE) GEMM, persistent.  Work items are (expert e, weight tile tn,
+// activation tile mt) with mt < ceil(rows_e / BM), ordered by e, then tn, then
+// mt, and numbered 0..total-1.  Each workgroup first builds, in LDS, the
+// table of the first item of every expert (one wavefront scans the clamped
+// offset table), then walks the items
+//   t = xcd * ceil(total / 8) + local + k * (grid / 8)   (xcd = id % 8, local = id / 8)
+// so each XCD's workgroups run a contiguous range together: the activation
+// tiles of one weight tile run side by side on one XCD (the weight rows come
+// from HBM once and from its L2 after), and an expert's rows stay in that L2
+// across its weight tiles.  While a tile's last stages run, the next tile's
+// first two stages are already loading into the freed buffers.
 // ---------------------------------------------------------------------------
+constexpr int GROUP_MAX_E = 2048;
+constexpr int GROUP_TABLE_BYTES = (3 * GROUP_MAX_E + 1) * 4;
+
 __device__ __forceinline__ int wave_inclusive_scan(int v) {
     const int lane = threadIdx.x & 63;
 #pragma unroll
@@ -525,62 +607,95 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
 }
 
 struct GroupItem {
-    int e, tn;
-    int m0, m_end;
+    int e, tn, m0, m_end, jl;   // jl: 32-row blocks of the tile holding rows (1..4)
 };
 
-// Row range of expert e, clamped into [0, total_M) and non-decreasing.
-__device__ __forceinline__ void expert_rows(const int32_t* __restrict__ offsets, int e,
-                                            int total_M, int& a0, int& a1) {
-    a0 = offsets[e];
-    a1 = offsets[e + 1];
-    a0 = a0 < 0 ? 0 : (a0 > total_M ? total_M : a0);
-    a1 = a1 < a0 ? a0 : (a1 > total_M ? total_M : a1);
-}
+// first[e] = number of the expert's first item (first[E] = total),
+// row0[e], row1[e] = its clamped row range [row0, row1).
+struct GroupTable {
+    int* first;
+    int* row0;
+    int* row1;
+};
 
 template <int BM>
-__device__ GroupItem find_item(const int32_t* __restrict__ offsets, int E, int total_M,
-                               int tiles_n) {
+__device__ void build_table(const int32_t* __restrict__ offsets, int E, int total_M, int tiles_n,
+                            GroupTable tb) {
     const int lane = threadIdx.x & 63;
-    GroupItem it{-1, 0, 0, 0};
-    int total = 0;
-    for (int e0 = 0; e0 < E; e0 += 64) {
-        int cnt = 0;
-        if (e0 + lane < E) {
-            int a0, a1;
-            expert_rows(offsets, e0 + lane, total_M, a0, a1);
-            cnt = (a1 - a0 + BM - 1) / BM * tiles_n;
-        }
-        total += __shfl(wave_inclusive_scan(cnt), 63, 64);
-    }
-    const int per_xcd = (total + 7) / 8;
-    const int id = (int)blockIdx.x;
-    const int local = id / 8;
-    const int t = (id % 8) * per_xcd + local;
-    if (local >= per_xcd || t >= total) return it;
     int base = 0;
     for (int e0 = 0; e0 < E; e0 += 64) {
-        int cnt = 0, a0 = 0, a1 = 0;
-        if (e0 + lane < E) {
-            expert_rows(offsets, e0 + lane, total_M, a0, a1);
-            cnt = (a1 - a0 + BM - 1) / BM * tiles_n;
+        const int e = e0 + lane;
+        int a0 = 0, a1 = 0;
+        if (e < E) {
+            a0 = offsets[e];
+            a1 = offsets[e + 1];
+            a0 = a0 < 0 ? 0 : (a0 > total_M ? total_M : a0);
+            a1 = a1 < a0 ? a0 : (a1 > total_M ? total_M : a1);
         }
+        const int cnt = (a1 - a0 + BM - 1) / BM * tiles_n;
         const int incl = wave_inclusive_scan(cnt);
-        const int lo = base + incl - cnt;
-        const uint64_t hit = __ballot(cnt > 0 && t >= lo && t < lo + cnt);
-        if (hit) {
-            const int src = __ffsll((unsigned long long)hit) - 1;
-            const int r = __shfl(t - lo, src, 64);
-            const int mts = __shfl(cnt / tiles_n, src, 64);
-            it.e = e0 + src;
-            it.tn = r / mts;
-            it.m0 = __shfl(a0, src, 64) + (r % mts) * BM;
-            it.m_end = __shfl(a1, src, 64);
-            return it;
+        if (e < E) {
+            tb.first[e] = base + incl - cnt;
+            tb.row0[e] = a0;
+            tb.row1[e] = a1;
         }
         base += __shfl(incl, 63, 64);
     }
+    if (lane == 0) tb.first[E] = base;
+}
+
+// Item t (< total), searching experts from `from` on (items only grow).
+template <int BM>
+__device__ __forceinline__ GroupItem decode_item(GroupTable tb, int E, int tiles_n, int t,
+                                                 int from) {
+    const int lane = threadIdx.x & 63;
+    int e = -1;
+    for (int e0 = from; e0 < E; e0 += 64) {
+        const int c = e0 + lane;
+        const bool hit = c < E && tb.first[c] <= t && t < tb.first[c + 1];
+        const uint64_t m = __ballot(hit);
+        if (m) {
+            e = e0 + __ffsll((unsigned long long)m) - 1;
+            break;
+        }
+    }
+    GroupItem it;
+    it.e = __builtin_amdgcn_readfirstlane(e);
+    const int a0 = __builtin_amdgcn_readfirstlane(tb.row0[it.e]);
+    const int a1 = __builtin_amdgcn_readfirstlane(tb.row1[it.e]);
+    const int r = t - __builtin_amdgcn_readfirstlane(tb.first[it.e]);
+    const int mts = (a1 - a0 + BM - 1) / BM;
+    it.tn = r / mts;
+    it.m0 = a0 + (r - it.tn * mts) * BM;
+    it.m_end = a1;
+    const int rows = min(a1 - it.m0, BM);
+    it.jl = (rows + 31) / 32;
     return it;
+}
+
+template <class S>
+__device__ __forceinline__ TileSrc<S> item_src(const GroupItem& it, const uint8_t* x,
+                                               const uint8_t* xs, const uint8_t* w,
+                                               const uint8_t* ws, int64_t N, int64_t K) {
+    const int64_t nkb = K / 32;
+    return tile_src<S>(x, xs, w + (int64_t)it.e * N * nkb * 16, ws + (int64_t)it.e * N * nkb,
+                       it.m0, it.m_end, (int64_t)it.tn * S::BN, N, K);
+}
+
+template <class S, bool PREFETCH>
+__device__ __forceinline__ void main_loop_jl(int jl, lds_u8* lds, const TileSrc<S>& cur,
+                                             const TileSrc<S>& nxt, int nkt, int cbase,
+                                             Pipe<S>& pp, v16f (&acc)[S::NB][S::MB],
+                                             const ReadOffsets& ro) {
+    static_assert(S::WGM == 1 && S::MB == 4, "one wave row of four 32-row blocks");
+    if (jl >= 4)
+        main_loop<S, 4, PREFETCH>(lds, cur, nxt, nkt, cbase, pp, acc, ro);
+    else if (jl == 3)
+        main_loop<S, 3, PREFETCH>(lds, cur, nxt, nkt, cbase, pp, acc, ro);
+    else if (jl == 2)
+        main_loop<S, 2, PREFETCH>(lds, cur, nxt, nkt, cbase, pp, acc, ro);
+    else
+        main_loop<S, 1, PREFETCH>(lds, cur, nxt, nkt, cbase, pp, acc, ro);
 }
 
 template <bool OUT_BF16>
@@ -590,36 +705,60 @@ __global__ __launch_bounds__(256, 1) void grouped_tiled_kernel(
     const int32_t* __restrict__ offsets, int E, int total_M, int64_t N, int64_t K,
     void* __restrict__ y) {
     using S = GroupShape;
-    __shared__ __attribute__((aligned(16))) uint8_t smem[S::LDS_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t smem[S::LDS_BYTES + GROUP_TABLE_BYTES];
+    lds_u8* lds = (lds_u8*)smem;
+    int* table = reinterpret_cast<int*>(smem + S::LDS_BYTES);
+    const GroupTable tb{table, table + GROUP_MAX_E + 1, table + 2 * GROUP_MAX_E + 1};
     const int tiles_n = (int)((N + S::BN - 1) / S::BN);
-    GroupItem* shared_item = reinterpret_cast<GroupItem*>(smem);
-    if (threadIdx.x < 64) {
-        const GroupItem it = find_item<S::BM>(offsets, E, total_M, tiles_n);
-        if (threadIdx.x == 0) *shared_item = it;
-    }
+    if (threadIdx.x < 64) build_table<S::BM>(offsets, E, total_M, tiles_n, tb);
     __syncthreads();
-    const GroupItem it = *shared_item;
-    __syncthreads();                           // the pipeline reuses this LDS
-    const int e = __builtin_amdgcn_readfirstlane(it.e);
-    if (e < 0) return;
-    const int tn = __builtin_amdgcn_readfirstlane(it.tn);
-    const int m0 = __builtin_amdgcn_readfirstlane(it.m0);
-    const int m_end = __builtin_amdgcn_readfirstlane(it.m_end);
-    const int64_t nkb = K / 32;
-    const uint8_t* we = w + (int64_t)e * N * nkb * 16;
-    const uint8_t* wse = ws + (int64_t)e * N * nkb;
-    const int64_t n0 = (int64_t)tn * S::BN;
-    static_assert(S::WGM == 1 && S::MB == 4, "one wave row of four 32-row blocks");
-    // 32-row blocks of the tile that hold rows of this expert (1..4)
-    const int blocks = (min(m_end - m0, S::BM) + 31) / 32;
-    if (blocks >= 4)
-        tile_gemm<S, 4, OUT_BF16>((lds_u8*)smem, x, xs, we, wse, m0, m_end, n0, N, K, y);
-    else if (blocks == 3)
-        tile_gemm<S, 3, OUT_BF16>((lds_u8*)smem, x, xs, we, wse, m0, m_end, n0, N, K, y);
-    else if (blocks == 2)
-        tile_gemm<S, 2, OUT_BF16>((lds_u8*)smem, x, xs, we, wse, m0, m_end, n0, N, K, y);
-    else
-        tile_gemm<S, 1, OUT_BF16>((lds_u8*)smem, x, xs, we, wse, m0, m_end, n0, N, K, y);
+
+    const int total = __builtin_amdgcn_readfirstlane(tb.first[E]);
+    const int per_xcd = (total + 7) / 8;
+    const int stride = (int)gridDim.x / 8;
+    const int t_end = min((int)(blockIdx.x % 8) * per_xcd + per_xcd, total);
+    int t = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+    if (t >= t_end) return;
+
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wn = wave % S::WGN, wm = wave / S::WGN;
+    const int nkt = (int)(K / 256);           // even: K % 512 == 0
+    const ReadOffsets ro = read_offsets<S>(wn, wm);
+
+    GroupItem it = decode_item<S::BM>(tb, E, tiles_n, t, 0);
+    TileSrc<S> cur = item_src<S>(it, x, xs, w, ws, N, K);
+    v16f acc[S::NB][S::MB];
+    zero_acc<S>(acc);
+    Pipe<S> pp;
+    int cbase = 0;
+    prologue<S>(lds, cur, nkt, cbase, pp, ro);
+    for (;;) {
+        const int tn = t + stride;
+        const bool have_next = tn < t_end;
+        const GroupItem nx = have_next ? decode_item<S::BM>(tb, E, tiles_n, tn, it.e) : it;
+        const TileSrc<S> nxt = item_src<S>(nx, x, xs, w, ws, N, K);
+        const bool prefetch = have_next && nkt >= 4;
+        if (prefetch)
+            main_loop_jl<S, true>(it.jl, lds, cur, nxt, nkt, cbase, pp, acc, ro);
+        else
+            main_loop_jl<S, false>(it.jl, lds, cur, cur, nkt, cbase, pp, acc, ro);
+        if (!prefetch) wait_vm<0>();          // drain the surplus loads
+        store_tile<S, OUT_BF16>(acc, y, it.m0, it.m_end, (int64_t)it.tn * S::BN, N, wn, wm);
+        if (!have_next) break;
+        zero_acc<S>(acc);
+        if (prefetch) {
+            cbase += nkt / 2;
+        } else {
+            // every wave is past its last LDS read of this tile
+            __builtin_amdgcn_s_barrier();
+            cbase = 0;
+            prologue<S>(lds, nxt, nkt, cbase, pp, ro);
+        }
+        it = nx;
+        cur = nxt;
+        t = tn;
+    }
+    wait_vm<0>();
 }
 
 }  // namespace tiled
@@ -640,9 +779,8 @@ bool grouped_tiled_supported(int64_t E, int64_t total_M, int64_t N, int64_t K,
                              const void* a_scales, const void* b_scales) {
     using S = tiled::GroupShape;
     const int64_t bound = ((total_M + S::BM - 1) / S::BM + E) * ((N + S::BN - 1) / S::BN);
-    return K % 512 == 0 && fits_buffer(total_M, K) && fits_buffer(N, K) &&
-           total_M < ((int64_t)1 << 30) && E < ((int64_t)1 << 30) &&
-           bound + 8 < ((int64_t)1 << 31) &&
+    return K % 512 == 0 && E <= tiled::GROUP_MAX_E && fits_buffer(total_M, K) &&
+           fits_buffer(N, K) && total_M < ((int64_t)1 << 30) && bound < ((int64_t)1 << 30) &&
            (reinterpret_cast<uintptr_t>(a_scales) % 4) == 0 &&
            (reinterpret_cast<uintptr_t>(b_scales) % 4) == 0;
 }
@@ -678,8 +816,17 @@ hipError_t launch_grouped_gemm_tiled(const uint8_t* a_codes, const uint8_t* a_sc
                                      int64_t N, int64_t K, void* y, bool out_bf16,
                                      hipStream_t stream) {
     using S = tiled::GroupShape;
+    // one persistent workgroup per CU (the tile's LDS allows no more), never
+    // more workgroups than the largest possible number of work items
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return hipErrorInvalidDevice;
     const int64_t bound = ((total_M + S::BM - 1) / S::BM + E) * ((N + S::BN - 1) / S::BN);
-    const dim3 grid((unsigned)((bound + 7) / 8 * 8));
+    int64_t g = (int64_t)cus / 8 * 8;
+    if (g < 8) g = 8;
+    if (g > (bound + 7) / 8 * 8) g = (bound + 7) / 8 * 8;
+    const dim3 grid((unsigned)g);
     if (out_bf16)
         hipLaunchKernelGGL(tiled::grouped_tiled_kernel<true>, grid, dim3(256), 0, stream,
                            a_codes, a_scales, b_codes, b_scales, offsets, (int)E, (int)total_M, N,
