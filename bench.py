@@ -37,6 +37,7 @@ METRIC = "MXFP4 W4A4 GEMM TFLOP/s (incl. act quant) + requant GB/s, % of rooflin
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 MXFP4_PEAK_TFLOPS = 10100.0     # MI355X dense MXFP4 MFMA
 ROTATE_BYTES = 1 << 30          # > 3x the 256 MiB MALL
+CALIBRATION_BYTES = 512 << 20   # copy kernel of known size for the HBM counters
 
 
 def parse():
@@ -47,6 +48,10 @@ def parse():
     p.add_argument("--workload", default="decode",
                    choices=["decode", "prefill", "moe", "layerwise"])
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--eager", type=int, default=0, metavar="N",
+                   help="counter-collection pass: no graphs and no timing; run a "
+                        "%d MiB copy (the calibration kernel), then every phase "
+                        "N times eagerly" % (CALIBRATION_BYTES >> 20))
     return p.parse_args()
 
 
@@ -414,13 +419,36 @@ def layerwise_workload(torch, mx, synth):
         gbps = b / (tt * 1e-3) / 1e9
         roof = {"kernel": "mxfp4_requant_from_nvfp4", "bound": "hbm", "achieved": round(gbps, 1),
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
-                "traffic": recorded_traffic("requant")}
+                "traffic": recorded_traffic("requant"),
+                "algorithmic_bytes_per_launch": round(b / len(runs)),
+                "avg_launch_us": round(tt / len(runs) * 1e3, 3)}
         cfg = {"workload": "layerwise load: 48 MoE layers x 128 experts x ([2048,4096] + "
                            "[4096,1024]) NVFP4 -> MXFP4, 5% of tensors excluded",
                "tensors_requantized": n_tensors, "launches": len(runs)}
         return gbps, "GB/s", roof, {"ms_all_layers": round(tt, 3)}, cfg
 
     return ph, report, None
+
+
+def eager_pass(torch, ph, n):
+    """For rocprofv3 --pmc runs: an elementwise kernel that reads and writes
+    CALIBRATION_BYTES once each (torch's bitwise_not on u8; its FETCH_SIZE /
+    WRITE_SIZE per byte calibrate the counters), then each phase other than
+    the whole step, n times, eagerly."""
+    src = torch.full((CALIBRATION_BYTES,), 1, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(n):
+        torch.bitwise_not(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+    names = [k for k in ph.fns if k != "step"] or ["step"]
+    for name in names:
+        for i in range(n):
+            ph.fns[name](i % ph.slots)
+        torch.cuda.synchronize()
+        print(f"eager phase {name}: {n} runs", flush=True)
+    print(json.dumps({"eager": n, "calibration_copy_bytes": CALIBRATION_BYTES,
+                      "phases": names}), flush=True)
 
 
 def main():
@@ -439,6 +467,9 @@ def main():
     make = {"decode": decode_workload, "prefill": prefill_workload, "moe": moe_workload,
             "layerwise": layerwise_workload}[args.workload]
     ph, report, cpu_baseline = make(torch, mx, synth)
+    if args.eager:
+        eager_pass(torch, ph, args.eager)
+        return
     ph.capture()
     # the contract's timed region: exactly `steps` steps after `warmup` untimed ones
     t = {"step": ph.time("step", args.steps, args.warmup)}
