@@ -122,6 +122,12 @@ __device__ __forceinline__ void dma16(v4i r, lds_u8* dst, uint32_t voff, uint32_
                  : "memory", "m0");
 }
 
+// The wavefront's index in the workgroup as a scalar (uniform) value, so the
+// LDS destinations of the DMA loads are computed in scalar registers.
+__device__ __forceinline__ int wave_id() {
+    return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+}
+
 // Per-lane byte offsets of this thread's loads (constant over K; the K
 // position enters as the scalar offset).  Rows past an operand's end are
 // clamped to its last row: those results are never stored.
@@ -157,7 +163,7 @@ __device__ __forceinline__ LoadOffsets<S> load_offsets(int64_t n0, int64_t N, in
 template <class S>
 __device__ __forceinline__ void load_codes(lds_u8* lds, const Operands& op,
                                            const LoadOffsets<S>& o, int buf, int kt) {
-    const int wave = threadIdx.x >> 6;
+    const int wave = wave_id();
     const uint32_t k = (uint32_t)kt * BKB;
     lds_u8* w = lds + buf * S::CODE_STAGE;
     lds_u8* x = w + S::W_OPERAND;
@@ -176,7 +182,7 @@ template <class S>
 __device__ __forceinline__ void load_scales(lds_u8* lds, const Operands& op,
                                             const LoadOffsets<S>& o, bool weights, int c,
                                             int slot) {
-    const int wave = threadIdx.x >> 6;
+    const int wave = wave_id();
     lds_u8* dst = lds + S::SCALE_BASE + slot * SCALE_CHUNK + (weights ? 0 : SCALE_OPERAND) +
                   wave * 1024;
     dma16(weights ? op.ws : op.xs, dst, weights ? o.ws : o.xs, (uint32_t)c * 16);
@@ -298,7 +304,7 @@ __device__ __forceinline__ void settle(Half<S>&, Scales<S>&) {}
 template <class S, int Q>
 __device__ __forceinline__ void load_op(lds_u8* lds, const TileSrc<S>& cs, const TileSrc<S>& ss,
                                         int buf, int kt, bool scale_w, int chunk, int slot) {
-    const int wave = threadIdx.x >> 6;
+    const int wave = wave_id();
     if constexpr (Q < S::WLOADS) {
         dma16(cs.op.w, lds + buf * S::CODE_STAGE + (wave * S::WLOADS + Q) * 1024, cs.o.w[Q],
               (uint32_t)kt * BKB);
