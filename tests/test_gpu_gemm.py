@@ -31,7 +31,11 @@ def to_dev(*ts):
 
 # ---- random operands, every tile edge ------------------------------------------------
 SHAPES = [(1, 1, 32), (1, 300, 4096), (7, 17, 96), (16, 256, 512), (33, 200, 544),
-          (64, 129, 1024), (65, 260, 1056), (100, 64, 4096), (130, 131, 2080)]
+          (64, 129, 1024), (65, 260, 1056), (100, 64, 4096), (130, 131, 2080),
+          # weight-streaming kernel: every activation-block count, K = 2048 and 4096,
+          # ragged N, four and eight wavefronts
+          (5, 1000, 2048), (16, 16, 4096), (17, 300, 4096), (40, 72, 2048), (48, 257, 4096),
+          (64, 4099, 4096), (61, 1040, 2048)]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)
