@@ -38,6 +38,8 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 MXFP4_PEAK_TFLOPS = 10100.0     # MI355X dense MXFP4 MFMA
 ROTATE_BYTES = 1 << 30          # > 3x the 256 MiB MALL
 CALIBRATION_BYTES = 512 << 20   # copy kernel of known size for the HBM counters
+PREFILL_SLOTS = 16              # activation copies: 16 x 176 MiB over the three shapes
+MOE_SLOTS = 8                   # token / down-input copies for the MoE workload
 
 
 def parse():
@@ -112,12 +114,14 @@ class Phases:
     the graphs back to back between two HIP events recorded on the stream the
     kernels run on.  The step phase gets one graph per rotation slot (one
     replay = one step); every other phase gets a single graph holding all slots
-    in turn, so short kernels run back to back on the GPU and the time per slot
-    is not bounded by the host's graph-launch rate."""
+    in turn, repeated until it holds at least `min_launches` passes, so short
+    kernels run back to back on the GPU and the time per pass is not bounded
+    by the host's graph-launch rate."""
 
-    def __init__(self, torch, slots):
+    def __init__(self, torch, slots, min_launches=20):
         self.torch = torch
         self.slots = slots
+        self.rounds = max(1, math.ceil(min_launches / slots))
         self.fns = {}
         self.graphs = {}
 
@@ -140,8 +144,9 @@ class Phases:
             else:
                 g = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(g):
-                    for r in range(self.slots):
-                        fn(r)
+                    for _ in range(self.rounds):
+                        for r in range(self.slots):
+                            fn(r)
                 gs = [g]
             self.graphs[name] = gs
         torch.cuda.synchronize()
@@ -150,7 +155,7 @@ class Phases:
         """Average milliseconds per slot (per step for the step phase)."""
         torch = self.torch
         gs = self.graphs[name]
-        per_replay = 1 if name == "step" else self.slots
+        per_replay = 1 if name == "step" else self.slots * self.rounds
         for i in range(warmup):
             gs[i % len(gs)].replay()
         torch.cuda.synchronize()
@@ -269,24 +274,28 @@ def prefill_workload(torch, mx, synth):
         c, s, g = synth.nvfp4_from_bf16(w)
         del w
         wc, wsc = mx.mxfp4_requant_from_nvfp4(c, s, g.reshape(1))
-        x = synth.activations(M, K, seed=xs_, outlier_seed=os_, device=d)
-        xq = (torch.empty((M, K // 2), dtype=torch.uint8, device=d),
-              torch.empty((M, K // 32), dtype=torch.uint8, device=d))
+        x0 = synth.activations(M, K, seed=xs_, outlier_seed=os_, device=d)
+        # rotated copies of the activations and their quantized form, so the
+        # activation bytes come from HBM rather than the Infinity Cache
+        x = [x0.clone() for _ in range(PREFILL_SLOTS)]
+        xq = [(torch.empty((M, K // 2), dtype=torch.uint8, device=d),
+               torch.empty((M, K // 32), dtype=torch.uint8, device=d))
+              for _ in range(PREFILL_SLOTS)]
         y = torch.empty((M, N), dtype=torch.bfloat16, device=d)
         data.append((N, K, wc, wsc, x, xq, y))
 
-    ph = Phases(torch, 1)
+    ph = Phases(torch, PREFILL_SLOTS)
 
     def step(r):
         for N, K, wc, wsc, x, xq, y in data:
-            mx.mxfp4_quantize_act(x, *xq)
-            mx.mxfp4_gemm(xq[0], xq[1], wc, wsc, y)
+            mx.mxfp4_quantize_act(x[r], *xq[r])
+            mx.mxfp4_gemm(xq[r][0], xq[r][1], wc, wsc, y)
 
     ph.add("step", step)
     for N, K, wc, wsc, x, xq, y in data:
-        ph.add(f"aq_{N}x{K}", lambda r, x=x, xq=xq: mx.mxfp4_quantize_act(x, *xq))
+        ph.add(f"aq_{N}x{K}", lambda r, x=x, xq=xq: mx.mxfp4_quantize_act(x[r], *xq[r]))
         ph.add(f"gemm_{N}x{K}", lambda r, xq=xq, wc=wc, wsc=wsc, y=y:
-               mx.mxfp4_gemm(xq[0], xq[1], wc, wsc, y))
+               mx.mxfp4_gemm(xq[r][0], xq[r][1], wc, wsc, y))
 
     def report(t, steps):
         flops = sum(2 * M * N * K for N, K in shapes)
@@ -328,26 +337,32 @@ def moe_workload(torch, mx, synth):
             mx.mxfp4_requant_from_nvfp4(c, s, g.reshape(1), wc[e], ws[e])
         W[name] = (N, K, wc, ws)
     Mtot = T * TOPK
-    aq1 = (torch.empty((Mtot, 2048), dtype=torch.uint8, device=d),
-           torch.empty((Mtot, 128), dtype=torch.uint8, device=d))
-    aq2 = (torch.empty((Mtot, 512), dtype=torch.uint8, device=d),
-           torch.empty((Mtot, 32), dtype=torch.uint8, device=d))
-    y1 = torch.empty((Mtot, 2048), dtype=torch.bfloat16, device=d)
-    y2 = torch.empty((Mtot, 4096), dtype=torch.bfloat16, device=d)
+    # rotated copies of the activation-side buffers (the expert weights,
+    # 855 MB, exceed the Infinity Cache on their own)
+    R = MOE_SLOTS
+    tokens = [tokens.clone() for _ in range(R)]
+    down_in = [down_in.clone() for _ in range(R)]
+    aq1 = [(torch.empty((Mtot, 2048), dtype=torch.uint8, device=d),
+            torch.empty((Mtot, 128), dtype=torch.uint8, device=d)) for _ in range(R)]
+    aq2 = [(torch.empty((Mtot, 512), dtype=torch.uint8, device=d),
+            torch.empty((Mtot, 32), dtype=torch.uint8, device=d)) for _ in range(R)]
+    y1 = [torch.empty((Mtot, 2048), dtype=torch.bfloat16, device=d) for _ in range(R)]
+    y2 = [torch.empty((Mtot, 4096), dtype=torch.bfloat16, device=d) for _ in range(R)]
 
     def aq_gate_up(r):
-        mx.mxfp4_quantize_act(tokens, *aq1, row_index=perm)
+        mx.mxfp4_quantize_act(tokens[r], *aq1[r], row_index=perm)
 
     def gemm_gate_up(r):
-        mx.mxfp4_grouped_gemm(aq1[0], aq1[1], W["gate_up"][2], W["gate_up"][3], offsets, y1)
+        mx.mxfp4_grouped_gemm(aq1[r][0], aq1[r][1], W["gate_up"][2], W["gate_up"][3], offsets,
+                              y1[r])
 
     def aq_down(r):
-        mx.mxfp4_quantize_act(down_in, *aq2)
+        mx.mxfp4_quantize_act(down_in[r], *aq2[r])
 
     def gemm_down(r):
-        mx.mxfp4_grouped_gemm(aq2[0], aq2[1], W["down"][2], W["down"][3], offsets, y2)
+        mx.mxfp4_grouped_gemm(aq2[r][0], aq2[r][1], W["down"][2], W["down"][3], offsets, y2[r])
 
-    ph = Phases(torch, 1)
+    ph = Phases(torch, R)
     ph.add("step", lambda r: (aq_gate_up(r), gemm_gate_up(r), aq_down(r), gemm_down(r)))
     for f in (aq_gate_up, gemm_gate_up, aq_down, gemm_down):
         ph.add(f.__name__, f)
