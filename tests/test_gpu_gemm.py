@@ -262,6 +262,19 @@ def test_grouped_gemm_tiled_many_small_experts(mx):
     assert_gemm_fp32(gy, y, s, "grouped tiled small experts")
 
 
+def test_grouped_gemm_tiled_more_than_256_experts(mx):
+    """Three hundred experts, mostly with a handful of rows: the expert table
+    and the tile walk cross many short experts, under both K-prefetch settings
+    (K = 1024 streams the next tile's first stages, K = 512 does not)."""
+    rng = np.random.default_rng(9)
+    counts = rng.integers(0, 5, size=300)
+    counts[[3, 150, 299]] = [130, 257, 40]
+    for K in (1024, 512):
+        say(f"grouped tiled 300 experts total {counts.sum()} N=256 K={K}")
+        gy, y, s = grouped_case(mx, counts, 256, K, 71, torch.float32)
+        assert_gemm_fp32(gy, y, s, f"grouped tiled 300 experts K={K}")
+
+
 def test_grouped_gemm_tiled_bad_offsets_stay_inside_y(mx):
     say("grouped tiled gemm malformed offsets")
     E, N, K, M = 4, 256, 512, 300
