@@ -60,6 +60,7 @@ namespace tiled {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
 
 constexpr int BKB = 128;                     // code bytes per row per stage (256 K)
 constexpr int SCALE_OPERAND = 256 * 16;      // 4 KiB: 256 rows x 16 B
@@ -367,45 +368,97 @@ __device__ __forceinline__ void mfma_half(const Half<S>& f, const Scales<S>& sc,
     }
 }
 
+// Epilogue.  The MFMA result layout gives each lane one output row and runs
+// of 4 columns, so storing straight from the accumulators writes 8-16 bytes
+// into each of 32 rows per instruction, and the write path then runs at a
+// fraction of HBM speed.  Instead each wave parks ROWS rows of its tile in a
+// private LDS region (a row pitch padded by 16 bytes so the rows start on
+// different banks) and writes them back as row segments: 16 bytes a lane,
+// consecutive lanes along a row, so one instruction covers whole lines.
 template <class S, bool OUT_BF16>
-__device__ __forceinline__ void store_tile(const v16f (&acc)[S::NB][S::MB], void* __restrict__ y,
-                                           int64_t m0, int64_t m_end, int64_t n0, int64_t N,
-                                           int wn, int wm) {
+struct Stage {
+    static constexpr int ESIZE = OUT_BF16 ? 2 : 4;
+    static constexpr int ROW_BYTES = 32 * S::NB * ESIZE;  // one wave's columns
+    static constexpr int PITCH = ROW_BYTES + 16;
+    static constexpr int CHUNKS = ROW_BYTES / 16;         // 16-byte pieces a row
+    static constexpr int EPC = 16 / ESIZE;                // elements a piece
+    // rows per pass that fit a per-wave region of `bytes`
+    static constexpr int rows_for(int bytes) {
+        return 32 * PITCH <= bytes ? 32 : 16 * PITCH <= bytes ? 16 : 8;
+    }
+    static constexpr int bytes(int rows) { return rows * PITCH; }
+};
+
+// Store this wave's accumulators (rows [m0 + wm*32*MB, +32*MB) clipped to
+// m_end, columns [n0 + wn*32*NB, +32*NB) clipped to N) through `stage`, this
+// wave's own Stage::bytes(ROWS) bytes of LDS.  No other wave touches the
+// region, so the only ordering needed is this wave's own.
+template <class S, bool OUT_BF16, int ROWS>
+__device__ __forceinline__ void store_tile(const v16f (&acc)[S::NB][S::MB], lds_u8* stage,
+                                           void* __restrict__ y, int64_t m0, int64_t m_end,
+                                           int64_t n0, int64_t N, int wn, int wm) {
+    using T = Stage<S, OUT_BF16>;
+    static_assert(ROWS == 32 || ROWS == 16 || ROWS == 8, "a 32-row block in 1, 2 or 4 passes");
+    static_assert((ROWS * T::CHUNKS) % 64 == 0, "whole instructions per pass");
     const int lane = threadIdx.x & 63;
     const int r32 = lane & 31, h = lane >> 5;
-    const bool vec_ok = (N % 4) == 0 && (reinterpret_cast<uintptr_t>(y) % 16) == 0;
+    const bool vec_ok = (N % T::EPC) == 0 && (reinterpret_cast<uintptr_t>(y) % 16) == 0;
+    const int64_t col0 = n0 + wn * 32 * S::NB;
 #pragma unroll
     for (int j = 0; j < S::MB; ++j) {
-        const int64_t m = m0 + wm * 32 * S::MB + 32 * j + r32;
-        if (m >= m_end) continue;
 #pragma unroll
-        for (int i = 0; i < S::NB; ++i) {
+        for (int p = 0; p < 32 / ROWS; ++p) {
+            const int64_t row0 = m0 + wm * 32 * S::MB + 32 * j + p * ROWS;
+            if (row0 >= m_end) return;            // wave-uniform
+            // park: lane (r32, h) holds row r32, columns 32i + 8b + 4h + 0..3
+            const int r = r32 - p * ROWS;
+            if (ROWS == 32 || (r >= 0 && r < ROWS)) {
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const int64_t n = n0 + wn * 32 * S::NB + 32 * i + 8 * b + 4 * h;
-                if (n >= N) continue;
-                const float v0 = acc[i][j][4 * b], v1 = acc[i][j][4 * b + 1];
-                const float v2 = acc[i][j][4 * b + 2], v3 = acc[i][j][4 * b + 3];
-                if (vec_ok && n + 3 < N) {
-                    if (OUT_BF16)
-                        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(y) + m * N + n) =
-                            make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
-                    else
-                        *reinterpret_cast<float4*>(reinterpret_cast<float*>(y) + m * N + n) =
-                            make_float4(v0, v1, v2, v3);
-                } else {
-                    const float v[4] = {v0, v1, v2, v3};
+                for (int i = 0; i < S::NB; ++i) {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        if (n + r >= N) break;
+                    for (int b = 0; b < 4; ++b) {
+                        lds_u8* dst = stage + r * T::PITCH + (32 * i + 8 * b + 4 * h) * T::ESIZE;
+                        const float v0 = acc[i][j][4 * b], v1 = acc[i][j][4 * b + 1];
+                        const float v2 = acc[i][j][4 * b + 2], v3 = acc[i][j][4 * b + 3];
                         if (OUT_BF16)
-                            reinterpret_cast<uint16_t*>(y)[m * N + n + r] =
-                                (uint16_t)f32_to_bf16_rne(v[r]);
+                            *reinterpret_cast<__attribute__((address_space(3))) v2u*>(dst) =
+                                v2u{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
                         else
-                            reinterpret_cast<float*>(y)[m * N + n + r] = v[r];
+                            *reinterpret_cast<__attribute__((address_space(3))) v4u*>(dst) =
+                                v4u{__float_as_uint(v0), __float_as_uint(v1), __float_as_uint(v2),
+                                    __float_as_uint(v3)};
                     }
                 }
             }
+            // this wave's LDS operations complete in order; the fence keeps
+            // the compiler from moving the reads above the writes
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+            for (int q = 0; q < ROWS * T::CHUNKS / 64; ++q) {
+                const int c = q * 64 + lane;
+                const int rr = c / T::CHUNKS, cc = c % T::CHUNKS;
+                const v4u v = *reinterpret_cast<const __attribute__((address_space(3))) v4u*>(
+                    stage + rr * T::PITCH + cc * 16);
+                const int64_t m = row0 + rr;
+                const int64_t n = col0 + (int64_t)cc * T::EPC;
+                if (m >= m_end || n >= N) continue;
+                if (vec_ok && n + T::EPC <= N) {
+                    *reinterpret_cast<v4u*>(reinterpret_cast<uint8_t*>(y) +
+                                            (m * N + n) * T::ESIZE) = v;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < T::EPC; ++e) {
+                        if (n + e >= N) break;
+                        if (OUT_BF16)
+                            reinterpret_cast<uint16_t*>(y)[m * N + n + e] =
+                                (uint16_t)(v[e / 2] >> (16 * (e % 2)));
+                        else
+                            reinterpret_cast<uint32_t*>(y)[m * N + n + e] = v[e];
+                    }
+                }
+            }
+            // the next pass overwrites the region only after these reads
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         }
     }
 }
@@ -583,7 +636,12 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(
     prologue<S>(lds, src, nkt, 0, pp, ro);
     main_loop<S, S::MB, false>(lds, src, src, nkt, 0, pp, acc, ro);
     wait_vm<0>();                             // drain the surplus loads
-    store_tile<S, OUT_BF16>(acc, y, m0, M, n0, N, wn, wm);
+    // every wave is past its last read of the stage buffers, which now hold
+    // the four waves' epilogue regions
+    __syncthreads();
+    using T = Stage<S, OUT_BF16>;
+    constexpr int ROWS = T::rows_for(S::SCALE_BASE / 4);   // both code stages
+    store_tile<S, OUT_BF16, ROWS>(acc, lds + wave * T::bytes(ROWS), y, m0, M, n0, N, wn, wm);
 }
 
 // ---------------------------------------------------------------------------
@@ -601,6 +659,7 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(
 // ---------------------------------------------------------------------------
 constexpr int GROUP_MAX_E = 2048;
 constexpr int GROUP_TABLE_BYTES = (3 * GROUP_MAX_E + 1) * 4;
+constexpr int GROUP_LDS_LIMIT = 160 * 1024;     // LDS a workgroup may hold
 
 __device__ __forceinline__ int wave_inclusive_scan(int v) {
     const int lane = threadIdx.x & 63;
@@ -711,7 +770,14 @@ __global__ __launch_bounds__(256, 1) void grouped_tiled_kernel(
     const int32_t* __restrict__ offsets, int E, int total_M, int64_t N, int64_t K,
     void* __restrict__ y) {
     using S = GroupShape;
-    __shared__ __attribute__((aligned(16))) uint8_t smem[S::LDS_BYTES + GROUP_TABLE_BYTES];
+    // pipeline, expert table, then the four waves' epilogue regions (the
+    // pipeline buffers already hold the next tile's first stages when a tile
+    // is stored)
+    using T = Stage<S, OUT_BF16>;
+    constexpr int STAGE_BASE = (S::LDS_BYTES + GROUP_TABLE_BYTES + 15) / 16 * 16;
+    constexpr int ROWS = T::rows_for((GROUP_LDS_LIMIT - STAGE_BASE) / 4);
+    static_assert(STAGE_BASE + 4 * T::bytes(ROWS) <= GROUP_LDS_LIMIT, "LDS budget");
+    __shared__ __attribute__((aligned(16))) uint8_t smem[STAGE_BASE + 4 * T::bytes(ROWS)];
     lds_u8* lds = (lds_u8*)smem;
     int* table = reinterpret_cast<int*>(smem + S::LDS_BYTES);
     const GroupTable tb{table, table + GROUP_MAX_E + 1, table + 2 * GROUP_MAX_E + 1};
@@ -749,7 +815,8 @@ __global__ __launch_bounds__(256, 1) void grouped_tiled_kernel(
         else
             main_loop_jl<S, false>(it.jl, lds, cur, cur, nkt, cbase, pp, acc, ro);
         if (!prefetch) wait_vm<0>();          // drain the surplus loads
-        store_tile<S, OUT_BF16>(acc, y, it.m0, it.m_end, (int64_t)it.tn * S::BN, N, wn, wm);
+        store_tile<S, OUT_BF16, ROWS>(acc, lds + STAGE_BASE + wave * T::bytes(ROWS), y, it.m0,
+                                      it.m_end, (int64_t)it.tn * S::BN, N, wn, wm);
         if (!have_next) break;
         zero_acc<S>(acc);
         if (prefetch) {
