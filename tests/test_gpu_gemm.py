@@ -35,7 +35,10 @@ SHAPES = [(1, 1, 32), (1, 300, 4096), (7, 17, 96), (16, 256, 512), (33, 200, 544
           # weight-streaming kernel: every activation-block count, K = 2048 and 4096,
           # ragged N, four and eight wavefronts
           (5, 1000, 2048), (16, 16, 4096), (17, 300, 4096), (40, 72, 2048), (48, 257, 4096),
-          (64, 4099, 4096), (61, 1040, 2048)]
+          (64, 4099, 4096), (61, 1040, 2048),
+          # more tiles than one round on the chip (persistent walk, ragged M and
+          # N), with and without the next tile's stages streamed early
+          (2200, 7700, 1024), (2200, 7700, 512)]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)

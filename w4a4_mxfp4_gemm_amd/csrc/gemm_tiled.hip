@@ -129,17 +129,19 @@ __device__ __forceinline__ int wave_id() {
     return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 }
 
-// Per-lane byte offsets of this thread's loads (constant over K; the K
-// position enters as the scalar offset).  Rows past an operand's end are
-// clamped to its last row: those results are never stored.
+// Per-lane byte offsets of this thread's loads from a tile's first row: the
+// same for every tile (the tile's first row is the buffer descriptors' base)
+// and over K (the K position enters as the scalar offset).  A row past an
+// operand's end has an offset past its descriptor's range, so its loads
+// return zeros without touching memory; those rows' results are never
+// stored.
 template <class S>
 struct LoadOffsets {
     uint32_t w[S::WLOADS], x[S::XLOADS], ws, xs;
 };
 
 template <class S>
-__device__ __forceinline__ LoadOffsets<S> load_offsets(int64_t n0, int64_t N, int64_t m0,
-                                                       int64_t M, int64_t ldc, int64_t lds_) {
+__device__ __forceinline__ LoadOffsets<S> load_offsets(int64_t ldc, int64_t lds_) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     LoadOffsets<S> o;
@@ -147,17 +149,17 @@ __device__ __forceinline__ LoadOffsets<S> load_offsets(int64_t n0, int64_t N, in
     for (int i = 0; i < S::WLOADS; ++i) {
         const int row = (wave * S::WLOADS + i) * 8 + (lane >> 3);
         const int c = (lane & 7) ^ ((row >> 1) & 7);
-        o.w[i] = (uint32_t)(min(n0 + row, N - 1) * ldc + 16 * c);
+        o.w[i] = (uint32_t)(row * ldc + 16 * c);
     }
 #pragma unroll
     for (int i = 0; i < S::XLOADS; ++i) {
         const int row = (wave * S::XLOADS + i) * 8 + (lane >> 3);
         const int c = (lane & 7) ^ ((row >> 1) & 7);
-        o.x[i] = (uint32_t)(min(m0 + row, M - 1) * ldc + 16 * c);
+        o.x[i] = (uint32_t)(row * ldc + 16 * c);
     }
     const int row = wave * 64 + lane;
-    o.ws = (uint32_t)(min(n0 + row, N - 1) * lds_);
-    o.xs = (uint32_t)(min(m0 + row, M - 1) * lds_);
+    o.ws = (uint32_t)(row * lds_);
+    o.xs = (uint32_t)(row * lds_);
     return o;
 }
 
@@ -189,11 +191,11 @@ __device__ __forceinline__ void load_scales(lds_u8* lds, const Operands& op,
     dma16(weights ? op.ws : op.xs, dst, weights ? o.ws : o.xs, (uint32_t)c * 16);
 }
 
-// Everything a thread needs to fetch one output tile's operands.
+// Where one output tile's operands come from: the four buffer descriptors,
+// each starting at the tile's first row and ending at its operand's end.
 template <class S>
 struct TileSrc {
     Operands op;
-    LoadOffsets<S> o;
 };
 
 template <class S>
@@ -201,10 +203,12 @@ __device__ __forceinline__ TileSrc<S> tile_src(const uint8_t* x, const uint8_t* 
                                                const uint8_t* w, const uint8_t* ws, int64_t m0,
                                                int64_t m_end, int64_t n0, int64_t N, int64_t K) {
     const int64_t ldc = K / 2, lds_ = K / 32;
+    const int64_t rows_w = N > n0 ? N - n0 : 0, rows_x = m_end > m0 ? m_end - m0 : 0;
     TileSrc<S> t;
-    t.op = Operands{make_rsrc(w, (uint32_t)(N * ldc)), make_rsrc(ws, (uint32_t)(N * lds_)),
-                    make_rsrc(x, (uint32_t)(m_end * ldc)), make_rsrc(xs, (uint32_t)(m_end * lds_))};
-    t.o = load_offsets<S>(n0, N, m0, m_end, ldc, lds_);
+    t.op = Operands{make_rsrc(w + n0 * ldc, (uint32_t)(rows_w * ldc)),
+                    make_rsrc(ws + n0 * lds_, (uint32_t)(rows_w * lds_)),
+                    make_rsrc(x + m0 * ldc, (uint32_t)(rows_x * ldc)),
+                    make_rsrc(xs + m0 * lds_, (uint32_t)(rows_x * lds_))};
     return t;
 }
 
@@ -219,12 +223,6 @@ __device__ __forceinline__ TileSrc<S> pick(bool p, const TileSrc<S>& a, const Ti
         t.op.x[k] = p ? a.op.x[k] : b.op.x[k];
         t.op.xs[k] = p ? a.op.xs[k] : b.op.xs[k];
     }
-#pragma unroll
-    for (int i = 0; i < S::WLOADS; ++i) t.o.w[i] = p ? a.o.w[i] : b.o.w[i];
-#pragma unroll
-    for (int i = 0; i < S::XLOADS; ++i) t.o.x[i] = p ? a.o.x[i] : b.o.x[i];
-    t.o.ws = p ? a.o.ws : b.o.ws;
-    t.o.xs = p ? a.o.xs : b.o.xs;
     return t;
 }
 
@@ -304,17 +302,18 @@ __device__ __forceinline__ void settle(Half<S>&, Scales<S>&) {}
 // (from `ss`: chunk `chunk` of that tile into ring slot `slot`).
 template <class S, int Q>
 __device__ __forceinline__ void load_op(lds_u8* lds, const TileSrc<S>& cs, const TileSrc<S>& ss,
-                                        int buf, int kt, bool scale_w, int chunk, int slot) {
+                                        const LoadOffsets<S>& lo, int buf, int kt, bool scale_w,
+                                        int chunk, int slot) {
     const int wave = wave_id();
     if constexpr (Q < S::WLOADS) {
-        dma16(cs.op.w, lds + buf * S::CODE_STAGE + (wave * S::WLOADS + Q) * 1024, cs.o.w[Q],
+        dma16(cs.op.w, lds + buf * S::CODE_STAGE + (wave * S::WLOADS + Q) * 1024, lo.w[Q],
               (uint32_t)kt * BKB);
     } else if constexpr (Q < S::WLOADS + S::XLOADS) {
         constexpr int i = Q - S::WLOADS;
         dma16(cs.op.x, lds + buf * S::CODE_STAGE + S::W_OPERAND + (wave * S::XLOADS + i) * 1024,
-              cs.o.x[i], (uint32_t)kt * BKB);
+              lo.x[i], (uint32_t)kt * BKB);
     } else {
-        load_scales<S>(lds, ss.op, ss.o, scale_w, chunk, slot);
+        load_scales<S>(lds, ss.op, lo, scale_w, chunk, slot);
     }
 }
 
@@ -372,9 +371,11 @@ __device__ __forceinline__ void mfma_half(const Half<S>& f, const Scales<S>& sc,
 // of 4 columns, so storing straight from the accumulators writes 8-16 bytes
 // into each of 32 rows per instruction, and the write path then runs at a
 // fraction of HBM speed.  Instead each wave parks ROWS rows of its tile in a
-// private LDS region (a row pitch padded by 16 bytes so the rows start on
-// different banks) and writes them back as row segments: 16 bytes a lane,
-// consecutive lanes along a row, so one instruction covers whole lines.
+// private LDS region and writes them back as row segments: 16 bytes a lane,
+// consecutive lanes along a row, so one instruction covers whole lines.  The
+// region's row pitch is padded by 16 bytes, which puts the rows that one
+// parking instruction writes on different banks and keeps every parking
+// address a lane base plus an immediate.
 template <class S, bool OUT_BF16>
 struct Stage {
     static constexpr int ESIZE = OUT_BF16 ? 2 : 4;
@@ -382,9 +383,12 @@ struct Stage {
     static constexpr int PITCH = ROW_BYTES + 16;
     static constexpr int CHUNKS = ROW_BYTES / 16;         // 16-byte pieces a row
     static constexpr int EPC = 16 / ESIZE;                // elements a piece
-    // rows per pass that fit a per-wave region of `bytes`
-    static constexpr int rows_for(int bytes) {
-        return 32 * PITCH <= bytes ? 32 : 16 * PITCH <= bytes ? 16 : 8;
+    // most rows per pass (32 .. 2, a whole number of 64-lane write-backs)
+    // that fit a per-wave region of `budget` bytes
+    static constexpr int rows_for(int budget) {
+        int rows = 32;
+        while (rows > 2 && (rows * PITCH > budget || (rows * CHUNKS) % 64 != 0)) rows /= 2;
+        return rows;
     }
     static constexpr int bytes(int rows) { return rows * PITCH; }
 };
@@ -392,15 +396,21 @@ struct Stage {
 // Store this wave's accumulators (rows [m0 + wm*32*MB, +32*MB) clipped to
 // m_end, columns [n0 + wn*32*NB, +32*NB) clipped to N) through `stage`, this
 // wave's own Stage::bytes(ROWS) bytes of LDS.  No other wave touches the
-// region, so the only ordering needed is this wave's own.
+// region, and one wave's LDS instructions take effect in issue order, so the
+// passes need only compiler fences: a read after the parking writes sees
+// them, and the next pass's writes cannot overtake this pass's reads.
 template <class S, bool OUT_BF16, int ROWS>
 __device__ __forceinline__ void store_tile(const v16f (&acc)[S::NB][S::MB], lds_u8* stage,
                                            void* __restrict__ y, int64_t m0, int64_t m_end,
                                            int64_t n0, int64_t N, int wn, int wm) {
     using T = Stage<S, OUT_BF16>;
-    static_assert(ROWS == 32 || ROWS == 16 || ROWS == 8, "a 32-row block in 1, 2 or 4 passes");
+    static_assert(ROWS >= 2 && ROWS <= 32 && (ROWS & (ROWS - 1)) == 0, "a 32-row block in passes");
     static_assert((ROWS * T::CHUNKS) % 64 == 0, "whole instructions per pass");
-    const int lane = threadIdx.x & 63;
+    // an opaque lane index keeps the per-lane addresses below inside the
+    // epilogue: hoisted out of a persistent walk's tile loop they are held
+    // across the main loop, which spills them
+    int lane = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane));
     const int r32 = lane & 31, h = lane >> 5;
     const bool vec_ok = (N % T::EPC) == 0 && (reinterpret_cast<uintptr_t>(y) % 16) == 0;
     const int64_t col0 = n0 + wn * 32 * S::NB;
@@ -430,9 +440,7 @@ __device__ __forceinline__ void store_tile(const v16f (&acc)[S::NB][S::MB], lds_
                     }
                 }
             }
-            // this wave's LDS operations complete in order; the fence keeps
-            // the compiler from moving the reads above the writes
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            asm volatile("" ::: "memory");         // reads after the writes
 #pragma unroll
             for (int q = 0; q < ROWS * T::CHUNKS / 64; ++q) {
                 const int c = q * 64 + lane;
@@ -457,8 +465,7 @@ __device__ __forceinline__ void store_tile(const v16f (&acc)[S::NB][S::MB], lds_
                     }
                 }
             }
-            // the next pass overwrites the region only after these reads
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            asm volatile("" ::: "memory");         // next writes after the reads
         }
     }
 }
@@ -499,16 +506,17 @@ __device__ __forceinline__ uint32_t scale_addr(uint32_t lds0, int cbase, int s) 
 //
 // Prologue: chunk 0, stage 0, stage 1; wait for stage 0; read its first half.
 template <class S>
-__device__ __forceinline__ void prologue(lds_u8* lds, const TileSrc<S>& src, int nkt, int cbase,
-                                         Pipe<S>& pp, const ReadOffsets& ro) {
+__device__ __forceinline__ void prologue(lds_u8* lds, const TileSrc<S>& src,
+                                         const LoadOffsets<S>& lo, int nkt, int cbase, Pipe<S>& pp,
+                                         const ReadOffsets& ro) {
     const int last_chunk = nkt / 2 - 1;
     const int c1 = last_chunk >= 1 ? 1 : 0;
-    load_codes<S>(lds, src.op, src.o, 0, 0);
-    load_scales<S>(lds, src.op, src.o, true, 0, cbase % 3);
-    load_scales<S>(lds, src.op, src.o, false, 0, cbase % 3);
-    load_scales<S>(lds, src.op, src.o, true, c1, (cbase + c1) % 3);
-    load_scales<S>(lds, src.op, src.o, false, c1, (cbase + c1) % 3);
-    load_codes<S>(lds, src.op, src.o, 1, nkt > 1 ? 1 : 0);
+    load_codes<S>(lds, src.op, lo, 0, 0);
+    load_scales<S>(lds, src.op, lo, true, 0, cbase % 3);
+    load_scales<S>(lds, src.op, lo, false, 0, cbase % 3);
+    load_scales<S>(lds, src.op, lo, true, c1, (cbase + c1) % 3);
+    load_scales<S>(lds, src.op, lo, false, c1, (cbase + c1) % 3);
+    load_codes<S>(lds, src.op, lo, 1, nkt > 1 ? 1 : 0);
     wait_vm<S::WLOADS + S::XLOADS>();
     __builtin_amdgcn_s_barrier();
     const uint32_t lds0 = lds_addr(lds);
@@ -523,13 +531,18 @@ __device__ __forceinline__ void prologue(lds_u8* lds, const TileSrc<S>& src, int
 // loads of stages nkt and nkt+1 are the next tile's stages 0 and 1 (and its
 // scale chunks 0 and 1), and the loop ends with the next tile's stage 0
 // first half in pp.h0 / pp.sc_cur: the next tile needs no prologue.
-// PREFETCH needs nkt >= 4.  Per stage kt (one barrier per stage):
+// PREFETCH needs nkt >= 4.  With DEFER as well, the next tile's stage 1 code
+// loads are left out, so the stage-1 buffer is free once the loop ends (the
+// last stage's barrier is past every wave's reads of it); the caller issues
+// them (load_codes into buffer 1) after using the buffer.
+// Per stage kt (one barrier per stage):
 //   read half 1 of stage kt;  MFMAs on half 0;  wait for the reads
 //   wait for stage kt+1's loads; barrier; load stage kt+2 (+ one scale half-chunk)
 //   read half 0 of stage kt+1;  MFMAs on half 1;  wait for the reads
-template <class S, int JL, bool PREFETCH>
+template <class S, int JL, bool PREFETCH, bool DEFER = false>
 __device__ __forceinline__ void main_loop(lds_u8* lds, const TileSrc<S>& cur,
-                                          const TileSrc<S>& nxt, int nkt, int cbase, Pipe<S>& pp,
+                                          const TileSrc<S>& nxt, const LoadOffsets<S>& lo,
+                                          int nkt, int cbase, Pipe<S>& pp,
                                           v16f (&acc)[S::NB][S::MB], const ReadOffsets& ro) {
     const int last_chunk = nkt / 2 - 1;
     const uint32_t lds0 = lds_addr(lds);
@@ -571,10 +584,15 @@ __device__ __forceinline__ void main_loop(lds_u8* lds, const TileSrc<S>& cur,
             const uint32_t scales = scale_addr<S>(lds0, cbase, kt + 1);
             const TileSrc<S> cs = PREFETCH ? pick(code_next, nxt, cur) : cur;
             const TileSrc<S> ss = PREFETCH ? pick(scale_next, nxt, cur) : cur;
+            const bool codes_deferred = PREFETCH && DEFER && kt == nkt - 1;
             mfma_half<S, JL, 1>(pp.h1, pp.sc_cur, acc, [&](auto q) {
                 constexpr int Q = decltype(q)::value;
-                if constexpr (Q < S::LOADS_PER_STAGE)
-                    load_op<S, Q>(lds, cs, ss, s2 & 1, ks, scale_w, chunk, slot);
+                if constexpr (Q < S::WLOADS + S::XLOADS) {
+                    if (!codes_deferred)
+                        load_op<S, Q>(lds, cs, ss, lo, s2 & 1, ks, scale_w, chunk, slot);
+                } else if constexpr (Q < S::LOADS_PER_STAGE) {
+                    load_op<S, Q>(lds, cs, ss, lo, s2 & 1, ks, scale_w, chunk, slot);
+                }
                 read_range<S, 0, second_half_read<S>(Q), second_half_read<S>(Q + 1)>(
                     pp.h0, pp.sc_nxt, codes, scales, ro);
             });
@@ -592,16 +610,10 @@ __device__ __forceinline__ void zero_acc(v16f (&acc)[S::NB][S::MB]) {
         for (int j = 0; j < S::MB; ++j) acc[i][j] = v16f{};
 }
 
-// XCD-aware tile order: workgroup ids are dealt to the 8 XCDs round-robin, so
-// id -> (xcd, local) is remapped to a linear tile index that gives each XCD a
-// contiguous run, walked in groups of `gm` tile-rows so the run covers a
-// compact block of the output (shared operand rows stay in that XCD's L2).
-__device__ __forceinline__ bool tile_coords(int tiles_m, int tiles_n, int gm, int& tm, int& tn) {
-    const int total = tiles_m * tiles_n;
-    const int per_xcd = (int)gridDim.x / 8;
-    const int id = (int)blockIdx.x;
-    const int t = (id % 8) * per_xcd + id / 8;
-    if (t >= total) return false;
+// Linear tile index -> (tile row, tile column), walked in groups of `gm`
+// tile-rows so that a run of consecutive indices covers a compact block of
+// the output (the operand rows it shares stay in one XCD's L2).
+__device__ __forceinline__ void tile_of(int t, int tiles_m, int tiles_n, int gm, int& tm, int& tn) {
     const int group_size = gm * tiles_n;
     const int group = t / group_size;
     const int first_m = group * gm;
@@ -609,6 +621,32 @@ __device__ __forceinline__ bool tile_coords(int tiles_m, int tiles_n, int gm, in
     const int in_group = t - group * group_size;
     tm = first_m + in_group % rows;
     tn = in_group / rows;
+}
+
+// Zero the accumulators for the next tile of a persistent walk, after the
+// epilogue.  With a plain zero_acc the compiler zeroes the next tile's AGPRs
+// before the epilogue and first moves all results into VGPRs, which spills;
+// zeros that come out of a volatile asm cannot move above the epilogue's
+// LDS writes.
+template <class S>
+__device__ __forceinline__ void rezero_acc(v16f (&acc)[S::NB][S::MB]) {
+    v16f z = v16f{};
+    asm volatile("" : "+v"(z));
+#pragma unroll
+    for (int i = 0; i < S::NB; ++i)
+#pragma unroll
+        for (int j = 0; j < S::MB; ++j) acc[i][j] = z;
+}
+
+// XCD-aware tile order: workgroup ids are dealt to the 8 XCDs round-robin, so
+// id -> (xcd, local) is remapped to a linear tile index that gives each XCD a
+// contiguous run.
+__device__ __forceinline__ bool tile_coords(int tiles_m, int tiles_n, int gm, int& tm, int& tn) {
+    const int per_xcd = (int)gridDim.x / 8;
+    const int id = (int)blockIdx.x;
+    const int t = (id % 8) * per_xcd + id / 8;
+    if (t >= tiles_m * tiles_n) return false;
+    tile_of(t, tiles_m, tiles_n, gm, tm, tn);
     return true;
 }
 
@@ -630,11 +668,12 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(
     lds_u8* lds = (lds_u8*)smem;
     const TileSrc<S> src = tile_src<S>(x, xs, w, ws, m0, M, n0, N, K);
     const ReadOffsets ro = read_offsets<S>(wn, wm);
+    const LoadOffsets<S> lo = load_offsets<S>(K / 2, K / 32);
     v16f acc[S::NB][S::MB];
     zero_acc<S>(acc);
     Pipe<S> pp;
-    prologue<S>(lds, src, nkt, 0, pp, ro);
-    main_loop<S, S::MB, false>(lds, src, src, nkt, 0, pp, acc, ro);
+    prologue<S>(lds, src, lo, nkt, 0, pp, ro);
+    main_loop<S, S::MB, false>(lds, src, src, lo, nkt, 0, pp, acc, ro);
     wait_vm<0>();                             // drain the surplus loads
     // every wave is past its last read of the stage buffers, which now hold
     // the four waves' epilogue regions
@@ -642,6 +681,80 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(
     using T = Stage<S, OUT_BF16>;
     constexpr int ROWS = T::rows_for(S::SCALE_BASE / 4);   // both code stages
     store_tile<S, OUT_BF16, ROWS>(acc, lds + wave * T::bytes(ROWS), y, m0, M, n0, N, wn, wm);
+}
+
+// ---------------------------------------------------------------------------
+// Dense GEMM, persistent, for more than one round of tiles and K >= 1024: one
+// workgroup per CU walks the tiles
+//   t = xcd * ceil(total / 8) + local + k * (grid / 8)   (xcd = id % 8, local = id / 8)
+// (the XCD-contiguous runs above, now visited by the XCD's workgroups side by
+// side).  While a tile's last two stages run, the next tile's first stage
+// and its first two scale chunks load into the freed buffers, so only a
+// workgroup's first tile pays the prologue.  The epilogue parks each wave's
+// rows in the part of the stage-1 buffer that the wave's own loads of the
+// next tile's stage 1 fill, and issues those loads right after: Y's stores
+// then drain while the next tile runs.
+// ---------------------------------------------------------------------------
+constexpr int LDS_LIMIT = 160 * 1024;           // LDS a workgroup may hold
+
+template <bool OUT_BF16>
+__global__ __launch_bounds__(256, 1) void gemm_persistent_kernel(
+    const uint8_t* __restrict__ x, const uint8_t* __restrict__ xs,
+    const uint8_t* __restrict__ w, const uint8_t* __restrict__ ws, int64_t M, int64_t N,
+    int64_t K, void* __restrict__ y, int gm) {
+    using S = DenseShape;
+    using T = Stage<S, OUT_BF16>;
+    constexpr int ROWS = T::rows_for(S::WLOADS * 1024);   // a wave's weight rows of a stage
+    __shared__ __attribute__((aligned(16))) uint8_t smem[S::LDS_BYTES];
+    const int tiles_m = (int)((M + S::BM - 1) / S::BM);
+    const int tiles_n = (int)((N + S::BN - 1) / S::BN);
+    const int total = tiles_m * tiles_n;
+    const int per_xcd = (total + 7) / 8;
+    const int stride = (int)gridDim.x / 8;
+    const int xcd = (int)blockIdx.x % 8;
+    const int t_end = min(xcd * per_xcd + per_xcd, total);
+    int t = xcd * per_xcd + (int)blockIdx.x / 8;
+    if (t >= t_end) return;
+
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wn = wave % S::WGN, wm = wave / S::WGN;
+    const int nkt = (int)(K / 256);           // even, >= 4: K % 512 == 0, K >= 1024
+    lds_u8* lds = (lds_u8*)smem;
+    // where load_codes puts this wave's weight rows of stage 1
+    lds_u8* stage = lds + S::CODE_STAGE + wave * S::WLOADS * 1024;
+    const ReadOffsets ro = read_offsets<S>(wn, wm);
+    const LoadOffsets<S> lo = load_offsets<S>(K / 2, K / 32);
+    int tm, tn;
+    tile_of(t, tiles_m, tiles_n, gm, tm, tn);
+    TileSrc<S> cur =
+        tile_src<S>(x, xs, w, ws, (int64_t)tm * S::BM, M, (int64_t)tn * S::BN, N, K);
+    v16f acc[S::NB][S::MB];
+    zero_acc<S>(acc);
+    Pipe<S> pp;
+    int cbase = 0;
+    prologue<S>(lds, cur, lo, nkt, cbase, pp, ro);
+    for (;;) {
+        const int t_next = t + stride;
+        const bool have_next = t_next < t_end;
+        int tm_next = tm, tn_next = tn;
+        if (have_next) tile_of(t_next, tiles_m, tiles_n, gm, tm_next, tn_next);
+        // the last tile streams its own first stages again: surplus loads,
+        // drained before the workgroup ends, that keep one loop body
+        const TileSrc<S> nxt = tile_src<S>(x, xs, w, ws, (int64_t)tm_next * S::BM, M,
+                                           (int64_t)tn_next * S::BN, N, K);
+        main_loop<S, S::MB, true, true>(lds, cur, nxt, lo, nkt, cbase, pp, acc, ro);
+        store_tile<S, OUT_BF16, ROWS>(acc, stage, y, (int64_t)tm * S::BM, M,
+                                      (int64_t)tn * S::BN, N, wn, wm);
+        if (!have_next) break;
+        load_codes<S>(lds, nxt.op, lo, 1, 1);     // after this wave's epilogue reads
+        rezero_acc<S>(acc);
+        cbase += nkt / 2;
+        cur = nxt;
+        t = t_next;
+        tm = tm_next;
+        tn = tn_next;
+    }
+    wait_vm<0>();
 }
 
 // ---------------------------------------------------------------------------
@@ -659,7 +772,6 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(
 // ---------------------------------------------------------------------------
 constexpr int GROUP_MAX_E = 2048;
 constexpr int GROUP_TABLE_BYTES = (3 * GROUP_MAX_E + 1) * 4;
-constexpr int GROUP_LDS_LIMIT = 160 * 1024;     // LDS a workgroup may hold
 
 __device__ __forceinline__ int wave_inclusive_scan(int v) {
     const int lane = threadIdx.x & 63;
@@ -749,18 +861,19 @@ __device__ __forceinline__ TileSrc<S> item_src(const GroupItem& it, const uint8_
 
 template <class S, bool PREFETCH>
 __device__ __forceinline__ void main_loop_jl(int jl, lds_u8* lds, const TileSrc<S>& cur,
-                                             const TileSrc<S>& nxt, int nkt, int cbase,
+                                             const TileSrc<S>& nxt, const LoadOffsets<S>& lo,
+                                             int nkt, int cbase,
                                              Pipe<S>& pp, v16f (&acc)[S::NB][S::MB],
                                              const ReadOffsets& ro) {
     static_assert(S::WGM == 1 && S::MB == 4, "one wave row of four 32-row blocks");
     if (jl >= 4)
-        main_loop<S, 4, PREFETCH>(lds, cur, nxt, nkt, cbase, pp, acc, ro);
+        main_loop<S, 4, PREFETCH>(lds, cur, nxt, lo, nkt, cbase, pp, acc, ro);
     else if (jl == 3)
-        main_loop<S, 3, PREFETCH>(lds, cur, nxt, nkt, cbase, pp, acc, ro);
+        main_loop<S, 3, PREFETCH>(lds, cur, nxt, lo, nkt, cbase, pp, acc, ro);
     else if (jl == 2)
-        main_loop<S, 2, PREFETCH>(lds, cur, nxt, nkt, cbase, pp, acc, ro);
+        main_loop<S, 2, PREFETCH>(lds, cur, nxt, lo, nkt, cbase, pp, acc, ro);
     else
-        main_loop<S, 1, PREFETCH>(lds, cur, nxt, nkt, cbase, pp, acc, ro);
+        main_loop<S, 1, PREFETCH>(lds, cur, nxt, lo, nkt, cbase, pp, acc, ro);
 }
 
 template <bool OUT_BF16>
@@ -775,8 +888,8 @@ __global__ __launch_bounds__(256, 1) void grouped_tiled_kernel(
     // is stored)
     using T = Stage<S, OUT_BF16>;
     constexpr int STAGE_BASE = (S::LDS_BYTES + GROUP_TABLE_BYTES + 15) / 16 * 16;
-    constexpr int ROWS = T::rows_for((GROUP_LDS_LIMIT - STAGE_BASE) / 4);
-    static_assert(STAGE_BASE + 4 * T::bytes(ROWS) <= GROUP_LDS_LIMIT, "LDS budget");
+    constexpr int ROWS = T::rows_for((LDS_LIMIT - STAGE_BASE) / 4);
+    static_assert(STAGE_BASE + 4 * T::bytes(ROWS) <= LDS_LIMIT, "LDS budget");
     __shared__ __attribute__((aligned(16))) uint8_t smem[STAGE_BASE + 4 * T::bytes(ROWS)];
     lds_u8* lds = (lds_u8*)smem;
     int* table = reinterpret_cast<int*>(smem + S::LDS_BYTES);
@@ -796,6 +909,7 @@ __global__ __launch_bounds__(256, 1) void grouped_tiled_kernel(
     const int wn = wave % S::WGN, wm = wave / S::WGN;
     const int nkt = (int)(K / 256);           // even: K % 512 == 0
     const ReadOffsets ro = read_offsets<S>(wn, wm);
+    const LoadOffsets<S> lo = load_offsets<S>(K / 2, K / 32);
 
     GroupItem it = decode_item<S::BM>(tb, E, tiles_n, t, 0);
     TileSrc<S> cur = item_src<S>(it, x, xs, w, ws, N, K);
@@ -803,7 +917,7 @@ __global__ __launch_bounds__(256, 1) void grouped_tiled_kernel(
     zero_acc<S>(acc);
     Pipe<S> pp;
     int cbase = 0;
-    prologue<S>(lds, cur, nkt, cbase, pp, ro);
+    prologue<S>(lds, cur, lo, nkt, cbase, pp, ro);
     for (;;) {
         const int tn = t + stride;
         const bool have_next = tn < t_end;
@@ -811,9 +925,9 @@ __global__ __launch_bounds__(256, 1) void grouped_tiled_kernel(
         const TileSrc<S> nxt = item_src<S>(nx, x, xs, w, ws, N, K);
         const bool prefetch = have_next && nkt >= 4;
         if (prefetch)
-            main_loop_jl<S, true>(it.jl, lds, cur, nxt, nkt, cbase, pp, acc, ro);
+            main_loop_jl<S, true>(it.jl, lds, cur, nxt, lo, nkt, cbase, pp, acc, ro);
         else
-            main_loop_jl<S, false>(it.jl, lds, cur, cur, nkt, cbase, pp, acc, ro);
+            main_loop_jl<S, false>(it.jl, lds, cur, cur, lo, nkt, cbase, pp, acc, ro);
         if (!prefetch) wait_vm<0>();          // drain the surplus loads
         store_tile<S, OUT_BF16, ROWS>(acc, lds + STAGE_BASE + wave * T::bytes(ROWS), y, it.m0,
                                       it.m_end, (int64_t)it.tn * S::BN, N, wn, wm);
@@ -825,7 +939,7 @@ __global__ __launch_bounds__(256, 1) void grouped_tiled_kernel(
             // every wave is past its last LDS read of this tile
             __builtin_amdgcn_s_barrier();
             cbase = 0;
-            prologue<S>(lds, nxt, nkt, cbase, pp, ro);
+            prologue<S>(lds, nxt, lo, nkt, cbase, pp, ro);
         }
         it = nx;
         cur = nxt;
@@ -872,6 +986,24 @@ hipError_t launch_gemm_tiled(const uint8_t* a_codes, const uint8_t* a_scales,
     const int tiles_n = (int)((N + S::BN - 1) / S::BN);
     const int total = tiles_m * tiles_n;
     const int per_xcd = (total + 7) / 8;
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return hipErrorInvalidDevice;
+    const int slots = cus / 8 > 0 ? cus / 8 : 1;   // resident workgroups per XCD
+    if (per_xcd > slots && K >= 1024) {
+        // more than one round: persistent, each XCD's workgroups walking its
+        // run side by side in compact blocks
+        const int gm = group_rows(tiles_m, slots);
+        const dim3 grid((unsigned)(slots * 8));
+        if (out_bf16)
+            hipLaunchKernelGGL(tiled::gemm_persistent_kernel<true>, grid, dim3(256), 0, stream,
+                               a_codes, a_scales, b_codes, b_scales, M, N, K, y, gm);
+        else
+            hipLaunchKernelGGL(tiled::gemm_persistent_kernel<false>, grid, dim3(256), 0, stream,
+                               a_codes, a_scales, b_codes, b_scales, M, N, K, y, gm);
+        return hipGetLastError();
+    }
     const int gm = group_rows(tiles_m, per_xcd);
     const dim3 grid((unsigned)(per_xcd * 8));
     if (out_bf16)
