@@ -82,6 +82,23 @@ int mxfp4_requant_from_nvfp4(const uint8_t* nv_codes, const uint8_t* nv_scales,
                              uint32_t flags, hipStream_t stream);
 
 /*
+ * The same requant of a chosen subset of the T tensors, in one launch: a
+ * loader converting a layer whose excluded tensors (the blog's note on
+ * producer excludes) break it into runs.  Arguments as above, plus
+ *   tensors    [n_tensors] int32, HOST memory, read during the call: the
+ *              tensor indices to convert, strictly increasing, each in
+ *              [0, T); tensor t is read from slot t of the source and
+ *              written to slot t of the destination, other slots untouched
+ * Errors: MXFP4_EINVAL for a list out of range or not strictly increasing
+ * (checked before anything is launched).  n_tensors == 0 is a no-op.
+ */
+int mxfp4_requant_from_nvfp4_subset(const uint8_t* nv_codes, const uint8_t* nv_scales,
+                                    const float* nv_global, int64_t T, int64_t N, int64_t K,
+                                    const int32_t* tensors, int64_t n_tensors,
+                                    uint8_t* mx_codes, uint8_t* mx_scales,
+                                    uint32_t flags, hipStream_t stream);
+
+/*
  * Dynamic per-call MXFP4 quantization of bf16 activations (AMD blog, closing
  * list: activations are quantized for each batch, no stored scales).  Row i
  * of the output is the OCP MX quantization (rule as above, amax over the 32

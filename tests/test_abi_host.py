@@ -105,3 +105,21 @@ def test_requant_argument_checks(lib):
     assert f(ODD, FAKE, FAKE, 1, 16, 64, FAKE, FAKE, 0, None) == -2
     assert f(FAKE, ODD, FAKE, 1, 16, 64, FAKE, FAKE, 0, None) == -2      # u16 scale loads
     assert f(FAKE, FAKE, FAKE, 0, 16, 64, FAKE, FAKE, 0, None) == 0      # T == 0
+
+
+def test_requant_subset_argument_checks(lib):
+    f = lib.mxfp4_requant_from_nvfp4_subset
+    ok = (ctypes.c_int32 * 3)(0, 2, 5)
+    bad_order = (ctypes.c_int32 * 3)(0, 2, 2)
+    bad_range = (ctypes.c_int32 * 2)(0, 6)
+    negative = (ctypes.c_int32 * 1)(-1)
+    P = lambda a: ctypes.cast(a, ctypes.c_void_p)
+    assert f(FAKE, FAKE, FAKE, 6, 16, 64, P(bad_order), 3, FAKE, FAKE, 0, None) == -1
+    assert f(FAKE, FAKE, FAKE, 6, 16, 64, P(bad_range), 2, FAKE, FAKE, 0, None) == -1
+    assert f(FAKE, FAKE, FAKE, 6, 16, 64, P(negative), 1, FAKE, FAKE, 0, None) == -1
+    assert f(FAKE, FAKE, FAKE, 6, 16, 64, None, 3, FAKE, FAKE, 0, None) == -1
+    assert f(FAKE, FAKE, FAKE, 6, 16, 64, P(ok), -1, FAKE, FAKE, 0, None) == -1
+    assert f(FAKE, FAKE, FAKE, 6, 16, 48, P(ok), 3, FAKE, FAKE, 0, None) == -1      # K % 32
+    assert f(FAKE, FAKE, FAKE, 6, 16, 64, P(ok), 3, FAKE, FAKE, 2, None) == -1      # flags
+    assert f(ODD, FAKE, FAKE, 6, 16, 64, P(ok), 3, FAKE, FAKE, 0, None) == -2
+    assert f(FAKE, FAKE, FAKE, 6, 16, 64, P(ok), 0, FAKE, FAKE, 0, None) == 0       # empty list

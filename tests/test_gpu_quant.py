@@ -236,3 +236,31 @@ def test_requant_rerun_is_identical(mx):
     s2 = torch.full_like(s1, 0x5A)
     mx.mxfp4_requant_from_nvfp4(codes, scales, g.reshape(-1), c2, s2)
     assert torch.equal(c1, c2) and torch.equal(s1, s2)
+
+
+@pytest.mark.parametrize("T,N,K,every", [(8, 256, 1024, (0, 2, 3, 7)), (1100, 16, 64, None)])
+def test_requant_subset(mx, T, N, K, every):
+    """The subset call converts exactly the listed tensors (bit-exact against
+    the oracle) and leaves every other destination slot as it was.  1100 tiny
+    tensors with 825 listed take two launches (512 indices a launch)."""
+    say(f"requant subset T={T} N={N} K={K}")
+    w = synth.bf16_normal((T, N, K), 0.02, seed=T + N)
+    codes, scales, g = synth.nvfp4_from_bf16(w)
+    sel = list(every) if every else [t for t in range(T) if t % 4 != 1]
+    gc = Guarded((T, N, K // 2), torch.uint8)
+    gs = Guarded((T, N, K // 32), torch.uint8)
+    gc.view.fill_(0x5A)
+    gs.view.fill_(0xA5)
+    mx.mxfp4_requant_from_nvfp4(codes.to(dev()), scales.to(dev()), g.reshape(-1).to(dev()),
+                                gc.view, gs.view, tensors=sel)
+    torch.cuda.synchronize()
+    assert gc.intact() and gs.intact(), "write outside the destination"
+    oc, os_ = oracle.requant(u8(codes), u8(scales), g.reshape(-1).numpy().astype(np.float32))
+    oc, os_ = oc.reshape(T, N, K // 2), os_.reshape(T, N, K // 32)
+    got_c, got_s = u8(gc.view), u8(gs.view)
+    rest = [t for t in range(T) if t not in set(sel)]
+    assert np.array_equal(got_c[sel], oc[sel]) and np.array_equal(got_s[sel], os_[sel])
+    assert (got_c[rest] == 0x5A).all() and (got_s[rest] == 0xA5).all()
+    with pytest.raises(mx.Mxfp4Error):
+        mx.mxfp4_requant_from_nvfp4(codes.to(dev()), scales.to(dev()), g.reshape(-1).to(dev()),
+                                    gc.view, gs.view, tensors=[1, 0])

@@ -39,6 +39,8 @@ def _load_library() -> ctypes.CDLL:
     P, I, U32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32, ctypes.c_size_t
     lib.mxfp4_requant_from_nvfp4.argtypes = [P, P, P, I, I, I, P, P, U32, P]
     lib.mxfp4_requant_from_nvfp4.restype = ctypes.c_int
+    lib.mxfp4_requant_from_nvfp4_subset.argtypes = [P, P, P, I, I, I, P, I, P, P, U32, P]
+    lib.mxfp4_requant_from_nvfp4_subset.restype = ctypes.c_int
     lib.mxfp4_quantize_act.argtypes = [P, I, P, I, I, P, P, U32, P]
     lib.mxfp4_quantize_act.restype = ctypes.c_int
     lib.mxfp4_gemm.argtypes = [P, P, P, P, I, I, I, P, ctypes.c_int, P, SZ, U32, P]
@@ -56,7 +58,8 @@ def _load_library() -> ctypes.CDLL:
 
 _lib = _load_library()
 
-EXPORTED_SYMBOLS = ("mxfp4_requant_from_nvfp4", "mxfp4_quantize_act", "mxfp4_gemm",
+EXPORTED_SYMBOLS = ("mxfp4_requant_from_nvfp4", "mxfp4_requant_from_nvfp4_subset",
+                    "mxfp4_quantize_act", "mxfp4_gemm",
                     "mxfp4_grouped_gemm", "mxfp4_gemm_workspace_size",
                     "mxfp4_status_string", "mxfp4_version")
 
@@ -108,10 +111,12 @@ def _check(fn, status):
 
 # ---- the four calls ---------------------------------------------------------------
 def mxfp4_requant_from_nvfp4(nv_codes, nv_scales, nv_global, mx_codes=None, mx_scales=None,
-                             *, bf16_intermediate=False, stream=None):
+                             *, bf16_intermediate=False, tensors=None, stream=None):
     """NVFP4 ([T,]N,K/2 codes, [T,]N,K/16 E4M3 bytes, fp32 global [T]) -> MXFP4
     ([T,]N,K/2 codes, [T,]N,K/32 E8M0 bytes), written into mx_codes/mx_scales
-    (allocated when None).  Returns (mx_codes, mx_scales)."""
+    (allocated when None).  `tensors` (strictly increasing indices into the T
+    tensors) converts only those, in one launch, leaving the other slots of
+    the destination untouched.  Returns (mx_codes, mx_scales)."""
     _need(nv_codes, "nv_codes", torch.uint8)
     dev = nv_codes.device
     _need(nv_scales, "nv_scales", torch.uint8, dev)
@@ -132,6 +137,14 @@ def mxfp4_requant_from_nvfp4(nv_codes, nv_scales, nv_global, mx_codes=None, mx_s
     if mx_codes.shape != (*lead, N, K // 2) or mx_scales.shape != (*lead, N, K // 32):
         raise ValueError("destination shapes do not match the source")
     flags = MXFP4_REQ_INTERMEDIATE_BF16 if bf16_intermediate else 0
+    if tensors is not None:
+        sel = [int(t) for t in tensors]
+        arr = (ctypes.c_int32 * max(len(sel), 1))(*sel)
+        _check("mxfp4_requant_from_nvfp4_subset", _lib.mxfp4_requant_from_nvfp4_subset(
+            _ptr(nv_codes), _ptr(nv_scales), _ptr(nv_global), T, N, K,
+            ctypes.cast(arr, ctypes.c_void_p), len(sel),
+            _ptr(mx_codes), _ptr(mx_scales), flags, _stream(stream, dev)))
+        return mx_codes, mx_scales
     _check("mxfp4_requant_from_nvfp4", _lib.mxfp4_requant_from_nvfp4(
         _ptr(nv_codes), _ptr(nv_scales), _ptr(nv_global), T, N, K,
         _ptr(mx_codes), _ptr(mx_scales), flags, _stream(stream, dev)))

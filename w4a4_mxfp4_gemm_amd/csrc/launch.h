@@ -11,10 +11,12 @@ hipError_t launch_act_quant(const uint16_t* x, int64_t ldx, const int32_t* row_i
                             int64_t M, int64_t K, uint8_t* codes, uint8_t* scales,
                             hipStream_t stream);
 
+// tensors == nullptr: all T tensors; else the n_tensors listed (host memory,
+// each in [0, T)).
 hipError_t launch_requant(const uint8_t* nv_codes, const uint8_t* nv_scales,
                           const float* nv_global, int64_t T, int64_t N, int64_t K,
-                          uint8_t* mx_codes, uint8_t* mx_scales, bool bf16_intermediate,
-                          hipStream_t stream);
+                          const int32_t* tensors, int64_t n_tensors, uint8_t* mx_codes,
+                          uint8_t* mx_scales, bool bf16_intermediate, hipStream_t stream);
 
 hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
                        const uint8_t* b_codes, const uint8_t* b_scales,

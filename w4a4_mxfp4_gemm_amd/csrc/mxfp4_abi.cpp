@@ -45,9 +45,30 @@ int mxfp4_requant_from_nvfp4(const uint8_t* nv_codes, const uint8_t* nv_scales,
     if (!aligned(nv_codes, 16) || !aligned(mx_codes, 16) || !aligned(nv_scales, 2) ||
         !aligned(nv_global, 4))
         return MXFP4_EALIGN;
-    return from_hip(mx::launch_requant(nv_codes, nv_scales, nv_global, T, N, K, mx_codes,
-                                       mx_scales, (flags & MXFP4_REQ_INTERMEDIATE_BF16) != 0,
-                                       stream));
+    return from_hip(mx::launch_requant(nv_codes, nv_scales, nv_global, T, N, K, nullptr, 0,
+                                       mx_codes, mx_scales,
+                                       (flags & MXFP4_REQ_INTERMEDIATE_BF16) != 0, stream));
+}
+
+int mxfp4_requant_from_nvfp4_subset(const uint8_t* nv_codes, const uint8_t* nv_scales,
+                                    const float* nv_global, int64_t T, int64_t N, int64_t K,
+                                    const int32_t* tensors, int64_t n_tensors,
+                                    uint8_t* mx_codes, uint8_t* mx_scales, uint32_t flags,
+                                    hipStream_t stream) {
+    if (T < 0 || N <= 0 || check_k(K) != MXFP4_OK || n_tensors < 0) return MXFP4_EINVAL;
+    if ((flags & ~(uint32_t)MXFP4_REQ_INTERMEDIATE_BF16) != 0) return MXFP4_EINVAL;
+    if (n_tensors == 0) return MXFP4_OK;
+    if (!tensors) return MXFP4_EINVAL;
+    for (int64_t i = 0; i < n_tensors; ++i)    // in range, strictly increasing
+        if (tensors[i] < 0 || tensors[i] >= T || (i > 0 && tensors[i] <= tensors[i - 1]))
+            return MXFP4_EINVAL;
+    if (!nv_codes || !nv_scales || !nv_global || !mx_codes || !mx_scales) return MXFP4_EINVAL;
+    if (!aligned(nv_codes, 16) || !aligned(mx_codes, 16) || !aligned(nv_scales, 2) ||
+        !aligned(nv_global, 4))
+        return MXFP4_EALIGN;
+    return from_hip(mx::launch_requant(nv_codes, nv_scales, nv_global, T, N, K, tensors,
+                                       n_tensors, mx_codes, mx_scales,
+                                       (flags & MXFP4_REQ_INTERMEDIATE_BF16) != 0, stream));
 }
 
 int mxfp4_quantize_act(const void* x_bf16, int64_t ldx, const int32_t* row_index, int64_t M,

@@ -152,13 +152,24 @@ __device__ __forceinline__ void requant_block(uint4 raw, uint32_t sc, float g_ab
 // y walks tensors (each with its own global scale).  Source and destination
 // are touched exactly once and are far larger than the caches, so loads and
 // stores are non-temporal (measured: about 12% more bandwidth on a layer).
-template <bool BF16_INTERMEDIATE>
+// Tensors of a subset requant, chosen on the host and passed by value in
+// the kernel arguments (no device memory): up to NSEL per launch.  NSEL = 1
+// is the whole-batch form, where the list is unused.
+template <int NSEL>
+struct TensorSel {
+    int32_t t[NSEL];
+};
+constexpr int REQUANT_SEL = 512;
+
+// `count` tensors: tensor i of the launch is sel.t[i] (NSEL > 1) or i.
+template <bool BF16_INTERMEDIATE, int NSEL>
 __global__ __launch_bounds__(256) void requant_kernel(
     const uint8_t* __restrict__ nv_codes, const uint8_t* __restrict__ nv_scales,
-    const float* __restrict__ nv_global, int64_t T, int64_t blocks_per_tensor,
-    uint8_t* __restrict__ mx_codes, uint8_t* __restrict__ mx_scales) {
+    const float* __restrict__ nv_global, int64_t count, const TensorSel<NSEL> sel,
+    int64_t blocks_per_tensor, uint8_t* __restrict__ mx_codes, uint8_t* __restrict__ mx_scales) {
     constexpr int UNROLL = 2;
-    for (int64_t t = blockIdx.y; t < T; t += gridDim.y) {
+    for (int64_t i = blockIdx.y; i < count; i += gridDim.y) {
+        const int64_t t = NSEL > 1 ? (int64_t)sel.t[i] : i;
         const float g = nv_global[t];
         const float g_abs = __builtin_fabsf(g);
         const uint32_t g_sign = __float_as_uint(g) >> 31;
@@ -209,20 +220,40 @@ hipError_t launch_act_quant(const uint16_t* x, int64_t ldx, const int32_t* row_i
 
 hipError_t launch_requant(const uint8_t* nv_codes, const uint8_t* nv_scales,
                           const float* nv_global, int64_t T, int64_t N, int64_t K,
-                          uint8_t* mx_codes, uint8_t* mx_scales, bool bf16_intermediate,
-                          hipStream_t stream) {
+                          const int32_t* tensors, int64_t n_tensors, uint8_t* mx_codes,
+                          uint8_t* mx_scales, bool bf16_intermediate, hipStream_t stream) {
     const int64_t bpt = N * (K / 32);
     int64_t gx = (bpt + 511) / 512;
     if (gx > 8192) gx = 8192;
-    const int64_t gy = T > 65535 ? 65535 : T;
-    const dim3 grid((unsigned)gx, (unsigned)gy);
-    if (bf16_intermediate)
-        hipLaunchKernelGGL(requant_kernel<true>, grid, dim3(256), 0, stream, nv_codes, nv_scales,
-                           nv_global, T, bpt, mx_codes, mx_scales);
-    else
-        hipLaunchKernelGGL(requant_kernel<false>, grid, dim3(256), 0, stream, nv_codes,
-                           nv_scales, nv_global, T, bpt, mx_codes, mx_scales);
-    return hipGetLastError();
+    auto grid = [&](int64_t count) {
+        return dim3((unsigned)gx, (unsigned)(count > 65535 ? 65535 : count));
+    };
+    if (!tensors) {
+        const TensorSel<1> none{{0}};
+        if (bf16_intermediate)
+            hipLaunchKernelGGL((requant_kernel<true, 1>), grid(T), dim3(256), 0, stream,
+                               nv_codes, nv_scales, nv_global, T, none, bpt, mx_codes, mx_scales);
+        else
+            hipLaunchKernelGGL((requant_kernel<false, 1>), grid(T), dim3(256), 0, stream,
+                               nv_codes, nv_scales, nv_global, T, none, bpt, mx_codes, mx_scales);
+        return hipGetLastError();
+    }
+    for (int64_t c0 = 0; c0 < n_tensors; c0 += REQUANT_SEL) {
+        const int64_t count = n_tensors - c0 < REQUANT_SEL ? n_tensors - c0 : REQUANT_SEL;
+        TensorSel<REQUANT_SEL> sel{};
+        for (int64_t i = 0; i < count; ++i) sel.t[i] = tensors[c0 + i];
+        if (bf16_intermediate)
+            hipLaunchKernelGGL((requant_kernel<true, REQUANT_SEL>), grid(count), dim3(256), 0,
+                               stream, nv_codes, nv_scales, nv_global, count, sel, bpt, mx_codes,
+                               mx_scales);
+        else
+            hipLaunchKernelGGL((requant_kernel<false, REQUANT_SEL>), grid(count), dim3(256), 0,
+                               stream, nv_codes, nv_scales, nv_global, count, sel, bpt, mx_codes,
+                               mx_scales);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace mx
