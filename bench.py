@@ -194,27 +194,39 @@ def decode_workload(torch, mx, synth):
         mx.mxfp4_quantize_act(xs[M], *xq[M])
         mx.mxfp4_gemm(xq[M][0], xq[M][1], dst[r][0], dst[r][1], ys[M])
 
+    ws_bytes = max(mx.mxfp4_linear_workspace_size(M, N, K) for M in Ms)
+    ws = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=d)
+
+    def linear(r, M):               # the same pair as one call
+        mx.mxfp4_linear_bf16(xs[M], dst[r][0], dst[r][1], ys[M], workspace=ws)
+
     ph = Phases(torch, R)
-    ph.add("step", lambda r: (requant(r), [pair(r, M) for M in Ms]))
+    ph.add("step", lambda r: (requant(r), [linear(r, M) for M in Ms]))
+    ph.add("linears", lambda r: [linear(r, M) for M in Ms])
     ph.add("pairs", lambda r: [pair(r, M) for M in Ms])
     ph.add("gemm", lambda r: [mx.mxfp4_gemm(xq[M][0], xq[M][1], dst[r][0], dst[r][1], ys[M])
                               for M in Ms])
     ph.add("requant", requant)
     for M in Ms:
+        ph.add(f"linear_M{M}", lambda r, M=M: linear(r, M))
         ph.add(f"act_quant_M{M}", lambda r, M=M: mx.mxfp4_quantize_act(xs[M], *xq[M]))
         ph.add(f"gemm_M{M}", lambda r, M=M: mx.mxfp4_gemm(xq[M][0], xq[M][1], dst[r][0],
                                                            dst[r][1], ys[M]))
 
     def report(t, steps):
         flops = sum(2 * M * N * K for M in Ms)
-        value = flops / (t["pairs"] * 1e-3) / 1e12
+        value = flops / (t["linears"] * 1e-3) / 1e12
         gb_req = requant_bytes(1, N, K) / (t["requant"] * 1e-3) / 1e9
         gemm_b = sum(gemm_bytes(M, N, K) for M in Ms)
         gemm_gbps = gemm_b / (t["gemm"] * 1e-3) / 1e9
         per_m = {}
         for M in Ms:
             ta, tg = t[f"act_quant_M{M}"], t[f"gemm_M{M}"]
+            tl = t[f"linear_M{M}"]
             per_m[str(M)] = {
+                "linear_us": round(tl * 1e3, 2),
+                "linear_one_launch": mx.mxfp4_linear_workspace_size(M, N, K) == 0,
+                "TFLOPs_linear": round(2 * M * N * K / (tl * 1e-3) / 1e12, 3),
                 "act_quant_us": round(ta * 1e3, 2), "gemm_us": round(tg * 1e3, 2),
                 "gemm_GBps": round(gemm_bytes(M, N, K) / (tg * 1e-3) / 1e9, 1),
                 "gemm_frac_hbm": round(gemm_bytes(M, N, K) / (tg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
@@ -229,10 +241,12 @@ def decode_workload(torch, mx, synth):
         extra = {"requant_GBps": round(gb_req, 1),
                  "requant_frac_hbm": round(gb_req / HBM_PEAK_GBPS, 4),
                  "requant_us": round(t["requant"] * 1e3, 2),
+                 "linear_calls_us": round(t["linears"] * 1e3, 2),
                  "act_quant_plus_gemm_us": round(t["pairs"] * 1e3, 2),
                  "per_M": per_m, "weight_copies_rotated": R}
         cfg = {"workload": "decode-shaped dense linear: NVFP4->MXFP4 requant of W "
-                           "[12288,4096] + act-quant + W4A4 GEMM for M in {1,8,32,64}, bf16 out",
+                           "[12288,4096] + act-quant + W4A4 GEMM for M in {1,8,32,64} "
+                           "(mxfp4_linear_bf16), bf16 out",
                "N": N, "K": K, "M": list(Ms)}
         return value, "TFLOP/s", roof, extra, cfg
 

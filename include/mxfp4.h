@@ -163,6 +163,32 @@ int mxfp4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
 /* Workspace bytes mxfp4_gemm / mxfp4_grouped_gemm need (currently 0). */
 size_t mxfp4_gemm_workspace_size(int64_t M, int64_t N, int64_t K);
 
+/*
+ * One linear layer on bf16 activations: the MXFP4 quantization of
+ * mxfp4_quantize_act (row i of x, no gather) followed by mxfp4_gemm with B,
+ * giving the same y bit for bit.  For decode-shaped calls (M <= 16, K = 2048
+ * or 4096, N >= 16, 16-byte-aligned b_scales) it is one launch whose
+ * workgroups quantize their own activation blocks while their weight loads
+ * stream; otherwise the two launches run through the caller's workspace.
+ *
+ *   x_bf16      [M][ldx] bf16, device, read (16-byte aligned, ldx % 8 == 0,
+ *               ldx >= K)
+ *   b_codes, b_scales, y, out_dtype   as for mxfp4_gemm
+ *   workspace   device memory of at least mxfp4_linear_workspace_size(M, N,
+ *               K) bytes (16-byte aligned; may be NULL when that is 0):
+ *               the quantized activations of the two-launch form
+ *   flags       0
+ * Errors as for mxfp4_gemm; MXFP4_EINVAL also for a workspace smaller than
+ * the two-launch form needs when that form is taken.
+ */
+int mxfp4_linear_bf16(const void* x_bf16, int64_t ldx, int64_t M, int64_t N, int64_t K,
+                      const uint8_t* b_codes, const uint8_t* b_scales, void* y,
+                      int out_dtype, void* workspace, size_t workspace_bytes,
+                      uint32_t flags, hipStream_t stream);
+
+/* Workspace bytes mxfp4_linear_bf16 needs: 0 for the one-launch shapes. */
+size_t mxfp4_linear_workspace_size(int64_t M, int64_t N, int64_t K);
+
 /* Static description of a status code; never NULL. */
 const char* mxfp4_status_string(int status);
 

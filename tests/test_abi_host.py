@@ -123,3 +123,29 @@ def test_requant_subset_argument_checks(lib):
     assert f(FAKE, FAKE, FAKE, 6, 16, 64, P(ok), 3, FAKE, FAKE, 2, None) == -1      # flags
     assert f(ODD, FAKE, FAKE, 6, 16, 64, P(ok), 3, FAKE, FAKE, 0, None) == -2
     assert f(FAKE, FAKE, FAKE, 6, 16, 64, P(ok), 0, FAKE, FAKE, 0, None) == 0       # empty list
+
+
+def test_linear_argument_checks(lib):
+    f = lib.mxfp4_linear_bf16
+    #        x    ldx  M  N    K     b_codes b_scales y    dtype ws   ws_bytes flags stream
+    assert f(FAKE, 4000, 1, 256, 4096, FAKE, FAKE, FAKE, 0, None, 0, 0, None) == -1   # ldx < K
+    assert f(FAKE, 4096, 1, 256, 4080, FAKE, FAKE, FAKE, 0, None, 0, 0, None) == -1   # K % 32
+    assert f(FAKE, 4096, 1, 0, 4096, FAKE, FAKE, FAKE, 0, None, 0, 0, None) == -1      # N
+    assert f(FAKE, 4096, 1, 256, 4096, FAKE, FAKE, FAKE, 7, None, 0, 0, None) == -1    # out_dtype
+    assert f(FAKE, 4096, 1, 256, 4096, FAKE, FAKE, FAKE, 0, None, 0, 1, None) == -1    # flags
+    assert f(FAKE, 4096, 1, 256, 4096, FAKE, FAKE, FAKE, 0, None, 64, 0, None) == -1   # ws NULL
+    assert f(None, 4096, 1, 256, 4096, FAKE, FAKE, FAKE, 0, None, 0, 0, None) == -1
+    assert f(ODD, 4096, 1, 256, 4096, FAKE, FAKE, FAKE, 0, None, 0, 0, None) == -2
+    assert f(FAKE, 4100, 1, 256, 4096, FAKE, FAKE, FAKE, 0, None, 0, 0, None) == -2    # ldx % 8
+    assert f(FAKE, 4096, 0, 256, 4096, FAKE, FAKE, FAKE, 0, None, 0, 0, None) == 0     # M == 0
+    # the two-launch form needs its workspace
+    assert f(FAKE, 1024, 200, 256, 1024, FAKE, FAKE, FAKE, 0, None, 0, 0, None) == -1
+
+
+def test_linear_workspace_size(lib):
+    ws = lib.mxfp4_linear_workspace_size
+    assert ws(1, 12288, 4096) == 0 and ws(16, 4096, 2048) == 0           # one launch
+    assert ws(17, 512, 4096) == (17 * 2048 + 255) // 256 * 256 + 17 * 128
+    assert ws(65, 512, 4096) == (65 * 2048 + 255) // 256 * 256 + 65 * 128
+    assert ws(8, 256, 1024) == (8 * 512 + 255) // 256 * 256 + 8 * 32     # K = 1024
+    assert ws(0, 256, 1024) == 0 and ws(8, 256, 48) == 0                 # nothing to run

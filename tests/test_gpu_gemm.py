@@ -390,3 +390,58 @@ def test_graph_replay_matches_eager(mx):
             assert torch.equal(a, b)
         step()                          # eager work between replays
         torch.cuda.synchronize()
+
+
+# ---- act-quant + GEMM in one call ---------------------------------------------------
+def same_bits(a, b):
+    """Bitwise equality that also accepts NaN against NaN (payloads may differ)."""
+    a, b = a.float().cpu(), b.float().cpu()
+    both_nan = torch.isnan(a) & torch.isnan(b)
+    return bool(((a.view(torch.int32) == b.view(torch.int32)) | both_nan).all())
+
+
+@pytest.mark.parametrize("M,N,K,ldx", [(1, 1000, 4096, 4096), (5, 300, 2048, 2048),
+                                       (16, 12288, 4096, 4096), (17, 257, 4096, 4104),
+                                       (33, 1040, 2048, 2056), (64, 4099, 4096, 4096),
+                                       (65, 512, 4096, 4096), (200, 300, 1024, 1032),
+                                       (8, 256, 1024, 1024)])
+def test_linear_bf16_matches_act_quant_then_gemm(mx, M, N, K, ldx):
+    """mxfp4_linear_bf16 gives the act-quant call followed by the GEMM bit for
+    bit: one launch for the decode shapes (M <= 16, K = 2048/4096), the two
+    launches through the workspace otherwise (M = 17 .. 200; K = 1024); rows
+    wider than K; both output types; NaN and Inf blocks in x."""
+    say(f"linear bf16 M={M} N={N} K={K} ldx={ldx}")
+    x = synth.activations(M, ldx, seed=M + N, outlier_seed=K).to(dev())
+    if M >= 5:
+        x[1, 40] = float("nan")
+        x[2, K - 1] = float("inf")
+        x[4, 64:96] = 0.0
+    w = synth.bf16_normal((N, K), 0.02, seed=N)
+    codes, scales, g = synth.nvfp4_from_bf16(w)
+    wc, ws = mx.mxfp4_requant_from_nvfp4(codes.to(dev()), scales.to(dev()), g.reshape(1).to(dev()))
+    xc, xs = mx.mxfp4_quantize_act(x, K=K)
+    for dt in (torch.bfloat16, torch.float32):
+        ref = mx.mxfp4_gemm(xc, xs, wc, ws, out_dtype=dt)
+        gy = Guarded((M, N), dt)
+        mx.mxfp4_linear_bf16(x, wc, ws, gy.view, K=K)
+        torch.cuda.synchronize()
+        assert gy.intact(), "write outside y"
+        assert same_bits(gy.view, ref), dt
+
+
+def test_linear_bf16_against_oracle(mx):
+    """The one-launch form against the oracle's act-quant and GEMM (decode
+    weight, outlier activations, M = 8)."""
+    M, N, K = 8, 2048, 4096
+    say(f"linear bf16 vs oracle M={M} N={N} K={K}")
+    x = synth.activations(M, K, seed=91, outlier_seed=92)
+    w = synth.bf16_normal((N, K), 0.02, seed=93)
+    codes, scales, g = synth.nvfp4_from_bf16(w)
+    oc, os_ = oracle.requant(u8(codes), u8(scales), np.atleast_1d(g.numpy()))
+    wc, ws = mx.mxfp4_requant_from_nvfp4(codes.to(dev()), scales.to(dev()), g.reshape(1).to(dev()))
+    y32 = mx.mxfp4_linear_bf16(x.to(dev()), wc, ws, out_dtype=torch.float32)
+    yb = mx.mxfp4_linear_bf16(x.to(dev()), wc, ws, out_dtype=torch.bfloat16)
+    ac, as_ = oracle.quantize_act(bf16_bits(x))
+    y, s = oracle.gemm(ac, as_, oc, os_)
+    assert_gemm_fp32(y32, y, s, "linear fp32")
+    assert_gemm_bf16(yb, y, "linear bf16")

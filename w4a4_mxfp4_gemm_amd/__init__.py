@@ -47,6 +47,10 @@ def _load_library() -> ctypes.CDLL:
     lib.mxfp4_gemm.restype = ctypes.c_int
     lib.mxfp4_grouped_gemm.argtypes = [P, P, P, P, P, I, I, I, I, P, ctypes.c_int, P, SZ, U32, P]
     lib.mxfp4_grouped_gemm.restype = ctypes.c_int
+    lib.mxfp4_linear_bf16.argtypes = [P, I, I, I, I, P, P, P, ctypes.c_int, P, SZ, U32, P]
+    lib.mxfp4_linear_bf16.restype = ctypes.c_int
+    lib.mxfp4_linear_workspace_size.argtypes = [I, I, I]
+    lib.mxfp4_linear_workspace_size.restype = SZ
     lib.mxfp4_gemm_workspace_size.argtypes = [I, I, I]
     lib.mxfp4_gemm_workspace_size.restype = SZ
     lib.mxfp4_status_string.argtypes = [ctypes.c_int]
@@ -60,7 +64,8 @@ _lib = _load_library()
 
 EXPORTED_SYMBOLS = ("mxfp4_requant_from_nvfp4", "mxfp4_requant_from_nvfp4_subset",
                     "mxfp4_quantize_act", "mxfp4_gemm",
-                    "mxfp4_grouped_gemm", "mxfp4_gemm_workspace_size",
+                    "mxfp4_grouped_gemm", "mxfp4_linear_bf16", "mxfp4_gemm_workspace_size",
+                    "mxfp4_linear_workspace_size",
                     "mxfp4_status_string", "mxfp4_version")
 
 
@@ -211,6 +216,42 @@ def mxfp4_gemm(a_codes, a_scales, b_codes, b_scales, y=None, *, out_dtype=torch.
     return y
 
 
+def mxfp4_linear_workspace_size(M: int, N: int, K: int) -> int:
+    return int(_lib.mxfp4_linear_workspace_size(M, N, K))
+
+
+def mxfp4_linear_bf16(x, b_codes, b_scales, y=None, *, K=None, out_dtype=torch.bfloat16,
+                      workspace=None, stream=None):
+    """y [M, N] = MXFP4(x) [M, K] * B [N, K]^T from bf16 x [M, ldx] (the act-quant
+    call followed by the GEMM, bit for bit; one launch for decode shapes).  K
+    defaults to x's row length.  A workspace of mxfp4_linear_workspace_size
+    bytes is allocated when none is given and one is needed."""
+    _need(x, "x", torch.bfloat16)
+    dev = x.device
+    _need(b_codes, "b_codes", torch.uint8, dev)
+    _need(b_scales, "b_scales", torch.uint8, dev)
+    if x.dim() != 2:
+        raise ValueError("x must be [M, ldx]")
+    M, ldx = x.shape
+    K = ldx if K is None else K
+    N = b_codes.shape[0]
+    if b_codes.shape != (N, K // 2) or b_scales.shape != (N, K // 32):
+        raise ValueError("operand shapes disagree")
+    if y is None:
+        y = torch.empty((M, N), dtype=out_dtype, device=dev)
+    _need(y, "y", y.dtype, dev)
+    if y.shape != (M, N):
+        raise ValueError("y must be [M, N]")
+    need = mxfp4_linear_workspace_size(M, N, K)
+    if workspace is None and need:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
+    ws_ptr, ws_bytes = (None, 0) if workspace is None else (_ptr(workspace), workspace.numel())
+    _check("mxfp4_linear_bf16", _lib.mxfp4_linear_bf16(
+        _ptr(x), ldx, M, N, K, _ptr(b_codes), _ptr(b_scales), _ptr(y), _out_dtype(y.dtype),
+        ws_ptr, ws_bytes, 0, _stream(stream, dev)))
+    return y
+
+
 def mxfp4_grouped_gemm(a_codes, a_scales, b_codes, b_scales, offsets, y=None, *,
                        out_dtype=torch.bfloat16, stream=None):
     """For each expert e: y[off[e]:off[e+1]] = A[off[e]:off[e+1]] * B[e]^T.
@@ -239,6 +280,7 @@ def mxfp4_grouped_gemm(a_codes, a_scales, b_codes, b_scales, offsets, y=None, *,
 
 
 __all__ = ["mxfp4_requant_from_nvfp4", "mxfp4_quantize_act", "mxfp4_gemm",
-           "mxfp4_grouped_gemm", "mxfp4_gemm_workspace_size", "mxfp4_status_string",
+           "mxfp4_grouped_gemm", "mxfp4_linear_bf16", "mxfp4_gemm_workspace_size",
+           "mxfp4_linear_workspace_size", "mxfp4_status_string",
            "mxfp4_version", "Mxfp4Error", "LIBRARY_PATH", "EXPORTED_SYMBOLS",
            "MXFP4_OUT_BF16", "MXFP4_OUT_FP32", "MXFP4_REQ_INTERMEDIATE_BF16"]

@@ -88,12 +88,67 @@ __device__ __forceinline__ void load_block(Frag<SPW>& f, const uint8_t* codes,
     }
 }
 
-template <int MT, int SPW, int NW, int TPW, bool OUT_BF16>
+// The same share of a 16-row block quantized from bf16 rows (row stride ldx
+// elements) instead of loaded as MXFP4.  Each lane's operand is one whole
+// 32-element MX block of one row, so the lane quantizes it alone, by the
+// activation rule (quant_block32_bf16), into the layout load_block gives --
+// except the scale word of MFMA q, which holds only this lane's byte, at bits
+// 8g.  The codes and scales equal those of the act-quant kernel.  In two
+// steps: load_raw issues the loads (before the weights', so that waiting for
+// them does not wait for the weight stream: vmcnt counts in issue order),
+// quant_raw does the arithmetic once they land.
+template <int SPW>
+struct RawX {
+    v4u v[SPW][4][4];   // super-step j, MFMA q: the lane's 32 values, 4 x 16 B
+};
+
+template <int SPW, int NW>
+__device__ __forceinline__ void load_raw(RawX<SPW>& r, const uint16_t* x, int64_t ldx,
+                                         int64_t row) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int g = lane >> 4;
+    const uint16_t* xrow = x + row * ldx;
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) {
+        const int kb0 = (wave + NW * j) * 16;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const v4u* p = reinterpret_cast<const v4u*>(xrow + (int64_t)(kb0 + 4 * q + g) * 32);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) r.v[j][q][i] = p[i];
+        }
+    }
+}
+
+template <int SPW>
+__device__ __forceinline__ void quant_raw(Frag<SPW>& f, const RawX<SPW>& r) {
+    const int g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            uint32_t v[16], c[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                v[4 * i] = r.v[j][q][i][0], v[4 * i + 1] = r.v[j][q][i][1],
+                v[4 * i + 2] = r.v[j][q][i][2], v[4 * i + 3] = r.v[j][q][i][3];
+            const uint32_t byte = quant_block32_bf16(v, c);
+            f.c[j][q] = v4u{c[0], c[1], c[2], c[3]};
+            f.s[j][q] = byte << (8 * g);
+        }
+    }
+}
+
+// BF16A: x is bf16 [M][ldx] (xs unused) and each wave quantizes its share of
+// the activations itself while its weight loads stream.
+template <int MT, int SPW, int NW, int TPW, bool OUT_BF16, bool BF16A>
 __global__ __launch_bounds__(64 * NW, 1) void gemm_skinny_kernel(
-    const uint8_t* __restrict__ x, const uint8_t* __restrict__ xs,
-    // no __restrict__ on the weights: with it the compiler may sink the weight
-    // loads below the first MFMA, serialising the two memory latencies
-    const uint8_t* w, const uint8_t* ws, int M, int N, int K, void* __restrict__ y) {
+    // no __restrict__ on the operands: with it the compiler may move their loads
+    // across the points that order them (below the first MFMA, or the bf16
+    // activation loads behind the weight loads), serialising the latencies
+    const uint8_t* x, const uint8_t* xs, int64_t ldx, const uint8_t* w, const uint8_t* ws,
+    int M, int N, int K, void* __restrict__ y) {
     __shared__ __attribute__((aligned(16))) Smem<MT, NW> sm;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -102,18 +157,28 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_skinny_kernel(
     const int ntiles = (N + 15) / 16;
     const int stride = gridDim.x;
 
-    // 1. this wave's share of the activations, rows m >= M repeating row M-1
-    //    (their outputs are never stored); issued first so that the first
-    //    MFMA waits for them and for the first weight tile only
-    Frag<SPW> a[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-        load_block<SPW, NW>(a[mt], x, xs, (int64_t)min(mt * 16 + r16, M - 1), nkb);
-
     auto tile_row = [&](int t) {
         const int tt = t < ntiles ? t : ntiles - 1;     // surplus loads: any valid row
         return (int64_t)min(tt * 16 + r16, N - 1);
     };
+
+    // 1. this wave's share of the activations, rows m >= M repeating row M-1
+    //    (their outputs are never stored); issued first so that the first
+    //    MFMA (bf16: the quantization) waits for them and for the first
+    //    weight tile only
+    Frag<SPW> a[MT];
+    RawX<SPW> xr[BF16A ? MT : 1];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int64_t row = (int64_t)min(mt * 16 + r16, M - 1);
+        if constexpr (BF16A)
+            load_raw<SPW, NW>(xr[mt], reinterpret_cast<const uint16_t*>(x), ldx, row);
+        else
+            load_block<SPW, NW>(a[mt], x, xs, row, nkb);
+    }
+    // the activation loads stay ahead of the weight loads (a memory clobber
+    // is a point no load moves across)
+    if constexpr (BF16A) asm volatile("" ::: "memory");
 
     // 2. weights: TPW tiles in flight per wave
     Frag<SPW> slot[TPW];
@@ -121,6 +186,11 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_skinny_kernel(
     for (int i = 0; i < TPW; ++i)
         load_block<SPW, NW>(slot[i], w, ws, tile_row(blockIdx.x + i * stride), nkb);
     __builtin_amdgcn_sched_barrier(0);   // issue every load before the first use
+    if constexpr (BF16A) {
+        asm volatile("" ::: "memory");   // ... and every weight load before the quantization
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) quant_raw<SPW>(a[mt], xr[mt]);
+    }
 
     const uint32_t sh = 8u * (uint32_t)g;
     auto compute = [&](const Frag<SPW>& f, v4f (&acc)[MT]) {
@@ -205,8 +275,25 @@ bool skinny_gemm_supported(int64_t M, int64_t N, int64_t K, const void* x, const
     return M >= 1 && M <= 64 && (K == 2048 || K == 4096) && N >= 16 && aligned;
 }
 
+// ldx > 0: `a` is bf16 activations [M][ldx] (as unused), quantized in the kernel.
+// Shapes the act-quant + GEMM launch serves: those of the skinny GEMM with
+// one 16-row activation block (the raw bf16 share of a wave, 64 registers a
+// lane at one super-step, has to fit beside the weight tiles in flight),
+// bf16 rows 16-byte aligned.
+constexpr int64_t LINEAR_FUSED_MAX = 16;
+
+bool linear_skinny_shape(int64_t M, int64_t N, int64_t K) {
+    return M >= 1 && M <= LINEAR_FUSED_MAX && (K == 2048 || K == 4096) && N >= 16;
+}
+
+bool linear_skinny_supported(int64_t M, int64_t N, int64_t K, const void* x, int64_t ldx,
+                             const void* w_scales) {
+    return linear_skinny_shape(M, N, K) && (reinterpret_cast<uintptr_t>(x) % 16) == 0 &&
+           ldx % 8 == 0 && (reinterpret_cast<uintptr_t>(w_scales) % 16) == 0;
+}
+
 template <int MT, int SPW, int NW>
-static hipError_t launch_mt(const uint8_t* a, const uint8_t* as, const uint8_t* b,
+static hipError_t launch_mt(const uint8_t* a, const uint8_t* as, int64_t ldx, const uint8_t* b,
                             const uint8_t* bs, int64_t M, int64_t N, int64_t K, void* y,
                             bool out_bf16, hipStream_t stream) {
     // tiles in flight per wave: all of a workgroup's tiles when they fit
@@ -214,42 +301,63 @@ static hipError_t launch_mt(const uint8_t* a, const uint8_t* as, const uint8_t* 
     const int ntiles = (int)((N + 15) / 16);
     int grid = (ntiles + TPW - 1) / TPW;
     if (grid > 256) grid = 256;
-    if (out_bf16)
-        hipLaunchKernelGGL((skinny::gemm_skinny_kernel<MT, SPW, NW, TPW, true>), dim3(grid),
-                           dim3(64 * NW), 0, stream, a, as, b, bs, (int)M, (int)N, (int)K, y);
-    else
-        hipLaunchKernelGGL((skinny::gemm_skinny_kernel<MT, SPW, NW, TPW, false>), dim3(grid),
-                           dim3(64 * NW), 0, stream, a, as, b, bs, (int)M, (int)N, (int)K, y);
-    return hipGetLastError();
+    auto go = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, dim3(grid), dim3(64 * NW), 0, stream, a, as, ldx, b, bs,
+                           (int)M, (int)N, (int)K, y);
+        return hipGetLastError();
+    };
+    using namespace skinny;
+    if (ldx > 0) {
+        // the bf16 form exists for one block at one super-step per wave only
+        if constexpr (MT == 1 && SPW == 1)
+            return out_bf16 ? go(gemm_skinny_kernel<MT, SPW, NW, TPW, true, true>)
+                            : go(gemm_skinny_kernel<MT, SPW, NW, TPW, false, true>);
+        return hipErrorInvalidValue;
+    }
+    return out_bf16 ? go(gemm_skinny_kernel<MT, SPW, NW, TPW, true, false>)
+                    : go(gemm_skinny_kernel<MT, SPW, NW, TPW, false, false>);
 }
 
 // K = 4096: NW super-steps of 512 K per wave pass (SPW = 8 / NW each);
 // K = 2048: four waves, one super-step each.
 template <int NW4096>
-static hipError_t launch_k(const uint8_t* a, const uint8_t* as, const uint8_t* b,
+static hipError_t launch_k(const uint8_t* a, const uint8_t* as, int64_t ldx, const uint8_t* b,
                            const uint8_t* bs, int64_t M, int64_t N, int64_t K, void* y,
                            bool out_bf16, hipStream_t stream) {
     constexpr int SPW = 8 / NW4096;
     if (K == 2048) {
-        if (M <= 16) return launch_mt<1, 1, 4>(a, as, b, bs, M, N, K, y, out_bf16, stream);
-        if (M <= 32) return launch_mt<2, 1, 4>(a, as, b, bs, M, N, K, y, out_bf16, stream);
-        if (M <= 48) return launch_mt<3, 1, 4>(a, as, b, bs, M, N, K, y, out_bf16, stream);
-        return launch_mt<4, 1, 4>(a, as, b, bs, M, N, K, y, out_bf16, stream);
+        if (M <= 16) return launch_mt<1, 1, 4>(a, as, ldx, b, bs, M, N, K, y, out_bf16, stream);
+        if (M <= 32) return launch_mt<2, 1, 4>(a, as, ldx, b, bs, M, N, K, y, out_bf16, stream);
+        if (M <= 48) return launch_mt<3, 1, 4>(a, as, ldx, b, bs, M, N, K, y, out_bf16, stream);
+        return launch_mt<4, 1, 4>(a, as, ldx, b, bs, M, N, K, y, out_bf16, stream);
     }
-    if (M <= 16) return launch_mt<1, SPW, NW4096>(a, as, b, bs, M, N, K, y, out_bf16, stream);
-    if (M <= 32) return launch_mt<2, SPW, NW4096>(a, as, b, bs, M, N, K, y, out_bf16, stream);
-    if (M <= 48) return launch_mt<3, SPW, NW4096>(a, as, b, bs, M, N, K, y, out_bf16, stream);
-    return launch_mt<4, SPW, NW4096>(a, as, b, bs, M, N, K, y, out_bf16, stream);
+    if (M <= 16)
+        return launch_mt<1, SPW, NW4096>(a, as, ldx, b, bs, M, N, K, y, out_bf16, stream);
+    if (M <= 32)
+        return launch_mt<2, SPW, NW4096>(a, as, ldx, b, bs, M, N, K, y, out_bf16, stream);
+    if (M <= 48)
+        return launch_mt<3, SPW, NW4096>(a, as, ldx, b, bs, M, N, K, y, out_bf16, stream);
+    return launch_mt<4, SPW, NW4096>(a, as, ldx, b, bs, M, N, K, y, out_bf16, stream);
 }
 
+// two wavefronts per SIMD (at K = 4096; measured 0.3-0.5 us less than one
+// per SIMD at every M)
 hipError_t launch_gemm_skinny(const uint8_t* a_codes, const uint8_t* a_scales,
                               const uint8_t* b_codes, const uint8_t* b_scales, int64_t M,
                               int64_t N, int64_t K, void* y, bool out_bf16, hipStream_t stream) {
-    // two wavefronts per SIMD once the MFMA work matters (measured: ~0.5 us
-    // less at M = 32..64, no gain at M <= 16)
-    if (M > 16)
-        return launch_k<8>(a_codes, a_scales, b_codes, b_scales, M, N, K, y, out_bf16, stream);
-    return launch_k<4>(a_codes, a_scales, b_codes, b_scales, M, N, K, y, out_bf16, stream);
+    return launch_k<8>(a_codes, a_scales, 0, b_codes, b_scales, M, N, K, y, out_bf16, stream);
+}
+
+hipError_t launch_linear_skinny(const uint16_t* x, int64_t ldx, const uint8_t* b_codes,
+                                const uint8_t* b_scales, int64_t M, int64_t N, int64_t K,
+                                void* y, bool out_bf16, hipStream_t stream) {
+    // M <= 16: one activation block; one super-step per wave (eight waves at
+    // K = 4096, four at 2048)
+    const uint8_t* a = reinterpret_cast<const uint8_t*>(x);
+    if (K == 4096)
+        return launch_mt<1, 1, 8>(a, nullptr, ldx, b_codes, b_scales, M, N, K, y, out_bf16,
+                                  stream);
+    return launch_mt<1, 1, 4>(a, nullptr, ldx, b_codes, b_scales, M, N, K, y, out_bf16, stream);
 }
 
 }  // namespace mx

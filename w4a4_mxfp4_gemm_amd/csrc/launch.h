@@ -18,6 +18,16 @@ hipError_t launch_requant(const uint8_t* nv_codes, const uint8_t* nv_scales,
                           const int32_t* tensors, int64_t n_tensors, uint8_t* mx_codes,
                           uint8_t* mx_scales, bool bf16_intermediate, hipStream_t stream);
 
+// Act-quant and weight-streaming GEMM in one launch: x bf16 [M][ldx], for
+// the shapes and alignments linear_skinny_supported accepts
+// (linear_skinny_shape: the shape alone).
+bool linear_skinny_shape(int64_t M, int64_t N, int64_t K);
+bool linear_skinny_supported(int64_t M, int64_t N, int64_t K, const void* x, int64_t ldx,
+                             const void* w_scales);
+hipError_t launch_linear_skinny(const uint16_t* x, int64_t ldx, const uint8_t* b_codes,
+                                const uint8_t* b_scales, int64_t M, int64_t N, int64_t K,
+                                void* y, bool out_bf16, hipStream_t stream);
+
 hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
                        const uint8_t* b_codes, const uint8_t* b_scales,
                        int64_t M, int64_t N, int64_t K, void* y, bool out_bf16,

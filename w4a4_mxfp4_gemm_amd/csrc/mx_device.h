@@ -101,6 +101,32 @@ __device__ __forceinline__ uint32_t cvt_fp4x2_bf16(uint32_t old, uint32_t pair, 
                                                      scale, SEL);
 }
 
+// One whole 32-element MX block of bf16 values held by one lane (16 packed
+// pairs, element 2i in the low half of w[i]) -> its E8M0 byte and 16 code
+// bytes (element 2i in the low nibble of byte i).  The activation rule: amax
+// over the bf16 magnitudes (compared as integers, so NaN and Inf patterns
+// rank above every finite value), the OCP MX exponent, each value divided by
+// the scale and rounded to E2M1; a NaN or Inf block gives 0xFF and zero codes.
+__device__ __forceinline__ uint32_t quant_block32_bf16(const uint32_t (&w)[16], uint32_t (&c)[4]) {
+    typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+    u16x2_t a = __builtin_bit_cast(u16x2_t, w[0] & 0x7FFF7FFFu);
+#pragma unroll
+    for (int i = 1; i < 16; ++i)
+        a = __builtin_elementwise_max(a, __builtin_bit_cast(u16x2_t, w[i] & 0x7FFF7FFFu));
+    const uint32_t amax = a[0] > a[1] ? a[0] : a[1];
+    const uint32_t byte = mx_scale_from_amax_bits(amax << 16);
+    const float scale = e8m0_to_f32(byte);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        uint32_t v = cvt_fp4x2_bf16<0>(0u, w[4 * d], scale);
+        v = cvt_fp4x2_bf16<1>(v, w[4 * d + 1], scale);
+        v = cvt_fp4x2_bf16<2>(v, w[4 * d + 2], scale);
+        v = cvt_fp4x2_bf16<3>(v, w[4 * d + 3], scale);
+        c[d] = byte == 255u ? 0u : v;
+    }
+    return byte;
+}
+
 // Byte permute (v_perm_b32): selector byte k in 0..3 picks byte k of lo,
 // 4..7 picks byte k-4 of hi.
 __device__ __forceinline__ uint32_t byte_perm(uint32_t hi, uint32_t lo, uint32_t sel) {

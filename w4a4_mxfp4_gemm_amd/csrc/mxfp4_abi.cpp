@@ -16,6 +16,12 @@ int from_hip(hipError_t e) { return e == hipSuccess ? MXFP4_OK : MXFP4_EHIP; }
 
 int check_k(int64_t K) { return (K > 0 && K % 32 == 0) ? MXFP4_OK : MXFP4_EINVAL; }
 
+// The linear call's workspace: codes [M][K/2], then scales [M][K/32] from the
+// next 256-byte boundary.
+size_t linear_codes_bytes(int64_t M, int64_t K) {
+    return ((size_t)M * (size_t)(K / 2) + 255) / 256 * 256;
+}
+
 int check_gemm_common(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
                       const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, void* y,
                       int out_dtype, void* workspace, size_t workspace_bytes, uint32_t flags) {
@@ -93,6 +99,42 @@ int mxfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b
     if (st != MXFP4_OK || M == 0) return st;
     return from_hip(mx::launch_gemm(a_codes, a_scales, b_codes, b_scales, M, N, K, y,
                                     out_dtype == MXFP4_OUT_BF16, stream));
+}
+
+size_t mxfp4_linear_workspace_size(int64_t M, int64_t N, int64_t K) {
+    if (M <= 0 || N <= 0 || check_k(K) != MXFP4_OK) return 0;
+    if (mx::linear_skinny_shape(M, N, K)) return 0;
+    return linear_codes_bytes(M, K) + (size_t)M * (size_t)(K / 32);
+}
+
+int mxfp4_linear_bf16(const void* x_bf16, int64_t ldx, int64_t M, int64_t N, int64_t K,
+                      const uint8_t* b_codes, const uint8_t* b_scales, void* y, int out_dtype,
+                      void* workspace, size_t workspace_bytes, uint32_t flags,
+                      hipStream_t stream) {
+    if (M < 0 || N <= 0 || check_k(K) != MXFP4_OK || ldx < K) return MXFP4_EINVAL;
+    if (out_dtype != MXFP4_OUT_BF16 && out_dtype != MXFP4_OUT_FP32) return MXFP4_EINVAL;
+    if (flags != 0) return MXFP4_EINVAL;
+    if (workspace_bytes != 0 && workspace == nullptr) return MXFP4_EINVAL;
+    if (M == 0) return MXFP4_OK;
+    if (!x_bf16 || !b_codes || !b_scales || !y) return MXFP4_EINVAL;
+    if (!aligned(x_bf16, 16) || ldx % 8 != 0 || !aligned(b_codes, 16)) return MXFP4_EALIGN;
+    if (!aligned(y, out_dtype == MXFP4_OUT_FP32 ? 4 : 2)) return MXFP4_EALIGN;
+    const bool out_bf16 = out_dtype == MXFP4_OUT_BF16;
+    if (mx::linear_skinny_supported(M, N, K, x_bf16, ldx, b_scales))
+        return from_hip(mx::launch_linear_skinny(static_cast<const uint16_t*>(x_bf16), ldx,
+                                                 b_codes, b_scales, M, N, K, y, out_bf16,
+                                                 stream));
+    // two launches through the workspace: the act-quant call, then the GEMM
+    const size_t need = linear_codes_bytes(M, K) + (size_t)M * (size_t)(K / 32);
+    if (workspace_bytes < need) return MXFP4_EINVAL;
+    if (!aligned(workspace, 16)) return MXFP4_EALIGN;
+    uint8_t* codes = static_cast<uint8_t*>(workspace);
+    uint8_t* scales = codes + linear_codes_bytes(M, K);
+    const hipError_t e = mx::launch_act_quant(static_cast<const uint16_t*>(x_bf16), ldx, nullptr,
+                                              M, K, codes, scales, stream);
+    if (e != hipSuccess) return MXFP4_EHIP;
+    return from_hip(mx::launch_gemm(codes, scales, b_codes, b_scales, M, N, K, y, out_bf16,
+                                    stream));
 }
 
 int mxfp4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
