@@ -66,14 +66,22 @@ def _load():
     lib.orc_e2m1_encode.argtypes = [ctypes.c_double]
     lib.orc_shared_exponent.restype = ctypes.c_uint
     lib.orc_shared_exponent.argtypes = [ctypes.c_double]
+    lib.orc_shared_exponent_uos.restype = ctypes.c_uint
+    lib.orc_shared_exponent_uos.argtypes = [ctypes.c_double]
     lib.orc_mx_quantize_block.restype = None
     lib.orc_mx_quantize_block.argtypes = [P, P, P]
+    lib.orc_mx_quantize_block_rule.restype = None
+    lib.orc_mx_quantize_block_rule.argtypes = [P, P, P, ctypes.c_int]
     lib.orc_nvfp4_dequant.restype = None
     lib.orc_nvfp4_dequant.argtypes = [P, P, ctypes.c_float, I, I, ctypes.c_int, P]
     lib.orc_requant.restype = None
     lib.orc_requant.argtypes = [P, P, P, I, I, I, ctypes.c_int, P, P]
+    lib.orc_requant_rule.restype = None
+    lib.orc_requant_rule.argtypes = [P, P, P, I, I, I, ctypes.c_int, ctypes.c_int, P, P]
     lib.orc_quantize_act.restype = None
     lib.orc_quantize_act.argtypes = [P, I, P, I, I, P, P]
+    lib.orc_quantize_act_rule.restype = None
+    lib.orc_quantize_act_rule.argtypes = [P, I, P, I, I, ctypes.c_int, P, P]
     lib.orc_gemm.restype = None
     lib.orc_gemm.argtypes = [P, P, P, P, I, I, I, P, P]
     lib.orc_gemm_at.restype = None
@@ -132,16 +140,23 @@ def e2m1_encode(q: float) -> int:
     return int(_load().orc_e2m1_encode(float(q)))
 
 
-def shared_exponent(amax: float) -> int:
-    return int(_load().orc_shared_exponent(float(amax)))
+# Scale rules: "ocp" (R3, the OCP MX shared exponent) and "uos" (R9, the
+# Qmax = 7.25 rule of the vLLM-Omni guide's single-scale setting 2).
+_RULES = {"ocp": 0, "uos": 1}
 
 
-def mx_quantize_block(v) -> tuple[np.ndarray, int]:
+def shared_exponent(amax: float, rule: str = "ocp") -> int:
+    fn = _load().orc_shared_exponent_uos if rule == "uos" else _load().orc_shared_exponent
+    assert rule in _RULES
+    return int(fn(float(amax)))
+
+
+def mx_quantize_block(v, rule: str = "ocp") -> tuple[np.ndarray, int]:
     v = _c(v, np.float64)
     assert v.shape == (32,)
     codes = np.empty(16, dtype=np.uint8)
     scale = np.empty(1, dtype=np.uint8)
-    _load().orc_mx_quantize_block(_ptr(v), _ptr(codes), _ptr(scale))
+    _load().orc_mx_quantize_block_rule(_ptr(v), _ptr(codes), _ptr(scale), _RULES[rule])
     return codes, int(scale[0])
 
 
@@ -157,7 +172,7 @@ def nvfp4_dequant(codes, scales, g, bf16_intermediate=False) -> np.ndarray:
     return out
 
 
-def requant(nv_codes, nv_scales, nv_global, bf16_intermediate=False):
+def requant(nv_codes, nv_scales, nv_global, bf16_intermediate=False, scale_rule="ocp"):
     """NVFP4 [T,N,K/2] + [T,N,K/16] + g[T] -> MXFP4 codes [T,N,K/2], E8M0 [T,N,K/32]."""
     nv_codes = _c(nv_codes, np.uint8)
     nv_scales = _c(nv_scales, np.uint8)
@@ -171,14 +186,15 @@ def requant(nv_codes, nv_scales, nv_global, bf16_intermediate=False):
     assert K % 32 == 0 and nv_scales.shape == (T, N, K // 16) and g.shape == (T,)
     codes = np.empty((T, N, K // 2), dtype=np.uint8)
     scales = np.empty((T, N, K // 32), dtype=np.uint8)
-    _load().orc_requant(_ptr(nv_codes), _ptr(nv_scales), _ptr(g), T, N, K,
-                        int(bool(bf16_intermediate)), _ptr(codes), _ptr(scales))
+    _load().orc_requant_rule(_ptr(nv_codes), _ptr(nv_scales), _ptr(g), T, N, K,
+                             int(bool(bf16_intermediate)), _RULES[scale_rule],
+                             _ptr(codes), _ptr(scales))
     if squeeze:
         return codes[0], scales[0]
     return codes, scales
 
 
-def quantize_act(x_bits, K=None, row_index=None):
+def quantize_act(x_bits, K=None, row_index=None, scale_rule="ocp"):
     """bf16 bit patterns (uint16) [R, ldx] -> codes [M, K/2], E8M0 [M, K/32]."""
     x_bits = _c(x_bits, np.uint16)
     R, ldx = x_bits.shape
@@ -193,8 +209,8 @@ def quantize_act(x_bits, K=None, row_index=None):
     codes = np.empty((M, K // 2), dtype=np.uint8)
     scales = np.empty((M, K // 32), dtype=np.uint8)
     if M:
-        _load().orc_quantize_act(_ptr(x_bits), ldx, _ptr(row_index), M, K,
-                                 _ptr(codes), _ptr(scales))
+        _load().orc_quantize_act_rule(_ptr(x_bits), ldx, _ptr(row_index), M, K,
+                                      _RULES[scale_rule], _ptr(codes), _ptr(scales))
     return codes, scales
 
 

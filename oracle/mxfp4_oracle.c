@@ -151,8 +151,37 @@ unsigned orc_shared_exponent(double amax)
     return (unsigned)(e + 127);
 }
 
+/* R9: the smallest e with amax <= 7.25 * 2^e, found by counting up from an
+   e that is certainly too small (7.25 * 2^(x-5) < 2^(x-1) <= amax); 7.25 * 2^e
+   and the comparison are exact in fp64. */
+unsigned orc_shared_exponent_uos(double amax)
+{
+    if (isnan(amax) || isinf(amax))
+        return 0xFFu;
+    int e;
+    if (amax == 0.0) {
+        e = -127;
+    } else {
+        int x;
+        frexp(amax, &x);
+        e = (x - 1) - 4;
+        while (amax > 7.25 * ldexp(1.0, e))
+            ++e;
+    }
+    if (e < -127) e = -127;
+    if (e > 127) e = 127;
+    return (unsigned)(e + 127);
+}
+
 /* R3 + R4 on one block of 32 values, packed per R1. */
 void orc_mx_quantize_block(const double v[32], uint8_t codes[16], uint8_t* scale)
+{
+    orc_mx_quantize_block_rule(v, codes, scale, ORC_RULE_OCP);
+}
+
+/* R3 (or R9) + R4 on one block of 32 values, packed per R1. */
+void orc_mx_quantize_block_rule(const double v[32], uint8_t codes[16], uint8_t* scale,
+                                int rule)
 {
     double amax = 0.0;
     int bad = 0;
@@ -162,7 +191,9 @@ void orc_mx_quantize_block(const double v[32], uint8_t codes[16], uint8_t* scale
         else if (fabs(v[i]) > amax)
             amax = fabs(v[i]);
     }
-    unsigned b = bad ? 0xFFu : orc_shared_exponent(amax);
+    unsigned b = bad ? 0xFFu
+                     : (rule == ORC_RULE_UOS ? orc_shared_exponent_uos(amax)
+                                             : orc_shared_exponent(amax));
     *scale = (uint8_t)b;
     if (b == 0xFFu) {
         memset(codes, 0, 16);
@@ -226,6 +257,15 @@ void orc_requant(const uint8_t* nv_codes, const uint8_t* nv_scales,
                  const float* nv_global, int64_t T, int64_t N, int64_t K,
                  int bf16_intermediate, uint8_t* mx_codes, uint8_t* mx_scales)
 {
+    orc_requant_rule(nv_codes, nv_scales, nv_global, T, N, K, bf16_intermediate,
+                     ORC_RULE_OCP, mx_codes, mx_scales);
+}
+
+void orc_requant_rule(const uint8_t* nv_codes, const uint8_t* nv_scales,
+                      const float* nv_global, int64_t T, int64_t N, int64_t K,
+                      int bf16_intermediate, int rule, uint8_t* mx_codes,
+                      uint8_t* mx_scales)
+{
     for (int64_t t = 0; t < T; ++t) {
 #pragma omp parallel
         {
@@ -239,8 +279,8 @@ void orc_requant(const uint8_t* nv_codes, const uint8_t* nv_scales,
                 for (int64_t j = 0; j < K / 32; ++j) {
                     for (int i = 0; i < 32; ++i)
                         blk[i] = (double)row[32 * j + i];
-                    orc_mx_quantize_block(blk, mx_codes + r * (K / 2) + 16 * j,
-                                          mx_scales + r * (K / 32) + j);
+                    orc_mx_quantize_block_rule(blk, mx_codes + r * (K / 2) + 16 * j,
+                                               mx_scales + r * (K / 32) + j, rule);
                 }
             }
             free(row);
@@ -253,6 +293,13 @@ void orc_requant(const uint8_t* nv_codes, const uint8_t* nv_scales,
 void orc_quantize_act(const uint16_t* x, int64_t ldx, const int32_t* row_index,
                       int64_t M, int64_t K, uint8_t* codes, uint8_t* scales)
 {
+    orc_quantize_act_rule(x, ldx, row_index, M, K, ORC_RULE_OCP, codes, scales);
+}
+
+void orc_quantize_act_rule(const uint16_t* x, int64_t ldx, const int32_t* row_index,
+                           int64_t M, int64_t K, int rule, uint8_t* codes,
+                           uint8_t* scales)
+{
 #pragma omp parallel for schedule(static)
     for (int64_t m = 0; m < M; ++m) {
         int64_t src = row_index ? (int64_t)row_index[m] : m;
@@ -261,8 +308,8 @@ void orc_quantize_act(const uint16_t* x, int64_t ldx, const int32_t* row_index,
         for (int64_t j = 0; j < K / 32; ++j) {
             for (int i = 0; i < 32; ++i)
                 blk[i] = orc_bf16_value(xr[32 * j + i]);
-            orc_mx_quantize_block(blk, codes + m * (K / 2) + 16 * j,
-                                  scales + m * (K / 32) + j);
+            orc_mx_quantize_block_rule(blk, codes + m * (K / 2) + 16 * j,
+                                       scales + m * (K / 32) + j, rule);
         }
     }
 }

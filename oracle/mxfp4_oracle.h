@@ -38,6 +38,10 @@
  *      +-6, sign bit copied from the input (so -0.1 * 2^e encodes as 0x8).
  *   R5 GEMM output: fp64 sum of exact products, rounded once (RNE) to the
  *      output type.
+ *   R9 shared exponent, UOS variant (vLLM-Omni guide, "Single-Scale Block
+ *      Scaling", setting 2, Qmax = 7.25): e = ceil(log2(amax / 7.25)), i.e.
+ *      the smallest e with amax <= 7.25 * 2^e, clamped to [-127, 127];
+ *      elements are encoded as in R4 (still saturating at 6).
  */
 #ifndef MXFP4_ORACLE_H
 #define MXFP4_ORACLE_H
@@ -57,9 +61,15 @@ uint16_t orc_bf16_from_double(double v);         /* RNE, NaN -> 0x7FC0      */
 uint16_t orc_bf16_from_float(float v);           /* RNE, NaN -> 0x7FC0      */
 unsigned orc_e2m1_encode(double q);              /* R4                      */
 unsigned orc_shared_exponent(double amax);       /* R3, amax >= 0 or NaN    */
+unsigned orc_shared_exponent_uos(double amax);   /* R9, amax >= 0 or NaN    */
+
+/* Scale rule of the _rule variants below: R3 (OCP MX) or R9 (UOS). */
+enum { ORC_RULE_OCP = 0, ORC_RULE_UOS = 1 };
 
 /* ---- MX quantization of one 32-element block (R3 + R4) ---------------- */
 void orc_mx_quantize_block(const double v[32], uint8_t codes[16], uint8_t* scale);
+void orc_mx_quantize_block_rule(const double v[32], uint8_t codes[16], uint8_t* scale,
+                                int rule);
 
 /* ---- NVFP4 dequantization of one tensor into fp32 (R2) ---------------- */
 void orc_nvfp4_dequant(const uint8_t* codes, const uint8_t* scales, float g,
@@ -70,10 +80,17 @@ void orc_nvfp4_dequant(const uint8_t* codes, const uint8_t* scales, float g,
 void orc_requant(const uint8_t* nv_codes, const uint8_t* nv_scales,
                  const float* nv_global, int64_t T, int64_t N, int64_t K,
                  int bf16_intermediate, uint8_t* mx_codes, uint8_t* mx_scales);
+void orc_requant_rule(const uint8_t* nv_codes, const uint8_t* nv_scales,
+                      const float* nv_global, int64_t T, int64_t N, int64_t K,
+                      int bf16_intermediate, int rule, uint8_t* mx_codes,
+                      uint8_t* mx_scales);
 
 /* bf16 [*, ldx] -> MXFP4 codes [M][K/2] + E8M0 [M][K/32]; optional gather. */
 void orc_quantize_act(const uint16_t* x, int64_t ldx, const int32_t* row_index,
                       int64_t M, int64_t K, uint8_t* codes, uint8_t* scales);
+void orc_quantize_act_rule(const uint16_t* x, int64_t ldx, const int32_t* row_index,
+                           int64_t M, int64_t K, int rule, uint8_t* codes,
+                           uint8_t* scales);
 
 /* y[m][n] = sum_k A[m,k] * B[n,k] over dequantized MXFP4 (fp64), and
    s[m][n] = sum_k |A[m,k] * B[n,k]|.  Either output may be NULL. */

@@ -152,6 +152,89 @@ def test_shared_exponent_fp32_sweep_and_specials():
 
 
 # ---- hand-worked block fixtures -------------------------------------------------
+def uos_exponent_by_fraction(a: float) -> int:
+    """UOS exponent from the binary fraction of a (a > 0, finite): with
+    a = f * 2^p, f in [1, 2), a / 2^(p-2) = 4f lies in [4, 8) and is at most
+    7.25 exactly when f <= 1.8125; otherwise one exponent more is needed."""
+    m, x = math.frexp(a)          # a = m * 2^x, m in [0.5, 1)
+    f, p = 2.0 * m, x - 1
+    e = p - 2 + (1 if f > 1.8125 else 0)
+    return min(max(e, -127), 127) + 127
+
+
+def test_uos_exponent_boundaries():
+    """Setting 2 of the vLLM-Omni guide (Single-Scale Block Scaling): the
+    exponent is the smallest e with amax <= 7.25 * 2^e; elements still
+    saturate at 6."""
+    for k in range(-120, 121, 7):
+        b = 7.25 * 2.0 ** k
+        assert oracle.shared_exponent(b, "uos") == k + 127
+        assert oracle.shared_exponent(np.nextafter(b, np.inf), "uos") == k + 128
+        assert oracle.shared_exponent(3.625 * 2.0 ** k, "uos") == k + 126
+        assert oracle.shared_exponent(np.nextafter(3.625 * 2.0 ** k, np.inf), "uos") == k + 127
+    assert oracle.shared_exponent(0.0, "uos") == 0
+    assert oracle.shared_exponent(float("nan"), "uos") == 0xFF
+    assert oracle.shared_exponent(float("inf"), "uos") == 0xFF
+    assert oracle.shared_exponent(3.0e38, "uos") == 125 + 127    # 7.25 * 2^124 < 3e38 <= 7.25 * 2^125
+    assert oracle.shared_exponent(1e-44, "uos") == 0             # clamped
+
+
+def test_uos_exponent_matches_fraction_rule_and_ocp():
+    """Random magnitudes over the whole fp32 range, subnormals included: the
+    oracle's search agrees with the fraction rule.  Against the OCP exponent
+    it is the same or one more, one more exactly when the fraction exceeds
+    1.8125 (unless the lower clamp holds both at 0)."""
+    rng = np.random.default_rng(7)
+    bits = rng.integers(1, 0x7F800000, size=20000, dtype=np.int64).astype(np.uint32)
+    vals = bits.view(np.float32).astype(np.float64)
+    for a in vals:
+        u = oracle.shared_exponent(a, "uos")
+        o = oracle.shared_exponent(a)
+        assert u == uos_exponent_by_fraction(a), a
+        f = 2.0 * math.frexp(a)[0]
+        assert u - o in (0, 1), a
+        if o > 0:
+            assert (u - o == 1) == (f > 1.8125), a
+
+
+def test_uos_block_worked_example():
+    """A block with amax 7.5: OCP picks 2^0 (7.5 saturates to 6); UOS picks 2^1,
+    so 7.5 -> 3.75 -> 4 (code 6), -7.5 -> code 14, 1.0 -> 0.5 (code 1),
+    0.375 -> 0.1875 -> 0 (code 0), 3.0 -> 1.5 (code 3); the rest 0."""
+    v = np.zeros(32)
+    v[:5] = [7.5, -7.5, 1.0, 0.375, 3.0]
+    codes, s = oracle.mx_quantize_block(v, "uos")
+    assert s == 128
+    nib = [(codes[i // 2] >> (4 * (i % 2))) & 15 for i in range(32)]
+    assert nib[:5] == [6, 14, 1, 0, 3] and all(n == 0 for n in nib[5:])
+    codes_o, s_o = oracle.mx_quantize_block(v)
+    nib_o = [(codes_o[i // 2] >> (4 * (i % 2))) & 15 for i in range(32)]
+    assert s_o == 127 and nib_o[:5] == [7, 15, 2, 1, 5]     # 6, -6, 1, 0.5 (0.375 rounds up), 3
+
+
+def test_uos_act_quant_and_requant_use_the_rule():
+    """The row operations under "uos" equal per-block quantization under the
+    same rule (act-quant of bf16 rows; requant of the NVFP4 values)."""
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((3, 128)) * np.array([1e-3, 1.0, 40.0])[:, None]
+    bits = oracle.bf16_from_double_array(x.ravel()).reshape(3, 128)
+    c, s = oracle.quantize_act(bits, scale_rule="uos")
+    for r in range(3):
+        for j in range(4):
+            vals = np.array([oracle.bf16_value(int(b)) for b in bits[r, 32 * j:32 * j + 32]])
+            cb, sb = oracle.mx_quantize_block(vals, "uos")
+            assert sb == s[r, j] and np.array_equal(cb, c[r, 16 * j:16 * j + 16])
+    codes = rng.integers(0, 256, size=(8, 64), dtype=np.uint8)
+    scales = rng.integers(0x20, 0x60, size=(8, 8), dtype=np.uint8)
+    g = np.float32(0.0123)
+    mc, ms = oracle.requant(codes, scales, g, scale_rule="uos")
+    deq = oracle.nvfp4_dequant(codes, scales, g)
+    for r in range(8):
+        for j in range(4):
+            cb, sb = oracle.mx_quantize_block(deq[r, 32 * j:32 * j + 32].astype(np.float64), "uos")
+            assert sb == ms[r, j] and np.array_equal(cb, mc[r, 16 * j:16 * j + 16])
+
+
 @pytest.mark.parametrize("row", read_table("mx_block_examples.txt"), ids=lambda r: r[0])
 def test_mx_block_examples(row):
     name, inputs, byte, codes = row
