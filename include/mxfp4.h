@@ -54,6 +54,19 @@ enum { MXFP4_OUT_BF16 = 0, MXFP4_OUT_FP32 = 1 };        /* out_dtype            
 enum { MXFP4_REQ_INTERMEDIATE_BF16 = 1u << 0 };         /* requant flags        */
 
 /*
+ * Scale-rule flag of every quantizing call (requant, act-quant, linear): the
+ * UOS shared exponent of the vLLM-Omni guide, "Single-Scale Block Scaling",
+ * setting 2 (Qmax = 7.25) in place of the OCP rule: the scale byte is
+ * e + 127 for the smallest e with amax <= 7.25 * 2^e, clamped to [0, 254]
+ * (the OCP byte, plus one when amax's binary fraction exceeds 1.8125).  The
+ * largest scaled magnitude of a block is then at most 7.25 (below 8 under
+ * OCP), so less of it saturates at 6; the codes' rounding and the NaN/Inf
+ * rule are unchanged.  Both rules give ordinary MXFP4 data: the GEMMs take
+ * no flag.
+ */
+enum { MXFP4_SCALE_UOS = 1u << 1 };
+
+/*
  * NVFP4 -> MXFP4 requant of T same-shape weight tensors, the load-time step
  * of the AMD blog's pipeline section (Figure 1): dequantize, quantize to
  * MXFP4, write into a preallocated destination.  Per element the NVFP4 value
@@ -72,7 +85,7 @@ enum { MXFP4_REQ_INTERMEDIATE_BF16 = 1u << 0 };         /* requant flags        
  *              (a checkpoint that stores a divisor passes its reciprocal)
  *   mx_codes   [T][N][K/2]  u8, device, written     (16-byte aligned)
  *   mx_scales  [T][N][K/32] u8 (E8M0 bits), device, written
- *   flags      0 or MXFP4_REQ_INTERMEDIATE_BF16
+ *   flags      0, or MXFP4_REQ_INTERMEDIATE_BF16 and/or MXFP4_SCALE_UOS
  * Tensors a loader keeps in high precision are simply not passed (the blog's
  * note on producer excludes).  Source and destination must not overlap.
  */
@@ -111,7 +124,7 @@ int mxfp4_requant_from_nvfp4_subset(const uint8_t* nv_codes, const uint8_t* nv_s
  *              existing row of x (not checked: reading it would need a sync).
  *   codes      [M][K/2] u8, device, written   (16-byte aligned)
  *   scales     [M][K/32] u8, device, written
- *   flags      must be 0
+ *   flags      0 or MXFP4_SCALE_UOS
  */
 int mxfp4_quantize_act(const void* x_bf16, int64_t ldx, const int32_t* row_index,
                        int64_t M, int64_t K, uint8_t* codes, uint8_t* scales,
@@ -177,7 +190,7 @@ size_t mxfp4_gemm_workspace_size(int64_t M, int64_t N, int64_t K);
  *   workspace   device memory of at least mxfp4_linear_workspace_size(M, N,
  *               K) bytes (16-byte aligned; may be NULL when that is 0):
  *               the quantized activations of the two-launch form
- *   flags       0
+ *   flags       0 or MXFP4_SCALE_UOS (the activations' scale rule)
  * Errors as for mxfp4_gemm; MXFP4_EINVAL also for a workspace smaller than
  * the two-launch form needs when that form is taken.
  */

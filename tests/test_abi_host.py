@@ -89,6 +89,8 @@ def test_quantize_act_argument_checks(lib):
     assert f(FAKE, 32, None, 4, 64, FAKE, FAKE, 0, None) == -1           # ldx < K
     assert f(FAKE, 64, None, 4, 48, FAKE, FAKE, 0, None) == -1           # K % 32
     assert f(FAKE, 64, None, 4, 64, FAKE, FAKE, 1, None) == -1           # flags
+    assert f(FAKE, 64, None, 4, 64, FAKE, FAKE, 4, None) == -1
+    assert f(FAKE, 64, None, 0, 64, FAKE, FAKE, 2, None) == 0            # UOS accepted
     assert f(FAKE, 68, None, 4, 64, FAKE, FAKE, 0, None) == -2           # ldx % 8
     assert f(ODD, 64, None, 4, 64, FAKE, FAKE, 0, None) == -2            # x alignment
     assert f(FAKE, 64, ODD, 4, 64, FAKE, FAKE, 0, None) == -2            # row_index
@@ -99,7 +101,10 @@ def test_quantize_act_argument_checks(lib):
 def test_requant_argument_checks(lib):
     f = lib.mxfp4_requant_from_nvfp4
     assert f(FAKE, FAKE, FAKE, 1, 16, 48, FAKE, FAKE, 0, None) == -1     # K % 32
-    assert f(FAKE, FAKE, FAKE, 1, 16, 64, FAKE, FAKE, 2, None) == -1     # flags
+    assert f(FAKE, FAKE, FAKE, 1, 16, 64, FAKE, FAKE, 4, None) == -1     # flags
+    # the two known flags pass the flag check and reach the next one
+    assert f(None, FAKE, FAKE, 1, 16, 64, FAKE, FAKE, 3, None) == -1     # null source
+    assert f(FAKE, FAKE, FAKE, 0, 16, 64, FAKE, FAKE, 3, None) == 0      # T == 0
     assert f(FAKE, FAKE, FAKE, 1, 0, 64, FAKE, FAKE, 0, None) == -1      # N
     assert f(None, FAKE, FAKE, 1, 16, 64, FAKE, FAKE, 0, None) == -1
     assert f(ODD, FAKE, FAKE, 1, 16, 64, FAKE, FAKE, 0, None) == -2
@@ -120,7 +125,8 @@ def test_requant_subset_argument_checks(lib):
     assert f(FAKE, FAKE, FAKE, 6, 16, 64, None, 3, FAKE, FAKE, 0, None) == -1
     assert f(FAKE, FAKE, FAKE, 6, 16, 64, P(ok), -1, FAKE, FAKE, 0, None) == -1
     assert f(FAKE, FAKE, FAKE, 6, 16, 48, P(ok), 3, FAKE, FAKE, 0, None) == -1      # K % 32
-    assert f(FAKE, FAKE, FAKE, 6, 16, 64, P(ok), 3, FAKE, FAKE, 2, None) == -1      # flags
+    assert f(FAKE, FAKE, FAKE, 6, 16, 64, P(ok), 3, FAKE, FAKE, 4, None) == -1      # flags
+    assert f(FAKE, FAKE, FAKE, 6, 16, 64, P(ok), 0, FAKE, FAKE, 3, None) == 0       # both flags
     assert f(ODD, FAKE, FAKE, 6, 16, 64, P(ok), 3, FAKE, FAKE, 0, None) == -2
     assert f(FAKE, FAKE, FAKE, 6, 16, 64, P(ok), 0, FAKE, FAKE, 0, None) == 0       # empty list
 
@@ -133,6 +139,7 @@ def test_linear_argument_checks(lib):
     assert f(FAKE, 4096, 1, 0, 4096, FAKE, FAKE, FAKE, 0, None, 0, 0, None) == -1      # N
     assert f(FAKE, 4096, 1, 256, 4096, FAKE, FAKE, FAKE, 7, None, 0, 0, None) == -1    # out_dtype
     assert f(FAKE, 4096, 1, 256, 4096, FAKE, FAKE, FAKE, 0, None, 0, 1, None) == -1    # flags
+    assert f(FAKE, 4096, 0, 256, 4096, FAKE, FAKE, FAKE, 0, None, 0, 2, None) == 0     # UOS
     assert f(FAKE, 4096, 1, 256, 4096, FAKE, FAKE, FAKE, 0, None, 64, 0, None) == -1   # ws NULL
     assert f(None, 4096, 1, 256, 4096, FAKE, FAKE, FAKE, 0, None, 0, 0, None) == -1
     assert f(ODD, 4096, 1, 256, 4096, FAKE, FAKE, FAKE, 0, None, 0, 0, None) == -2

@@ -445,3 +445,44 @@ def test_linear_bf16_against_oracle(mx):
     y, s = oracle.gemm(ac, as_, oc, os_)
     assert_gemm_fp32(y32, y, s, "linear fp32")
     assert_gemm_bf16(yb, y, "linear bf16")
+
+
+@pytest.mark.parametrize("M,N,K,ldx", [(1, 1000, 4096, 4096), (5, 300, 2048, 2048),
+                                       (16, 2048, 4096, 4104), (17, 257, 4096, 4104),
+                                       (200, 300, 1024, 1032)])
+def test_linear_bf16_uos_matches_act_quant_then_gemm(mx, M, N, K, ldx):
+    """The UOS activation rule through mxfp4_linear_bf16 (one launch and two)
+    equals the UOS act-quant call followed by the GEMM, bit for bit."""
+    say(f"linear bf16 uos M={M} N={N} K={K} ldx={ldx}")
+    x = synth.activations(M, ldx, seed=M + 3 * N, outlier_seed=K + 1).to(dev())
+    w = synth.bf16_normal((N, K), 0.02, seed=N + 1)
+    codes, scales, g = synth.nvfp4_from_bf16(w)
+    wc, ws = mx.mxfp4_requant_from_nvfp4(codes.to(dev()), scales.to(dev()), g.reshape(1).to(dev()),
+                                         scale_rule="uos")
+    xc, xs = mx.mxfp4_quantize_act(x, K=K, scale_rule="uos")
+    _, xs_ocp = mx.mxfp4_quantize_act(x, K=K)
+    assert not torch.equal(xs, xs_ocp), "the input does not tell the rules apart"
+    for dt in (torch.bfloat16, torch.float32):
+        ref = mx.mxfp4_gemm(xc, xs, wc, ws, out_dtype=dt)
+        gy = Guarded((M, N), dt)
+        mx.mxfp4_linear_bf16(x, wc, ws, gy.view, K=K, scale_rule="uos")
+        torch.cuda.synchronize()
+        assert gy.intact(), "write outside y"
+        assert same_bits(gy.view, ref), dt
+
+
+def test_linear_bf16_uos_against_oracle(mx):
+    """The one-launch form under UOS against the oracle (both operands under
+    the UOS rule)."""
+    M, N, K = 8, 2048, 4096
+    say(f"linear bf16 uos vs oracle M={M} N={N} K={K}")
+    x = synth.activations(M, K, seed=94, outlier_seed=95)
+    w = synth.bf16_normal((N, K), 0.02, seed=96)
+    codes, scales, g = synth.nvfp4_from_bf16(w)
+    oc, os_ = oracle.requant(u8(codes), u8(scales), np.atleast_1d(g.numpy()), scale_rule="uos")
+    wc, ws = mx.mxfp4_requant_from_nvfp4(codes.to(dev()), scales.to(dev()), g.reshape(1).to(dev()),
+                                         scale_rule="uos")
+    y32 = mx.mxfp4_linear_bf16(x.to(dev()), wc, ws, out_dtype=torch.float32, scale_rule="uos")
+    ac, as_ = oracle.quantize_act(bf16_bits(x), scale_rule="uos")
+    y, s = oracle.gemm(ac, as_, oc, os_)
+    assert_gemm_fp32(y32, y, s, "linear uos fp32")

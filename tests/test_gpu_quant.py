@@ -19,7 +19,7 @@ def mx():
     return m
 
 
-def act_quant_both(mx, x_cpu, row_index=None, K=None):
+def act_quant_both(mx, x_cpu, row_index=None, K=None, scale_rule="ocp"):
     """GPU and oracle act-quant of the same bf16 input; canary-guarded outputs."""
     xg = x_cpu.to(dev())
     M = x_cpu.shape[0] if row_index is None else row_index.shape[0]
@@ -27,10 +27,11 @@ def act_quant_both(mx, x_cpu, row_index=None, K=None):
     gc = Guarded((M, K // 2), torch.uint8)
     gs = Guarded((M, K // 32), torch.uint8)
     ri = None if row_index is None else torch.from_numpy(row_index).to(dev())
-    mx.mxfp4_quantize_act(xg, gc.view, gs.view, row_index=ri, K=K)
+    mx.mxfp4_quantize_act(xg, gc.view, gs.view, row_index=ri, K=K, scale_rule=scale_rule)
     torch.cuda.synchronize()
     assert gc.intact() and gs.intact(), "write outside the output"
-    oc, os_ = oracle.quantize_act(bf16_bits(x_cpu), K=K, row_index=row_index)
+    oc, os_ = oracle.quantize_act(bf16_bits(x_cpu), K=K, row_index=row_index,
+                                  scale_rule=scale_rule)
     return (u8(gc.view), u8(gs.view)), (oc, os_)
 
 
@@ -72,8 +73,7 @@ def test_act_quant_gather_and_wide_rows(mx):
     assert_same(g, o, "ldx>K")
 
 
-def test_act_quant_special_values(mx):
-    say("act_quant NaN/Inf/subnormal/ties")
+def special_values_input():
     rng = np.random.default_rng(1)
     K = 256
     bits = (rng.integers(0, 2 ** 16, size=(64, K), dtype=np.uint32)).astype(np.uint16)
@@ -89,8 +89,12 @@ def test_act_quant_special_values(mx):
         v[::32] = 4.0 * np.float32(2.0 ** rng.integers(-20, 20))
         v *= rng.choice(np.array([-1, 1], dtype=np.float32), size=K)
         bits[r] = (v.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
-    x = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16)
-    g, o = act_quant_both(mx, x)
+    return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16)
+
+
+def test_act_quant_special_values(mx):
+    say("act_quant NaN/Inf/subnormal/ties")
+    g, o = act_quant_both(mx, special_values_input())
     assert_same(g, o, "specials")
 
 
@@ -142,7 +146,7 @@ def test_act_quant_deterministic(mx):
 
 
 # ---- NVFP4 -> MXFP4 requant ------------------------------------------------------
-def requant_both(mx, codes, scales, g, bf16_intermediate=False):
+def requant_both(mx, codes, scales, g, bf16_intermediate=False, scale_rule="ocp"):
     T = 1 if codes.dim() == 2 else codes.shape[0]
     N, K = codes.shape[-2], codes.shape[-1] * 2
     shape_c = (T, N, K // 2) if codes.dim() == 3 else (N, K // 2)
@@ -151,11 +155,12 @@ def requant_both(mx, codes, scales, g, bf16_intermediate=False):
     gs = Guarded(shape_s, torch.uint8)
     mx.mxfp4_requant_from_nvfp4(codes.to(dev()), scales.to(dev()),
                                 g.reshape(-1).to(torch.float32).to(dev()),
-                                gc.view, gs.view, bf16_intermediate=bf16_intermediate)
+                                gc.view, gs.view, bf16_intermediate=bf16_intermediate,
+                                scale_rule=scale_rule)
     torch.cuda.synchronize()
     assert gc.intact() and gs.intact(), "write outside the destination"
     oc, os_ = oracle.requant(u8(codes), u8(scales), g.reshape(-1).numpy().astype(np.float32),
-                             bf16_intermediate=bf16_intermediate)
+                             bf16_intermediate=bf16_intermediate, scale_rule=scale_rule)
     return (u8(gc.view), u8(gs.view)), (oc.reshape(shape_c), os_.reshape(shape_s))
 
 
@@ -168,31 +173,33 @@ def test_requant_tiny(mx, bf16_intermediate):
     assert_same(gpu, ref, "tiny requant")
 
 
+@pytest.mark.parametrize("scale_rule", ["ocp", "uos"])
 @pytest.mark.parametrize("bf16_intermediate", [False, True])
-def test_requant_random_bytes_many_globals(mx, bf16_intermediate):
+def test_requant_random_bytes_many_globals(mx, bf16_intermediate, scale_rule):
     """Arbitrary NVFP4 bytes (every E4M3 byte incl. NaN and subnormals) under
     global scales from 2^-140 to 2^120, so fp32 denormals, overflow to Inf and
     NaN blocks all occur; ragged K (17 MX blocks)."""
-    say(f"requant random bytes T=12 N=37 K=544 bf16={bf16_intermediate}")
+    say(f"requant random bytes T=12 N=37 K=544 bf16={bf16_intermediate} {scale_rule}")
     rng = np.random.default_rng(3)
     T, N, K = 12, 37, 544
     codes = torch.from_numpy(rng.integers(0, 256, size=(T, N, K // 2), dtype=np.uint8))
     scales = torch.from_numpy(rng.integers(0, 256, size=(T, N, K // 16), dtype=np.uint8))
     g = torch.tensor([2.0 ** e for e in (-140, -130, -126, -120, -60, -20, -7, 0, 3, 30, 100,
                                          120)], dtype=torch.float32)
-    gpu, ref = requant_both(mx, codes, scales, g, bf16_intermediate)
+    gpu, ref = requant_both(mx, codes, scales, g, bf16_intermediate, scale_rule)
     assert_same(gpu, ref, "random requant")
     g2 = torch.from_numpy(rng.uniform(1e-6, 1e-2, size=T).astype(np.float32))
-    gpu, ref = requant_both(mx, codes, scales, g2, bf16_intermediate)
+    gpu, ref = requant_both(mx, codes, scales, g2, bf16_intermediate, scale_rule)
     assert_same(gpu, ref, "random requant, non-power-of-two g")
 
 
+@pytest.mark.parametrize("scale_rule", ["ocp", "uos"])
 @pytest.mark.parametrize("bf16_intermediate", [False, True])
-def test_requant_limited_code_range(mx, bf16_intermediate):
+def test_requant_limited_code_range(mx, bf16_intermediate, scale_rule):
     """Each NVFP4 block draws its codes from magnitudes 0..c_max with c_max
     itself random (so the block's largest code varies from 0 to 6), under
     E4M3 scales and global scales of both signs, including zero."""
-    say(f"requant limited code range T=8 N=64 K=1024 bf16={bf16_intermediate}")
+    say(f"requant limited code range T=8 N=64 K=1024 bf16={bf16_intermediate} {scale_rule}")
     rng = np.random.default_rng(17)
     T, N, K = 8, 64, 1024
     cmax = rng.integers(0, 8, size=(T, N, K // 16, 1))
@@ -203,7 +210,7 @@ def test_requant_limited_code_range(mx, bf16_intermediate):
     scales = torch.from_numpy(sc.astype(np.uint8))
     g = torch.tensor([1e-3, -2.5e-4, 0.0, -0.0, 3.0e-41, -7.0, 1.0e30, 2.0 ** -149],
                      dtype=torch.float32)
-    gpu, ref = requant_both(mx, codes, scales, g, bf16_intermediate)
+    gpu, ref = requant_both(mx, codes, scales, g, bf16_intermediate, scale_rule)
     assert_same(gpu, ref, "limited code range")
 
 
@@ -264,3 +271,69 @@ def test_requant_subset(mx, T, N, K, every):
     with pytest.raises(mx.Mxfp4Error):
         mx.mxfp4_requant_from_nvfp4(codes.to(dev()), scales.to(dev()), g.reshape(-1).to(dev()),
                                     gc.view, gs.view, tensors=[1, 0])
+
+
+# ---- the UOS scale rule (Qmax = 7.25) ------------------------------------------------
+def uos_act_inputs(case):
+    if case == "outliers":
+        return synth.activations(37, 544, seed=61, outlier_seed=62)
+    if case == "specials":
+        return special_values_input()
+    if case == "exhaustive":
+        # every bf16 magnitude is some block's amax, at every exponent: every
+        # side of every 1.8125 boundary
+        bits = exhaustive_encode_input()
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16)
+    raise ValueError(case)
+
+
+@pytest.mark.parametrize("case", ["outliers", "specials", "exhaustive"])
+def test_act_quant_uos(mx, case):
+    """Act-quant under MXFP4_SCALE_UOS, bit-exact against the oracle's UOS rule;
+    the inputs are chosen so that the two rules' scale bytes differ in places."""
+    say(f"act_quant uos {case}")
+    x = uos_act_inputs(case)
+    g, o = act_quant_both(mx, x, scale_rule="uos")
+    assert_same(g, o, f"uos {case}")
+    _, ocp_scales = oracle.quantize_act(bf16_bits(x))
+    assert (ocp_scales != o[1]).any(), "the input does not tell the rules apart"
+
+
+def test_act_quant_uos_gather(mx):
+    say("act_quant uos gather, ldx > K")
+    x = synth.activations(50, 1024, seed=63, outlier_seed=64)
+    idx = np.random.default_rng(5).integers(0, 50, size=77).astype(np.int32)
+    g, o = act_quant_both(mx, x, row_index=idx, scale_rule="uos")
+    assert_same(g, o, "uos gather")
+    g, o = act_quant_both(mx, x, K=512, scale_rule="uos")
+    assert_same(g, o, "uos ldx>K")
+
+
+def test_act_quant_uos_prefill_full_size(mx):
+    """The large-output (non-temporal store) form of the kernel under UOS."""
+    say("act_quant uos prefill [4096,14336] full compare")
+    x = synth.activations(4096, 14336, seed=65, outlier_seed=66)
+    g, o = act_quant_both(mx, x, scale_rule="uos")
+    assert_same(g, o, "uos prefill")
+
+
+@pytest.mark.parametrize("bf16_intermediate", [False, True])
+def test_requant_uos_tiny_and_subset(mx, bf16_intermediate):
+    """Requant of a realistic weight under UOS, whole and as a subset call."""
+    say(f"requant uos T=6 N=256 K=1024 bf16={bf16_intermediate}")
+    w = synth.bf16_normal((6, 256, 1024), 0.02, seed=67)
+    codes, scales, g = synth.nvfp4_from_bf16(w)
+    gpu, ref = requant_both(mx, codes, scales, g, bf16_intermediate, "uos")
+    assert_same(gpu, ref, "uos requant")
+    _, ocp_scales = oracle.requant(u8(codes), u8(scales), g.reshape(-1).numpy(),
+                                   bf16_intermediate=bf16_intermediate)
+    assert (ocp_scales.reshape(ref[1].shape) != ref[1]).any()
+    sel = [0, 3, 4]
+    dc = torch.full((6, 256, 512), 0x5A, dtype=torch.uint8, device=dev())
+    ds = torch.full((6, 256, 32), 0xA5, dtype=torch.uint8, device=dev())
+    mx.mxfp4_requant_from_nvfp4(codes.to(dev()), scales.to(dev()), g.reshape(-1).to(dev()),
+                                dc, ds, bf16_intermediate=bf16_intermediate, tensors=sel,
+                                scale_rule="uos")
+    got_c, got_s = u8(dc), u8(ds)
+    assert np.array_equal(got_c[sel], ref[0][sel]) and np.array_equal(got_s[sel], ref[1][sel])
+    assert (got_c[[1, 2, 5]] == 0x5A).all() and (got_s[[1, 2, 5]] == 0xA5).all()

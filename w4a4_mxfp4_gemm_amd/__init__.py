@@ -19,6 +19,7 @@ LIBRARY_PATH = _PKG / "libmxfp4_cdna4.so"
 MXFP4_OUT_BF16 = 0
 MXFP4_OUT_FP32 = 1
 MXFP4_REQ_INTERMEDIATE_BF16 = 1
+MXFP4_SCALE_UOS = 2
 
 _STATUS_NAMES = {0: "MXFP4_OK", -1: "MXFP4_EINVAL", -2: "MXFP4_EALIGN",
                  -3: "MXFP4_EUNSUPPORTED", -4: "MXFP4_EHIP"}
@@ -114,14 +115,24 @@ def _check(fn, status):
         raise Mxfp4Error(fn, status)
 
 
+def _rule_flag(scale_rule):
+    if scale_rule == "ocp":
+        return 0
+    if scale_rule == "uos":
+        return MXFP4_SCALE_UOS
+    raise ValueError(f"scale_rule must be 'ocp' or 'uos', not {scale_rule!r}")
+
+
 # ---- the four calls ---------------------------------------------------------------
 def mxfp4_requant_from_nvfp4(nv_codes, nv_scales, nv_global, mx_codes=None, mx_scales=None,
-                             *, bf16_intermediate=False, tensors=None, stream=None):
+                             *, bf16_intermediate=False, tensors=None, scale_rule="ocp",
+                             stream=None):
     """NVFP4 ([T,]N,K/2 codes, [T,]N,K/16 E4M3 bytes, fp32 global [T]) -> MXFP4
     ([T,]N,K/2 codes, [T,]N,K/32 E8M0 bytes), written into mx_codes/mx_scales
     (allocated when None).  `tensors` (strictly increasing indices into the T
     tensors) converts only those, in one launch, leaving the other slots of
-    the destination untouched.  Returns (mx_codes, mx_scales)."""
+    the destination untouched.  scale_rule: "ocp" or "uos" (MXFP4_SCALE_UOS).
+    Returns (mx_codes, mx_scales)."""
     _need(nv_codes, "nv_codes", torch.uint8)
     dev = nv_codes.device
     _need(nv_scales, "nv_scales", torch.uint8, dev)
@@ -141,7 +152,7 @@ def mxfp4_requant_from_nvfp4(nv_codes, nv_scales, nv_global, mx_codes=None, mx_s
     _need(mx_scales, "mx_scales", torch.uint8, dev)
     if mx_codes.shape != (*lead, N, K // 2) or mx_scales.shape != (*lead, N, K // 32):
         raise ValueError("destination shapes do not match the source")
-    flags = MXFP4_REQ_INTERMEDIATE_BF16 if bf16_intermediate else 0
+    flags = (MXFP4_REQ_INTERMEDIATE_BF16 if bf16_intermediate else 0) | _rule_flag(scale_rule)
     if tensors is not None:
         sel = [int(t) for t in tensors]
         arr = (ctypes.c_int32 * max(len(sel), 1))(*sel)
@@ -156,10 +167,12 @@ def mxfp4_requant_from_nvfp4(nv_codes, nv_scales, nv_global, mx_codes=None, mx_s
     return mx_codes, mx_scales
 
 
-def mxfp4_quantize_act(x, codes=None, scales=None, *, row_index=None, K=None, stream=None):
+def mxfp4_quantize_act(x, codes=None, scales=None, *, row_index=None, K=None,
+                       scale_rule="ocp", stream=None):
     """bf16 x [R, ldx] -> MXFP4 codes [M, K/2] and E8M0 bytes [M, K/32] where
     M = R, or len(row_index) with output row i taken from x[row_index[i]].
-    K defaults to x's row length; x may have extra columns (ldx >= K)."""
+    K defaults to x's row length; x may have extra columns (ldx >= K).
+    scale_rule: "ocp" or "uos"."""
     _need(x, "x", torch.bfloat16)
     dev = x.device
     if x.dim() != 2:
@@ -180,7 +193,7 @@ def mxfp4_quantize_act(x, codes=None, scales=None, *, row_index=None, K=None, st
     if codes.shape != (M, K // 2) or scales.shape != (M, K // 32):
         raise ValueError("output shapes do not match [M, K/2] / [M, K/32]")
     _check("mxfp4_quantize_act", _lib.mxfp4_quantize_act(
-        _ptr(x), ldx, _ptr(row_index), M, K, _ptr(codes), _ptr(scales), 0,
+        _ptr(x), ldx, _ptr(row_index), M, K, _ptr(codes), _ptr(scales), _rule_flag(scale_rule),
         _stream(stream, dev)))
     return codes, scales
 
@@ -221,11 +234,12 @@ def mxfp4_linear_workspace_size(M: int, N: int, K: int) -> int:
 
 
 def mxfp4_linear_bf16(x, b_codes, b_scales, y=None, *, K=None, out_dtype=torch.bfloat16,
-                      workspace=None, stream=None):
+                      workspace=None, scale_rule="ocp", stream=None):
     """y [M, N] = MXFP4(x) [M, K] * B [N, K]^T from bf16 x [M, ldx] (the act-quant
     call followed by the GEMM, bit for bit; one launch for decode shapes).  K
     defaults to x's row length.  A workspace of mxfp4_linear_workspace_size
-    bytes is allocated when none is given and one is needed."""
+    bytes is allocated when none is given and one is needed.  scale_rule: the
+    activations' rule, "ocp" or "uos"."""
     _need(x, "x", torch.bfloat16)
     dev = x.device
     _need(b_codes, "b_codes", torch.uint8, dev)
@@ -248,7 +262,7 @@ def mxfp4_linear_bf16(x, b_codes, b_scales, y=None, *, K=None, out_dtype=torch.b
     ws_ptr, ws_bytes = (None, 0) if workspace is None else (_ptr(workspace), workspace.numel())
     _check("mxfp4_linear_bf16", _lib.mxfp4_linear_bf16(
         _ptr(x), ldx, M, N, K, _ptr(b_codes), _ptr(b_scales), _ptr(y), _out_dtype(y.dtype),
-        ws_ptr, ws_bytes, 0, _stream(stream, dev)))
+        ws_ptr, ws_bytes, _rule_flag(scale_rule), _stream(stream, dev)))
     return y
 
 
@@ -283,4 +297,5 @@ __all__ = ["mxfp4_requant_from_nvfp4", "mxfp4_quantize_act", "mxfp4_gemm",
            "mxfp4_grouped_gemm", "mxfp4_linear_bf16", "mxfp4_gemm_workspace_size",
            "mxfp4_linear_workspace_size", "mxfp4_status_string",
            "mxfp4_version", "Mxfp4Error", "LIBRARY_PATH", "EXPORTED_SYMBOLS",
-           "MXFP4_OUT_BF16", "MXFP4_OUT_FP32", "MXFP4_REQ_INTERMEDIATE_BF16"]
+           "MXFP4_OUT_BF16", "MXFP4_OUT_FP32", "MXFP4_REQ_INTERMEDIATE_BF16",
+           "MXFP4_SCALE_UOS"]

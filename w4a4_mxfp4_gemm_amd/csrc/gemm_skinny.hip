@@ -121,7 +121,7 @@ __device__ __forceinline__ void load_raw(RawX<SPW>& r, const uint16_t* x, int64_
     }
 }
 
-template <int SPW>
+template <int SPW, bool UOS>
 __device__ __forceinline__ void quant_raw(Frag<SPW>& f, const RawX<SPW>& r) {
     const int g = (threadIdx.x & 63) >> 4;
 #pragma unroll
@@ -133,7 +133,7 @@ __device__ __forceinline__ void quant_raw(Frag<SPW>& f, const RawX<SPW>& r) {
             for (int i = 0; i < 4; ++i)
                 v[4 * i] = r.v[j][q][i][0], v[4 * i + 1] = r.v[j][q][i][1],
                 v[4 * i + 2] = r.v[j][q][i][2], v[4 * i + 3] = r.v[j][q][i][3];
-            const uint32_t byte = quant_block32_bf16(v, c);
+            const uint32_t byte = quant_block32_bf16<UOS>(v, c);
             f.c[j][q] = v4u{c[0], c[1], c[2], c[3]};
             f.s[j][q] = byte << (8 * g);
         }
@@ -141,8 +141,9 @@ __device__ __forceinline__ void quant_raw(Frag<SPW>& f, const RawX<SPW>& r) {
 }
 
 // BF16A: x is bf16 [M][ldx] (xs unused) and each wave quantizes its share of
-// the activations itself while its weight loads stream.
-template <int MT, int SPW, int NW, int TPW, bool OUT_BF16, bool BF16A>
+// the activations itself while its weight loads stream (UOS: by the Qmax =
+// 7.25 exponent rule).
+template <int MT, int SPW, int NW, int TPW, bool OUT_BF16, bool BF16A, bool UOS = false>
 __global__ __launch_bounds__(64 * NW, 1) void gemm_skinny_kernel(
     // no __restrict__ on the operands: with it the compiler may move their loads
     // across the points that order them (below the first MFMA, or the bf16
@@ -189,7 +190,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_skinny_kernel(
     if constexpr (BF16A) {
         asm volatile("" ::: "memory");   // ... and every weight load before the quantization
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) quant_raw<SPW>(a[mt], xr[mt]);
+        for (int mt = 0; mt < MT; ++mt) quant_raw<SPW, UOS>(a[mt], xr[mt]);
     }
 
     const uint32_t sh = 8u * (uint32_t)g;
@@ -295,7 +296,7 @@ bool linear_skinny_supported(int64_t M, int64_t N, int64_t K, const void* x, int
 template <int MT, int SPW, int NW>
 static hipError_t launch_mt(const uint8_t* a, const uint8_t* as, int64_t ldx, const uint8_t* b,
                             const uint8_t* bs, int64_t M, int64_t N, int64_t K, void* y,
-                            bool out_bf16, hipStream_t stream) {
+                            bool out_bf16, hipStream_t stream, bool uos = false) {
     // tiles in flight per wave: all of a workgroup's tiles when they fit
     constexpr int TPW = 3;
     const int ntiles = (int)((N + 15) / 16);
@@ -309,9 +310,13 @@ static hipError_t launch_mt(const uint8_t* a, const uint8_t* as, int64_t ldx, co
     using namespace skinny;
     if (ldx > 0) {
         // the bf16 form exists for one block at one super-step per wave only
-        if constexpr (MT == 1 && SPW == 1)
+        if constexpr (MT == 1 && SPW == 1) {
+            if (uos)
+                return out_bf16 ? go(gemm_skinny_kernel<MT, SPW, NW, TPW, true, true, true>)
+                                : go(gemm_skinny_kernel<MT, SPW, NW, TPW, false, true, true>);
             return out_bf16 ? go(gemm_skinny_kernel<MT, SPW, NW, TPW, true, true>)
                             : go(gemm_skinny_kernel<MT, SPW, NW, TPW, false, true>);
+        }
         return hipErrorInvalidValue;
     }
     return out_bf16 ? go(gemm_skinny_kernel<MT, SPW, NW, TPW, true, false>)
@@ -350,14 +355,15 @@ hipError_t launch_gemm_skinny(const uint8_t* a_codes, const uint8_t* a_scales,
 
 hipError_t launch_linear_skinny(const uint16_t* x, int64_t ldx, const uint8_t* b_codes,
                                 const uint8_t* b_scales, int64_t M, int64_t N, int64_t K,
-                                void* y, bool out_bf16, hipStream_t stream) {
+                                void* y, bool out_bf16, bool uos, hipStream_t stream) {
     // M <= 16: one activation block; one super-step per wave (eight waves at
     // K = 4096, four at 2048)
     const uint8_t* a = reinterpret_cast<const uint8_t*>(x);
     if (K == 4096)
         return launch_mt<1, 1, 8>(a, nullptr, ldx, b_codes, b_scales, M, N, K, y, out_bf16,
-                                  stream);
-    return launch_mt<1, 1, 4>(a, nullptr, ldx, b_codes, b_scales, M, N, K, y, out_bf16, stream);
+                                  stream, uos);
+    return launch_mt<1, 1, 4>(a, nullptr, ldx, b_codes, b_scales, M, N, K, y, out_bf16, stream,
+                              uos);
 }
 
 }  // namespace mx

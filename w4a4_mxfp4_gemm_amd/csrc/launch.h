@@ -8,15 +8,17 @@
 namespace mx {
 
 hipError_t launch_act_quant(const uint16_t* x, int64_t ldx, const int32_t* row_index,
-                            int64_t M, int64_t K, uint8_t* codes, uint8_t* scales,
+                            int64_t M, int64_t K, uint8_t* codes, uint8_t* scales, bool uos,
                             hipStream_t stream);
 
 // tensors == nullptr: all T tensors; else the n_tensors listed (host memory,
-// each in [0, T)).
+// each in [0, T)).  uos: the Qmax = 7.25 shared-exponent rule, else OCP's.
+// The same flag means the same for act-quant and the fused linear.
 hipError_t launch_requant(const uint8_t* nv_codes, const uint8_t* nv_scales,
                           const float* nv_global, int64_t T, int64_t N, int64_t K,
                           const int32_t* tensors, int64_t n_tensors, uint8_t* mx_codes,
-                          uint8_t* mx_scales, bool bf16_intermediate, hipStream_t stream);
+                          uint8_t* mx_scales, bool bf16_intermediate, bool uos,
+                          hipStream_t stream);
 
 // Act-quant and weight-streaming GEMM in one launch: x bf16 [M][ldx], for
 // the shapes and alignments linear_skinny_supported accepts
@@ -26,7 +28,7 @@ bool linear_skinny_supported(int64_t M, int64_t N, int64_t K, const void* x, int
                              const void* w_scales);
 hipError_t launch_linear_skinny(const uint16_t* x, int64_t ldx, const uint8_t* b_codes,
                                 const uint8_t* b_scales, int64_t M, int64_t N, int64_t K,
-                                void* y, bool out_bf16, hipStream_t stream);
+                                void* y, bool out_bf16, bool uos, hipStream_t stream);
 
 hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
                        const uint8_t* b_codes, const uint8_t* b_scales,

@@ -56,6 +56,23 @@ __device__ __forceinline__ uint32_t mx_scale_from_amax_bits(uint32_t amax_bits) 
     return E >= 2u ? E - 2u : 0u;
 }
 
+// UOS shared-exponent byte (the single-scale setting with Qmax = 7.25): the
+// smallest e with amax <= 7.25 * 2^e.  With amax = f * 2^p (f in [1, 2)),
+// amax / 2^(p-2) = 4f is at most 7.25 exactly when f <= 1.8125, so this is the
+// OCP byte plus one when the fraction bits exceed 0x680000, clamped at 0 the
+// same way (subnormal amax included).  NaN or Inf gives 0xFF.
+__device__ __forceinline__ uint32_t mx_scale_uos_from_amax_bits(uint32_t amax_bits) {
+    const uint32_t E = amax_bits >> 23;
+    if (E >= 255u) return 255u;
+    const uint32_t e = E + ((amax_bits & 0x7FFFFFu) > 0x680000u ? 1u : 0u);
+    return e >= 2u ? e - 2u : 0u;
+}
+
+template <bool UOS>
+__device__ __forceinline__ uint32_t mx_scale_byte(uint32_t amax_bits) {
+    return UOS ? mx_scale_uos_from_amax_bits(amax_bits) : mx_scale_from_amax_bits(amax_bits);
+}
+
 // E2M1 magnitude code (0..7) of q >= 0: the nearest of {0, .5, 1, 1.5, 2, 3,
 // 4, 6}, exact half-way points going to the even code, anything past 5
 // saturating to 6.  Each term counts one decision threshold: strict '>' where
@@ -107,6 +124,8 @@ __device__ __forceinline__ uint32_t cvt_fp4x2_bf16(uint32_t old, uint32_t pair, 
 // over the bf16 magnitudes (compared as integers, so NaN and Inf patterns
 // rank above every finite value), the OCP MX exponent, each value divided by
 // the scale and rounded to E2M1; a NaN or Inf block gives 0xFF and zero codes.
+// UOS: the Qmax = 7.25 exponent rule instead of the OCP one.
+template <bool UOS = false>
 __device__ __forceinline__ uint32_t quant_block32_bf16(const uint32_t (&w)[16], uint32_t (&c)[4]) {
     typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
     u16x2_t a = __builtin_bit_cast(u16x2_t, w[0] & 0x7FFF7FFFu);
@@ -114,7 +133,7 @@ __device__ __forceinline__ uint32_t quant_block32_bf16(const uint32_t (&w)[16], 
     for (int i = 1; i < 16; ++i)
         a = __builtin_elementwise_max(a, __builtin_bit_cast(u16x2_t, w[i] & 0x7FFF7FFFu));
     const uint32_t amax = a[0] > a[1] ? a[0] : a[1];
-    const uint32_t byte = mx_scale_from_amax_bits(amax << 16);
+    const uint32_t byte = mx_scale_byte<UOS>(amax << 16);
     const float scale = e8m0_to_f32(byte);
 #pragma unroll
     for (int d = 0; d < 4; ++d) {

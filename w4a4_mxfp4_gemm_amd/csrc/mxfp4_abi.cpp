@@ -45,7 +45,8 @@ int mxfp4_requant_from_nvfp4(const uint8_t* nv_codes, const uint8_t* nv_scales,
                              uint8_t* mx_codes, uint8_t* mx_scales, uint32_t flags,
                              hipStream_t stream) {
     if (T < 0 || N <= 0 || check_k(K) != MXFP4_OK) return MXFP4_EINVAL;
-    if ((flags & ~(uint32_t)MXFP4_REQ_INTERMEDIATE_BF16) != 0) return MXFP4_EINVAL;
+    if ((flags & ~(uint32_t)(MXFP4_REQ_INTERMEDIATE_BF16 | MXFP4_SCALE_UOS)) != 0)
+        return MXFP4_EINVAL;
     if (T == 0) return MXFP4_OK;
     if (!nv_codes || !nv_scales || !nv_global || !mx_codes || !mx_scales) return MXFP4_EINVAL;
     if (!aligned(nv_codes, 16) || !aligned(mx_codes, 16) || !aligned(nv_scales, 2) ||
@@ -53,7 +54,8 @@ int mxfp4_requant_from_nvfp4(const uint8_t* nv_codes, const uint8_t* nv_scales,
         return MXFP4_EALIGN;
     return from_hip(mx::launch_requant(nv_codes, nv_scales, nv_global, T, N, K, nullptr, 0,
                                        mx_codes, mx_scales,
-                                       (flags & MXFP4_REQ_INTERMEDIATE_BF16) != 0, stream));
+                                       (flags & MXFP4_REQ_INTERMEDIATE_BF16) != 0,
+                                       (flags & MXFP4_SCALE_UOS) != 0, stream));
 }
 
 int mxfp4_requant_from_nvfp4_subset(const uint8_t* nv_codes, const uint8_t* nv_scales,
@@ -62,7 +64,8 @@ int mxfp4_requant_from_nvfp4_subset(const uint8_t* nv_codes, const uint8_t* nv_s
                                     uint8_t* mx_codes, uint8_t* mx_scales, uint32_t flags,
                                     hipStream_t stream) {
     if (T < 0 || N <= 0 || check_k(K) != MXFP4_OK || n_tensors < 0) return MXFP4_EINVAL;
-    if ((flags & ~(uint32_t)MXFP4_REQ_INTERMEDIATE_BF16) != 0) return MXFP4_EINVAL;
+    if ((flags & ~(uint32_t)(MXFP4_REQ_INTERMEDIATE_BF16 | MXFP4_SCALE_UOS)) != 0)
+        return MXFP4_EINVAL;
     if (n_tensors == 0) return MXFP4_OK;
     if (!tensors) return MXFP4_EINVAL;
     for (int64_t i = 0; i < n_tensors; ++i)    // in range, strictly increasing
@@ -74,20 +77,22 @@ int mxfp4_requant_from_nvfp4_subset(const uint8_t* nv_codes, const uint8_t* nv_s
         return MXFP4_EALIGN;
     return from_hip(mx::launch_requant(nv_codes, nv_scales, nv_global, T, N, K, tensors,
                                        n_tensors, mx_codes, mx_scales,
-                                       (flags & MXFP4_REQ_INTERMEDIATE_BF16) != 0, stream));
+                                       (flags & MXFP4_REQ_INTERMEDIATE_BF16) != 0,
+                                       (flags & MXFP4_SCALE_UOS) != 0, stream));
 }
 
 int mxfp4_quantize_act(const void* x_bf16, int64_t ldx, const int32_t* row_index, int64_t M,
                        int64_t K, uint8_t* codes, uint8_t* scales, uint32_t flags,
                        hipStream_t stream) {
     if (M < 0 || check_k(K) != MXFP4_OK || ldx < K) return MXFP4_EINVAL;
-    if (flags != 0) return MXFP4_EINVAL;
+    if ((flags & ~(uint32_t)MXFP4_SCALE_UOS) != 0) return MXFP4_EINVAL;
     if (M == 0) return MXFP4_OK;
     if (!x_bf16 || !codes || !scales) return MXFP4_EINVAL;
     if (!aligned(x_bf16, 16) || ldx % 8 != 0 || !aligned(codes, 16)) return MXFP4_EALIGN;
     if (row_index && !aligned(row_index, 4)) return MXFP4_EALIGN;
     return from_hip(mx::launch_act_quant(static_cast<const uint16_t*>(x_bf16), ldx, row_index,
-                                         M, K, codes, scales, stream));
+                                         M, K, codes, scales, (flags & MXFP4_SCALE_UOS) != 0,
+                                         stream));
 }
 
 int mxfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
@@ -113,16 +118,17 @@ int mxfp4_linear_bf16(const void* x_bf16, int64_t ldx, int64_t M, int64_t N, int
                       hipStream_t stream) {
     if (M < 0 || N <= 0 || check_k(K) != MXFP4_OK || ldx < K) return MXFP4_EINVAL;
     if (out_dtype != MXFP4_OUT_BF16 && out_dtype != MXFP4_OUT_FP32) return MXFP4_EINVAL;
-    if (flags != 0) return MXFP4_EINVAL;
+    if ((flags & ~(uint32_t)MXFP4_SCALE_UOS) != 0) return MXFP4_EINVAL;
     if (workspace_bytes != 0 && workspace == nullptr) return MXFP4_EINVAL;
     if (M == 0) return MXFP4_OK;
     if (!x_bf16 || !b_codes || !b_scales || !y) return MXFP4_EINVAL;
     if (!aligned(x_bf16, 16) || ldx % 8 != 0 || !aligned(b_codes, 16)) return MXFP4_EALIGN;
     if (!aligned(y, out_dtype == MXFP4_OUT_FP32 ? 4 : 2)) return MXFP4_EALIGN;
     const bool out_bf16 = out_dtype == MXFP4_OUT_BF16;
+    const bool uos = (flags & MXFP4_SCALE_UOS) != 0;
     if (mx::linear_skinny_supported(M, N, K, x_bf16, ldx, b_scales))
         return from_hip(mx::launch_linear_skinny(static_cast<const uint16_t*>(x_bf16), ldx,
-                                                 b_codes, b_scales, M, N, K, y, out_bf16,
+                                                 b_codes, b_scales, M, N, K, y, out_bf16, uos,
                                                  stream));
     // two launches through the workspace: the act-quant call, then the GEMM
     const size_t need = linear_codes_bytes(M, K) + (size_t)M * (size_t)(K / 32);
@@ -131,7 +137,7 @@ int mxfp4_linear_bf16(const void* x_bf16, int64_t ldx, int64_t M, int64_t N, int
     uint8_t* codes = static_cast<uint8_t*>(workspace);
     uint8_t* scales = codes + linear_codes_bytes(M, K);
     const hipError_t e = mx::launch_act_quant(static_cast<const uint16_t*>(x_bf16), ldx, nullptr,
-                                              M, K, codes, scales, stream);
+                                              M, K, codes, scales, uos, stream);
     if (e != hipSuccess) return MXFP4_EHIP;
     return from_hip(mx::launch_gemm(codes, scales, b_codes, b_scales, M, N, K, y, out_bf16,
                                     stream));

@@ -23,7 +23,7 @@ typedef uint32_t v4u_t __attribute__((ext_vector_type(4)));
 // ---------------------------------------------------------------------------
 // NT_OUT: codes and scales stored non-temporally (outputs too large to stay
 // cached for the GEMM that reads them next).
-template <int ROWS, bool NT_OUT>
+template <int ROWS, bool NT_OUT, bool UOS>
 __global__ __launch_bounds__(256) void act_quant_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const int32_t* __restrict__ row_index,
     int64_t M, int64_t K, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
@@ -61,7 +61,7 @@ __global__ __launch_bounds__(256) void act_quant_kernel(
             for (int i = 1; i < 4; ++i)
                 a = __builtin_elementwise_max(a, __builtin_bit_cast(u16x2, w[i] & 0x7FFF7FFFu));
             const uint32_t amax = quad_max_u32(max((uint32_t)a[0], (uint32_t)a[1]));
-            const uint32_t byte = mx_scale_from_amax_bits(amax << 16);
+            const uint32_t byte = mx_scale_byte<UOS>(amax << 16);
             const float scale = e8m0_to_f32(byte);
             uint32_t packed = cvt_fp4x2_bf16<0>(0u, w[0], scale);
             packed = cvt_fp4x2_bf16<1>(packed, w[1], scale);
@@ -111,7 +111,7 @@ __device__ __forceinline__ float nv_mag(float e2m1_mag, float s_abs, float g_abs
 // magnitudes marks which magnitudes occur.
 constexpr uint32_t ONEHOT_LO = 0x08040201u, ONEHOT_HI = 0x80402010u;
 
-template <bool BF16_INTERMEDIATE>
+template <bool BF16_INTERMEDIATE, bool UOS>
 __device__ __forceinline__ void requant_block(uint4 raw, uint32_t sc, float g_abs,
                                               uint32_t g_sign, uint4& out, uint32_t& byte_out) {
     const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
@@ -141,7 +141,7 @@ __device__ __forceinline__ void requant_block(uint4 raw, uint32_t sc, float g_ab
         const float top = nv_mag<BF16_INTERMEDIATE>(e2m1_to_f32(cmax), s_abs, g_abs);
         amax_bits = max(amax_bits, __float_as_uint(top) & 0x7FFFFFFFu);
     }
-    const uint32_t byte = mx_scale_from_amax_bits(amax_bits);
+    const uint32_t byte = mx_scale_byte<UOS>(amax_bits);
     const float scale = e8m0_to_f32(byte);
     uint32_t res[4];
 #pragma unroll
@@ -180,7 +180,7 @@ struct TensorSel {
 constexpr int REQUANT_SEL = 512;
 
 // `count` tensors: tensor i of the launch is sel.t[i] (NSEL > 1) or i.
-template <bool BF16_INTERMEDIATE, int NSEL>
+template <bool BF16_INTERMEDIATE, int NSEL, bool UOS>
 __global__ __launch_bounds__(256) void requant_kernel(
     const uint8_t* __restrict__ nv_codes, const uint8_t* __restrict__ nv_scales,
     const float* __restrict__ nv_global, int64_t count, const TensorSel<NSEL> sel,
@@ -213,7 +213,7 @@ __global__ __launch_bounds__(256) void requant_kernel(
                 if (b < blocks_per_tensor) {
                     uint4 out;
                     uint32_t byte;
-                    requant_block<BF16_INTERMEDIATE>(raw[u], sc[u], g_abs, g_sign, out, byte);
+                    requant_block<BF16_INTERMEDIATE, UOS>(raw[u], sc[u], g_abs, g_sign, out, byte);
                     __builtin_nontemporal_store(v4u_t{out.x, out.y, out.z, out.w},
                                                 reinterpret_cast<v4u_t*>(mx_codes + (base + b) * 16));
                     __builtin_nontemporal_store((uint8_t)byte, mx_scales + base + b);
@@ -224,7 +224,7 @@ __global__ __launch_bounds__(256) void requant_kernel(
 }
 
 hipError_t launch_act_quant(const uint16_t* x, int64_t ldx, const int32_t* row_index,
-                            int64_t M, int64_t K, uint8_t* codes, uint8_t* scales,
+                            int64_t M, int64_t K, uint8_t* codes, uint8_t* scales, bool uos,
                             hipStream_t stream) {
     constexpr int ROWS = 2;            // 1 and 4 measured slower
     const int64_t chunks = K / 8;
@@ -237,48 +237,56 @@ hipError_t launch_act_quant(const uint16_t* x, int64_t ldx, const int32_t* row_i
     // slower for the decode and [4096,4096] sizes
     const bool nt_out = !row_index && M * (K / 2) >= ((int64_t)16 << 20);
     const dim3 grid((unsigned)gx, (unsigned)gy);
-    if (nt_out)
-        hipLaunchKernelGGL((act_quant_kernel<ROWS, true>), grid, dim3(256), 0, stream, x, ldx,
-                           row_index, M, K, codes, scales);
+    auto go = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, x, ldx, row_index, M, K, codes,
+                           scales);
+    };
+    if (uos)
+        nt_out ? go(act_quant_kernel<ROWS, true, true>) : go(act_quant_kernel<ROWS, false, true>);
     else
-        hipLaunchKernelGGL((act_quant_kernel<ROWS, false>), grid, dim3(256), 0, stream, x, ldx,
-                           row_index, M, K, codes, scales);
+        nt_out ? go(act_quant_kernel<ROWS, true, false>)
+               : go(act_quant_kernel<ROWS, false, false>);
     return hipGetLastError();
 }
 
 hipError_t launch_requant(const uint8_t* nv_codes, const uint8_t* nv_scales,
                           const float* nv_global, int64_t T, int64_t N, int64_t K,
                           const int32_t* tensors, int64_t n_tensors, uint8_t* mx_codes,
-                          uint8_t* mx_scales, bool bf16_intermediate, hipStream_t stream) {
+                          uint8_t* mx_scales, bool bf16_intermediate, bool uos,
+                          hipStream_t stream) {
     const int64_t bpt = N * (K / 32);
     int64_t gx = (bpt + 511) / 512;
     if (gx > 8192) gx = 8192;
     auto grid = [&](int64_t count) {
         return dim3((unsigned)gx, (unsigned)(count > 65535 ? 65535 : count));
     };
-    if (!tensors) {
-        const TensorSel<1> none{{0}};
-        if (bf16_intermediate)
-            hipLaunchKernelGGL((requant_kernel<true, 1>), grid(T), dim3(256), 0, stream,
-                               nv_codes, nv_scales, nv_global, T, none, bpt, mx_codes, mx_scales);
+    // the four variants of the kernel for one tensor-list size
+    auto go = [&](auto sel, dim3 g, int64_t count) {
+        constexpr int NSEL = sizeof(sel.t) / sizeof(int32_t);
+        if (bf16_intermediate && uos)
+            hipLaunchKernelGGL((requant_kernel<true, NSEL, true>), g, dim3(256), 0, stream,
+                               nv_codes, nv_scales, nv_global, count, sel, bpt, mx_codes,
+                               mx_scales);
+        else if (bf16_intermediate)
+            hipLaunchKernelGGL((requant_kernel<true, NSEL, false>), g, dim3(256), 0, stream,
+                               nv_codes, nv_scales, nv_global, count, sel, bpt, mx_codes,
+                               mx_scales);
+        else if (uos)
+            hipLaunchKernelGGL((requant_kernel<false, NSEL, true>), g, dim3(256), 0, stream,
+                               nv_codes, nv_scales, nv_global, count, sel, bpt, mx_codes,
+                               mx_scales);
         else
-            hipLaunchKernelGGL((requant_kernel<false, 1>), grid(T), dim3(256), 0, stream,
-                               nv_codes, nv_scales, nv_global, T, none, bpt, mx_codes, mx_scales);
+            hipLaunchKernelGGL((requant_kernel<false, NSEL, false>), g, dim3(256), 0, stream,
+                               nv_codes, nv_scales, nv_global, count, sel, bpt, mx_codes,
+                               mx_scales);
         return hipGetLastError();
-    }
+    };
+    if (!tensors) return go(TensorSel<1>{{0}}, grid(T), T);
     for (int64_t c0 = 0; c0 < n_tensors; c0 += REQUANT_SEL) {
         const int64_t count = n_tensors - c0 < REQUANT_SEL ? n_tensors - c0 : REQUANT_SEL;
         TensorSel<REQUANT_SEL> sel{};
         for (int64_t i = 0; i < count; ++i) sel.t[i] = tensors[c0 + i];
-        if (bf16_intermediate)
-            hipLaunchKernelGGL((requant_kernel<true, REQUANT_SEL>), grid(count), dim3(256), 0,
-                               stream, nv_codes, nv_scales, nv_global, count, sel, bpt, mx_codes,
-                               mx_scales);
-        else
-            hipLaunchKernelGGL((requant_kernel<false, REQUANT_SEL>), grid(count), dim3(256), 0,
-                               stream, nv_codes, nv_scales, nv_global, count, sel, bpt, mx_codes,
-                               mx_scales);
-        const hipError_t e = hipGetLastError();
+        const hipError_t e = go(sel, grid(count), count);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
