@@ -88,6 +88,14 @@ def _load():
     lib.orc_gemm_at.argtypes = [P, P, P, P, I, I, I, P, P, I, P, P]
     lib.orc_grouped_gemm.restype = None
     lib.orc_grouped_gemm.argtypes = [P, P, P, P, P, I, I, I, P, P]
+    lib.orc_silu_mul_f32.restype = ctypes.c_float
+    lib.orc_silu_mul_f32.argtypes = [ctypes.c_float, ctypes.c_float]
+    lib.orc_silu_mul.restype = None
+    lib.orc_silu_mul.argtypes = [P, I, I, I, P, P]
+    lib.orc_silu_mul_quantize.restype = None
+    lib.orc_silu_mul_quantize.argtypes = [P, I, I, I, ctypes.c_int, P, P]
+    lib.orc_moe_combine.restype = None
+    lib.orc_moe_combine.argtypes = [P, I, P, P, I, I, I, P, P]
     lib.orc_bf16_from_double_array.restype = None
     lib.orc_bf16_from_double_array.argtypes = [P, I, P]
     lib.orc_num_threads.restype = ctypes.c_int
@@ -264,6 +272,63 @@ def grouped_gemm(a_codes, a_scales, b_codes, b_scales, offsets):
     _load().orc_grouped_gemm(_ptr(a_codes), _ptr(a_scales), _ptr(b_codes),
                              _ptr(b_scales), _ptr(offsets), E, N, K, _ptr(y), _ptr(s))
     return y, s
+
+
+# ---- MoE expert epilogues (R10, R11) -------------------------------------------
+def silu_mul_f32(g: float, u: float) -> float:
+    """silu(g) * u with every step rounded to fp32 (R10)."""
+    return float(_load().orc_silu_mul_f32(float(g), float(u)))
+
+
+def _gate_up(gate_up_bits, I):
+    gate_up_bits = _c(gate_up_bits, np.uint16)
+    M, ldg = gate_up_bits.shape
+    I = ldg // 2 if I is None else int(I)
+    assert 2 * I <= ldg
+    return gate_up_bits, M, ldg, I
+
+
+def silu_mul(gate_up_bits, I=None):
+    """bf16 bits [M, ldg] (gate = columns [0, I), up = [I, 2I)) ->
+    (h bf16 bits [M, I], h fp32 [M, I] before the bf16 rounding)."""
+    gate_up_bits, M, ldg, I = _gate_up(gate_up_bits, I)
+    hb = np.empty((M, I), dtype=np.uint16)
+    hf = np.empty((M, I), dtype=np.float32)
+    if M and I:
+        _load().orc_silu_mul(_ptr(gate_up_bits), ldg, M, I, _ptr(hb), _ptr(hf))
+    return hb, hf
+
+
+def silu_mul_quantize(gate_up_bits, I=None, scale_rule="ocp"):
+    """R10 then act-quant: codes [M, I/2], E8M0 [M, I/32]."""
+    gate_up_bits, M, ldg, I = _gate_up(gate_up_bits, I)
+    assert I % 32 == 0
+    codes = np.empty((M, I // 2), dtype=np.uint8)
+    scales = np.empty((M, I // 32), dtype=np.uint8)
+    if M and I:
+        _load().orc_silu_mul_quantize(_ptr(gate_up_bits), ldg, M, I, _RULES[scale_rule],
+                                      _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+def moe_combine(y_bits, rows, weights, H=None):
+    """R11: y bf16 bits [R, ldy], rows int32 [T, topk] (sorted-row index of
+    each token's j-th expert), weights fp32 [T, topk] -> (out fp64 [T, H],
+    s = sum_j |w * y| [T, H])."""
+    y_bits = _c(y_bits, np.uint16)
+    R, ldy = y_bits.shape
+    H = ldy if H is None else int(H)
+    rows = _c(rows, np.int32)
+    weights = _c(weights, np.float32)
+    T, topk = rows.shape
+    assert weights.shape == (T, topk) and H <= ldy
+    assert rows.size == 0 or (rows.min() >= 0 and rows.max() < R)
+    out = np.empty((T, H), dtype=np.float64)
+    s = np.empty((T, H), dtype=np.float64)
+    if T and H:
+        _load().orc_moe_combine(_ptr(y_bits), ldy, _ptr(rows), _ptr(weights), T, topk, H,
+                                _ptr(out), _ptr(s))
+    return out, s
 
 
 # ---- parity bar for the GEMM ------------------------------------------------

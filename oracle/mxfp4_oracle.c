@@ -412,6 +412,68 @@ void orc_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
     }
 }
 
+/* ---- MoE expert epilogues ----------------------------------------------- */
+
+/* R10: silu(g) = g * sigma(g), sigma(g) = 1 / (1 + exp(-g)), times the up
+   value, each operation rounded to fp32 (the oracle's exp is the C library's
+   double exp rounded to fp32). */
+float orc_silu_mul_f32(float g, float u)
+{
+    float e = (float)exp(-(double)g);
+    float d = 1.0f + e;
+    float r = 1.0f / d;
+    float sg = g * r;
+    return sg * u;
+}
+
+void orc_silu_mul(const uint16_t* gate_up, int64_t ldg, int64_t M, int64_t I,
+                  uint16_t* h_bf16, float* h_f32)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        const uint16_t* row = gate_up + m * ldg;
+        for (int64_t i = 0; i < I; ++i) {
+            float g = (float)orc_bf16_value(row[i]);
+            float u = (float)orc_bf16_value(row[I + i]);
+            float h = orc_silu_mul_f32(g, u);
+            if (h_f32) h_f32[m * I + i] = h;
+            if (h_bf16) h_bf16[m * I + i] = orc_bf16_from_float(h);
+        }
+    }
+}
+
+/* R10 then the activation quantization of the down projection's input. */
+void orc_silu_mul_quantize(const uint16_t* gate_up, int64_t ldg, int64_t M, int64_t I,
+                           int rule, uint8_t* codes, uint8_t* scales)
+{
+    uint16_t* h = malloc((size_t)(M * I > 0 ? M * I : 1) * sizeof(uint16_t));
+    if (!h) abort();
+    orc_silu_mul(gate_up, ldg, M, I, h, NULL);
+    orc_quantize_act_rule(h, I, NULL, M, I, rule, codes, scales);
+    free(h);
+}
+
+/* R11: each output element is a sum of topk exact fp64 products (a bf16
+   value times an fp32 weight needs 32 significant bits), added in fp64. */
+void orc_moe_combine(const uint16_t* y, int64_t ldy, const int32_t* rows, const float* w,
+                     int64_t T, int64_t topk, int64_t H, double* out, double* s)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t n = 0; n < H; ++n) {
+            double acc = 0.0, mag = 0.0;
+            for (int64_t j = 0; j < topk; ++j) {
+                double p = (double)w[t * topk + j] *
+                           orc_bf16_value(y[(int64_t)rows[t * topk + j] * ldy + n]);
+                acc += p;
+                mag += fabs(p);
+            }
+            out[t * H + n] = acc;
+            if (s) s[t * H + n] = mag;
+        }
+    }
+}
+
 /* Elementwise helper for the tests: RNE of n doubles to bf16 bit patterns. */
 void orc_bf16_from_double_array(const double* v, int64_t n, uint16_t* out)
 {

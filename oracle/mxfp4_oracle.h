@@ -42,6 +42,21 @@
  *      Scaling", setting 2, Qmax = 7.25): e = ceil(log2(amax / 7.25)), i.e.
  *      the smallest e with amax <= 7.25 * 2^e, clamped to [-127, 127];
  *      elements are encoded as in R4 (still saturating at 6).
+ *   R10 expert activation between the two grouped GEMMs ([P1] closing list:
+ *      the MoE experts run as fused-MoE kernels; the expert weights are a
+ *      gate/up pair and a down projection): the gate_up output row holds the
+ *      gate half in columns [0, I) and the up half in [I, 2I); the down
+ *      projection's input is h = bf16(silu(gate) * up), quantized like any
+ *      activation (R3/R9 + R4).  The value decides quantized codes, so it is
+ *      computed in the kernel's precision, fp32 with every step rounded once:
+ *      e = fl32(exp(-g)), d = fl32(1 + e), r = fl32(1 / d), s = fl32(g * r),
+ *      h = fl32(s * u).  A GPU exp or reciprocal that is not correctly
+ *      rounded can move h by a few fp32 ulps, so where h lies that close to
+ *      a bf16 rounding midpoint either neighbour is a correct result.
+ *   R11 top-k combine ([P1] closing list, MoE experts): each token's output
+ *      row is the sum over its k routed rows of weight * expert output row,
+ *      computed exactly (fp64) and rounded once to the output type.  The
+ *      weights and the token -> sorted-row map are inputs.
  */
 #ifndef MXFP4_ORACLE_H
 #define MXFP4_ORACLE_H
@@ -110,6 +125,25 @@ void orc_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
                       const uint8_t* b_codes, const uint8_t* b_scales,
                       const int32_t* offsets, int64_t E, int64_t N, int64_t K,
                       double* y, double* s);
+
+/* ---- MoE expert epilogues (R10, R11) ---------------------------------- */
+/* silu(g) * u in fp32, every step rounded once (R10). */
+float orc_silu_mul_f32(float g, float u);
+
+/* gate_up bf16 [M][ldg] -> h = bf16(silu(gate) * up) [M][I] (h_bf16) and the
+   fp32 value before that rounding (h_f32); either output may be NULL. */
+void orc_silu_mul(const uint16_t* gate_up, int64_t ldg, int64_t M, int64_t I,
+                  uint16_t* h_bf16, float* h_f32);
+
+/* h as above, then quantized by orc_quantize_act_rule: codes [M][I/2],
+   E8M0 [M][I/32]. */
+void orc_silu_mul_quantize(const uint16_t* gate_up, int64_t ldg, int64_t M, int64_t I,
+                           int rule, uint8_t* codes, uint8_t* scales);
+
+/* out[t][n] = sum_{j<topk} w[t*topk+j] * y[rows[t*topk+j]][n] (fp64) and
+   s[t][n] = sum_j |w * y| (R11); y is bf16 [*][ldy]; s may be NULL. */
+void orc_moe_combine(const uint16_t* y, int64_t ldy, const int32_t* rows, const float* w,
+                     int64_t T, int64_t topk, int64_t H, double* out, double* s);
 
 void orc_bf16_from_double_array(const double* v, int64_t n, uint16_t* out);
 int  orc_num_threads(void);

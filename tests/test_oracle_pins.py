@@ -509,3 +509,134 @@ def test_tolerance_rules_accept_one_ulp_reject_two():
     assert not oracle.gemm_fp32_ok(y + 1.1e-5 * s, y, s).any()
     assert oracle.gemm_fp32_ok(np.array([0.0]), np.array([0.0]), np.array([0.0])).all()
     assert not oracle.gemm_fp32_ok(np.array([1e-30]), np.array([0.0]), np.array([0.0])).any()
+
+
+# ---- R10: expert activation (silu(gate) * up) before the down projection ------
+def bf16_bits(t):
+    return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def test_silu_mul_against_library_sigmoid():
+    """Random bf16 gate/up values: the oracle's fp32 evaluation lies within a
+    few fp32 ulps of g * expit(g) * u, with scipy's logistic function as the
+    independent sigmoid (a wrong sign in the exponent, a dropped term or the
+    gate and up roles swapped are off by far more)."""
+    from scipy.special import expit
+    rng = np.random.default_rng(101)
+    g = torch.from_numpy(rng.uniform(-30, 30, 4000).astype(np.float32)).to(torch.bfloat16)
+    u = torch.from_numpy(rng.normal(0, 2, 4000).astype(np.float32)).to(torch.bfloat16)
+    g64, u64 = g.double().numpy(), u.double().numpy()
+    want = g64 * expit(g64) * u64
+    got = np.array([oracle.silu_mul_f32(a, b) for a, b in zip(g64, u64)])
+    ulp = np.spacing(np.abs(want).astype(np.float32)).astype(np.float64)
+    assert (np.abs(got - want) <= 4 * ulp + 1e-44).all()
+
+
+def test_silu_mul_closed_forms():
+    f = oracle.silu_mul_f32
+    # silu(g) - silu(-g) = g
+    for g in (0.5, 1.0, 2.75, 7.0, 12.5):
+        assert abs((f(g, 1.0) - f(-g, 1.0)) - g) <= 4 * np.spacing(np.float32(g))
+    assert f(0.0, 3.0) == 0.0
+    for g in (17.0, 20.0, 60.0, 1e30):     # e^-g below half an ulp of 1: silu(g) = g
+        for u in (0.3, -1.7, 2.0 ** -100):
+            assert f(g, u) == float(np.float32(g) * np.float32(u))
+    assert f(-100.0, 1.0) == 0.0 and np.signbit(f(-100.0, 1.0))
+    assert f(float("inf"), 1.0) == float("inf")
+    assert np.isnan(f(float("-inf"), 1.0)) and np.isnan(f(float("nan"), 1.0))
+
+
+def test_silu_mul_quantize_linear_region_is_act_quant():
+    """Where every gate is >= 17 the activation is exactly fl32(g * u): the
+    composition must equal the act-quant of those products rounded to bf16
+    (rounded here by torch), for both scale rules; the gate and up halves are
+    told apart because swapping them leaves that region."""
+    rng = np.random.default_rng(102)
+    M, I = 6, 96
+    g = torch.from_numpy(rng.uniform(17, 400, (M, I)).astype(np.float32)).to(torch.bfloat16)
+    u = torch.from_numpy(rng.normal(0, 0.05, (M, I)).astype(np.float32)).to(torch.bfloat16)
+    gu = bf16_bits(torch.cat([g, u], dim=1))
+    prod = (g.float() * u.float()).to(torch.bfloat16)
+    for rule in ("ocp", "uos"):
+        want = oracle.quantize_act(bf16_bits(prod), scale_rule=rule)
+        got = oracle.silu_mul_quantize(gu, scale_rule=rule)
+        assert np.array_equal(got[0], want[0]) and np.array_equal(got[1], want[1])
+    hb, hf = oracle.silu_mul(gu)
+    assert np.array_equal(hb, bf16_bits(prod))
+    assert np.array_equal(hf, (g.float() * u.float()).numpy())
+
+
+@pytest.mark.parametrize("row", read_table("silu_mul_examples.txt"), ids=lambda r: r[0])
+def test_silu_mul_examples(row):
+    name, gate, up, hbits, byte, codes = row
+    gu = np.zeros((1, 64), dtype=np.float32)
+    for i, x in parse_sparse(gate, parse_float).items():
+        gu[0, i] = x
+    for i, x in parse_sparse(up, parse_float).items():
+        gu[0, 32 + i] = x
+    bits = bf16_bits(torch.from_numpy(gu).to(torch.bfloat16))
+    assert np.array_equal(torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).float()
+                          .numpy(), gu), "fixture inputs must be bf16 values"
+    hb, _ = oracle.silu_mul(bits)
+    want_h = np.zeros(32, dtype=np.uint16)
+    for i, b in parse_sparse(hbits, lambda t: int(t, 16)).items():
+        want_h[i] = b
+    assert np.array_equal(hb[0], want_h)
+    c, s = oracle.silu_mul_quantize(bits)
+    assert int(s[0, 0]) == int(byte)
+    want = np.zeros(32, dtype=np.int64)
+    for i, k in parse_sparse(codes, int).items():
+        want[i] = k
+    got = np.empty(32, dtype=np.int64)
+    got[0::2], got[1::2] = c[0] & 15, c[0] >> 4
+    assert np.array_equal(got, want)
+
+
+# ---- R11: top-k combine --------------------------------------------------------
+def combine_case(seed, T=12, topk=8, H=40, R=None):
+    rng = np.random.default_rng(seed)
+    R = R or T * topk
+    y = torch.from_numpy(rng.normal(0, 1, (R, H)).astype(np.float32)).to(torch.bfloat16)
+    rows = rng.permutation(R)[:T * topk].reshape(T, topk).astype(np.int32)
+    w = rng.dirichlet(np.ones(topk), size=T).astype(np.float32)
+    return bf16_bits(y), y.double().numpy(), rows, w
+
+
+def test_combine_one_hot_weights_select_rows():
+    bits, y, rows, w = combine_case(103)
+    w1 = np.zeros_like(w)
+    w1[np.arange(w.shape[0]), 3] = 1.0
+    out, s = oracle.moe_combine(bits, rows, w1)
+    assert np.array_equal(out, y[rows[:, 3]]) and np.array_equal(s, np.abs(out))
+
+
+def test_combine_equal_rows_and_power_of_two_weights():
+    """k copies of one row with weights 1/k (k a power of two) return the row
+    exactly; weights w and 2w give exactly twice the result."""
+    bits, y, rows, w = combine_case(104, topk=8)
+    rows_same = np.repeat(rows[:, :1], 8, axis=1)
+    out, _ = oracle.moe_combine(bits, rows_same, np.full(w.shape, 0.125, np.float32))
+    assert np.array_equal(out, y[rows[:, 0]])
+    a, _ = oracle.moe_combine(bits, rows, w)
+    b, _ = oracle.moe_combine(bits, rows, 2 * w)
+    assert np.array_equal(b, 2 * a)
+
+
+def test_combine_order_and_linearity_invariants():
+    """Permuting a token's k (row, weight) pairs changes nothing beyond fp64
+    rounding; the result is linear in the weights; s bounds |out| and equals
+    it when every product is non-negative."""
+    bits, y, rows, w = combine_case(105)
+    out, s = oracle.moe_combine(bits, rows, w)
+    perm = np.random.default_rng(6).permutation(rows.shape[1])
+    out2, s2 = oracle.moe_combine(bits, rows[:, perm], w[:, perm])
+    assert np.allclose(out2, out, rtol=0, atol=1e-15 * s.max())
+    assert np.allclose(s2, s, rtol=1e-15, atol=0)
+    half = (w / 2).astype(np.float32)
+    p, _ = oracle.moe_combine(bits, rows, half)
+    q, _ = oracle.moe_combine(bits, rows, w - half)
+    assert np.allclose(p + q, out, rtol=0, atol=1e-15 * s.max())
+    assert (np.abs(out) <= s).all()
+    pos_bits = bits & np.uint16(0x7FFF)
+    o3, s3 = oracle.moe_combine(pos_bits, rows, w)
+    assert np.array_equal(o3, s3)
