@@ -335,12 +335,15 @@ def prefill_workload(torch, mx, synth):
 
 
 def moe_workload(torch, mx, synth):
+    """One MoE layer's expert path: gathered act-quant of the routed tokens,
+    grouped gate_up GEMM, expert activation + act-quant of the down input
+    (silu(gate) * up), grouped down GEMM; the top-k combine that ends the layer
+    is timed beside it."""
     E, T, TOPK = 128, 2048, 8
     d = torch.device("cuda:0")
-    perm, offsets = synth.route_topk(T, E, TOPK, seed=34, device="cpu")
-    perm, offsets = perm.to(d), offsets.to(d)
+    perm, offsets, rows, weights = synth.route_topk_full(T, E, TOPK, seed=34, device="cpu")
+    perm, offsets, rows, weights = perm.to(d), offsets.to(d), rows.to(d), weights.to(d)
     tokens = synth.activations(T, 4096, seed=33, device=d)
-    down_in = synth.activations(T * TOPK, 1024, seed=35, device=d)
     W = {}
     for name, (N, K), seed in (("gate_up", (2048, 4096), 31), ("down", (4096, 1024), 32)):
         wc = torch.empty((E, N, K // 2), dtype=torch.uint8, device=d)
@@ -355,13 +358,13 @@ def moe_workload(torch, mx, synth):
     # 855 MB, exceed the Infinity Cache on their own)
     R = MOE_SLOTS
     tokens = [tokens.clone() for _ in range(R)]
-    down_in = [down_in.clone() for _ in range(R)]
     aq1 = [(torch.empty((Mtot, 2048), dtype=torch.uint8, device=d),
             torch.empty((Mtot, 128), dtype=torch.uint8, device=d)) for _ in range(R)]
     aq2 = [(torch.empty((Mtot, 512), dtype=torch.uint8, device=d),
             torch.empty((Mtot, 32), dtype=torch.uint8, device=d)) for _ in range(R)]
     y1 = [torch.empty((Mtot, 2048), dtype=torch.bfloat16, device=d) for _ in range(R)]
     y2 = [torch.empty((Mtot, 4096), dtype=torch.bfloat16, device=d) for _ in range(R)]
+    out = [torch.empty((T, 4096), dtype=torch.bfloat16, device=d) for _ in range(R)]
 
     def aq_gate_up(r):
         mx.mxfp4_quantize_act(tokens[r], *aq1[r], row_index=perm)
@@ -370,15 +373,22 @@ def moe_workload(torch, mx, synth):
         mx.mxfp4_grouped_gemm(aq1[r][0], aq1[r][1], W["gate_up"][2], W["gate_up"][3], offsets,
                               y1[r])
 
-    def aq_down(r):
-        mx.mxfp4_quantize_act(down_in[r], *aq2[r])
+    def act_down(r):
+        mx.mxfp4_silu_mul_quantize(y1[r], *aq2[r])
 
     def gemm_down(r):
         mx.mxfp4_grouped_gemm(aq2[r][0], aq2[r][1], W["down"][2], W["down"][3], offsets, y2[r])
 
+    def combine(r):
+        mx.mxfp4_moe_combine(y2[r], rows, weights, out[r])
+
+    def step(r):
+        aq_gate_up(r), gemm_gate_up(r), act_down(r), gemm_down(r)
+
     ph = Phases(torch, R)
-    ph.add("step", lambda r: (aq_gate_up(r), gemm_gate_up(r), aq_down(r), gemm_down(r)))
-    for f in (aq_gate_up, gemm_gate_up, aq_down, gemm_down):
+    ph.add("step", step)
+    ph.add("layer", lambda r: (step(r), combine(r)))
+    for f in (aq_gate_up, gemm_gate_up, act_down, gemm_down, combine):
         ph.add(f.__name__, f)
 
     def report(t, steps):
@@ -389,16 +399,25 @@ def moe_workload(torch, mx, synth):
         gb = (E * 2048 * 4096 * mx4 + Mtot * 4096 * mx4 + Mtot * 2048 * 2 +
               E * 4096 * 1024 * mx4 + Mtot * 1024 * mx4 + Mtot * 4096 * 2)
         ach = gb / (tg * 1e-3) / 1e9
-        per = {k: round(t[k] * 1e3, 2) for k in ("aq_gate_up", "gemm_gate_up", "aq_down",
-                                                 "gemm_down")}
+        per = {k: round(t[k] * 1e3, 2) for k in ("aq_gate_up", "gemm_gate_up", "act_down",
+                                                 "gemm_down", "combine")}
+        # algorithmic bytes of the two epilogue kernels
+        act_b = Mtot * 2048 * 2 + Mtot * 1024 * mx4
+        comb_b = Mtot * 4096 * 2 + T * 4096 * 2 + T * TOPK * 8
         roof = {"kernel": "mxfp4_grouped_gemm (gate_up + down)", "bound": "hbm",
                 "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBPS, 4),
                 "traffic": recorded_traffic("grouped_gemm_moe"),
                 "gemm_TFLOPs": round(flops / (tg * 1e-3) / 1e12, 1)}
+        extra = {"per_kernel_us": per,
+                 "layer_us": round(t["layer"] * 1e3, 2),
+                 "layer_TFLOPs": round(flops / (t["layer"] * 1e-3) / 1e12, 1),
+                 "act_down_GBps": round(act_b / (t["act_down"] * 1e-3) / 1e9, 1),
+                 "combine_GBps": round(comb_b / (t["combine"] * 1e-3) / 1e9, 1)}
         cfg = {"workload": "MoE 128 experts, 2048 tokens top-8: gather act-quant + grouped "
-                           "GEMM gate_up [2048,4096], act-quant + grouped GEMM down [4096,1024]"}
-        return value, "TFLOP/s", roof, {"per_kernel_us": per}, cfg
+                           "GEMM gate_up [2048,4096], silu(gate)*up act-quant + grouped GEMM "
+                           "down [4096,1024] (layer_us adds the top-k combine)"}
+        return value, "TFLOP/s", roof, extra, cfg
 
     return ph, report, None
 

@@ -202,6 +202,60 @@ int mxfp4_linear_bf16(const void* x_bf16, int64_t ldx, int64_t M, int64_t N, int
 /* Workspace bytes mxfp4_linear_bf16 needs: 0 for the one-launch shapes. */
 size_t mxfp4_linear_workspace_size(int64_t M, int64_t N, int64_t K);
 
+/*
+ * The activation between an MoE layer's two grouped GEMMs, quantized for the
+ * second (AMD blog, closing list: the MoE experts run as fused-MoE kernels on
+ * MXFP4).  Each expert is a gate/up projection followed by a down projection;
+ * the gate_up GEMM's output row holds the gate half g in columns [0, I) and
+ * the up half u in [I, 2I).  The down projection's input is
+ *   h = bf16_RNE(silu(g) * u),  silu(g) = g / (1 + e^-g),
+ * evaluated in fp32 (exp, 1 + e, a reciprocal, two products), and is
+ * quantized to MXFP4 exactly as mxfp4_quantize_act would quantize h.  The
+ * exponential and reciprocal are gfx950's (within 2 ulp), so an h lying
+ * within a few fp32 ulps of a bf16 rounding midpoint may round either way.
+ * Rows stay in the order given (expert-sorted, as the grouped GEMM wrote
+ * them).
+ *
+ *   gate_up_bf16  [M][ldg] bf16, device, read; ldg >= 2*I, ldg % 8 == 0,
+ *                 16-byte aligned
+ *   I             columns of h; a positive multiple of 32
+ *   codes         [M][I/2] u8, device, written (16-byte aligned)
+ *   scales        [M][I/32] u8, device, written
+ *   flags         0 or MXFP4_SCALE_UOS
+ */
+int mxfp4_silu_mul_quantize(const void* gate_up_bf16, int64_t ldg, int64_t M, int64_t I,
+                            uint8_t* codes, uint8_t* scales, uint32_t flags,
+                            hipStream_t stream);
+
+/* Largest topk mxfp4_moe_combine accepts. */
+enum { MXFP4_COMBINE_MAX_TOPK = 64 };
+
+/*
+ * The top-k combine that ends an MoE layer (AMD blog, closing list: MoE
+ * experts): each token's output row is the weighted sum of its topk routed
+ * expert-output rows,
+ *   out[t][n] = sum_{j < topk} weights[t*topk + j] * y[rows[t*topk + j]][n],
+ * accumulated in fp32 with one fused multiply-add per routed row, in the
+ * order j = 0, 1, ..., then rounded once to the output type (RNE).  The
+ * result is the same on every run.
+ *
+ *   y_bf16     [R][ldy] bf16, device, read: the down projection's output in
+ *              expert-sorted row order; ldy >= H, ldy % 8 == 0, 16-byte aligned
+ *   rows       [T][topk] int32, device, read: the sorted row holding token
+ *              t's j-th expert output.  Not checked on the host (that would
+ *              need a sync); the kernel clamps each index to [0, R), so a bad
+ *              table gives wrong sums but never a read outside y.
+ *   weights    [T][topk] fp32, device, read: the routing weights
+ *   T, topk    tokens and experts per token (1 <= topk <= 64)
+ *   H          columns; a positive multiple of 8
+ *   out        [T][H] bf16 (MXFP4_OUT_BF16) or fp32 (MXFP4_OUT_FP32),
+ *              device, written, 16-byte aligned; must not overlap y
+ *   flags      0
+ */
+int mxfp4_moe_combine(const void* y_bf16, int64_t ldy, int64_t R, const int32_t* rows,
+                      const float* weights, int64_t T, int64_t topk, int64_t H, void* out,
+                      int out_dtype, uint32_t flags, hipStream_t stream);
+
 /* Static description of a status code; never NULL. */
 const char* mxfp4_status_string(int status);
 

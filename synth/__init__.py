@@ -108,13 +108,16 @@ def canonical_mxfp4(rows: int, K: int, seed: int, scale_lo: int = 117,
     return codes, scales
 
 
-def route_topk(tokens: int, experts: int, topk: int, seed: int, device="cpu"):
-    """Softmax top-k routing.  Returns (perm int32 [tokens*topk]: token index of
-    each expert-sorted row, offsets int32 [experts+1])."""
+def route_topk_full(tokens: int, experts: int, topk: int, seed: int, device="cpu"):
+    """Softmax top-k routing over N(0,1) logits, ties to the lower expert index.
+    Returns (perm int32 [tokens*topk]: token index of each expert-sorted row,
+    offsets int32 [experts+1], rows int32 [tokens, topk]: the sorted row
+    holding token t's j-th choice, weights fp32 [tokens, topk]: the chosen
+    probabilities renormalised to sum to 1 per token)."""
     logits = torch.randn((tokens, experts), generator=generator(seed, device),
                          device=device, dtype=torch.float32)
     probs = torch.softmax(logits, dim=-1)
-    _, idx = torch.topk(probs, topk, dim=-1)
+    top, idx = torch.topk(probs, topk, dim=-1)
     flat_e = idx.reshape(-1)
     flat_t = torch.arange(tokens, device=device).repeat_interleave(topk)
     order = torch.sort(flat_e, stable=True).indices
@@ -122,7 +125,18 @@ def route_topk(tokens: int, experts: int, topk: int, seed: int, device="cpu"):
     counts = torch.bincount(flat_e, minlength=experts)
     offsets = torch.zeros(experts + 1, dtype=torch.int64, device=device)
     offsets[1:] = torch.cumsum(counts, 0)
-    return perm.contiguous(), offsets.to(torch.int32).contiguous()
+    rows = torch.empty_like(order)
+    rows[order] = torch.arange(order.numel(), device=device)
+    weights = top / top.sum(dim=-1, keepdim=True)
+    return (perm.contiguous(), offsets.to(torch.int32).contiguous(),
+            rows.reshape(tokens, topk).to(torch.int32).contiguous(),
+            weights.to(torch.float32).contiguous())
+
+
+def route_topk(tokens: int, experts: int, topk: int, seed: int, device="cpu"):
+    """route_topk_full's (perm, offsets)."""
+    perm, offsets, _, _ = route_topk_full(tokens, experts, topk, seed, device)
+    return perm, offsets
 
 
 def ceil_div(a: int, b: int) -> int:

@@ -156,3 +156,36 @@ def test_linear_workspace_size(lib):
     assert ws(65, 512, 4096) == (65 * 2048 + 255) // 256 * 256 + 65 * 128
     assert ws(8, 256, 1024) == (8 * 512 + 255) // 256 * 256 + 8 * 32     # K = 1024
     assert ws(0, 256, 1024) == 0 and ws(8, 256, 48) == 0                 # nothing to run
+
+
+def test_silu_mul_quantize_argument_checks(lib):
+    f = lib.mxfp4_silu_mul_quantize
+    #        gate_up ldg  M  I    codes scales flags stream
+    assert f(FAKE, 256, 4, 80, FAKE, FAKE, 0, None) == -1     # I % 32
+    assert f(FAKE, 120, 4, 64, FAKE, FAKE, 0, None) == -1     # ldg < 2I
+    assert f(FAKE, 128, 4, 64, FAKE, FAKE, 1, None) == -1     # flags
+    assert f(FAKE, 128, -1, 64, FAKE, FAKE, 0, None) == -1    # M
+    assert f(None, 128, 4, 64, FAKE, FAKE, 0, None) == -1
+    assert f(FAKE, 128, 4, 64, None, FAKE, 0, None) == -1
+    assert f(ODD, 128, 4, 64, FAKE, FAKE, 0, None) == -2      # gate_up alignment
+    assert f(FAKE, 132, 4, 64, FAKE, FAKE, 0, None) == -2     # ldg % 8
+    assert f(FAKE, 128, 4, 64, ODD, FAKE, 0, None) == -2      # codes alignment
+    assert f(FAKE, 128, 0, 64, FAKE, FAKE, 2, None) == 0      # M == 0, UOS accepted
+
+
+def test_moe_combine_argument_checks(lib):
+    f = lib.mxfp4_moe_combine
+    #        y    ldy  R   rows weights T  topk H    out  dtype flags stream
+    assert f(FAKE, 64, 16, FAKE, FAKE, 2, 8, 60, FAKE, 0, 0, None) == -1    # H % 8
+    assert f(FAKE, 56, 16, FAKE, FAKE, 2, 8, 64, FAKE, 0, 0, None) == -1    # ldy < H
+    assert f(FAKE, 64, 0, FAKE, FAKE, 2, 8, 64, FAKE, 0, 0, None) == -1     # R
+    assert f(FAKE, 64, 16, FAKE, FAKE, 2, 0, 64, FAKE, 0, 0, None) == -1    # topk
+    assert f(FAKE, 64, 16, FAKE, FAKE, 2, 65, 64, FAKE, 0, 0, None) == -1   # topk > 64
+    assert f(FAKE, 64, 16, FAKE, FAKE, 2, 8, 64, FAKE, 5, 0, None) == -1    # out dtype
+    assert f(FAKE, 64, 16, FAKE, FAKE, 2, 8, 64, FAKE, 0, 1, None) == -1    # flags
+    assert f(FAKE, 64, 16, None, FAKE, 2, 8, 64, FAKE, 0, 0, None) == -1    # rows
+    assert f(ODD, 64, 16, FAKE, FAKE, 2, 8, 64, FAKE, 0, 0, None) == -2
+    assert f(FAKE, 68, 16, FAKE, FAKE, 2, 8, 64, FAKE, 0, 0, None) == -2    # ldy % 8
+    assert f(FAKE, 64, 16, FAKE, FAKE, 2, 8, 64, FAKE + 8, 0, 0, None) == -2  # out
+    assert f(FAKE, 64, 16, ODD, FAKE, 2, 8, 64, FAKE, 0, 0, None) == -2     # rows
+    assert f(FAKE, 64, 16, FAKE, FAKE, 0, 8, 64, FAKE, 1, 0, None) == 0     # T == 0

@@ -50,6 +50,10 @@ def _load_library() -> ctypes.CDLL:
     lib.mxfp4_grouped_gemm.restype = ctypes.c_int
     lib.mxfp4_linear_bf16.argtypes = [P, I, I, I, I, P, P, P, ctypes.c_int, P, SZ, U32, P]
     lib.mxfp4_linear_bf16.restype = ctypes.c_int
+    lib.mxfp4_silu_mul_quantize.argtypes = [P, I, I, I, P, P, U32, P]
+    lib.mxfp4_silu_mul_quantize.restype = ctypes.c_int
+    lib.mxfp4_moe_combine.argtypes = [P, I, I, P, P, I, I, I, P, ctypes.c_int, U32, P]
+    lib.mxfp4_moe_combine.restype = ctypes.c_int
     lib.mxfp4_linear_workspace_size.argtypes = [I, I, I]
     lib.mxfp4_linear_workspace_size.restype = SZ
     lib.mxfp4_gemm_workspace_size.argtypes = [I, I, I]
@@ -66,8 +70,8 @@ _lib = _load_library()
 EXPORTED_SYMBOLS = ("mxfp4_requant_from_nvfp4", "mxfp4_requant_from_nvfp4_subset",
                     "mxfp4_quantize_act", "mxfp4_gemm",
                     "mxfp4_grouped_gemm", "mxfp4_linear_bf16", "mxfp4_gemm_workspace_size",
-                    "mxfp4_linear_workspace_size",
-                    "mxfp4_status_string", "mxfp4_version")
+                    "mxfp4_linear_workspace_size", "mxfp4_silu_mul_quantize",
+                    "mxfp4_moe_combine", "mxfp4_status_string", "mxfp4_version")
 
 
 def library() -> ctypes.CDLL:
@@ -266,6 +270,55 @@ def mxfp4_linear_bf16(x, b_codes, b_scales, y=None, *, K=None, out_dtype=torch.b
     return y
 
 
+def mxfp4_silu_mul_quantize(gate_up, codes=None, scales=None, *, I=None, scale_rule="ocp",
+                            stream=None):
+    """MoE expert activation for the down projection: bf16 gate_up [M, ldg]
+    (gate = columns [0, I), up = [I, 2I)) -> MXFP4 codes [M, I/2] and E8M0
+    bytes [M, I/32] of bf16(silu(gate) * up).  I defaults to ldg // 2."""
+    _need(gate_up, "gate_up", torch.bfloat16)
+    dev = gate_up.device
+    if gate_up.dim() != 2:
+        raise ValueError("gate_up must be 2-D [rows, ldg]")
+    M, ldg = gate_up.shape
+    I = ldg // 2 if I is None else int(I)
+    if codes is None:
+        codes = torch.empty((M, I // 2), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty((M, I // 32), dtype=torch.uint8, device=dev)
+    _need(codes, "codes", torch.uint8, dev)
+    _need(scales, "scales", torch.uint8, dev)
+    if codes.shape != (M, I // 2) or scales.shape != (M, I // 32):
+        raise ValueError("output shapes do not match [M, I/2] / [M, I/32]")
+    _check("mxfp4_silu_mul_quantize", _lib.mxfp4_silu_mul_quantize(
+        _ptr(gate_up), ldg, M, I, _ptr(codes), _ptr(scales), _rule_flag(scale_rule),
+        _stream(stream, dev)))
+    return codes, scales
+
+
+def mxfp4_moe_combine(y, rows, weights, out=None, *, H=None, out_dtype=torch.bfloat16,
+                      stream=None):
+    """out [T, H] = sum_j weights[t, j] * y[rows[t, j], :H] over bf16 y [R, ldy]
+    (expert-sorted rows), int32 rows [T, topk], fp32 weights [T, topk]."""
+    _need(y, "y", torch.bfloat16)
+    dev = y.device
+    _need(rows, "rows", torch.int32, dev)
+    _need(weights, "weights", torch.float32, dev)
+    if y.dim() != 2 or rows.dim() != 2 or weights.shape != rows.shape:
+        raise ValueError("y must be [R, ldy]; rows and weights [T, topk]")
+    R, ldy = y.shape
+    T, topk = rows.shape
+    H = ldy if H is None else int(H)
+    if out is None:
+        out = torch.empty((T, H), dtype=out_dtype, device=dev)
+    _need(out, "out", out.dtype, dev)
+    if out.shape != (T, H):
+        raise ValueError("out must be [T, H]")
+    _check("mxfp4_moe_combine", _lib.mxfp4_moe_combine(
+        _ptr(y), ldy, R, _ptr(rows), _ptr(weights), T, topk, H, _ptr(out),
+        _out_dtype(out.dtype), 0, _stream(stream, dev)))
+    return out
+
+
 def mxfp4_grouped_gemm(a_codes, a_scales, b_codes, b_scales, offsets, y=None, *,
                        out_dtype=torch.bfloat16, stream=None):
     """For each expert e: y[off[e]:off[e+1]] = A[off[e]:off[e+1]] * B[e]^T.
@@ -295,7 +348,8 @@ def mxfp4_grouped_gemm(a_codes, a_scales, b_codes, b_scales, offsets, y=None, *,
 
 __all__ = ["mxfp4_requant_from_nvfp4", "mxfp4_quantize_act", "mxfp4_gemm",
            "mxfp4_grouped_gemm", "mxfp4_linear_bf16", "mxfp4_gemm_workspace_size",
-           "mxfp4_linear_workspace_size", "mxfp4_status_string",
+           "mxfp4_linear_workspace_size", "mxfp4_silu_mul_quantize", "mxfp4_moe_combine",
+           "mxfp4_status_string",
            "mxfp4_version", "Mxfp4Error", "LIBRARY_PATH", "EXPORTED_SYMBOLS",
            "MXFP4_OUT_BF16", "MXFP4_OUT_FP32", "MXFP4_REQ_INTERMEDIATE_BF16",
            "MXFP4_SCALE_UOS"]

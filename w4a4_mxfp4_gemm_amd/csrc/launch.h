@@ -20,6 +20,18 @@ hipError_t launch_requant(const uint8_t* nv_codes, const uint8_t* nv_scales,
                           uint8_t* mx_scales, bool bf16_intermediate, bool uos,
                           hipStream_t stream);
 
+// MoE expert activation + act-quant: gate_up bf16 [M][ldg] (gate = columns
+// [0, I), up = [I, 2I)) -> MXFP4 of bf16(silu(gate) * up), [M][I/2] + [M][I/32].
+hipError_t launch_silu_mul_quantize(const uint16_t* gate_up, int64_t ldg, int64_t M, int64_t I,
+                                   uint8_t* codes, uint8_t* scales, bool uos,
+                                   hipStream_t stream);
+
+// Top-k combine: out[t] = sum_j weights[t*topk+j] * y[rows[t*topk+j]] over
+// bf16 y [R][ldy], H columns, bf16 or fp32 out [T][H].
+hipError_t launch_moe_combine(const uint16_t* y, int64_t ldy, int64_t R, const int32_t* rows,
+                              const float* weights, int64_t T, int64_t topk, int64_t H,
+                              void* out, bool out_bf16, hipStream_t stream);
+
 // Act-quant and weight-streaming GEMM in one launch: x bf16 [M][ldx], for
 // the shapes and alignments linear_skinny_supported accepts
 // (linear_skinny_shape: the shape alone).

@@ -143,6 +143,37 @@ int mxfp4_linear_bf16(const void* x_bf16, int64_t ldx, int64_t M, int64_t N, int
                                     stream));
 }
 
+int mxfp4_silu_mul_quantize(const void* gate_up_bf16, int64_t ldg, int64_t M, int64_t I,
+                            uint8_t* codes, uint8_t* scales, uint32_t flags,
+                            hipStream_t stream) {
+    if (M < 0 || check_k(I) != MXFP4_OK || ldg < 2 * I) return MXFP4_EINVAL;
+    if ((flags & ~(uint32_t)MXFP4_SCALE_UOS) != 0) return MXFP4_EINVAL;
+    if (M == 0) return MXFP4_OK;
+    if (!gate_up_bf16 || !codes || !scales) return MXFP4_EINVAL;
+    if (!aligned(gate_up_bf16, 16) || ldg % 8 != 0 || !aligned(codes, 16)) return MXFP4_EALIGN;
+    return from_hip(mx::launch_silu_mul_quantize(static_cast<const uint16_t*>(gate_up_bf16),
+                                                 ldg, M, I, codes, scales,
+                                                 (flags & MXFP4_SCALE_UOS) != 0, stream));
+}
+
+int mxfp4_moe_combine(const void* y_bf16, int64_t ldy, int64_t R, const int32_t* rows,
+                      const float* weights, int64_t T, int64_t topk, int64_t H, void* out,
+                      int out_dtype, uint32_t flags, hipStream_t stream) {
+    if (T < 0 || R <= 0 || topk < 1 || topk > MXFP4_COMBINE_MAX_TOPK || H <= 0 || H % 8 != 0 ||
+        ldy < H)
+        return MXFP4_EINVAL;
+    if (out_dtype != MXFP4_OUT_BF16 && out_dtype != MXFP4_OUT_FP32) return MXFP4_EINVAL;
+    if (flags != 0) return MXFP4_EINVAL;
+    if (T == 0) return MXFP4_OK;
+    if (!y_bf16 || !rows || !weights || !out) return MXFP4_EINVAL;
+    if (!aligned(y_bf16, 16) || ldy % 8 != 0 || !aligned(out, 16) || !aligned(rows, 4) ||
+        !aligned(weights, 4))
+        return MXFP4_EALIGN;
+    return from_hip(mx::launch_moe_combine(static_cast<const uint16_t*>(y_bf16), ldy, R, rows,
+                                           weights, T, topk, H, out,
+                                           out_dtype == MXFP4_OUT_BF16, stream));
+}
+
 int mxfp4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
                        const uint8_t* b_scales, const int32_t* offsets, int64_t E,
                        int64_t total_M, int64_t N, int64_t K, void* y, int out_dtype,

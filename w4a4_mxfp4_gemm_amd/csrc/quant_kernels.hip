@@ -23,7 +23,47 @@ typedef uint32_t v4u_t __attribute__((ext_vector_type(4)));
 // ---------------------------------------------------------------------------
 // NT_OUT: codes and scales stored non-temporally (outputs too large to stay
 // cached for the GEMM that reads them next).
-template <int ROWS, bool NT_OUT, bool UOS>
+//
+// GLU: x is an MoE expert's gate_up output, gate in columns [0, K) and up in
+// [K, 2K) of each row (row_index unused), and the values quantized are
+// h = bf16(silu(gate) * up), the down projection's input (glu_pair).
+
+// e^-g to within about 2 ulp in seven operations: e^x = 2^(x log2 e), with
+// the product split into ph = fl(x * L) and its rounding error pl (recovered
+// exactly by an fma, plus the part of log2 e below fp32), so that
+// 2^(ph + pl) = exp2(ph) * (1 + pl ln 2) to second order in pl (|pl| < 2^-17).
+// x is clamped to [-104, 89], beyond which e^x is 0 or Inf in fp32 anyway, to
+// keep pl meaningful; a NaN g gives some finite value here, and NaN in the
+// caller's g * r.
+__device__ __forceinline__ float exp_neg(float g) {
+    constexpr float LOG2E_HI = 1.44269502162933349609375f;      // fp32(log2 e)
+    constexpr float LOG2E_LO = 1.925963033500011e-08f;          // log2 e - LOG2E_HI
+    constexpr float LN2 = 0.693147180559945309f;
+    const float x = __builtin_amdgcn_fmed3f(-g, -104.0f, 89.0f);
+    const float ph = x * LOG2E_HI;
+    const float pl = __builtin_fmaf(x, LOG2E_LO, __builtin_fmaf(x, LOG2E_HI, -ph));
+    return __builtin_amdgcn_exp2f(ph) * __builtin_fmaf(pl, LN2, 1.0f);
+}
+
+// silu(g) * u for the two bf16 pairs packed in gw / uw, rounded to bf16 (RNE),
+// packed the same way.  fp32 steps: e = exp(-g), d = 1 + e, r = 1/d (v_rcp,
+// 1 ulp), s = g * r, h = s * u; d >= 1 or Inf, so the reciprocal never sees
+// a denormal, and g = -Inf gives -Inf * 0 = NaN.
+__device__ __forceinline__ uint32_t glu_pair(uint32_t gw, uint32_t uw) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    const float g[2] = {__uint_as_float(gw << 16), __uint_as_float(gw & 0xFFFF0000u)};
+    const float u[2] = {__uint_as_float(uw << 16), __uint_as_float(uw & 0xFFFF0000u)};
+    float h[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const float d = 1.0f + exp_neg(g[i]);
+        h[i] = (g[i] * __builtin_amdgcn_rcpf(d)) * u[i];
+    }
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{h[0], h[1]}, bf16x2_t));
+}
+
+template <int ROWS, bool NT_OUT, bool UOS, bool GLU = false>
 __global__ __launch_bounds__(256) void act_quant_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const int32_t* __restrict__ row_index,
     int64_t M, int64_t K, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
@@ -32,13 +72,21 @@ __global__ __launch_bounds__(256) void act_quant_kernel(
     if (kq >= chunks) return;                         // whole quads leave together
     for (int64_t m0 = (int64_t)blockIdx.y * ROWS; m0 < M; m0 += (int64_t)gridDim.y * ROWS) {
         uint4 raw[ROWS];
+        uint4 up[GLU ? ROWS : 1];
 #pragma unroll
         for (int r = 0; r < ROWS; ++r) {
             const int64_t m = m0 + r;
             if (m < M) {
                 const int64_t src = row_index ? (int64_t)row_index[m] : m;
                 const uint16_t* p = x + src * ldx + kq * 8;
-                if (row_index) {
+                if constexpr (GLU) {
+                    // gate and up, both read once
+                    const v4u_t c = __builtin_nontemporal_load(reinterpret_cast<const v4u_t*>(p));
+                    const v4u_t d =
+                        __builtin_nontemporal_load(reinterpret_cast<const v4u_t*>(p + K));
+                    raw[r] = make_uint4(c[0], c[1], c[2], c[3]);
+                    up[r] = make_uint4(d[0], d[1], d[2], d[3]);
+                } else if (row_index) {
                     // a gather reads rows several times: keep them cached
                     raw[r] = *reinterpret_cast<const uint4*>(p);
                 } else {
@@ -53,7 +101,12 @@ __global__ __launch_bounds__(256) void act_quant_kernel(
         for (int r = 0; r < ROWS; ++r) {
             const int64_t m = m0 + r;
             if (m >= M) break;                        // uniform across the workgroup
-            const uint32_t w[4] = {raw[r].x, raw[r].y, raw[r].z, raw[r].w};
+            uint32_t w[4] = {raw[r].x, raw[r].y, raw[r].z, raw[r].w};
+            if constexpr (GLU) {
+                const uint32_t uv[4] = {up[r].x, up[r].y, up[r].z, up[r].w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) w[i] = glu_pair(w[i], uv[i]);
+            }
             // amax over the 8 values as bf16 magnitudes (monotone as integers;
             // NaN and Inf patterns sort above every finite value).
             u16x2 a = __builtin_bit_cast(u16x2, w[0] & 0x7FFF7FFFu);
@@ -246,6 +299,24 @@ hipError_t launch_act_quant(const uint16_t* x, int64_t ldx, const int32_t* row_i
     else
         nt_out ? go(act_quant_kernel<ROWS, true, false>)
                : go(act_quant_kernel<ROWS, false, false>);
+    return hipGetLastError();
+}
+
+hipError_t launch_silu_mul_quantize(const uint16_t* gate_up, int64_t ldg, int64_t M, int64_t I,
+                                   uint8_t* codes, uint8_t* scales, bool uos,
+                                   hipStream_t stream) {
+    constexpr int ROWS = 2;
+    const int64_t gx = (I / 8 + 255) / 256;
+    int64_t gy = (M + ROWS - 1) / ROWS;
+    if (gy > 65535) gy = 65535;
+    const dim3 grid((unsigned)gx, (unsigned)gy);
+    // the codes feed the down GEMM next: normal stores
+    if (uos)
+        hipLaunchKernelGGL((act_quant_kernel<ROWS, false, true, true>), grid, dim3(256), 0,
+                           stream, gate_up, ldg, nullptr, M, I, codes, scales);
+    else
+        hipLaunchKernelGGL((act_quant_kernel<ROWS, false, false, true>), grid, dim3(256), 0,
+                           stream, gate_up, ldg, nullptr, M, I, codes, scales);
     return hipGetLastError();
 }
 
