@@ -96,6 +96,8 @@ def _load():
     lib.orc_silu_mul_quantize.argtypes = [P, I, I, I, ctypes.c_int, P, P]
     lib.orc_moe_combine.restype = None
     lib.orc_moe_combine.argtypes = [P, I, P, P, I, I, I, P, P]
+    lib.orc_add_row_bias.restype = None
+    lib.orc_add_row_bias.argtypes = [P, P, I, I, P]
     lib.orc_bf16_from_double_array.restype = None
     lib.orc_bf16_from_double_array.argtypes = [P, I, P]
     lib.orc_num_threads.restype = ctypes.c_int
@@ -271,6 +273,19 @@ def grouped_gemm(a_codes, a_scales, b_codes, b_scales, offsets):
     s = np.zeros((M, N), dtype=np.float64)
     _load().orc_grouped_gemm(_ptr(a_codes), _ptr(a_scales), _ptr(b_codes),
                              _ptr(b_scales), _ptr(offsets), E, N, K, _ptr(y), _ptr(s))
+    return y, s
+
+
+def add_row_bias(y, s, bias_bits):
+    """R12: (y + bias[n], s + |bias[n]|) for an [M, N] GEMM result (y, s) and
+    bf16 bias bits [N].  Returns new arrays."""
+    y = np.array(y, dtype=np.float64, order="C", copy=True)
+    s = np.array(s, dtype=np.float64, order="C", copy=True)
+    bias_bits = _c(bias_bits, np.uint16)
+    M, N = y.shape
+    assert s.shape == (M, N) and bias_bits.shape == (N,)
+    if M and N:
+        _load().orc_add_row_bias(_ptr(y), _ptr(s), M, N, _ptr(bias_bits))
     return y, s
 
 

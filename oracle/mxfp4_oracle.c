@@ -474,6 +474,20 @@ void orc_moe_combine(const uint16_t* y, int64_t ldy, const int32_t* rows, const 
     }
 }
 
+/* R12: the row bias joins the exact sum before any rounding (one fp64 add of
+   a bf16 value; its rounding error is far below the output's). */
+void orc_add_row_bias(double* y, double* s, int64_t M, int64_t N, const uint16_t* bias)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            double b = orc_bf16_value(bias[n]);
+            y[m * N + n] += b;
+            if (s) s[m * N + n] += fabs(b);
+        }
+    }
+}
+
 /* Elementwise helper for the tests: RNE of n doubles to bf16 bit patterns. */
 void orc_bf16_from_double_array(const double* v, int64_t n, uint16_t* out)
 {

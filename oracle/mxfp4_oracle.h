@@ -53,6 +53,10 @@
  *      h = fl32(s * u).  A GPU exp or reciprocal that is not correctly
  *      rounded can move h by a few fp32 ulps, so where h lies that close to
  *      a bf16 rounding midpoint either neighbour is a correct result.
+ *   R12 row bias ([P3] NVFP4 apply_weights: the GEMM output plus an optional
+ *      bias; [P2] W4A8 notes: bf16 output with a matching bf16 row bias): y
+ *      gains bias[n] on every row, one bias per weight row (output column),
+ *      added to the exact sum before the single rounding to the output type.
  *   R11 top-k combine ([P1] closing list, MoE experts): each token's output
  *      row is the sum over its k routed rows of weight * expert output row,
  *      computed exactly (fp64) and rounded once to the output type.  The
@@ -144,6 +148,10 @@ void orc_silu_mul_quantize(const uint16_t* gate_up, int64_t ldg, int64_t M, int6
    s[t][n] = sum_j |w * y| (R11); y is bf16 [*][ldy]; s may be NULL. */
 void orc_moe_combine(const uint16_t* y, int64_t ldy, const int32_t* rows, const float* w,
                      int64_t T, int64_t topk, int64_t H, double* out, double* s);
+
+/* R12: y[m][n] += bf16 bias[n] and s[m][n] += |bias[n]| (s may be NULL), over
+   an [M][N] result of orc_gemm. */
+void orc_add_row_bias(double* y, double* s, int64_t M, int64_t N, const uint16_t* bias);
 
 void orc_bf16_from_double_array(const double* v, int64_t n, uint16_t* out);
 int  orc_num_threads(void);

@@ -640,3 +640,29 @@ def test_combine_order_and_linearity_invariants():
     pos_bits = bits & np.uint16(0x7FFF)
     o3, s3 = oracle.moe_combine(pos_bits, rows, w)
     assert np.array_equal(o3, s3)
+
+
+# ---- R12: row bias ------------------------------------------------------------------
+def test_row_bias_closed_forms():
+    """All activation codes zero: the result is the bias itself, on every row;
+    a zero bias changes nothing; the bias is one value per weight row (output
+    column), not per activation row; s grows by |bias|."""
+    rng = np.random.default_rng(120)
+    M, N, K = 5, 24, 64
+    bc = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    bs = rng.integers(120, 135, (N, K // 32), dtype=np.uint8)
+    ac = np.zeros((M, K // 2), dtype=np.uint8)
+    as_ = np.full((M, K // 32), 127, dtype=np.uint8)
+    bias = bf16_bits(torch.from_numpy(rng.normal(0, 3, N).astype(np.float32)).to(torch.bfloat16))
+    bval = torch.from_numpy(bias.view(np.int16)).view(torch.bfloat16).double().numpy()
+    y0, s0 = oracle.gemm(ac, as_, bc, bs)
+    y, s = oracle.add_row_bias(y0, s0, bias)
+    assert np.array_equal(y, np.broadcast_to(bval, (M, N)))
+    assert np.array_equal(s, np.broadcast_to(np.abs(bval), (M, N)))
+    ac = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
+    y1, s1 = oracle.gemm(ac, as_, bc, bs)
+    yz, sz = oracle.add_row_bias(y1, s1, np.zeros(N, dtype=np.uint16))
+    assert np.array_equal(yz, y1) and np.array_equal(sz, s1)
+    yb, _ = oracle.add_row_bias(y1, s1, bias)
+    # scales 127 on A and B bytes in [120, 135): every term and sum is exact
+    assert np.array_equal(yb - y1, np.broadcast_to(bval, (M, N)))
