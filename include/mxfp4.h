@@ -179,7 +179,10 @@ size_t mxfp4_gemm_workspace_size(int64_t M, int64_t N, int64_t K);
 /*
  * One linear layer on bf16 activations: the MXFP4 quantization of
  * mxfp4_quantize_act (row i of x, no gather) followed by mxfp4_gemm with B,
- * giving the same y bit for bit.  For decode-shaped calls (M <= 16, K = 2048
+ * giving the same y bit for bit, plus an optional row bias (the SGLang FP4
+ * post's apply_weights: quantize, GEMM, add bias; the vLLM-Omni guide's
+ * W4A4/W4A8 notes: bf16 output with a bf16 row bias).  The bias joins each
+ * fp32 sum before its one rounding: y[m][n] = round(sum_k A B + bias[n]).  For decode-shaped calls (M <= 16, K = 2048
  * or 4096, N >= 16, 16-byte-aligned b_scales) it is one launch whose
  * workgroups quantize their own activation blocks while their weight loads
  * stream; otherwise the two launches run through the caller's workspace.
@@ -187,6 +190,7 @@ size_t mxfp4_gemm_workspace_size(int64_t M, int64_t N, int64_t K);
  *   x_bf16      [M][ldx] bf16, device, read (16-byte aligned, ldx % 8 == 0,
  *               ldx >= K)
  *   b_codes, b_scales, y, out_dtype   as for mxfp4_gemm
+ *   bias_bf16   [N] bf16, device, read, 16-byte aligned; or NULL for none
  *   workspace   device memory of at least mxfp4_linear_workspace_size(M, N,
  *               K) bytes (16-byte aligned; may be NULL when that is 0):
  *               the quantized activations of the two-launch form
@@ -195,8 +199,8 @@ size_t mxfp4_gemm_workspace_size(int64_t M, int64_t N, int64_t K);
  * the two-launch form needs when that form is taken.
  */
 int mxfp4_linear_bf16(const void* x_bf16, int64_t ldx, int64_t M, int64_t N, int64_t K,
-                      const uint8_t* b_codes, const uint8_t* b_scales, void* y,
-                      int out_dtype, void* workspace, size_t workspace_bytes,
+                      const uint8_t* b_codes, const uint8_t* b_scales, const void* bias_bf16,
+                      void* y, int out_dtype, void* workspace, size_t workspace_bytes,
                       uint32_t flags, hipStream_t stream);
 
 /* Workspace bytes mxfp4_linear_bf16 needs: 0 for the one-launch shapes. */

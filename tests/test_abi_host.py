@@ -133,20 +133,23 @@ def test_requant_subset_argument_checks(lib):
 
 def test_linear_argument_checks(lib):
     f = lib.mxfp4_linear_bf16
-    #        x    ldx  M  N    K     b_codes b_scales y    dtype ws   ws_bytes flags stream
-    assert f(FAKE, 4000, 1, 256, 4096, FAKE, FAKE, FAKE, 0, None, 0, 0, None) == -1   # ldx < K
-    assert f(FAKE, 4096, 1, 256, 4080, FAKE, FAKE, FAKE, 0, None, 0, 0, None) == -1   # K % 32
-    assert f(FAKE, 4096, 1, 0, 4096, FAKE, FAKE, FAKE, 0, None, 0, 0, None) == -1      # N
-    assert f(FAKE, 4096, 1, 256, 4096, FAKE, FAKE, FAKE, 7, None, 0, 0, None) == -1    # out_dtype
-    assert f(FAKE, 4096, 1, 256, 4096, FAKE, FAKE, FAKE, 0, None, 0, 1, None) == -1    # flags
-    assert f(FAKE, 4096, 0, 256, 4096, FAKE, FAKE, FAKE, 0, None, 0, 2, None) == 0     # UOS
-    assert f(FAKE, 4096, 1, 256, 4096, FAKE, FAKE, FAKE, 0, None, 64, 0, None) == -1   # ws NULL
-    assert f(None, 4096, 1, 256, 4096, FAKE, FAKE, FAKE, 0, None, 0, 0, None) == -1
-    assert f(ODD, 4096, 1, 256, 4096, FAKE, FAKE, FAKE, 0, None, 0, 0, None) == -2
-    assert f(FAKE, 4100, 1, 256, 4096, FAKE, FAKE, FAKE, 0, None, 0, 0, None) == -2    # ldx % 8
-    assert f(FAKE, 4096, 0, 256, 4096, FAKE, FAKE, FAKE, 0, None, 0, 0, None) == 0     # M == 0
+    #        x    ldx  M  N    K     b_codes b_scales bias y  dtype ws  ws_bytes flags stream
+    assert f(FAKE, 4000, 1, 256, 4096, FAKE, FAKE, None, FAKE, 0, None, 0, 0, None) == -1   # ldx < K
+    assert f(FAKE, 4096, 1, 256, 4080, FAKE, FAKE, None, FAKE, 0, None, 0, 0, None) == -1   # K % 32
+    assert f(FAKE, 4096, 1, 0, 4096, FAKE, FAKE, None, FAKE, 0, None, 0, 0, None) == -1      # N
+    assert f(FAKE, 4096, 1, 256, 4096, FAKE, FAKE, None, FAKE, 7, None, 0, 0, None) == -1    # out_dtype
+    assert f(FAKE, 4096, 1, 256, 4096, FAKE, FAKE, None, FAKE, 0, None, 0, 1, None) == -1    # flags
+    assert f(FAKE, 4096, 0, 256, 4096, FAKE, FAKE, None, FAKE, 0, None, 0, 2, None) == 0     # UOS
+    assert f(FAKE, 4096, 1, 256, 4096, FAKE, FAKE, None, FAKE, 0, None, 64, 0, None) == -1   # ws NULL
+    assert f(None, 4096, 1, 256, 4096, FAKE, FAKE, None, FAKE, 0, None, 0, 0, None) == -1
+    assert f(ODD, 4096, 1, 256, 4096, FAKE, FAKE, None, FAKE, 0, None, 0, 0, None) == -2
+    assert f(FAKE, 4100, 1, 256, 4096, FAKE, FAKE, None, FAKE, 0, None, 0, 0, None) == -2    # ldx % 8
+    assert f(FAKE, 4096, 0, 256, 4096, FAKE, FAKE, None, FAKE, 0, None, 0, 0, None) == 0     # M == 0
     # the two-launch form needs its workspace
-    assert f(FAKE, 1024, 200, 256, 1024, FAKE, FAKE, FAKE, 0, None, 0, 0, None) == -1
+    assert f(FAKE, 1024, 200, 256, 1024, FAKE, FAKE, None, FAKE, 0, None, 0, 0, None) == -1
+    # a misaligned bias is refused before anything is launched
+    assert f(FAKE, 4096, 1, 256, 4096, FAKE, FAKE, ODD, FAKE, 0, None, 0, 0, None) == -2
+    assert f(FAKE, 4096, 0, 256, 4096, FAKE, FAKE, FAKE, FAKE, 0, None, 0, 0, None) == 0
 
 
 def test_linear_workspace_size(lib):

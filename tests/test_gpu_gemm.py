@@ -486,3 +486,36 @@ def test_linear_bf16_uos_against_oracle(mx):
     ac, as_ = oracle.quantize_act(bf16_bits(x), scale_rule="uos")
     y, s = oracle.gemm(ac, as_, oc, os_)
     assert_gemm_fp32(y32, y, s, "linear uos fp32")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1000, 4096), (8, 2048, 4096), (5, 300, 2048),
+                                   (33, 1040, 2048), (100, 300, 1024), (150, 260, 800),
+                                   (300, 1000, 1024), (4096, 8192, 4096)])
+def test_linear_bf16_row_bias(mx, M, N, K):
+    """A bf16 row bias through every GEMM path (one-launch decode, skinny,
+    generic, tiled with a ragged N, persistent), against the oracle's act-quant,
+    requant and GEMM plus the bias before the one rounding.  Sizes the oracle
+    cannot finish whole are checked on sampled rows."""
+    say(f"linear bf16 + bias M={M} N={N} K={K}")
+    x = synth.activations(M, K, seed=M + 7, outlier_seed=K + 7)
+    w = synth.bf16_normal((N, K), 0.02, seed=N + 7)
+    codes, scales, g = synth.nvfp4_from_bf16(w)
+    bias = (torch.randn(N, generator=torch.Generator().manual_seed(N)) * 2).to(torch.bfloat16)
+    wc, ws = mx.mxfp4_requant_from_nvfp4(codes.to(dev()), scales.to(dev()), g.reshape(1).to(dev()))
+    oc, os_ = oracle.requant(u8(codes), u8(scales), np.atleast_1d(g.numpy()))
+    ac, as_ = oracle.quantize_act(bf16_bits(x))
+    rows = np.arange(M) if M * N <= 2_000_000 else np.unique(
+        np.concatenate([[0, M - 1], np.random.default_rng(1).integers(0, M, 24)]))
+    pm, pn = np.repeat(rows, N), np.tile(np.arange(N), rows.size)
+    y, s = oracle.gemm_at(ac, as_, oc, os_, pm, pn)
+    y, s = oracle.add_row_bias(y.reshape(rows.size, N), s.reshape(rows.size, N), bf16_bits(bias))
+    for dt in (torch.float32, torch.bfloat16):
+        gy = Guarded((M, N), dt)
+        mx.mxfp4_linear_bf16(x.to(dev()), wc, ws, gy.view, bias=bias.to(dev()))
+        torch.cuda.synchronize()
+        assert gy.intact(), "write outside y"
+        got = gy.view[torch.from_numpy(rows).to(dev())]
+        if dt == torch.float32:
+            assert_gemm_fp32(got, y, s, f"bias fp32 M={M}")
+        else:
+            assert_gemm_bf16(got, y, f"bias bf16 M={M}")

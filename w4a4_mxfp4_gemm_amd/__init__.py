@@ -48,7 +48,7 @@ def _load_library() -> ctypes.CDLL:
     lib.mxfp4_gemm.restype = ctypes.c_int
     lib.mxfp4_grouped_gemm.argtypes = [P, P, P, P, P, I, I, I, I, P, ctypes.c_int, P, SZ, U32, P]
     lib.mxfp4_grouped_gemm.restype = ctypes.c_int
-    lib.mxfp4_linear_bf16.argtypes = [P, I, I, I, I, P, P, P, ctypes.c_int, P, SZ, U32, P]
+    lib.mxfp4_linear_bf16.argtypes = [P, I, I, I, I, P, P, P, P, ctypes.c_int, P, SZ, U32, P]
     lib.mxfp4_linear_bf16.restype = ctypes.c_int
     lib.mxfp4_silu_mul_quantize.argtypes = [P, I, I, I, P, P, U32, P]
     lib.mxfp4_silu_mul_quantize.restype = ctypes.c_int
@@ -237,12 +237,13 @@ def mxfp4_linear_workspace_size(M: int, N: int, K: int) -> int:
     return int(_lib.mxfp4_linear_workspace_size(M, N, K))
 
 
-def mxfp4_linear_bf16(x, b_codes, b_scales, y=None, *, K=None, out_dtype=torch.bfloat16,
-                      workspace=None, scale_rule="ocp", stream=None):
+def mxfp4_linear_bf16(x, b_codes, b_scales, y=None, *, bias=None, K=None,
+                      out_dtype=torch.bfloat16, workspace=None, scale_rule="ocp", stream=None):
     """y [M, N] = MXFP4(x) [M, K] * B [N, K]^T from bf16 x [M, ldx] (the act-quant
     call followed by the GEMM, bit for bit; one launch for decode shapes).  K
     defaults to x's row length.  A workspace of mxfp4_linear_workspace_size
-    bytes is allocated when none is given and one is needed.  scale_rule: the
+    bytes is allocated when none is given and one is needed.  bias: bf16 [N],
+    added to each fp32 sum before the output rounding.  scale_rule: the
     activations' rule, "ocp" or "uos"."""
     _need(x, "x", torch.bfloat16)
     dev = x.device
@@ -255,6 +256,10 @@ def mxfp4_linear_bf16(x, b_codes, b_scales, y=None, *, K=None, out_dtype=torch.b
     N = b_codes.shape[0]
     if b_codes.shape != (N, K // 2) or b_scales.shape != (N, K // 32):
         raise ValueError("operand shapes disagree")
+    if bias is not None:
+        _need(bias, "bias", torch.bfloat16, dev)
+        if bias.shape != (N,):
+            raise ValueError("bias must be [N]")
     if y is None:
         y = torch.empty((M, N), dtype=out_dtype, device=dev)
     _need(y, "y", y.dtype, dev)
@@ -265,7 +270,8 @@ def mxfp4_linear_bf16(x, b_codes, b_scales, y=None, *, K=None, out_dtype=torch.b
         workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
     ws_ptr, ws_bytes = (None, 0) if workspace is None else (_ptr(workspace), workspace.numel())
     _check("mxfp4_linear_bf16", _lib.mxfp4_linear_bf16(
-        _ptr(x), ldx, M, N, K, _ptr(b_codes), _ptr(b_scales), _ptr(y), _out_dtype(y.dtype),
+        _ptr(x), ldx, M, N, K, _ptr(b_codes), _ptr(b_scales), _ptr(bias), _ptr(y),
+        _out_dtype(y.dtype),
         ws_ptr, ws_bytes, _rule_flag(scale_rule), _stream(stream, dev)))
     return y
 

@@ -80,7 +80,8 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a_codes,
                                           const uint8_t* __restrict__ b_codes,
                                           const uint8_t* __restrict__ b_scales, int64_t m0,
                                           int64_t m_end, int64_t n0_wg, int64_t N, int64_t K,
-                                          void* __restrict__ y) {
+                                          void* __restrict__ y,
+                                          const uint16_t* __restrict__ bias) {
     constexpr int WAVES_N = 4 / KSPLIT;
     static_assert(WAVES_N * KSPLIT == 4, "4 wavefronts per workgroup");
     const int lane = threadIdx.x & 63;
@@ -146,15 +147,17 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a_codes,
         for (int j = 0; j < WN; ++j) {
             const int64_t n = n0 + 16 * j + r16;
             if (n >= N) continue;
+            // the row bias joins the fp32 sum before its one rounding
+            const float bn = bias ? __uint_as_float((uint32_t)bias[n] << 16) : 0.f;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int64_t m = m0 + 16 * i + 4 * g + r;
                 if (m >= m_end) continue;
+                const float v = bias ? acc[i][j][r] + bn : acc[i][j][r];
                 if (OUT_BF16)
-                    reinterpret_cast<uint16_t*>(y)[m * N + n] =
-                        (uint16_t)f32_to_bf16_rne(acc[i][j][r]);
+                    reinterpret_cast<uint16_t*>(y)[m * N + n] = (uint16_t)f32_to_bf16_rne(v);
                 else
-                    reinterpret_cast<float*>(y)[m * N + n] = acc[i][j][r];
+                    reinterpret_cast<float*>(y)[m * N + n] = v;
             }
         }
 }
@@ -165,12 +168,13 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ a
                                                    const uint8_t* __restrict__ b_codes,
                                                    const uint8_t* __restrict__ b_scales,
                                                    int64_t M, int64_t N, int64_t K,
-                                                   void* __restrict__ y) {
+                                                   void* __restrict__ y,
+                                                   const uint16_t* __restrict__ bias) {
     constexpr int TN = 16 * WN * (4 / KSPLIT);
     const int64_t m0 = (int64_t)blockIdx.y * 16 * WM;
     const int64_t n0 = (int64_t)blockIdx.x * TN;
     gemm_tile<WM, WN, KSPLIT, OUT_BF16>(a_codes, a_scales, b_codes, b_scales, m0, M, n0, N, K,
-                                        y);
+                                        y, bias);
 }
 
 // Grouped variant: blockIdx.y enumerates the row tiles of all experts in
@@ -204,45 +208,45 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(
     const int64_t n0 = (int64_t)blockIdx.x * TN;
     const int64_t nkb = K / 32;
     gemm_tile<WM, WN, KSPLIT, OUT_BF16>(a_codes, a_scales, b_codes + e * N * nkb * 16,
-                                        b_scales + e * N * nkb, r0, r1, n0, N, K, y);
+                                        b_scales + e * N * nkb, r0, r1, n0, N, K, y, nullptr);
 }
 
 template <int WM, int WN, int KSPLIT>
 static hipError_t launch_dense(const uint8_t* a, const uint8_t* as, const uint8_t* b,
                                const uint8_t* bs, int64_t M, int64_t N, int64_t K, void* y,
-                               bool out_bf16, hipStream_t stream) {
+                               const uint16_t* bias, bool out_bf16, hipStream_t stream) {
     constexpr int TM = 16 * WM;
     constexpr int TN = 16 * WN * (4 / KSPLIT);
     const dim3 grid((unsigned)((N + TN - 1) / TN), (unsigned)((M + TM - 1) / TM));
     if (out_bf16)
         hipLaunchKernelGGL((gemm_kernel<WM, WN, KSPLIT, true>), grid, dim3(256), 0, stream, a, as,
-                           b, bs, M, N, K, y);
+                           b, bs, M, N, K, y, bias);
     else
         hipLaunchKernelGGL((gemm_kernel<WM, WN, KSPLIT, false>), grid, dim3(256), 0, stream, a,
-                           as, b, bs, M, N, K, y);
+                           as, b, bs, M, N, K, y, bias);
     return hipGetLastError();
 }
 
 hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
                        const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, void* y,
-                       bool out_bf16, hipStream_t stream) {
+                       const uint16_t* bias, bool out_bf16, hipStream_t stream) {
     if (skinny_gemm_supported(M, N, K, a_codes, a_scales, b_scales))
-        return launch_gemm_skinny(a_codes, a_scales, b_codes, b_scales, M, N, K, y, out_bf16,
-                                  stream);
+        return launch_gemm_skinny(a_codes, a_scales, b_codes, b_scales, M, N, K, y, bias,
+                                  out_bf16, stream);
     if (tiled_gemm_supported(M, N, K, a_scales, b_scales))
-        return launch_gemm_tiled(a_codes, a_scales, b_codes, b_scales, M, N, K, y, out_bf16,
-                                 stream);
+        return launch_gemm_tiled(a_codes, a_scales, b_codes, b_scales, M, N, K, y, bias,
+                                 out_bf16, stream);
     if (M <= 16)
-        return launch_dense<1, 1, 4>(a_codes, a_scales, b_codes, b_scales, M, N, K, y, out_bf16,
-                                     stream);
+        return launch_dense<1, 1, 4>(a_codes, a_scales, b_codes, b_scales, M, N, K, y, bias,
+                                     out_bf16, stream);
     if (M <= 32)
-        return launch_dense<2, 1, 4>(a_codes, a_scales, b_codes, b_scales, M, N, K, y, out_bf16,
-                                     stream);
+        return launch_dense<2, 1, 4>(a_codes, a_scales, b_codes, b_scales, M, N, K, y, bias,
+                                     out_bf16, stream);
     if (M <= 64)
-        return launch_dense<4, 1, 4>(a_codes, a_scales, b_codes, b_scales, M, N, K, y, out_bf16,
-                                     stream);
-    return launch_dense<2, 2, 1>(a_codes, a_scales, b_codes, b_scales, M, N, K, y, out_bf16,
-                                 stream);
+        return launch_dense<4, 1, 4>(a_codes, a_scales, b_codes, b_scales, M, N, K, y, bias,
+                                     out_bf16, stream);
+    return launch_dense<2, 2, 1>(a_codes, a_scales, b_codes, b_scales, M, N, K, y, bias,
+                                 out_bf16, stream);
 }
 
 hipError_t launch_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales,

@@ -149,7 +149,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_skinny_kernel(
     // across the points that order them (below the first MFMA, or the bf16
     // activation loads behind the weight loads), serialising the latencies
     const uint8_t* x, const uint8_t* xs, int64_t ldx, const uint8_t* w, const uint8_t* ws,
-    int M, int N, int K, void* __restrict__ y) {
+    int M, int N, int K, void* __restrict__ y, const uint16_t* __restrict__ bias) {
     __shared__ __attribute__((aligned(16))) Smem<MT, NW> sm;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -230,6 +230,17 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_skinny_kernel(
 #pragma unroll
             for (int q = 1; q < NW; ++q) v += sm.red[buf][q][mt][lane];
             if (m >= M) continue;
+            if (bias) {   // the row bias joins the fp32 sum before its one rounding
+                if (n + 3 < N) {
+                    const uint2 b = *reinterpret_cast<const uint2*>(bias + n);
+                    v += v4f{__uint_as_float(b.x << 16), __uint_as_float(b.x & 0xFFFF0000u),
+                             __uint_as_float(b.y << 16), __uint_as_float(b.y & 0xFFFF0000u)};
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (n + r < N) v[r] += __uint_as_float((uint32_t)bias[n + r] << 16);
+                }
+            }
             if (OUT_BF16) {
                 uint16_t* yr = reinterpret_cast<uint16_t*>(y) + (int64_t)m * N;
                 if (n + 3 < N && (N % 4) == 0 && (reinterpret_cast<uintptr_t>(y) % 8) == 0) {
@@ -296,7 +307,8 @@ bool linear_skinny_supported(int64_t M, int64_t N, int64_t K, const void* x, int
 template <int MT, int SPW, int NW>
 static hipError_t launch_mt(const uint8_t* a, const uint8_t* as, int64_t ldx, const uint8_t* b,
                             const uint8_t* bs, int64_t M, int64_t N, int64_t K, void* y,
-                            bool out_bf16, hipStream_t stream, bool uos = false) {
+                            const uint16_t* bias, bool out_bf16, hipStream_t stream,
+                            bool uos = false) {
     // tiles in flight per wave: all of a workgroup's tiles when they fit
     constexpr int TPW = 3;
     const int ntiles = (int)((N + 15) / 16);
@@ -304,7 +316,7 @@ static hipError_t launch_mt(const uint8_t* a, const uint8_t* as, int64_t ldx, co
     if (grid > 256) grid = 256;
     auto go = [&](auto kernel) {
         hipLaunchKernelGGL(kernel, dim3(grid), dim3(64 * NW), 0, stream, a, as, ldx, b, bs,
-                           (int)M, (int)N, (int)K, y);
+                           (int)M, (int)N, (int)K, y, bias);
         return hipGetLastError();
     };
     using namespace skinny;
@@ -328,42 +340,48 @@ static hipError_t launch_mt(const uint8_t* a, const uint8_t* as, int64_t ldx, co
 template <int NW4096>
 static hipError_t launch_k(const uint8_t* a, const uint8_t* as, int64_t ldx, const uint8_t* b,
                            const uint8_t* bs, int64_t M, int64_t N, int64_t K, void* y,
-                           bool out_bf16, hipStream_t stream) {
+                           const uint16_t* bias, bool out_bf16, hipStream_t stream) {
     constexpr int SPW = 8 / NW4096;
     if (K == 2048) {
-        if (M <= 16) return launch_mt<1, 1, 4>(a, as, ldx, b, bs, M, N, K, y, out_bf16, stream);
-        if (M <= 32) return launch_mt<2, 1, 4>(a, as, ldx, b, bs, M, N, K, y, out_bf16, stream);
-        if (M <= 48) return launch_mt<3, 1, 4>(a, as, ldx, b, bs, M, N, K, y, out_bf16, stream);
-        return launch_mt<4, 1, 4>(a, as, ldx, b, bs, M, N, K, y, out_bf16, stream);
+        if (M <= 16)
+            return launch_mt<1, 1, 4>(a, as, ldx, b, bs, M, N, K, y, bias, out_bf16, stream);
+        if (M <= 32)
+            return launch_mt<2, 1, 4>(a, as, ldx, b, bs, M, N, K, y, bias, out_bf16, stream);
+        if (M <= 48)
+            return launch_mt<3, 1, 4>(a, as, ldx, b, bs, M, N, K, y, bias, out_bf16, stream);
+        return launch_mt<4, 1, 4>(a, as, ldx, b, bs, M, N, K, y, bias, out_bf16, stream);
     }
     if (M <= 16)
-        return launch_mt<1, SPW, NW4096>(a, as, ldx, b, bs, M, N, K, y, out_bf16, stream);
+        return launch_mt<1, SPW, NW4096>(a, as, ldx, b, bs, M, N, K, y, bias, out_bf16, stream);
     if (M <= 32)
-        return launch_mt<2, SPW, NW4096>(a, as, ldx, b, bs, M, N, K, y, out_bf16, stream);
+        return launch_mt<2, SPW, NW4096>(a, as, ldx, b, bs, M, N, K, y, bias, out_bf16, stream);
     if (M <= 48)
-        return launch_mt<3, SPW, NW4096>(a, as, ldx, b, bs, M, N, K, y, out_bf16, stream);
-    return launch_mt<4, SPW, NW4096>(a, as, ldx, b, bs, M, N, K, y, out_bf16, stream);
+        return launch_mt<3, SPW, NW4096>(a, as, ldx, b, bs, M, N, K, y, bias, out_bf16, stream);
+    return launch_mt<4, SPW, NW4096>(a, as, ldx, b, bs, M, N, K, y, bias, out_bf16, stream);
 }
 
 // two wavefronts per SIMD (at K = 4096; measured 0.3-0.5 us less than one
 // per SIMD at every M)
 hipError_t launch_gemm_skinny(const uint8_t* a_codes, const uint8_t* a_scales,
                               const uint8_t* b_codes, const uint8_t* b_scales, int64_t M,
-                              int64_t N, int64_t K, void* y, bool out_bf16, hipStream_t stream) {
-    return launch_k<8>(a_codes, a_scales, 0, b_codes, b_scales, M, N, K, y, out_bf16, stream);
+                              int64_t N, int64_t K, void* y, const uint16_t* bias,
+                              bool out_bf16, hipStream_t stream) {
+    return launch_k<8>(a_codes, a_scales, 0, b_codes, b_scales, M, N, K, y, bias, out_bf16,
+                       stream);
 }
 
 hipError_t launch_linear_skinny(const uint16_t* x, int64_t ldx, const uint8_t* b_codes,
                                 const uint8_t* b_scales, int64_t M, int64_t N, int64_t K,
-                                void* y, bool out_bf16, bool uos, hipStream_t stream) {
+                                void* y, const uint16_t* bias, bool out_bf16, bool uos,
+                                hipStream_t stream) {
     // M <= 16: one activation block; one super-step per wave (eight waves at
     // K = 4096, four at 2048)
     const uint8_t* a = reinterpret_cast<const uint8_t*>(x);
     if (K == 4096)
-        return launch_mt<1, 1, 8>(a, nullptr, ldx, b_codes, b_scales, M, N, K, y, out_bf16,
+        return launch_mt<1, 1, 8>(a, nullptr, ldx, b_codes, b_scales, M, N, K, y, bias, out_bf16,
                                   stream, uos);
-    return launch_mt<1, 1, 4>(a, nullptr, ldx, b_codes, b_scales, M, N, K, y, out_bf16, stream,
-                              uos);
+    return launch_mt<1, 1, 4>(a, nullptr, ldx, b_codes, b_scales, M, N, K, y, bias, out_bf16,
+                              stream, uos);
 }
 
 }  // namespace mx

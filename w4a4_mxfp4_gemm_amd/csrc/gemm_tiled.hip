@@ -61,6 +61,7 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int BKB = 128;                     // code bytes per row per stage (256 K)
 constexpr int SCALE_OPERAND = 256 * 16;      // 4 KiB: 256 rows x 16 B
@@ -399,10 +400,27 @@ struct Stage {
 // region, and one wave's LDS instructions take effect in issue order, so the
 // passes need only compiler fences: a read after the parking writes sees
 // them, and the next pass's writes cannot overtake this pass's reads.
-template <class S, bool OUT_BF16, int ROWS>
+// bf16 bias[col .. col+3] as fp32 (0 past N); col is a multiple of 4, so the
+// four values are one aligned 8-byte load when all are inside.
+__device__ __forceinline__ v4f bias4(const uint16_t* __restrict__ bias, int64_t col, int64_t N) {
+    if (col + 3 < N) {
+        const v2u b = *reinterpret_cast<const v2u*>(bias + col);
+        return v4f{__uint_as_float(b[0] << 16), __uint_as_float(b[0] & 0xFFFF0000u),
+                   __uint_as_float(b[1] << 16), __uint_as_float(b[1] & 0xFFFF0000u)};
+    }
+    v4f r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        r[e] = col + e < N ? __uint_as_float((uint32_t)bias[col + e] << 16) : 0.f;
+    return r;
+}
+
+// BIAS: bias[n] (bf16) joins each fp32 sum before its one rounding.
+template <class S, bool OUT_BF16, int ROWS, bool BIAS = false>
 __device__ __forceinline__ void store_tile(const v16f (&acc)[S::NB][S::MB], lds_u8* stage,
                                            void* __restrict__ y, int64_t m0, int64_t m_end,
-                                           int64_t n0, int64_t N, int wn, int wm) {
+                                           int64_t n0, int64_t N, int wn, int wm,
+                                           const uint16_t* __restrict__ bias = nullptr) {
     using T = Stage<S, OUT_BF16>;
     static_assert(ROWS >= 2 && ROWS <= 32 && (ROWS & (ROWS - 1)) == 0, "a 32-row block in passes");
     static_assert((ROWS * T::CHUNKS) % 64 == 0, "whole instructions per pass");
@@ -428,8 +446,12 @@ __device__ __forceinline__ void store_tile(const v16f (&acc)[S::NB][S::MB], lds_
 #pragma unroll
                     for (int b = 0; b < 4; ++b) {
                         lds_u8* dst = stage + r * T::PITCH + (32 * i + 8 * b + 4 * h) * T::ESIZE;
-                        const float v0 = acc[i][j][4 * b], v1 = acc[i][j][4 * b + 1];
-                        const float v2 = acc[i][j][4 * b + 2], v3 = acc[i][j][4 * b + 3];
+                        float v0 = acc[i][j][4 * b], v1 = acc[i][j][4 * b + 1];
+                        float v2 = acc[i][j][4 * b + 2], v3 = acc[i][j][4 * b + 3];
+                        if constexpr (BIAS) {
+                            const v4f bv = bias4(bias, col0 + 32 * i + 8 * b + 4 * h, N);
+                            v0 += bv[0], v1 += bv[1], v2 += bv[2], v3 += bv[3];
+                        }
                         if (OUT_BF16)
                             *reinterpret_cast<__attribute__((address_space(3))) v2u*>(dst) =
                                 v2u{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
@@ -655,11 +677,11 @@ __device__ __forceinline__ bool tile_coords(int tiles_m, int tiles_n, int gm, in
     return true;
 }
 
-template <bool OUT_BF16>
+template <bool OUT_BF16, bool BIAS>
 __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(
     const uint8_t* __restrict__ x, const uint8_t* __restrict__ xs,
     const uint8_t* __restrict__ w, const uint8_t* __restrict__ ws, int64_t M, int64_t N,
-    int64_t K, void* __restrict__ y, int gm) {
+    int64_t K, void* __restrict__ y, int gm, const uint16_t* __restrict__ bias) {
     using S = DenseShape;
     __shared__ __attribute__((aligned(16))) uint8_t smem[S::LDS_BYTES];
     const int tiles_m = (int)((M + S::BM - 1) / S::BM);
@@ -685,7 +707,8 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(
     __syncthreads();
     using T = Stage<S, OUT_BF16>;
     constexpr int ROWS = T::rows_for(S::SCALE_BASE / 4);   // both code stages
-    store_tile<S, OUT_BF16, ROWS>(acc, lds + wave * T::bytes(ROWS), y, m0, M, n0, N, wn, wm);
+    store_tile<S, OUT_BF16, ROWS, BIAS>(acc, lds + wave * T::bytes(ROWS), y, m0, M, n0, N, wn,
+                                        wm, bias);
 }
 
 // ---------------------------------------------------------------------------
@@ -702,11 +725,11 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(
 // ---------------------------------------------------------------------------
 constexpr int LDS_LIMIT = 160 * 1024;           // LDS a workgroup may hold
 
-template <bool OUT_BF16>
+template <bool OUT_BF16, bool BIAS>
 __global__ __launch_bounds__(256, 1) void gemm_persistent_kernel(
     const uint8_t* __restrict__ x, const uint8_t* __restrict__ xs,
     const uint8_t* __restrict__ w, const uint8_t* __restrict__ ws, int64_t M, int64_t N,
-    int64_t K, void* __restrict__ y, int gm) {
+    int64_t K, void* __restrict__ y, int gm, const uint16_t* __restrict__ bias) {
     using S = DenseShape;
     using T = Stage<S, OUT_BF16>;
     constexpr int ROWS = T::rows_for(S::WLOADS * 1024);   // a wave's weight rows of a stage
@@ -748,8 +771,8 @@ __global__ __launch_bounds__(256, 1) void gemm_persistent_kernel(
         const TileSrc<S> nxt = tile_src<S>(x, xs, w, ws, (int64_t)tm_next * S::BM, M,
                                            (int64_t)tn_next * S::BN, N, K);
         main_loop<S, S::MB, true, true>(lds, cur, nxt, lo, nkt, cbase, pp, acc, ro);
-        store_tile<S, OUT_BF16, ROWS>(acc, stage, y, (int64_t)tm * S::BM, M,
-                                      (int64_t)tn * S::BN, N, wn, wm);
+        store_tile<S, OUT_BF16, ROWS, BIAS>(acc, stage, y, (int64_t)tm * S::BM, M,
+                                            (int64_t)tn * S::BN, N, wn, wm, bias);
         if (!have_next) break;
         load_codes<S>(lds, nxt.op, lo, 1, 1);     // after this wave's epilogue reads
         rezero_acc<S>(acc);
@@ -985,7 +1008,8 @@ static int group_rows(int tiles_m, int per_xcd) {
 
 hipError_t launch_gemm_tiled(const uint8_t* a_codes, const uint8_t* a_scales,
                              const uint8_t* b_codes, const uint8_t* b_scales, int64_t M,
-                             int64_t N, int64_t K, void* y, bool out_bf16, hipStream_t stream) {
+                             int64_t N, int64_t K, void* y, const uint16_t* bias,
+                             bool out_bf16, hipStream_t stream) {
     using S = tiled::DenseShape;
     const int tiles_m = (int)((M + S::BM - 1) / S::BM);
     const int tiles_n = (int)((N + S::BN - 1) / S::BN);
@@ -1001,22 +1025,30 @@ hipError_t launch_gemm_tiled(const uint8_t* a_codes, const uint8_t* a_scales,
         // run side by side in compact blocks
         const int gm = group_rows(tiles_m, slots);
         const dim3 grid((unsigned)(slots * 8));
-        if (out_bf16)
-            hipLaunchKernelGGL(tiled::gemm_persistent_kernel<true>, grid, dim3(256), 0, stream,
-                               a_codes, a_scales, b_codes, b_scales, M, N, K, y, gm);
+        auto go = [&](auto kernel) {
+            hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, a_codes, a_scales, b_codes,
+                               b_scales, M, N, K, y, gm, bias);
+        };
+        if (bias)
+            out_bf16 ? go(tiled::gemm_persistent_kernel<true, true>)
+                     : go(tiled::gemm_persistent_kernel<false, true>);
         else
-            hipLaunchKernelGGL(tiled::gemm_persistent_kernel<false>, grid, dim3(256), 0, stream,
-                               a_codes, a_scales, b_codes, b_scales, M, N, K, y, gm);
+            out_bf16 ? go(tiled::gemm_persistent_kernel<true, false>)
+                     : go(tiled::gemm_persistent_kernel<false, false>);
         return hipGetLastError();
     }
     const int gm = group_rows(tiles_m, per_xcd);
     const dim3 grid((unsigned)(per_xcd * 8));
-    if (out_bf16)
-        hipLaunchKernelGGL(tiled::gemm_tiled_kernel<true>, grid, dim3(256), 0, stream, a_codes,
-                           a_scales, b_codes, b_scales, M, N, K, y, gm);
+    auto go = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, a_codes, a_scales, b_codes,
+                           b_scales, M, N, K, y, gm, bias);
+    };
+    if (bias)
+        out_bf16 ? go(tiled::gemm_tiled_kernel<true, true>)
+                 : go(tiled::gemm_tiled_kernel<false, true>);
     else
-        hipLaunchKernelGGL(tiled::gemm_tiled_kernel<false>, grid, dim3(256), 0, stream, a_codes,
-                           a_scales, b_codes, b_scales, M, N, K, y, gm);
+        out_bf16 ? go(tiled::gemm_tiled_kernel<true, false>)
+                 : go(tiled::gemm_tiled_kernel<false, false>);
     return hipGetLastError();
 }
 

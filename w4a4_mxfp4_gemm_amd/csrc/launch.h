@@ -40,12 +40,15 @@ bool linear_skinny_supported(int64_t M, int64_t N, int64_t K, const void* x, int
                              const void* w_scales);
 hipError_t launch_linear_skinny(const uint16_t* x, int64_t ldx, const uint8_t* b_codes,
                                 const uint8_t* b_scales, int64_t M, int64_t N, int64_t K,
-                                void* y, bool out_bf16, bool uos, hipStream_t stream);
+                                void* y, const uint16_t* bias, bool out_bf16, bool uos,
+                                hipStream_t stream);
 
+// bias: bf16 [N] added to every row's fp32 sum before the output rounding, or
+// nullptr (16-byte aligned when given).
 hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
                        const uint8_t* b_codes, const uint8_t* b_scales,
-                       int64_t M, int64_t N, int64_t K, void* y, bool out_bf16,
-                       hipStream_t stream);
+                       int64_t M, int64_t N, int64_t K, void* y, const uint16_t* bias,
+                       bool out_bf16, hipStream_t stream);
 
 hipError_t launch_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
                                const uint8_t* b_codes, const uint8_t* b_scales,
@@ -58,7 +61,8 @@ bool tiled_gemm_supported(int64_t M, int64_t N, int64_t K, const void* a_scales,
 
 hipError_t launch_gemm_tiled(const uint8_t* a_codes, const uint8_t* a_scales,
                              const uint8_t* b_codes, const uint8_t* b_scales, int64_t M,
-                             int64_t N, int64_t K, void* y, bool out_bf16, hipStream_t stream);
+                             int64_t N, int64_t K, void* y, const uint16_t* bias,
+                             bool out_bf16, hipStream_t stream);
 
 bool grouped_tiled_supported(int64_t E, int64_t total_M, int64_t N, int64_t K,
                              const void* a_scales, const void* b_scales);
@@ -74,6 +78,7 @@ bool skinny_gemm_supported(int64_t M, int64_t N, int64_t K, const void* x, const
 
 hipError_t launch_gemm_skinny(const uint8_t* a_codes, const uint8_t* a_scales,
                               const uint8_t* b_codes, const uint8_t* b_scales, int64_t M,
-                              int64_t N, int64_t K, void* y, bool out_bf16, hipStream_t stream);
+                              int64_t N, int64_t K, void* y, const uint16_t* bias,
+                              bool out_bf16, hipStream_t stream);
 
 }  // namespace mx

@@ -102,7 +102,7 @@ int mxfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b
     const int st = check_gemm_common(a_codes, a_scales, b_codes, b_scales, M, N, K, y, out_dtype,
                                      workspace, workspace_bytes, flags);
     if (st != MXFP4_OK || M == 0) return st;
-    return from_hip(mx::launch_gemm(a_codes, a_scales, b_codes, b_scales, M, N, K, y,
+    return from_hip(mx::launch_gemm(a_codes, a_scales, b_codes, b_scales, M, N, K, y, nullptr,
                                     out_dtype == MXFP4_OUT_BF16, stream));
 }
 
@@ -113,9 +113,9 @@ size_t mxfp4_linear_workspace_size(int64_t M, int64_t N, int64_t K) {
 }
 
 int mxfp4_linear_bf16(const void* x_bf16, int64_t ldx, int64_t M, int64_t N, int64_t K,
-                      const uint8_t* b_codes, const uint8_t* b_scales, void* y, int out_dtype,
-                      void* workspace, size_t workspace_bytes, uint32_t flags,
-                      hipStream_t stream) {
+                      const uint8_t* b_codes, const uint8_t* b_scales, const void* bias_bf16,
+                      void* y, int out_dtype, void* workspace, size_t workspace_bytes,
+                      uint32_t flags, hipStream_t stream) {
     if (M < 0 || N <= 0 || check_k(K) != MXFP4_OK || ldx < K) return MXFP4_EINVAL;
     if (out_dtype != MXFP4_OUT_BF16 && out_dtype != MXFP4_OUT_FP32) return MXFP4_EINVAL;
     if ((flags & ~(uint32_t)MXFP4_SCALE_UOS) != 0) return MXFP4_EINVAL;
@@ -124,12 +124,14 @@ int mxfp4_linear_bf16(const void* x_bf16, int64_t ldx, int64_t M, int64_t N, int
     if (!x_bf16 || !b_codes || !b_scales || !y) return MXFP4_EINVAL;
     if (!aligned(x_bf16, 16) || ldx % 8 != 0 || !aligned(b_codes, 16)) return MXFP4_EALIGN;
     if (!aligned(y, out_dtype == MXFP4_OUT_FP32 ? 4 : 2)) return MXFP4_EALIGN;
+    if (bias_bf16 && !aligned(bias_bf16, 16)) return MXFP4_EALIGN;
     const bool out_bf16 = out_dtype == MXFP4_OUT_BF16;
     const bool uos = (flags & MXFP4_SCALE_UOS) != 0;
+    const uint16_t* bias = static_cast<const uint16_t*>(bias_bf16);
     if (mx::linear_skinny_supported(M, N, K, x_bf16, ldx, b_scales))
         return from_hip(mx::launch_linear_skinny(static_cast<const uint16_t*>(x_bf16), ldx,
-                                                 b_codes, b_scales, M, N, K, y, out_bf16, uos,
-                                                 stream));
+                                                 b_codes, b_scales, M, N, K, y, bias, out_bf16,
+                                                 uos, stream));
     // two launches through the workspace: the act-quant call, then the GEMM
     const size_t need = linear_codes_bytes(M, K) + (size_t)M * (size_t)(K / 32);
     if (workspace_bytes < need) return MXFP4_EINVAL;
@@ -139,7 +141,7 @@ int mxfp4_linear_bf16(const void* x_bf16, int64_t ldx, int64_t M, int64_t N, int
     const hipError_t e = mx::launch_act_quant(static_cast<const uint16_t*>(x_bf16), ldx, nullptr,
                                               M, K, codes, scales, uos, stream);
     if (e != hipSuccess) return MXFP4_EHIP;
-    return from_hip(mx::launch_gemm(codes, scales, b_codes, b_scales, M, N, K, y, out_bf16,
+    return from_hip(mx::launch_gemm(codes, scales, b_codes, b_scales, M, N, K, y, bias, out_bf16,
                                     stream));
 }
 
