@@ -96,6 +96,16 @@ def _load():
     lib.orc_silu_mul_quantize.argtypes = [P, I, I, I, ctypes.c_int, P, P]
     lib.orc_moe_combine.restype = None
     lib.orc_moe_combine.argtypes = [P, I, P, P, I, I, I, P, P]
+    lib.orc_e4m3_encode.restype = ctypes.c_uint
+    lib.orc_e4m3_encode.argtypes = [ctypes.c_double]
+    lib.orc_shared_exponent_fp8.restype = ctypes.c_uint
+    lib.orc_shared_exponent_fp8.argtypes = [ctypes.c_double]
+    lib.orc_mx8_quantize_block.restype = None
+    lib.orc_mx8_quantize_block.argtypes = [P, P, P]
+    lib.orc_quantize_act_fp8.restype = None
+    lib.orc_quantize_act_fp8.argtypes = [P, I, P, I, I, P, P]
+    lib.orc_gemm_w4a8_at.restype = None
+    lib.orc_gemm_w4a8_at.argtypes = [P, P, P, P, I, I, I, P, P, I, P, P]
     lib.orc_add_row_bias.restype = None
     lib.orc_add_row_bias.argtypes = [P, P, I, I, P]
     lib.orc_bf16_from_double_array.restype = None
@@ -273,6 +283,76 @@ def grouped_gemm(a_codes, a_scales, b_codes, b_scales, offsets):
     s = np.zeros((M, N), dtype=np.float64)
     _load().orc_grouped_gemm(_ptr(a_codes), _ptr(a_scales), _ptr(b_codes),
                              _ptr(b_scales), _ptr(offsets), E, N, K, _ptr(y), _ptr(s))
+    return y, s
+
+
+# ---- W4A8 (R13-R15) -------------------------------------------------------------
+def e4m3_encode(q: float) -> int:
+    return int(_load().orc_e4m3_encode(float(q)))
+
+
+def shared_exponent_fp8(amax: float) -> int:
+    return int(_load().orc_shared_exponent_fp8(float(amax)))
+
+
+def mx8_quantize_block(v) -> tuple[np.ndarray, int]:
+    """32 values -> (32 E4M3 code bytes, E8M0 byte)."""
+    v = _c(v, np.float64)
+    assert v.shape == (32,)
+    codes = np.empty(32, dtype=np.uint8)
+    scale = np.empty(1, dtype=np.uint8)
+    _load().orc_mx8_quantize_block(_ptr(v), _ptr(codes), _ptr(scale))
+    return codes, int(scale[0])
+
+
+def quantize_act_fp8(x_bits, K=None, row_index=None):
+    """bf16 bit patterns [R, ldx] -> MXFP8 codes [M, K] (E4M3 bytes), E8M0 [M, K/32]."""
+    x_bits = _c(x_bits, np.uint16)
+    R, ldx = x_bits.shape
+    K = ldx if K is None else int(K)
+    assert K % 32 == 0 and K <= ldx
+    if row_index is not None:
+        row_index = _c(row_index, np.int32)
+        M = row_index.shape[0]
+        assert M == 0 or (row_index.min() >= 0 and row_index.max() < R)
+    else:
+        M = R
+    codes = np.empty((M, K), dtype=np.uint8)
+    scales = np.empty((M, K // 32), dtype=np.uint8)
+    if M:
+        _load().orc_quantize_act_fp8(_ptr(x_bits), ldx, _ptr(row_index), M, K, _ptr(codes),
+                                     _ptr(scales))
+    return codes, scales
+
+
+def gemm_w4a8(a_codes, a_scales, b_codes, b_scales, pm=None, pn=None):
+    """R15: A MXFP8 [M, K] + [M, K/32], B MXFP4 [N, K/2] + [N, K/32].  Whole
+    [M, N] result (y, s), or at the sampled positions (pm, pn)."""
+    a_codes = _c(a_codes, np.uint8)
+    a_scales = _c(a_scales, np.uint8)
+    b_codes = _c(b_codes, np.uint8)
+    b_scales = _c(b_scales, np.uint8)
+    M, K = a_codes.shape
+    N = b_codes.shape[0]
+    assert K % 32 == 0 and b_codes.shape == (N, K // 2)
+    assert a_scales.shape == (M, K // 32) and b_scales.shape == (N, K // 32)
+    if pm is None:
+        P = M * N
+        y = np.empty((M, N), dtype=np.float64)
+        s = np.empty((M, N), dtype=np.float64)
+        if P:
+            _load().orc_gemm_w4a8_at(_ptr(a_codes), _ptr(a_scales), _ptr(b_codes),
+                                     _ptr(b_scales), M, N, K, None, None, P, _ptr(y), _ptr(s))
+        return y, s
+    pm = _c(pm, np.int64)
+    pn = _c(pn, np.int64)
+    assert pm.shape == pn.shape and pm.ndim == 1
+    assert (pm >= 0).all() and (pm < M).all() and (pn >= 0).all() and (pn < N).all()
+    y = np.empty(pm.shape, dtype=np.float64)
+    s = np.empty(pm.shape, dtype=np.float64)
+    if pm.size:
+        _load().orc_gemm_w4a8_at(_ptr(a_codes), _ptr(a_scales), _ptr(b_codes), _ptr(b_scales),
+                                 M, N, K, _ptr(pm), _ptr(pn), pm.shape[0], _ptr(y), _ptr(s))
     return y, s
 
 

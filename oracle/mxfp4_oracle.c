@@ -412,6 +412,114 @@ void orc_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
     }
 }
 
+/* ---- W4A8: MXFP8 activations x MXFP4 weights ------------------------------ */
+
+/* R14: the float8_e4m3fn value nearest to q, found by scanning the 127
+   non-negative finite codes (values increase with the code); on an exact tie
+   the even code (mantissa bit 0) wins.  448 (0x7E) is the largest, so larger
+   q saturate to it.  Distances are exact in fp64 for the q the path forms
+   (a bf16 value times a power of two, |q| < 512). */
+unsigned orc_e4m3_encode(double q)
+{
+    double a = fabs(q);
+    unsigned best = 0;
+    double bestd = a;
+    for (unsigned c = 1; c < 0x7Fu; ++c) {
+        double d = fabs(a - orc_e4m3_value(c));
+        if (d < bestd || (d == bestd && (c % 2u) == 0u)) {
+            best = c;
+            bestd = d;
+        }
+    }
+    return (signbit(q) ? 0x80u : 0u) | best;
+}
+
+/* R13: 2^(floor(log2 amax) - 8), clamped to E8M0's range. */
+unsigned orc_shared_exponent_fp8(double amax)
+{
+    if (isnan(amax) || isinf(amax))
+        return 0xFFu;
+    int e;
+    if (amax == 0.0) {
+        e = -127;
+    } else {
+        int x;
+        frexp(amax, &x);
+        e = (x - 1) - 8;
+    }
+    if (e < -127) e = -127;
+    if (e > 127) e = 127;
+    return (unsigned)(e + 127);
+}
+
+void orc_mx8_quantize_block(const double v[32], uint8_t codes[32], uint8_t* scale)
+{
+    double amax = 0.0;
+    int bad = 0;
+    for (int i = 0; i < 32; ++i) {
+        if (isnan(v[i]) || isinf(v[i]))
+            bad = 1;
+        else if (fabs(v[i]) > amax)
+            amax = fabs(v[i]);
+    }
+    unsigned b = bad ? 0xFFu : orc_shared_exponent_fp8(amax);
+    *scale = (uint8_t)b;
+    if (b == 0xFFu) {
+        memset(codes, 0, 32);
+        return;
+    }
+    int e = (int)b - 127;
+    for (int i = 0; i < 32; ++i)
+        codes[i] = (uint8_t)orc_e4m3_encode(ldexp(v[i], -e));
+}
+
+void orc_quantize_act_fp8(const uint16_t* x, int64_t ldx, const int32_t* row_index,
+                          int64_t M, int64_t K, uint8_t* codes, uint8_t* scales)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        int64_t src = row_index ? (int64_t)row_index[m] : m;
+        const uint16_t* xr = x + src * ldx;
+        double blk[32];
+        for (int64_t j = 0; j < K / 32; ++j) {
+            for (int i = 0; i < 32; ++i)
+                blk[i] = orc_bf16_value(xr[32 * j + i]);
+            orc_mx8_quantize_block(blk, codes + m * K + 32 * j, scales + m * (K / 32) + j);
+        }
+    }
+}
+
+/* R15: the products e4m3 * e2m1 are exact in fp64, as are their scaled sums
+   within the GEMM's parity domain; summed in fp64 like orc_gemm. */
+void orc_gemm_w4a8_at(const uint8_t* a_codes, const uint8_t* a_scales,
+                      const uint8_t* b_codes, const uint8_t* b_scales,
+                      int64_t M, int64_t N, int64_t K,
+                      const int64_t* pm, const int64_t* pn, int64_t P,
+                      double* y, double* s)
+{
+    (void)M;   /* positions are given; M only bounds them (checked by the caller) */
+#pragma omp parallel
+    {
+        double* ad = (double*)malloc((size_t)K * sizeof(double));
+        double* bd = (double*)malloc((size_t)K * sizeof(double));
+#pragma omp for schedule(static)
+        for (int64_t i = 0; i < P; ++i) {
+            int64_t m = pm ? pm[i] : i / N;
+            int64_t n = pn ? pn[i] : i % N;
+            for (int64_t k = 0; k < K; ++k)
+                ad[k] = orc_e4m3_value(a_codes[m * K + k]) *
+                        orc_e8m0_value(a_scales[m * (K / 32) + k / 32]);
+            mx_row(b_codes, b_scales, n, K, bd);
+            double yy, ss;
+            dot_row(ad, bd, K, &yy, &ss);
+            y[i] = yy;
+            if (s) s[i] = ss;
+        }
+        free(ad);
+        free(bd);
+    }
+}
+
 /* ---- MoE expert epilogues ----------------------------------------------- */
 
 /* R10: silu(g) = g * sigma(g), sigma(g) = 1 / (1 + exp(-g)), times the up

@@ -53,6 +53,20 @@
  *      h = fl32(s * u).  A GPU exp or reciprocal that is not correctly
  *      rounded can move h by a few fp32 ulps, so where h lies that close to
  *      a bf16 rounding midpoint either neighbour is a correct result.
+ *   R13 W4A8 activations ([P2] "W4A8 fallback": MXFP8 activations,
+ *      float8_e4m3fn with scale_alg=0, the same block-32 grouping and "rint"
+ *      rounding, no UOS; the weights stay the MXFP4 ones): the OCP MX shared
+ *      exponent for E4M3 elements is e = floor(log2 amax) - 8 (8 is the
+ *      exponent of E4M3's largest binade, 448 = 1.75 * 2^8), clamped to
+ *      [-127, 127]; a NaN/Inf block gets byte 0xFF and all-zero codes.
+ *   R14 E4M3 element encode: the float8_e4m3fn value nearest to q = v / 2^e,
+ *      ties to the even code, saturating at +-448 (beyond it 448 is nearest;
+ *      the NaN code 0x7F is never produced), sign bit copied.  Codes are one
+ *      byte per element, row-major [M][K].
+ *   R15 W4A8 GEMM: y[m][n] = sum_k A[m,k] * B[n,k] with A = e4m3 * 2^(sa-127)
+ *      and B = e2m1 * 2^(sb-127), exact, rounded once (as R5), plus the
+ *      optional row bias (R12) ([P2]: the mixed FP8/FP4 GEMM gives bf16
+ *      output with a bf16 row bias).
  *   R12 row bias ([P3] NVFP4 apply_weights: the GEMM output plus an optional
  *      bias; [P2] W4A8 notes: bf16 output with a matching bf16 row bias): y
  *      gains bias[n] on every row, one bias per weight row (output column),
@@ -128,6 +142,27 @@ void orc_gemm_at(const uint8_t* a_codes, const uint8_t* a_scales,
 void orc_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
                       const uint8_t* b_codes, const uint8_t* b_scales,
                       const int32_t* offsets, int64_t E, int64_t N, int64_t K,
+                      double* y, double* s);
+
+/* ---- W4A8: MXFP8 (E4M3) activations x MXFP4 weights (R13-R15) --------- */
+unsigned orc_e4m3_encode(double q);              /* R14: float8_e4m3fn byte  */
+unsigned orc_shared_exponent_fp8(double amax);   /* R13                      */
+
+/* R13 + R14 on one block of 32 values: 32 code bytes and the scale byte. */
+void orc_mx8_quantize_block(const double v[32], uint8_t codes[32], uint8_t* scale);
+
+/* bf16 [*, ldx] -> MXFP8 codes [M][K] (one byte each) + E8M0 [M][K/32];
+   optional gather as orc_quantize_act. */
+void orc_quantize_act_fp8(const uint16_t* x, int64_t ldx, const int32_t* row_index,
+                          int64_t M, int64_t K, uint8_t* codes, uint8_t* scales);
+
+/* R15 at P sampled (m, n) positions (P = M*N with pm/pn NULL gives the whole
+   [M][N] result, row-major): A is MXFP8 [M][K] + [M][K/32], B is MXFP4
+   [N][K/2] + [N][K/32].  y and s as for orc_gemm. */
+void orc_gemm_w4a8_at(const uint8_t* a_codes, const uint8_t* a_scales,
+                      const uint8_t* b_codes, const uint8_t* b_scales,
+                      int64_t M, int64_t N, int64_t K,
+                      const int64_t* pm, const int64_t* pn, int64_t P,
                       double* y, double* s);
 
 /* ---- MoE expert epilogues (R10, R11) ---------------------------------- */

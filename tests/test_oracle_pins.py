@@ -666,3 +666,107 @@ def test_row_bias_closed_forms():
     yb, _ = oracle.add_row_bias(y1, s1, bias)
     # scales 127 on A and B bytes in [120, 135): every term and sum is exact
     assert np.array_equal(yb - y1, np.broadcast_to(bval, (M, N)))
+
+
+# ---- R13-R15: W4A8 (MXFP8 activations x MXFP4 weights) ---------------------------------
+def all_bf16_values():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    v = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).float()
+    return v[torch.isfinite(v)]
+
+
+def test_e4m3_encode_matches_torch_cast_and_saturates():
+    """Every finite bf16 value q with |q| <= 448 encodes to torch's
+    float32 -> float8_e4m3fn cast (round to nearest even, a library routine);
+    448 < |q| < 512 saturates to 0x7E with the sign kept."""
+    v = all_bf16_values()
+    inside = v[v.abs() <= 448]
+    want = inside.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([oracle.e4m3_encode(q) for q in inside.double().numpy()], dtype=np.uint8)
+    assert np.array_equal(got, want)
+    over = v[(v.abs() > 448) & (v.abs() < 512)].double().numpy()
+    assert over.size > 0
+    for q in over:
+        assert oracle.e4m3_encode(q) == (0xFE if q < 0 else 0x7E)
+
+
+def test_shared_exponent_fp8_brute_force():
+    """The byte is the unique b with 256 <= amax / 2^(b-127) < 512 (a block's
+    amax lands in E4M3's top binade), clamped to [0, 254]; NaN/Inf -> 0xFF."""
+    v = all_bf16_values().double().numpy()
+    v = np.unique(np.abs(v[v != 0]))
+    rng = np.random.default_rng(130)
+    v = np.concatenate([v, rng.uniform(1, 2, 200) * 2.0 ** rng.integers(-140, 128, 200)])
+    for a in v:
+        b = oracle.shared_exponent_fp8(a)
+        fits = [c for c in range(255) if 256 <= a / 2.0 ** (c - 127) < 512]
+        if fits:
+            assert b == fits[0]
+        else:
+            assert b == (0 if a < 2.0 ** -119 else 254)
+    assert oracle.shared_exponent_fp8(0.0) == 0
+    assert oracle.shared_exponent_fp8(float("nan")) == 0xFF
+    assert oracle.shared_exponent_fp8(float("inf")) == 0xFF
+
+
+@pytest.mark.parametrize("row", read_table("mx8_block_examples.txt"), ids=lambda r: r[0])
+def test_mx8_block_examples(row):
+    name, inputs, byte, codes = row
+    v = np.zeros(32)
+    for i, x in parse_sparse(inputs, parse_float).items():
+        v[i] = x
+    want = np.zeros(32, dtype=np.uint8)
+    for i, c in parse_sparse(codes, lambda t: int(t, 16)).items():
+        want[i] = c
+    got, b = oracle.mx8_quantize_block(v)
+    assert b == int(byte) and np.array_equal(got, want)
+
+
+def test_quantize_act_fp8_round_trip_of_canonical_mxfp8():
+    """A canonical MXFP8 tensor (every block's largest |code| in E4M3's top
+    binade, scale bytes 20..230) dequantized to bf16 (exact: 4 significant
+    bits) quantizes back to the same codes and bytes; a gather picks rows."""
+    rng = np.random.default_rng(131)
+    M, K = 12, 256
+    nb = K // 32
+    mag = rng.integers(0, 0x7F, (M, nb, 32))
+    mag[:, :, 0] = rng.integers(0x78, 0x7F, (M, nb))          # top binade: exponent 15
+    codes = (mag | (rng.integers(0, 2, mag.shape) << 7)).astype(np.uint8).reshape(M, K)
+    scales = rng.integers(20, 231, (M, nb)).astype(np.uint8)
+    vals = np.array([oracle.e4m3_value(int(c)) for c in codes.reshape(-1)]).reshape(M, nb, 32)
+    vals = vals * (2.0 ** (scales.astype(np.float64) - 127))[:, :, None]
+    x = torch.from_numpy(vals.reshape(M, K)).to(torch.bfloat16)
+    assert np.array_equal(x.double().numpy(), vals.reshape(M, K)), "bf16 must hold them exactly"
+    c, s = oracle.quantize_act_fp8(bf16_bits(x))
+    assert np.array_equal(s, scales)
+    # -0 codes come back as 0x80, +0 as 0x00: compare as values and signs
+    assert np.array_equal(c, codes)
+    idx = np.array([3, 3, 0, 11], dtype=np.int32)
+    cg, sg = oracle.quantize_act_fp8(bf16_bits(x), row_index=idx)
+    assert np.array_equal(cg, codes[idx]) and np.array_equal(sg, scales[idx])
+
+
+def test_gemm_w4a8_against_numpy_and_closed_form():
+    """Against an fp64 numpy matmul of operands dequantized by other means
+    (torch's float8_e4m3fn decode, the E2M1 golden table); and A = 1.0
+    everywhere (code 0x38, scale 127) gives B's row sums."""
+    rng = np.random.default_rng(132)
+    M, N, K = 7, 9, 96
+    ac = rng.integers(0, 0x7F, (M, K)) | (rng.integers(0, 2, (M, K)) << 7)
+    ac = ac.astype(np.uint8)
+    as_ = rng.integers(110, 140, (M, K // 32)).astype(np.uint8)
+    bc = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    bs = rng.integers(110, 140, (N, K // 32)).astype(np.uint8)
+    a = torch.from_numpy(ac).view(torch.float8_e4m3fn).double().numpy()
+    a = a * np.repeat(2.0 ** (as_.astype(np.float64) - 127), 32, axis=1)
+    nib = np.stack([bc & 15, bc >> 4], axis=-1).reshape(N, K)
+    b = E2M1[nib] * np.repeat(2.0 ** (bs.astype(np.float64) - 127), 32, axis=1)
+    y, s = oracle.gemm_w4a8(ac, as_, bc, bs)
+    assert np.allclose(y, a @ b.T, rtol=0, atol=1e-12 * s.max())
+    assert np.allclose(s, np.abs(a) @ np.abs(b).T, rtol=1e-12, atol=0)
+    ones = np.full((M, K), 0x38, dtype=np.uint8)
+    y1, _ = oracle.gemm_w4a8(ones, np.full((M, K // 32), 127, np.uint8), bc, bs)
+    assert np.array_equal(y1, np.broadcast_to(b.sum(axis=1), (M, N)))
+    pm = np.array([0, 6, 3]); pn = np.array([8, 0, 4])
+    ys, ss = oracle.gemm_w4a8(ac, as_, bc, bs, pm, pn)
+    assert np.array_equal(ys, y[pm, pn]) and np.array_equal(ss, s[pm, pn])
