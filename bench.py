@@ -48,7 +48,7 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="decode",
-                   choices=["decode", "prefill", "moe", "layerwise"])
+                   choices=["decode", "prefill", "moe", "layerwise", "w4a8"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--eager", type=int, default=0, metavar="N",
                    help="counter-collection pass: no graphs and no timing; run a "
@@ -422,6 +422,81 @@ def moe_workload(torch, mx, synth):
     return ph, report, None
 
 
+def w4a8_workload(torch, mx, synth):
+    """W4A8 (MXFP8 activations x the same MXFP4 weights): the decode-shaped
+    layer W [12288, 4096] for M in {1, 8, 32, 64} through mxfp4_linear_w4a8_bf16
+    with a bf16 row bias, weight copies rotated past the Infinity Cache; a
+    prefill-shaped [4096, 4096] x [4096, 4096] W4A8 GEMM is timed beside it."""
+    N, K, Ms = 12288, 4096, (1, 8, 32, 64)
+    d = torch.device("cuda:0")
+    w = synth.bf16_normal((N, K), 0.02, seed=11, device=d)
+    codes, scales, g = synth.nvfp4_from_bf16(w)
+    wc, ws = mx.mxfp4_requant_from_nvfp4(codes, scales, g.reshape(1))
+    del w, codes, scales
+    R = max(2, math.ceil(ROTATE_BYTES / gemm_bytes(0, N, K)))
+    W = [(wc.clone(), ws.clone()) for _ in range(R)]
+    bias = (torch.randn(N, generator=torch.Generator().manual_seed(3)) * 0.5).to(
+        torch.bfloat16).to(d)
+    x = synth.activations(64, K, seed=12, outlier_seed=13, device="cpu").to(d)
+    xs = {M: x[:M].contiguous() for M in Ms}
+    xq = {M: (torch.empty((M, K), dtype=torch.uint8, device=d),
+              torch.empty((M, K // 32), dtype=torch.uint8, device=d)) for M in Ms}
+    ys = {M: torch.empty((M, N), dtype=torch.bfloat16, device=d) for M in Ms}
+    wsp = torch.empty((max(mx.mxfp4_linear_w4a8_workspace_size(M, N, K) for M in Ms),),
+                      dtype=torch.uint8, device=d)
+    PM, PN, PK = 4096, 4096, 4096
+    xp = synth.activations(PM, PK, seed=24, outlier_seed=26, device=d)
+    xpq = mx.mxfp8_quantize_act(xp)
+    wp = synth.bf16_normal((PN, PK), 0.02, seed=21, device=d)
+    cp, sp, gp = synth.nvfp4_from_bf16(wp)
+    wpc, wps = mx.mxfp4_requant_from_nvfp4(cp, sp, gp.reshape(1))
+    del wp, cp, sp
+    yp = torch.empty((PM, PN), dtype=torch.bfloat16, device=d)
+
+    def linear(r, M):
+        mx.mxfp4_linear_w4a8_bf16(xs[M], W[r][0], W[r][1], ys[M], bias=bias, workspace=wsp)
+
+    def gemm(r, M):
+        mx.mxfp4_gemm_w4a8(xq[M][0], xq[M][1], W[r][0], W[r][1], ys[M], bias=bias)
+
+    ph = Phases(torch, R)
+    ph.add("step", lambda r: [linear(r, M) for M in Ms])
+    ph.add("gemm", lambda r: [gemm(r, M) for M in Ms])
+    for M in Ms:
+        ph.add(f"act_quant_M{M}", lambda r, M=M: mx.mxfp8_quantize_act(xs[M], *xq[M]))
+        ph.add(f"gemm_M{M}", lambda r, M=M: gemm(r, M))
+    ph.add("prefill_gemm", lambda r: mx.mxfp4_gemm_w4a8(xpq[0], xpq[1], wpc, wps, yp))
+
+    def report(t, steps):
+        flops = sum(2 * M * N * K for M in Ms)
+        value = flops / (t["step"] * 1e-3) / 1e12
+        wbytes = N * K * (0.5 + 1 / 32)
+        gb = [wbytes + M * K * (1 + 1 / 32) + M * N * 2 + N * 2 for M in Ms]
+        gemm_gbps = sum(gb) / (t["gemm"] * 1e-3) / 1e9
+        per_m = {str(M): {"act_quant_us": round(t[f"act_quant_M{M}"] * 1e3, 2),
+                          "gemm_us": round(t[f"gemm_M{M}"] * 1e3, 2),
+                          "gemm_GBps": round(b / (t[f"gemm_M{M}"] * 1e-3) / 1e9, 1)}
+                 for M, b in zip(Ms, gb)}
+        pf = 2 * PM * PN * PK / (t["prefill_gemm"] * 1e-3) / 1e12
+        roof = {"kernel": "mxfp4_gemm_w4a8, decode (M=1,8,32,64)", "bound": "hbm",
+                "achieved": round(gemm_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(gemm_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                "algorithmic_bytes_per_launch": round(sum(gb) / len(Ms)),
+                "avg_launch_us": round(t["gemm"] / len(Ms) * 1e3, 3)}
+        extra = {"dtype": "w4a8 (e4m3 x e2m1, e8m0 scales, fp32 acc)", "per_M": per_m,
+                 "prefill_gemm_us": round(t["prefill_gemm"] * 1e3, 2),
+                 "prefill_gemm_TFLOPs": round(pf, 1),
+                 "prefill_gemm_frac_fp8_peak": round(pf / 5000.0, 4),
+                 "weight_copies_rotated": R}
+        cfg = {"workload": "W4A8 decode-shaped linear W [12288,4096], M in {1,8,32,64} "
+                           "(mxfp4_linear_w4a8_bf16 with bf16 bias, bf16 out); beside it a "
+                           "[4096,4096]x[4096,4096] W4A8 GEMM",
+               "N": N, "K": K, "M": list(Ms)}
+        return value, "TFLOP/s", roof, extra, cfg
+
+    return ph, report, None
+
+
 def layerwise_workload(torch, mx, synth):
     """One MoE layer's NVFP4 tensors resident in a one-layer scratch buffer,
     requantized into a 48-layer preallocated destination, layer after layer
@@ -506,7 +581,7 @@ def main():
     import w4a4_mxfp4_gemm_amd as mx
 
     make = {"decode": decode_workload, "prefill": prefill_workload, "moe": moe_workload,
-            "layerwise": layerwise_workload}[args.workload]
+            "layerwise": layerwise_workload, "w4a8": w4a8_workload}[args.workload]
     ph, report, cpu_baseline = make(torch, mx, synth)
     if args.eager:
         eager_pass(torch, ph, args.eager)

@@ -207,6 +207,59 @@ int mxfp4_linear_bf16(const void* x_bf16, int64_t ldx, int64_t M, int64_t N, int
 size_t mxfp4_linear_workspace_size(int64_t M, int64_t N, int64_t K);
 
 /*
+ * W4A8: MXFP8 activations with the same MXFP4 weights (vLLM-Omni guide,
+ * "W4A8 fallback": activations quantized to float8_e4m3fn with the OCP MX
+ * scale (scale_alg=0), block 32 along K, round to nearest even, never UOS;
+ * the prepared MXFP4 weight and scale are shared with W4A4).  Per 32-element
+ * block: scale byte = floor(log2 amax) - 8 + 127 clamped to [0, 254] (8 is
+ * the exponent of E4M3's top binade, 448 = 1.75 * 2^8); each element is the
+ * E4M3 value nearest to v / 2^(byte-127), ties to the even code, saturating
+ * at +-448 (the NaN code 0x7F is never produced), sign kept.  A block holding
+ * NaN or Inf gets scale 0xFF and zero codes.
+ *
+ *   x_bf16, ldx, row_index, M, K   as for mxfp4_quantize_act
+ *   codes      [M][K] u8 (float8_e4m3fn bits, one per element), device,
+ *              written (16-byte aligned)
+ *   scales     [M][K/32] u8 (E8M0), device, written
+ *   flags      must be 0
+ */
+int mxfp8_quantize_act(const void* x_bf16, int64_t ldx, const int32_t* row_index, int64_t M,
+                       int64_t K, uint8_t* codes, uint8_t* scales, uint32_t flags,
+                       hipStream_t stream);
+
+/*
+ * The mixed FP8 x FP4 GEMM of W4A8: y[m][n] = round(sum_k A[m,k] * B[n,k] +
+ * bias[n]) with A = e4m3 * 2^(a_scale - 127) (MXFP8, as mxfp8_quantize_act
+ * writes it) and B the MXFP4 weight of mxfp4_gemm, fp32 accumulation on the
+ * block-scaled MFMA (E4M3 x E2M1 formats), bf16 or fp32 output (the guide
+ * gives the mixed GEMM bf16 output and a bf16 row bias).
+ *
+ *   a_codes, a_scales   [M][K], [M][K/32] u8, device, read (16-byte aligned)
+ *   b_codes, b_scales   [N][K/2], [N][K/32] u8, device, read
+ *   bias_bf16           [N] bf16, device, read, 16-byte aligned; or NULL
+ *   y, out_dtype        as for mxfp4_gemm
+ *   flags               must be 0
+ */
+int mxfp4_gemm_w4a8(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
+                    const uint8_t* b_scales, int64_t M, int64_t N, int64_t K,
+                    const void* bias_bf16, void* y, int out_dtype, uint32_t flags,
+                    hipStream_t stream);
+
+/*
+ * One W4A8 linear layer on bf16 activations: mxfp8_quantize_act into the
+ * caller's workspace (mxfp4_linear_w4a8_workspace_size(M, N, K) bytes,
+ * 16-byte aligned), then mxfp4_gemm_w4a8 -- the same y bit for bit.
+ * Arguments as for mxfp4_linear_bf16; flags must be 0.
+ */
+int mxfp4_linear_w4a8_bf16(const void* x_bf16, int64_t ldx, int64_t M, int64_t N, int64_t K,
+                           const uint8_t* b_codes, const uint8_t* b_scales,
+                           const void* bias_bf16, void* y, int out_dtype, void* workspace,
+                           size_t workspace_bytes, uint32_t flags, hipStream_t stream);
+
+/* Workspace bytes mxfp4_linear_w4a8_bf16 needs (the MXFP8 activations). */
+size_t mxfp4_linear_w4a8_workspace_size(int64_t M, int64_t N, int64_t K);
+
+/*
  * The activation between an MoE layer's two grouped GEMMs, quantized for the
  * second (AMD blog, closing list: the MoE experts run as fused-MoE kernels on
  * MXFP4).  Each expert is a gate/up projection followed by a down projection;

@@ -192,3 +192,34 @@ def test_moe_combine_argument_checks(lib):
     assert f(FAKE, 64, 16, FAKE, FAKE, 2, 8, 64, FAKE + 8, 0, 0, None) == -2  # out
     assert f(FAKE, 64, 16, ODD, FAKE, 2, 8, 64, FAKE, 0, 0, None) == -2     # rows
     assert f(FAKE, 64, 16, FAKE, FAKE, 0, 8, 64, FAKE, 1, 0, None) == 0     # T == 0
+
+
+def test_w4a8_argument_checks(lib):
+    q = lib.mxfp8_quantize_act
+    assert q(FAKE, 32, None, 4, 64, FAKE, FAKE, 0, None) == -1           # ldx < K
+    assert q(FAKE, 64, None, 4, 48, FAKE, FAKE, 0, None) == -1           # K % 32
+    assert q(FAKE, 64, None, 4, 64, FAKE, FAKE, 2, None) == -1           # flags (no UOS)
+    assert q(FAKE, 68, None, 4, 64, FAKE, FAKE, 0, None) == -2           # ldx % 8
+    assert q(FAKE, 64, None, 4, 64, ODD, FAKE, 0, None) == -2            # codes alignment
+    assert q(FAKE, 64, None, 0, 64, FAKE, FAKE, 0, None) == 0            # M == 0
+    g = lib.mxfp4_gemm_w4a8
+    #        a     sa    b     sb    M  N   K   bias  y     dt flags stream
+    assert g(FAKE, FAKE, FAKE, FAKE, 4, 16, 48, None, FAKE, 0, 0, None) == -1    # K % 32
+    assert g(FAKE, FAKE, FAKE, FAKE, 4, 16, 64, None, FAKE, 3, 0, None) == -1    # out dtype
+    assert g(FAKE, FAKE, FAKE, FAKE, 4, 16, 64, None, FAKE, 0, 1, None) == -1    # flags
+    assert g(None, FAKE, FAKE, FAKE, 4, 16, 64, None, FAKE, 0, 0, None) == -1
+    assert g(ODD, FAKE, FAKE, FAKE, 4, 16, 64, None, FAKE, 0, 0, None) == -2
+    assert g(FAKE, FAKE, FAKE, FAKE, 4, 16, 64, ODD, FAKE, 0, 0, None) == -2     # bias
+    assert g(FAKE, FAKE, FAKE, FAKE, 0, 16, 64, None, FAKE, 0, 0, None) == 0     # M == 0
+    f = lib.mxfp4_linear_w4a8_bf16
+    assert f(FAKE, 4096, 8, 256, 4096, FAKE, FAKE, None, FAKE, 0, None, 0, 0, None) == -1  # ws
+    assert f(FAKE, 4096, 8, 256, 4096, FAKE, FAKE, None, FAKE, 0, FAKE, 1 << 20, 1,
+             None) == -1                                                           # flags
+    assert f(FAKE, 4096, 8, 256, 4096, FAKE, FAKE, ODD, FAKE, 0, FAKE, 1 << 20, 0,
+             None) == -2                                                           # bias
+    assert f(FAKE, 4096, 8, 256, 4096, FAKE, FAKE, None, FAKE, 0, ODD, 1 << 20, 0,
+             None) == -2                                                           # ws align
+    assert f(FAKE, 4096, 0, 256, 4096, FAKE, FAKE, None, FAKE, 0, None, 0, 0, None) == 0
+    ws = lib.mxfp4_linear_w4a8_workspace_size
+    assert ws(8, 256, 4096) == 8 * 4096 + 8 * 128
+    assert ws(3, 256, 96) == 512 + 9

@@ -1,0 +1,185 @@
+"""GPU parity of the W4A8 path (MXFP8 activations x MXFP4 weights) against the
+CPU oracle: the MXFP8 activation quantization bit for bit, and the mixed
+FP8 x FP4 GEMM (with and without the row bias) within the W4A8 bar: the GEMM
+bar (1e-5 * sum_k |a_k b_k|) plus the MFMA's own truncation inside each MX
+block, bounded from the block's operand maxima (gpu_util)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import (Guarded, assert_w4a8, bf16_bits, dev, say, u8, w4a8_block_maxima,
+                      w4a8_truncation_bound)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mx():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import w4a4_mxfp4_gemm_amd as m
+    return m
+
+
+def quant8_both(mx, x_cpu, row_index=None, K=None):
+    M = x_cpu.shape[0] if row_index is None else row_index.shape[0]
+    K = x_cpu.shape[1] if K is None else K
+    gc = Guarded((M, K), torch.uint8)
+    gs = Guarded((M, K // 32), torch.uint8)
+    ri = None if row_index is None else torch.from_numpy(row_index).to(dev())
+    mx.mxfp8_quantize_act(x_cpu.to(dev()), gc.view, gs.view, row_index=ri, K=K)
+    torch.cuda.synchronize()
+    assert gc.intact() and gs.intact(), "write outside the output"
+    oc, os_ = oracle.quantize_act_fp8(bf16_bits(x_cpu), K=K, row_index=row_index)
+    return (u8(gc.view), u8(gs.view)), (oc, os_)
+
+
+def assert_same(gpu, ref, what):
+    (gc, gs), (oc, os_) = gpu, ref
+    if not np.array_equal(gs, os_):
+        i = tuple(np.argwhere(gs != os_)[0])
+        raise AssertionError(f"{what}: scale byte mismatch at {i}: gpu {gs[i]} oracle {os_[i]}")
+    if not np.array_equal(gc, oc):
+        i = tuple(np.argwhere(gc != oc)[0])
+        raise AssertionError(f"{what}: code mismatch at {i}: gpu {gc[i]:#04x} oracle {oc[i]:#04x}")
+
+
+# ---- MXFP8 activation quantization ---------------------------------------------
+@pytest.mark.parametrize("M,K", [(1, 32), (16, 512), (37, 544), (5, 4096), (64, 4096)])
+def test_act_quant_fp8_ragged_with_outliers(mx, M, K):
+    say(f"act_quant_fp8 M={M} K={K}")
+    x = synth.activations(M, K, seed=M + K, outlier_seed=K + 1)
+    g, o = quant8_both(mx, x)
+    assert_same(g, o, f"M={M} K={K}")
+
+
+def test_act_quant_fp8_gather_and_wide_rows(mx):
+    say("act_quant_fp8 gather, ldx > K")
+    x = synth.activations(50, 1024, seed=5, outlier_seed=6)
+    idx = np.random.default_rng(2).integers(0, 50, size=77).astype(np.int32)
+    g, o = quant8_both(mx, x, row_index=idx)
+    assert_same(g, o, "gather")
+    g, o = quant8_both(mx, x, K=512)
+    assert_same(g, o, "ldx>K")
+
+
+def test_act_quant_fp8_special_values(mx):
+    """Random bit patterns (NaN, Inf, subnormals), subnormal-only blocks,
+    signed zeros, and E4M3 tie points at many scales."""
+    say("act_quant_fp8 specials")
+    rng = np.random.default_rng(11)
+    K = 256
+    bits = rng.integers(0, 2 ** 16, size=(40, K), dtype=np.uint32).astype(np.uint16)
+    bits[8:16] = rng.integers(0, 0x80, size=(8, K)).astype(np.uint16) | \
+        (rng.integers(0, 2, size=(8, K)).astype(np.uint16) << 15)
+    bits[16:24] = rng.choice(np.array([0, 0x8000], dtype=np.uint16), size=(8, K))
+    for r in range(24, 40):
+        # multiples of 2^-4 between 0 and 2 against an anchor of 1: q = 256 v
+        # lands on every E4M3 tie in [64, 512) and saturates above 448
+        v = rng.integers(0, 33, size=K).astype(np.float32) / 16
+        v[::32] = 1.0
+        v *= np.float32(2.0 ** rng.integers(-100, 100)) * rng.choice([-1, 1], size=K)
+        bits[r] = (v.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    x = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16)
+    g, o = quant8_both(mx, x)
+    assert_same(g, o, "specials")
+
+
+def exhaustive_fp8_input():
+    """Every bf16 magnitude (both signs) against every scale byte b it can meet:
+    element 0 of each block is the anchor 256 * 2^(b-127) = 2^(b-119), the
+    others lie below 512 * 2^(b-127), so the block's byte is b."""
+    vals = []
+    for b in range(0, 247):
+        anchor = (b + 8) << 7
+        mags = np.arange(0, (b + 9) << 7, dtype=np.uint32)
+        v = np.concatenate([mags, mags | 0x8000]).astype(np.uint16)
+        nblk = -(-v.size // 31)
+        body = np.concatenate([v, np.zeros(nblk * 31 - v.size, np.uint16)]).reshape(nblk, 31)
+        head = np.full((nblk, 1), anchor, dtype=np.uint16)
+        head[1::2] |= 0x8000
+        vals.append(np.concatenate([head, body], axis=1))
+    blocks = np.concatenate(vals)
+    per_row = 128
+    nrow = -(-blocks.shape[0] // per_row)
+    pad = np.zeros((nrow * per_row - blocks.shape[0], 32), dtype=np.uint16)
+    return np.concatenate([blocks, pad]).reshape(nrow, per_row * 32)
+
+
+def test_act_quant_fp8_exhaustive_encoder(mx):
+    say("act_quant_fp8 exhaustive: all bf16 magnitudes x all scale bytes")
+    bits = exhaustive_fp8_input()
+    x = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16)
+    g, o = quant8_both(mx, x)
+    assert_same(g, o, "exhaustive")
+    assert set(np.unique(o[1])) >= set(range(0, 247)), "every scale byte is met"
+
+
+# ---- the FP8 x FP4 GEMM ----------------------------------------------------------
+def mxfp8_operand(M, K, seed):
+    """Random MXFP8 operand: every finite E4M3 code (0x7F / 0xFF excluded),
+    scale bytes 117..137 (the GEMM's exact-sum domain)."""
+    rng = np.random.default_rng(seed)
+    c = rng.integers(0, 0x7F, (M, K)) | (rng.integers(0, 2, (M, K)) << 7)
+    s = rng.integers(117, 138, (M, K // 32))
+    return torch.from_numpy(c.astype(np.uint8)), torch.from_numpy(s.astype(np.uint8))
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 256, 4096), (8, 1000, 4096), (33, 520, 2048),
+                                   (48, 300, 4096), (64, 300, 4096), (5, 260, 1024),
+                                   (20, 96, 96), (200, 520, 1056)])
+def test_gemm_w4a8_against_oracle(mx, M, N, K):
+    """Skinny (M <= 48, K = 2048/4096), and the 16x16x128 tile kernel (other
+    K, M = 64, large M), fp32 and bf16 output, with and without the bias."""
+    say(f"gemm_w4a8 M={M} N={N} K={K}")
+    ac, as_ = mxfp8_operand(M, K, seed=M + N)
+    bc, bs = synth.canonical_mxfp4(N, K, seed=N + K)
+    bias = (torch.randn(N, generator=torch.Generator().manual_seed(N)) * 4).to(torch.bfloat16)
+    y, s = oracle.gemm_w4a8(u8(ac), u8(as_), u8(bc), u8(bs))
+    yb, sb = oracle.add_row_bias(y, s, bf16_bits(bias))
+    amax, bmax = w4a8_block_maxima(u8(ac), u8(as_), u8(bc), u8(bs))
+    pm, pn = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    bound = w4a8_truncation_bound(amax, bmax, pm, pn)
+    A = [t.to(dev()) for t in (ac, as_, bc, bs)]
+    for dt in (torch.float32, torch.bfloat16):
+        for use_bias, (yy, ss) in ((False, (y, s)), (True, (yb, sb))):
+            gy = Guarded((M, N), dt)
+            mx.mxfp4_gemm_w4a8(*A, gy.view, bias=bias.to(dev()) if use_bias else None)
+            torch.cuda.synchronize()
+            assert gy.intact(), "write outside y"
+            assert_w4a8(gy.view, yy, ss, bound, f"w4a8 {dt} bias={use_bias}")
+    # the bar stays far below what a misplaced operand byte or scale costs (O(S)):
+    # full-range E4M3 operands span 2^18 inside a block, so the worst-case
+    # truncation allowance is a few tenths of a percent of S here
+    assert np.median(bound / np.maximum(s, 1e-300)) < 2.0 ** -6
+
+
+@pytest.mark.parametrize("M", [1, 8, 32, 64])
+def test_linear_w4a8_decode_full_size(mx, M):
+    """The decode-shaped layer (W [12288, 4096]) through the W4A8 linear call
+    with a bias: the MXFP8 activations bit for bit, the output against the
+    oracle on sampled columns, and the call equal to its two launches."""
+    say(f"linear w4a8 M={M} N=12288 K=4096")
+    N, K = 12288, 4096
+    x = synth.activations(M, K, seed=12, outlier_seed=13)
+    w = synth.bf16_normal((N, K), 0.02, seed=11)
+    codes, scales, g = synth.nvfp4_from_bf16(w)
+    wc, ws = mx.mxfp4_requant_from_nvfp4(codes.to(dev()), scales.to(dev()), g.reshape(1).to(dev()))
+    bias = (torch.randn(N, generator=torch.Generator().manual_seed(3)) * 0.5).to(torch.bfloat16)
+    yl = mx.mxfp4_linear_w4a8_bf16(x.to(dev()), wc, ws, bias=bias.to(dev()),
+                                   out_dtype=torch.float32)
+    xc, xs = mx.mxfp8_quantize_act(x.to(dev()))
+    y2 = mx.mxfp4_gemm_w4a8(xc, xs, wc, ws, bias=bias.to(dev()), out_dtype=torch.float32)
+    assert torch.equal(yl, y2)
+    oc, os_ = oracle.quantize_act_fp8(bf16_bits(x))
+    assert np.array_equal(u8(xc), oc) and np.array_equal(u8(xs), os_)
+    wo = oracle.requant(u8(codes), u8(scales), np.atleast_1d(g.numpy()))
+    cols = np.unique(np.concatenate([[0, N - 1], np.random.default_rng(M).integers(0, N, 600)]))
+    pm, pn = np.repeat(np.arange(M), cols.size), np.tile(cols, M)
+    y, s = oracle.gemm_w4a8(oc, os_, wo[0], wo[1], pm, pn)
+    bv = bias.double().numpy()[pn]
+    amax, bmax = w4a8_block_maxima(oc, os_, wo[0], wo[1])
+    bound = w4a8_truncation_bound(amax, bmax, pm, pn)
+    assert_w4a8(yl.cpu()[pm, pn], y + bv, s + np.abs(bv), bound, "linear w4a8")

@@ -50,6 +50,15 @@ def _load_library() -> ctypes.CDLL:
     lib.mxfp4_grouped_gemm.restype = ctypes.c_int
     lib.mxfp4_linear_bf16.argtypes = [P, I, I, I, I, P, P, P, P, ctypes.c_int, P, SZ, U32, P]
     lib.mxfp4_linear_bf16.restype = ctypes.c_int
+    lib.mxfp8_quantize_act.argtypes = [P, I, P, I, I, P, P, U32, P]
+    lib.mxfp8_quantize_act.restype = ctypes.c_int
+    lib.mxfp4_gemm_w4a8.argtypes = [P, P, P, P, I, I, I, P, P, ctypes.c_int, U32, P]
+    lib.mxfp4_gemm_w4a8.restype = ctypes.c_int
+    lib.mxfp4_linear_w4a8_bf16.argtypes = [P, I, I, I, I, P, P, P, P, ctypes.c_int, P, SZ, U32,
+                                           P]
+    lib.mxfp4_linear_w4a8_bf16.restype = ctypes.c_int
+    lib.mxfp4_linear_w4a8_workspace_size.argtypes = [I, I, I]
+    lib.mxfp4_linear_w4a8_workspace_size.restype = SZ
     lib.mxfp4_silu_mul_quantize.argtypes = [P, I, I, I, P, P, U32, P]
     lib.mxfp4_silu_mul_quantize.restype = ctypes.c_int
     lib.mxfp4_moe_combine.argtypes = [P, I, I, P, P, I, I, I, P, ctypes.c_int, U32, P]
@@ -71,7 +80,9 @@ EXPORTED_SYMBOLS = ("mxfp4_requant_from_nvfp4", "mxfp4_requant_from_nvfp4_subset
                     "mxfp4_quantize_act", "mxfp4_gemm",
                     "mxfp4_grouped_gemm", "mxfp4_linear_bf16", "mxfp4_gemm_workspace_size",
                     "mxfp4_linear_workspace_size", "mxfp4_silu_mul_quantize",
-                    "mxfp4_moe_combine", "mxfp4_status_string", "mxfp4_version")
+                    "mxfp4_moe_combine", "mxfp8_quantize_act", "mxfp4_gemm_w4a8",
+                    "mxfp4_linear_w4a8_bf16", "mxfp4_linear_w4a8_workspace_size",
+                    "mxfp4_status_string", "mxfp4_version")
 
 
 def library() -> ctypes.CDLL:
@@ -276,6 +287,100 @@ def mxfp4_linear_bf16(x, b_codes, b_scales, y=None, *, bias=None, K=None,
     return y
 
 
+def mxfp8_quantize_act(x, codes=None, scales=None, *, row_index=None, K=None, stream=None):
+    """W4A8 activations: bf16 x [R, ldx] -> E4M3 codes [M, K] (one byte each) and
+    E8M0 bytes [M, K/32]; M = R, or len(row_index) with row i from x[row_index[i]]."""
+    _need(x, "x", torch.bfloat16)
+    dev = x.device
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [rows, ldx]")
+    ldx = x.shape[1]
+    K = ldx if K is None else int(K)
+    if row_index is not None:
+        _need(row_index, "row_index", torch.int32, dev)
+        M = row_index.shape[0]
+    else:
+        M = x.shape[0]
+    if codes is None:
+        codes = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
+    _need(codes, "codes", torch.uint8, dev)
+    _need(scales, "scales", torch.uint8, dev)
+    if codes.shape != (M, K) or scales.shape != (M, K // 32):
+        raise ValueError("output shapes do not match [M, K] / [M, K/32]")
+    _check("mxfp8_quantize_act", _lib.mxfp8_quantize_act(
+        _ptr(x), ldx, _ptr(row_index), M, K, _ptr(codes), _ptr(scales), 0, _stream(stream, dev)))
+    return codes, scales
+
+
+def _bias_arg(bias, N, dev):
+    if bias is None:
+        return None
+    _need(bias, "bias", torch.bfloat16, dev)
+    if bias.shape != (N,):
+        raise ValueError("bias must be [N]")
+    return bias
+
+
+def mxfp4_gemm_w4a8(a_codes, a_scales, b_codes, b_scales, y=None, *, bias=None,
+                    out_dtype=torch.bfloat16, stream=None):
+    """W4A8: y [M, N] = A [M, K] (MXFP8) * B [N, K]^T (MXFP4) + bias."""
+    _need(a_codes, "a_codes", torch.uint8)
+    dev = a_codes.device
+    for t, n in ((a_scales, "a_scales"), (b_codes, "b_codes"), (b_scales, "b_scales")):
+        _need(t, n, torch.uint8, dev)
+    M, K = a_codes.shape
+    N = b_codes.shape[0]
+    if b_codes.shape != (N, K // 2) or a_scales.shape != (M, K // 32) or \
+            b_scales.shape != (N, K // 32):
+        raise ValueError("operand shapes disagree")
+    bias = _bias_arg(bias, N, dev)
+    if y is None:
+        y = torch.empty((M, N), dtype=out_dtype, device=dev)
+    _need(y, "y", y.dtype, dev)
+    if y.shape != (M, N):
+        raise ValueError("y must be [M, N]")
+    _check("mxfp4_gemm_w4a8", _lib.mxfp4_gemm_w4a8(
+        _ptr(a_codes), _ptr(a_scales), _ptr(b_codes), _ptr(b_scales), M, N, K, _ptr(bias),
+        _ptr(y), _out_dtype(y.dtype), 0, _stream(stream, dev)))
+    return y
+
+
+def mxfp4_linear_w4a8_workspace_size(M: int, N: int, K: int) -> int:
+    return int(_lib.mxfp4_linear_w4a8_workspace_size(M, N, K))
+
+
+def mxfp4_linear_w4a8_bf16(x, b_codes, b_scales, y=None, *, bias=None, K=None,
+                           out_dtype=torch.bfloat16, workspace=None, stream=None):
+    """W4A8 linear: y [M, N] = MXFP8(x) [M, K] * B [N, K]^T + bias from bf16 x
+    [M, ldx] (mxfp8_quantize_act then mxfp4_gemm_w4a8, bit for bit)."""
+    _need(x, "x", torch.bfloat16)
+    dev = x.device
+    _need(b_codes, "b_codes", torch.uint8, dev)
+    _need(b_scales, "b_scales", torch.uint8, dev)
+    if x.dim() != 2:
+        raise ValueError("x must be [M, ldx]")
+    M, ldx = x.shape
+    K = ldx if K is None else K
+    N = b_codes.shape[0]
+    if b_codes.shape != (N, K // 2) or b_scales.shape != (N, K // 32):
+        raise ValueError("operand shapes disagree")
+    bias = _bias_arg(bias, N, dev)
+    if y is None:
+        y = torch.empty((M, N), dtype=out_dtype, device=dev)
+    _need(y, "y", y.dtype, dev)
+    if y.shape != (M, N):
+        raise ValueError("y must be [M, N]")
+    if workspace is None:
+        workspace = torch.empty((max(mxfp4_linear_w4a8_workspace_size(M, N, K), 1),),
+                                dtype=torch.uint8, device=dev)
+    _check("mxfp4_linear_w4a8_bf16", _lib.mxfp4_linear_w4a8_bf16(
+        _ptr(x), ldx, M, N, K, _ptr(b_codes), _ptr(b_scales), _ptr(bias), _ptr(y),
+        _out_dtype(y.dtype), _ptr(workspace), workspace.numel(), 0, _stream(stream, dev)))
+    return y
+
+
 def mxfp4_silu_mul_quantize(gate_up, codes=None, scales=None, *, I=None, scale_rule="ocp",
                             stream=None):
     """MoE expert activation for the down projection: bf16 gate_up [M, ldg]
@@ -355,6 +460,8 @@ def mxfp4_grouped_gemm(a_codes, a_scales, b_codes, b_scales, offsets, y=None, *,
 __all__ = ["mxfp4_requant_from_nvfp4", "mxfp4_quantize_act", "mxfp4_gemm",
            "mxfp4_grouped_gemm", "mxfp4_linear_bf16", "mxfp4_gemm_workspace_size",
            "mxfp4_linear_workspace_size", "mxfp4_silu_mul_quantize", "mxfp4_moe_combine",
+           "mxfp8_quantize_act", "mxfp4_gemm_w4a8", "mxfp4_linear_w4a8_bf16",
+           "mxfp4_linear_w4a8_workspace_size",
            "mxfp4_status_string",
            "mxfp4_version", "Mxfp4Error", "LIBRARY_PATH", "EXPORTED_SYMBOLS",
            "MXFP4_OUT_BF16", "MXFP4_OUT_FP32", "MXFP4_REQ_INTERMEDIATE_BF16",

@@ -17,6 +17,8 @@
 #include "mx_device.h"
 #include "launch.h"
 
+#include <type_traits>
+
 namespace mx {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -56,6 +58,66 @@ __device__ __forceinline__ void load_frag(const uint8_t* __restrict__ codes,
     f.s = s;
 }
 
+// W4A8: an MXFP8 operand row's share of a super-step.  An E4M3 operand is 32
+// bytes a lane (8 registers), but not one MX block: in lane group g, bytes
+// 0..15 are K 16g..16g+15 of the 128 and bytes 16..31 are K 64+16g..64+16g+15
+// (measured), while an E2M1 operand's lane group g holds K 32g..32g+31, and
+// the scale of lane group j applies to K 32j..32j+31 for both.  So the MX
+// block that MFMA q takes at K 32j.. (block 4j+q of the super-step, as for
+// E2M1) is split: its first half goes to lane group 2(j%2), its second half to
+// 2(j%2)+1, in bytes 0..15 for j < 2 and 16..31 for j >= 2.  Lane group g
+// therefore loads half g%2 of blocks 4(g/2)+q and 4(2+g/2)+q; its scale byte
+// stays block 4g+q's.  Rows are K bytes long.
+struct Frag8 {
+    uint4 c[4][2];
+    uint32_t s;
+};
+
+__device__ __forceinline__ void load_frag8(const uint8_t* __restrict__ codes,
+                                           const uint8_t* __restrict__ scales, int64_t row,
+                                           bool row_ok, int base, int g, int nkb, Frag8& f) {
+    const uint8_t* crow = codes + row * (int64_t)nkb * 32 + 16 * (g & 1);
+    const uint8_t* srow = scales + row * (int64_t)nkb;
+    uint32_t s = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int k0 = base + 4 * (g >> 1) + q, k1 = k0 + 8;
+        const bool ok0 = row_ok && k0 < nkb, ok1 = row_ok && k1 < nkb;
+        f.c[q][0] = ok0 ? *reinterpret_cast<const uint4*>(crow + (int64_t)k0 * 32)
+                        : make_uint4(0, 0, 0, 0);
+        f.c[q][1] = ok1 ? *reinterpret_cast<const uint4*>(crow + (int64_t)k1 * 32)
+                        : make_uint4(0, 0, 0, 0);
+        const int ks = base + 4 * g + q;
+        s |= (row_ok && ks < nkb ? (uint32_t)srow[ks] : 127u) << (8 * q);
+    }
+    f.s = s;
+}
+
+// E4M3 A (format code 0) times E2M1 B (format code 4)
+template <int S>
+__device__ __forceinline__ v4f mfma_e4m3_e2m1(const uint4 (&a)[2], const uint4& b, v4f acc,
+                                              uint32_t sa, uint32_t sb) {
+    const v8i av = {(int)a[0].x, (int)a[0].y, (int)a[0].z, (int)a[0].w,
+                    (int)a[1].x, (int)a[1].y, (int)a[1].z, (int)a[1].w};
+    const v8i bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc, 0, 4, S, (int)sa, S,
+                                                            (int)sb);
+}
+
+template <int WM, int WN>
+__device__ __forceinline__ void mfma_superstep(const Frag8 (&fa)[WM], const Frag (&fb)[WN],
+                                               v4f (&acc)[WM][WN]) {
+#pragma unroll
+    for (int i = 0; i < WM; ++i)
+#pragma unroll
+        for (int j = 0; j < WN; ++j) {
+            acc[i][j] = mfma_e4m3_e2m1<0>(fa[i].c[0], fb[j].c[0], acc[i][j], fa[i].s, fb[j].s);
+            acc[i][j] = mfma_e4m3_e2m1<1>(fa[i].c[1], fb[j].c[1], acc[i][j], fa[i].s, fb[j].s);
+            acc[i][j] = mfma_e4m3_e2m1<2>(fa[i].c[2], fb[j].c[2], acc[i][j], fa[i].s, fb[j].s);
+            acc[i][j] = mfma_e4m3_e2m1<3>(fa[i].c[3], fb[j].c[3], acc[i][j], fa[i].s, fb[j].s);
+        }
+}
+
 template <int WM, int WN>
 __device__ __forceinline__ void mfma_superstep(const Frag (&fa)[WM], const Frag (&fb)[WN],
                                                v4f (&acc)[WM][WN]) {
@@ -74,7 +136,8 @@ __device__ __forceinline__ void mfma_superstep(const Frag (&fa)[WM], const Frag 
 // split its K super-steps round-robin (their partial tiles are summed through
 // LDS in a fixed order); the other factor tiles N.  Each wavefront owns a
 // (16*WM) x (16*WN) tile of 16x16 MFMA blocks.
-template <int WM, int WN, int KSPLIT, bool OUT_BF16>
+// A8: A is MXFP8 (W4A8 activations), else MXFP4.
+template <int WM, int WN, int KSPLIT, bool OUT_BF16, bool A8 = false>
 __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a_codes,
                                           const uint8_t* __restrict__ a_scales,
                                           const uint8_t* __restrict__ b_codes,
@@ -102,11 +165,15 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a_codes,
 
     for (int ss = kw; ss < nss; ss += KSPLIT) {
         const int kb_first = ss * 16 + 4 * g;
-        Frag fa[WM], fb[WN];
+        std::conditional_t<A8, Frag8, Frag> fa[WM];
+        Frag fb[WN];
 #pragma unroll
         for (int i = 0; i < WM; ++i) {
             const int64_t row = m0 + 16 * i + r16;
-            load_frag(a_codes, a_scales, row, row < m_end, kb_first, nkb, fa[i]);
+            if constexpr (A8)
+                load_frag8(a_codes, a_scales, row, row < m_end, ss * 16, g, nkb, fa[i]);
+            else
+                load_frag(a_codes, a_scales, row, row < m_end, kb_first, nkb, fa[i]);
         }
 #pragma unroll
         for (int j = 0; j < WN; ++j) {
@@ -162,7 +229,7 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a_codes,
         }
 }
 
-template <int WM, int WN, int KSPLIT, bool OUT_BF16>
+template <int WM, int WN, int KSPLIT, bool OUT_BF16, bool A8 = false>
 __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ a_codes,
                                                    const uint8_t* __restrict__ a_scales,
                                                    const uint8_t* __restrict__ b_codes,
@@ -173,8 +240,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ a
     constexpr int TN = 16 * WN * (4 / KSPLIT);
     const int64_t m0 = (int64_t)blockIdx.y * 16 * WM;
     const int64_t n0 = (int64_t)blockIdx.x * TN;
-    gemm_tile<WM, WN, KSPLIT, OUT_BF16>(a_codes, a_scales, b_codes, b_scales, m0, M, n0, N, K,
-                                        y, bias);
+    gemm_tile<WM, WN, KSPLIT, OUT_BF16, A8>(a_codes, a_scales, b_codes, b_scales, m0, M, n0, N,
+                                            K, y, bias);
 }
 
 // Grouped variant: blockIdx.y enumerates the row tiles of all experts in
@@ -211,7 +278,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(
                                         b_scales + e * N * nkb, r0, r1, n0, N, K, y, nullptr);
 }
 
-template <int WM, int WN, int KSPLIT>
+template <int WM, int WN, int KSPLIT, bool A8 = false>
 static hipError_t launch_dense(const uint8_t* a, const uint8_t* as, const uint8_t* b,
                                const uint8_t* bs, int64_t M, int64_t N, int64_t K, void* y,
                                const uint16_t* bias, bool out_bf16, hipStream_t stream) {
@@ -219,12 +286,31 @@ static hipError_t launch_dense(const uint8_t* a, const uint8_t* as, const uint8_
     constexpr int TN = 16 * WN * (4 / KSPLIT);
     const dim3 grid((unsigned)((N + TN - 1) / TN), (unsigned)((M + TM - 1) / TM));
     if (out_bf16)
-        hipLaunchKernelGGL((gemm_kernel<WM, WN, KSPLIT, true>), grid, dim3(256), 0, stream, a, as,
-                           b, bs, M, N, K, y, bias);
-    else
-        hipLaunchKernelGGL((gemm_kernel<WM, WN, KSPLIT, false>), grid, dim3(256), 0, stream, a,
+        hipLaunchKernelGGL((gemm_kernel<WM, WN, KSPLIT, true, A8>), grid, dim3(256), 0, stream, a,
                            as, b, bs, M, N, K, y, bias);
+    else
+        hipLaunchKernelGGL((gemm_kernel<WM, WN, KSPLIT, false, A8>), grid, dim3(256), 0, stream,
+                           a, as, b, bs, M, N, K, y, bias);
     return hipGetLastError();
+}
+
+// W4A8: A MXFP8 [M][K] + [M][K/32], B MXFP4.  The skinny weight-streaming
+// kernel for decode shapes, the 16x16x128 tile kernel otherwise.
+hipError_t launch_gemm_w4a8(const uint8_t* a_codes, const uint8_t* a_scales,
+                            const uint8_t* b_codes, const uint8_t* b_scales, int64_t M, int64_t N,
+                            int64_t K, void* y, const uint16_t* bias, bool out_bf16,
+                            hipStream_t stream) {
+    if (skinny_gemm_supported(M, N, K, a_codes, a_scales, b_scales))
+        return launch_gemm_skinny_w4a8(a_codes, a_scales, b_codes, b_scales, M, N, K, y, bias,
+                                       out_bf16, stream);
+    if (M <= 16)
+        return launch_dense<1, 1, 4, true>(a_codes, a_scales, b_codes, b_scales, M, N, K, y, bias,
+                                           out_bf16, stream);
+    if (M <= 32)
+        return launch_dense<2, 1, 4, true>(a_codes, a_scales, b_codes, b_scales, M, N, K, y, bias,
+                                           out_bf16, stream);
+    return launch_dense<2, 2, 1, true>(a_codes, a_scales, b_codes, b_scales, M, N, K, y, bias,
+                                       out_bf16, stream);
 }
 
 hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,

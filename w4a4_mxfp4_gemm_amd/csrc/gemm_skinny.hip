@@ -27,6 +27,8 @@
 #include "mx_device.h"
 #include "launch.h"
 
+#include <type_traits>
+
 namespace mx {
 namespace skinny {
 
@@ -88,6 +90,51 @@ __device__ __forceinline__ void load_block(Frag<SPW>& f, const uint8_t* codes,
     }
 }
 
+// W4A8 activations: the same share of an MXFP8 row.  An E4M3 operand is 32
+// bytes a lane, but in lane group g bytes 0..15 hold K 16g.. and bytes 16..31
+// K 64+16g.. of the MFMA's 128 (measured), while the E2M1 weight operand and
+// the scales go by 32-K blocks per lane group.  So MFMA q's block at K 32j..
+// (super-step block 4q+j) is split over lane groups 2(j%2) and 2(j%2)+1:
+// lane group g loads half g%2 of blocks 4q+g/2 (bytes 0..15) and 4q+2+g/2
+// (bytes 16..31).  Scale bytes are loaded as for E2M1.  Rows are K bytes.
+template <int SPW>
+struct Frag8 {
+    v4u c[SPW][4][2];
+    v4u s[SPW];
+};
+
+template <int SPW, int NW>
+__device__ __forceinline__ void load_block8(Frag8<SPW>& f, const uint8_t* codes,
+                                            const uint8_t* scales, int64_t row, int nkb) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int g = lane >> 4;
+    const uint8_t* crow = codes + row * (int64_t)nkb * 32 + 16 * (g & 1);
+    const uint8_t* srow = scales + row * (int64_t)nkb;
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) {
+        const int kb0 = (wave + NW * j) * 16;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int k0 = kb0 + 4 * q + (g >> 1);
+            f.c[j][q][0] = *reinterpret_cast<const v4u*>(crow + (int64_t)k0 * 32);
+            f.c[j][q][1] = *reinterpret_cast<const v4u*>(crow + (int64_t)(k0 + 2) * 32);
+        }
+        f.s[j] = *reinterpret_cast<const v4u*>(srow + kb0);
+    }
+}
+
+// E2M1 weights (A, format code 4) times E4M3 activations (B, format code 0)
+template <int S>
+__device__ __forceinline__ v4f mfma_s8(const v4u& a, const v4u (&b)[2], v4f acc, uint32_t sa,
+                                       uint32_t sb) {
+    const v8i av = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0, 0, 0};
+    const v8i bv = {(int)b[0][0], (int)b[0][1], (int)b[0][2], (int)b[0][3],
+                    (int)b[1][0], (int)b[1][1], (int)b[1][2], (int)b[1][3]};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc, 4, 0, S, (int)sa, S,
+                                                            (int)sb);
+}
+
 // The same share of a 16-row block quantized from bf16 rows (row stride ldx
 // elements) instead of loaded as MXFP4.  Each lane's operand is one whole
 // 32-element MX block of one row, so the lane quantizes it alone, by the
@@ -142,8 +189,9 @@ __device__ __forceinline__ void quant_raw(Frag<SPW>& f, const RawX<SPW>& r) {
 
 // BF16A: x is bf16 [M][ldx] (xs unused) and each wave quantizes its share of
 // the activations itself while its weight loads stream (UOS: by the Qmax =
-// 7.25 exponent rule).
-template <int MT, int SPW, int NW, int TPW, bool OUT_BF16, bool BF16A, bool UOS = false>
+// 7.25 exponent rule).  A8: x is MXFP8 (the W4A8 activations).
+template <int MT, int SPW, int NW, int TPW, bool OUT_BF16, bool BF16A, bool UOS = false,
+          bool A8 = false>
 __global__ __launch_bounds__(64 * NW, 1) void gemm_skinny_kernel(
     // no __restrict__ on the operands: with it the compiler may move their loads
     // across the points that order them (below the first MFMA, or the bf16
@@ -167,13 +215,15 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_skinny_kernel(
     //    (their outputs are never stored); issued first so that the first
     //    MFMA (bf16: the quantization) waits for them and for the first
     //    weight tile only
-    Frag<SPW> a[MT];
+    std::conditional_t<A8, Frag8<SPW>, Frag<SPW>> a[MT];
     RawX<SPW> xr[BF16A ? MT : 1];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
         const int64_t row = (int64_t)min(mt * 16 + r16, M - 1);
         if constexpr (BF16A)
             load_raw<SPW, NW>(xr[mt], reinterpret_cast<const uint16_t*>(x), ldx, row);
+        else if constexpr (A8)
+            load_block8<SPW, NW>(a[mt], x, xs, row, nkb);
         else
             load_block<SPW, NW>(a[mt], x, xs, row, nkb);
     }
@@ -205,10 +255,17 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_skinny_kernel(
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 const v4u& as = a[mt].s[j];
-                acc[mt] = mfma_s<0>(f.c[j][0], a[mt].c[j][0], acc[mt], s0, as[0] >> sh);
-                acc[mt] = mfma_s<0>(f.c[j][1], a[mt].c[j][1], acc[mt], s1, as[1] >> sh);
-                acc[mt] = mfma_s<0>(f.c[j][2], a[mt].c[j][2], acc[mt], s2, as[2] >> sh);
-                acc[mt] = mfma_s<0>(f.c[j][3], a[mt].c[j][3], acc[mt], s3, as[3] >> sh);
+                if constexpr (A8) {
+                    acc[mt] = mfma_s8<0>(f.c[j][0], a[mt].c[j][0], acc[mt], s0, as[0] >> sh);
+                    acc[mt] = mfma_s8<0>(f.c[j][1], a[mt].c[j][1], acc[mt], s1, as[1] >> sh);
+                    acc[mt] = mfma_s8<0>(f.c[j][2], a[mt].c[j][2], acc[mt], s2, as[2] >> sh);
+                    acc[mt] = mfma_s8<0>(f.c[j][3], a[mt].c[j][3], acc[mt], s3, as[3] >> sh);
+                } else {
+                    acc[mt] = mfma_s<0>(f.c[j][0], a[mt].c[j][0], acc[mt], s0, as[0] >> sh);
+                    acc[mt] = mfma_s<0>(f.c[j][1], a[mt].c[j][1], acc[mt], s1, as[1] >> sh);
+                    acc[mt] = mfma_s<0>(f.c[j][2], a[mt].c[j][2], acc[mt], s2, as[2] >> sh);
+                    acc[mt] = mfma_s<0>(f.c[j][3], a[mt].c[j][3], acc[mt], s3, as[3] >> sh);
+                }
             }
         }
     };
@@ -304,7 +361,7 @@ bool linear_skinny_supported(int64_t M, int64_t N, int64_t K, const void* x, int
            ldx % 8 == 0 && (reinterpret_cast<uintptr_t>(w_scales) % 16) == 0;
 }
 
-template <int MT, int SPW, int NW>
+template <int MT, int SPW, int NW, bool A8 = false>
 static hipError_t launch_mt(const uint8_t* a, const uint8_t* as, int64_t ldx, const uint8_t* b,
                             const uint8_t* bs, int64_t M, int64_t N, int64_t K, void* y,
                             const uint16_t* bias, bool out_bf16, hipStream_t stream,
@@ -331,33 +388,43 @@ static hipError_t launch_mt(const uint8_t* a, const uint8_t* as, int64_t ldx, co
         }
         return hipErrorInvalidValue;
     }
+    if constexpr (A8)
+        return out_bf16 ? go(gemm_skinny_kernel<MT, SPW, NW, TPW, true, false, false, true>)
+                        : go(gemm_skinny_kernel<MT, SPW, NW, TPW, false, false, false, true>);
     return out_bf16 ? go(gemm_skinny_kernel<MT, SPW, NW, TPW, true, false>)
                     : go(gemm_skinny_kernel<MT, SPW, NW, TPW, false, false>);
 }
 
 // K = 4096: NW super-steps of 512 K per wave pass (SPW = 8 / NW each);
 // K = 2048: four waves, one super-step each.
-template <int NW4096>
+template <int NW4096, bool A8 = false>
 static hipError_t launch_k(const uint8_t* a, const uint8_t* as, int64_t ldx, const uint8_t* b,
                            const uint8_t* bs, int64_t M, int64_t N, int64_t K, void* y,
                            const uint16_t* bias, bool out_bf16, hipStream_t stream) {
     constexpr int SPW = 8 / NW4096;
     if (K == 2048) {
         if (M <= 16)
-            return launch_mt<1, 1, 4>(a, as, ldx, b, bs, M, N, K, y, bias, out_bf16, stream);
+            return launch_mt<1, 1, 4, A8>(a, as, ldx, b, bs, M, N, K, y, bias, out_bf16,
+                                             stream);
         if (M <= 32)
-            return launch_mt<2, 1, 4>(a, as, ldx, b, bs, M, N, K, y, bias, out_bf16, stream);
+            return launch_mt<2, 1, 4, A8>(a, as, ldx, b, bs, M, N, K, y, bias, out_bf16,
+                                             stream);
         if (M <= 48)
-            return launch_mt<3, 1, 4>(a, as, ldx, b, bs, M, N, K, y, bias, out_bf16, stream);
-        return launch_mt<4, 1, 4>(a, as, ldx, b, bs, M, N, K, y, bias, out_bf16, stream);
+            return launch_mt<3, 1, 4, A8>(a, as, ldx, b, bs, M, N, K, y, bias, out_bf16,
+                                             stream);
+        return launch_mt<4, 1, 4, A8>(a, as, ldx, b, bs, M, N, K, y, bias, out_bf16, stream);
     }
     if (M <= 16)
-        return launch_mt<1, SPW, NW4096>(a, as, ldx, b, bs, M, N, K, y, bias, out_bf16, stream);
+        return launch_mt<1, SPW, NW4096, A8>(a, as, ldx, b, bs, M, N, K, y, bias, out_bf16,
+                                                stream);
     if (M <= 32)
-        return launch_mt<2, SPW, NW4096>(a, as, ldx, b, bs, M, N, K, y, bias, out_bf16, stream);
+        return launch_mt<2, SPW, NW4096, A8>(a, as, ldx, b, bs, M, N, K, y, bias, out_bf16,
+                                                stream);
     if (M <= 48)
-        return launch_mt<3, SPW, NW4096>(a, as, ldx, b, bs, M, N, K, y, bias, out_bf16, stream);
-    return launch_mt<4, SPW, NW4096>(a, as, ldx, b, bs, M, N, K, y, bias, out_bf16, stream);
+        return launch_mt<3, SPW, NW4096, A8>(a, as, ldx, b, bs, M, N, K, y, bias, out_bf16,
+                                                stream);
+    return launch_mt<4, SPW, NW4096, A8>(a, as, ldx, b, bs, M, N, K, y, bias, out_bf16,
+                                            stream);
 }
 
 // two wavefronts per SIMD (at K = 4096; measured 0.3-0.5 us less than one
@@ -368,6 +435,19 @@ hipError_t launch_gemm_skinny(const uint8_t* a_codes, const uint8_t* a_scales,
                               bool out_bf16, hipStream_t stream) {
     return launch_k<8>(a_codes, a_scales, 0, b_codes, b_scales, M, N, K, y, bias, out_bf16,
                        stream);
+}
+
+hipError_t launch_gemm_skinny_w4a8(const uint8_t* a_codes, const uint8_t* a_scales,
+                                   const uint8_t* b_codes, const uint8_t* b_scales, int64_t M,
+                                   int64_t N, int64_t K, void* y, const uint16_t* bias,
+                                   bool out_bf16, hipStream_t stream) {
+    // four activation blocks of E4M3 (twice the E2M1 registers) spill at two
+    // wavefronts per SIMD: one wavefront per SIMD, two super-steps each
+    if (M > 48 && K == 4096)
+        return launch_mt<4, 2, 4, true>(a_codes, a_scales, 0, b_codes, b_scales, M, N, K, y,
+                                        bias, out_bf16, stream);
+    return launch_k<8, true>(a_codes, a_scales, 0, b_codes, b_scales, M, N, K, y, bias, out_bf16,
+                             stream);
 }
 
 hipError_t launch_linear_skinny(const uint16_t* x, int64_t ldx, const uint8_t* b_codes,

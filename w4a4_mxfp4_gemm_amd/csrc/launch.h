@@ -76,6 +76,19 @@ hipError_t launch_grouped_gemm_tiled(const uint8_t* a_codes, const uint8_t* a_sc
 bool skinny_gemm_supported(int64_t M, int64_t N, int64_t K, const void* x, const void* x_scales,
                            const void* w_scales);
 
+// W4A8: A is MXFP8 (E4M3 codes [M][K], E8M0 [M][K/32]), B MXFP4.
+hipError_t launch_act_quant_fp8(const uint16_t* x, int64_t ldx, const int32_t* row_index,
+                                int64_t M, int64_t K, uint8_t* codes, uint8_t* scales,
+                                hipStream_t stream);
+hipError_t launch_gemm_w4a8(const uint8_t* a_codes, const uint8_t* a_scales,
+                            const uint8_t* b_codes, const uint8_t* b_scales, int64_t M, int64_t N,
+                            int64_t K, void* y, const uint16_t* bias, bool out_bf16,
+                            hipStream_t stream);
+hipError_t launch_gemm_skinny_w4a8(const uint8_t* a_codes, const uint8_t* a_scales,
+                                   const uint8_t* b_codes, const uint8_t* b_scales, int64_t M,
+                                   int64_t N, int64_t K, void* y, const uint16_t* bias,
+                                   bool out_bf16, hipStream_t stream);
+
 hipError_t launch_gemm_skinny(const uint8_t* a_codes, const uint8_t* a_scales,
                               const uint8_t* b_codes, const uint8_t* b_scales, int64_t M,
                               int64_t N, int64_t K, void* y, const uint16_t* bias,

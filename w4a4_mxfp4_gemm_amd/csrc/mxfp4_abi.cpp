@@ -22,6 +22,11 @@ size_t linear_codes_bytes(int64_t M, int64_t K) {
     return ((size_t)M * (size_t)(K / 2) + 255) / 256 * 256;
 }
 
+// MXFP8 codes: one byte per element
+size_t fp8_codes_bytes(int64_t M, int64_t K) {
+    return ((size_t)M * (size_t)K + 255) / 256 * 256;
+}
+
 int check_gemm_common(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
                       const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, void* y,
                       int out_dtype, void* workspace, size_t workspace_bytes, uint32_t flags) {
@@ -143,6 +148,63 @@ int mxfp4_linear_bf16(const void* x_bf16, int64_t ldx, int64_t M, int64_t N, int
     if (e != hipSuccess) return MXFP4_EHIP;
     return from_hip(mx::launch_gemm(codes, scales, b_codes, b_scales, M, N, K, y, bias, out_bf16,
                                     stream));
+}
+
+int mxfp8_quantize_act(const void* x_bf16, int64_t ldx, const int32_t* row_index, int64_t M,
+                       int64_t K, uint8_t* codes, uint8_t* scales, uint32_t flags,
+                       hipStream_t stream) {
+    if (M < 0 || check_k(K) != MXFP4_OK || ldx < K) return MXFP4_EINVAL;
+    if (flags != 0) return MXFP4_EINVAL;
+    if (M == 0) return MXFP4_OK;
+    if (!x_bf16 || !codes || !scales) return MXFP4_EINVAL;
+    if (!aligned(x_bf16, 16) || ldx % 8 != 0 || !aligned(codes, 16)) return MXFP4_EALIGN;
+    if (row_index && !aligned(row_index, 4)) return MXFP4_EALIGN;
+    return from_hip(mx::launch_act_quant_fp8(static_cast<const uint16_t*>(x_bf16), ldx,
+                                             row_index, M, K, codes, scales, stream));
+}
+
+int mxfp4_gemm_w4a8(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
+                    const uint8_t* b_scales, int64_t M, int64_t N, int64_t K,
+                    const void* bias_bf16, void* y, int out_dtype, uint32_t flags,
+                    hipStream_t stream) {
+    const int st = check_gemm_common(a_codes, a_scales, b_codes, b_scales, M, N, K, y, out_dtype,
+                                     nullptr, 0, flags);
+    if (st != MXFP4_OK || M == 0) return st;
+    if (bias_bf16 && !aligned(bias_bf16, 16)) return MXFP4_EALIGN;
+    return from_hip(mx::launch_gemm_w4a8(a_codes, a_scales, b_codes, b_scales, M, N, K, y,
+                                         static_cast<const uint16_t*>(bias_bf16),
+                                         out_dtype == MXFP4_OUT_BF16, stream));
+}
+
+size_t mxfp4_linear_w4a8_workspace_size(int64_t M, int64_t N, int64_t K) {
+    if (M <= 0 || N <= 0 || check_k(K) != MXFP4_OK) return 0;
+    return fp8_codes_bytes(M, K) + (size_t)M * (size_t)(K / 32);
+}
+
+int mxfp4_linear_w4a8_bf16(const void* x_bf16, int64_t ldx, int64_t M, int64_t N, int64_t K,
+                           const uint8_t* b_codes, const uint8_t* b_scales,
+                           const void* bias_bf16, void* y, int out_dtype, void* workspace,
+                           size_t workspace_bytes, uint32_t flags, hipStream_t stream) {
+    if (M < 0 || N <= 0 || check_k(K) != MXFP4_OK || ldx < K) return MXFP4_EINVAL;
+    if (out_dtype != MXFP4_OUT_BF16 && out_dtype != MXFP4_OUT_FP32) return MXFP4_EINVAL;
+    if (flags != 0) return MXFP4_EINVAL;
+    if (workspace_bytes != 0 && workspace == nullptr) return MXFP4_EINVAL;
+    if (M == 0) return MXFP4_OK;
+    if (!x_bf16 || !b_codes || !b_scales || !y) return MXFP4_EINVAL;
+    if (!aligned(x_bf16, 16) || ldx % 8 != 0 || !aligned(b_codes, 16)) return MXFP4_EALIGN;
+    if (!aligned(y, out_dtype == MXFP4_OUT_FP32 ? 4 : 2)) return MXFP4_EALIGN;
+    if (bias_bf16 && !aligned(bias_bf16, 16)) return MXFP4_EALIGN;
+    const size_t need = fp8_codes_bytes(M, K) + (size_t)M * (size_t)(K / 32);
+    if (workspace_bytes < need) return MXFP4_EINVAL;
+    if (!aligned(workspace, 16)) return MXFP4_EALIGN;
+    uint8_t* codes = static_cast<uint8_t*>(workspace);
+    uint8_t* scales = codes + fp8_codes_bytes(M, K);
+    const hipError_t e = mx::launch_act_quant_fp8(static_cast<const uint16_t*>(x_bf16), ldx,
+                                                  nullptr, M, K, codes, scales, stream);
+    if (e != hipSuccess) return MXFP4_EHIP;
+    return from_hip(mx::launch_gemm_w4a8(codes, scales, b_codes, b_scales, M, N, K, y,
+                                         static_cast<const uint16_t*>(bias_bf16),
+                                         out_dtype == MXFP4_OUT_BF16, stream));
 }
 
 int mxfp4_silu_mul_quantize(const void* gate_up_bf16, int64_t ldg, int64_t M, int64_t I,

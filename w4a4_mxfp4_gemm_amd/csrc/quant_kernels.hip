@@ -135,6 +135,92 @@ __global__ __launch_bounds__(256) void act_quant_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// MXFP8 activation quantization (the W4A8 activations): E4M3 elements, one
+// byte each, OCP MX scale 2^(floor(log2 amax) - 8).  Same thread layout as
+// act_quant_kernel: a thread owns 8 bf16 values (one 16-byte load, one 8-byte
+// store of codes), an aligned quad owns the 32-element block.
+// ---------------------------------------------------------------------------
+
+// E4M3 code of v * 2^-e, where inv = 2^-e and the block's amax makes
+// |q| < 512: saturate at 448 (0x7E); below 2^-6 the subnormal grid is
+// multiples of 2^-9, rounded to nearest even by v_rndne (8 * 2^-9 = 2^-6 is
+// code 8, the smallest normal, so the two ranges meet); above, the fp32 bits
+// rounded to 3 mantissa bits (ties to even) give exponent and mantissa in
+// one field, rebased from fp32's exponent bias (127) to E4M3's (7).
+__device__ __forceinline__ uint32_t e4m3_code(uint32_t bf16, float inv) {
+    const float a = __builtin_fabsf(__uint_as_float(bf16 << 16) * inv);
+    uint32_t c;
+    if (a >= 448.0f) {
+        c = 0x7Eu;
+    } else if (a < 0.015625f) {
+        c = (uint32_t)__builtin_rintf(a * 512.0f);
+    } else {
+        const uint32_t b = __float_as_uint(a);
+        c = ((b + 0x7FFFFu + ((b >> 20) & 1u)) >> 20) - ((127u - 7u) << 3);
+    }
+    return c | ((bf16 >> 8) & 0x80u);
+}
+
+template <int ROWS>
+__global__ __launch_bounds__(256) void act_quant_fp8_kernel(
+    const uint16_t* __restrict__ x, int64_t ldx, const int32_t* __restrict__ row_index,
+    int64_t M, int64_t K, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+    const int64_t chunks = K / 8;
+    const int64_t kq = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (kq >= chunks) return;                         // whole quads leave together
+    for (int64_t m0 = (int64_t)blockIdx.y * ROWS; m0 < M; m0 += (int64_t)gridDim.y * ROWS) {
+        uint4 raw[ROWS];
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r) {
+            const int64_t m = m0 + r;
+            if (m < M) {
+                const int64_t src = row_index ? (int64_t)row_index[m] : m;
+                raw[r] = *reinterpret_cast<const uint4*>(x + src * ldx + kq * 8);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r) {
+            const int64_t m = m0 + r;
+            if (m >= M) break;                        // uniform across the workgroup
+            const uint32_t w[4] = {raw[r].x, raw[r].y, raw[r].z, raw[r].w};
+            u16x2 a = __builtin_bit_cast(u16x2, w[0] & 0x7FFF7FFFu);
+#pragma unroll
+            for (int i = 1; i < 4; ++i)
+                a = __builtin_elementwise_max(a, __builtin_bit_cast(u16x2, w[i] & 0x7FFF7FFFu));
+            const uint32_t amax = quad_max_u32(max((uint32_t)a[0], (uint32_t)a[1]));
+            // bf16 amax exponent field E: byte = E - 8 clamped at 0; 0xFF for NaN/Inf
+            const uint32_t E = amax >> 7;
+            const uint32_t byte = E >= 255u ? 255u : (E > 8u ? E - 8u : 0u);
+            // 2^-(byte-127) = 2^(127-byte): fp32 exponent field 254 - byte (byte <= 246)
+            const float inv = __uint_as_float((254u - (byte > 253u ? 253u : byte)) << 23);
+            uint32_t out[2] = {0u, 0u};
+            if (byte != 255u) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t lo = e4m3_code(w[i] & 0xFFFFu, inv);
+                    const uint32_t hi = e4m3_code(w[i] >> 16, inv);
+                    out[i / 2] |= (lo | (hi << 8)) << (16 * (i % 2));
+                }
+            }
+            *reinterpret_cast<uint2*>(codes + m * K + kq * 8) = make_uint2(out[0], out[1]);
+            if ((kq & 3) == 0) scales[m * (K / 32) + kq / 4] = (uint8_t)byte;
+        }
+    }
+}
+
+hipError_t launch_act_quant_fp8(const uint16_t* x, int64_t ldx, const int32_t* row_index,
+                                int64_t M, int64_t K, uint8_t* codes, uint8_t* scales,
+                                hipStream_t stream) {
+    constexpr int ROWS = 2;
+    const int64_t gx = (K / 8 + 255) / 256;
+    int64_t gy = (M + ROWS - 1) / ROWS;
+    if (gy > 65535) gy = 65535;
+    hipLaunchKernelGGL(act_quant_fp8_kernel<ROWS>, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0,
+                       stream, x, ldx, row_index, M, K, codes, scales);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // NVFP4 -> MXFP4 requant.  One thread owns one 32-element MX block: 16 code
 // bytes (one 16-byte load) and the E4M3 scales of its two NVFP4 blocks.
 //
