@@ -78,6 +78,7 @@ KERNEL_SOURCES = {
     "gemm_decode": ("gemm_skinny.hip", "mx_device.h"),
     "gemm_prefill": ("gemm_tiled.hip", "mx_device.h"),
     "grouped_gemm_moe": ("gemm_tiled.hip", "mx_device.h"),
+    "gemm_w4a8_decode": ("gemm_skinny.hip", "mx_device.h"),
 }
 
 
@@ -480,7 +481,8 @@ def w4a8_workload(torch, mx, synth):
         pf = 2 * PM * PN * PK / (t["prefill_gemm"] * 1e-3) / 1e12
         roof = {"kernel": "mxfp4_gemm_w4a8, decode (M=1,8,32,64)", "bound": "hbm",
                 "achieved": round(gemm_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(gemm_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                "frac": round(gemm_gbps / HBM_PEAK_GBPS, 4),
+                "traffic": recorded_traffic("gemm_w4a8_decode"),
                 "algorithmic_bytes_per_launch": round(sum(gb) / len(Ms)),
                 "avg_launch_us": round(t["gemm"] / len(Ms) * 1e3, 3)}
         extra = {"dtype": "w4a8 (e4m3 x e2m1, e8m0 scales, fp32 acc)", "per_M": per_m,
