@@ -129,10 +129,12 @@ def mxfp8_operand(M, K, seed):
 
 @pytest.mark.parametrize("M,N,K", [(1, 256, 4096), (8, 1000, 4096), (33, 520, 2048),
                                    (48, 300, 4096), (64, 300, 4096), (5, 260, 1024),
-                                   (20, 96, 96), (200, 520, 1056)])
+                                   (20, 96, 96), (200, 520, 1056), (128, 256, 512),
+                                   (300, 1000, 1024), (520, 776, 2048)])
 def test_gemm_w4a8_against_oracle(mx, M, N, K):
-    """Skinny (M <= 48, K = 2048/4096), and the 16x16x128 tile kernel (other
-    K, M = 64, large M), fp32 and bf16 output, with and without the bias."""
+    """Skinny (M <= 64, K = 2048/4096), the LDS-staged tiled kernel (M >= 128,
+    K % 512 == 0; ragged M and N), and the 16x16x128 tile kernel (other K,
+    small M), fp32 and bf16 output, with and without the bias."""
     say(f"gemm_w4a8 M={M} N={N} K={K}")
     ac, as_ = mxfp8_operand(M, K, seed=M + N)
     bc, bs = synth.canonical_mxfp4(N, K, seed=N + K)
@@ -183,3 +185,19 @@ def test_linear_w4a8_decode_full_size(mx, M):
     amax, bmax = w4a8_block_maxima(oc, os_, wo[0], wo[1])
     bound = w4a8_truncation_bound(amax, bmax, pm, pn)
     assert_w4a8(yl.cpu()[pm, pn], y + bv, s + np.abs(bv), bound, "linear w4a8")
+
+
+def test_gemm_w4a8_tiled_large_sampled(mx):
+    """A prefill-sized W4A8 GEMM ([4096, 4096] x [1024, 4096]) through the tiled
+    kernel, checked on sampled rows (every tile row and the last)."""
+    M, N, K = 4096, 1024, 4096
+    say(f"gemm_w4a8 tiled M={M} N={N} K={K} sampled")
+    ac, as_ = mxfp8_operand(M, K, seed=91)
+    bc, bs = synth.canonical_mxfp4(N, K, seed=92)
+    gy = mx.mxfp4_gemm_w4a8(*[t.to(dev()) for t in (ac, as_, bc, bs)], out_dtype=torch.float32)
+    rows = np.unique(np.concatenate([np.arange(0, M, 128) + np.arange(M // 128) % 128, [M - 1]]))
+    pm, pn = np.repeat(rows, N), np.tile(np.arange(N), rows.size)
+    y, s = oracle.gemm_w4a8(u8(ac), u8(as_), u8(bc), u8(bs), pm, pn)
+    amax, bmax = w4a8_block_maxima(u8(ac), u8(as_), u8(bc), u8(bs))
+    bound = w4a8_truncation_bound(amax, bmax, pm, pn)
+    assert_w4a8(gy.cpu()[pm, pn], y, s, bound, "tiled large")

@@ -295,7 +295,8 @@ static hipError_t launch_dense(const uint8_t* a, const uint8_t* as, const uint8_
 }
 
 // W4A8: A MXFP8 [M][K] + [M][K/32], B MXFP4.  The skinny weight-streaming
-// kernel for decode shapes, the 16x16x128 tile kernel otherwise.
+// kernel for decode shapes, the LDS-staged tiled kernel from 128 rows, the
+// 16x16x128 tile kernel otherwise.
 hipError_t launch_gemm_w4a8(const uint8_t* a_codes, const uint8_t* a_scales,
                             const uint8_t* b_codes, const uint8_t* b_scales, int64_t M, int64_t N,
                             int64_t K, void* y, const uint16_t* bias, bool out_bf16,
@@ -303,6 +304,9 @@ hipError_t launch_gemm_w4a8(const uint8_t* a_codes, const uint8_t* a_scales,
     if (skinny_gemm_supported(M, N, K, a_codes, a_scales, b_scales))
         return launch_gemm_skinny_w4a8(a_codes, a_scales, b_codes, b_scales, M, N, K, y, bias,
                                        out_bf16, stream);
+    if (tiled_w4a8_supported(M, N, K, a_scales, b_scales))
+        return launch_gemm_tiled_w4a8(a_codes, a_scales, b_codes, b_scales, M, N, K, y, bias,
+                                      out_bf16, stream);
     if (M <= 16)
         return launch_dense<1, 1, 4, true>(a_codes, a_scales, b_codes, b_scales, M, N, K, y, bias,
                                            out_bf16, stream);

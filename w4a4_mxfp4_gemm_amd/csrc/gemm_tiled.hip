@@ -67,28 +67,37 @@ constexpr int BKB = 128;                     // code bytes per row per stage (25
 constexpr int SCALE_OPERAND = 256 * 16;      // 4 KiB: 256 rows x 16 B
 constexpr int SCALE_CHUNK = 2 * SCALE_OPERAND;
 
-template <int MB_, int NB_, int WGM_, int WGN_>
+// A8: the activations are MXFP8 (E4M3, one byte per element; W4A8), so an
+// activation row carries 256 code bytes per 256-K stage and each activation
+// fragment is two 16-byte reads (see read_offsets).
+template <int MB_, int NB_, int WGM_, int WGN_, bool A8_ = false>
 struct Shape {
     static_assert(WGM_ * WGN_ == 4, "four wavefronts per workgroup");
     static constexpr int MB = MB_, NB = NB_, WGM = WGM_, WGN = WGN_;
+    static constexpr bool A8 = A8_;
     static constexpr int BM = 32 * MB * WGM;              // activation rows per tile
     static constexpr int BN = 32 * NB * WGN;              // weight rows per tile
     static_assert(BM <= 256 && BN == 256, "scale staging holds 256 rows per operand");
+    static constexpr int XBKB = A8 ? 2 * BKB : BKB;       // activation code bytes per row, stage
+    static constexpr int XPARTS = A8 ? 2 : 1;             // 16-byte reads per activation fragment
     static constexpr int WLOADS = BN / 32;                // 1 KiB code loads per thread per stage
-    static constexpr int XLOADS = BM / 32;
+    static constexpr int XLOADS = BM * XBKB / 4096;
     static constexpr int W_OPERAND = BN * BKB;
-    static constexpr int CODE_STAGE = (BN + BM) * BKB;    // W then X
+    static constexpr int CODE_STAGE = BN * BKB + BM * XBKB;   // W then X
     static constexpr int SCALE_BASE = 2 * CODE_STAGE;     // after the two code stages
     static constexpr int LDS_BYTES = SCALE_BASE + 3 * SCALE_CHUNK;
     static constexpr int LOADS_PER_STAGE = WLOADS + XLOADS + 1;
     static constexpr int SLOTS = 2 * MB * NB;             // MFMAs per half stage
-    static constexpr int CODE_READS = 2 * (MB + NB);      // ds_read_b128 per half stage
+    static constexpr int CODE_READS = 2 * (NB + MB * XPARTS);   // ds_read_b128 per half stage
     static constexpr int SCALE_READS = MB + NB;           // ds_read_b32 per stage
-    static_assert(LOADS_PER_STAGE <= SLOTS && CODE_READS <= SLOTS, "slot budget");
+    // a stage's loads take one or two per MFMA slot
+    static_assert(LOADS_PER_STAGE <= 2 * SLOTS && CODE_READS <= SLOTS, "slot budget");
 };
 
 using DenseShape = Shape<4, 4, 2, 2>;
 using GroupShape = Shape<4, 2, 1, 4>;
+// W4A8: 128 activation rows, so that two stages of 256-byte rows fit the LDS
+using W4A8Shape = Shape<2, 4, 2, 2, true>;
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 #define AS_LDS(p) ((__attribute__((address_space(3))) void*)(p))
@@ -141,8 +150,11 @@ struct LoadOffsets {
     uint32_t w[S::WLOADS], x[S::XLOADS], ws, xs;
 };
 
+// E2M1 rows are 8 chunks of 16 bytes per stage, swizzled by (row >> 1) & 7;
+// E4M3 activation rows are 16 chunks, swizzled by row & 15 (16 rows of a
+// 16-lane read group then cover all 64 banks).
 template <class S>
-__device__ __forceinline__ LoadOffsets<S> load_offsets(int64_t ldc, int64_t lds_) {
+__device__ __forceinline__ LoadOffsets<S> load_offsets(int64_t ldc, int64_t ldx, int64_t lds_) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     LoadOffsets<S> o;
@@ -152,11 +164,13 @@ __device__ __forceinline__ LoadOffsets<S> load_offsets(int64_t ldc, int64_t lds_
         const int c = (lane & 7) ^ ((row >> 1) & 7);
         o.w[i] = (uint32_t)(row * ldc + 16 * c);
     }
+    constexpr int XCH = S::XBKB / 16;          // chunks per row and stage
 #pragma unroll
     for (int i = 0; i < S::XLOADS; ++i) {
-        const int row = (wave * S::XLOADS + i) * 8 + (lane >> 3);
-        const int c = (lane & 7) ^ ((row >> 1) & 7);
-        o.x[i] = (uint32_t)(row * ldc + 16 * c);
+        const int row = (wave * S::XLOADS + i) * (1024 / S::XBKB) + lane / XCH;
+        const int slot = lane % XCH;
+        const int c = S::A8 ? (slot ^ (row & 15)) : (slot ^ ((row >> 1) & 7));
+        o.x[i] = (uint32_t)(row * ldx + 16 * c);
     }
     const int row = wave * 64 + lane;
     o.ws = (uint32_t)(row * lds_);
@@ -169,6 +183,7 @@ __device__ __forceinline__ void load_codes(lds_u8* lds, const Operands& op,
                                            const LoadOffsets<S>& o, int buf, int kt) {
     const int wave = wave_id();
     const uint32_t k = (uint32_t)kt * BKB;
+    const uint32_t kx = S::A8 ? (uint32_t)kt * S::XBKB : k;
     lds_u8* w = lds + buf * S::CODE_STAGE;
     lds_u8* x = w + S::W_OPERAND;
 #pragma unroll
@@ -176,7 +191,7 @@ __device__ __forceinline__ void load_codes(lds_u8* lds, const Operands& op,
         dma16(op.w, w + (wave * S::WLOADS + i) * 1024, o.w[i], k);
 #pragma unroll
     for (int i = 0; i < S::XLOADS; ++i)
-        dma16(op.x, x + (wave * S::XLOADS + i) * 1024, o.x[i], k);
+        dma16(op.x, x + (wave * S::XLOADS + i) * 1024, o.x[i], kx);
 }
 
 // One operand's scales for chunk c (stages 2c, 2c+1) into ring slot `slot`:
@@ -203,12 +218,12 @@ template <class S>
 __device__ __forceinline__ TileSrc<S> tile_src(const uint8_t* x, const uint8_t* xs,
                                                const uint8_t* w, const uint8_t* ws, int64_t m0,
                                                int64_t m_end, int64_t n0, int64_t N, int64_t K) {
-    const int64_t ldc = K / 2, lds_ = K / 32;
+    const int64_t ldc = K / 2, ldx = S::A8 ? K : K / 2, lds_ = K / 32;
     const int64_t rows_w = N > n0 ? N - n0 : 0, rows_x = m_end > m0 ? m_end - m0 : 0;
     TileSrc<S> t;
     t.op = Operands{make_rsrc(w + n0 * ldc, (uint32_t)(rows_w * ldc)),
                     make_rsrc(ws + n0 * lds_, (uint32_t)(rows_w * lds_)),
-                    make_rsrc(x + m0 * ldc, (uint32_t)(rows_x * ldc)),
+                    make_rsrc(x + m0 * ldx, (uint32_t)(rows_x * ldx)),
                     make_rsrc(xs + m0 * lds_, (uint32_t)(rows_x * lds_))};
     return t;
 }
@@ -244,11 +259,27 @@ __device__ __forceinline__ v16f mfma(const v4u& a, const v4u& b, v16f acc, uint3
                                                            (int)sb);
 }
 
+// E2M1 weights (format code 4) times E4M3 activations (format code 0): the
+// activation operand is 32 bytes a lane, bytes 0..15 and 16..31 as read_offsets
+// places them.
+template <int T>
+__device__ __forceinline__ v16f mfma8(const v4u& a, const v4u& b0, const v4u& b1, v16f acc,
+                                      uint32_t sa, uint32_t sb) {
+    const v8i av = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0, 0, 0};
+    const v8i bv = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3],
+                    (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc, 4, 0, T, (int)sa, T,
+                                                           (int)sb);
+}
+
+template <class S>
+constexpr int XP1 = S::XPARTS - 1;
+
 // Half a stage of one wave's operands: NB weight and MB activation 32-row
-// blocks, 2 K-steps each, 16 bytes per lane.
+// blocks, 2 K-steps each, 16 bytes per lane (activations: XPARTS x 16 bytes).
 template <class S>
 struct Half {
-    v4u w[S::NB][2], x[S::MB][2];
+    v4u w[S::NB][2], x[S::MB][2][S::XPARTS];
 };
 // A stage's scale bytes: one 32-bit word (4 K-steps) per row block.
 template <class S>
@@ -271,20 +302,36 @@ __device__ __forceinline__ void ds_read_b32(uint32_t& r, uint32_t addr) {
 // Lane-constant LDS offsets.  Row r32 of block i sits at
 // (base_row + 32 i + r32); its swizzled chunk for K-step t depends on r32 and
 // t only, so every block is the same address plus 4 KiB * i.
-struct ReadOffsets {
+struct ReadOffsetsE2M1 {
     uint32_t w[4], x[4], ws, xs;
 };
+struct ReadOffsetsE4M3 {
+    uint32_t w[4], x[4], xh[4], ws, xs;   // xh: bytes 16..31 of an activation fragment
+};
+template <class S>
+using ReadOffsets = std::conditional_t<S::A8, ReadOffsetsE4M3, ReadOffsetsE2M1>;
 
 template <class S>
-__device__ __forceinline__ ReadOffsets read_offsets(int wn, int wm) {
+__device__ __forceinline__ ReadOffsets<S> read_offsets(int wn, int wm) {
     const int lane = threadIdx.x & 63;
     const int r32 = lane & 31, h = lane >> 5;
-    ReadOffsets r;
+    ReadOffsets<S> r;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         const int pos = (4 * h + t) ^ ((r32 >> 1) & 7);
         r.w[t] = (uint32_t)((wn * 32 * S::NB + r32) * BKB + 16 * pos);
-        r.x[t] = (uint32_t)(S::W_OPERAND + (wm * 32 * S::MB + r32) * BKB + 16 * pos);
+        if constexpr (S::A8) {
+            const uint32_t xrow = (uint32_t)(S::W_OPERAND + (wm * 32 * S::MB + r32) * S::XBKB);
+            // the E4M3 operand of the 32x32x64 MFMA (measured): lane half h
+            // holds, in bytes 0..15, half h of the 32-K block whose scale lane
+            // half 0 supplies and, in bytes 16..31, half h of lane half 1's.
+            // In K-step t those are blocks t and 4+t of the stage (as for
+            // E2M1), i.e. 16-byte chunks 2t+h and 8+2t+h of the row.
+            r.x[t] = xrow + 16 * ((2 * t + h) ^ (r32 & 15));
+            r.xh[t] = xrow + 16 * ((8 + 2 * t + h) ^ (r32 & 15));
+        } else {
+            r.x[t] = (uint32_t)(S::W_OPERAND + (wm * 32 * S::MB + r32) * BKB + 16 * pos);
+        }
     }
     r.ws = (uint32_t)((wn * 32 * S::NB + r32) * 16 + 4 * h);
     r.xs = (uint32_t)(SCALE_OPERAND + (wm * 32 * S::MB + r32) * 16 + 4 * h);
@@ -312,7 +359,7 @@ __device__ __forceinline__ void load_op(lds_u8* lds, const TileSrc<S>& cs, const
     } else if constexpr (Q < S::WLOADS + S::XLOADS) {
         constexpr int i = Q - S::WLOADS;
         dma16(cs.op.x, lds + buf * S::CODE_STAGE + S::W_OPERAND + (wave * S::XLOADS + i) * 1024,
-              lo.x[i], (uint32_t)kt * BKB);
+              lo.x[i], (uint32_t)kt * S::XBKB);
     } else {
         load_scales<S>(lds, ss.op, lo, scale_w, chunk, slot);
     }
@@ -323,14 +370,19 @@ __device__ __forceinline__ void load_op(lds_u8* lds, const TileSrc<S>& cs, const
 // per row block (weights first).
 template <class S, int H, int Q>
 __device__ __forceinline__ void read_op(Half<S>& f, Scales<S>& sc, uint32_t codes,
-                                        uint32_t scales, const ReadOffsets& ro) {
-    constexpr int P = S::NB + S::MB;
+                                        uint32_t scales, const ReadOffsets<S>& ro) {
+    constexpr int P = S::NB + S::MB * S::XPARTS;
     if constexpr (Q < S::CODE_READS) {
         constexpr int s = Q / P, r = Q % P;
-        if constexpr (r < S::NB)
+        if constexpr (r < S::NB) {
             ds_read_b128<r * 32 * BKB>(f.w[r][s], codes + ro.w[2 * H + s]);
-        else
-            ds_read_b128<(r - S::NB) * 32 * BKB>(f.x[r - S::NB][s], codes + ro.x[2 * H + s]);
+        } else {
+            constexpr int j = (r - S::NB) / S::XPARTS, part = (r - S::NB) % S::XPARTS;
+            if constexpr (part == 0)
+                ds_read_b128<j * 32 * S::XBKB>(f.x[j][s][0], codes + ro.x[2 * H + s]);
+            else
+                ds_read_b128<j * 32 * S::XBKB>(f.x[j][s][part], codes + ro.xh[2 * H + s]);
+        }
     } else if constexpr (Q < S::CODE_READS + S::NB) {
         constexpr int i = Q - S::CODE_READS;
         ds_read_b32<i * 32 * 16>(sc.w[i], scales + ro.ws);
@@ -343,7 +395,7 @@ __device__ __forceinline__ void read_op(Half<S>& f, Scales<S>& sc, uint32_t code
 // Issue reads [R0, R1) of a half-stage.
 template <class S, int H, int R0, int R1>
 __device__ __forceinline__ void read_range(Half<S>& f, Scales<S>& sc, uint32_t codes,
-                                           uint32_t scales, const ReadOffsets& ro) {
+                                           uint32_t scales, const ReadOffsets<S>& ro) {
     if constexpr (R0 < R1) {
         read_op<S, H, R0>(f, sc, codes, scales, ro);
         read_range<S, H, R0 + 1, R1>(f, sc, codes, scales, ro);
@@ -360,8 +412,13 @@ __device__ __forceinline__ void mfma_half(const Half<S>& f, const Scales<S>& sc,
                                           v16f (&acc)[S::NB][S::MB], Step&& step) {
     if constexpr (Q < S::SLOTS) {
         constexpr int t = Q / (S::NB * S::MB), i = (Q / S::MB) % S::NB, j = Q % S::MB;
-        if constexpr (j < JL)
-            acc[i][j] = mfma<2 * H + t>(f.w[i][t], f.x[j][t], acc[i][j], sc.w[i], sc.x[j]);
+        if constexpr (j < JL) {
+            if constexpr (S::A8)
+                acc[i][j] = mfma8<2 * H + t>(f.w[i][t], f.x[j][t][0], f.x[j][t][XP1<S>], acc[i][j],
+                                             sc.w[i], sc.x[j]);
+            else
+                acc[i][j] = mfma<2 * H + t>(f.w[i][t], f.x[j][t][0], acc[i][j], sc.w[i], sc.x[j]);
+        }
         step(std::integral_constant<int, Q>{});
         __builtin_amdgcn_sched_barrier(0);   // keep this slot's order
         mfma_half<S, JL, H, Q + 1>(f, sc, acc, step);
@@ -535,7 +592,7 @@ __device__ __forceinline__ uint32_t scale_addr(uint32_t lds0, int cbase, int s) 
 template <class S>
 __device__ __forceinline__ void prologue(lds_u8* lds, const TileSrc<S>& src,
                                          const LoadOffsets<S>& lo, int nkt, int cbase, Pipe<S>& pp,
-                                         const ReadOffsets& ro) {
+                                         const ReadOffsets<S>& ro) {
     const int last_chunk = nkt / 2 - 1;
     const int c1 = last_chunk >= 1 ? 1 : 0;
     load_codes<S>(lds, src.op, lo, 0, 0);
@@ -570,7 +627,7 @@ template <class S, int JL, bool PREFETCH, bool DEFER = false>
 __device__ __forceinline__ void main_loop(lds_u8* lds, const TileSrc<S>& cur,
                                           const TileSrc<S>& nxt, const LoadOffsets<S>& lo,
                                           int nkt, int cbase, Pipe<S>& pp,
-                                          v16f (&acc)[S::NB][S::MB], const ReadOffsets& ro) {
+                                          v16f (&acc)[S::NB][S::MB], const ReadOffsets<S>& ro) {
     const int last_chunk = nkt / 2 - 1;
     const uint32_t lds0 = lds_addr(lds);
     for (int kt = 0; kt < nkt; ++kt) {
@@ -619,6 +676,12 @@ __device__ __forceinline__ void main_loop(lds_u8* lds, const TileSrc<S>& cur,
                         load_op<S, Q>(lds, cs, ss, lo, s2 & 1, ks, scale_w, chunk, slot);
                 } else if constexpr (Q < S::LOADS_PER_STAGE) {
                     load_op<S, Q>(lds, cs, ss, lo, s2 & 1, ks, scale_w, chunk, slot);
+                }
+                // a stage with more loads than slots (W4A8): the rest, scale
+                // loads only, ride along from slot 0
+                if constexpr (Q + S::SLOTS < S::LOADS_PER_STAGE) {
+                    static_assert(Q + S::SLOTS >= S::WLOADS + S::XLOADS, "only scale loads");
+                    load_op<S, Q + S::SLOTS>(lds, cs, ss, lo, s2 & 1, ks, scale_w, chunk, slot);
                 }
                 read_range<S, 0, second_half_read<S>(Q), second_half_read<S>(Q + 1)>(
                     pp.h0, pp.sc_nxt, codes, scales, ro);
@@ -677,12 +740,11 @@ __device__ __forceinline__ bool tile_coords(int tiles_m, int tiles_n, int gm, in
     return true;
 }
 
-template <bool OUT_BF16, bool BIAS>
+template <bool OUT_BF16, bool BIAS, class S = DenseShape>
 __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(
     const uint8_t* __restrict__ x, const uint8_t* __restrict__ xs,
     const uint8_t* __restrict__ w, const uint8_t* __restrict__ ws, int64_t M, int64_t N,
     int64_t K, void* __restrict__ y, int gm, const uint16_t* __restrict__ bias) {
-    using S = DenseShape;
     __shared__ __attribute__((aligned(16))) uint8_t smem[S::LDS_BYTES];
     const int tiles_m = (int)((M + S::BM - 1) / S::BM);
     const int tiles_n = (int)((N + S::BN - 1) / S::BN);
@@ -694,8 +756,8 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(
     const int nkt = (int)(K / 256);           // even: K % 512 == 0
     lds_u8* lds = (lds_u8*)smem;
     const TileSrc<S> src = tile_src<S>(x, xs, w, ws, m0, M, n0, N, K);
-    const ReadOffsets ro = read_offsets<S>(wn, wm);
-    const LoadOffsets<S> lo = load_offsets<S>(K / 2, K / 32);
+    const ReadOffsets<S> ro = read_offsets<S>(wn, wm);
+    const LoadOffsets<S> lo = load_offsets<S>(K / 2, S::A8 ? K : K / 2, K / 32);
     v16f acc[S::NB][S::MB];
     zero_acc<S>(acc);
     Pipe<S> pp;
@@ -750,8 +812,8 @@ __global__ __launch_bounds__(256, 1) void gemm_persistent_kernel(
     lds_u8* lds = (lds_u8*)smem;
     // where load_codes puts this wave's weight rows of stage 1
     lds_u8* stage = lds + S::CODE_STAGE + wave * S::WLOADS * 1024;
-    const ReadOffsets ro = read_offsets<S>(wn, wm);
-    const LoadOffsets<S> lo = load_offsets<S>(K / 2, K / 32);
+    const ReadOffsets<S> ro = read_offsets<S>(wn, wm);
+    const LoadOffsets<S> lo = load_offsets<S>(K / 2, S::A8 ? K : K / 2, K / 32);
     int tm, tn;
     tile_of(t, tiles_m, tiles_n, gm, tm, tn);
     TileSrc<S> cur =
@@ -892,7 +954,7 @@ __device__ __forceinline__ void main_loop_jl(int jl, lds_u8* lds, const TileSrc<
                                              const TileSrc<S>& nxt, const LoadOffsets<S>& lo,
                                              int nkt, int cbase,
                                              Pipe<S>& pp, v16f (&acc)[S::NB][S::MB],
-                                             const ReadOffsets& ro) {
+                                             const ReadOffsets<S>& ro) {
     static_assert(S::WGM == 1 && S::MB == 4, "one wave row of four 32-row blocks");
     if (jl >= 4)
         main_loop<S, 4, PREFETCH>(lds, cur, nxt, lo, nkt, cbase, pp, acc, ro);
@@ -936,8 +998,8 @@ __global__ __launch_bounds__(256, 1) void grouped_tiled_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wn = wave % S::WGN, wm = wave / S::WGN;
     const int nkt = (int)(K / 256);           // even: K % 512 == 0
-    const ReadOffsets ro = read_offsets<S>(wn, wm);
-    const LoadOffsets<S> lo = load_offsets<S>(K / 2, K / 32);
+    const ReadOffsets<S> ro = read_offsets<S>(wn, wm);
+    const LoadOffsets<S> lo = load_offsets<S>(K / 2, S::A8 ? K : K / 2, K / 32);
 
     GroupItem it = decode_item<S::BM>(tb, E, tiles_n, t, 0);
     TileSrc<S> cur = item_src<S>(it, x, xs, w, ws, N, K);
@@ -1049,6 +1111,37 @@ hipError_t launch_gemm_tiled(const uint8_t* a_codes, const uint8_t* a_scales,
     else
         out_bf16 ? go(tiled::gemm_tiled_kernel<true, false>)
                  : go(tiled::gemm_tiled_kernel<false, false>);
+    return hipGetLastError();
+}
+
+// W4A8: MXFP8 activations [M][K] (one byte per element), MXFP4 weights.
+bool tiled_w4a8_supported(int64_t M, int64_t N, int64_t K, const void* a_scales,
+                          const void* b_scales) {
+    return M >= 128 && K % 512 == 0 && M * K < ((int64_t)1 << 31) && fits_buffer(N, K) &&
+           (reinterpret_cast<uintptr_t>(a_scales) % 4) == 0 &&
+           (reinterpret_cast<uintptr_t>(b_scales) % 4) == 0;
+}
+
+hipError_t launch_gemm_tiled_w4a8(const uint8_t* a_codes, const uint8_t* a_scales,
+                                  const uint8_t* b_codes, const uint8_t* b_scales, int64_t M,
+                                  int64_t N, int64_t K, void* y, const uint16_t* bias,
+                                  bool out_bf16, hipStream_t stream) {
+    using S = tiled::W4A8Shape;
+    const int tiles_m = (int)((M + S::BM - 1) / S::BM);
+    const int tiles_n = (int)((N + S::BN - 1) / S::BN);
+    const int per_xcd = (tiles_m * tiles_n + 7) / 8;
+    const int gm = group_rows(tiles_m, per_xcd);
+    const dim3 grid((unsigned)(per_xcd * 8));
+    auto go = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, a_codes, a_scales, b_codes,
+                           b_scales, M, N, K, y, gm, bias);
+    };
+    if (bias)
+        out_bf16 ? go(tiled::gemm_tiled_kernel<true, true, S>)
+                 : go(tiled::gemm_tiled_kernel<false, true, S>);
+    else
+        out_bf16 ? go(tiled::gemm_tiled_kernel<true, false, S>)
+                 : go(tiled::gemm_tiled_kernel<false, false, S>);
     return hipGetLastError();
 }
 

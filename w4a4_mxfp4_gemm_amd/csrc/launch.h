@@ -84,6 +84,12 @@ hipError_t launch_gemm_w4a8(const uint8_t* a_codes, const uint8_t* a_scales,
                             const uint8_t* b_codes, const uint8_t* b_scales, int64_t M, int64_t N,
                             int64_t K, void* y, const uint16_t* bias, bool out_bf16,
                             hipStream_t stream);
+bool tiled_w4a8_supported(int64_t M, int64_t N, int64_t K, const void* a_scales,
+                          const void* b_scales);
+hipError_t launch_gemm_tiled_w4a8(const uint8_t* a_codes, const uint8_t* a_scales,
+                                  const uint8_t* b_codes, const uint8_t* b_scales, int64_t M,
+                                  int64_t N, int64_t K, void* y, const uint16_t* bias,
+                                  bool out_bf16, hipStream_t stream);
 hipError_t launch_gemm_skinny_w4a8(const uint8_t* a_codes, const uint8_t* a_scales,
                                    const uint8_t* b_codes, const uint8_t* b_scales, int64_t M,
                                    int64_t N, int64_t K, void* y, const uint16_t* bias,
