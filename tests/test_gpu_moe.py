@@ -262,3 +262,37 @@ def test_moe_layer_end_to_end(mx):
     ref, s = oracle.moe_combine(bf16_bits(y2), rows.numpy(), w.numpy())
     assert_combine(out, ref, s, TOPK, "layer combine")
     assert torch.isfinite(out).all()
+
+
+def test_moe_epilogues_graph_replay_matches_eager(mx):
+    """The expert activation + quantization and the combine captured in a HIP
+    graph give the eager results on every replay, with eager work between."""
+    say("moe epilogues: graph replay vs eager")
+    d = dev()
+    gu = gate_up_input(256, 512, seed=97).to(d)
+    _, _, rows, w = synth.route_topk_full(64, 16, 4, seed=98)
+    y = synth.activations(256, 384, seed=99).to(d)
+    rows, w = rows.to(d), w.to(d)
+    hc = torch.empty((256, 128), dtype=torch.uint8, device=d)
+    hs = torch.empty((256, 8), dtype=torch.uint8, device=d)
+    out = torch.empty((64, 384), dtype=torch.bfloat16, device=d)
+
+    def step():
+        mx.mxfp4_silu_mul_quantize(gu, hc, hs)
+        mx.mxfp4_moe_combine(y, rows, w, out)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (hc, hs, out)]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(3):
+        for t in (hc, hs, out):
+            t.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip((hc, hs, out), ref):
+            assert torch.equal(a, b)
+        step()
+        torch.cuda.synchronize()

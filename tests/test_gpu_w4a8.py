@@ -201,3 +201,79 @@ def test_gemm_w4a8_tiled_large_sampled(mx):
     amax, bmax = w4a8_block_maxima(u8(ac), u8(as_), u8(bc), u8(bs))
     bound = w4a8_truncation_bound(amax, bmax, pm, pn)
     assert_w4a8(gy.cpu()[pm, pn], y, s, bound, "tiled large")
+
+
+def test_w4a8_graph_replay_matches_eager(mx):
+    """The W4A8 act-quant and GEMM (skinny and tiled, with bias) captured in a
+    HIP graph give the eager results on every replay."""
+    say("w4a8: graph replay vs eager")
+    d = dev()
+    K, N = 4096, 512
+    xs_ = synth.activations(8, K, seed=41).to(d)
+    xl = synth.activations(256, K, seed=42).to(d)
+    bc, bs = [t.to(d) for t in synth.canonical_mxfp4(N, K, seed=43)]
+    bias = torch.randn(N, generator=torch.Generator().manual_seed(44)).to(torch.bfloat16).to(d)
+    qs = (torch.empty((8, K), dtype=torch.uint8, device=d),
+          torch.empty((8, K // 32), dtype=torch.uint8, device=d))
+    ql = (torch.empty((256, K), dtype=torch.uint8, device=d),
+          torch.empty((256, K // 32), dtype=torch.uint8, device=d))
+    ys = torch.empty((8, N), dtype=torch.bfloat16, device=d)
+    yl = torch.empty((256, N), dtype=torch.float32, device=d)
+
+    def step():
+        mx.mxfp8_quantize_act(xs_, *qs)
+        mx.mxfp8_quantize_act(xl, *ql)
+        mx.mxfp4_gemm_w4a8(*qs, bc, bs, ys, bias=bias)
+        mx.mxfp4_gemm_w4a8(*ql, bc, bs, yl, bias=bias)
+
+    outs = (*qs, *ql, ys, yl)
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outs]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(3):
+        for t in outs:
+            t.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(outs, ref):
+            assert torch.equal(a, b)
+        step()
+        torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("M,K", [(2, 512), (130, 512)])
+def test_w4a8_in_block_truncation_model(mx, M, K):
+    """Pins, through the C-ABI, the hardware arithmetic the W4A8 bar rests on:
+    inside one 32-element block the E4M3 x E2M1 products are summed 13 bits
+    below the block's largest (448 + x keeps x truncated to a multiple of
+    2^-5), while separate blocks add without that loss.  B = 1.0 everywhere,
+    all scales 2^0; row r puts 448 at k = 0 and x_r at k = 1 (same block) and
+    x_r at k = 32 + r % 32 in row r's copy for the other-block case.  (The
+    16x16x128 tile kernel at M = 2, the tiled kernel at M = 130.)"""
+    say(f"w4a8 truncation model M={M} K={K}")
+    xs = np.array([2.0 ** -9, 0.0234375, 0.05859375, 0.140625, 0.25, 1.0], dtype=np.float32)
+    codes8 = torch.from_numpy(xs).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(torch.from_numpy(codes8).view(torch.float8_e4m3fn).float().numpy(), xs)
+    ac = np.zeros((M, K), dtype=np.uint8)
+    ac[:, 0] = 0x7E                                   # 448
+    pick = np.arange(M) % xs.size
+    same = np.arange(M) % 2 == 0
+    ac[same, 1] = codes8[pick[same]]                  # same block as the 448
+    ac[~same, 32] = codes8[pick[~same]]               # next block
+    as_ = np.full((M, K // 32), 127, dtype=np.uint8)
+    bc = np.full((8, K // 2), 0x22, dtype=np.uint8)   # E2M1 1.0 in both nibbles
+    bs = np.full((8, K // 32), 127, dtype=np.uint8)
+    y = mx.mxfp4_gemm_w4a8(*[torch.from_numpy(t).to(dev()) for t in (ac, as_, bc, bs)],
+                           out_dtype=torch.float32).cpu().numpy()
+    x = xs[pick].astype(np.float64)
+    want = np.where(same, 448 + np.floor(x / 2.0 ** -5) * 2.0 ** -5, 448 + x)
+    assert np.array_equal(y, np.repeat(want[:, None], 8, axis=1))
+    # and the W4A8 bar covers what the truncation drops
+    amax, bmax = w4a8_block_maxima(ac, as_, bc, bs)
+    pm, pn = np.repeat(np.arange(M), 8), np.tile(np.arange(8), M)
+    bound = w4a8_truncation_bound(amax, bmax, pm, pn)
+    exact = np.repeat((448 + x)[:, None], 8, axis=1).reshape(-1)
+    assert (np.abs(y.reshape(-1) - exact) <= bound).all()
