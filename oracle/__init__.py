@@ -96,6 +96,8 @@ def _load():
     lib.orc_silu_mul_quantize.argtypes = [P, I, I, I, ctypes.c_int, P, P]
     lib.orc_moe_combine.restype = None
     lib.orc_moe_combine.argtypes = [P, I, P, P, I, I, I, P, P]
+    lib.orc_smooth_rows.restype = None
+    lib.orc_smooth_rows.argtypes = [P, I, P, P, I, I, P]
     lib.orc_e4m3_encode.restype = ctypes.c_uint
     lib.orc_e4m3_encode.argtypes = [ctypes.c_double]
     lib.orc_shared_exponent_fp8.restype = ctypes.c_uint
@@ -284,6 +286,39 @@ def grouped_gemm(a_codes, a_scales, b_codes, b_scales, offsets):
     _load().orc_grouped_gemm(_ptr(a_codes), _ptr(a_scales), _ptr(b_codes),
                              _ptr(b_scales), _ptr(offsets), E, N, K, _ptr(y), _ptr(s))
     return y, s
+
+
+# ---- Smooth pre-scale (R17) ---------------------------------------------------------
+def smooth_rows(x_bits, smooth_bits, K=None, row_index=None):
+    """bf16 bits [R, ldx] times the bf16 Smooth vector [K] (fp32 product, RNE to
+    bf16) -> bf16 bits [M, K] (M = R, or len(row_index) with a gather)."""
+    x_bits = _c(x_bits, np.uint16)
+    R, ldx = x_bits.shape
+    K = ldx if K is None else int(K)
+    smooth_bits = _c(smooth_bits, np.uint16)
+    assert smooth_bits.shape == (K,) and K <= ldx
+    if row_index is not None:
+        row_index = _c(row_index, np.int32)
+        M = row_index.shape[0]
+    else:
+        M = R
+    out = np.empty((M, K), dtype=np.uint16)
+    if M and K:
+        _load().orc_smooth_rows(_ptr(x_bits), ldx, _ptr(row_index), _ptr(smooth_bits), M, K,
+                                _ptr(out))
+    return out
+
+
+def quantize_act_smooth(x_bits, smooth_bits, K=None, row_index=None, scale_rule="ocp"):
+    """R17 then R3/R9 + R4: MXFP4 of bf16(x * smooth)."""
+    h = smooth_rows(x_bits, smooth_bits, K, row_index)
+    return quantize_act(h, scale_rule=scale_rule)
+
+
+def quantize_act_fp8_smooth(x_bits, smooth_bits, K=None, row_index=None):
+    """R17 then R13 + R14: MXFP8 of bf16(x * smooth)."""
+    h = smooth_rows(x_bits, smooth_bits, K, row_index)
+    return quantize_act_fp8(h)
 
 
 # ---- W4A8 (R13-R15) -------------------------------------------------------------

@@ -412,6 +412,24 @@ void orc_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
     }
 }
 
+/* ---- Smooth pre-scale ------------------------------------------------------ */
+
+/* R17: the per-channel product in fp32 (contraction off), rounded to bf16. */
+void orc_smooth_rows(const uint16_t* x, int64_t ldx, const int32_t* row_index,
+                     const uint16_t* smooth, int64_t M, int64_t K, uint16_t* out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        int64_t src = row_index ? (int64_t)row_index[m] : m;
+        for (int64_t k = 0; k < K; ++k) {
+            float v = (float)orc_bf16_value(x[src * ldx + k]);
+            float s = (float)orc_bf16_value(smooth[k]);
+            float p = v * s;
+            out[m * K + k] = orc_bf16_from_float(p);
+        }
+    }
+}
+
 /* ---- W4A8: MXFP8 activations x MXFP4 weights ------------------------------ */
 
 /* R14: the float8_e4m3fn value nearest to q, found by scanning the 127

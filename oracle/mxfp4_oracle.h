@@ -67,6 +67,12 @@
  *      and B = e2m1 * 2^(sb-127), exact, rounded once (as R5), plus the
  *      optional row bias (R12) ([P2]: the mixed FP8/FP4 GEMM gives bf16
  *      output with a bf16 row bias).
+ *   R17 Smooth pre-scale ([P2] pre-quantized single-scale weights: both
+ *      W4A4 and W4A8 quantize x * mul_scale, the per-input-channel Smooth
+ *      tensor converted to the activation dtype): the quantized values are
+ *      h_k = bf16(fl32(x_k * s_k)) with s = the bf16 Smooth vector [K] (a
+ *      product of two bf16 values is exact in fp32 except in fp32's
+ *      subnormal range), then quantized as R3/R9 + R4 or R13 + R14.
  *   R12 row bias ([P3] NVFP4 apply_weights: the GEMM output plus an optional
  *      bias; [P2] W4A8 notes: bf16 output with a matching bf16 row bias): y
  *      gains bias[n] on every row, one bias per weight row (output column),
@@ -143,6 +149,12 @@ void orc_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
                       const uint8_t* b_codes, const uint8_t* b_scales,
                       const int32_t* offsets, int64_t E, int64_t N, int64_t K,
                       double* y, double* s);
+
+/* ---- Smooth pre-scale (R17) ---------------------------------------------- */
+/* x bf16 [*][ldx] (optional gather) times the bf16 Smooth vector [K], each
+   product rounded to fp32 then to bf16: out bf16 [M][K]. */
+void orc_smooth_rows(const uint16_t* x, int64_t ldx, const int32_t* row_index,
+                     const uint16_t* smooth, int64_t M, int64_t K, uint16_t* out);
 
 /* ---- W4A8: MXFP8 (E4M3) activations x MXFP4 weights (R13-R15) --------- */
 unsigned orc_e4m3_encode(double q);              /* R14: float8_e4m3fn byte  */

@@ -770,3 +770,45 @@ def test_gemm_w4a8_against_numpy_and_closed_form():
     pm = np.array([0, 6, 3]); pn = np.array([8, 0, 4])
     ys, ss = oracle.gemm_w4a8(ac, as_, bc, bs, pm, pn)
     assert np.array_equal(ys, y[pm, pn]) and np.array_equal(ss, s[pm, pn])
+
+
+# ---- R17: Smooth pre-scale ----------------------------------------------------------
+def test_smooth_rows_matches_torch_bf16_multiply():
+    """bf16 x times bf16 smooth through torch's bf16 multiply (fp32 product
+    rounded to bf16, a library routine), random values over the whole bf16
+    range including subnormal and huge products."""
+    rng = np.random.default_rng(140)
+    M, K = 9, 96
+    x = torch.from_numpy((rng.standard_normal((M, K)) * 2.0 ** rng.integers(-60, 60, (M, K)))
+                         .astype(np.float32)).to(torch.bfloat16)
+    sm = torch.from_numpy((rng.uniform(0.01, 8, K) * 2.0 ** rng.integers(-70, 70, K))
+                          .astype(np.float32)).to(torch.bfloat16)
+    want = bf16_bits(x * sm)
+    got = oracle.smooth_rows(bf16_bits(x), bf16_bits(sm))
+    assert np.array_equal(got, want)
+
+
+def test_quantize_act_smooth_closed_forms():
+    """A Smooth vector of ones changes nothing; a power of two per 32-block
+    shifts that block's scale byte by its exponent and keeps its codes (while
+    nothing clamps); a gather picks smoothed rows."""
+    rng = np.random.default_rng(141)
+    M, K = 6, 128
+    x = torch.from_numpy(rng.normal(0, 1, (M, K)).astype(np.float32)).to(torch.bfloat16)
+    xb = bf16_bits(x)
+    ones = bf16_bits(torch.ones(K, dtype=torch.bfloat16))
+    for rule in ("ocp", "uos"):
+        a = oracle.quantize_act(xb, scale_rule=rule)
+        b = oracle.quantize_act_smooth(xb, ones, scale_rule=rule)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    c8 = oracle.quantize_act_fp8(xb)
+    d8 = oracle.quantize_act_fp8_smooth(xb, ones)
+    assert np.array_equal(c8[0], d8[0]) and np.array_equal(c8[1], d8[1])
+    e = np.array([3, -5, 0, 9])
+    pw = torch.from_numpy(np.repeat(2.0 ** e, 32).astype(np.float32)).to(torch.bfloat16)
+    c, s_ = oracle.quantize_act_smooth(xb, bf16_bits(pw))
+    c0, s0 = oracle.quantize_act(xb)
+    assert np.array_equal(c, c0) and np.array_equal(s_.astype(int), s0.astype(int) + e)
+    idx = np.array([5, 0, 5], dtype=np.int32)
+    g = oracle.quantize_act_smooth(xb, bf16_bits(pw), row_index=idx)
+    assert np.array_equal(g[0], c[idx]) and np.array_equal(g[1], s_[idx])
