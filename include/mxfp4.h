@@ -131,6 +131,20 @@ int mxfp4_quantize_act(const void* x_bf16, int64_t ldx, const int32_t* row_index
                        uint32_t flags, hipStream_t stream);
 
 /*
+ * mxfp4_quantize_act with the Smooth pre-scale (vLLM-Omni guide, pre-quantized
+ * single-scale weights: W4A4 and W4A8 quantize x * mul_scale, the Smooth
+ * tensor held in the activation dtype): the values quantized are
+ * h[k] = bf16_RNE(x[k] * smooth[k]), the product of the two bf16 values
+ * formed in fp32.  Arguments as for mxfp4_quantize_act, plus
+ *   smooth_bf16  [K] bf16, device, read, 16-byte aligned: the per-input-channel
+ *                factor (a checkpoint's fp32 mul_scale rounded to bf16)
+ *   flags        0 or MXFP4_SCALE_UOS
+ */
+int mxfp4_quantize_act_smooth(const void* x_bf16, int64_t ldx, const int32_t* row_index,
+                              const void* smooth_bf16, int64_t M, int64_t K, uint8_t* codes,
+                              uint8_t* scales, uint32_t flags, hipStream_t stream);
+
+/*
  * Y = A * B^T over MXFP4 operands with fp32 accumulation on gfx950's
  * block-scaled MFMA (AMD blog, closing list: both operands MXFP4, no
  * separate dequantize step).  y[m][n] = sum_k A[m,k] * B[n,k] where
@@ -226,6 +240,12 @@ size_t mxfp4_linear_workspace_size(int64_t M, int64_t N, int64_t K);
 int mxfp8_quantize_act(const void* x_bf16, int64_t ldx, const int32_t* row_index, int64_t M,
                        int64_t K, uint8_t* codes, uint8_t* scales, uint32_t flags,
                        hipStream_t stream);
+
+/* mxfp8_quantize_act with the Smooth pre-scale (as mxfp4_quantize_act_smooth);
+   flags must be 0. */
+int mxfp8_quantize_act_smooth(const void* x_bf16, int64_t ldx, const int32_t* row_index,
+                              const void* smooth_bf16, int64_t M, int64_t K, uint8_t* codes,
+                              uint8_t* scales, uint32_t flags, hipStream_t stream);
 
 /*
  * The mixed FP8 x FP4 GEMM of W4A8: y[m][n] = round(sum_k A[m,k] * B[n,k] +

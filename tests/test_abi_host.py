@@ -223,3 +223,15 @@ def test_w4a8_argument_checks(lib):
     ws = lib.mxfp4_linear_w4a8_workspace_size
     assert ws(8, 256, 4096) == 8 * 4096 + 8 * 128
     assert ws(3, 256, 96) == 512 + 9
+
+
+def test_smooth_quantize_argument_checks(lib):
+    for name, good_flag in (("mxfp4_quantize_act_smooth", 2), ("mxfp8_quantize_act_smooth", 0)):
+        f = getattr(lib, name)
+        #        x     ldx  ri    smooth M  K   codes scales flags stream
+        assert f(FAKE, 64, None, FAKE, 4, 48, FAKE, FAKE, 0, None) == -1       # K % 32
+        assert f(FAKE, 64, None, None, 4, 64, FAKE, FAKE, 0, None) == -1       # smooth NULL
+        assert f(FAKE, 64, None, ODD, 4, 64, FAKE, FAKE, 0, None) == -2        # smooth align
+        assert f(FAKE, 64, None, FAKE, 4, 64, FAKE, FAKE, 4, None) == -1       # flags
+        assert f(FAKE, 64, None, FAKE, 0, 64, FAKE, FAKE, good_flag, None) == 0
+    assert lib.mxfp8_quantize_act_smooth(FAKE, 64, None, FAKE, 4, 64, FAKE, FAKE, 2, None) == -1

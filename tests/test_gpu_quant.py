@@ -337,3 +337,44 @@ def test_requant_uos_tiny_and_subset(mx, bf16_intermediate):
     got_c, got_s = u8(dc), u8(ds)
     assert np.array_equal(got_c[sel], ref[0][sel]) and np.array_equal(got_s[sel], ref[1][sel])
     assert (got_c[[1, 2, 5]] == 0x5A).all() and (got_s[[1, 2, 5]] == 0xA5).all()
+
+
+
+# ---- Smooth pre-scale ------------------------------------------------------------
+def smooth_vector(K, seed):
+    rng = np.random.default_rng(seed)
+    return torch.from_numpy((rng.uniform(0.05, 4, K) * 2.0 ** rng.integers(-3, 4, K))
+                            .astype(np.float32)).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("M,K,gather,rule", [(1, 32, False, "ocp"), (37, 544, False, "ocp"),
+                                             (64, 4096, False, "uos"), (50, 1024, True, "ocp"),
+                                             (4096, 4096, False, "ocp")])
+def test_act_quant_smooth(mx, M, K, gather, rule):
+    """Act-quant of bf16(x * smooth), bit-exact against the oracle (gather, both
+    scale rules, the large-output form)."""
+    say(f"act_quant smooth M={M} K={K} gather={gather} {rule}")
+    x = synth.activations(M, K, seed=M + 1, outlier_seed=K + 1)
+    sm = smooth_vector(K, seed=K)
+    idx = np.random.default_rng(3).integers(0, M, size=2 * M).astype(np.int32) if gather else None
+    Mo = M if idx is None else idx.size
+    gc = Guarded((Mo, K // 2), torch.uint8)
+    gs = Guarded((Mo, K // 32), torch.uint8)
+    mx.mxfp4_quantize_act_smooth(x.to(dev()), sm.to(dev()), gc.view, gs.view,
+                                 row_index=None if idx is None else torch.from_numpy(idx).to(dev()),
+                                 scale_rule=rule)
+    torch.cuda.synchronize()
+    assert gc.intact() and gs.intact()
+    oc, os_ = oracle.quantize_act_smooth(bf16_bits(x), bf16_bits(sm), row_index=idx,
+                                         scale_rule=rule)
+    assert_same((u8(gc.view), u8(gs.view)), (oc, os_), "smooth")
+
+
+@pytest.mark.parametrize("M,K", [(5, 4096), (300, 1024)])
+def test_act_quant_fp8_smooth(mx, M, K):
+    say(f"act_quant_fp8 smooth M={M} K={K}")
+    x = synth.activations(M, K, seed=M + 2, outlier_seed=K + 2)
+    sm = smooth_vector(K, seed=K + 1)
+    c, s = mx.mxfp8_quantize_act_smooth(x.to(dev()), sm.to(dev()))
+    oc, os_ = oracle.quantize_act_fp8_smooth(bf16_bits(x), bf16_bits(sm))
+    assert_same((u8(c), u8(s)), (oc, os_), "fp8 smooth")

@@ -50,6 +50,10 @@ def _load_library() -> ctypes.CDLL:
     lib.mxfp4_grouped_gemm.restype = ctypes.c_int
     lib.mxfp4_linear_bf16.argtypes = [P, I, I, I, I, P, P, P, P, ctypes.c_int, P, SZ, U32, P]
     lib.mxfp4_linear_bf16.restype = ctypes.c_int
+    lib.mxfp4_quantize_act_smooth.argtypes = [P, I, P, P, I, I, P, P, U32, P]
+    lib.mxfp4_quantize_act_smooth.restype = ctypes.c_int
+    lib.mxfp8_quantize_act_smooth.argtypes = [P, I, P, P, I, I, P, P, U32, P]
+    lib.mxfp8_quantize_act_smooth.restype = ctypes.c_int
     lib.mxfp8_quantize_act.argtypes = [P, I, P, I, I, P, P, U32, P]
     lib.mxfp8_quantize_act.restype = ctypes.c_int
     lib.mxfp4_gemm_w4a8.argtypes = [P, P, P, P, I, I, I, P, P, ctypes.c_int, U32, P]
@@ -82,6 +86,7 @@ EXPORTED_SYMBOLS = ("mxfp4_requant_from_nvfp4", "mxfp4_requant_from_nvfp4_subset
                     "mxfp4_linear_workspace_size", "mxfp4_silu_mul_quantize",
                     "mxfp4_moe_combine", "mxfp8_quantize_act", "mxfp4_gemm_w4a8",
                     "mxfp4_linear_w4a8_bf16", "mxfp4_linear_w4a8_workspace_size",
+                    "mxfp4_quantize_act_smooth", "mxfp8_quantize_act_smooth",
                     "mxfp4_status_string", "mxfp4_version")
 
 
@@ -287,6 +292,48 @@ def mxfp4_linear_bf16(x, b_codes, b_scales, y=None, *, bias=None, K=None,
     return y
 
 
+def _quantize_smooth(fn, elem_cols, x, smooth, codes, scales, row_index, K, flags, stream):
+    _need(x, "x", torch.bfloat16)
+    dev = x.device
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [rows, ldx]")
+    ldx = x.shape[1]
+    K = ldx if K is None else int(K)
+    _need(smooth, "smooth", torch.bfloat16, dev)
+    if smooth.shape != (K,):
+        raise ValueError("smooth must be [K]")
+    if row_index is not None:
+        _need(row_index, "row_index", torch.int32, dev)
+        M = row_index.shape[0]
+    else:
+        M = x.shape[0]
+    if codes is None:
+        codes = torch.empty((M, elem_cols(K)), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
+    _need(codes, "codes", torch.uint8, dev)
+    _need(scales, "scales", torch.uint8, dev)
+    if codes.shape != (M, elem_cols(K)) or scales.shape != (M, K // 32):
+        raise ValueError("output shapes do not match")
+    _check(fn, getattr(_lib, fn)(_ptr(x), ldx, _ptr(row_index), _ptr(smooth), M, K, _ptr(codes),
+                                 _ptr(scales), flags, _stream(stream, dev)))
+    return codes, scales
+
+
+def mxfp4_quantize_act_smooth(x, smooth, codes=None, scales=None, *, row_index=None, K=None,
+                              scale_rule="ocp", stream=None):
+    """mxfp4_quantize_act of bf16(x * smooth) (smooth: bf16 [K])."""
+    return _quantize_smooth("mxfp4_quantize_act_smooth", lambda k: k // 2, x, smooth, codes,
+                            scales, row_index, K, _rule_flag(scale_rule), stream)
+
+
+def mxfp8_quantize_act_smooth(x, smooth, codes=None, scales=None, *, row_index=None, K=None,
+                              stream=None):
+    """mxfp8_quantize_act of bf16(x * smooth) (smooth: bf16 [K])."""
+    return _quantize_smooth("mxfp8_quantize_act_smooth", lambda k: k, x, smooth, codes, scales,
+                            row_index, K, 0, stream)
+
+
 def mxfp8_quantize_act(x, codes=None, scales=None, *, row_index=None, K=None, stream=None):
     """W4A8 activations: bf16 x [R, ldx] -> E4M3 codes [M, K] (one byte each) and
     E8M0 bytes [M, K/32]; M = R, or len(row_index) with row i from x[row_index[i]]."""
@@ -461,7 +508,8 @@ __all__ = ["mxfp4_requant_from_nvfp4", "mxfp4_quantize_act", "mxfp4_gemm",
            "mxfp4_grouped_gemm", "mxfp4_linear_bf16", "mxfp4_gemm_workspace_size",
            "mxfp4_linear_workspace_size", "mxfp4_silu_mul_quantize", "mxfp4_moe_combine",
            "mxfp8_quantize_act", "mxfp4_gemm_w4a8", "mxfp4_linear_w4a8_bf16",
-           "mxfp4_linear_w4a8_workspace_size",
+           "mxfp4_linear_w4a8_workspace_size", "mxfp4_quantize_act_smooth",
+           "mxfp8_quantize_act_smooth",
            "mxfp4_status_string",
            "mxfp4_version", "Mxfp4Error", "LIBRARY_PATH", "EXPORTED_SYMBOLS",
            "MXFP4_OUT_BF16", "MXFP4_OUT_FP32", "MXFP4_REQ_INTERMEDIATE_BF16",

@@ -7,9 +7,11 @@
 
 namespace mx {
 
+// smooth: bf16 [K] per-channel pre-scale (values quantized: bf16(x * smooth)),
+// or nullptr; 16-byte aligned.
 hipError_t launch_act_quant(const uint16_t* x, int64_t ldx, const int32_t* row_index,
                             int64_t M, int64_t K, uint8_t* codes, uint8_t* scales, bool uos,
-                            hipStream_t stream);
+                            hipStream_t stream, const uint16_t* smooth = nullptr);
 
 // tensors == nullptr: all T tensors; else the n_tensors listed (host memory,
 // each in [0, T)).  uos: the Qmax = 7.25 shared-exponent rule, else OCP's.
@@ -79,7 +81,7 @@ bool skinny_gemm_supported(int64_t M, int64_t N, int64_t K, const void* x, const
 // W4A8: A is MXFP8 (E4M3 codes [M][K], E8M0 [M][K/32]), B MXFP4.
 hipError_t launch_act_quant_fp8(const uint16_t* x, int64_t ldx, const int32_t* row_index,
                                 int64_t M, int64_t K, uint8_t* codes, uint8_t* scales,
-                                hipStream_t stream);
+                                hipStream_t stream, const uint16_t* smooth = nullptr);
 hipError_t launch_gemm_w4a8(const uint8_t* a_codes, const uint8_t* a_scales,
                             const uint8_t* b_codes, const uint8_t* b_scales, int64_t M, int64_t N,
                             int64_t K, void* y, const uint16_t* bias, bool out_bf16,

@@ -100,6 +100,21 @@ int mxfp4_quantize_act(const void* x_bf16, int64_t ldx, const int32_t* row_index
                                          stream));
 }
 
+int mxfp4_quantize_act_smooth(const void* x_bf16, int64_t ldx, const int32_t* row_index,
+                              const void* smooth_bf16, int64_t M, int64_t K, uint8_t* codes,
+                              uint8_t* scales, uint32_t flags, hipStream_t stream) {
+    if (M < 0 || check_k(K) != MXFP4_OK || ldx < K) return MXFP4_EINVAL;
+    if ((flags & ~(uint32_t)MXFP4_SCALE_UOS) != 0) return MXFP4_EINVAL;
+    if (M == 0) return MXFP4_OK;
+    if (!x_bf16 || !smooth_bf16 || !codes || !scales) return MXFP4_EINVAL;
+    if (!aligned(x_bf16, 16) || ldx % 8 != 0 || !aligned(codes, 16) || !aligned(smooth_bf16, 16))
+        return MXFP4_EALIGN;
+    if (row_index && !aligned(row_index, 4)) return MXFP4_EALIGN;
+    return from_hip(mx::launch_act_quant(static_cast<const uint16_t*>(x_bf16), ldx, row_index,
+                                         M, K, codes, scales, (flags & MXFP4_SCALE_UOS) != 0,
+                                         stream, static_cast<const uint16_t*>(smooth_bf16)));
+}
+
 int mxfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
                const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, void* y,
                int out_dtype, void* workspace, size_t workspace_bytes, uint32_t flags,
@@ -161,6 +176,21 @@ int mxfp8_quantize_act(const void* x_bf16, int64_t ldx, const int32_t* row_index
     if (row_index && !aligned(row_index, 4)) return MXFP4_EALIGN;
     return from_hip(mx::launch_act_quant_fp8(static_cast<const uint16_t*>(x_bf16), ldx,
                                              row_index, M, K, codes, scales, stream));
+}
+
+int mxfp8_quantize_act_smooth(const void* x_bf16, int64_t ldx, const int32_t* row_index,
+                              const void* smooth_bf16, int64_t M, int64_t K, uint8_t* codes,
+                              uint8_t* scales, uint32_t flags, hipStream_t stream) {
+    if (M < 0 || check_k(K) != MXFP4_OK || ldx < K) return MXFP4_EINVAL;
+    if (flags != 0) return MXFP4_EINVAL;
+    if (M == 0) return MXFP4_OK;
+    if (!x_bf16 || !smooth_bf16 || !codes || !scales) return MXFP4_EINVAL;
+    if (!aligned(x_bf16, 16) || ldx % 8 != 0 || !aligned(codes, 16) || !aligned(smooth_bf16, 16))
+        return MXFP4_EALIGN;
+    if (row_index && !aligned(row_index, 4)) return MXFP4_EALIGN;
+    return from_hip(mx::launch_act_quant_fp8(static_cast<const uint16_t*>(x_bf16), ldx,
+                                             row_index, M, K, codes, scales, stream,
+                                             static_cast<const uint16_t*>(smooth_bf16)));
 }
 
 int mxfp4_gemm_w4a8(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,

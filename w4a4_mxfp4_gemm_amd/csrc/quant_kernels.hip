@@ -63,13 +63,29 @@ __device__ __forceinline__ uint32_t glu_pair(uint32_t gw, uint32_t uw) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{h[0], h[1]}, bf16x2_t));
 }
 
-template <int ROWS, bool NT_OUT, bool UOS, bool GLU = false>
+// Two packed bf16 values times two packed bf16 Smooth factors, each product in
+// fp32 rounded to bf16 (RNE), packed the same way.
+__device__ __forceinline__ uint32_t smooth_pair(uint32_t xw, uint32_t sw) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    const float p0 = __uint_as_float(xw << 16) * __uint_as_float(sw << 16);
+    const float p1 = __uint_as_float(xw & 0xFFFF0000u) * __uint_as_float(sw & 0xFFFF0000u);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{p0, p1}, bf16x2_t));
+}
+
+// SMOOTH: the values quantized are bf16(x * smooth[k]) (smooth: bf16 [K], the
+// per-channel Smooth pre-scale), each product in fp32 (exact for two bf16
+// values outside fp32's subnormal range) rounded to bf16.
+template <int ROWS, bool NT_OUT, bool UOS, bool GLU = false, bool SMOOTH = false>
 __global__ __launch_bounds__(256) void act_quant_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const int32_t* __restrict__ row_index,
-    int64_t M, int64_t K, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+    int64_t M, int64_t K, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+    const uint16_t* __restrict__ smooth) {
     const int64_t chunks = K / 8;                     // 16-byte chunks per row; multiple of 4
     const int64_t kq = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (kq >= chunks) return;                         // whole quads leave together
+    uint4 sm = make_uint4(0, 0, 0, 0);
+    if constexpr (SMOOTH) sm = *reinterpret_cast<const uint4*>(smooth + kq * 8);
     for (int64_t m0 = (int64_t)blockIdx.y * ROWS; m0 < M; m0 += (int64_t)gridDim.y * ROWS) {
         uint4 raw[ROWS];
         uint4 up[GLU ? ROWS : 1];
@@ -106,6 +122,11 @@ __global__ __launch_bounds__(256) void act_quant_kernel(
                 const uint32_t uv[4] = {up[r].x, up[r].y, up[r].z, up[r].w};
 #pragma unroll
                 for (int i = 0; i < 4; ++i) w[i] = glu_pair(w[i], uv[i]);
+            }
+            if constexpr (SMOOTH) {
+                const uint32_t sv[4] = {sm.x, sm.y, sm.z, sm.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) w[i] = smooth_pair(w[i], sv[i]);
             }
             // amax over the 8 values as bf16 magnitudes (monotone as integers;
             // NaN and Inf patterns sort above every finite value).
@@ -161,13 +182,16 @@ __device__ __forceinline__ uint32_t e4m3_code(uint32_t bf16, float inv) {
     return c | ((bf16 >> 8) & 0x80u);
 }
 
-template <int ROWS>
+template <int ROWS, bool SMOOTH = false>
 __global__ __launch_bounds__(256) void act_quant_fp8_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const int32_t* __restrict__ row_index,
-    int64_t M, int64_t K, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+    int64_t M, int64_t K, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+    const uint16_t* __restrict__ smooth) {
     const int64_t chunks = K / 8;
     const int64_t kq = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (kq >= chunks) return;                         // whole quads leave together
+    uint4 sm = make_uint4(0, 0, 0, 0);
+    if constexpr (SMOOTH) sm = *reinterpret_cast<const uint4*>(smooth + kq * 8);
     for (int64_t m0 = (int64_t)blockIdx.y * ROWS; m0 < M; m0 += (int64_t)gridDim.y * ROWS) {
         uint4 raw[ROWS];
 #pragma unroll
@@ -182,7 +206,12 @@ __global__ __launch_bounds__(256) void act_quant_fp8_kernel(
         for (int r = 0; r < ROWS; ++r) {
             const int64_t m = m0 + r;
             if (m >= M) break;                        // uniform across the workgroup
-            const uint32_t w[4] = {raw[r].x, raw[r].y, raw[r].z, raw[r].w};
+            uint32_t w[4] = {raw[r].x, raw[r].y, raw[r].z, raw[r].w};
+            if constexpr (SMOOTH) {
+                const uint32_t sv[4] = {sm.x, sm.y, sm.z, sm.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) w[i] = smooth_pair(w[i], sv[i]);
+            }
             u16x2 a = __builtin_bit_cast(u16x2, w[0] & 0x7FFF7FFFu);
 #pragma unroll
             for (int i = 1; i < 4; ++i)
@@ -210,13 +239,18 @@ __global__ __launch_bounds__(256) void act_quant_fp8_kernel(
 
 hipError_t launch_act_quant_fp8(const uint16_t* x, int64_t ldx, const int32_t* row_index,
                                 int64_t M, int64_t K, uint8_t* codes, uint8_t* scales,
-                                hipStream_t stream) {
+                                hipStream_t stream, const uint16_t* smooth) {
     constexpr int ROWS = 2;
     const int64_t gx = (K / 8 + 255) / 256;
     int64_t gy = (M + ROWS - 1) / ROWS;
     if (gy > 65535) gy = 65535;
-    hipLaunchKernelGGL(act_quant_fp8_kernel<ROWS>, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0,
-                       stream, x, ldx, row_index, M, K, codes, scales);
+    const dim3 grid((unsigned)gx, (unsigned)gy);
+    if (smooth)
+        hipLaunchKernelGGL((act_quant_fp8_kernel<ROWS, true>), grid, dim3(256), 0, stream, x, ldx,
+                           row_index, M, K, codes, scales, smooth);
+    else
+        hipLaunchKernelGGL((act_quant_fp8_kernel<ROWS, false>), grid, dim3(256), 0, stream, x,
+                           ldx, row_index, M, K, codes, scales, smooth);
     return hipGetLastError();
 }
 
@@ -364,7 +398,7 @@ __global__ __launch_bounds__(256) void requant_kernel(
 
 hipError_t launch_act_quant(const uint16_t* x, int64_t ldx, const int32_t* row_index,
                             int64_t M, int64_t K, uint8_t* codes, uint8_t* scales, bool uos,
-                            hipStream_t stream) {
+                            hipStream_t stream, const uint16_t* smooth) {
     constexpr int ROWS = 2;            // 1 and 4 measured slower
     const int64_t chunks = K / 8;
     const int64_t gx = (chunks + 255) / 256;
@@ -378,13 +412,21 @@ hipError_t launch_act_quant(const uint16_t* x, int64_t ldx, const int32_t* row_i
     const dim3 grid((unsigned)gx, (unsigned)gy);
     auto go = [&](auto kernel) {
         hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, x, ldx, row_index, M, K, codes,
-                           scales);
+                           scales, smooth);
     };
-    if (uos)
+    if (smooth) {
+        if (uos)
+            nt_out ? go(act_quant_kernel<ROWS, true, true, false, true>)
+                   : go(act_quant_kernel<ROWS, false, true, false, true>);
+        else
+            nt_out ? go(act_quant_kernel<ROWS, true, false, false, true>)
+                   : go(act_quant_kernel<ROWS, false, false, false, true>);
+    } else if (uos) {
         nt_out ? go(act_quant_kernel<ROWS, true, true>) : go(act_quant_kernel<ROWS, false, true>);
-    else
+    } else {
         nt_out ? go(act_quant_kernel<ROWS, true, false>)
                : go(act_quant_kernel<ROWS, false, false>);
+    }
     return hipGetLastError();
 }
 
@@ -399,10 +441,10 @@ hipError_t launch_silu_mul_quantize(const uint16_t* gate_up, int64_t ldg, int64_
     // the codes feed the down GEMM next: normal stores
     if (uos)
         hipLaunchKernelGGL((act_quant_kernel<ROWS, false, true, true>), grid, dim3(256), 0,
-                           stream, gate_up, ldg, nullptr, M, I, codes, scales);
+                           stream, gate_up, ldg, nullptr, M, I, codes, scales, nullptr);
     else
         hipLaunchKernelGGL((act_quant_kernel<ROWS, false, false, true>), grid, dim3(256), 0,
-                           stream, gate_up, ldg, nullptr, M, I, codes, scales);
+                           stream, gate_up, ldg, nullptr, M, I, codes, scales, nullptr);
     return hipGetLastError();
 }
 
