@@ -464,6 +464,7 @@ def w4a8_workload(torch, mx, synth):
     ph.add("step", lambda r: [linear(r, M) for M in Ms])
     ph.add("gemm", lambda r: [gemm(r, M) for M in Ms])
     for M in Ms:
+        ph.add(f"linear_M{M}", lambda r, M=M: linear(r, M))
         ph.add(f"act_quant_M{M}", lambda r, M=M: mx.mxfp8_quantize_act(xs[M], *xq[M]))
         ph.add(f"gemm_M{M}", lambda r, M=M: gemm(r, M))
     ph.add("prefill_gemm", lambda r: mx.mxfp4_gemm_w4a8(xpq[0], xpq[1], wpc, wps, yp))
@@ -474,7 +475,9 @@ def w4a8_workload(torch, mx, synth):
         wbytes = N * K * (0.5 + 1 / 32)
         gb = [wbytes + M * K * (1 + 1 / 32) + M * N * 2 + N * 2 for M in Ms]
         gemm_gbps = sum(gb) / (t["gemm"] * 1e-3) / 1e9
-        per_m = {str(M): {"act_quant_us": round(t[f"act_quant_M{M}"] * 1e3, 2),
+        per_m = {str(M): {"linear_us": round(t[f"linear_M{M}"] * 1e3, 2),
+                          "linear_one_launch": mx.mxfp4_linear_w4a8_workspace_size(M, N, K) == 0,
+                          "act_quant_us": round(t[f"act_quant_M{M}"] * 1e3, 2),
                           "gemm_us": round(t[f"gemm_M{M}"] * 1e3, 2),
                           "gemm_GBps": round(b / (t[f"gemm_M{M}"] * 1e-3) / 1e9, 1)}
                  for M, b in zip(Ms, gb)}

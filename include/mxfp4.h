@@ -266,9 +266,12 @@ int mxfp4_gemm_w4a8(const uint8_t* a_codes, const uint8_t* a_scales, const uint8
                     hipStream_t stream);
 
 /*
- * One W4A8 linear layer on bf16 activations: mxfp8_quantize_act into the
- * caller's workspace (mxfp4_linear_w4a8_workspace_size(M, N, K) bytes,
- * 16-byte aligned), then mxfp4_gemm_w4a8 -- the same y bit for bit.
+ * One W4A8 linear layer on bf16 activations: mxfp8_quantize_act then
+ * mxfp4_gemm_w4a8, the same y bit for bit.  For the decode shapes of
+ * mxfp4_linear_bf16 (M <= 16, K = 2048 or 4096, N >= 16) it is one launch
+ * that quantizes the activations inside the GEMM kernel; otherwise the two
+ * launches run through the caller's workspace
+ * (mxfp4_linear_w4a8_workspace_size(M, N, K) bytes, 16-byte aligned).
  * Arguments as for mxfp4_linear_bf16; flags must be 0.
  */
 int mxfp4_linear_w4a8_bf16(const void* x_bf16, int64_t ldx, int64_t M, int64_t N, int64_t K,
@@ -276,7 +279,8 @@ int mxfp4_linear_w4a8_bf16(const void* x_bf16, int64_t ldx, int64_t M, int64_t N
                            const void* bias_bf16, void* y, int out_dtype, void* workspace,
                            size_t workspace_bytes, uint32_t flags, hipStream_t stream);
 
-/* Workspace bytes mxfp4_linear_w4a8_bf16 needs (the MXFP8 activations). */
+/* Workspace bytes mxfp4_linear_w4a8_bf16 needs: 0 for the one-launch shapes,
+   else the MXFP8 activations. */
 size_t mxfp4_linear_w4a8_workspace_size(int64_t M, int64_t N, int64_t K);
 
 /*

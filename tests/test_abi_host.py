@@ -212,16 +212,17 @@ def test_w4a8_argument_checks(lib):
     assert g(FAKE, FAKE, FAKE, FAKE, 4, 16, 64, ODD, FAKE, 0, 0, None) == -2     # bias
     assert g(FAKE, FAKE, FAKE, FAKE, 0, 16, 64, None, FAKE, 0, 0, None) == 0     # M == 0
     f = lib.mxfp4_linear_w4a8_bf16
-    assert f(FAKE, 4096, 8, 256, 4096, FAKE, FAKE, None, FAKE, 0, None, 0, 0, None) == -1  # ws
+    assert f(FAKE, 4096, 17, 256, 4096, FAKE, FAKE, None, FAKE, 0, None, 0, 0, None) == -1  # ws
     assert f(FAKE, 4096, 8, 256, 4096, FAKE, FAKE, None, FAKE, 0, FAKE, 1 << 20, 1,
              None) == -1                                                           # flags
     assert f(FAKE, 4096, 8, 256, 4096, FAKE, FAKE, ODD, FAKE, 0, FAKE, 1 << 20, 0,
              None) == -2                                                           # bias
-    assert f(FAKE, 4096, 8, 256, 4096, FAKE, FAKE, None, FAKE, 0, ODD, 1 << 20, 0,
+    assert f(FAKE, 4096, 17, 256, 4096, FAKE, FAKE, None, FAKE, 0, ODD, 1 << 20, 0,
              None) == -2                                                           # ws align
     assert f(FAKE, 4096, 0, 256, 4096, FAKE, FAKE, None, FAKE, 0, None, 0, 0, None) == 0
     ws = lib.mxfp4_linear_w4a8_workspace_size
-    assert ws(8, 256, 4096) == 8 * 4096 + 8 * 128
+    assert ws(8, 256, 4096) == 0                    # one launch: no workspace
+    assert ws(17, 256, 4096) == 17 * 4096 + 17 * 128
     assert ws(3, 256, 96) == 512 + 9
 
 

@@ -277,3 +277,34 @@ def test_w4a8_in_block_truncation_model(mx, M, K):
     bound = w4a8_truncation_bound(amax, bmax, pm, pn)
     exact = np.repeat((448 + x)[:, None], 8, axis=1).reshape(-1)
     assert (np.abs(y.reshape(-1) - exact) <= bound).all()
+
+
+
+@pytest.mark.parametrize("M,N,K,ldx", [(1, 1000, 4096, 4096), (5, 300, 2048, 2048),
+                                       (16, 2048, 4096, 4104), (8, 520, 2048, 2056),
+                                       (17, 300, 4096, 4096)])
+def test_linear_w4a8_one_launch_matches_two(mx, M, N, K, ldx):
+    """The one-launch W4A8 decode call (M <= 16, K = 2048/4096: MXFP8 quantized
+    inside the GEMM kernel) equals mxfp8_quantize_act followed by
+    mxfp4_gemm_w4a8 bit for bit -- rows wider than K, NaN and Inf in x, the
+    bias, both output types; M = 17 takes the two-launch form."""
+    say(f"linear w4a8 fused M={M} N={N} K={K} ldx={ldx}")
+    d = dev()
+    x = synth.activations(M, ldx, seed=M + N, outlier_seed=K + 5).to(d)
+    if M >= 5:
+        x[1, 40] = float("nan")
+        x[2, K - 1] = float("inf")
+        x[4, 64:96] = 0.0
+    bc, bs = [t.to(d) for t in synth.canonical_mxfp4(N, K, seed=N + 3)]
+    bias = torch.randn(N, generator=torch.Generator().manual_seed(N)).to(torch.bfloat16).to(d)
+    assert (mx.mxfp4_linear_w4a8_workspace_size(M, N, K) == 0) == (M <= 16)
+    xc, xs_ = mx.mxfp8_quantize_act(x, K=K)
+    for dt in (torch.bfloat16, torch.float32):
+        ref = mx.mxfp4_gemm_w4a8(xc, xs_, bc, bs, bias=bias, out_dtype=dt)
+        gy = Guarded((M, N), dt)
+        mx.mxfp4_linear_w4a8_bf16(x, bc, bs, gy.view, bias=bias, K=K)
+        torch.cuda.synchronize()
+        assert gy.intact(), "write outside y"
+        a, b = gy.view.float().cpu(), ref.float().cpu()
+        nan = torch.isnan(a) & torch.isnan(b)
+        assert bool(((a.view(torch.int32) == b.view(torch.int32)) | nan).all()), dt

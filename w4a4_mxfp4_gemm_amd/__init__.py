@@ -401,7 +401,9 @@ def mxfp4_linear_w4a8_workspace_size(M: int, N: int, K: int) -> int:
 def mxfp4_linear_w4a8_bf16(x, b_codes, b_scales, y=None, *, bias=None, K=None,
                            out_dtype=torch.bfloat16, workspace=None, stream=None):
     """W4A8 linear: y [M, N] = MXFP8(x) [M, K] * B [N, K]^T + bias from bf16 x
-    [M, ldx] (mxfp8_quantize_act then mxfp4_gemm_w4a8, bit for bit)."""
+    [M, ldx] (mxfp8_quantize_act then mxfp4_gemm_w4a8, bit for bit; one launch
+    for decode shapes).  A workspace is allocated when one is needed and none
+    is given."""
     _need(x, "x", torch.bfloat16)
     dev = x.device
     _need(b_codes, "b_codes", torch.uint8, dev)
@@ -419,12 +421,13 @@ def mxfp4_linear_w4a8_bf16(x, b_codes, b_scales, y=None, *, bias=None, K=None,
     _need(y, "y", y.dtype, dev)
     if y.shape != (M, N):
         raise ValueError("y must be [M, N]")
-    if workspace is None:
-        workspace = torch.empty((max(mxfp4_linear_w4a8_workspace_size(M, N, K), 1),),
-                                dtype=torch.uint8, device=dev)
+    need = mxfp4_linear_w4a8_workspace_size(M, N, K)
+    if workspace is None and need:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
+    ws_ptr, ws_bytes = (None, 0) if workspace is None else (_ptr(workspace), workspace.numel())
     _check("mxfp4_linear_w4a8_bf16", _lib.mxfp4_linear_w4a8_bf16(
         _ptr(x), ldx, M, N, K, _ptr(b_codes), _ptr(b_scales), _ptr(bias), _ptr(y),
-        _out_dtype(y.dtype), _ptr(workspace), workspace.numel(), 0, _stream(stream, dev)))
+        _out_dtype(y.dtype), ws_ptr, ws_bytes, 0, _stream(stream, dev)))
     return y
 
 

@@ -187,6 +187,78 @@ __device__ __forceinline__ void quant_raw(Frag<SPW>& f, const RawX<SPW>& r) {
     }
 }
 
+// The W4A8 form of the two steps above: the lane's 32 E4M3 bytes are half g%2
+// of two MX blocks (Frag8 layout), so it loads those two 16-value halves of
+// bf16 and quantizes them by the MXFP8 rule.  Each block's other half sits in
+// lane ^ 16, whose magnitude maximum completes the block's amax; lane group g
+// then supplies MFMA q's scale for block 4q+g, which lane group 0 (g = 0: lo,
+// g = 2: hi), 2 (g = 1: lo) or 3 (g = 3: hi) computed.  The codes and scales
+// equal those of the MXFP8 act-quant kernel.
+template <int SPW, int NW>
+__device__ __forceinline__ void load_raw8(RawX<SPW>& r, const uint16_t* x, int64_t ldx,
+                                          int64_t row) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int g = lane >> 4;
+    const uint16_t* xrow = x + row * ldx + 16 * (g & 1);
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) {
+        const int kb0 = (wave + NW * j) * 16;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int lo = kb0 + 4 * q + (g >> 1);
+            const v4u* pl = reinterpret_cast<const v4u*>(xrow + (int64_t)lo * 32);
+            const v4u* ph = reinterpret_cast<const v4u*>(xrow + (int64_t)(lo + 2) * 32);
+            r.v[j][q][0] = pl[0];
+            r.v[j][q][1] = pl[1];
+            r.v[j][q][2] = ph[0];
+            r.v[j][q][3] = ph[1];
+        }
+    }
+}
+
+template <int SPW>
+__device__ __forceinline__ void quant_raw8(Frag8<SPW>& f, const RawX<SPW>& r) {
+    typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4, r16 = lane & 15;
+    auto half_amax = [](const v4u& a, const v4u& b) {
+        u16x2_t m = __builtin_bit_cast(u16x2_t, a[0] & 0x7FFF7FFFu);
+#pragma unroll
+        for (int i = 1; i < 4; ++i)
+            m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2_t, a[i] & 0x7FFF7FFFu));
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2_t, b[i] & 0x7FFF7FFFu));
+        return max((uint32_t)m[0], (uint32_t)m[1]);
+    };
+    auto codes16 = [](const v4u& a, const v4u& b, uint32_t byte) {
+        if (byte == 255u) return v4u{0u, 0u, 0u, 0u};
+        const uint32_t wa[4] = {a[0], a[1], a[2], a[3]}, wb[4] = {b[0], b[1], b[2], b[3]};
+        const uint2 ca = e4m3_codes8(wa, byte), cb = e4m3_codes8(wb, byte);
+        return v4u{ca.x, ca.y, cb.x, cb.y};
+    };
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) {
+        uint32_t sw[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            uint32_t alo = half_amax(r.v[j][q][0], r.v[j][q][1]);
+            uint32_t ahi = half_amax(r.v[j][q][2], r.v[j][q][3]);
+            alo = max(alo, (uint32_t)__shfl_xor((int)alo, 16));
+            ahi = max(ahi, (uint32_t)__shfl_xor((int)ahi, 16));
+            const uint32_t blo = mx8_scale_from_bf16_amax(alo);
+            const uint32_t bhi = mx8_scale_from_bf16_amax(ahi);
+            f.c[j][q][0] = codes16(r.v[j][q][0], r.v[j][q][1], blo);
+            f.c[j][q][1] = codes16(r.v[j][q][2], r.v[j][q][3], bhi);
+            const uint32_t from_lo = (uint32_t)__shfl((int)blo, r16 + 32 * (g & 1));
+            const uint32_t from_hi = (uint32_t)__shfl((int)bhi, r16 + 48 * (g & 1));
+            sw[q] = (g < 2 ? from_lo : from_hi) << (8 * g);
+        }
+        f.s[j] = v4u{sw[0], sw[1], sw[2], sw[3]};
+    }
+}
+
 // BF16A: x is bf16 [M][ldx] (xs unused) and each wave quantizes its share of
 // the activations itself while its weight loads stream (UOS: by the Qmax =
 // 7.25 exponent rule).  A8: x is MXFP8 (the W4A8 activations).
@@ -220,7 +292,9 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_skinny_kernel(
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
         const int64_t row = (int64_t)min(mt * 16 + r16, M - 1);
-        if constexpr (BF16A)
+        if constexpr (BF16A && A8)
+            load_raw8<SPW, NW>(xr[mt], reinterpret_cast<const uint16_t*>(x), ldx, row);
+        else if constexpr (BF16A)
             load_raw<SPW, NW>(xr[mt], reinterpret_cast<const uint16_t*>(x), ldx, row);
         else if constexpr (A8)
             load_block8<SPW, NW>(a[mt], x, xs, row, nkb);
@@ -240,7 +314,12 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_skinny_kernel(
     if constexpr (BF16A) {
         asm volatile("" ::: "memory");   // ... and every weight load before the quantization
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) quant_raw<SPW, UOS>(a[mt], xr[mt]);
+        for (int mt = 0; mt < MT; ++mt) {
+            if constexpr (A8)
+                quant_raw8<SPW>(a[mt], xr[mt]);
+            else
+                quant_raw<SPW, UOS>(a[mt], xr[mt]);
+        }
     }
 
     const uint32_t sh = 8u * (uint32_t)g;
@@ -380,6 +459,9 @@ static hipError_t launch_mt(const uint8_t* a, const uint8_t* as, int64_t ldx, co
     if (ldx > 0) {
         // the bf16 form exists for one block at one super-step per wave only
         if constexpr (MT == 1 && SPW == 1) {
+            if constexpr (A8)
+                return out_bf16 ? go(gemm_skinny_kernel<MT, SPW, NW, TPW, true, true, false, true>)
+                                : go(gemm_skinny_kernel<MT, SPW, NW, TPW, false, true, false, true>);
             if (uos)
                 return out_bf16 ? go(gemm_skinny_kernel<MT, SPW, NW, TPW, true, true, true>)
                                 : go(gemm_skinny_kernel<MT, SPW, NW, TPW, false, true, true>);
@@ -448,6 +530,18 @@ hipError_t launch_gemm_skinny_w4a8(const uint8_t* a_codes, const uint8_t* a_scal
                                         bias, out_bf16, stream);
     return launch_k<8, true>(a_codes, a_scales, 0, b_codes, b_scales, M, N, K, y, bias, out_bf16,
                              stream);
+}
+
+hipError_t launch_linear_skinny_w4a8(const uint16_t* x, int64_t ldx, const uint8_t* b_codes,
+                                     const uint8_t* b_scales, int64_t M, int64_t N, int64_t K,
+                                     void* y, const uint16_t* bias, bool out_bf16,
+                                     hipStream_t stream) {
+    const uint8_t* a = reinterpret_cast<const uint8_t*>(x);
+    if (K == 4096)
+        return launch_mt<1, 1, 8, true>(a, nullptr, ldx, b_codes, b_scales, M, N, K, y, bias,
+                                        out_bf16, stream);
+    return launch_mt<1, 1, 4, true>(a, nullptr, ldx, b_codes, b_scales, M, N, K, y, bias,
+                                    out_bf16, stream);
 }
 
 hipError_t launch_linear_skinny(const uint16_t* x, int64_t ldx, const uint8_t* b_codes,

@@ -47,6 +47,12 @@ hipError_t launch_linear_skinny(const uint16_t* x, int64_t ldx, const uint8_t* b
 
 // bias: bf16 [N] added to every row's fp32 sum before the output rounding, or
 // nullptr (16-byte aligned when given).
+// The W4A8 form: x quantized to MXFP8 in the kernel (same shapes).
+hipError_t launch_linear_skinny_w4a8(const uint16_t* x, int64_t ldx, const uint8_t* b_codes,
+                                     const uint8_t* b_scales, int64_t M, int64_t N, int64_t K,
+                                     void* y, const uint16_t* bias, bool out_bf16,
+                                     hipStream_t stream);
+
 hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
                        const uint8_t* b_codes, const uint8_t* b_scales,
                        int64_t M, int64_t N, int64_t K, void* y, const uint16_t* bias,

@@ -146,6 +146,44 @@ __device__ __forceinline__ uint32_t quant_block32_bf16(const uint32_t (&w)[16], 
     return byte;
 }
 
+// E4M3 codes of four packed bf16 pairs under scale byte `byte` (< 255), 8
+// bytes, element 2i+h in byte 2i+h.  gfx950's v_cvt_scalef32_pk_fp8_bf16
+// divides by the scale and rounds to the nearest E4M3 value (ties to even,
+// subnormals included) but turns quotients of 464 and more into the NaN code
+// instead of saturating -- measured against the nearest-value encoder over
+// every bf16 magnitude and scale byte.  So each magnitude is first clamped to
+// 448 * 2^(byte-127), whose bf16 pattern is exponent field byte + 8 with
+// mantissa 0x60 (448 = 1.75 * 2^8); quotients up to 464 round to 448 anyway.
+__device__ __forceinline__ uint2 e4m3_codes8(const uint32_t (&w)[4], uint32_t byte) {
+    typedef short s16x2_t __attribute__((ext_vector_type(2)));
+    const uint32_t lim = ((byte + 8u) << 7) | 0x60u;
+    typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+    const u16x2_t limv = {(unsigned short)lim, (unsigned short)lim};
+    const float scale = e8m0_to_f32(byte);
+    auto clamp = [&](uint32_t x) {
+        const u16x2_t mag =
+            __builtin_elementwise_min(__builtin_bit_cast(u16x2_t, x & 0x7FFF7FFFu), limv);
+        return __builtin_bit_cast(bf16x2_t, __builtin_bit_cast(uint32_t, mag) | (x & 0x80008000u));
+    };
+    uint32_t out[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        s16x2_t v = {0, 0};
+        v = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(v, clamp(w[2 * i]), scale, false);
+        v = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(v, clamp(w[2 * i + 1]), scale, true);
+        out[i] = __builtin_bit_cast(uint32_t, v);
+    }
+    return make_uint2(out[0], out[1]);
+}
+
+// MXFP8 (E4M3) scale byte of a block whose bf16 magnitude maximum has bits
+// `amax` (16-bit pattern): the exponent field E minus 8 (448 = 1.75 * 2^8),
+// clamped at 0; 0xFF for NaN or Inf.
+__device__ __forceinline__ uint32_t mx8_scale_from_bf16_amax(uint32_t amax) {
+    const uint32_t E = amax >> 7;
+    return E >= 255u ? 255u : (E > 8u ? E - 8u : 0u);
+}
+
 // Byte permute (v_perm_b32): selector byte k in 0..3 picks byte k of lo,
 // 4..7 picks byte k-4 of hi.
 __device__ __forceinline__ uint32_t byte_perm(uint32_t hi, uint32_t lo, uint32_t sel) {

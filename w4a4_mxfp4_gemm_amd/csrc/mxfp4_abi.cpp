@@ -208,6 +208,7 @@ int mxfp4_gemm_w4a8(const uint8_t* a_codes, const uint8_t* a_scales, const uint8
 
 size_t mxfp4_linear_w4a8_workspace_size(int64_t M, int64_t N, int64_t K) {
     if (M <= 0 || N <= 0 || check_k(K) != MXFP4_OK) return 0;
+    if (mx::linear_skinny_shape(M, N, K)) return 0;
     return fp8_codes_bytes(M, K) + (size_t)M * (size_t)(K / 32);
 }
 
@@ -224,6 +225,11 @@ int mxfp4_linear_w4a8_bf16(const void* x_bf16, int64_t ldx, int64_t M, int64_t N
     if (!aligned(x_bf16, 16) || ldx % 8 != 0 || !aligned(b_codes, 16)) return MXFP4_EALIGN;
     if (!aligned(y, out_dtype == MXFP4_OUT_FP32 ? 4 : 2)) return MXFP4_EALIGN;
     if (bias_bf16 && !aligned(bias_bf16, 16)) return MXFP4_EALIGN;
+    const uint16_t* bias = static_cast<const uint16_t*>(bias_bf16);
+    if (mx::linear_skinny_supported(M, N, K, x_bf16, ldx, b_scales))
+        return from_hip(mx::launch_linear_skinny_w4a8(static_cast<const uint16_t*>(x_bf16), ldx,
+                                                      b_codes, b_scales, M, N, K, y, bias,
+                                                      out_dtype == MXFP4_OUT_BF16, stream));
     const size_t need = fp8_codes_bytes(M, K) + (size_t)M * (size_t)(K / 32);
     if (workspace_bytes < need) return MXFP4_EINVAL;
     if (!aligned(workspace, 16)) return MXFP4_EALIGN;

@@ -162,35 +162,6 @@ __global__ __launch_bounds__(256) void act_quant_kernel(
 // store of codes), an aligned quad owns the 32-element block.
 // ---------------------------------------------------------------------------
 
-// E4M3 codes of four packed bf16 pairs under scale byte `byte` (< 255), 8
-// bytes, element 2i+h in byte 2i+h.  gfx950's v_cvt_scalef32_pk_fp8_bf16
-// divides by the scale and rounds to the nearest E4M3 value (ties to even,
-// subnormals included) but turns quotients of 464 and more into the NaN code
-// instead of saturating -- measured against the nearest-value encoder over
-// every bf16 magnitude and scale byte.  So each magnitude is first clamped to
-// 448 * 2^(byte-127), whose bf16 pattern is exponent field byte + 8 with
-// mantissa 0x60 (448 = 1.75 * 2^8); quotients up to 464 round to 448 anyway.
-__device__ __forceinline__ uint2 e4m3_codes8(const uint32_t (&w)[4], uint32_t byte) {
-    typedef short s16x2_t __attribute__((ext_vector_type(2)));
-    const uint32_t lim = ((byte + 8u) << 7) | 0x60u;
-    const u16x2 limv = {(unsigned short)lim, (unsigned short)lim};
-    const float scale = e8m0_to_f32(byte);
-    auto clamp = [&](uint32_t x) {
-        const u16x2 mag =
-            __builtin_elementwise_min(__builtin_bit_cast(u16x2, x & 0x7FFF7FFFu), limv);
-        return __builtin_bit_cast(bf16x2_t, __builtin_bit_cast(uint32_t, mag) | (x & 0x80008000u));
-    };
-    uint32_t out[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        s16x2_t v = {0, 0};
-        v = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(v, clamp(w[2 * i]), scale, false);
-        v = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(v, clamp(w[2 * i + 1]), scale, true);
-        out[i] = __builtin_bit_cast(uint32_t, v);
-    }
-    return make_uint2(out[0], out[1]);
-}
-
 template <int ROWS, bool SMOOTH = false>
 __global__ __launch_bounds__(256) void act_quant_fp8_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const int32_t* __restrict__ row_index,
@@ -226,9 +197,7 @@ __global__ __launch_bounds__(256) void act_quant_fp8_kernel(
             for (int i = 1; i < 4; ++i)
                 a = __builtin_elementwise_max(a, __builtin_bit_cast(u16x2, w[i] & 0x7FFF7FFFu));
             const uint32_t amax = quad_max_u32(max((uint32_t)a[0], (uint32_t)a[1]));
-            // bf16 amax exponent field E: byte = E - 8 clamped at 0; 0xFF for NaN/Inf
-            const uint32_t E = amax >> 7;
-            const uint32_t byte = E >= 255u ? 255u : (E > 8u ? E - 8u : 0u);
+            const uint32_t byte = mx8_scale_from_bf16_amax(amax);
             const uint2 out = byte == 255u ? make_uint2(0u, 0u) : e4m3_codes8(w, byte);
             *reinterpret_cast<uint2*>(codes + m * K + kq * 8) = out;
             if ((kq & 3) == 0) scales[m * (K / 32) + kq / 4] = (uint8_t)byte;
