@@ -203,6 +203,33 @@ def test_gemm_w4a8_tiled_large_sampled(mx):
     assert_w4a8(gy.cpu()[pm, pn], y, s, bound, "tiled large")
 
 
+
+def test_gemm_w4a8_persistent_sampled(mx):
+    """More than one round of tiles ([4000, 2048] x [2600, 2048]: 32 x 11 tiles
+    of 128 x 256, ragged in M and N) takes the persistent walk; fp32 and bf16
+    output with the bias, checked on sampled rows (one per tile row, the
+    ragged tail included) and every column."""
+    M, N, K = 4000, 2600, 2048
+    say(f"gemm_w4a8 persistent M={M} N={N} K={K} sampled")
+    ac, as_ = mxfp8_operand(M, K, seed=93)
+    bc, bs = synth.canonical_mxfp4(N, K, seed=94)
+    bias = (torch.randn(N, generator=torch.Generator().manual_seed(95)) * 4).to(torch.bfloat16)
+    rows = np.unique(np.concatenate([np.arange(0, M, 128) + np.arange((M + 127) // 128) * 5 % 128,
+                                     [M - 1]]))
+    rows = rows[rows < M]
+    pm, pn = np.repeat(rows, N), np.tile(np.arange(N), rows.size)
+    y, s = oracle.gemm_w4a8(u8(ac), u8(as_), u8(bc), u8(bs), pm, pn)
+    bv = bias.double().numpy()[pn]
+    amax, bmax = w4a8_block_maxima(u8(ac), u8(as_), u8(bc), u8(bs))
+    bound = w4a8_truncation_bound(amax, bmax, pm, pn)
+    A = [t.to(dev()) for t in (ac, as_, bc, bs)]
+    for dt in (torch.float32, torch.bfloat16):
+        gy = Guarded((M, N), dt)
+        mx.mxfp4_gemm_w4a8(*A, gy.view, bias=bias.to(dev()))
+        torch.cuda.synchronize()
+        assert gy.intact(), "write outside y"
+        assert_w4a8(gy.view.cpu()[pm, pn], y + bv, s + np.abs(bv), bound, f"persistent {dt}")
+
 def test_w4a8_graph_replay_matches_eager(mx):
     """The W4A8 act-quant and GEMM (skinny and tiled, with bias) captured in a
     HIP graph give the eager results on every replay."""

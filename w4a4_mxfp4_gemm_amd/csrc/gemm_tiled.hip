@@ -787,12 +787,11 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(
 // ---------------------------------------------------------------------------
 constexpr int LDS_LIMIT = 160 * 1024;           // LDS a workgroup may hold
 
-template <bool OUT_BF16, bool BIAS>
+template <bool OUT_BF16, bool BIAS, class S = DenseShape>
 __global__ __launch_bounds__(256, 1) void gemm_persistent_kernel(
     const uint8_t* __restrict__ x, const uint8_t* __restrict__ xs,
     const uint8_t* __restrict__ w, const uint8_t* __restrict__ ws, int64_t M, int64_t N,
     int64_t K, void* __restrict__ y, int gm, const uint16_t* __restrict__ bias) {
-    using S = DenseShape;
     using T = Stage<S, OUT_BF16>;
     constexpr int ROWS = T::rows_for(S::WLOADS * 1024);   // a wave's weight rows of a stage
     __shared__ __attribute__((aligned(16))) uint8_t smem[S::LDS_BYTES];
@@ -1130,6 +1129,27 @@ hipError_t launch_gemm_tiled_w4a8(const uint8_t* a_codes, const uint8_t* a_scale
     const int tiles_m = (int)((M + S::BM - 1) / S::BM);
     const int tiles_n = (int)((N + S::BN - 1) / S::BN);
     const int per_xcd = (tiles_m * tiles_n + 7) / 8;
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return hipErrorInvalidDevice;
+    const int slots = cus / 8 > 0 ? cus / 8 : 1;   // resident workgroups per XCD
+    if (per_xcd > slots && K >= 1024) {
+        // more than one round: the persistent walk of the W4A4 prefill
+        const int gm = group_rows(tiles_m, slots);
+        const dim3 grid((unsigned)(slots * 8));
+        auto go = [&](auto kernel) {
+            hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, a_codes, a_scales, b_codes,
+                               b_scales, M, N, K, y, gm, bias);
+        };
+        if (bias)
+            out_bf16 ? go(tiled::gemm_persistent_kernel<true, true, S>)
+                     : go(tiled::gemm_persistent_kernel<false, true, S>);
+        else
+            out_bf16 ? go(tiled::gemm_persistent_kernel<true, false, S>)
+                     : go(tiled::gemm_persistent_kernel<false, false, S>);
+        return hipGetLastError();
+    }
     const int gm = group_rows(tiles_m, per_xcd);
     const dim3 grid((unsigned)(per_xcd * 8));
     auto go = [&](auto kernel) {
