@@ -305,11 +305,31 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_skinny_kernel(
     // is a point no load moves across)
     if constexpr (BF16A) asm volatile("" ::: "memory");
 
+    // The row bias (raw bf16 pairs) of this lane's 4 output columns of tile t
+    // when all 4 are inside N; a tile that ends past N is the last of its
+    // workgroup, and finish loads those values itself.  Loaded just before
+    // the tile's weights: vmcnt counts in issue order, so a bias load issued
+    // after them would make its first use wait for every weight load in flight.
+    // The load is never predicated (merging a predicated load's result with
+    // a default waits for it on the spot): the column is clamped, and without
+    // a bias the first 2N bytes of the weight scales (N x K/32 bytes, 16-byte
+    // aligned) stand in as the source, their values unused.  n is a multiple
+    // of 4 and N >= 16, so the clamp keeps the 8-byte load aligned and inside
+    // N, and leaves every tile whose 4 columns fit unchanged.
+    const uint16_t* bias_src = bias ? bias : reinterpret_cast<const uint16_t*>(ws);
+    auto load_bias = [&](int t) {
+        const int n = min(t * 16 + 4 * g, (N & ~3) - 4);
+        return *reinterpret_cast<const uint2*>(bias_src + n);
+    };
+
     // 2. weights: TPW tiles in flight per wave
     Frag<SPW> slot[TPW];
+    uint2 bslot[TPW];
 #pragma unroll
-    for (int i = 0; i < TPW; ++i)
+    for (int i = 0; i < TPW; ++i) {
+        bslot[i] = load_bias(blockIdx.x + i * stride);
         load_block<SPW, NW>(slot[i], w, ws, tile_row(blockIdx.x + i * stride), nkb);
+    }
     __builtin_amdgcn_sched_barrier(0);   // issue every load before the first use
     if constexpr (BF16A) {
         asm volatile("" ::: "memory");   // ... and every weight load before the quantization
@@ -353,7 +373,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_skinny_kernel(
     //    w finishes activation blocks mt = w, w + NW, ... of the tile.  The
     //    buffer written here is next written two tiles on, after the next
     //    tile's barrier, by which point every wave has read it.
-    auto finish = [&](int t, int buf, const v4f (&acc)[MT]) {
+    auto finish = [&](int t, int buf, const v4f (&acc)[MT], const uint2 bv) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) sm.red[buf][wave][mt][lane] = acc[mt];
         lds_barrier();
@@ -368,9 +388,8 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_skinny_kernel(
             if (m >= M) continue;
             if (bias) {   // the row bias joins the fp32 sum before its one rounding
                 if (n + 3 < N) {
-                    const uint2 b = *reinterpret_cast<const uint2*>(bias + n);
-                    v += v4f{__uint_as_float(b.x << 16), __uint_as_float(b.x & 0xFFFF0000u),
-                             __uint_as_float(b.y << 16), __uint_as_float(b.y & 0xFFFF0000u)};
+                    v += v4f{__uint_as_float(bv.x << 16), __uint_as_float(bv.x & 0xFFFF0000u),
+                             __uint_as_float(bv.y << 16), __uint_as_float(bv.y & 0xFFFF0000u)};
                 } else {
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
@@ -396,8 +415,24 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_skinny_kernel(
         }
     };
 
-    // 4. tiles: slot i % TPW holds tile blockIdx.x + i*stride; once consumed it
-    //    is refilled with the tile TPW further on.
+    // 4. tiles: slot i % TPW holds tile blockIdx.x + i*stride.  When every
+    //    tile of the workgroup is already in flight (N <= 16 * TPW * grid),
+    //    straight-line code: in the loop below the compiler copies the
+    //    loop-carried slots, and each copy waits for its loads, so the first
+    //    MFMA waited for all of them.
+    if (ntiles <= TPW * stride) {
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) {
+            const int t = blockIdx.x + i * stride;
+            if (t >= ntiles) break;
+            v4f acc[MT];
+            compute(slot[i], acc);
+            finish(t, i & 1, acc, bslot[i]);
+        }
+        return;
+    }
+    //    Otherwise a slot, once consumed, is refilled with the tile TPW
+    //    further on.
     int k = 0;
     for (int base = blockIdx.x; base < ntiles; base += TPW * stride) {
 #pragma unroll
@@ -406,9 +441,12 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_skinny_kernel(
             if (t >= ntiles) break;
             v4f acc[MT];
             compute(slot[i], acc);
-            if (t + TPW * stride < ntiles)
+            const uint2 bv = bslot[i];
+            if (t + TPW * stride < ntiles) {
+                bslot[i] = load_bias(t + TPW * stride);
                 load_block<SPW, NW>(slot[i], w, ws, tile_row(t + TPW * stride), nkb);
-            finish(t, k & 1, acc);
+            }
+            finish(t, k & 1, acc, bv);
         }
     }
 }
