@@ -36,6 +36,9 @@ SHAPES = [(1, 1, 32), (1, 300, 4096), (7, 17, 96), (16, 256, 512), (33, 200, 544
           # ragged N, four and eight wavefronts
           (5, 1000, 2048), (16, 16, 4096), (17, 300, 4096), (40, 72, 2048), (48, 257, 4096),
           (64, 4099, 4096), (61, 1040, 2048),
+          # more weight tiles than a grid's slots hold at once (over 16 x 3 x 256
+          # rows): each slot is refilled as it is consumed
+          (3, 13000, 2048), (64, 12352, 2048),
           # more tiles than one round on the chip (persistent walk, ragged M and
           # N), with and without the next tile's stages streamed early
           (2200, 7700, 1024), (2200, 7700, 512)]
@@ -400,7 +403,7 @@ def same_bits(a, b):
     return bool(((a.view(torch.int32) == b.view(torch.int32)) | both_nan).all())
 
 
-@pytest.mark.parametrize("M,N,K,ldx", [(1, 1000, 4096, 4096), (5, 300, 2048, 2048),
+@pytest.mark.parametrize("M,N,K,ldx", [(1, 1000, 4096, 4096), (2, 12600, 2048, 2048), (5, 300, 2048, 2048),
                                        (16, 12288, 4096, 4096), (17, 257, 4096, 4104),
                                        (33, 1040, 2048, 2056), (64, 4099, 4096, 4096),
                                        (65, 512, 4096, 4096), (200, 300, 1024, 1032),
@@ -490,10 +493,11 @@ def test_linear_bf16_uos_against_oracle(mx):
 
 @pytest.mark.parametrize("M,N,K", [(1, 1000, 4096), (8, 2048, 4096), (5, 300, 2048),
                                    (33, 1040, 2048), (100, 300, 1024), (150, 260, 800),
-                                   (300, 1000, 1024), (4096, 8192, 4096)])
+                                   (300, 1000, 1024), (4096, 8192, 4096), (20, 13001, 2048)])
 def test_linear_bf16_row_bias(mx, M, N, K):
-    """A bf16 row bias through every GEMM path (one-launch decode, skinny,
-    generic, tiled with a ragged N, persistent), against the oracle's act-quant,
+    """A bf16 row bias through every GEMM path (one-launch decode, skinny, with
+    its slots refilled past 12288 rows, generic, tiled with a ragged N,
+    persistent), against the oracle's act-quant,
     requant and GEMM plus the bias before the one rounding.  Sizes the oracle
     cannot finish whole are checked on sampled rows."""
     say(f"linear bf16 + bias M={M} N={N} K={K}")

@@ -130,7 +130,7 @@ def mxfp8_operand(M, K, seed):
 @pytest.mark.parametrize("M,N,K", [(1, 256, 4096), (8, 1000, 4096), (33, 520, 2048),
                                    (48, 300, 4096), (64, 300, 4096), (5, 260, 1024),
                                    (20, 96, 96), (200, 520, 1056), (128, 256, 512),
-                                   (300, 1000, 1024), (520, 776, 2048)])
+                                   (300, 1000, 1024), (520, 776, 2048), (5, 12500, 2048)])
 def test_gemm_w4a8_against_oracle(mx, M, N, K):
     """Skinny (M <= 64, K = 2048/4096), the LDS-staged tiled kernel (M >= 128,
     K % 512 == 0; ragged M and N), and the 16x16x128 tile kernel (other K,
