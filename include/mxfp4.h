@@ -308,6 +308,38 @@ int mxfp4_silu_mul_quantize(const void* gate_up_bf16, int64_t ldg, int64_t M, in
                             uint8_t* codes, uint8_t* scales, uint32_t flags,
                             hipStream_t stream);
 
+/*
+ * The gate_up grouped GEMM of an MoE layer with the expert activation and its
+ * MXFP4 quantization in the GEMM's epilogue (AMD blog, closing list: the MoE
+ * experts run as fused-MoE kernels on MXFP4): one launch in place of
+ * mxfp4_grouped_gemm (bf16 out) followed by mxfp4_silu_mul_quantize, and
+ * without the bf16 gate_up output in HBM.  The result is the same, bit for
+ * bit: each gate and up value is the bf16 (RNE) of its fp32 sum, then
+ * h = bf16_RNE(silu(g) * u) is quantized by the act-quant rule.
+ *
+ * Layout: each expert's 2I weight rows are interleaved in groups of 64, 32
+ * gate rows then the 32 up rows of the same columns of h: row 64q + r is the
+ * gate row of h column 32q + r and row 64q + 32 + r its up row (r < 32).  A
+ * caller holding [gate; up] stacked permutes the rows once, at load time.
+ *
+ *   a_codes, a_scales   [total_M][K/2], [total_M][K/32] u8, device, read
+ *   b_codes, b_scales   [E][2I][K/2], [E][2I][K/32] u8, device, read,
+ *                       interleaved as above
+ *   offsets             [E+1] int32, device, read, as for mxfp4_grouped_gemm
+ *   I                   columns of h; a positive multiple of 32
+ *   h_codes, h_scales   [total_M][I/2], [total_M][I/32] u8, device, written
+ *                       (h_codes 16-byte aligned)
+ *   flags               0 or MXFP4_SCALE_UOS
+ * Returns MXFP4_EUNSUPPORTED where the LDS-tiled grouped kernel does not
+ * apply (K % 512 != 0, more than its expert table holds, operands over 2 GiB,
+ * scale pointers not 4-byte aligned); the two calls above cover those shapes.
+ */
+int mxfp4_grouped_gemm_silu_quantize(const uint8_t* a_codes, const uint8_t* a_scales,
+                                     const uint8_t* b_codes, const uint8_t* b_scales,
+                                     const int32_t* offsets, int64_t E, int64_t total_M,
+                                     int64_t I, int64_t K, uint8_t* h_codes,
+                                     uint8_t* h_scales, uint32_t flags, hipStream_t stream);
+
 /* Largest topk mxfp4_moe_combine accepts. */
 enum { MXFP4_COMBINE_MAX_TOPK = 64 };
 

@@ -176,6 +176,30 @@ def test_silu_mul_quantize_argument_checks(lib):
     assert f(FAKE, 128, 0, 64, FAKE, FAKE, 2, None) == 0      # M == 0, UOS accepted
 
 
+def test_grouped_gemm_silu_quantize_argument_checks(lib):
+    """Every rejected call returns before a launch (the pointers are fake)."""
+    f = lib.mxfp4_grouped_gemm_silu_quantize
+    def g(a=FAKE, sa=FAKE, b=FAKE, sb=FAKE, off=FAKE, E=4, M=64, I=64, K=512, hc=FAKE,
+          hs=FAKE, flags=0):
+        return f(a, sa, b, sb, off, E, M, I, K, hc, hs, flags, None)
+    assert g(E=0) == -1
+    assert g(M=-1) == -1
+    assert g(I=80) == -1                 # I % 32
+    assert g(I=0) == -1
+    assert g(K=48) == -1                 # K % 32
+    assert g(flags=1) == -1
+    assert g(flags=4) == -1
+    assert g(off=None) == -1
+    assert g(hs=None) == -1
+    assert g(a=ODD) == -2
+    assert g(hc=ODD) == -2               # 16-byte code stores
+    assert g(off=ODD) == -2
+    assert g(K=544) == -3                # the tiled kernel needs K % 512 == 0
+    assert g(sa=ODD) == -3               # ... and 4-byte aligned scales
+    assert g(E=4096) == -3               # more experts than its table holds
+    assert g(M=0, flags=2) == 0          # nothing to do; UOS accepted
+
+
 def test_moe_combine_argument_checks(lib):
     f = lib.mxfp4_moe_combine
     #        y    ldy  R   rows weights T  topk H    out  dtype flags stream

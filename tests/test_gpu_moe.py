@@ -225,6 +225,77 @@ def test_moe_combine_clamps_rows_and_propagates_nan(mx):
 
 
 # ---- a whole MoE layer ----------------------------------------------------------------
+# ---- gate_up GEMM with the activation in its epilogue ------------------------------
+def interleaved_to_stacked(cols):
+    """Column (or weight-row) order of the fused call, 64-groups of 32 gate then
+    32 up, -> [gate | up] stacked: index arrays for the last axis."""
+    n = cols
+    q, r = np.divmod(np.arange(n // 2), 32)
+    return np.concatenate([64 * q + r, 64 * q + 32 + r])
+
+
+def fused_glu_both(mx, E, counts, I, K, seed, rule):
+    """The fused call on exact-domain operands (E2M1 codes, scale bytes 126..128:
+    every fp32 sum of the GEMM is exact, so the bf16 gate_up values the fused
+    epilogue sees are the RNE of the exact sums the oracle computes), checked
+    against the oracle from the same inputs and against the two-call path."""
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    M, N = int(offsets[-1]), 2 * I
+    ac, as_ = synth.canonical_mxfp4(M, K, seed=seed, scale_lo=126, scale_hi=128)
+    bc, bs = synth.canonical_mxfp4(E * N, K, seed=seed + 1, scale_lo=126, scale_hi=128)
+    bc, bs = bc.reshape(E, N, K // 2), bs.reshape(E, N, K // 32)
+    d = dev()
+    A = [t.to(d) for t in (ac, as_, bc, bs)] + [torch.from_numpy(offsets).to(d)]
+    gc = Guarded((M, I // 2), torch.uint8)
+    gs = Guarded((M, I // 32), torch.uint8)
+    mx.mxfp4_grouped_gemm_silu_quantize(*A, gc.view, gs.view, scale_rule=rule)
+    torch.cuda.synchronize()
+    assert gc.intact() and gs.intact(), "write outside the outputs"
+    # oracle: exact grouped GEMM, bf16 RNE, columns back to [gate | up], activation
+    y, _ = oracle.grouped_gemm(u8(ac), u8(as_), u8(bc), u8(bs), offsets)
+    assert (np.abs(y) < 2.0 ** 20).all()          # the exact-sum domain
+    gu = oracle.bf16_from_double_array(y)[:, interleaved_to_stacked(N)]
+    check_silu_quant(u8(gc.view), u8(gs.view), gu, I, rule, f"fused glu {rule}")
+    # the two calls it replaces, bit for bit
+    y1 = mx.mxfp4_grouped_gemm(*A, out_dtype=torch.bfloat16)
+    idx = torch.from_numpy(interleaved_to_stacked(N)).to(d)
+    hc, hs = mx.mxfp4_silu_mul_quantize(y1[:, idx].contiguous(), scale_rule=rule)
+    torch.cuda.synchronize()
+    assert torch.equal(hc, gc.view) and torch.equal(hs, gs.view), "fused != two calls"
+
+
+@pytest.mark.parametrize("E,counts,I,K", [
+    (4, [0, 37, 130, 1], 96, 512),             # empty expert, ragged rows, N = 192 < one tile
+    (3, [128, 0, 300], 256, 1024),              # a partial tile of waves, the persistent walk
+    (8, [64, 200, 5, 0, 129, 256, 17, 90], 512, 2048)])
+@pytest.mark.parametrize("rule", ["ocp", "uos"])
+def test_grouped_gemm_silu_quantize(mx, E, counts, I, K, rule):
+    say(f"grouped gemm + silu quantize E={E} I={I} K={K} {rule}")
+    fused_glu_both(mx, E, counts, I, K, seed=E * 7 + I, rule=rule)
+
+
+def test_grouped_gemm_silu_quantize_moe_size(mx):
+    """At the MoE bench's shape (128 experts, 2048 tokens x top-8 routed, H =
+    4096, I = 1024; real routing) the fused call equals the two calls, bit for
+    bit, on random MXFP4 weights (made on the GPU: 512 MiB of codes) and
+    quantized activations."""
+    say("grouped gemm + silu quantize, MoE size")
+    E, T, TOPK, H, I = 128, 2048, 8, 4096, 1024
+    d = dev()
+    perm, offsets, _, _ = synth.route_topk_full(T, E, TOPK, seed=61)
+    x = synth.activations(T, H, seed=62, outlier_seed=63).to(d)
+    wc, ws = synth.canonical_mxfp4(E * 2 * I, H, seed=64, device=d)
+    wc, ws = wc.reshape(E, 2 * I, H // 2), ws.reshape(E, 2 * I, H // 32)
+    off = offsets.to(d)
+    xc, xs = mx.mxfp4_quantize_act(x, row_index=perm.to(d))
+    hc, hs = mx.mxfp4_grouped_gemm_silu_quantize(xc, xs, wc, ws, off)
+    y1 = mx.mxfp4_grouped_gemm(xc, xs, wc, ws, off, out_dtype=torch.bfloat16)
+    idx = torch.from_numpy(interleaved_to_stacked(2 * I)).to(d)
+    rc, rs = mx.mxfp4_silu_mul_quantize(y1[:, idx].contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(hc, rc) and torch.equal(hs, rs)
+
+
 def test_moe_layer_end_to_end(mx):
     """Routed tokens through the whole expert path on the GPU: gathered
     act-quant, grouped gate_up GEMM, expert activation + quantization, grouped

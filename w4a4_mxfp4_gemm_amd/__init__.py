@@ -65,6 +65,8 @@ def _load_library() -> ctypes.CDLL:
     lib.mxfp4_linear_w4a8_workspace_size.restype = SZ
     lib.mxfp4_silu_mul_quantize.argtypes = [P, I, I, I, P, P, U32, P]
     lib.mxfp4_silu_mul_quantize.restype = ctypes.c_int
+    lib.mxfp4_grouped_gemm_silu_quantize.argtypes = [P, P, P, P, P, I, I, I, I, P, P, U32, P]
+    lib.mxfp4_grouped_gemm_silu_quantize.restype = ctypes.c_int
     lib.mxfp4_moe_combine.argtypes = [P, I, I, P, P, I, I, I, P, ctypes.c_int, U32, P]
     lib.mxfp4_moe_combine.restype = ctypes.c_int
     lib.mxfp4_linear_workspace_size.argtypes = [I, I, I]
@@ -87,6 +89,7 @@ EXPORTED_SYMBOLS = ("mxfp4_requant_from_nvfp4", "mxfp4_requant_from_nvfp4_subset
                     "mxfp4_moe_combine", "mxfp8_quantize_act", "mxfp4_gemm_w4a8",
                     "mxfp4_linear_w4a8_bf16", "mxfp4_linear_w4a8_workspace_size",
                     "mxfp4_quantize_act_smooth", "mxfp8_quantize_act_smooth",
+                    "mxfp4_grouped_gemm_silu_quantize",
                     "mxfp4_status_string", "mxfp4_version")
 
 
@@ -507,12 +510,50 @@ def mxfp4_grouped_gemm(a_codes, a_scales, b_codes, b_scales, offsets, y=None, *,
     return y
 
 
+
+def mxfp4_grouped_gemm_silu_quantize(a_codes, a_scales, b_codes, b_scales, offsets,
+                                     codes=None, scales=None, *, scale_rule="ocp", stream=None):
+    """The MoE gate_up grouped GEMM with the expert activation and its MXFP4
+    quantization fused in: A [total_M, K/2] expert-sorted, B [E, 2I, K/2] with
+    each expert's rows interleaved by 32 (rows 64q..64q+31 gate, 64q+32..64q+63
+    up, for h columns 32q..32q+31), offsets int32 [E+1] -> MXFP4 codes
+    [total_M, I/2] and E8M0 bytes [total_M, I/32] of bf16(silu(gate) * up)."""
+    _need(a_codes, "a_codes", torch.uint8)
+    dev = a_codes.device
+    for t, n in ((a_scales, "a_scales"), (b_codes, "b_codes"), (b_scales, "b_scales")):
+        _need(t, n, torch.uint8, dev)
+    _need(offsets, "offsets", torch.int32, dev)
+    total_M, K = a_codes.shape[0], a_codes.shape[1] * 2
+    E, N = b_codes.shape[0], b_codes.shape[1]
+    if offsets.shape != (E + 1,):
+        raise ValueError("offsets must have E+1 entries")
+    if b_codes.shape != (E, N, K // 2) or b_scales.shape != (E, N, K // 32) or \
+            a_scales.shape != (total_M, K // 32):
+        raise ValueError("operand shapes disagree")
+    if N % 2:
+        raise ValueError("B must hold 2I rows per expert")
+    I = N // 2
+    if codes is None:
+        codes = torch.empty((total_M, I // 2), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty((total_M, I // 32), dtype=torch.uint8, device=dev)
+    _need(codes, "codes", torch.uint8, dev)
+    _need(scales, "scales", torch.uint8, dev)
+    if codes.shape != (total_M, I // 2) or scales.shape != (total_M, I // 32):
+        raise ValueError("output shapes do not match [total_M, I/2] / [total_M, I/32]")
+    _check("mxfp4_grouped_gemm_silu_quantize", _lib.mxfp4_grouped_gemm_silu_quantize(
+        _ptr(a_codes), _ptr(a_scales), _ptr(b_codes), _ptr(b_scales), _ptr(offsets),
+        E, total_M, I, K, _ptr(codes), _ptr(scales), _rule_flag(scale_rule),
+        _stream(stream, dev)))
+    return codes, scales
+
+
 __all__ = ["mxfp4_requant_from_nvfp4", "mxfp4_quantize_act", "mxfp4_gemm",
            "mxfp4_grouped_gemm", "mxfp4_linear_bf16", "mxfp4_gemm_workspace_size",
            "mxfp4_linear_workspace_size", "mxfp4_silu_mul_quantize", "mxfp4_moe_combine",
            "mxfp8_quantize_act", "mxfp4_gemm_w4a8", "mxfp4_linear_w4a8_bf16",
            "mxfp4_linear_w4a8_workspace_size", "mxfp4_quantize_act_smooth",
-           "mxfp8_quantize_act_smooth",
+           "mxfp8_quantize_act_smooth", "mxfp4_grouped_gemm_silu_quantize",
            "mxfp4_status_string",
            "mxfp4_version", "Mxfp4Error", "LIBRARY_PATH", "EXPORTED_SYMBOLS",
            "MXFP4_OUT_BF16", "MXFP4_OUT_FP32", "MXFP4_REQ_INTERMEDIATE_BF16",

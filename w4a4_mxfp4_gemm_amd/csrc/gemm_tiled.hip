@@ -740,6 +740,75 @@ __device__ __forceinline__ bool tile_coords(int tiles_m, int tiles_n, int gm, in
     return true;
 }
 
+// The epilogue of an MoE gate_up GEMM fused with the expert activation and
+// its MXFP4 quantization.  The gate_up weight rows are interleaved in groups
+// of 64: 32 gate rows, then the 32 up rows of the same columns of h, so a
+// wave's 64 output columns are the gate and up halves of one 32-column MX
+// block of h.  The accumulators are parked as bf16 (RNE, what the plain
+// GEMM would store), then lane r of a pass takes row r: the 32 gate and 32
+// up values, h = bf16(silu(g) * u) in the act-quant kernel's GLU arithmetic,
+// and the block's 16 code bytes and scale byte by the act-quant rule.  So the
+// result equals the plain GEMM followed by the act-quant kernel's GLU mode,
+// bit for bit.  h codes are [rows][N/4] bytes, scales [rows][N/64].
+template <class S, int ROWS, bool UOS>
+__device__ __forceinline__ void store_tile_glu(const v16f (&acc)[S::NB][S::MB], lds_u8* stage,
+                                               uint8_t* __restrict__ hc,
+                                               uint8_t* __restrict__ hs, int64_t m0,
+                                               int64_t m_end, int64_t n0, int64_t N, int wn,
+                                               int wm) {
+    static_assert(S::NB == 2, "one gate block and one up block per wave");
+    using T = Stage<S, true>;
+    static_assert(ROWS >= 2 && ROWS <= 32 && (ROWS & (ROWS - 1)) == 0, "a 32-row block in passes");
+    int lane = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane));
+    const int r32 = lane & 31, h = lane >> 5;
+    const int64_t col0 = n0 + wn * 64;
+    if (col0 >= N) return;                    // wave-uniform; N % 64 == 0
+    const int64_t blk = col0 / 64;            // this wave's MX block of h
+    const int64_t hrow = N / 4, srow = N / 64;
+#pragma unroll
+    for (int j = 0; j < S::MB; ++j) {
+#pragma unroll
+        for (int p = 0; p < 32 / ROWS; ++p) {
+            const int64_t row0 = m0 + wm * 32 * S::MB + 32 * j + p * ROWS;
+            if (row0 >= m_end) return;            // wave-uniform
+            const int r = r32 - p * ROWS;
+            if (ROWS == 32 || (r >= 0 && r < ROWS)) {
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) {
+                        lds_u8* dst = stage + r * T::PITCH + (32 * i + 8 * b + 4 * h) * 2;
+                        *reinterpret_cast<__attribute__((address_space(3))) v2u*>(dst) =
+                            v2u{pack_bf16x2(acc[i][j][4 * b], acc[i][j][4 * b + 1]),
+                                pack_bf16x2(acc[i][j][4 * b + 2], acc[i][j][4 * b + 3])};
+                    }
+                }
+            }
+            asm volatile("" ::: "memory");         // reads after the writes
+            const int64_t m = row0 + lane;
+            if (lane < ROWS && m < m_end) {
+                const lds_u8* src = stage + lane * T::PITCH;
+                uint32_t w[16];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const v4u gv =
+                        *reinterpret_cast<const __attribute__((address_space(3))) v4u*>(src + 16 * c);
+                    const v4u uv = *reinterpret_cast<const __attribute__((address_space(3))) v4u*>(
+                        src + 64 + 16 * c);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) w[4 * c + e] = glu_pair(gv[e], uv[e]);
+                }
+                uint32_t c4[4];
+                const uint32_t byte = quant_block32_bf16<UOS>(w, c4);
+                *reinterpret_cast<v4u*>(hc + m * hrow + blk * 16) = v4u{c4[0], c4[1], c4[2], c4[3]};
+                hs[m * srow + blk] = (uint8_t)byte;
+            }
+            asm volatile("" ::: "memory");         // the next pass's writes after these reads
+        }
+    }
+}
+
 template <bool OUT_BF16, bool BIAS, class S = DenseShape>
 __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(
     const uint8_t* __restrict__ x, const uint8_t* __restrict__ xs,
@@ -965,12 +1034,15 @@ __device__ __forceinline__ void main_loop_jl(int jl, lds_u8* lds, const TileSrc<
         main_loop<S, 1, PREFETCH>(lds, cur, nxt, lo, nkt, cbase, pp, acc, ro);
 }
 
-template <bool OUT_BF16>
+// GLU: y is the MXFP4 codes of h = bf16(silu(gate) * up) and hs its scales
+// (store_tile_glu); otherwise hs is unused.
+template <bool OUT_BF16, bool GLU = false, bool UOS = false>
 __global__ __launch_bounds__(256, 1) void grouped_tiled_kernel(
     const uint8_t* __restrict__ x, const uint8_t* __restrict__ xs,
     const uint8_t* __restrict__ w, const uint8_t* __restrict__ ws,
     const int32_t* __restrict__ offsets, int E, int total_M, int64_t N, int64_t K,
-    void* __restrict__ y) {
+    void* __restrict__ y, uint8_t* __restrict__ hs) {
+    static_assert(!GLU || OUT_BF16, "the GLU epilogue parks bf16");
     using S = GroupShape;
     // pipeline, expert table, then the four waves' epilogue regions (the
     // pipeline buffers already hold the next tile's first stages when a tile
@@ -1018,8 +1090,13 @@ __global__ __launch_bounds__(256, 1) void grouped_tiled_kernel(
         else
             main_loop_jl<S, false>(it.jl, lds, cur, cur, lo, nkt, cbase, pp, acc, ro);
         if (!prefetch) wait_vm<0>();          // drain the surplus loads
-        store_tile<S, OUT_BF16, ROWS>(acc, lds + STAGE_BASE + wave * T::bytes(ROWS), y, it.m0,
-                                      it.m_end, (int64_t)it.tn * S::BN, N, wn, wm);
+        if constexpr (GLU)
+            store_tile_glu<S, ROWS, UOS>(acc, lds + STAGE_BASE + wave * T::bytes(ROWS),
+                                         static_cast<uint8_t*>(y), hs, it.m0, it.m_end,
+                                         (int64_t)it.tn * S::BN, N, wn, wm);
+        else
+            store_tile<S, OUT_BF16, ROWS>(acc, lds + STAGE_BASE + wave * T::bytes(ROWS), y,
+                                          it.m0, it.m_end, (int64_t)it.tn * S::BN, N, wn, wm);
         if (!have_next) break;
         zero_acc<S>(acc);
         if (prefetch) {
@@ -1165,14 +1242,10 @@ hipError_t launch_gemm_tiled_w4a8(const uint8_t* a_codes, const uint8_t* a_scale
     return hipGetLastError();
 }
 
-hipError_t launch_grouped_gemm_tiled(const uint8_t* a_codes, const uint8_t* a_scales,
-                                     const uint8_t* b_codes, const uint8_t* b_scales,
-                                     const int32_t* offsets, int64_t E, int64_t total_M,
-                                     int64_t N, int64_t K, void* y, bool out_bf16,
-                                     hipStream_t stream) {
+// One persistent workgroup per CU (the tile's LDS allows no more), never
+// more workgroups than the largest possible number of work items.
+static hipError_t grouped_grid(int64_t E, int64_t total_M, int64_t N, dim3& grid) {
     using S = tiled::GroupShape;
-    // one persistent workgroup per CU (the tile's LDS allows no more), never
-    // more workgroups than the largest possible number of work items
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
@@ -1181,15 +1254,51 @@ hipError_t launch_grouped_gemm_tiled(const uint8_t* a_codes, const uint8_t* a_sc
     int64_t g = (int64_t)cus / 8 * 8;
     if (g < 8) g = 8;
     if (g > (bound + 7) / 8 * 8) g = (bound + 7) / 8 * 8;
-    const dim3 grid((unsigned)g);
+    grid = dim3((unsigned)g);
+    return hipSuccess;
+}
+
+hipError_t launch_grouped_gemm_tiled(const uint8_t* a_codes, const uint8_t* a_scales,
+                                     const uint8_t* b_codes, const uint8_t* b_scales,
+                                     const int32_t* offsets, int64_t E, int64_t total_M,
+                                     int64_t N, int64_t K, void* y, bool out_bf16,
+                                     hipStream_t stream) {
+    dim3 grid;
+    const hipError_t e = grouped_grid(E, total_M, N, grid);
+    if (e != hipSuccess) return e;
+    uint8_t* const none = nullptr;
     if (out_bf16)
         hipLaunchKernelGGL(tiled::grouped_tiled_kernel<true>, grid, dim3(256), 0, stream,
                            a_codes, a_scales, b_codes, b_scales, offsets, (int)E, (int)total_M, N,
-                           K, y);
+                           K, y, none);
     else
         hipLaunchKernelGGL(tiled::grouped_tiled_kernel<false>, grid, dim3(256), 0, stream,
                            a_codes, a_scales, b_codes, b_scales, offsets, (int)E, (int)total_M, N,
-                           K, y);
+                           K, y, none);
+    return hipGetLastError();
+}
+
+bool grouped_glu_supported(int64_t E, int64_t total_M, int64_t N, int64_t K,
+                           const void* a_scales, const void* b_scales) {
+    return N % 64 == 0 && grouped_tiled_supported(E, total_M, N, K, a_scales, b_scales);
+}
+
+hipError_t launch_grouped_glu_quant(const uint8_t* a_codes, const uint8_t* a_scales,
+                                    const uint8_t* b_codes, const uint8_t* b_scales,
+                                    const int32_t* offsets, int64_t E, int64_t total_M,
+                                    int64_t N, int64_t K, uint8_t* h_codes, uint8_t* h_scales,
+                                    bool uos, hipStream_t stream) {
+    dim3 grid;
+    const hipError_t e = grouped_grid(E, total_M, N, grid);
+    if (e != hipSuccess) return e;
+    if (uos)
+        hipLaunchKernelGGL((tiled::grouped_tiled_kernel<true, true, true>), grid, dim3(256), 0,
+                           stream, a_codes, a_scales, b_codes, b_scales, offsets, (int)E,
+                           (int)total_M, N, K, static_cast<void*>(h_codes), h_scales);
+    else
+        hipLaunchKernelGGL((tiled::grouped_tiled_kernel<true, true, false>), grid, dim3(256), 0,
+                           stream, a_codes, a_scales, b_codes, b_scales, offsets, (int)E,
+                           (int)total_M, N, K, static_cast<void*>(h_codes), h_scales);
     return hipGetLastError();
 }
 

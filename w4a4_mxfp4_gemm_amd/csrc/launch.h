@@ -81,6 +81,18 @@ hipError_t launch_grouped_gemm_tiled(const uint8_t* a_codes, const uint8_t* a_sc
                                      int64_t N, int64_t K, void* y, bool out_bf16,
                                      hipStream_t stream);
 
+// The grouped gate_up GEMM with the expert activation and its MXFP4
+// quantization in the epilogue (gate/up weight rows interleaved by 32): the
+// tiled kernel's shapes with N % 64 == 0.
+bool grouped_glu_supported(int64_t E, int64_t total_M, int64_t N, int64_t K,
+                           const void* a_scales, const void* b_scales);
+
+hipError_t launch_grouped_glu_quant(const uint8_t* a_codes, const uint8_t* a_scales,
+                                    const uint8_t* b_codes, const uint8_t* b_scales,
+                                    const int32_t* offsets, int64_t E, int64_t total_M,
+                                    int64_t N, int64_t K, uint8_t* h_codes, uint8_t* h_scales,
+                                    bool uos, hipStream_t stream);
+
 bool skinny_gemm_supported(int64_t M, int64_t N, int64_t K, const void* x, const void* x_scales,
                            const void* w_scales);
 

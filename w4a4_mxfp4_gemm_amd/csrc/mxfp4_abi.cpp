@@ -256,6 +256,28 @@ int mxfp4_silu_mul_quantize(const void* gate_up_bf16, int64_t ldg, int64_t M, in
                                                  (flags & MXFP4_SCALE_UOS) != 0, stream));
 }
 
+int mxfp4_grouped_gemm_silu_quantize(const uint8_t* a_codes, const uint8_t* a_scales,
+                                     const uint8_t* b_codes, const uint8_t* b_scales,
+                                     const int32_t* offsets, int64_t E, int64_t total_M,
+                                     int64_t I, int64_t K, uint8_t* h_codes,
+                                     uint8_t* h_scales, uint32_t flags, hipStream_t stream) {
+    if (E <= 0 || total_M < 0 || check_k(I) != MXFP4_OK || check_k(K) != MXFP4_OK)
+        return MXFP4_EINVAL;
+    if ((flags & ~(uint32_t)MXFP4_SCALE_UOS) != 0) return MXFP4_EINVAL;
+    if (total_M == 0) return MXFP4_OK;
+    if (!a_codes || !a_scales || !b_codes || !b_scales || !offsets || !h_codes || !h_scales)
+        return MXFP4_EINVAL;
+    if (!aligned(a_codes, 16) || !aligned(b_codes, 16) || !aligned(h_codes, 16) ||
+        !aligned(offsets, 4))
+        return MXFP4_EALIGN;
+    const int64_t N = 2 * I;
+    if (!mx::grouped_glu_supported(E, total_M, N, K, a_scales, b_scales))
+        return MXFP4_EUNSUPPORTED;
+    return from_hip(mx::launch_grouped_glu_quant(a_codes, a_scales, b_codes, b_scales, offsets,
+                                                 E, total_M, N, K, h_codes, h_scales,
+                                                 (flags & MXFP4_SCALE_UOS) != 0, stream));
+}
+
 int mxfp4_moe_combine(const void* y_bf16, int64_t ldy, int64_t R, const int32_t* rows,
                       const float* weights, int64_t T, int64_t topk, int64_t H, void* out,
                       int out_dtype, uint32_t flags, hipStream_t stream) {

@@ -28,41 +28,6 @@ typedef uint32_t v4u_t __attribute__((ext_vector_type(4)));
 // [K, 2K) of each row (row_index unused), and the values quantized are
 // h = bf16(silu(gate) * up), the down projection's input (glu_pair).
 
-// e^-g to within about 2 ulp in seven operations: e^x = 2^(x log2 e), with
-// the product split into ph = fl(x * L) and its rounding error pl (recovered
-// exactly by an fma, plus the part of log2 e below fp32), so that
-// 2^(ph + pl) = exp2(ph) * (1 + pl ln 2) to second order in pl (|pl| < 2^-17).
-// x is clamped to [-104, 89], beyond which e^x is 0 or Inf in fp32 anyway, to
-// keep pl meaningful; a NaN g gives some finite value here, and NaN in the
-// caller's g * r.
-__device__ __forceinline__ float exp_neg(float g) {
-    constexpr float LOG2E_HI = 1.44269502162933349609375f;      // fp32(log2 e)
-    constexpr float LOG2E_LO = 1.925963033500011e-08f;          // log2 e - LOG2E_HI
-    constexpr float LN2 = 0.693147180559945309f;
-    const float x = __builtin_amdgcn_fmed3f(-g, -104.0f, 89.0f);
-    const float ph = x * LOG2E_HI;
-    const float pl = __builtin_fmaf(x, LOG2E_LO, __builtin_fmaf(x, LOG2E_HI, -ph));
-    return __builtin_amdgcn_exp2f(ph) * __builtin_fmaf(pl, LN2, 1.0f);
-}
-
-// silu(g) * u for the two bf16 pairs packed in gw / uw, rounded to bf16 (RNE),
-// packed the same way.  fp32 steps: e = exp(-g), d = 1 + e, r = 1/d (v_rcp,
-// 1 ulp), s = g * r, h = s * u; d >= 1 or Inf, so the reciprocal never sees
-// a denormal, and g = -Inf gives -Inf * 0 = NaN.
-__device__ __forceinline__ uint32_t glu_pair(uint32_t gw, uint32_t uw) {
-    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-    typedef float f32x2_t __attribute__((ext_vector_type(2)));
-    const float g[2] = {__uint_as_float(gw << 16), __uint_as_float(gw & 0xFFFF0000u)};
-    const float u[2] = {__uint_as_float(uw << 16), __uint_as_float(uw & 0xFFFF0000u)};
-    float h[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const float d = 1.0f + exp_neg(g[i]);
-        h[i] = (g[i] * __builtin_amdgcn_rcpf(d)) * u[i];
-    }
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{h[0], h[1]}, bf16x2_t));
-}
-
 // Two packed bf16 values times two packed bf16 Smooth factors, each product in
 // fp32 rounded to bf16 (RNE), packed the same way.
 __device__ __forceinline__ uint32_t smooth_pair(uint32_t xw, uint32_t sw) {
