@@ -339,7 +339,10 @@ def moe_workload(torch, mx, synth):
     """One MoE layer's expert path: gathered act-quant of the routed tokens,
     grouped gate_up GEMM, expert activation + act-quant of the down input
     (silu(gate) * up), grouped down GEMM; the top-k combine that ends the layer
-    is timed beside it."""
+    is timed beside it, and so is the step with the gate_up stage as one
+    launch (the activation in the GEMM's epilogue).  That call reads the
+    gate_up weights as rows interleaved by 32 (gate, up); the synthetic
+    weights are the same bytes either way."""
     E, T, TOPK = 128, 2048, 8
     d = torch.device("cuda:0")
     perm, offsets, rows, weights = synth.route_topk_full(T, E, TOPK, seed=34, device="cpu")
@@ -383,13 +386,21 @@ def moe_workload(torch, mx, synth):
     def combine(r):
         mx.mxfp4_moe_combine(y2[r], rows, weights, out[r])
 
+    def gate_up_glu(r):
+        mx.mxfp4_grouped_gemm_silu_quantize(aq1[r][0], aq1[r][1], W["gate_up"][2],
+                                            W["gate_up"][3], offsets, *aq2[r])
+
     def step(r):
         aq_gate_up(r), gemm_gate_up(r), act_down(r), gemm_down(r)
 
+    def step_fused(r):
+        aq_gate_up(r), gate_up_glu(r), gemm_down(r)
+
     ph = Phases(torch, R)
     ph.add("step", step)
+    ph.add("step_fused", step_fused)
     ph.add("layer", lambda r: (step(r), combine(r)))
-    for f in (aq_gate_up, gemm_gate_up, act_down, gemm_down, combine):
+    for f in (aq_gate_up, gate_up_glu, gemm_gate_up, act_down, gemm_down, combine):
         ph.add(f.__name__, f)
 
     def report(t, steps):
@@ -400,8 +411,8 @@ def moe_workload(torch, mx, synth):
         gb = (E * 2048 * 4096 * mx4 + Mtot * 4096 * mx4 + Mtot * 2048 * 2 +
               E * 4096 * 1024 * mx4 + Mtot * 1024 * mx4 + Mtot * 4096 * 2)
         ach = gb / (tg * 1e-3) / 1e9
-        per = {k: round(t[k] * 1e3, 2) for k in ("aq_gate_up", "gemm_gate_up", "act_down",
-                                                 "gemm_down", "combine")}
+        per = {k: round(t[k] * 1e3, 2) for k in ("aq_gate_up", "gate_up_glu", "gemm_gate_up",
+                                                 "act_down", "gemm_down", "combine")}
         # algorithmic bytes of the two epilogue kernels
         act_b = Mtot * 2048 * 2 + Mtot * 1024 * mx4
         comb_b = Mtot * 4096 * 2 + T * 4096 * 2 + T * TOPK * 8
@@ -411,6 +422,8 @@ def moe_workload(torch, mx, synth):
                 "traffic": recorded_traffic("grouped_gemm_moe"),
                 "gemm_TFLOPs": round(flops / (tg * 1e-3) / 1e12, 1)}
         extra = {"per_kernel_us": per,
+                 "step_fused_us": round(t["step_fused"] * 1e3, 2),
+                 "step_fused_TFLOPs": round(flops / (t["step_fused"] * 1e-3) / 1e12, 1),
                  "layer_us": round(t["layer"] * 1e3, 2),
                  "layer_TFLOPs": round(flops / (t["layer"] * 1e-3) / 1e12, 1),
                  "act_down_GBps": round(act_b / (t["act_down"] * 1e-3) / 1e9, 1),

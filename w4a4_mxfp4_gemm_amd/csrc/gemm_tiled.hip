@@ -745,11 +745,13 @@ __device__ __forceinline__ bool tile_coords(int tiles_m, int tiles_n, int gm, in
 // of 64: 32 gate rows, then the 32 up rows of the same columns of h, so a
 // wave's 64 output columns are the gate and up halves of one 32-column MX
 // block of h.  The accumulators are parked as bf16 (RNE, what the plain
-// GEMM would store), then lane r of a pass takes row r: the 32 gate and 32
-// up values, h = bf16(silu(g) * u) in the act-quant kernel's GLU arithmetic,
-// and the block's 16 code bytes and scale byte by the act-quant rule.  So the
-// result equals the plain GEMM followed by the act-quant kernel's GLU mode,
-// bit for bit.  h codes are [rows][N/4] bytes, scales [rows][N/64].
+// GEMM would store); then the 64 lanes split a pass's ROWS rows, 64 / ROWS
+// lanes a row, each taking a run of the block's gate and up values:
+// h = bf16(silu(g) * u) in the act-quant kernel's GLU arithmetic, the block
+// amax across the row's lanes, and the codes and scale byte by the act-quant
+// rule.  So the result equals the plain GEMM followed by the act-quant
+// kernel's GLU mode, bit for bit.  h codes are [rows][N/4] bytes, scales
+// [rows][N/64].
 template <class S, int ROWS, bool UOS>
 __device__ __forceinline__ void store_tile_glu(const v16f (&acc)[S::NB][S::MB], lds_u8* stage,
                                                uint8_t* __restrict__ hc,
@@ -757,11 +759,14 @@ __device__ __forceinline__ void store_tile_glu(const v16f (&acc)[S::NB][S::MB], 
                                                int64_t m_end, int64_t n0, int64_t N, int wn,
                                                int wm) {
     static_assert(S::NB == 2, "one gate block and one up block per wave");
+    static_assert(ROWS == 16 || ROWS == 32, "4 or 2 lanes a row");
     using T = Stage<S, true>;
-    static_assert(ROWS >= 2 && ROWS <= 32 && (ROWS & (ROWS - 1)) == 0, "a 32-row block in passes");
+    constexpr int LPR = 64 / ROWS;            // lanes a row
+    constexpr int WPL = 16 / LPR;             // packed bf16 pairs a lane (4 or 8)
     int lane = threadIdx.x & 63;
     asm volatile("" : "+v"(lane));
     const int r32 = lane & 31, h = lane >> 5;
+    const int rr = lane % ROWS, part = lane / ROWS;
     const int64_t col0 = n0 + wn * 64;
     if (col0 >= N) return;                    // wave-uniform; N % 64 == 0
     const int64_t blk = col0 / 64;            // this wave's MX block of h
@@ -786,25 +791,49 @@ __device__ __forceinline__ void store_tile_glu(const v16f (&acc)[S::NB][S::MB], 
                 }
             }
             asm volatile("" ::: "memory");         // reads after the writes
-            const int64_t m = row0 + lane;
-            if (lane < ROWS && m < m_end) {
-                const lds_u8* src = stage + lane * T::PITCH;
-                uint32_t w[16];
+            // lane: row rr, columns [2 WPL part, 2 WPL (part + 1)) of the block
+            const lds_u8* src = stage + rr * T::PITCH + part * 4 * WPL;
+            uint32_t w[WPL];
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const v4u gv =
-                        *reinterpret_cast<const __attribute__((address_space(3))) v4u*>(src + 16 * c);
-                    const v4u uv = *reinterpret_cast<const __attribute__((address_space(3))) v4u*>(
-                        src + 64 + 16 * c);
+            for (int c = 0; c < WPL / 4; ++c) {
+                const v4u gv =
+                    *reinterpret_cast<const __attribute__((address_space(3))) v4u*>(src + 16 * c);
+                const v4u uv = *reinterpret_cast<const __attribute__((address_space(3))) v4u*>(
+                    src + 64 + 16 * c);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) w[4 * c + e] = glu_pair(gv[e], uv[e]);
-                }
-                uint32_t c4[4];
-                const uint32_t byte = quant_block32_bf16<UOS>(w, c4);
-                *reinterpret_cast<v4u*>(hc + m * hrow + blk * 16) = v4u{c4[0], c4[1], c4[2], c4[3]};
-                hs[m * srow + blk] = (uint8_t)byte;
+                for (int e = 0; e < 4; ++e) w[4 * c + e] = glu_pair(gv[e], uv[e]);
             }
             asm volatile("" ::: "memory");         // the next pass's writes after these reads
+            // the act-quant rule on the block: amax of the bf16 magnitudes
+            // (as integers) over the row's lanes, then one scale for all
+            uint32_t amax = 0;
+#pragma unroll
+            for (int i = 0; i < WPL; ++i) {
+                const uint32_t a = w[i] & 0x7FFF7FFFu;
+                amax = max(amax, max(a & 0xFFFFu, a >> 16));
+            }
+#pragma unroll
+            for (int o = ROWS; o < 64; o *= 2) amax = max(amax, (uint32_t)__shfl_xor((int)amax, o));
+            const uint32_t byte = mx_scale_byte<UOS>(amax << 16);
+            const float scale = e8m0_to_f32(byte);
+            const int64_t m = row0 + rr;
+            if (m < m_end) {
+                uint32_t c[WPL / 4];
+#pragma unroll
+                for (int d = 0; d < WPL / 4; ++d) {
+                    uint32_t v = cvt_fp4x2_bf16<0>(0u, w[4 * d], scale);
+                    v = cvt_fp4x2_bf16<1>(v, w[4 * d + 1], scale);
+                    v = cvt_fp4x2_bf16<2>(v, w[4 * d + 2], scale);
+                    v = cvt_fp4x2_bf16<3>(v, w[4 * d + 3], scale);
+                    c[d] = byte == 255u ? 0u : v;
+                }
+                uint8_t* dst = hc + m * hrow + blk * 16 + part * WPL;   // WPL code bytes a lane
+                if constexpr (WPL == 4)
+                    *reinterpret_cast<uint32_t*>(dst) = c[0];
+                else
+                    *reinterpret_cast<uint2*>(dst) = make_uint2(c[0], c[1]);
+                if (part == 0) hs[m * srow + blk] = (uint8_t)byte;
+            }
         }
     }
 }
