@@ -523,3 +523,28 @@ def test_linear_bf16_row_bias(mx, M, N, K):
             assert_gemm_fp32(got, y, s, f"bias fp32 M={M}")
         else:
             assert_gemm_bf16(got, y, f"bias bf16 M={M}")
+
+
+def test_gemm_at_the_32bit_offset_limit(mx):
+    """The tiled kernel reaches each operand through a buffer descriptor with
+    32-bit offsets, so it takes operands under 2 GiB: A of 2^31 - 2048 bytes
+    (1048575 rows at K = 4096) runs tiled; A of exactly 2^31 bytes goes to the
+    16x16x128 tile kernel, which addresses with 64 bits.  Both are checked on
+    sampled rows, the last 40 included (the largest offsets)."""
+    K, N = 4096, 256
+    d = dev()
+    m_over = (1 << 31) // (K // 2)
+    ac, as_ = synth.canonical_mxfp4(m_over, K, seed=71, device=d)
+    bc, bs = synth.canonical_mxfp4(N, K, seed=72, device=d)
+    b_cpu = (u8(bc.cpu()), u8(bs.cpu()))
+    rng = np.random.default_rng(73)
+    for M in (m_over - 1, m_over):
+        say(f"gemm at the offset limit M={M} N={N} K={K}")
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=d)
+        mx.mxfp4_gemm(ac[:M], as_[:M], bc, bs, y)
+        torch.cuda.synchronize()
+        rows = np.unique(np.concatenate([[0, 1], np.arange(M - 40, M), rng.integers(0, M, 24)]))
+        ri = torch.from_numpy(rows).to(d)
+        yo, _ = oracle.gemm(u8(ac[ri].cpu()), u8(as_[ri].cpu()), *b_cpu)
+        assert_gemm_bf16(y[ri], yo, f"offset limit M={M}")
+        del y

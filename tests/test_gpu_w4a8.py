@@ -335,3 +335,37 @@ def test_linear_w4a8_one_launch_matches_two(mx, M, N, K, ldx):
         a, b = gy.view.float().cpu(), ref.float().cpu()
         nan = torch.isnan(a) & torch.isnan(b)
         assert bool(((a.view(torch.int32) == b.view(torch.int32)) | nan).all()), dt
+
+
+def test_gemm_w4a8_at_the_32bit_offset_limit(mx):
+    """The W4A8 tiled kernel takes MXFP8 activations under 2 GiB (one byte an
+    element): 524287 rows at K = 4096 run tiled, 524288 rows (exactly 2^31
+    bytes) go to the 16x16x128 tile kernel.  Sampled rows, the last ones
+    included; operands made on the GPU."""
+    K, N = 4096, 256
+    d = dev()
+    m_over = (1 << 31) // K
+    g = torch.Generator(device=d)
+    g.manual_seed(81)
+    ac = (torch.randint(0, 0x7F, (m_over, K), generator=g, device=d, dtype=torch.int32) |
+          (torch.randint(0, 2, (m_over, K), generator=g, device=d, dtype=torch.int32) << 7)
+          ).to(torch.uint8)
+    as_ = torch.randint(117, 138, (m_over, K // 32), generator=g, device=d,
+                        dtype=torch.int32).to(torch.uint8)
+    bc, bs = synth.canonical_mxfp4(N, K, seed=82, device=d)
+    b_cpu = (u8(bc.cpu()), u8(bs.cpu()))
+    rng = np.random.default_rng(83)
+    for M in (m_over - 1, m_over):
+        say(f"gemm_w4a8 at the offset limit M={M} N={N} K={K}")
+        y = torch.empty((M, N), dtype=torch.float32, device=d)
+        mx.mxfp4_gemm_w4a8(ac[:M], as_[:M], bc, bs, y)
+        torch.cuda.synchronize()
+        rows = np.unique(np.concatenate([[0, 1], np.arange(M - 40, M), rng.integers(0, M, 24)]))
+        ri = torch.from_numpy(rows).to(d)
+        a_cpu = (u8(ac[ri].cpu()), u8(as_[ri].cpu()))
+        yo, s = oracle.gemm_w4a8(*a_cpu, *b_cpu)
+        amax, bmax = w4a8_block_maxima(*a_cpu, *b_cpu)
+        pm, pn = np.meshgrid(np.arange(rows.size), np.arange(N), indexing="ij")
+        bound = w4a8_truncation_bound(amax, bmax, pm, pn)
+        assert_w4a8(y[ri].cpu(), yo, s, bound, f"w4a8 offset limit M={M}")
+        del y
