@@ -396,3 +396,19 @@ def test_moe_epilogues_graph_replay_matches_eager(mx):
             assert torch.equal(a, b)
         step()
         torch.cuda.synchronize()
+
+
+def test_moe_epilogues_rows_past_one_grid(mx):
+    """The activation kernel over 131073 rows and the combine over 65537
+    tokens: more than one launch grid's rows, walked with a grid stride."""
+    M, I = 2 * 65535 + 3, 32
+    say(f"silu_mul_quantize rows past one grid M={M}")
+    gu = gate_up_input(M, 2 * I, seed=43)
+    gc, gs = silu_quant_both(mx, gu, I)
+    check_silu_quant(gc, gs, bf16_bits(gu), I, "ocp", "rows past one grid")
+    T, TOPK, H = 65537, 2, 8
+    say(f"moe_combine tokens past one grid T={T}")
+    _, _, rows, w = synth.route_topk_full(T, 4, TOPK, seed=44)
+    y = synth.activations(T * TOPK, H, seed=45)
+    go, out, sc = combine_both(mx, y, rows, w)
+    assert_combine(go, out, sc, TOPK, "combine past one grid")
