@@ -131,6 +131,31 @@ int mxfp4_quantize_act(const void* x_bf16, int64_t ldx, const int32_t* row_index
                        uint32_t flags, hipStream_t stream);
 
 /*
+ * MoE dispatch of the activations: each of the T token rows of x is quantized
+ * once, exactly as mxfp4_quantize_act would quantize it (AMD blog, pipeline:
+ * each batch quantized on the fly), and its codes and scale bytes are written
+ * to output rows dest_rows[t*fan + j], j < fan: the expert-sorted rows the
+ * grouped GEMM reads.  With dest_rows the inverse of a gather index (the
+ * routing's token -> sorted-row table), the output equals mxfp4_quantize_act
+ * with that gather index, bit for bit, and each token row is read once
+ * instead of fan times.  Output rows no entry names are left as they are.
+ *
+ *   x_bf16      [T][ldx] bf16, device, read; ldx >= K, ldx % 8 == 0, 16-byte
+ *               aligned
+ *   dest_rows   [T][fan] int32, device, read; each entry is clamped to
+ *               [0, R) in the kernel, so a bad table gives wrong rows but
+ *               never a write outside the outputs
+ *   fan         destinations per row, 1 .. 65536 (the MoE top-k)
+ *   R           rows of the outputs
+ *   codes       [R][K/2] u8, device, written (4-byte aligned)
+ *   scales      [R][K/32] u8, device, written
+ *   flags       0 or MXFP4_SCALE_UOS
+ */
+int mxfp4_quantize_act_scatter(const void* x_bf16, int64_t ldx, int64_t T, int64_t K,
+                               const int32_t* dest_rows, int64_t fan, int64_t R, uint8_t* codes,
+                               uint8_t* scales, uint32_t flags, hipStream_t stream);
+
+/*
  * mxfp4_quantize_act with the Smooth pre-scale (vLLM-Omni guide, pre-quantized
  * single-scale weights: W4A4 and W4A8 quantize x * mul_scale, the Smooth
  * tensor held in the activation dtype): the values quantized are

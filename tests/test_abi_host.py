@@ -176,6 +176,26 @@ def test_silu_mul_quantize_argument_checks(lib):
     assert f(FAKE, 128, 0, 64, FAKE, FAKE, 2, None) == 0      # M == 0, UOS accepted
 
 
+def test_quantize_act_scatter_argument_checks(lib):
+    f = lib.mxfp4_quantize_act_scatter
+    def g(x=FAKE, ldx=64, T=4, K=64, dest=FAKE, fan=2, R=8, c=FAKE, sc=FAKE, flags=0):
+        return f(x, ldx, T, K, dest, fan, R, c, sc, flags, None)
+    assert g(K=48) == -1                 # K % 32
+    assert g(ldx=32) == -1               # ldx < K
+    assert g(fan=0) == -1
+    assert g(fan=70000) == -1
+    assert g(R=0) == -1
+    assert g(T=-1) == -1
+    assert g(flags=1) == -1
+    assert g(dest=None) == -1
+    assert g(x=None) == -1
+    assert g(ldx=68) == -2               # ldx % 8
+    assert g(x=ODD) == -2
+    assert g(dest=ODD) == -2
+    assert g(c=ODD) == -2
+    assert g(T=0, flags=2) == 0          # nothing to do; UOS accepted
+
+
 def test_grouped_gemm_silu_quantize_argument_checks(lib):
     """Every rejected call returns before a launch (the pointers are fake)."""
     f = lib.mxfp4_grouped_gemm_silu_quantize

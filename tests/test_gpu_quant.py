@@ -393,3 +393,47 @@ def test_quantizers_rows_past_one_grid(mx):
     torch.cuda.synchronize()
     oc8, os8 = oracle.quantize_act_fp8(bf16_bits(x))
     assert np.array_equal(u8(c8), oc8) and np.array_equal(u8(s8), os8)
+
+
+@pytest.mark.parametrize("T,E,topk,K,rule", [(256, 16, 4, 512, "ocp"), (2048, 128, 8, 4096, "ocp"),
+                                            (37, 5, 3, 96, "uos")])
+def test_act_quant_scatter_equals_the_gather(mx, T, E, topk, K, rule):
+    """Each token row quantized once and written to its routed rows: bit for
+    bit the oracle's act-quant gathered by the routing's sorted order."""
+    say(f"act_quant scatter T={T} E={E} top-{topk} K={K} {rule}")
+    perm, _, rows, _ = synth.route_topk_full(T, E, topk, seed=T + K)
+    x = synth.activations(T, K, seed=T, outlier_seed=K)
+    R = T * topk
+    gc = Guarded((R, K // 2), torch.uint8)
+    gs = Guarded((R, K // 32), torch.uint8)
+    mx.mxfp4_quantize_act_scatter(x.to(dev()), rows.to(dev()), gc.view, gs.view,
+                                  scale_rule=rule)
+    torch.cuda.synchronize()
+    assert gc.intact() and gs.intact(), "write outside the outputs"
+    oc, os_ = oracle.quantize_act(bf16_bits(x), row_index=perm.numpy(), scale_rule=rule)
+    assert_same((u8(gc.view), u8(gs.view)), (oc, os_), "scatter")
+
+
+def test_act_quant_scatter_clamps_bad_rows(mx):
+    """Destination rows outside [0, R) are clamped in the kernel: no write
+    outside the outputs, and the rows named once by a valid entry are right."""
+    say("act_quant scatter with bad destination rows")
+    T, fan, K = 64, 2, 256
+    R = T * fan
+    x = synth.activations(T, K, seed=5)
+    dest = np.arange(R, dtype=np.int32).reshape(T, fan)
+    dest[3, 0], dest[9, 1], dest[20, 0] = -7, R + 100, 2 ** 31 - 1
+    gc = Guarded((R, K // 2), torch.uint8)
+    gs = Guarded((R, K // 32), torch.uint8)
+    mx.mxfp4_quantize_act_scatter(x.to(dev()), torch.from_numpy(dest).to(dev()), gc.view,
+                                  gs.view)
+    torch.cuda.synchronize()
+    assert gc.intact() and gs.intact(), "write outside the outputs"
+    oc, os_ = oracle.quantize_act(bf16_bits(x))
+    clamped = np.clip(dest.astype(np.int64), 0, R - 1)
+    owners = np.bincount(clamped.ravel(), minlength=R)
+    for t in range(T):
+        for j in range(fan):
+            d = clamped[t, j]
+            if owners[d] == 1 and dest[t, j] == d:
+                assert np.array_equal(u8(gc.view)[d], oc[t]) and np.array_equal(u8(gs.view)[d], os_[t])

@@ -50,6 +50,8 @@ def _load_library() -> ctypes.CDLL:
     lib.mxfp4_grouped_gemm.restype = ctypes.c_int
     lib.mxfp4_linear_bf16.argtypes = [P, I, I, I, I, P, P, P, P, ctypes.c_int, P, SZ, U32, P]
     lib.mxfp4_linear_bf16.restype = ctypes.c_int
+    lib.mxfp4_quantize_act_scatter.argtypes = [P, I, I, I, P, I, I, P, P, U32, P]
+    lib.mxfp4_quantize_act_scatter.restype = ctypes.c_int
     lib.mxfp4_quantize_act_smooth.argtypes = [P, I, P, P, I, I, P, P, U32, P]
     lib.mxfp4_quantize_act_smooth.restype = ctypes.c_int
     lib.mxfp8_quantize_act_smooth.argtypes = [P, I, P, P, I, I, P, P, U32, P]
@@ -89,7 +91,7 @@ EXPORTED_SYMBOLS = ("mxfp4_requant_from_nvfp4", "mxfp4_requant_from_nvfp4_subset
                     "mxfp4_moe_combine", "mxfp8_quantize_act", "mxfp4_gemm_w4a8",
                     "mxfp4_linear_w4a8_bf16", "mxfp4_linear_w4a8_workspace_size",
                     "mxfp4_quantize_act_smooth", "mxfp8_quantize_act_smooth",
-                    "mxfp4_grouped_gemm_silu_quantize",
+                    "mxfp4_grouped_gemm_silu_quantize", "mxfp4_quantize_act_scatter",
                     "mxfp4_status_string", "mxfp4_version")
 
 
@@ -511,6 +513,34 @@ def mxfp4_grouped_gemm(a_codes, a_scales, b_codes, b_scales, offsets, y=None, *,
 
 
 
+def mxfp4_quantize_act_scatter(x, dest_rows, codes=None, scales=None, *, R=None, K=None,
+                               scale_rule="ocp", stream=None):
+    """MoE dispatch: bf16 x [T, ldx] -> MXFP4 rows written to
+    dest_rows[t, j] (int32 [T, fan]) of codes [R, K/2] / scales [R, K/32].
+    R defaults to T * fan (every routed row once)."""
+    _need(x, "x", torch.bfloat16)
+    dev = x.device
+    _need(dest_rows, "dest_rows", torch.int32, dev)
+    if x.dim() != 2 or dest_rows.dim() != 2 or dest_rows.shape[0] != x.shape[0]:
+        raise ValueError("x must be [T, ldx] and dest_rows [T, fan]")
+    T, ldx = x.shape
+    fan = dest_rows.shape[1]
+    K = ldx if K is None else int(K)
+    R = T * fan if R is None else int(R)
+    if codes is None:
+        codes = torch.empty((R, K // 2), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty((R, K // 32), dtype=torch.uint8, device=dev)
+    _need(codes, "codes", torch.uint8, dev)
+    _need(scales, "scales", torch.uint8, dev)
+    if codes.shape != (R, K // 2) or scales.shape != (R, K // 32):
+        raise ValueError("output shapes do not match [R, K/2] / [R, K/32]")
+    _check("mxfp4_quantize_act_scatter", _lib.mxfp4_quantize_act_scatter(
+        _ptr(x), ldx, T, K, _ptr(dest_rows), fan, R, _ptr(codes), _ptr(scales),
+        _rule_flag(scale_rule), _stream(stream, dev)))
+    return codes, scales
+
+
 def mxfp4_grouped_gemm_silu_quantize(a_codes, a_scales, b_codes, b_scales, offsets,
                                      codes=None, scales=None, *, scale_rule="ocp", stream=None):
     """The MoE gate_up grouped GEMM with the expert activation and its MXFP4
@@ -554,6 +584,7 @@ __all__ = ["mxfp4_requant_from_nvfp4", "mxfp4_quantize_act", "mxfp4_gemm",
            "mxfp8_quantize_act", "mxfp4_gemm_w4a8", "mxfp4_linear_w4a8_bf16",
            "mxfp4_linear_w4a8_workspace_size", "mxfp4_quantize_act_smooth",
            "mxfp8_quantize_act_smooth", "mxfp4_grouped_gemm_silu_quantize",
+           "mxfp4_quantize_act_scatter",
            "mxfp4_status_string",
            "mxfp4_version", "Mxfp4Error", "LIBRARY_PATH", "EXPORTED_SYMBOLS",
            "MXFP4_OUT_BF16", "MXFP4_OUT_FP32", "MXFP4_REQ_INTERMEDIATE_BF16",

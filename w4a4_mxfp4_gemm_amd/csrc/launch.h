@@ -24,6 +24,13 @@ hipError_t launch_requant(const uint8_t* nv_codes, const uint8_t* nv_scales,
 
 // MoE expert activation + act-quant: gate_up bf16 [M][ldg] (gate = columns
 // [0, I), up = [I, 2I)) -> MXFP4 of bf16(silu(gate) * up), [M][I/2] + [M][I/32].
+// Act-quant of T rows, each written to rows dest[t * fan + j] (clamped to
+// [0, R)) of the outputs.
+hipError_t launch_act_quant_scatter(const uint16_t* x, int64_t ldx, int64_t T, int64_t K,
+                                    const int32_t* dest, int64_t fan, int64_t R,
+                                    uint8_t* codes, uint8_t* scales, bool uos,
+                                    hipStream_t stream);
+
 hipError_t launch_silu_mul_quantize(const uint16_t* gate_up, int64_t ldg, int64_t M, int64_t I,
                                    uint8_t* codes, uint8_t* scales, bool uos,
                                    hipStream_t stream);

@@ -100,6 +100,21 @@ int mxfp4_quantize_act(const void* x_bf16, int64_t ldx, const int32_t* row_index
                                          stream));
 }
 
+int mxfp4_quantize_act_scatter(const void* x_bf16, int64_t ldx, int64_t T, int64_t K,
+                               const int32_t* dest_rows, int64_t fan, int64_t R, uint8_t* codes,
+                               uint8_t* scales, uint32_t flags, hipStream_t stream) {
+    if (T < 0 || check_k(K) != MXFP4_OK || ldx < K || fan < 1 || fan > (1 << 16) || R < 0)
+        return MXFP4_EINVAL;
+    if ((flags & ~(uint32_t)MXFP4_SCALE_UOS) != 0) return MXFP4_EINVAL;
+    if (T == 0) return MXFP4_OK;
+    if (R == 0 || !x_bf16 || !dest_rows || !codes || !scales) return MXFP4_EINVAL;
+    if (!aligned(x_bf16, 16) || ldx % 8 != 0 || !aligned(codes, 4) || !aligned(dest_rows, 4))
+        return MXFP4_EALIGN;
+    return from_hip(mx::launch_act_quant_scatter(static_cast<const uint16_t*>(x_bf16), ldx, T,
+                                                 K, dest_rows, fan, R, codes, scales,
+                                                 (flags & MXFP4_SCALE_UOS) != 0, stream));
+}
+
 int mxfp4_quantize_act_smooth(const void* x_bf16, int64_t ldx, const int32_t* row_index,
                               const void* smooth_bf16, int64_t M, int64_t K, uint8_t* codes,
                               uint8_t* scales, uint32_t flags, hipStream_t stream) {

@@ -41,11 +41,16 @@ __device__ __forceinline__ uint32_t smooth_pair(uint32_t xw, uint32_t sw) {
 // SMOOTH: the values quantized are bf16(x * smooth[k]) (smooth: bf16 [K], the
 // per-channel Smooth pre-scale), each product in fp32 (exact for two bf16
 // values outside fp32's subnormal range) rounded to bf16.
-template <int ROWS, bool NT_OUT, bool UOS, bool GLU = false, bool SMOOTH = false>
+// SCATTER: row m of x is quantized once and its codes and scale bytes are
+// written to output rows dest[m * fan + j], j < fan, each clamped to [0, R)
+// (the MoE dispatch: a token's row to each of its routed expert rows).
+template <int ROWS, bool NT_OUT, bool UOS, bool GLU = false, bool SMOOTH = false,
+          bool SCATTER = false>
 __global__ __launch_bounds__(256) void act_quant_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const int32_t* __restrict__ row_index,
     int64_t M, int64_t K, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
-    const uint16_t* __restrict__ smooth) {
+    const uint16_t* __restrict__ smooth, const int32_t* __restrict__ dest = nullptr,
+    int fan = 0, int64_t R = 0) {
     const int64_t chunks = K / 8;                     // 16-byte chunks per row; multiple of 4
     const int64_t kq = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (kq >= chunks) return;                         // whole quads leave together
@@ -107,6 +112,15 @@ __global__ __launch_bounds__(256) void act_quant_kernel(
             packed = cvt_fp4x2_bf16<2>(packed, w[2], scale);
             packed = cvt_fp4x2_bf16<3>(packed, w[3], scale);
             if (byte == 255u) packed = 0u;            // NaN/Inf block: codes are zero
+            if constexpr (SCATTER) {
+                for (int j = 0; j < fan; ++j) {
+                    int64_t d = dest[m * fan + j];
+                    d = d < 0 ? 0 : (d >= R ? R - 1 : d);
+                    *reinterpret_cast<uint32_t*>(codes + d * (K / 2) + kq * 4) = packed;
+                    if ((kq & 3) == 0) scales[d * (K / 32) + kq / 4] = (uint8_t)byte;
+                }
+                continue;
+            }
             uint32_t* cdst = reinterpret_cast<uint32_t*>(codes + m * (K / 2) + kq * 4);
             uint8_t* sdst = scales + m * (K / 32) + kq / 4;
             if (NT_OUT) {
@@ -343,9 +357,10 @@ hipError_t launch_act_quant(const uint16_t* x, int64_t ldx, const int32_t* row_i
     // slower for the decode and [4096,4096] sizes
     const bool nt_out = !row_index && M * (K / 2) >= ((int64_t)16 << 20);
     const dim3 grid((unsigned)gx, (unsigned)gy);
+    const int32_t* no_dest = nullptr;
     auto go = [&](auto kernel) {
         hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, x, ldx, row_index, M, K, codes,
-                           scales, smooth);
+                           scales, smooth, no_dest, 0, (int64_t)0);
     };
     if (smooth) {
         if (uos)
@@ -363,6 +378,28 @@ hipError_t launch_act_quant(const uint16_t* x, int64_t ldx, const int32_t* row_i
     return hipGetLastError();
 }
 
+hipError_t launch_act_quant_scatter(const uint16_t* x, int64_t ldx, int64_t T, int64_t K,
+                                    const int32_t* dest, int64_t fan, int64_t R,
+                                    uint8_t* codes, uint8_t* scales, bool uos,
+                                    hipStream_t stream) {
+    constexpr int ROWS = 2;
+    const int64_t gx = (K / 8 + 255) / 256;
+    int64_t gy = (T + ROWS - 1) / ROWS;
+    if (gy > 65535) gy = 65535;
+    const dim3 grid((unsigned)gx, (unsigned)gy);
+    const uint16_t* none = nullptr;
+    const int32_t* no_index = nullptr;
+    if (uos)
+        hipLaunchKernelGGL((act_quant_kernel<ROWS, false, true, false, false, true>), grid,
+                           dim3(256), 0, stream, x, ldx, no_index, T, K, codes, scales, none,
+                           dest, (int)fan, R);
+    else
+        hipLaunchKernelGGL((act_quant_kernel<ROWS, false, false, false, false, true>), grid,
+                           dim3(256), 0, stream, x, ldx, no_index, T, K, codes, scales, none,
+                           dest, (int)fan, R);
+    return hipGetLastError();
+}
+
 hipError_t launch_silu_mul_quantize(const uint16_t* gate_up, int64_t ldg, int64_t M, int64_t I,
                                    uint8_t* codes, uint8_t* scales, bool uos,
                                    hipStream_t stream) {
@@ -372,12 +409,16 @@ hipError_t launch_silu_mul_quantize(const uint16_t* gate_up, int64_t ldg, int64_
     if (gy > 65535) gy = 65535;
     const dim3 grid((unsigned)gx, (unsigned)gy);
     // the codes feed the down GEMM next: normal stores
+    const int32_t* no_index = nullptr;
+    const uint16_t* none = nullptr;
     if (uos)
         hipLaunchKernelGGL((act_quant_kernel<ROWS, false, true, true>), grid, dim3(256), 0,
-                           stream, gate_up, ldg, nullptr, M, I, codes, scales, nullptr);
+                           stream, gate_up, ldg, no_index, M, I, codes, scales, none, no_index, 0,
+                           (int64_t)0);
     else
         hipLaunchKernelGGL((act_quant_kernel<ROWS, false, false, true>), grid, dim3(256), 0,
-                           stream, gate_up, ldg, nullptr, M, I, codes, scales, nullptr);
+                           stream, gate_up, ldg, no_index, M, I, codes, scales, none, no_index, 0,
+                           (int64_t)0);
     return hipGetLastError();
 }
 
