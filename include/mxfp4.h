@@ -147,7 +147,7 @@ int mxfp4_quantize_act(const void* x_bf16, int64_t ldx, const int32_t* row_index
  *               never a write outside the outputs
  *   fan         destinations per row, 1 .. 65536 (the MoE top-k)
  *   R           rows of the outputs
- *   codes       [R][K/2] u8, device, written (4-byte aligned)
+ *   codes       [R][K/2] u8, device, written (16-byte aligned)
  *   scales      [R][K/32] u8, device, written
  *   flags       0 or MXFP4_SCALE_UOS
  */

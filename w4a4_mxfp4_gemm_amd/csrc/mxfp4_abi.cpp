@@ -108,7 +108,7 @@ int mxfp4_quantize_act_scatter(const void* x_bf16, int64_t ldx, int64_t T, int64
     if ((flags & ~(uint32_t)MXFP4_SCALE_UOS) != 0) return MXFP4_EINVAL;
     if (T == 0) return MXFP4_OK;
     if (R == 0 || !x_bf16 || !dest_rows || !codes || !scales) return MXFP4_EINVAL;
-    if (!aligned(x_bf16, 16) || ldx % 8 != 0 || !aligned(codes, 4) || !aligned(dest_rows, 4))
+    if (!aligned(x_bf16, 16) || ldx % 8 != 0 || !aligned(codes, 16) || !aligned(dest_rows, 4))
         return MXFP4_EALIGN;
     return from_hip(mx::launch_act_quant_scatter(static_cast<const uint16_t*>(x_bf16), ldx, T,
                                                  K, dest_rows, fan, R, codes, scales,
