@@ -64,6 +64,8 @@ def _load():
     lib.orc_bf16_from_double.argtypes = [ctypes.c_double]
     lib.orc_e2m1_encode.restype = ctypes.c_uint
     lib.orc_e2m1_encode.argtypes = [ctypes.c_double]
+    lib.orc_e2m1_encode_bf16_at_scale.restype = None
+    lib.orc_e2m1_encode_bf16_at_scale.argtypes = [P, I, ctypes.c_uint, P]
     lib.orc_shared_exponent.restype = ctypes.c_uint
     lib.orc_shared_exponent.argtypes = [ctypes.c_double]
     lib.orc_shared_exponent_uos.restype = ctypes.c_uint
@@ -160,6 +162,15 @@ def bf16_from_double_array(v) -> np.ndarray:
 
 def e2m1_encode(q: float) -> int:
     return int(_load().orc_e2m1_encode(float(q)))
+
+
+def e2m1_encode_bf16_at_scale(x_bits, byte: int) -> np.ndarray:
+    """R4 at a fixed scale byte: the E2M1 code (0..15) of each bf16 value
+    divided by 2^(byte - 127), as the block quantizer encodes its elements."""
+    x_bits = _c(x_bits, np.uint16)
+    out = np.empty(x_bits.shape, dtype=np.uint8)
+    _load().orc_e2m1_encode_bf16_at_scale(_ptr(x_bits), x_bits.size, int(byte), _ptr(out))
+    return out
 
 
 # Scale rules: "ocp" (R3, the OCP MX shared exponent) and "uos" (R9, the
@@ -286,6 +297,42 @@ def grouped_gemm(a_codes, a_scales, b_codes, b_scales, offsets):
     _load().orc_grouped_gemm(_ptr(a_codes), _ptr(a_scales), _ptr(b_codes),
                              _ptr(b_scales), _ptr(offsets), E, N, K, _ptr(y), _ptr(s))
     return y, s
+
+
+# ---- O12: the layerwise load ----------------------------------------------------
+def layerwise_requant(sources, excluded, dest, first_layer=0, flags_bf16=False,
+                      scale_rule="ocp"):
+    """The layerwise load of the AMD blog's pipeline section (Figure 1): the
+    model's NVFP4 weights are requantized one layer at a time into a
+    destination allocated beforehand, and tensors the producer excluded are
+    skipped (the blog's note on producer excludes).  In symbols, for every
+    layer l >= first_layer, tensor kind k and tensor t:
+
+        dest[k][l, t] = requant(sources[l][k][t])   unless excluded[l][k][t]
+
+    and every excluded slot keeps whatever it held.
+
+    sources   per layer, per kind: (codes [T,N,K/2], E4M3 [T,N,K/16], g [T])
+    excluded  bool [L, kinds, T]
+    dest      per kind: (codes [L,T,N,K/2], E8M0 [L,T,N,K/32]), written in place
+    Returns the number of tensors requantized.  Peak extra memory is one
+    layer's source, which the caller holds; this function holds nothing more
+    than one requantized kind of one layer."""
+    excluded = np.asarray(excluded, dtype=bool)
+    L = len(sources)
+    done = 0
+    for l in range(first_layer, L):
+        for k, (codes, scales, g) in enumerate(sources[l]):
+            keep = np.nonzero(~excluded[l, k])[0]
+            if keep.size == 0:
+                continue
+            c, sc = requant(np.asarray(codes)[keep], np.asarray(scales)[keep],
+                            np.asarray(g, dtype=np.float32).reshape(-1)[keep],
+                            bf16_intermediate=flags_bf16, scale_rule=scale_rule)
+            dest[k][0][l, keep] = c
+            dest[k][1][l, keep] = sc
+            done += keep.size
+    return done
 
 
 # ---- Smooth pre-scale (R17) ---------------------------------------------------------

@@ -110,14 +110,17 @@ uint16_t orc_bf16_from_float(float v) { return orc_bf16_from_double((double)v); 
 /* R4 -- element encode ([P2] single-scale section: round_mode="rint", E2M1
    maximum 6).  The E2M1 value nearest to q is chosen; when q lies exactly
    half-way between two neighbours the one with the even code (mantissa bit
-   0) wins.  Values beyond 6 are nearest to 6, so saturation falls out of the
-   nearest-value rule.  The sign bit is copied from q.  Distances are exact in
-   fp64 for every q the path produces (q has at most 24 significant bits and
-   |q| < 8), so no false ties arise. */
+   0) wins.  Magnitudes of 6 and above saturate to 6 (E2M1 has no Inf); the
+   test comes first because for |q| beyond about 2^53 the fp64 distances to
+   4 and 6 are no longer exact and would tie.  The sign bit is copied from q.
+   Below 6 the distances are exact in fp64 (q has at most 24 significant
+   bits), so no false ties arise. */
 unsigned orc_e2m1_encode(double q)
 {
     static const double grid[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
     double a = fabs(q);
+    if (a >= 6.0)
+        return (signbit(q) ? 8u : 0u) | 7u;
     unsigned best = 0;
     double bestd = a;
     for (unsigned i = 1; i < 8; ++i) {
@@ -128,6 +131,21 @@ unsigned orc_e2m1_encode(double q)
         }
     }
     return (signbit(q) ? 8u : 0u) | best;
+}
+
+/* R4 applied to bf16 values at one fixed scale byte: the element step of
+   the block quantizer below (q = v / 2^(byte - 127), exact by ldexp, then the
+   nearest E2M1 code), one code per input in the low nibble of codes[i].
+   Exposed so that the encoder can be swept over every (bf16 value, scale
+   byte) pair; NaN and Inf inputs are the block rule's business and get 0. */
+void orc_e2m1_encode_bf16_at_scale(const uint16_t* x, int64_t n, unsigned byte,
+                                   uint8_t* codes)
+{
+    int e = (int)byte - 127;
+    for (int64_t i = 0; i < n; ++i) {
+        double v = orc_bf16_value(x[i]);
+        codes[i] = (isnan(v) || isinf(v)) ? 0u : (uint8_t)orc_e2m1_encode(ldexp(v, -e));
+    }
 }
 
 /* R3 -- shared exponent of an OCP MX block ([P2] single-scale section:

@@ -99,6 +99,10 @@ double   orc_bf16_value(uint16_t bits);
 uint16_t orc_bf16_from_double(double v);         /* RNE, NaN -> 0x7FC0      */
 uint16_t orc_bf16_from_float(float v);           /* RNE, NaN -> 0x7FC0      */
 unsigned orc_e2m1_encode(double q);              /* R4                      */
+/* R4 at one scale byte over n bf16 values (the block quantizer's element
+   step); NaN/Inf inputs give 0. */
+void     orc_e2m1_encode_bf16_at_scale(const uint16_t* x, int64_t n, unsigned byte,
+                                       uint8_t* codes);
 unsigned orc_shared_exponent(double amax);       /* R3, amax >= 0 or NaN    */
 unsigned orc_shared_exponent_uos(double amax);   /* R9, amax >= 0 or NaN    */
 

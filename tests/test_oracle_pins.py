@@ -114,6 +114,26 @@ def test_e2m1_encode_matches_regionwise_rint():
     assert np.array_equal(codes >= 8, np.signbit(q))
 
 
+def test_e2m1_encode_exhaustive_every_bf16_at_every_scale_byte():
+    """The block quantizer's element step over all 65,536 bf16 patterns (NaN
+    and Inf aside) at every finite scale byte 0..254: the code equals the
+    region-wise rint of |v| / 2^(byte-127), computed here from torch's bf16
+    decode, and carries v's sign bit (so negative values that round to zero
+    give 0x8)."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    v = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).double().numpy()
+    finite = np.isfinite(v)
+    bits, v = bits[finite], v[finite]
+    sign = np.signbit(v)
+    for byte in range(255):
+        codes = oracle.e2m1_encode_bf16_at_scale(bits, byte)
+        q = np.ldexp(v, 127 - byte)
+        mag = rint_reference(q)
+        got = E2M1[codes]
+        bad = (np.abs(got) != mag) | ((codes >= 8) != sign)
+        assert not bad.any(), (byte, int(bits[np.argmax(bad)]))
+
+
 def test_e2m1_encode_roundtrip_all_codes():
     for c in range(16):
         assert oracle.e2m1_encode(E2M1[c]) == c
@@ -608,6 +628,26 @@ def test_combine_one_hot_weights_select_rows():
     w1[np.arange(w.shape[0]), 3] = 1.0
     out, s = oracle.moe_combine(bits, rows, w1)
     assert np.array_equal(out, y[rows[:, 3]]) and np.array_equal(s, np.abs(out))
+
+
+def test_combine_per_token_weights_and_rows():
+    """Each token has its own weights and rows: token t one-hot at column
+    t mod topk returns its own routed row there, and distinct random weights
+    give numpy's fp64 weighted sum of the gathered rows.  A weight read from
+    the wrong token (w[j] in place of w[t*topk+j]) or a row from the wrong
+    token fails both."""
+    T, topk, H = 24, 8, 40
+    bits, y, rows, w = combine_case(106, T=T, topk=topk, H=H)
+    w1 = np.zeros_like(w)
+    col = np.arange(T) % topk
+    w1[np.arange(T), col] = 1.0
+    out, _ = oracle.moe_combine(bits, rows, w1)
+    assert np.array_equal(out, y[rows[np.arange(T), col]])
+    assert len({tuple(r) for r in w.round(6)}) == T         # the weights differ per token
+    out, s = oracle.moe_combine(bits, rows, w)
+    ref = np.einsum("tj,tjn->tn", w.astype(np.float64), y[rows])
+    assert np.allclose(out, ref, rtol=0, atol=4e-16 * s.max())
+    assert not np.allclose(out[1:], ref[0], rtol=0, atol=1e-6)
 
 
 def test_combine_equal_rows_and_power_of_two_weights():
