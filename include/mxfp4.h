@@ -19,15 +19,23 @@
  *
  * Conventions:
  *   - Every tensor pointer is a DEVICE pointer to row-major memory owned by
- *     the caller.  The library never allocates, frees or synchronises; all
- *     work is enqueued on `stream`.  It keeps no global state.
+ *     the caller, except the host buffers of the layerwise load and the
+ *     subset requant's tensor list (marked HOST).  No call allocates or frees
+ *     device memory or synchronises the host; all work is enqueued on
+ *     `stream`.  The library holds no device memory of its own.
  *   - Every call returns MXFP4_OK or a negative mxfp4_status.  Arguments are
  *     checked before anything is enqueued; on an error nothing is launched.
  *   - K must be a positive multiple of 32 (whole MX blocks).  A zero row
  *     count (M == 0, total_M == 0, T == 0) is a no-op returning MXFP4_OK.
- *   - Code pointers (u8 [rows][K/2]) and bf16 activation pointers must be
- *     16-byte aligned; scale pointers have no alignment requirement; fp32
- *     outputs must be 4-byte and bf16 outputs 2-byte aligned.
+ *   - Alignment, enforced with MXFP4_EALIGN: code pointers (u8 [rows][K/2])
+ *     and bf16 activation pointers 16 bytes; fp32 outputs 4 bytes, bf16
+ *     outputs 2 bytes; the requant's E4M3 scales (nv_scales) 2 bytes; the
+ *     linear calls' weight scales (b_scales) 16 bytes; bias and Smooth
+ *     vectors 16 bytes.  Other scale pointers may have any alignment, but
+ *     the fast GEMM kernels need them aligned (16 bytes for the decode
+ *     kernel, 4 for the tiled ones) and a call whose scale pointers are not
+ *     falls back to the generic kernel: the same results, slower.  Each GEMM
+ *     call lists its kernel choice.
  *   - Results are bitwise reproducible from run to run (no atomics, fixed
  *     reduction order).
  */
@@ -80,7 +88,8 @@ enum { MXFP4_SCALE_UOS = 1u << 1 };
  * holding a NaN or Inf gets scale 0xFF and all-zero codes.
  *
  *   nv_codes   [T][N][K/2]  u8, device, read        (16-byte aligned)
- *   nv_scales  [T][N][K/16] u8 (float8_e4m3fn bits), device, read
+ *   nv_scales  [T][N][K/16] u8 (float8_e4m3fn bits), device, read (2-byte
+ *              aligned: the two E4M3 scales of an MX block are one load)
  *   nv_global  [T] fp32, device, read: the multiplier applied on dequant
  *              (a checkpoint that stores a divisor passes its reciprocal)
  *   mx_codes   [T][N][K/2]  u8, device, written     (16-byte aligned)
@@ -110,6 +119,86 @@ int mxfp4_requant_from_nvfp4_subset(const uint8_t* nv_codes, const uint8_t* nv_s
                                     const int32_t* tensors, int64_t n_tensors,
                                     uint8_t* mx_codes, uint8_t* mx_scales,
                                     uint32_t flags, hipStream_t stream);
+
+/*
+ * The layerwise load (AMD blog, pipeline section under Figure 1: the NVFP4
+ * checkpoint is requantized one layer at a time into a destination allocated
+ * beforehand, so the load needs one layer's worth of extra memory; tensors
+ * the producer excluded are skipped, per the blog's note on producer
+ * excludes).  A part is one tensor kind of one layer: T same-shape NVFP4
+ * tensors in HOST memory and their MXFP4 destination in DEVICE memory.
+ *
+ *   nv_codes   [T][N][K/2]  u8, host, read   (pinned, e.g. hipHostMalloc, for
+ *   nv_scales  [T][N][K/16] u8, host, read    the copies to overlap the
+ *   nv_global  [T] fp32, host, read           requant; pageable memory works
+ *                                             but serialises them)
+ *   excluded   [T] u8, host, read, or NULL: a non-zero entry leaves that
+ *              tensor's destination slot untouched and its source unread
+ *   mx_codes   [T][N][K/2]  u8, device, written (16-byte aligned)
+ *   mx_scales  [T][N][K/32] u8, device, written
+ *   T, N, K    T >= 0, N > 0, K a positive multiple of 32
+ */
+typedef struct {
+    const uint8_t* nv_codes;
+    const uint8_t* nv_scales;
+    const float* nv_global;
+    const uint8_t* excluded;
+    uint8_t* mx_codes;
+    uint8_t* mx_scales;
+    int64_t T, N, K;
+} mxfp4_load_part;
+
+/*
+ * One step of the load plan: tensors [t0, t1) of parts[part], staged in
+ * scratch slot `slot` (0 or 1) at the given byte offsets from the scratch
+ * base (codes of tensor t0 + i at codes_offset + i*N*K/2, its E4M3 scales at
+ * scales_offset + i*N*K/16, its global at global_offset + 4i).  t0 and t1-1
+ * are never excluded; excluded tensors between them are neither copied nor
+ * converted.  Slot s spans [s * slot_bytes, (s+1) * slot_bytes).
+ */
+typedef struct {
+    int64_t part;
+    int64_t t0, t1;
+    int64_t slot;
+    uint64_t codes_offset, scales_offset, global_offset;
+} mxfp4_load_chunk;
+
+/*
+ * The plan mxfp4_requant_layers_from_host follows, computed on the host
+ * alone (no HIP call, no device pointer read; only the parts' sizes and
+ * excluded lists matter).  The scratch is split into two slots of
+ * slot_bytes = scratch_bytes / 2 rounded down to 256; each chunk is the
+ * largest run of one part's tensors that fits a slot, parts in order, slots
+ * alternating.  With chunks == NULL only *n_chunks (and *slot_bytes if not
+ * NULL) is written.  Errors: MXFP4_EINVAL for a bad part, a slot too small
+ * for one tensor of some part (N*K/2 and N*K/16 bytes each rounded up to
+ * 256, plus 4), or max_chunks below the chunk count.
+ */
+int mxfp4_layerwise_plan(const mxfp4_load_part* parts, int64_t n_parts, size_t scratch_bytes,
+                         mxfp4_load_chunk* chunks, int64_t max_chunks, int64_t* n_chunks,
+                         uint64_t* slot_bytes);
+
+/*
+ * Runs the plan: for each chunk, the kept tensors' NVFP4 bytes are copied
+ * host -> device into their slot on copy_stream, then converted on `stream`
+ * by the requant of mxfp4_requant_from_nvfp4 into the destination; a slot is
+ * refilled only after the requant that read it.  Every kept tensor of every
+ * part is written exactly as mxfp4_requant_from_nvfp4 would write it; every
+ * excluded slot is left alone.  The call only enqueues work: the host
+ * buffers must stay valid, and the scratch unused by others, until `stream`
+ * has finished it (which implies copy_stream has).  copy_stream may equal
+ * stream (no overlap).  Besides the scratch it uses no device memory; it
+ * creates and destroys four HIP events.
+ *
+ *   parts, n_parts   as for mxfp4_layerwise_plan, with every pointer set for
+ *                    parts with T > 0
+ *   scratch          device memory of scratch_bytes, 256-byte aligned; one
+ *                    layer's NVFP4 bytes is enough for any layer
+ *   flags            0, or MXFP4_REQ_INTERMEDIATE_BF16 and/or MXFP4_SCALE_UOS
+ */
+int mxfp4_requant_layers_from_host(const mxfp4_load_part* parts, int64_t n_parts,
+                                   void* scratch, size_t scratch_bytes, uint32_t flags,
+                                   hipStream_t copy_stream, hipStream_t stream);
 
 /*
  * Dynamic per-call MXFP4 quantization of bf16 activations (AMD blog, closing
@@ -182,6 +271,13 @@ int mxfp4_quantize_act_smooth(const void* x_bf16, int64_t ldx, const int32_t* ro
  *   workspace           reserved: the current kernels need none; pass NULL
  *                       and 0 (mxfp4_gemm_workspace_size returns 0)
  *   flags               must be 0
+ * Kernel choice (every kernel gives the same results):
+ *   M <= 64, K = 2048 or 4096, N >= 16, a_codes/a_scales/b_scales 16-byte
+ *     aligned: the weight-streaming decode kernel;
+ *   else M >= 128, K % 512 == 0, each operand's codes under 2 GiB, both scale
+ *     pointers 4-byte aligned: the LDS-tiled MFMA kernel (persistent tile walk
+ *     when there is more than one round of tiles);
+ *   else the generic 16x16x128 MFMA kernel.
  */
 int mxfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
                const uint8_t* b_codes, const uint8_t* b_scales,
@@ -204,6 +300,9 @@ int mxfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
  *                       outside y.
  *   y                   [total_M][N] bf16 or fp32, device, written
  *   workspace, flags    as for mxfp4_gemm
+ * Kernel choice (same results): K % 512 == 0, E <= 2048, each operand's
+ * codes under 2 GiB and both scale pointers 4-byte aligned: the LDS-tiled
+ * persistent kernel that walks the offset table; else the generic kernel.
  */
 int mxfp4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
                        const uint8_t* b_codes, const uint8_t* b_scales,
@@ -221,14 +320,17 @@ size_t mxfp4_gemm_workspace_size(int64_t M, int64_t N, int64_t K);
  * giving the same y bit for bit, plus an optional row bias (the SGLang FP4
  * post's apply_weights: quantize, GEMM, add bias; the vLLM-Omni guide's
  * W4A4/W4A8 notes: bf16 output with a bf16 row bias).  The bias joins each
- * fp32 sum before its one rounding: y[m][n] = round(sum_k A B + bias[n]).  For decode-shaped calls (M <= 16, K = 2048
- * or 4096, N >= 16, 16-byte-aligned b_scales) it is one launch whose
- * workgroups quantize their own activation blocks while their weight loads
- * stream; otherwise the two launches run through the caller's workspace.
+ * fp32 sum before its one rounding: y[m][n] = round(sum_k A B + bias[n]).
+ * For decode shapes (M <= 16, K = 2048 or 4096, N >= 16) it is one launch
+ * whose workgroups quantize their own activation blocks while their weight
+ * loads stream; for every other shape the two launches run through the
+ * caller's workspace.  The choice depends on the shape alone, so
+ * mxfp4_linear_workspace_size is exact.
  *
  *   x_bf16      [M][ldx] bf16, device, read (16-byte aligned, ldx % 8 == 0,
  *               ldx >= K)
- *   b_codes, b_scales, y, out_dtype   as for mxfp4_gemm
+ *   b_codes, b_scales, y, out_dtype   as for mxfp4_gemm, with b_scales
+ *               16-byte aligned
  *   bias_bf16   [N] bf16, device, read, 16-byte aligned; or NULL for none
  *   workspace   device memory of at least mxfp4_linear_workspace_size(M, N,
  *               K) bytes (16-byte aligned; may be NULL when that is 0):
@@ -284,6 +386,7 @@ int mxfp8_quantize_act_smooth(const void* x_bf16, int64_t ldx, const int32_t* ro
  *   bias_bf16           [N] bf16, device, read, 16-byte aligned; or NULL
  *   y, out_dtype        as for mxfp4_gemm
  *   flags               must be 0
+ * Kernel choice as for mxfp4_gemm, the tiled kernel needing M * K < 2^31.
  */
 int mxfp4_gemm_w4a8(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
                     const uint8_t* b_scales, int64_t M, int64_t N, int64_t K,
@@ -296,8 +399,9 @@ int mxfp4_gemm_w4a8(const uint8_t* a_codes, const uint8_t* a_scales, const uint8
  * mxfp4_linear_bf16 (M <= 16, K = 2048 or 4096, N >= 16) it is one launch
  * that quantizes the activations inside the GEMM kernel; otherwise the two
  * launches run through the caller's workspace
- * (mxfp4_linear_w4a8_workspace_size(M, N, K) bytes, 16-byte aligned).
- * Arguments as for mxfp4_linear_bf16; flags must be 0.
+ * (mxfp4_linear_w4a8_workspace_size(M, N, K) bytes, 16-byte aligned), the
+ * choice made by shape alone.  Arguments as for mxfp4_linear_bf16 (b_scales
+ * 16-byte aligned); flags must be 0.
  */
 int mxfp4_linear_w4a8_bf16(const void* x_bf16, int64_t ldx, int64_t M, int64_t N, int64_t K,
                            const uint8_t* b_codes, const uint8_t* b_scales,

@@ -280,3 +280,49 @@ def test_smooth_quantize_argument_checks(lib):
         assert f(FAKE, 64, None, FAKE, 4, 64, FAKE, FAKE, 4, None) == -1       # flags
         assert f(FAKE, 64, None, FAKE, 0, 64, FAKE, FAKE, good_flag, None) == 0
     assert lib.mxfp8_quantize_act_smooth(FAKE, 64, None, FAKE, 4, 64, FAKE, FAKE, 2, None) == -1
+
+
+def test_linear_weight_scales_must_be_16_byte_aligned(lib):
+    """Both linear calls pick the one-launch form by shape alone, so they need
+    the alignment that form needs from every caller: b_scales 16-byte aligned
+    (else EALIGN before anything is launched), and the workspace query is
+    exact for every call it accepts."""
+    for f in (lib.mxfp4_linear_bf16, lib.mxfp4_linear_w4a8_bf16):
+        for M in (1, 200):                                # one-launch and two-launch shapes
+            assert f(FAKE, 4096, M, 256, 4096, FAKE, FAKE + 4, None, FAKE, 0, FAKE, 1 << 24, 0,
+                     None) == -2
+            assert f(FAKE, 4096, 0, 256, 4096, FAKE, FAKE + 4, None, FAKE, 0, None, 0, 0,
+                     None) == 0
+
+
+def test_layerwise_argument_checks(lib):
+    import w4a4_mxfp4_gemm_amd as m
+    parts = (m.LoadPart * 2)()
+    for p, (T, N, K) in zip(parts, ((4, 64, 128), (0, 32, 64))):
+        p.T, p.N, p.K = T, N, K
+        p.nv_codes = p.nv_scales = p.nv_global = p.mx_codes = p.mx_scales = FAKE
+    P = ctypes.cast(parts, ctypes.c_void_p)
+    n = ctypes.c_int64(0)
+    plan = lib.mxfp4_layerwise_plan
+    assert plan(P, 2, 1 << 20, None, 0, ctypes.byref(n), None) == 0 and n.value == 1
+    assert plan(P, 2, 1 << 20, None, 0, None, None) == -1                 # no count
+    assert plan(P, -1, 1 << 20, None, 0, ctypes.byref(n), None) == -1
+    assert plan(P, 2, 1024, None, 0, ctypes.byref(n), None) == -1          # slot < one tensor
+    chunks = (m.LoadChunk * 1)()
+    assert plan(P, 2, 1 << 20, ctypes.cast(chunks, ctypes.c_void_p), 0, ctypes.byref(n),
+                None) == -1                                                # max_chunks too small
+    parts[0].K = 48
+    assert plan(P, 2, 1 << 20, None, 0, ctypes.byref(n), None) == -1      # K % 32
+    parts[0].K = 128
+    run = lib.mxfp4_requant_layers_from_host
+    assert run(P, 2, FAKE, 1 << 20, 4, None, None) == -1                   # flags
+    assert run(P, 2, None, 1 << 20, 0, None, None) == -1                   # no scratch
+    assert run(P, 2, FAKE + 16, 1 << 20, 0, None, None) == -2              # scratch alignment
+    assert run(P, 2, FAKE, 1024, 0, None, None) == -1                      # scratch too small
+    parts[0].mx_codes = ODD
+    assert run(P, 2, FAKE, 1 << 20, 0, None, None) == -2                   # destination alignment
+    parts[0].mx_codes = FAKE
+    parts[0].nv_global = None
+    assert run(P, 2, FAKE, 1 << 20, 0, None, None) == -1                   # a null source
+    parts[0].T = 0
+    assert run(P, 2, None, 0, 0, None, None) == 0                          # nothing to load

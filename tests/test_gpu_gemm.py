@@ -288,12 +288,23 @@ def test_grouped_gemm_tiled_bad_offsets_stay_inside_y(mx):
     b, sb = synth.canonical_mxfp4(E * N, K, seed=14)
     A, SA, B, SB = to_dev(a, sa, b.reshape(E, N, K // 2), sb.reshape(E, N, K // 32))
     for table in ([0, 400, 10, -5, 300], [-100, 0, 1000, 20, 300], [0, 0, 0, 0, 0],
-                  [0, 300, 300, 300, 300]):
+                  [0, 300, 300, 300, 300], [0, 300, 0, 300, 0], [0, 200, 100, 250, 300]):
         OFF = torch.tensor(table, dtype=torch.int32, device=dev())
         gy = Guarded((M, N), torch.float32)
         mx.mxfp4_grouped_gemm(A, SA, B, SB, OFF, gy.view)
         torch.cuda.synchronize()
         assert gy.intact(), table
+        # the tiled kernel reads a table as its row ends clamped to [0, M]
+        # and made non-decreasing (a running maximum), so the ranges stay
+        # disjoint: rows of that table's experts equal the oracle's
+        ends = np.maximum.accumulate(np.clip(np.array(table[1:]), 0, M))
+        start = int(np.clip(table[0], 0, M))
+        fixed = np.concatenate([[start], np.maximum(ends, start)]).astype(np.int32)
+        r0, r1 = int(fixed[0]), int(fixed[-1])
+        if r1 > r0:
+            y, s = oracle.grouped_gemm(u8(a)[r0:r1], u8(sa)[r0:r1], u8(b).reshape(E, N, K // 2),
+                                       u8(sb).reshape(E, N, K // 32), fixed - r0)
+            assert_gemm_fp32(gy.view[r0:r1], y, s, f"bad table {table}")
 
 
 @pytest.fixture(scope="module")

@@ -75,6 +75,11 @@ def _load_library() -> ctypes.CDLL:
     lib.mxfp4_linear_workspace_size.restype = SZ
     lib.mxfp4_gemm_workspace_size.argtypes = [I, I, I]
     lib.mxfp4_gemm_workspace_size.restype = SZ
+    lib.mxfp4_layerwise_plan.argtypes = [P, I, SZ, P, I, ctypes.POINTER(ctypes.c_int64),
+                                         ctypes.POINTER(ctypes.c_uint64)]
+    lib.mxfp4_layerwise_plan.restype = ctypes.c_int
+    lib.mxfp4_requant_layers_from_host.argtypes = [P, I, P, SZ, U32, P, P]
+    lib.mxfp4_requant_layers_from_host.restype = ctypes.c_int
     lib.mxfp4_status_string.argtypes = [ctypes.c_int]
     lib.mxfp4_status_string.restype = ctypes.c_char_p
     lib.mxfp4_version.argtypes = []
@@ -92,6 +97,7 @@ EXPORTED_SYMBOLS = ("mxfp4_requant_from_nvfp4", "mxfp4_requant_from_nvfp4_subset
                     "mxfp4_linear_w4a8_bf16", "mxfp4_linear_w4a8_workspace_size",
                     "mxfp4_quantize_act_smooth", "mxfp8_quantize_act_smooth",
                     "mxfp4_grouped_gemm_silu_quantize", "mxfp4_quantize_act_scatter",
+                    "mxfp4_layerwise_plan", "mxfp4_requant_layers_from_host",
                     "mxfp4_status_string", "mxfp4_version")
 
 
@@ -190,6 +196,96 @@ def mxfp4_requant_from_nvfp4(nv_codes, nv_scales, nv_global, mx_codes=None, mx_s
         _ptr(nv_codes), _ptr(nv_scales), _ptr(nv_global), T, N, K,
         _ptr(mx_codes), _ptr(mx_scales), flags, _stream(stream, dev)))
     return mx_codes, mx_scales
+
+
+class LoadPart(ctypes.Structure):
+    """mxfp4_load_part of include/mxfp4.h."""
+    _fields_ = [("nv_codes", ctypes.c_void_p), ("nv_scales", ctypes.c_void_p),
+                ("nv_global", ctypes.c_void_p), ("excluded", ctypes.c_void_p),
+                ("mx_codes", ctypes.c_void_p), ("mx_scales", ctypes.c_void_p),
+                ("T", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64)]
+
+
+class LoadChunk(ctypes.Structure):
+    """mxfp4_load_chunk of include/mxfp4.h."""
+    _fields_ = [("part", ctypes.c_int64), ("t0", ctypes.c_int64), ("t1", ctypes.c_int64),
+                ("slot", ctypes.c_int64), ("codes_offset", ctypes.c_uint64),
+                ("scales_offset", ctypes.c_uint64), ("global_offset", ctypes.c_uint64)]
+
+
+def _excluded_u8(excluded, T):
+    if excluded is None:
+        return None
+    e = torch.as_tensor(excluded).to("cpu").reshape(-1).to(torch.uint8).contiguous()
+    if e.numel() != T:
+        raise ValueError(f"excluded has {e.numel()} entries, expected {T}")
+    return e
+
+
+def mxfp4_layerwise_plan(shapes, excluded, scratch_bytes):
+    """The layerwise load's plan (host code only, no GPU needed): shapes is a
+    list of (T, N, K) per part, excluded a matching list of [T] masks (or
+    None entries).  Returns (chunks, slot_bytes) with each chunk a dict of
+    part, t0, t1, slot, codes_offset, scales_offset, global_offset."""
+    keep = [_excluded_u8(e, int(T)) for (T, _, _), e in zip(shapes, excluded)]
+    parts = (LoadPart * max(len(shapes), 1))()
+    for i, ((T, N, K), e) in enumerate(zip(shapes, keep)):
+        parts[i].T, parts[i].N, parts[i].K = int(T), int(N), int(K)
+        parts[i].excluded = None if e is None else e.data_ptr()
+    n = ctypes.c_int64(0)
+    slot = ctypes.c_uint64(0)
+    _check("mxfp4_layerwise_plan", _lib.mxfp4_layerwise_plan(
+        ctypes.cast(parts, ctypes.c_void_p), len(shapes), int(scratch_bytes), None, 0,
+        ctypes.byref(n), ctypes.byref(slot)))
+    chunks = (LoadChunk * max(n.value, 1))()
+    _check("mxfp4_layerwise_plan", _lib.mxfp4_layerwise_plan(
+        ctypes.cast(parts, ctypes.c_void_p), len(shapes), int(scratch_bytes),
+        ctypes.cast(chunks, ctypes.c_void_p), n.value, ctypes.byref(n), ctypes.byref(slot)))
+    out = [{f: int(getattr(chunks[i], f)) for f, _ in LoadChunk._fields_} for i in range(n.value)]
+    return out, int(slot.value)
+
+
+def mxfp4_requant_layers_from_host(parts, scratch, *, copy_stream=None, bf16_intermediate=False,
+                                   scale_rule="ocp", stream=None):
+    """The layerwise load: each part is a dict with nv_codes [T,N,K/2] u8,
+    nv_scales [T,N,K/16] u8, nv_global [T] fp32 (CPU tensors, pinned for the
+    copies to overlap), optional excluded [T] mask, and mx_codes [T,N,K/2],
+    mx_scales [T,N,K/32] u8 GPU tensors written in place.  scratch: a u8 GPU
+    tensor (256-byte aligned; one layer's NVFP4 bytes is enough).  The copies
+    run on copy_stream (default: the compute stream), the requant on stream
+    (default: the current stream).  The host tensors must stay alive until
+    that stream has finished."""
+    _need(scratch, "scratch", torch.uint8)
+    dev = scratch.device
+    keep = []
+    arr = (LoadPart * max(len(parts), 1))()
+    for i, p in enumerate(parts):
+        c, sc, g = p["nv_codes"], p["nv_scales"], p["nv_global"]
+        mc, ms = p["mx_codes"], p["mx_scales"]
+        for t, name, dt in ((c, "nv_codes", torch.uint8), (sc, "nv_scales", torch.uint8),
+                            (g, "nv_global", torch.float32)):
+            if t.device.type != "cpu" or t.dtype != dt or not t.is_contiguous():
+                raise ValueError(f"part {i}: {name} must be a contiguous CPU {dt} tensor")
+        _need(mc, "mx_codes", torch.uint8, dev)
+        _need(ms, "mx_scales", torch.uint8, dev)
+        T, N, K = (int(torch.tensor(c.shape[:-2]).prod().item()) if c.dim() > 2 else 1,
+                   c.shape[-2], c.shape[-1] * 2)
+        if (sc.numel() != T * N * (K // 16) or g.numel() != T or mc.numel() != T * N * (K // 2)
+                or ms.numel() != T * N * (K // 32)):
+            raise ValueError(f"part {i}: shapes do not match codes [{T},{N},{K // 2}]")
+        e = _excluded_u8(p.get("excluded"), T)
+        keep.append(e)
+        arr[i].nv_codes, arr[i].nv_scales, arr[i].nv_global = (c.data_ptr(), sc.data_ptr(),
+                                                                g.data_ptr())
+        arr[i].excluded = None if e is None else e.data_ptr()
+        arr[i].mx_codes, arr[i].mx_scales = mc.data_ptr(), ms.data_ptr()
+        arr[i].T, arr[i].N, arr[i].K = T, N, K
+    flags = (MXFP4_REQ_INTERMEDIATE_BF16 if bf16_intermediate else 0) | _rule_flag(scale_rule)
+    s = _stream(stream, dev)
+    cs = s if copy_stream is None else _stream(copy_stream, dev)
+    _check("mxfp4_requant_layers_from_host", _lib.mxfp4_requant_layers_from_host(
+        ctypes.cast(arr, ctypes.c_void_p), len(parts), _ptr(scratch), scratch.numel(), flags,
+        cs, s))
 
 
 def mxfp4_quantize_act(x, codes=None, scales=None, *, row_index=None, K=None,

@@ -472,12 +472,6 @@ bool linear_skinny_shape(int64_t M, int64_t N, int64_t K) {
     return M >= 1 && M <= LINEAR_FUSED_MAX && (K == 2048 || K == 4096) && N >= 16;
 }
 
-bool linear_skinny_supported(int64_t M, int64_t N, int64_t K, const void* x, int64_t ldx,
-                             const void* w_scales) {
-    return linear_skinny_shape(M, N, K) && (reinterpret_cast<uintptr_t>(x) % 16) == 0 &&
-           ldx % 8 == 0 && (reinterpret_cast<uintptr_t>(w_scales) % 16) == 0;
-}
-
 template <int MT, int SPW, int NW, bool A8 = false>
 static hipError_t launch_mt(const uint8_t* a, const uint8_t* as, int64_t ldx, const uint8_t* b,
                             const uint8_t* bs, int64_t M, int64_t N, int64_t K, void* y,

@@ -982,21 +982,36 @@ struct GroupTable {
     int* row1;
 };
 
+__device__ __forceinline__ int wave_inclusive_max(int v) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int d = 1; d < 64; d *= 2) {
+        const int u = __shfl_up(v, d, 64);
+        if (lane >= d) v = max(v, u);
+    }
+    return v;
+}
+
+// The offset table is read as row ends clamped to [0, total_M] and made
+// non-decreasing by a running maximum: expert e gets rows [end(e-1), end(e))
+// with end(-1) = clamp(offsets[0]).  A well-formed table is unchanged; a
+// malformed one still gives disjoint ranges inside [0, total_M), so the item
+// count stays below (ceil(total_M / BM) + E) * tiles_n, the bound the host
+// checks, and no sum can wrap.
 template <int BM>
 __device__ void build_table(const int32_t* __restrict__ offsets, int E, int total_M, int tiles_n,
                             GroupTable tb) {
     const int lane = threadIdx.x & 63;
     int base = 0;
+    int prev_end = min(max((int)offsets[0], 0), total_M);
     for (int e0 = 0; e0 < E; e0 += 64) {
         const int e = e0 + lane;
-        int a0 = 0, a1 = 0;
-        if (e < E) {
-            a0 = offsets[e];
-            a1 = offsets[e + 1];
-            a0 = a0 < 0 ? 0 : (a0 > total_M ? total_M : a0);
-            a1 = a1 < a0 ? a0 : (a1 > total_M ? total_M : a1);
-        }
-        const int cnt = (a1 - a0 + BM - 1) / BM * tiles_n;
+        const int v = e < E ? min(max((int)offsets[e + 1], 0), total_M) : 0;
+        const int a1 = max(wave_inclusive_max(v), prev_end);
+        int a0 = __shfl_up(a1, 1, 64);
+        if (lane == 0) a0 = prev_end;
+        prev_end = __shfl(a1, 63, 64);
+        const int cnt = e < E ? (a1 - a0 + BM - 1) / BM * tiles_n : 0;
         const int incl = wave_inclusive_scan(cnt);
         if (e < E) {
             tb.first[e] = base + incl - cnt;
@@ -1009,6 +1024,8 @@ __device__ void build_table(const int32_t* __restrict__ offsets, int E, int tota
 }
 
 // Item t (< total), searching experts from `from` on (items only grow).
+// it.e < 0 if no expert holds item t (the table guarantees one does; the
+// caller then ends its walk rather than index the table with it).
 template <int BM>
 __device__ __forceinline__ GroupItem decode_item(GroupTable tb, int E, int tiles_n, int t,
                                                  int from) {
@@ -1025,6 +1042,11 @@ __device__ __forceinline__ GroupItem decode_item(GroupTable tb, int E, int tiles
     }
     GroupItem it;
     it.e = __builtin_amdgcn_readfirstlane(e);
+    if (it.e < 0) {
+        it.tn = it.m0 = it.m_end = 0;
+        it.jl = 1;
+        return it;
+    }
     const int a0 = __builtin_amdgcn_readfirstlane(tb.row0[it.e]);
     const int a1 = __builtin_amdgcn_readfirstlane(tb.row1[it.e]);
     const int r = t - __builtin_amdgcn_readfirstlane(tb.first[it.e]);
@@ -1102,6 +1124,7 @@ __global__ __launch_bounds__(256, 1) void grouped_tiled_kernel(
     const LoadOffsets<S> lo = load_offsets<S>(K / 2, S::A8 ? K : K / 2, K / 32);
 
     GroupItem it = decode_item<S::BM>(tb, E, tiles_n, t, 0);
+    if (it.e < 0) return;
     TileSrc<S> cur = item_src<S>(it, x, xs, w, ws, N, K);
     v16f acc[S::NB][S::MB];
     zero_acc<S>(acc);
@@ -1110,8 +1133,13 @@ __global__ __launch_bounds__(256, 1) void grouped_tiled_kernel(
     prologue<S>(lds, cur, lo, nkt, cbase, pp, ro);
     for (;;) {
         const int tn = t + stride;
-        const bool have_next = tn < t_end;
-        const GroupItem nx = have_next ? decode_item<S::BM>(tb, E, tiles_n, tn, it.e) : it;
+        GroupItem nx = it;
+        bool have_next = tn < t_end;
+        if (have_next) {
+            nx = decode_item<S::BM>(tb, E, tiles_n, tn, it.e);
+            have_next = nx.e >= 0;
+            if (!have_next) nx = it;
+        }
         const TileSrc<S> nxt = item_src<S>(nx, x, xs, w, ws, N, K);
         const bool prefetch = have_next && nkt >= 4;
         if (prefetch)

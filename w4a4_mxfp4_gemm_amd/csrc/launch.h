@@ -42,11 +42,9 @@ hipError_t launch_moe_combine(const uint16_t* y, int64_t ldy, int64_t R, const i
                               void* out, bool out_bf16, hipStream_t stream);
 
 // Act-quant and weight-streaming GEMM in one launch: x bf16 [M][ldx], for
-// the shapes and alignments linear_skinny_supported accepts
-// (linear_skinny_shape: the shape alone).
+// the shapes linear_skinny_shape accepts, with x, ldx and the weight scales
+// 16-byte aligned (the linear calls require that of every caller).
 bool linear_skinny_shape(int64_t M, int64_t N, int64_t K);
-bool linear_skinny_supported(int64_t M, int64_t N, int64_t K, const void* x, int64_t ldx,
-                             const void* w_scales);
 hipError_t launch_linear_skinny(const uint16_t* x, int64_t ldx, const uint8_t* b_codes,
                                 const uint8_t* b_scales, int64_t M, int64_t N, int64_t K,
                                 void* y, const uint16_t* bias, bool out_bf16, bool uos,
@@ -126,5 +124,16 @@ hipError_t launch_gemm_skinny(const uint8_t* a_codes, const uint8_t* a_scales,
                               const uint8_t* b_codes, const uint8_t* b_scales, int64_t M,
                               int64_t N, int64_t K, void* y, const uint16_t* bias,
                               bool out_bf16, hipStream_t stream);
+
+// Validation and dispatch of the bf16 linear call, shared by its entry
+// points (mxfp4_abi.cpp): status codes of include/mxfp4.h.
+size_t linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
+int check_linear_bf16(const void* x_bf16, int64_t ldx, int64_t M, int64_t N, int64_t K,
+                      const uint8_t* b_codes, const uint8_t* b_scales, const void* bias_bf16,
+                      void* y, int out_dtype, uint32_t flags);
+int run_linear_bf16(const void* x_bf16, int64_t ldx, int64_t M, int64_t N, int64_t K,
+                    const uint8_t* b_codes, const uint8_t* b_scales, const void* bias_bf16,
+                    void* y, int out_dtype, uint8_t* workspace, uint32_t flags,
+                    hipStream_t stream);
 
 }  // namespace mx

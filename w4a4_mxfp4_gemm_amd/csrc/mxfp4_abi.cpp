@@ -43,6 +43,55 @@ int check_gemm_common(const uint8_t* a_codes, const uint8_t* a_scales, const uin
 
 }  // namespace
 
+namespace mx {
+
+// The one-launch form (act-quant inside the skinny GEMM) is chosen by shape
+// alone: the call requires every pointer alignment that form needs.
+size_t linear_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    if (M <= 0 || N <= 0 || check_k(K) != MXFP4_OK) return 0;
+    if (linear_skinny_shape(M, N, K)) return 0;
+    return linear_codes_bytes(M, K) + (size_t)M * (size_t)(K / 32);
+}
+
+int check_linear_bf16(const void* x_bf16, int64_t ldx, int64_t M, int64_t N, int64_t K,
+                      const uint8_t* b_codes, const uint8_t* b_scales, const void* bias_bf16,
+                      void* y, int out_dtype, uint32_t flags) {
+    if (M < 0 || N <= 0 || check_k(K) != MXFP4_OK || ldx < K) return MXFP4_EINVAL;
+    if (out_dtype != MXFP4_OUT_BF16 && out_dtype != MXFP4_OUT_FP32) return MXFP4_EINVAL;
+    if ((flags & ~(uint32_t)MXFP4_SCALE_UOS) != 0) return MXFP4_EINVAL;
+    if (M == 0) return MXFP4_OK;
+    if (!x_bf16 || !b_codes || !b_scales || !y) return MXFP4_EINVAL;
+    if (!aligned(x_bf16, 16) || ldx % 8 != 0 || !aligned(b_codes, 16) || !aligned(b_scales, 16))
+        return MXFP4_EALIGN;
+    if (!aligned(y, out_dtype == MXFP4_OUT_FP32 ? 4 : 2)) return MXFP4_EALIGN;
+    if (bias_bf16 && !aligned(bias_bf16, 16)) return MXFP4_EALIGN;
+    return MXFP4_OK;
+}
+
+// Arguments checked by check_linear_bf16 (M > 0); workspace holds at least
+// linear_workspace_bytes(M, N, K) bytes, 16-byte aligned.
+int run_linear_bf16(const void* x_bf16, int64_t ldx, int64_t M, int64_t N, int64_t K,
+                    const uint8_t* b_codes, const uint8_t* b_scales, const void* bias_bf16,
+                    void* y, int out_dtype, uint8_t* workspace, uint32_t flags,
+                    hipStream_t stream) {
+    const bool out_bf16 = out_dtype == MXFP4_OUT_BF16;
+    const bool uos = (flags & MXFP4_SCALE_UOS) != 0;
+    const uint16_t* x = static_cast<const uint16_t*>(x_bf16);
+    const uint16_t* bias = static_cast<const uint16_t*>(bias_bf16);
+    if (linear_skinny_shape(M, N, K))
+        return from_hip(launch_linear_skinny(x, ldx, b_codes, b_scales, M, N, K, y, bias,
+                                             out_bf16, uos, stream));
+    // two launches through the workspace: the act-quant call, then the GEMM
+    uint8_t* codes = workspace;
+    uint8_t* scales = codes + linear_codes_bytes(M, K);
+    const hipError_t e = launch_act_quant(x, ldx, nullptr, M, K, codes, scales, uos, stream);
+    if (e != hipSuccess) return MXFP4_EHIP;
+    return from_hip(launch_gemm(codes, scales, b_codes, b_scales, M, N, K, y, bias, out_bf16,
+                                stream));
+}
+
+}  // namespace mx
+
 extern "C" {
 
 int mxfp4_requant_from_nvfp4(const uint8_t* nv_codes, const uint8_t* nv_scales,
@@ -142,42 +191,21 @@ int mxfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b
 }
 
 size_t mxfp4_linear_workspace_size(int64_t M, int64_t N, int64_t K) {
-    if (M <= 0 || N <= 0 || check_k(K) != MXFP4_OK) return 0;
-    if (mx::linear_skinny_shape(M, N, K)) return 0;
-    return linear_codes_bytes(M, K) + (size_t)M * (size_t)(K / 32);
+    return mx::linear_workspace_bytes(M, N, K);
 }
 
 int mxfp4_linear_bf16(const void* x_bf16, int64_t ldx, int64_t M, int64_t N, int64_t K,
                       const uint8_t* b_codes, const uint8_t* b_scales, const void* bias_bf16,
                       void* y, int out_dtype, void* workspace, size_t workspace_bytes,
                       uint32_t flags, hipStream_t stream) {
-    if (M < 0 || N <= 0 || check_k(K) != MXFP4_OK || ldx < K) return MXFP4_EINVAL;
-    if (out_dtype != MXFP4_OUT_BF16 && out_dtype != MXFP4_OUT_FP32) return MXFP4_EINVAL;
-    if ((flags & ~(uint32_t)MXFP4_SCALE_UOS) != 0) return MXFP4_EINVAL;
     if (workspace_bytes != 0 && workspace == nullptr) return MXFP4_EINVAL;
-    if (M == 0) return MXFP4_OK;
-    if (!x_bf16 || !b_codes || !b_scales || !y) return MXFP4_EINVAL;
-    if (!aligned(x_bf16, 16) || ldx % 8 != 0 || !aligned(b_codes, 16)) return MXFP4_EALIGN;
-    if (!aligned(y, out_dtype == MXFP4_OUT_FP32 ? 4 : 2)) return MXFP4_EALIGN;
-    if (bias_bf16 && !aligned(bias_bf16, 16)) return MXFP4_EALIGN;
-    const bool out_bf16 = out_dtype == MXFP4_OUT_BF16;
-    const bool uos = (flags & MXFP4_SCALE_UOS) != 0;
-    const uint16_t* bias = static_cast<const uint16_t*>(bias_bf16);
-    if (mx::linear_skinny_supported(M, N, K, x_bf16, ldx, b_scales))
-        return from_hip(mx::launch_linear_skinny(static_cast<const uint16_t*>(x_bf16), ldx,
-                                                 b_codes, b_scales, M, N, K, y, bias, out_bf16,
-                                                 uos, stream));
-    // two launches through the workspace: the act-quant call, then the GEMM
-    const size_t need = linear_codes_bytes(M, K) + (size_t)M * (size_t)(K / 32);
-    if (workspace_bytes < need) return MXFP4_EINVAL;
-    if (!aligned(workspace, 16)) return MXFP4_EALIGN;
-    uint8_t* codes = static_cast<uint8_t*>(workspace);
-    uint8_t* scales = codes + linear_codes_bytes(M, K);
-    const hipError_t e = mx::launch_act_quant(static_cast<const uint16_t*>(x_bf16), ldx, nullptr,
-                                              M, K, codes, scales, uos, stream);
-    if (e != hipSuccess) return MXFP4_EHIP;
-    return from_hip(mx::launch_gemm(codes, scales, b_codes, b_scales, M, N, K, y, bias, out_bf16,
-                                    stream));
+    const int st = mx::check_linear_bf16(x_bf16, ldx, M, N, K, b_codes, b_scales, bias_bf16, y,
+                                         out_dtype, flags);
+    if (st != MXFP4_OK || M == 0) return st;
+    if (workspace_bytes < mx::linear_workspace_bytes(M, N, K)) return MXFP4_EINVAL;
+    if (workspace && !aligned(workspace, 16)) return MXFP4_EALIGN;
+    return mx::run_linear_bf16(x_bf16, ldx, M, N, K, b_codes, b_scales, bias_bf16, y, out_dtype,
+                               static_cast<uint8_t*>(workspace), flags, stream);
 }
 
 int mxfp8_quantize_act(const void* x_bf16, int64_t ldx, const int32_t* row_index, int64_t M,
@@ -237,11 +265,12 @@ int mxfp4_linear_w4a8_bf16(const void* x_bf16, int64_t ldx, int64_t M, int64_t N
     if (workspace_bytes != 0 && workspace == nullptr) return MXFP4_EINVAL;
     if (M == 0) return MXFP4_OK;
     if (!x_bf16 || !b_codes || !b_scales || !y) return MXFP4_EINVAL;
-    if (!aligned(x_bf16, 16) || ldx % 8 != 0 || !aligned(b_codes, 16)) return MXFP4_EALIGN;
+    if (!aligned(x_bf16, 16) || ldx % 8 != 0 || !aligned(b_codes, 16) || !aligned(b_scales, 16))
+        return MXFP4_EALIGN;
     if (!aligned(y, out_dtype == MXFP4_OUT_FP32 ? 4 : 2)) return MXFP4_EALIGN;
     if (bias_bf16 && !aligned(bias_bf16, 16)) return MXFP4_EALIGN;
     const uint16_t* bias = static_cast<const uint16_t*>(bias_bf16);
-    if (mx::linear_skinny_supported(M, N, K, x_bf16, ldx, b_scales))
+    if (mx::linear_skinny_shape(M, N, K))
         return from_hip(mx::launch_linear_skinny_w4a8(static_cast<const uint16_t*>(x_bf16), ldx,
                                                       b_codes, b_scales, M, N, K, y, bias,
                                                       out_dtype == MXFP4_OUT_BF16, stream));
