@@ -22,7 +22,8 @@
  *     the caller, except the host buffers of the layerwise load and the
  *     subset requant's tensor list (marked HOST).  No call allocates or frees
  *     device memory or synchronises the host; all work is enqueued on
- *     `stream`.  The library holds no device memory of its own.
+ *     `stream`.  The only device memory the library holds is the static
+ *     scratch of mxfp4_linear_bf16_noalloc.
  *   - Every call returns MXFP4_OK or a negative mxfp4_status.  Arguments are
  *     checked before anything is enqueued; on an error nothing is launched.
  *   - K must be a positive multiple of 32 (whole MX blocks).  A zero row
@@ -55,7 +56,9 @@ typedef enum {
     MXFP4_EINVAL = -1,       /* bad size, null pointer, unknown flag/dtype    */
     MXFP4_EALIGN = -2,       /* a pointer or leading dimension misaligned     */
     MXFP4_EUNSUPPORTED = -3, /* valid request this build does not implement   */
-    MXFP4_EHIP = -4          /* the HIP runtime refused a launch              */
+    MXFP4_EHIP = -4,         /* the HIP runtime refused a launch              */
+    MXFP4_ESCRATCH = -5      /* needs more than mxfp4_linear_bf16_noalloc's
+                                static scratch (MXFP4_NOALLOC_SCRATCH_BYTES)  */
 } mxfp4_status;
 
 enum { MXFP4_OUT_BF16 = 0, MXFP4_OUT_FP32 = 1 };        /* out_dtype            */
@@ -346,6 +349,34 @@ int mxfp4_linear_bf16(const void* x_bf16, int64_t ldx, int64_t M, int64_t N, int
 
 /* Workspace bytes mxfp4_linear_bf16 needs: 0 for the one-launch shapes. */
 size_t mxfp4_linear_workspace_size(int64_t M, int64_t N, int64_t K);
+
+/* Bytes of the device scratch mxfp4_linear_bf16_noalloc holds on each GPU. */
+#define MXFP4_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/*
+ * mxfp4_linear_bf16 for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  It takes no workspace: where mxfp4_linear_bf16 would quantize
+ * the activations into the caller's workspace (shapes with
+ * mxfp4_linear_workspace_size(M, N, K) > 0), it uses a device array of
+ * MXFP4_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held from the
+ * library's load until the process ends.  The call itself allocates and
+ * frees nothing; the array's address on a device is looked up on the first
+ * call made with that device current.
+ *
+ * Arguments, results and errors as for mxfp4_linear_bf16, plus
+ * MXFP4_ESCRATCH when mxfp4_linear_workspace_size(M, N, K) exceeds
+ * MXFP4_NOALLOC_SCRATCH_BYTES (M * K * 17/32 bytes, rounded up; 32 MiB holds
+ * e.g. M = 4096 rows at K = 14336).  The device current at the call must be
+ * the one that owns `stream` and the buffers.  Every call on one GPU shares
+ * that GPU's array, so calls that may overlap on one GPU (other streams,
+ * other threads) race on it: the caller orders them.  The array keeps the
+ * last call's quantized activations; nothing in it needs clearing.
+ */
+int mxfp4_linear_bf16_noalloc(const void* x_bf16, int64_t ldx, int64_t M, int64_t N, int64_t K,
+                              const uint8_t* b_codes, const uint8_t* b_scales,
+                              const void* bias_bf16, void* y, int out_dtype, uint32_t flags,
+                              hipStream_t stream);
 
 /*
  * W4A8: MXFP8 activations with the same MXFP4 weights (vLLM-Omni guide,

@@ -293,6 +293,31 @@ def test_linear_weight_scales_must_be_16_byte_aligned(lib):
                      None) == -2
             assert f(FAKE, 4096, 0, 256, 4096, FAKE, FAKE + 4, None, FAKE, 0, None, 0, 0,
                      None) == 0
+    g = lib.mxfp4_linear_bf16_noalloc
+    assert g(FAKE, 4096, 1, 256, 4096, FAKE, FAKE + 4, None, FAKE, 0, 0, None) == -2
+
+
+def test_noalloc_linear_argument_checks(lib):
+    f = lib.mxfp4_linear_bf16_noalloc
+    #        x     ldx   M  N    K     b_codes b_scales bias y  dtype flags stream
+    assert f(FAKE, 4000, 1, 256, 4096, FAKE, FAKE, None, FAKE, 0, 0, None) == -1    # ldx < K
+    assert f(FAKE, 4096, 1, 256, 4080, FAKE, FAKE, None, FAKE, 0, 0, None) == -1    # K % 32
+    assert f(FAKE, 4096, 1, 256, 4096, FAKE, FAKE, None, FAKE, 7, 0, None) == -1    # out_dtype
+    assert f(FAKE, 4096, 1, 256, 4096, FAKE, FAKE, None, FAKE, 0, 1, None) == -1    # flags
+    assert f(None, 4096, 1, 256, 4096, FAKE, FAKE, None, FAKE, 0, 0, None) == -1
+    assert f(ODD, 4096, 1, 256, 4096, FAKE, FAKE, None, FAKE, 0, 0, None) == -2
+    assert f(FAKE, 4096, 1, 256, 4096, FAKE, FAKE, ODD, FAKE, 0, 0, None) == -2     # bias
+    assert f(FAKE, 4096, 0, 256, 4096, FAKE, FAKE, None, FAKE, 0, 2, None) == 0     # M == 0
+    # one row past what the static scratch holds at K = 14336: MXFP4_ESCRATCH,
+    # decided before any HIP call
+    K = 14336
+    M = (32 << 20) // (K // 2 + K // 32) + 1
+    assert lib.mxfp4_linear_workspace_size(M, 256, K) > (32 << 20)
+    assert lib.mxfp4_linear_workspace_size(M - 1, 256, K) <= (32 << 20)
+    assert f(FAKE, K, M, 256, K, FAKE, FAKE, None, FAKE, 0, 0, None) == -5
+    import w4a4_mxfp4_gemm_amd as m
+    assert "scratch" in m.mxfp4_status_string(-5)
+    assert m.MXFP4_NOALLOC_SCRATCH_BYTES == 32 << 20
 
 
 def test_layerwise_argument_checks(lib):

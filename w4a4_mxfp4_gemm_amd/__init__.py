@@ -22,7 +22,9 @@ MXFP4_REQ_INTERMEDIATE_BF16 = 1
 MXFP4_SCALE_UOS = 2
 
 _STATUS_NAMES = {0: "MXFP4_OK", -1: "MXFP4_EINVAL", -2: "MXFP4_EALIGN",
-                 -3: "MXFP4_EUNSUPPORTED", -4: "MXFP4_EHIP"}
+                 -3: "MXFP4_EUNSUPPORTED", -4: "MXFP4_EHIP", -5: "MXFP4_ESCRATCH"}
+
+MXFP4_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class Mxfp4Error(RuntimeError):
@@ -80,6 +82,8 @@ def _load_library() -> ctypes.CDLL:
     lib.mxfp4_layerwise_plan.restype = ctypes.c_int
     lib.mxfp4_requant_layers_from_host.argtypes = [P, I, P, SZ, U32, P, P]
     lib.mxfp4_requant_layers_from_host.restype = ctypes.c_int
+    lib.mxfp4_linear_bf16_noalloc.argtypes = [P, I, I, I, I, P, P, P, P, ctypes.c_int, U32, P]
+    lib.mxfp4_linear_bf16_noalloc.restype = ctypes.c_int
     lib.mxfp4_status_string.argtypes = [ctypes.c_int]
     lib.mxfp4_status_string.restype = ctypes.c_char_p
     lib.mxfp4_version.argtypes = []
@@ -98,6 +102,7 @@ EXPORTED_SYMBOLS = ("mxfp4_requant_from_nvfp4", "mxfp4_requant_from_nvfp4_subset
                     "mxfp4_quantize_act_smooth", "mxfp8_quantize_act_smooth",
                     "mxfp4_grouped_gemm_silu_quantize", "mxfp4_quantize_act_scatter",
                     "mxfp4_layerwise_plan", "mxfp4_requant_layers_from_host",
+                    "mxfp4_linear_bf16_noalloc",
                     "mxfp4_status_string", "mxfp4_version")
 
 
@@ -390,6 +395,35 @@ def mxfp4_linear_bf16(x, b_codes, b_scales, y=None, *, bias=None, K=None,
         _ptr(x), ldx, M, N, K, _ptr(b_codes), _ptr(b_scales), _ptr(bias), _ptr(y),
         _out_dtype(y.dtype),
         ws_ptr, ws_bytes, _rule_flag(scale_rule), _stream(stream, dev)))
+    return y
+
+
+def mxfp4_linear_bf16_noalloc(x, b_codes, b_scales, y, *, bias=None, K=None, scale_rule="ocp",
+                              stream=None):
+    """mxfp4_linear_bf16 without a workspace: the library's static per-GPU
+    scratch (MXFP4_NOALLOC_SCRATCH_BYTES) holds the quantized activations.
+    y [M, N] (bf16 or fp32) is the caller's; nothing is allocated."""
+    _need(x, "x", torch.bfloat16)
+    dev = x.device
+    _need(b_codes, "b_codes", torch.uint8, dev)
+    _need(b_scales, "b_scales", torch.uint8, dev)
+    if x.dim() != 2:
+        raise ValueError("x must be [M, ldx]")
+    M, ldx = x.shape
+    K = ldx if K is None else K
+    N = b_codes.shape[0]
+    if b_codes.shape != (N, K // 2) or b_scales.shape != (N, K // 32):
+        raise ValueError("operand shapes disagree")
+    if bias is not None:
+        _need(bias, "bias", torch.bfloat16, dev)
+        if bias.shape != (N,):
+            raise ValueError("bias must be [N]")
+    _need(y, "y", y.dtype, dev)
+    if y.shape != (M, N):
+        raise ValueError("y must be [M, N]")
+    _check("mxfp4_linear_bf16_noalloc", _lib.mxfp4_linear_bf16_noalloc(
+        _ptr(x), ldx, M, N, K, _ptr(b_codes), _ptr(b_scales), _ptr(bias), _ptr(y),
+        _out_dtype(y.dtype), _rule_flag(scale_rule), _stream(stream, dev)))
     return y
 
 

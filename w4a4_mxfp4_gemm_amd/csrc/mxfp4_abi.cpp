@@ -365,6 +365,8 @@ const char* mxfp4_status_string(int status) {
         case MXFP4_EALIGN: return "misaligned pointer or leading dimension";
         case MXFP4_EUNSUPPORTED: return "unsupported request";
         case MXFP4_EHIP: return "HIP runtime error at launch";
+        case MXFP4_ESCRATCH:
+            return "request needs more than the static scratch of the no-allocation call";
         default: return "unknown status";
     }
 }
