@@ -1,32 +1,43 @@
 #!/usr/bin/env python3
 """Benchmark of the MXFP4 W4A4 linear-layer path on one MI355X.
 
-Default workload (the decode-shaped dense linear): an NVFP4 weight
-[N=12288, K=4096] from bf16 N(0, 0.02) is requantized to MXFP4, then for each
-M in {1, 8, 32, 64} bf16 activations [M, 4096] ~ N(0, 1) with 1% outlier
-channels (x50) are quantized to MXFP4 and multiplied with the weight (bf16
-out).  One step = requant + the four (act-quant, GEMM) pairs.  Weight sources
-and destinations rotate over copies totalling > 768 MiB so that the bytes
-come from HBM, not the 256 MiB Infinity Cache.
+Headline workload (the largest single-GPU configuration): the prefill-shaped
+dense linears, M = 4096 tokens of bf16 activations ~ N(0, 1) with 1% outlier
+channels (x50), times MXFP4 weights requantized from NVFP4 (bf16 N(0, 0.02)),
+for (N, K) in (4096, 4096), (28672, 4096), (4096, 14336).  One step = the
+three act-quant + GEMM pairs (bf16 out); ``value`` = their 2MNK flops over the
+step's time, i.e. GEMM TFLOP/s including the activation quantization.
 
-Other workloads (``--workload prefill|moe|layerwise``) print their own JSON
-line; they are measurements of the remaining configurations.
+The default run (``--workload all``) measures every other configuration in the
+same process and adds it to the same JSON line:
+* ``decode``: requant of W [12288, 4096] + act-quant + GEMM for M in
+  {1, 8, 32, 64} (weight-streaming, HBM-bound);
+* ``moe``: 128 experts, 2048 tokens top-8: dispatch act-quant, gate_up GEMM
+  with the expert activation in its epilogue, down GEMM, top-k combine;
+* ``layerwise``: 48 MoE layers x 128 experts x ([2048, 4096] + [4096, 1024])
+  NVFP4 -> MXFP4, 5% excluded: kernel-only requant rate, and the end-to-end
+  load from pinned host memory through the layerwise driver;
+* ``w4a8``: MXFP8 activations with the same weights (decode and a 4096^3 GEMM);
+* ``measured_peaks``: this GPU's own MFMA-loop and copy ceilings, with the
+  clock the MFMAs ran at; every fraction is also given against them.
 
-Prints ONE JSON line.  ``value`` = GEMM TFLOP/s including activation
-quantization (sum of 2MNK over the time of the act-quant + GEMM launches);
-requant GB/s and roofline fractions are extra fields.  Each phase of a step
-(the whole step, the act-quant + GEMM pairs, the GEMMs alone, ...) is captured
-into HIP graphs, one per rotated weight copy, and timed by replaying them back
-to back between two HIP events recorded on the stream the kernels run on.
+Each phase is captured into HIP graphs and timed by replaying them back to
+back between two HIP events recorded on the stream the kernels run on (the
+current torch stream, which the binding launches on).  Inputs are resident in
+HBM before the timed region; the rotating copies exceed the 256 MiB Infinity
+Cache, so the bytes come from HBM.  ``cpu_baseline`` times the CPU oracle, as
+it stands, on a row sample of the headline workload on this host's cores.
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import math
 import os
 import pathlib
+import platform
 import sys
 import time
 
@@ -36,25 +47,31 @@ sys.path.insert(0, str(ROOT))
 METRIC = "MXFP4 W4A4 GEMM TFLOP/s (incl. act quant) + requant GB/s, % of roofline"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 MXFP4_PEAK_TFLOPS = 10100.0     # MI355X dense MXFP4 MFMA
+FP8_PEAK_TFLOPS = 5000.0        # MI355X dense FP8 MFMA (W4A8's E4M3 x E2M1 runs at this rate)
 ROTATE_BYTES = 1 << 30          # > 3x the 256 MiB MALL
 CALIBRATION_BYTES = 512 << 20   # copy kernel of known size for the HBM counters
 PREFILL_SLOTS = 16              # activation copies: 16 x 176 MiB over the three shapes
 MOE_SLOTS = 8                   # token / down-input copies for the MoE workload
+MX4 = 0.5 + 1 / 32              # MXFP4 bytes per element (codes + E8M0)
 
 
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", default="decode",
-                   choices=["decode", "prefill", "moe", "layerwise", "w4a8"])
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="all",
+                   choices=["all", "prefill", "decode", "moe", "layerwise", "w4a8"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--eager", type=int, default=0, metavar="N",
-                   help="counter-collection pass: no graphs and no timing; run a "
-                        "%d MiB copy (the calibration kernel), then every phase "
-                        "N times eagerly" % (CALIBRATION_BYTES >> 20))
+                   help="counter-collection pass for one workload: no graphs and no "
+                        "timing; run a %d MiB copy (the calibration kernel), then every "
+                        "phase N times eagerly" % (CALIBRATION_BYTES >> 20))
     return p.parse_args()
+
+
+def say(msg):
+    print(msg, file=sys.stderr, flush=True)
 
 
 # ---- algorithmic bytes (per launch) ---------------------------------------------
@@ -63,11 +80,11 @@ def requant_bytes(T, N, K):          # codes+E4M3 in, codes+E8M0 out, one g per 
 
 
 def act_quant_bytes(M, K):           # bf16 in, codes + E8M0 out
-    return M * K * (2 + 0.5 + 1 / 32)
+    return M * K * (2 + MX4)
 
 
 def gemm_bytes(M, N, K, out_bytes=2):  # both MXFP4 operands in, Y out
-    return (M + N) * K * (0.5 + 1 / 32) + M * N * out_bytes
+    return (M + N) * K * MX4 + M * N * out_bytes
 
 
 # The source files each measured kernel is built from (its traffic record is
@@ -92,7 +109,7 @@ def kernel_source_digest(tag=None):
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(kernel_tag):
+def recorded_traffic(kernel_tag, key="hbm_bytes_per_dispatch"):
     """HBM bytes per dispatch measured by rocprofv3 PMC runs (profiles/), valid
     only while the kernel's sources hash to the digest stored with them."""
     f = ROOT / "profiles" / f"{kernel_tag}_traffic.txt"
@@ -106,7 +123,7 @@ def recorded_traffic(kernel_tag):
     if kv.get("kernel_source_digest") != kernel_source_digest(kernel_tag):
         return None
     try:
-        return float(kv["hbm_bytes_per_dispatch"])
+        return float(kv[key])
     except (KeyError, ValueError):
         return None
 
@@ -170,126 +187,52 @@ class Phases:
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / (reps * per_replay)
 
+    def time_all(self, reps):
+        return {name: self.time(name, reps, 1) for name in self.fns if name != "step"}
+
+
+def roofline(kernel, bound, achieved, peak, unit, traffic, per_launch, avg_us, measured=None):
+    r = {"kernel": kernel, "bound": bound, "achieved": round(achieved, 1), "peak": peak,
+         "unit": unit, "frac": round(achieved / peak, 4), "traffic": traffic,
+         "algorithmic_per_launch": per_launch, "avg_launch_us": round(avg_us, 3)}
+    if measured:
+        r["measured_peak"] = round(measured, 1)
+        r["frac_of_measured_peak"] = round(achieved / measured, 4)
+    return r
+
+
+# ---- host / CPU description for the CPU baselines ----------------------------------
+def host_info():
+    model = platform.processor() or "unknown"
+    try:
+        for line in pathlib.Path("/proc/cpuinfo").read_text().splitlines():
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    aff = sorted(os.sched_getaffinity(0))
+    runs, start = [], aff[0] if aff else 0
+    for a, b in zip(aff, aff[1:] + [None]):
+        if b != a + 1:
+            runs.append(f"{start}-{a}" if a != start else f"{a}")
+            start = b
+    return {"cpu_model": model, "nproc": os.cpu_count(), "affinity": ",".join(runs),
+            "affinity_cpus": len(aff)}
+
 
 # ---- workloads ------------------------------------------------------------------------
-def decode_workload(torch, mx, synth):
-    N, K, Ms = 12288, 4096, (1, 8, 32, 64)
-    d = torch.device("cuda:0")
-    w = synth.bf16_normal((N, K), 0.02, seed=11, device=d)
-    codes, scales, g = synth.nvfp4_from_bf16(w)
-    g = g.reshape(1)
-    R = max(2, math.ceil(ROTATE_BYTES / requant_bytes(1, N, K)))
-    src = [(codes.clone(), scales.clone(), g.clone()) for _ in range(R)]
-    dst = [(torch.empty((N, K // 2), dtype=torch.uint8, device=d),
-            torch.empty((N, K // 32), dtype=torch.uint8, device=d)) for _ in range(R)]
-    x = synth.activations(64, K, seed=12, outlier_seed=13, device="cpu").to(d)
-    xs = {M: x[:M].contiguous() for M in Ms}
-    xq = {M: (torch.empty((M, K // 2), dtype=torch.uint8, device=d),
-              torch.empty((M, K // 32), dtype=torch.uint8, device=d)) for M in Ms}
-    ys = {M: torch.empty((M, N), dtype=torch.bfloat16, device=d) for M in Ms}
-
-    def requant(r):
-        c, s, gg = src[r]
-        mx.mxfp4_requant_from_nvfp4(c, s, gg, *dst[r])
-
-    def pair(r, M):
-        mx.mxfp4_quantize_act(xs[M], *xq[M])
-        mx.mxfp4_gemm(xq[M][0], xq[M][1], dst[r][0], dst[r][1], ys[M])
-
-    ws_bytes = max(mx.mxfp4_linear_workspace_size(M, N, K) for M in Ms)
-    ws = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=d)
-
-    def linear(r, M):               # the same pair as one call
-        mx.mxfp4_linear_bf16(xs[M], dst[r][0], dst[r][1], ys[M], workspace=ws)
-
-    ph = Phases(torch, R)
-    ph.add("step", lambda r: (requant(r), [linear(r, M) for M in Ms]))
-    ph.add("linears", lambda r: [linear(r, M) for M in Ms])
-    ph.add("pairs", lambda r: [pair(r, M) for M in Ms])
-    ph.add("gemm", lambda r: [mx.mxfp4_gemm(xq[M][0], xq[M][1], dst[r][0], dst[r][1], ys[M])
-                              for M in Ms])
-    ph.add("requant", requant)
-    for M in Ms:
-        ph.add(f"linear_M{M}", lambda r, M=M: linear(r, M))
-        ph.add(f"act_quant_M{M}", lambda r, M=M: mx.mxfp4_quantize_act(xs[M], *xq[M]))
-        ph.add(f"gemm_M{M}", lambda r, M=M: mx.mxfp4_gemm(xq[M][0], xq[M][1], dst[r][0],
-                                                           dst[r][1], ys[M]))
-
-    def report(t, steps):
-        flops = sum(2 * M * N * K for M in Ms)
-        value = flops / (t["linears"] * 1e-3) / 1e12
-        gb_req = requant_bytes(1, N, K) / (t["requant"] * 1e-3) / 1e9
-        gemm_b = sum(gemm_bytes(M, N, K) for M in Ms)
-        gemm_gbps = gemm_b / (t["gemm"] * 1e-3) / 1e9
-        per_m = {}
-        for M in Ms:
-            ta, tg = t[f"act_quant_M{M}"], t[f"gemm_M{M}"]
-            tl = t[f"linear_M{M}"]
-            per_m[str(M)] = {
-                "linear_us": round(tl * 1e3, 2),
-                "linear_one_launch": mx.mxfp4_linear_workspace_size(M, N, K) == 0,
-                "TFLOPs_linear": round(2 * M * N * K / (tl * 1e-3) / 1e12, 3),
-                "act_quant_us": round(ta * 1e3, 2), "gemm_us": round(tg * 1e3, 2),
-                "gemm_GBps": round(gemm_bytes(M, N, K) / (tg * 1e-3) / 1e9, 1),
-                "gemm_frac_hbm": round(gemm_bytes(M, N, K) / (tg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-                "TFLOPs_incl_act_quant": round(2 * M * N * K / ((ta + tg) * 1e-3) / 1e12, 3),
-            }
-        roof = {"kernel": "mxfp4_gemm, decode (M=1,8,32,64)", "bound": "hbm",
-                "achieved": round(gemm_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(gemm_gbps / HBM_PEAK_GBPS, 4),
-                "traffic": recorded_traffic("gemm_decode"),
-                "algorithmic_bytes_per_launch": round(gemm_b / len(Ms)),
-                "avg_launch_us": round(t["gemm"] / len(Ms) * 1e3, 3)}
-        extra = {"requant_GBps": round(gb_req, 1),
-                 "requant_frac_hbm": round(gb_req / HBM_PEAK_GBPS, 4),
-                 "requant_us": round(t["requant"] * 1e3, 2),
-                 "linear_calls_us": round(t["linears"] * 1e3, 2),
-                 "act_quant_plus_gemm_us": round(t["pairs"] * 1e3, 2),
-                 "per_M": per_m, "weight_copies_rotated": R}
-        cfg = {"workload": "decode-shaped dense linear: NVFP4->MXFP4 requant of W "
-                           "[12288,4096] + act-quant + W4A4 GEMM for M in {1,8,32,64} "
-                           "(mxfp4_linear_bf16), bf16 out",
-               "N": N, "K": K, "M": list(Ms)}
-        return value, "TFLOP/s", roof, extra, cfg
-
-    def cpu_baseline():
-        import numpy as np
-        import oracle
-        wc, ws, gg = codes.cpu().numpy(), scales.cpu().numpy(), g.cpu().numpy()
-        xb = x.cpu().view(torch.int16).numpy().view(np.uint16)
-        t0 = time.perf_counter()
-        oc, os_ = oracle.requant(wc, ws, gg)
-        t1 = time.perf_counter()
-        reps = 0
-        while True:
-            for M in Ms:
-                ac, as_ = oracle.quantize_act(xb[:M])
-                oracle.gemm(ac, as_, oc, os_)
-            reps += 1
-            t2 = time.perf_counter()
-            if t2 - t1 > 10.0:
-                break
-        flops = sum(2 * M * N * K for M in Ms) * reps
-        return {"value": round(flops / (t2 - t1) / 1e12, 6), "unit": "TFLOP/s",
-                "cores": oracle.num_threads(), "kind": "oracle",
-                "sample": f"the whole workload: oracle requant of W [12288,4096] once "
-                          f"({requant_bytes(1, N, K) / (t1 - t0) / 1e9:.3f} GB/s), then act-quant "
-                          f"+ fp64 GEMM for M in {{1,8,32,64}} repeated {reps}x over >= 10 s",
-                "seconds": round(t2 - t0, 2)}
-
-    return ph, report, cpu_baseline
-
-
 def prefill_workload(torch, mx, synth):
     M = 4096
     shapes = [(4096, 4096), (28672, 4096), (4096, 14336)]
     d = torch.device("cuda:0")
-    data = []
+    data, nv_host = [], []
     for (N, K), ws, xs_, os_ in zip(shapes, (21, 22, 23), (24, 24, 25), (26, 26, 27)):
         w = synth.bf16_normal((N, K), 0.02, seed=ws, device=d)
         c, s, g = synth.nvfp4_from_bf16(w)
         del w
         wc, wsc = mx.mxfp4_requant_from_nvfp4(c, s, g.reshape(1))
+        nv_host.append((c.cpu(), s.cpu(), g.reshape(1).cpu()))
         x0 = synth.activations(M, K, seed=xs_, outlier_seed=os_, device=d)
         # rotated copies of the activations and their quantized form, so the
         # activation bytes come from HBM rather than the Infinity Cache
@@ -313,7 +256,7 @@ def prefill_workload(torch, mx, synth):
         ph.add(f"gemm_{N}x{K}", lambda r, xq=xq, wc=wc, wsc=wsc, y=y:
                mx.mxfp4_gemm(xq[r][0], xq[r][1], wc, wsc, y))
 
-    def report(t, steps):
+    def report(t, peaks):
         flops = sum(2 * M * N * K for N, K in shapes)
         value = flops / (t["step"] * 1e-3) / 1e12
         per = {}
@@ -321,19 +264,161 @@ def prefill_workload(torch, mx, synth):
         for N, K in shapes:
             ta, tg = t[f"aq_{N}x{K}"], t[f"gemm_{N}x{K}"]
             tg_all += tg
-            per[f"{N}x{K}"] = {"act_quant_us": round(ta * 1e3, 2), "gemm_us": round(tg * 1e3, 2),
-                               "gemm_TFLOPs": round(2 * M * N * K / (tg * 1e-3) / 1e12, 1),
-                               "TFLOPs_incl_act_quant": round(2 * M * N * K / ((ta + tg) * 1e-3) / 1e12, 1),
-                               "act_quant_GBps": round(act_quant_bytes(M, K) / (ta * 1e-3) / 1e9, 1)}
-        ach = flops / (tg_all * 1e-3) / 1e12
-        roof = {"kernel": "mxfp4_gemm, prefill", "bound": "mfma", "achieved": round(ach, 1),
-                "peak": MXFP4_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / MXFP4_PEAK_TFLOPS, 4),
-                "traffic": recorded_traffic("gemm_prefill")}
+            gb = act_quant_bytes(M, K) / (ta * 1e-3) / 1e9
+            per[f"{N}x{K}"] = {
+                "act_quant_us": round(ta * 1e3, 2), "gemm_us": round(tg * 1e3, 2),
+                "gemm_TFLOPs": round(2 * M * N * K / (tg * 1e-3) / 1e12, 1),
+                "TFLOPs_incl_act_quant": round(2 * M * N * K / ((ta + tg) * 1e-3) / 1e12, 1),
+                "act_quant_GBps": round(gb, 1), "act_quant_frac_hbm": round(gb / HBM_PEAK_GBPS, 4)}
+        # the dominant kernel: the 28672 x 4096 GEMM (persistent tile walk)
+        N, K = 28672, 4096
+        tg = t[f"gemm_{N}x{K}"]
+        ach = 2 * M * N * K / (tg * 1e-3) / 1e12
+        roof = roofline("mxfp4_gemm M=4096 N=28672 K=4096 (gemm_persistent_kernel), bf16 out",
+                        "mfma", ach, MXFP4_PEAK_TFLOPS, "TFLOP/s",
+                        recorded_traffic("gemm_prefill", "hbm_bytes_per_dispatch_28672x4096"),
+                        {"flop": 2 * M * N * K, "bytes": gemm_bytes(M, N, K)}, tg * 1e3,
+                        peaks.get("mfma_TFLOPs"))
+        extra = {"per_shape": per,
+                 "three_gemms_TFLOPs": round(flops / (tg_all * 1e-3) / 1e12, 1),
+                 "step_frac_mfma_peak": round(value / MXFP4_PEAK_TFLOPS, 4)}
+        if peaks.get("mfma_TFLOPs"):
+            extra["step_frac_of_measured_mfma_peak"] = round(value / peaks["mfma_TFLOPs"], 4)
         cfg = {"workload": "prefill dense linears M=4096, (N,K) in (4096,4096),(28672,4096),"
-                           "(4096,14336): act-quant + W4A4 GEMM, bf16 out"}
-        return value, "TFLOP/s", roof, {"per_shape": per}, cfg
+                           "(4096,14336): act-quant + W4A4 GEMM, bf16 out",
+               "M": M, "NK": [list(s) for s in shapes]}
+        return value, "TFLOP/s", roof, extra, cfg
 
-    return ph, report, None
+    def cpu_baseline():
+        """The oracle on a row sample of the step: act-quant of the sampled
+        rows, then the exact GEMM against each whole weight (requantized by
+        the oracle beforehand, not timed), all threads on 1024 rows and one
+        thread on 32 rows, each scaled to TFLOP/s of the same flops."""
+        import numpy as np
+        import oracle
+        ops = []
+        for (N, K), (c, s, g), (_, _, _, _, x, _, _) in zip(shapes, nv_host, data):
+            oc, os_ = oracle.requant(c.numpy(), s.numpy(), g.numpy())
+            xb = x[0].cpu().view(torch.int16).numpy().view(np.uint16)
+            ops.append((N, K, oc, os_, xb))
+
+        def run(rows, threads):
+            oracle.set_num_threads(threads)
+            t0 = time.perf_counter()
+            flops = 0
+            for N, K, oc, os_, xb in ops:
+                ac, as_ = oracle.quantize_act(xb[rows])
+                oracle.gemm(ac, as_, oc, os_)
+                flops += 2 * len(rows) * N * K
+            return flops, time.perf_counter() - t0
+
+        all_threads = oracle.num_threads()
+        rows_all = np.arange(0, M, M // 1024)
+        f_all, t_all = run(rows_all, all_threads)
+        f_one, t_one = run(np.arange(0, M, M // 32), 1)
+        oracle.set_num_threads(all_threads)
+        return {"value": round(f_all / t_all / 1e12, 6), "unit": "TFLOP/s",
+                "cores": all_threads, "kind": "oracle",
+                "sample": f"{len(rows_all)} of the 4096 rows (every 4th) through act-quant + "
+                          f"exact GEMM for the three (N,K), all {all_threads} threads: "
+                          f"{t_all:.2f} s; scaled by flops",
+                "seconds": round(t_all, 2),
+                "single_thread": {"value": round(f_one / t_one / 1e12, 6), "unit": "TFLOP/s",
+                                  "sample": "32 rows (every 128th), 1 thread",
+                                  "seconds": round(t_one, 2)},
+                **host_info()}
+
+    return ph, report, cpu_baseline
+
+
+def decode_workload(torch, mx, synth):
+    N, K, Ms = 12288, 4096, (1, 8, 32, 64)
+    d = torch.device("cuda:0")
+    w = synth.bf16_normal((N, K), 0.02, seed=11, device=d)
+    codes, scales, g = synth.nvfp4_from_bf16(w)
+    del w
+    g = g.reshape(1)
+    R = max(2, math.ceil(ROTATE_BYTES / requant_bytes(1, N, K)))
+    src = [(codes.clone(), scales.clone(), g.clone()) for _ in range(R)]
+    dst = [(torch.empty((N, K // 2), dtype=torch.uint8, device=d),
+            torch.empty((N, K // 32), dtype=torch.uint8, device=d)) for _ in range(R)]
+    x = synth.activations(64, K, seed=12, outlier_seed=13, device="cpu").to(d)
+    xs = {M: x[:M].contiguous() for M in Ms}
+    xq = {M: (torch.empty((M, K // 2), dtype=torch.uint8, device=d),
+              torch.empty((M, K // 32), dtype=torch.uint8, device=d)) for M in Ms}
+    ys = {M: torch.empty((M, N), dtype=torch.bfloat16, device=d) for M in Ms}
+    ws_bytes = max(mx.mxfp4_linear_workspace_size(M, N, K) for M in Ms)
+    ws = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=d)
+
+    def requant(r):
+        c, s, gg = src[r]
+        mx.mxfp4_requant_from_nvfp4(c, s, gg, *dst[r])
+
+    def linear(r, M):
+        mx.mxfp4_linear_bf16(xs[M], dst[r][0], dst[r][1], ys[M], workspace=ws)
+
+    def gemm(r, M):
+        mx.mxfp4_gemm(xq[M][0], xq[M][1], dst[r][0], dst[r][1], ys[M])
+
+    ph = Phases(torch, R)
+    ph.add("step", lambda r: (requant(r), [linear(r, M) for M in Ms]))
+    ph.add("linears", lambda r: [linear(r, M) for M in Ms])
+    ph.add("gemm", lambda r: [gemm(r, M) for M in Ms])
+    ph.add("requant", requant)
+    for M in Ms:
+        ph.add(f"linear_M{M}", lambda r, M=M: linear(r, M))
+        ph.add(f"act_quant_M{M}", lambda r, M=M: mx.mxfp4_quantize_act(xs[M], *xq[M]))
+        ph.add(f"gemm_M{M}", lambda r, M=M: gemm(r, M))
+
+    def report(t, peaks):
+        flops = sum(2 * M * N * K for M in Ms)
+        gemm_b = sum(gemm_bytes(M, N, K) for M in Ms)
+        gemm_gbps = gemm_b / (t["gemm"] * 1e-3) / 1e9
+        gb_req = requant_bytes(1, N, K) / (t["requant"] * 1e-3) / 1e9
+        copy = peaks.get("copy_GBps")
+        per_m = {}
+        for M in Ms:
+            ta, tg, tl = t[f"act_quant_M{M}"], t[f"gemm_M{M}"], t[f"linear_M{M}"]
+            gb = gemm_bytes(M, N, K) / (tg * 1e-3) / 1e9
+            per_m[str(M)] = {
+                "linear_us": round(tl * 1e3, 2),
+                "linear_one_launch": mx.mxfp4_linear_workspace_size(M, N, K) == 0,
+                "TFLOPs_linear": round(2 * M * N * K / (tl * 1e-3) / 1e12, 3),
+                "act_quant_us": round(ta * 1e3, 2), "gemm_us": round(tg * 1e3, 2),
+                "gemm_GBps": round(gb, 1), "gemm_frac_hbm": round(gb / HBM_PEAK_GBPS, 4)}
+        return {
+            "workload": "decode-shaped dense linear: requant of W [12288,4096] + act-quant + "
+                        "W4A4 GEMM for M in {1,8,32,64} (mxfp4_linear_bf16), bf16 out",
+            "step_ms": round(t["step"], 4),
+            "TFLOPs_incl_act_quant": round(flops / (t["linears"] * 1e-3) / 1e12, 3),
+            "roofline": roofline("mxfp4_gemm decode (M=1,8,32,64), gemm_skinny", "hbm",
+                                 gemm_gbps, HBM_PEAK_GBPS, "GB/s", recorded_traffic("gemm_decode"),
+                                 {"bytes": round(gemm_b / len(Ms))},
+                                 t["gemm"] / len(Ms) * 1e3, copy),
+            "requant": roofline("mxfp4_requant_from_nvfp4 W [12288,4096]", "hbm", gb_req,
+                                HBM_PEAK_GBPS, "GB/s", recorded_traffic("requant"),
+                                {"bytes": requant_bytes(1, N, K)}, t["requant"] * 1e3, copy),
+            "per_M": per_m, "weight_copies_rotated": R}
+
+    def cpu_baseline():
+        import numpy as np
+        import oracle
+        wc, wsc, gg = codes.cpu().numpy(), scales.cpu().numpy(), g.cpu().numpy()
+        xb = x.cpu().view(torch.int16).numpy().view(np.uint16)
+        t0 = time.perf_counter()
+        oc, os_ = oracle.requant(wc, wsc, gg)
+        t1 = time.perf_counter()
+        for M in Ms:
+            ac, as_ = oracle.quantize_act(xb[:M])
+            oracle.gemm(ac, as_, oc, os_)
+        t2 = time.perf_counter()
+        return {"TFLOPs": round(sum(2 * M * N * K for M in Ms) / (t2 - t1) / 1e12, 6),
+                "requant_GBps": round(requant_bytes(1, N, K) / (t1 - t0) / 1e9, 3),
+                "cores": oracle.num_threads(), "kind": "oracle",
+                "sample": "the whole workload once: requant, then act-quant + exact GEMM for "
+                          "M in {1,8,32,64}", "seconds": round(t2 - t0, 2)}
+
+    return ph, report, cpu_baseline
 
 
 def moe_workload(torch, mx, synth):
@@ -360,8 +445,6 @@ def moe_workload(torch, mx, synth):
             mx.mxfp4_requant_from_nvfp4(c, s, g.reshape(1), wc[e], ws[e])
         W[name] = (N, K, wc, ws)
     Mtot = T * TOPK
-    # rotated copies of the activation-side buffers (the expert weights,
-    # 855 MB, exceed the Infinity Cache on their own)
     R = MOE_SLOTS
     tokens = [tokens.clone() for _ in range(R)]
     aq1 = [(torch.empty((Mtot, 2048), dtype=torch.uint8, device=d),
@@ -373,7 +456,6 @@ def moe_workload(torch, mx, synth):
     out = [torch.empty((T, 4096), dtype=torch.bfloat16, device=d) for _ in range(R)]
 
     def aq_gate_up(r):
-        # each token quantized once, written to its top-k expert-sorted rows
         mx.mxfp4_quantize_act_scatter(tokens[r], rows, *aq1[r])
 
     def aq_gate_up_gather(r):
@@ -399,66 +481,79 @@ def moe_workload(torch, mx, synth):
     def step(r):
         aq_gate_up(r), gate_up_glu(r), gemm_down(r)
 
-    def step_two_call(r):
-        aq_gate_up(r), gemm_gate_up(r), act_down(r), gemm_down(r)
-
     ph = Phases(torch, R)
     ph.add("step", step)
-    ph.add("step_two_call", step_two_call)
+    ph.add("step_two_call", lambda r: (aq_gate_up(r), gemm_gate_up(r), act_down(r),
+                                       gemm_down(r)))
     ph.add("layer", lambda r: (step(r), combine(r)))
     for f in (aq_gate_up, aq_gate_up_gather, gate_up_glu, gemm_gate_up, act_down, gemm_down,
               combine):
         ph.add(f.__name__, f)
 
-    def report(t, steps):
+    def report(t, peaks):
         flops = 2 * Mtot * (2048 * 4096 + 4096 * 1024)
-        value = flops / (t["step"] * 1e-3) / 1e12
-        # the step's two grouped GEMMs: gate_up with the activation in its
-        # epilogue (writes MXFP4 h), then down
         tg = t["gate_up_glu"] + t["gemm_down"]
-        mx4 = 0.5 + 1 / 32
-        gb = (E * 2048 * 4096 * mx4 + Mtot * 4096 * mx4 + Mtot * 1024 * mx4 +
-              E * 4096 * 1024 * mx4 + Mtot * 1024 * mx4 + Mtot * 4096 * 2)
+        gb = (E * 2048 * 4096 * MX4 + Mtot * 4096 * MX4 + Mtot * 1024 * MX4 +
+              E * 4096 * 1024 * MX4 + Mtot * 1024 * MX4 + Mtot * 4096 * 2)
         ach = gb / (tg * 1e-3) / 1e9
         tg2 = t["gemm_gate_up"] + t["gemm_down"]
-        gb2 = gb - Mtot * 1024 * mx4 + Mtot * 2048 * 2
-        per = {k: round(t[k] * 1e3, 2) for k in ("aq_gate_up", "aq_gate_up_gather", "gate_up_glu",
-                                                 "gemm_gate_up", "act_down", "gemm_down",
-                                                 "combine")}
-        # algorithmic bytes of the two epilogue kernels
-        act_b = Mtot * 2048 * 2 + Mtot * 1024 * mx4
+        gb2 = gb - Mtot * 1024 * MX4 + Mtot * 2048 * 2
+        act_b = Mtot * 2048 * 2 + Mtot * 1024 * MX4
         comb_b = Mtot * 4096 * 2 + T * 4096 * 2 + T * TOPK * 8
-        roof = {"kernel": "mxfp4_grouped_gemm_silu_quantize (gate_up) + mxfp4_grouped_gemm "
-                          "(down)", "bound": "hbm",
-                "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBPS, 4),
-                "traffic": recorded_traffic("grouped_gemm_moe_step"),
-                "algorithmic_bytes_per_launch": round(gb / 2),
-                "avg_launch_us": round(tg / 2 * 1e3, 2),
-                "gemm_TFLOPs": round(flops / (tg * 1e-3) / 1e12, 1)}
-        extra = {"per_kernel_us": per,
-                 "step_two_call_us": round(t["step_two_call"] * 1e3, 2),
-                 "step_two_call_TFLOPs": round(flops / (t["step_two_call"] * 1e-3) / 1e12, 1),
-                 "two_call_grouped_gemms_GBps": round(gb2 / (tg2 * 1e-3) / 1e9, 1),
-                 "two_call_grouped_gemms_traffic": recorded_traffic("grouped_gemm_moe"),
-                 "layer_us": round(t["layer"] * 1e3, 2),
-                 "layer_TFLOPs": round(flops / (t["layer"] * 1e-3) / 1e12, 1),
-                 "act_down_GBps": round(act_b / (t["act_down"] * 1e-3) / 1e9, 1),
-                 "combine_GBps": round(comb_b / (t["combine"] * 1e-3) / 1e9, 1)}
-        cfg = {"workload": "MoE 128 experts, 2048 tokens top-8: act-quant scattered to the "
-                           "routed rows + grouped GEMM gate_up [2048,4096] with silu(gate)*up "
-                           "act-quant in its epilogue + grouped GEMM down [4096,1024] "
-                           "(layer_us adds the top-k combine)"}
-        return value, "TFLOP/s", roof, extra, cfg
+        return {
+            "workload": "MoE 128 experts, 2048 tokens top-8: act-quant scattered to the routed "
+                        "rows + grouped GEMM gate_up [2048,4096] with silu(gate)*up act-quant in "
+                        "its epilogue + grouped GEMM down [4096,1024]; layer adds the combine",
+            "step_us": round(t["step"] * 1e3, 2),
+            "TFLOPs_incl_act_quant": round(flops / (t["step"] * 1e-3) / 1e12, 1),
+            "roofline": roofline("mxfp4_grouped_gemm_silu_quantize (gate_up) + "
+                                 "mxfp4_grouped_gemm (down)", "hbm", ach, HBM_PEAK_GBPS, "GB/s",
+                                 recorded_traffic("grouped_gemm_moe_step"), {"bytes": round(gb / 2)},
+                                 tg / 2 * 1e3, peaks.get("copy_GBps")),
+            "grouped_gemms_TFLOPs": round(flops / (tg * 1e-3) / 1e12, 1),
+            "per_kernel_us": {k: round(t[k] * 1e3, 2) for k in (
+                "aq_gate_up", "aq_gate_up_gather", "gate_up_glu", "gemm_gate_up", "act_down",
+                "gemm_down", "combine")},
+            "step_two_call_us": round(t["step_two_call"] * 1e3, 2),
+            "two_call_grouped_gemms_GBps": round(gb2 / (tg2 * 1e-3) / 1e9, 1),
+            "layer_us": round(t["layer"] * 1e3, 2),
+            "layer_TFLOPs": round(flops / (t["layer"] * 1e-3) / 1e12, 1),
+            "act_down_GBps": round(act_b / (t["act_down"] * 1e-3) / 1e9, 1),
+            "combine_GBps": round(comb_b / (t["combine"] * 1e-3) / 1e9, 1)}
 
-    return ph, report, None
+    def cpu_baseline():
+        """Four experts' rows through the oracle's act-quant + exact gate_up and
+        down GEMMs, scaled by flops."""
+        import numpy as np
+        import oracle
+        off = offsets.cpu().numpy()
+        tok = tokens[0].cpu().view(torch.int16).numpy().view(np.uint16)
+        pm = perm.cpu().numpy()
+        gu = [u.cpu().numpy() for u in W["gate_up"][2:]]
+        dn = [u.cpu().numpy() for u in W["down"][2:]]
+        t0 = time.perf_counter()
+        flops = 0
+        for e in (0, 41, 87, 127):
+            r0, r1 = int(off[e]), int(off[e + 1])
+            ac, as_ = oracle.quantize_act(tok, row_index=pm[r0:r1])
+            oracle.gemm(ac, as_, gu[0][e], gu[1][e])
+            hc = np.zeros((r1 - r0, 512), np.uint8)
+            hs = np.full((r1 - r0, 32), 127, np.uint8)
+            oracle.gemm(hc, hs, dn[0][e], dn[1][e])
+            flops += 2 * (r1 - r0) * (2048 * 4096 + 4096 * 1024)
+        dt = time.perf_counter() - t0
+        return {"TFLOPs": round(flops / dt / 1e12, 6), "cores": oracle.num_threads(),
+                "kind": "oracle", "sample": "4 experts' routed rows: act-quant + exact gate_up "
+                "and down GEMMs, scaled by flops", "seconds": round(dt, 2)}
+
+    return ph, report, cpu_baseline
 
 
 def w4a8_workload(torch, mx, synth):
     """W4A8 (MXFP8 activations x the same MXFP4 weights): the decode-shaped
     layer W [12288, 4096] for M in {1, 8, 32, 64} through mxfp4_linear_w4a8_bf16
     with a bf16 row bias, weight copies rotated past the Infinity Cache; a
-    prefill-shaped [4096, 4096] x [4096, 4096] W4A8 GEMM is timed beside it."""
+    prefill-shaped [4096, 4096] x [4096, 4096] W4A8 GEMM beside it."""
     N, K, Ms = 12288, 4096, (1, 8, 32, 64)
     d = torch.device("cuda:0")
     w = synth.bf16_normal((N, K), 0.02, seed=11, device=d)
@@ -500,10 +595,9 @@ def w4a8_workload(torch, mx, synth):
         ph.add(f"gemm_M{M}", lambda r, M=M: gemm(r, M))
     ph.add("prefill_gemm", lambda r: mx.mxfp4_gemm_w4a8(xpq[0], xpq[1], wpc, wps, yp))
 
-    def report(t, steps):
+    def report(t, peaks):
         flops = sum(2 * M * N * K for M in Ms)
-        value = flops / (t["step"] * 1e-3) / 1e12
-        wbytes = N * K * (0.5 + 1 / 32)
+        wbytes = N * K * MX4
         gb = [wbytes + M * K * (1 + 1 / 32) + M * N * 2 + N * 2 for M in Ms]
         gemm_gbps = sum(gb) / (t["gemm"] * 1e-3) / 1e9
         per_m = {str(M): {"linear_us": round(t[f"linear_M{M}"] * 1e3, 2),
@@ -513,48 +607,66 @@ def w4a8_workload(torch, mx, synth):
                           "gemm_GBps": round(b / (t[f"gemm_M{M}"] * 1e-3) / 1e9, 1)}
                  for M, b in zip(Ms, gb)}
         pf = 2 * PM * PN * PK / (t["prefill_gemm"] * 1e-3) / 1e12
-        roof = {"kernel": "mxfp4_gemm_w4a8, decode (M=1,8,32,64)", "bound": "hbm",
-                "achieved": round(gemm_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(gemm_gbps / HBM_PEAK_GBPS, 4),
-                "traffic": recorded_traffic("gemm_w4a8_decode"),
-                "algorithmic_bytes_per_launch": round(sum(gb) / len(Ms)),
-                "avg_launch_us": round(t["gemm"] / len(Ms) * 1e3, 3)}
-        extra = {"dtype": "w4a8 (e4m3 x e2m1, e8m0 scales, fp32 acc)", "per_M": per_m,
-                 "prefill_gemm_us": round(t["prefill_gemm"] * 1e3, 2),
-                 "prefill_gemm_TFLOPs": round(pf, 1),
-                 "prefill_gemm_frac_fp8_peak": round(pf / 5000.0, 4),
-                 "weight_copies_rotated": R}
-        cfg = {"workload": "W4A8 decode-shaped linear W [12288,4096], M in {1,8,32,64} "
-                           "(mxfp4_linear_w4a8_bf16 with bf16 bias, bf16 out); beside it a "
-                           "[4096,4096]x[4096,4096] W4A8 GEMM",
-               "N": N, "K": K, "M": list(Ms)}
-        return value, "TFLOP/s", roof, extra, cfg
+        return {"workload": "W4A8 decode-shaped linear W [12288,4096], M in {1,8,32,64} "
+                            "(mxfp4_linear_w4a8_bf16 with bf16 bias); a [4096]^3 W4A8 GEMM",
+                "dtype": "w4a8 (e4m3 x e2m1, e8m0 scales, fp32 acc)",
+                "TFLOPs_incl_act_quant": round(flops / (t["step"] * 1e-3) / 1e12, 3),
+                "roofline": roofline("mxfp4_gemm_w4a8 decode (M=1,8,32,64)", "hbm", gemm_gbps,
+                                     HBM_PEAK_GBPS, "GB/s", recorded_traffic("gemm_w4a8_decode"),
+                                     {"bytes": round(sum(gb) / len(Ms))},
+                                     t["gemm"] / len(Ms) * 1e3, peaks.get("copy_GBps")),
+                "per_M": per_m, "prefill_gemm_us": round(t["prefill_gemm"] * 1e3, 2),
+                "prefill_gemm_TFLOPs": round(pf, 1),
+                "prefill_gemm_frac_fp8_peak": round(pf / FP8_PEAK_TFLOPS, 4)}
 
     return ph, report, None
 
 
 def layerwise_workload(torch, mx, synth):
-    """One MoE layer's NVFP4 tensors resident in a one-layer scratch buffer,
-    requantized into a 48-layer preallocated destination, layer after layer
-    (kernel time only; 5% of tensors excluded and skipped)."""
-    E, L = 128, 48
+    """The layerwise load, 48 MoE layers x 128 experts x ([2048,4096] +
+    [4096,1024]) with 5% of the tensors excluded, measured two ways:
+    * kernel only: one layer's NVFP4 source resident in HBM, requantized into
+      the 48-layer destination one launch per layer and tensor kind (the
+      subset requant), timed like the other phases;
+    * end to end: the layerwise driver streaming every layer from pinned host
+      memory (a pool of 2 distinct layers, layer l = pool[l % 2]) through a
+      one-layer scratch into the same destination, copies on their own
+      stream overlapping the requant, timed by the host around one call."""
+    E, L, P = 128, 48, 2
     d = torch.device("cuda:0")
     gen = torch.Generator().manual_seed(42)
     excluded = torch.rand((L, 2, E), generator=gen) < 0.05
     shapes = {0: (2048, 4096), 1: (4096, 1024)}
-    src = {}
-    for k, (N, K) in shapes.items():
-        w = synth.bf16_normal((E, N, K), 0.02, seed=41 + k, device=d)
-        src[k] = synth.nvfp4_from_bf16(w)
-        del w
+    src, pool = {}, []
+    for p in range(P):
+        layer = []
+        for k, (N, K) in shapes.items():
+            w = synth.bf16_normal((E, N, K), 0.02, seed=41 + 10 * p + k, device=d)
+            c, s, g = synth.nvfp4_from_bf16(w)
+            del w
+            if p == 0:
+                src[k] = (c, s, g)
+            host = []
+            for t in (c, s, g):
+                h = torch.empty(t.shape, dtype=t.dtype, pin_memory=True)
+                h.copy_(t)
+                host.append(h)
+            layer.append(host)
+        pool.append(layer)
     dst = {k: (torch.empty((L, E, N, K // 2), dtype=torch.uint8, device=d),
                torch.empty((L, E, N, K // 32), dtype=torch.uint8, device=d))
            for k, (N, K) in shapes.items()}
-    # one launch per layer and tensor kind: the experts not excluded, passed
-    # as a tensor list (excluded slots of the destination stay untouched)
     calls = [(l, k, (~excluded[l, k]).nonzero().flatten().tolist())
              for l in range(L) for k in shapes]
     n_tensors = sum(len(keep) for _, _, keep in calls)
+    layer_bytes = sum(E * (N * K // 2 + N * K // 16) for N, K in shapes.values())
+    scratch = torch.empty(layer_bytes, dtype=torch.uint8, device=d)
+    parts = [dict(nv_codes=pool[l % P][k][0], nv_scales=pool[l % P][k][1],
+                  nv_global=pool[l % P][k][2], excluded=excluded[l, k].to(torch.uint8),
+                  mx_codes=dst[k][0][l], mx_scales=dst[k][1][l])
+             for l in range(L) for k in shapes]
+    copied = sum(int((~excluded[l, k]).sum()) * (N * K // 2 + N * K // 16)
+                 for l in range(L) for k, (N, K) in shapes.items())
 
     def step(r):
         for l, k, keep in calls:
@@ -562,24 +674,117 @@ def layerwise_workload(torch, mx, synth):
             mc, ms = dst[k]
             mx.mxfp4_requant_from_nvfp4(c, s, g, mc[l], ms[l], tensors=keep)
 
-    ph = Phases(torch, 1)
+    ph = Phases(torch, 1, min_launches=1)
     ph.add("step", step)
 
-    def report(t, steps):
+    def end_to_end(runs=2):
+        cs = torch.cuda.Stream(d)
+        best = None
+        for _ in range(runs):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            mx.mxfp4_requant_layers_from_host(parts, scratch, copy_stream=cs)
+            torch.cuda.synchronize()
+            dt = time.perf_counter() - t0
+            best = dt if best is None else min(best, dt)
+        return best
+
+    def report(t, peaks):
         tt = t["step"]
         b = sum(requant_bytes(len(keep), *shapes[k]) for _, k, keep in calls)
         gbps = b / (tt * 1e-3) / 1e9
-        roof = {"kernel": "mxfp4_requant_from_nvfp4_subset", "bound": "hbm",
-                "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": recorded_traffic("requant"),
-                "algorithmic_bytes_per_launch": round(b / len(calls)),
-                "avg_launch_us": round(tt / len(calls) * 1e3, 3)}
-        cfg = {"workload": "layerwise load: 48 MoE layers x 128 experts x ([2048,4096] + "
-                           "[4096,1024]) NVFP4 -> MXFP4, 5% of tensors excluded",
-               "tensors_requantized": n_tensors, "launches": len(calls)}
-        return gbps, "GB/s", roof, {"ms_all_layers": round(tt, 3)}, cfg
+        e2e = end_to_end()
+        return {"workload": "layerwise load: 48 MoE layers x 128 experts x ([2048,4096] + "
+                            "[4096,1024]) NVFP4 -> MXFP4, 5% of tensors excluded",
+                "tensors_requantized": n_tensors, "launches": len(calls),
+                "roofline": roofline("mxfp4_requant_from_nvfp4_subset (kernel only, source "
+                                     "resident)", "hbm", gbps, HBM_PEAK_GBPS, "GB/s",
+                                     recorded_traffic("requant"),
+                                     {"bytes": round(b / len(calls))}, tt / len(calls) * 1e3,
+                                     peaks.get("copy_GBps")),
+                "kernel_ms_all_layers": round(tt, 3),
+                "end_to_end": {"seconds": round(e2e, 3),
+                               "host_to_device_GB": round(copied / 1e9, 2),
+                               "host_to_device_GBps": round(copied / e2e / 1e9, 1),
+                               "scratch_bytes": layer_bytes, "pool_layers": P,
+                               "how": "mxfp4_requant_layers_from_host over all 48 layers, "
+                                      "pinned host source, copies on a second stream; best "
+                                      "of 2 runs"}}
 
-    return ph, report, None
+    def cpu_baseline():
+        import oracle
+        c, s, g = (u.cpu().numpy() for u in src[0])
+        t0 = time.perf_counter()
+        oracle.requant(c[:8], s[:8], g[:8])
+        dt = time.perf_counter() - t0
+        return {"GBps": round(requant_bytes(8, 2048, 4096) / dt / 1e9, 3),
+                "cores": oracle.num_threads(), "kind": "oracle",
+                "sample": "8 gate_up tensors [2048,4096]", "seconds": round(dt, 2)}
+
+    return ph, report, cpu_baseline
+
+
+WORKLOADS = {"prefill": prefill_workload, "decode": decode_workload, "moe": moe_workload,
+             "layerwise": layerwise_workload, "w4a8": w4a8_workload}
+
+
+# ---- this GPU's own ceilings ------------------------------------------------------------
+def measure_peaks(torch):
+    """MFMA-loop TFLOP/s with its clock, and copy GB/s (read + write), from
+    libmxfp4_calibrate.so; {} if that library is missing."""
+    lib_path = ROOT / "w4a4_mxfp4_gemm_amd" / "libmxfp4_calibrate.so"
+    if not lib_path.exists():
+        return {}
+    lib = ctypes.CDLL(str(lib_path))
+    lib.mxfp4_calibrate_mfma.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_void_p]
+    lib.mxfp4_calibrate_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                         ctypes.c_int, ctypes.c_void_p]
+    lib.mxfp4_calibrate_mfma_flop_per_round.restype = ctypes.c_double
+    d = torch.device("cuda:0")
+    stream = ctypes.c_void_p(torch.cuda.current_stream(d).cuda_stream)
+    waves = lib.mxfp4_calibrate_mfma_waves()
+    clocks = torch.zeros(2 * waves, dtype=torch.int64, device=d)
+    sink = torch.zeros(256 * 256, dtype=torch.float32, device=d)
+    iters = 40000
+    out = {}
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    ms = timed(lambda: lib.mxfp4_calibrate_mfma(iters, ctypes.c_void_p(clocks.data_ptr()),
+                                                ctypes.c_void_p(sink.data_ptr()), stream), 3)
+    flop = waves * iters * lib.mxfp4_calibrate_mfma_flop_per_round()
+    c = clocks.cpu().view(-1, 2).double()
+    ghz = float((c[:, 0] / (c[:, 1] / 100e6)).mean() / 1e9)
+    out["mfma_TFLOPs"] = round(flop / (ms * 1e-3) / 1e12, 1)
+    out["mfma_clock_GHz"] = round(ghz, 3)
+    out["mfma_how"] = ("one wavefront per SIMD, back-to-back 32x32x64 E2M1 scaled MFMAs on "
+                       "operands that change every round; clock from the shader and 100 MHz "
+                       "counters of each wave")
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device=d)
+    b = torch.empty(n, dtype=torch.uint8, device=d)
+    a.fill_(1)
+    best = None
+    for cfg in range(lib.mxfp4_calibrate_copy_configs()):
+        ms = timed(lambda: lib.mxfp4_calibrate_copy(ctypes.c_void_p(a.data_ptr()),
+                                                    ctypes.c_void_p(b.data_ptr()), n, cfg,
+                                                    stream), 5)
+        best = ms if best is None else min(best, ms)
+    out["copy_GBps"] = round(2 * n / (best * 1e-3) / 1e9, 1)
+    out["copy_how"] = ("1 GiB copy, 16-byte loads and stores, fastest of a few launch shapes "
+                       "(plain and non-temporal), read + write counted")
+    del a, b
+    return out
 
 
 def eager_pass(torch, ph, n):
@@ -616,21 +821,41 @@ def main():
     import synth
     import w4a4_mxfp4_gemm_amd as mx
 
-    make = {"decode": decode_workload, "prefill": prefill_workload, "moe": moe_workload,
-            "layerwise": layerwise_workload, "w4a8": w4a8_workload}[args.workload]
-    ph, report, cpu_baseline = make(torch, mx, synth)
+    headline = "prefill" if args.workload == "all" else args.workload
+    extras = [w for w in WORKLOADS if w != headline] if args.workload == "all" else []
     if args.eager:
+        ph, _, _ = WORKLOADS[headline](torch, mx, synth)
         eager_pass(torch, ph, args.eager)
         return
+
+    peaks = measure_peaks(torch) if args.workload == "all" else {}
+    say(f"measured peaks: {peaks}")
+    ph, report, cpu_baseline = WORKLOADS[headline](torch, mx, synth)
     ph.capture()
-    # the contract's timed region: exactly `steps` steps after `warmup` untimed ones
+    # the contract's timed region: exactly `steps` steps after `warmup` untimed ones,
+    # synchronised on both sides (one process, one GPU)
     t = {"step": ph.time("step", args.steps, args.warmup)}
     total_ms = t["step"] * args.steps
     reps = max(3, args.steps // max(1, ph.slots))
-    for name in ph.fns:
-        if name != "step":
-            t[name] = ph.time(name, reps, 1)
-    value, unit, roof, extra, cfg = report(t, args.steps)
+    t.update(ph.time_all(reps))
+    value, unit, roof, extra, cfg = report(t, peaks)
+    say(f"{headline}: {value:.1f} {unit}")
+    del ph
+    torch.cuda.synchronize()
+
+    more = {}
+    for name in extras:
+        wph, wreport, wcpu = WORKLOADS[name](torch, mx, synth)
+        wph.capture()
+        wt = {"step": wph.time("step", max(3, args.steps // 2), 2)}
+        wt.update(wph.time_all(max(2, args.steps // (2 * max(1, wph.slots)))))
+        more[name] = wreport(wt, peaks)
+        if wcpu is not None and not args.no_cpu_baseline:
+            more[name]["cpu_baseline"] = wcpu()
+        say(f"{name}: done")
+        del wph, wreport, wcpu
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
 
     out = {"metric": METRIC, "value": round(value, 4), "unit": unit, "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup,
@@ -638,8 +863,10 @@ def main():
            "scaling": "weak", "vs_baseline": None, "dtype": "mxfp4 (e2m1 x e8m0, fp32 acc)",
            "data": "synthetic (seeded; NVFP4 weights from bf16 N(0,0.02), bf16 activations "
                    "N(0,1) with 1% outlier channels x50)",
-           "config": cfg, "roofline": roof, **extra,
-           "kernel_source_digest": kernel_source_digest()}
+           "config": cfg, "roofline": roof, **extra, **more}
+    if peaks:
+        out["measured_peaks"] = peaks
+    out["kernel_source_digest"] = kernel_source_digest()
     if cpu_baseline is not None and not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)

@@ -116,6 +116,8 @@ def _load():
     lib.orc_bf16_from_double_array.argtypes = [P, I, P]
     lib.orc_num_threads.restype = ctypes.c_int
     lib.orc_num_threads.argtypes = []
+    lib.orc_set_num_threads.restype = None
+    lib.orc_set_num_threads.argtypes = [ctypes.c_int]
     _lib = lib
     return lib
 
@@ -130,6 +132,11 @@ def _c(a, dtype):
 
 def num_threads() -> int:
     return int(_load().orc_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """OpenMP threads for the oracle's loops from now on."""
+    _load().orc_set_num_threads(int(n))
 
 
 # ---- scalar codecs (for the pins) ----------------------------------------
@@ -281,6 +288,41 @@ def gemm_at(a_codes, a_scales, b_codes, b_scales, pm, pn):
     s = np.empty(pm.shape, dtype=np.float64)
     _load().orc_gemm_at(_ptr(a_codes), _ptr(a_scales), _ptr(b_codes), _ptr(b_scales),
                         M, N, K, _ptr(pm), _ptr(pn), pm.shape[0], _ptr(y), _ptr(s))
+    return y, s
+
+
+def mxfp4_dequant_f64(codes, scales) -> np.ndarray:
+    """MXFP4 codes [rows, K/2] + E8M0 [rows, K/32] -> fp64 values [rows, K]:
+    e2m1(code) * 2^(byte - 127), exact in fp64 (the E2M1 table is the C
+    oracle's own decode, R1 nibble order); byte 0xFF gives NaN."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    scales = np.asarray(scales, dtype=np.uint8)
+    rows, Kh = codes.shape
+    table = np.array([e2m1_value(c) for c in range(16)], dtype=np.float64)
+    v = np.empty((rows, 2 * Kh), dtype=np.float64)
+    v[:, 0::2] = table[codes & 15]
+    v[:, 1::2] = table[codes >> 4]
+    f = np.where(scales == 255, np.nan, np.ldexp(1.0, scales.astype(np.int64) - 127))
+    v *= np.repeat(f, 32, axis=1)
+    return v
+
+
+def gemm_blas(a_codes, a_scales, b_codes, b_scales, row_chunk=1024):
+    """R5's result through a library matmul, for sizes the exact oracle cannot
+    finish in seconds: both operands dequantized exactly to fp64, then
+    y = A B^T and s = |A| |B|^T by numpy's BLAS, in row chunks.  Every product
+    is exact; the fp64 sums carry an error of at most about K * 2^-53 * s
+    (against the 1e-5 * s parity bar).  Returns (y, s) like gemm."""
+    M = np.asarray(a_codes).shape[0]
+    B = mxfp4_dequant_f64(b_codes, b_scales)
+    Bt, Bat = np.ascontiguousarray(B.T), np.ascontiguousarray(np.abs(B).T)
+    del B
+    y = np.empty((M, Bt.shape[1]), dtype=np.float64)
+    s = np.empty_like(y)
+    for r0 in range(0, M, row_chunk):
+        A = mxfp4_dequant_f64(a_codes[r0:r0 + row_chunk], a_scales[r0:r0 + row_chunk])
+        np.matmul(A, Bt, out=y[r0:r0 + A.shape[0]])
+        np.matmul(np.abs(A), Bat, out=s[r0:r0 + A.shape[0]])
     return y, s
 
 

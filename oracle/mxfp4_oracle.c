@@ -640,6 +640,18 @@ void orc_bf16_from_double_array(const double* v, int64_t n, uint16_t* out)
         out[i] = orc_bf16_from_double(v[i]);
 }
 
+/* Threads the OpenMP loops use from now on (n >= 1); for timing the oracle
+   on one core beside all of them. */
+void orc_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 int orc_num_threads(void)
 {
 #ifdef _OPENMP

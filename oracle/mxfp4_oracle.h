@@ -206,6 +206,7 @@ void orc_add_row_bias(double* y, double* s, int64_t M, int64_t N, const uint16_t
 
 void orc_bf16_from_double_array(const double* v, int64_t n, uint16_t* out);
 int  orc_num_threads(void);
+void orc_set_num_threads(int n);
 
 #ifdef __cplusplus
 }

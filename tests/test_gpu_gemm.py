@@ -160,38 +160,6 @@ def test_gemm_decode_pipeline_full(mx, decode_weight, M):
     assert_gemm_fp32(yf, y, s, f"decode M={M} fp32")
 
 
-def sample_positions(M, N, seed, n_random=3000):
-    rng = np.random.default_rng(seed)
-    pm = [rng.integers(0, M, n_random)]
-    pn = [rng.integers(0, N, n_random)]
-    for m in (0, 1, 15, 16, 127, 128, 255, 256, M - 1):       # whole rows at tile edges
-        cols = np.unique(np.concatenate([np.arange(0, min(N, 300)), rng.integers(0, N, 200),
-                                         [N - 1]]))
-        pm.append(np.full(cols.size, m))
-        pn.append(cols)
-    return np.concatenate(pm), np.concatenate(pn)
-
-
-@pytest.mark.parametrize("N,K,wseed,xseed,oseed", [(4096, 4096, 21, 24, 26),
-                                                   (28672, 4096, 22, 24, 26),
-                                                   (4096, 14336, 23, 25, 27)])
-def test_gemm_prefill_pipeline_sampled(mx, N, K, wseed, xseed, oseed):
-    M = 4096
-    say(f"prefill pipeline M={M} N={N} K={K} (sampled outputs)")
-    nv, (oc, os_) = pipeline_weight(N, K, seed=wseed)
-    wc, ws = gpu_weight(mx, nv)
-    x = synth.activations(M, K, seed=xseed, outlier_seed=oseed)
-    xc, xs = mx.mxfp4_quantize_act(x.to(dev()))
-    yg = mx.mxfp4_gemm(xc, xs, wc, ws, out_dtype=torch.bfloat16)
-    ac, as_ = oracle.quantize_act(bf16_bits(x))
-    pm, pn = sample_positions(M, N, seed=N + K)
-    y, s = oracle.gemm_at(ac, as_, oc, os_, pm, pn)
-    got = bf16_bits(yg)[pm, pn]
-    ok = oracle.gemm_bf16_ok(got, y)
-    assert ok.all(), f"{int((~ok).sum())} of {ok.size} sampled outputs off by >1 bf16 ulp"
-    assert torch.isfinite(yg.float()).all()
-
-
 # ---- grouped GEMM -------------------------------------------------------------------
 def test_grouped_gemm_ragged_and_empty_experts(mx):
     say("grouped gemm ragged/empty experts")
@@ -305,68 +273,6 @@ def test_grouped_gemm_tiled_bad_offsets_stay_inside_y(mx):
             y, s = oracle.grouped_gemm(u8(a)[r0:r1], u8(sa)[r0:r1], u8(b).reshape(E, N, K // 2),
                                        u8(sb).reshape(E, N, K // 32), fixed - r0)
             assert_gemm_fp32(gy.view[r0:r1], y, s, f"bad table {table}")
-
-
-@pytest.fixture(scope="module")
-def moe_setup(mx):
-    """MoE layer: 128 experts, gate_up [2048,4096], down [4096,1024], 2048 tokens,
-    top-8 softmax routing.  Weights are generated, NVFP4-encoded and requantized
-    on the GPU; the oracle side rebuilds the sampled experts on the host."""
-    say("building MoE layer (128 experts)")
-    E, T, TOPK = 128, 2048, 8
-    d = dev()
-    perm, offsets = synth.route_topk(T, E, TOPK, seed=34)
-    tokens = synth.activations(T, 4096, seed=33)
-    down_in = synth.activations(T * TOPK, 1024, seed=35)
-    nv = {}
-    mxw = {}
-    for name, (N, K), seed in (("gate_up", (2048, 4096), 31), ("down", (4096, 1024), 32)):
-        codes = torch.empty((E, N, K // 2), dtype=torch.uint8, device=d)
-        scales = torch.empty((E, N, K // 16), dtype=torch.uint8, device=d)
-        gs = torch.empty((E,), dtype=torch.float32, device=d)
-        for e in range(E):
-            w = synth.bf16_normal((N, K), 0.02, seed=seed * 1000 + e, device=d)
-            c, s, g = synth.nvfp4_from_bf16(w)
-            codes[e], scales[e], gs[e] = c, s, g
-        nv[name] = (codes, scales, gs)
-        mxw[name] = mx.mxfp4_requant_from_nvfp4(codes, scales, gs)
-    torch.cuda.synchronize()
-    return dict(perm=perm, offsets=offsets, tokens=tokens, down_in=down_in, nv=nv, mxw=mxw)
-
-
-@pytest.mark.parametrize("which", ["gate_up", "down"])
-def test_grouped_gemm_moe_pipeline_sampled(mx, moe_setup, which):
-    say(f"MoE pipeline {which} (sampled experts)")
-    st = moe_setup
-    perm, offsets = st["perm"], st["offsets"]
-    codes, scales, gs = st["nv"][which]
-    wc, ws = st["mxw"][which]
-    E = codes.shape[0]
-    if which == "gate_up":
-        x, ri = st["tokens"], perm
-    else:
-        x, ri = st["down_in"], None
-    xc, xs = mx.mxfp4_quantize_act(x.to(dev()), row_index=None if ri is None else ri.to(dev()))
-    yg = mx.mxfp4_grouped_gemm(xc, xs, wc, ws, offsets.to(dev()), out_dtype=torch.bfloat16)
-    ybits = bf16_bits(yg)
-    ac, as_ = oracle.quantize_act(bf16_bits(x), row_index=None if ri is None else ri.numpy())
-    off = offsets.numpy()
-    rng = np.random.default_rng(7)
-    experts = sorted(set(rng.choice(E, 10, replace=False).tolist()) | {0, E - 1})
-    N = codes.shape[1]
-    for e in experts:
-        r0, r1 = int(off[e]), int(off[e + 1])
-        if r1 == r0:
-            continue
-        oc, os_ = oracle.requant(u8(codes[e]), u8(scales[e]), np.atleast_1d(u8(gs[e:e + 1])))
-        rows = np.unique(np.concatenate([[r0, r1 - 1], rng.integers(r0, r1, 4)]))
-        pm = np.repeat(rows - r0, N)
-        pn = np.tile(np.arange(N), rows.size)
-        y, _ = oracle.gemm_at(ac[r0:r1], as_[r0:r1], oc, os_, pm, pn)
-        got = ybits[np.repeat(rows, N), pn]
-        ok = oracle.gemm_bf16_ok(got, y)
-        assert ok.all(), f"{which} expert {e}: {int((~ok).sum())} outputs off by >1 bf16 ulp"
-    assert torch.isfinite(yg.float()).all()
 
 
 def test_graph_replay_matches_eager(mx):

@@ -612,6 +612,42 @@ def test_silu_mul_examples(row):
     assert np.array_equal(got, want)
 
 
+# ---- R5 through BLAS, for full-size parity ----------------------------------------
+@pytest.mark.parametrize("M,N,K,lo,hi", [(7, 9, 64, 100, 150), (33, 40, 1024, 0, 254),
+                                         (64, 17, 4096, 117, 137)])
+def test_gemm_blas_matches_the_exact_gemm(M, N, K, lo, hi):
+    """The fp64 dequantize + numpy matmul form of the GEMM agrees with the
+    exact integer-sum oracle to within K * 2^-52 * s, over random codes and
+    scale bytes (the whole E8M0 range in one case), whole or in row chunks."""
+    rng = np.random.default_rng(M + N + K)
+    ac = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
+    bc = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    as_ = rng.integers(lo, hi + 1, (M, K // 32), dtype=np.uint8)
+    bs = rng.integers(lo, hi + 1, (N, K // 32), dtype=np.uint8)
+    y, s = oracle.gemm(ac, as_, bc, bs)
+    yb, sb = oracle.gemm_blas(ac, as_, bc, bs)
+    fin = np.isfinite(s)
+    assert np.array_equal(fin, np.isfinite(sb))
+    assert (np.abs(yb - y)[fin] <= K * 2.0 ** -52 * s[fin]).all()
+    assert (np.abs(sb - s)[fin] <= K * 2.0 ** -52 * s[fin]).all()
+    yc, _ = oracle.gemm_blas(ac, as_, bc, bs, row_chunk=5)    # BLAS may reorder the sums
+    assert (np.abs(yc - y)[fin] <= K * 2.0 ** -52 * s[fin]).all()
+
+
+def test_gemm_blas_nan_scale_and_decode():
+    """Scale byte 0xFF makes its row's results NaN; the dequantized operand is
+    the E2M1 value times 2^(byte-127), nibble order R1."""
+    ac = np.array([[0x21, 0x00] * 8, [0x7F, 0xF7] * 8], dtype=np.uint8)
+    v = oracle.mxfp4_dequant_f64(ac, np.array([[127], [130]], dtype=np.uint8))
+    assert v[0, 0] == 0.5 and v[0, 1] == 1.0 and v[0, 2] == 0.0
+    assert v[1, 0] == -6 * 8 and v[1, 1] == 6 * 8 and v[1, 2] == 6 * 8 and v[1, 3] == -6 * 8
+    bc = np.full((3, 16), 0x22, dtype=np.uint8)
+    y, _ = oracle.gemm_blas(ac, np.array([[127], [255]], dtype=np.uint8), bc,
+                            np.full((3, 1), 127, dtype=np.uint8))
+    assert np.isfinite(y[0]).all() and np.isnan(y[1]).all()
+    assert y[0, 0] == 8 * (0.5 * 1 + 1 * 1)
+
+
 # ---- R11: top-k combine --------------------------------------------------------
 def combine_case(seed, T=12, topk=8, H=40, R=None):
     rng = np.random.default_rng(seed)
