@@ -211,17 +211,33 @@ def grouped_case(mx, counts, N, K, seed, out_dtype):
     return gy.view, y, s
 
 
-def test_grouped_gemm_tiled_row_blocks(mx):
+@pytest.mark.parametrize("K", [1024, 1536, 3072])
+def test_grouped_gemm_tiled_row_blocks(mx, K):
     """Expert sizes that end in each 32-row block of a 128-row tile, span
     several tiles, or are empty; N with a partial 256-row weight tile.  The
     bf16 output is the RNE of the same fp32 accumulator (random scales make
-    cancellation common, so the oracle bound is the fp32 one)."""
+    cancellation common, so the oracle bound is the fp32 one).  K = 1024 and
+    3072 take the kernel with the weights streamed into registers (an item
+    of 4 stages, and of 12: its steady loop), K = 1536 the one that stages
+    them in LDS."""
     counts = [0, 1, 31, 32, 33, 97, 128, 129, 257, 300, 0]
-    say(f"grouped tiled row blocks counts={counts} N=300 K=1024")
-    gy, y, s = grouped_case(mx, counts, 300, 1024, 51, torch.float32)
+    say(f"grouped tiled row blocks counts={counts} N=300 K={K}")
+    gy, y, s = grouped_case(mx, counts, 300, K, 51, torch.float32)
     assert_gemm_fp32(gy, y, s, "grouped tiled")
-    yb, _, _ = grouped_case(mx, counts, 300, 1024, 51, torch.bfloat16)
+    yb, _, _ = grouped_case(mx, counts, 300, K, 51, torch.bfloat16)
     assert np.array_equal(bf16_bits(yb), bf16_bits(gy.to(torch.bfloat16)))
+
+
+def test_grouped_gemm_stream_many_items(mx):
+    """More work items than workgroups (480 items of 4 stages over 96 experts),
+    so the workgroups walk several: each item's first stages arrive during
+    the previous item, whose row count (32-row blocks 1..4) may differ."""
+    rng = np.random.default_rng(17)
+    counts = rng.integers(0, 160, size=96)
+    counts[rng.random(96) < 0.15] = 0
+    say(f"grouped stream many items total {counts.sum()} N=1280 K=1024")
+    gy, y, s = grouped_case(mx, counts, 1280, 1024, 81, torch.float32)
+    assert_gemm_fp32(gy, y, s, "grouped stream many items")
 
 
 def test_grouped_gemm_tiled_many_small_experts(mx):
@@ -249,9 +265,10 @@ def test_grouped_gemm_tiled_more_than_256_experts(mx):
         assert_gemm_fp32(gy, y, s, f"grouped tiled 300 experts K={K}")
 
 
-def test_grouped_gemm_tiled_bad_offsets_stay_inside_y(mx):
-    say("grouped tiled gemm malformed offsets")
-    E, N, K, M = 4, 256, 512, 300
+@pytest.mark.parametrize("K", [512, 1024])
+def test_grouped_gemm_tiled_bad_offsets_stay_inside_y(mx, K):
+    say(f"grouped tiled gemm malformed offsets K={K}")
+    E, N, M = 4, 256, 300
     a, sa = synth.canonical_mxfp4(M, K, seed=13)
     b, sb = synth.canonical_mxfp4(E * N, K, seed=14)
     A, SA, B, SB = to_dev(a, sa, b.reshape(E, N, K // 2), sb.reshape(E, N, K // 32))

@@ -1171,6 +1171,371 @@ __global__ __launch_bounds__(256, 1) void grouped_tiled_kernel(
     wait_vm<0>();
 }
 
+// ---------------------------------------------------------------------------
+// Grouped (MoE) GEMM with the weights streamed into registers.  At ~128 rows
+// an expert the grouped GEMM is bound by the weight stream, and staging the
+// weights through LDS caps it: the LDS holds only two stages, so too few
+// bytes are in flight.  In the 128 x 256 grouped tile every weight row is
+// used by one wavefront only (waves 1 x 4, each 128 activation rows x 64
+// weight rows), so it needs no sharing: here each wave loads its own 64
+// weight rows straight into registers in the MFMA's operand layout, four
+// stages ahead, and only the activation tile, which all four waves read,
+// goes through LDS (LDS-DMA, a ring of four stage buffers).
+//
+// Stage g of a wave's walk (K stage = 256 elements; stages are numbered
+// across the wave's items, and an item has a multiple of 4, so g % 4 is
+// static in the unrolled loop and names the stage's weight set and LDS
+// buffer).  Entering it, the wave holds K-step 0's activation fragments.
+//   K-step 0: read K-step 1's fragments; its MFMAs
+//   K-step 1: read K-step 2's; MFMAs
+//   wait until stage g+1's activations landed; barrier; DMA stage g+3's
+//             activation codes and scales into the buffer of stage g-1
+//   K-step 2: read K-step 3's; MFMAs
+//   K-step 3: read stage g+1's K-step 0 fragments and scale words; MFMAs
+//   load weight set g % 4 with stage g+4 (codes, then scale words)
+// Each stage issues 10 weight loads (ordinary buffer loads: the compiler
+// places their waits) and 5 activation DMA loads (inline assembly, waited
+// for explicitly).  Vector memory loads complete in issue order, so at the
+// wait in stage g, "stage g+1's activations (issued in stage g-2) landed" is
+// "at most 10 + 15 = 25 loads outstanding": the weight loads that followed
+// them in stage g-2 and the 15 loads of stage g-1.
+// The next item's first stages are loaded during the current item's last
+// ones; the last item loads its own first stages again (surplus, drained at
+// the end) so that every stage issues the same loads.
+// ---------------------------------------------------------------------------
+namespace rs {
+
+constexpr int XBUF = 128 * BKB;               // a stage's activation codes: 128 rows x 128 B
+constexpr int NBUF = 4;
+constexpr int RING = NBUF * XBUF;             // 64 KiB
+// The scale bytes of a group of four stages, 32 a row (8 a stage): the 256
+// weight rows, then the 128 activation rows.  Two groups' buffers.
+constexpr int SCW = 256 * 32;
+constexpr int SC = SCW + 128 * 32;            // 12 KiB
+constexpr int SCB = RING;
+constexpr int LDS_END = SCB + 2 * SC;         // 88 KiB
+
+// The wait in stage U of a group: 20 loads were issued after stage g+1's
+// activations, 23 when the group's first stage (which also loads the next
+// group's scales) is among the two stages before.
+template <int U>
+constexpr int wait_x() {
+    return 20 + (U == 1 || U == 2 ? 3 : 0);
+}
+
+// One stage of one wave's weight codes: blocks i (32 rows), K-steps t.
+struct WSet {
+    v4u c[2][4];
+};
+
+// Per-lane offsets, the same for every item and stage.
+struct Offs {
+    uint32_t w[2];              // weight code loads of blocks i (+ 16 t)
+    uint32_t x[4];              // activation code DMA
+    uint32_t sw[2], sx;         // scale DMA: the wave's weight rows (two loads), activation rows
+    uint32_t rx[4];             // LDS reads: code chunk of K-step t
+    uint32_t rsw, rsx;          // LDS reads: scale words of weight / activation block 0
+};
+
+__device__ __forceinline__ Offs offsets(int64_t K, int wave) {
+    const int lane = threadIdx.x & 63;
+    const int r32 = lane & 31, h = lane >> 5;
+    const uint32_t ldc = (uint32_t)(K / 2), lds_ = (uint32_t)(K / 32);
+    Offs o;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) o.w[i] = (uint32_t)(64 * wave + 32 * i + r32) * ldc + 64 * h;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int row = (wave * 4 + q) * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ ((row >> 1) & 7);
+        o.x[q] = (uint32_t)row * ldc + 16 * c;
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+        o.sw[q] = (uint32_t)(64 * wave + 32 * q + (lane >> 1)) * lds_ + 16 * (lane & 1);
+    o.sx = (uint32_t)(32 * wave + (lane >> 1)) * lds_ + 16 * (lane & 1);
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+        o.rx[t] = (uint32_t)(r32 * BKB + 16 * ((4 * h + t) ^ ((r32 >> 1) & 7)));
+    o.rsw = (uint32_t)((64 * wave + r32) * 32 + 4 * h);
+    o.rsx = (uint32_t)(SCW + r32 * 32 + 4 * h);
+    return o;
+}
+
+// Where an item's operands come from, each starting at the item's first row
+// (rows past N, or past the expert's last row, read 0): the weight codes as
+// a buffer resource for ordinary loads, the rest as raw descriptors for the
+// DMA.
+struct Src {
+    __amdgpu_buffer_rsrc_t w;
+    v4i ws, x, xs;
+};
+
+__device__ __forceinline__ Src item_src(const GroupItem& it, const uint8_t* x, const uint8_t* xs,
+                                        const uint8_t* w, const uint8_t* ws, int64_t N,
+                                        int64_t K) {
+    const int64_t ldc = K / 2, lds_ = K / 32;
+    const int64_t n0 = (int64_t)it.tn * 256;
+    const int64_t rows_w = N > n0 ? N - n0 : 0;
+    const int64_t rows_x = it.m_end > it.m0 ? it.m_end - it.m0 : 0;
+    const int64_t wrow = (int64_t)it.e * N + n0;
+    Src s;
+    s.w = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(w + wrow * ldc), (short)0,
+                                            (int)(rows_w * ldc), 0x00020000);
+    s.ws = make_rsrc(ws + wrow * lds_, (uint32_t)(rows_w * lds_));
+    s.x = make_rsrc(x + (int64_t)it.m0 * ldc, (uint32_t)(rows_x * ldc));
+    s.xs = make_rsrc(xs + (int64_t)it.m0 * lds_, (uint32_t)(rows_x * lds_));
+    return s;
+}
+
+// Stage kt's activation codes of the item `s` into ring buffer B.
+template <int B>
+__device__ __forceinline__ void load_x(lds_u8* lds, const Src& s, const Offs& o, int wave,
+                                       int kt) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        dma16(s.x, lds + B * XBUF + (wave * 4 + q) * 1024, o.x[q], (uint32_t)kt * BKB);
+}
+
+// The scales of stages 4 grp .. 4 grp + 3 into scale buffer `par`: each wave
+// its own 64 weight rows and 32 of the activation rows, two lanes a row.
+__device__ __forceinline__ void load_sc(lds_u8* lds, int par, const Src& s, const Offs& o,
+                                        int wave, int grp) {
+    lds_u8* b = lds + SCB + par * SC;
+    const uint32_t k = (uint32_t)grp * 32;
+    dma16(s.ws, b + (2 * wave) * 1024, o.sw[0], k);
+    dma16(s.ws, b + (2 * wave + 1) * 1024, o.sw[1], k);
+    dma16(s.xs, b + SCW + wave * 1024, o.sx, k);
+}
+
+// Stage kt's weight codes into a set: each 32-row block's four K-step
+// registers back to back, so each row's 128-byte line is still in L1 for
+// the three loads after the first.
+__device__ __forceinline__ void load_w(WSet& w, const Src& s, const Offs& o, int kt) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            w.c[i][t] = __builtin_bit_cast(
+                v4u,
+                __builtin_amdgcn_raw_buffer_load_b128(s.w, (int)(o.w[i] + 16 * t), kt * BKB, 0));
+}
+
+// K-step T's activation fragments of the stage in ring buffer B (all four
+// 32-row blocks).
+struct XFrag {
+    v4u x[4];
+};
+template <int B, int T>
+__device__ __forceinline__ void read_x(XFrag& f, uint32_t lds0, const Offs& o) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        f.x[j] = *reinterpret_cast<lds_v4u*>((uintptr_t)(lds0 + B * XBUF + j * 32 * BKB + o.rx[T]));
+}
+// Stage S (of its group, in the scale buffer at `sbase`): the scale words
+// of the wave's two weight blocks and of the four activation blocks.
+template <int S>
+__device__ __forceinline__ void read_scales(uint32_t (&wsc)[2], uint32_t (&sc)[4], uint32_t sbase,
+                                            const Offs& o) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+        wsc[i] = *reinterpret_cast<lds_u32*>((uintptr_t)(sbase + o.rsw + i * 32 * 32 + 8 * S));
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        sc[j] = *reinterpret_cast<lds_u32*>((uintptr_t)(sbase + o.rsx + j * 32 * 32 + 8 * S));
+}
+
+// The MFMAs of K-step T on the activation blocks that hold rows (j < jl,
+// uniform: the blocks past an expert's last row are skipped).
+template <int T>
+__device__ __forceinline__ void mfma_k(v16f (&acc)[2][4], const WSet& w, const XFrag& f,
+                                       const uint32_t (&wsc)[2], const uint32_t (&sc)[4], int jl) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if (j == 0 || jl > j) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                acc[i][j] = mfma<T>(w.c[i][T], f.x[j], acc[i][j], wsc[i], sc[j]);
+        }
+    }
+}
+
+// Pipeline registers of a wave: the four weight sets, two K-steps of
+// activation fragments, the scale words of the stage the MFMAs use.
+struct Pipe {
+    WSet w[4];
+    XFrag f[2];
+    uint32_t wsc[2], sc[4];
+};
+
+// Stage kt = 4q + U of item `cur`, in the group whose scales are in buffer
+// `par`.  It loads stage kt+3's activations and stage kt+4's weights (and,
+// in a group's first stage, the next group's scales); in an item's last
+// four stages (LAST) those belong to the next item.  On entry f[0] holds
+// K-step 0's fragments; each K-step reads the next one's into the other
+// slot (K-step 3: stage kt+1's K-step 0, and its scale words).
+template <int U, bool LAST>
+__device__ __forceinline__ void stage(lds_u8* lds, uint32_t lds0, const Src& cur, const Src& nxt,
+                                      const Offs& o, int wave, int kt, int jl, int par, Pipe& p,
+                                      v16f (&acc)[2][4]) {
+    constexpr bool X_NEXT = LAST && U >= 1;
+    const Src& sw = LAST ? nxt : cur;
+    const Src& sx = X_NEXT ? nxt : cur;
+    const int kw = LAST ? U : kt + 4;
+    const int kx = X_NEXT ? U - 1 : kt + 3;
+    WSet& w = p.w[U];
+    // jl is the same for the whole item; made opaque here so that the
+    // compiler neither versions the loop on it nor moves one block's MFMAs
+    // out of their stage (either keeps every weight set alive far longer)
+    asm volatile("" : "+s"(jl));
+    read_x<U, 1>(p.f[1], lds0, o);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_k<0>(acc, w, p.f[0], p.wsc, p.sc, jl);
+    read_x<U, 2>(p.f[0], lds0, o);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_k<1>(acc, w, p.f[1], p.wsc, p.sc, jl);
+    // stage kt+1's activations (and, in the group's last stage, the next
+    // group's scales) landed in every wave; every wave is done with the
+    // buffers about to be reloaded
+    wait_vm<wait_x<U>()>();
+    __builtin_amdgcn_s_barrier();
+    load_x<(U + 3) % 4>(lds, sx, o, wave, kx);
+    if constexpr (U == 0) load_sc(lds, par ^ 1, sw, o, wave, LAST ? 0 : kt / 4 + 1);
+    read_x<U, 3>(p.f[1], lds0, o);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_k<2>(acc, w, p.f[0], p.wsc, p.sc, jl);
+    uint32_t wsc_next[2], sc_next[4];
+    read_x<(U + 1) % 4, 0>(p.f[0], lds0, o);
+    read_scales<(U + 1) % 4>(wsc_next, sc_next,
+                             lds0 + SCB + (uint32_t)((U == 3 ? par ^ 1 : par) * SC), o);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_k<3>(acc, w, p.f[1], p.wsc, p.sc, jl);
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(w, sw, o, kw);                     // the set's registers are free
+#pragma unroll
+    for (int i = 0; i < 2; ++i) p.wsc[i] = wsc_next[i];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) p.sc[j] = sc_next[j];
+    // this stage's MFMAs complete their chains here
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) asm volatile("" : "+a"(acc[i][j]));
+}
+
+// All stages of item `cur`; par: the scale buffer of its first group
+// (toggled per group).
+__device__ __forceinline__ void item_stages(lds_u8* lds, uint32_t lds0, const Src& cur,
+                                            const Src& nxt, const Offs& o, int wave, int nkt,
+                                            int jl, int& par, Pipe& p, v16f (&acc)[2][4]) {
+    int kt = 0;
+    for (; kt < nkt - 4; kt += 4) {
+        stage<0, false>(lds, lds0, cur, nxt, o, wave, kt, jl, par, p, acc);
+        stage<1, false>(lds, lds0, cur, nxt, o, wave, kt + 1, jl, par, p, acc);
+        stage<2, false>(lds, lds0, cur, nxt, o, wave, kt + 2, jl, par, p, acc);
+        stage<3, false>(lds, lds0, cur, nxt, o, wave, kt + 3, jl, par, p, acc);
+        par ^= 1;
+    }
+    stage<0, true>(lds, lds0, cur, nxt, o, wave, kt, jl, par, p, acc);
+    stage<1, true>(lds, lds0, cur, nxt, o, wave, kt + 1, jl, par, p, acc);
+    stage<2, true>(lds, lds0, cur, nxt, o, wave, kt + 2, jl, par, p, acc);
+    stage<3, true>(lds, lds0, cur, nxt, o, wave, kt + 3, jl, par, p, acc);
+    par ^= 1;
+}
+
+// The first item's loads in the order the stages issue them (as if stages
+// -4..-1 had run, the first group's scales ahead of them), then its stage
+// 0's first fragments and scale words.
+__device__ __forceinline__ void prologue(lds_u8* lds, uint32_t lds0, const Src& s, const Offs& o,
+                                         int wave, Pipe& p) {
+    load_sc(lds, 0, s, o, wave, 0);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        if (g == 1) load_x<0>(lds, s, o, wave, 0);
+        if (g == 2) load_x<1>(lds, s, o, wave, 1);
+        if (g == 3) load_x<2>(lds, s, o, wave, 2);
+        load_w(p.w[g], s, o, g);
+    }
+    // stage 0's activations: 8 + 12 + 12 = 32 loads were issued after them
+    wait_vm<32>();
+    __builtin_amdgcn_s_barrier();
+    read_x<0, 0>(p.f[0], lds0, o);
+    read_scales<0>(p.wsc, p.sc, lds0 + SCB, o);
+}
+
+}  // namespace rs
+
+// K % 1024 == 0 (stages of an item a multiple of 4).
+template <bool OUT_BF16, bool GLU = false, bool UOS = false>
+__global__ __launch_bounds__(256, 1) void grouped_stream_kernel(
+    const uint8_t* __restrict__ x, const uint8_t* __restrict__ xs,
+    const uint8_t* __restrict__ w, const uint8_t* __restrict__ ws,
+    const int32_t* __restrict__ offsets, int E, int total_M, int64_t N, int64_t K,
+    void* __restrict__ y, uint8_t* __restrict__ hs) {
+    static_assert(!GLU || OUT_BF16, "the GLU epilogue parks bf16");
+    using S = GroupShape;                       // the accumulator and epilogue layout
+    using T = Stage<S, OUT_BF16>;
+    constexpr int TABLE = rs::LDS_END;
+    constexpr int STAGE_BASE = (TABLE + GROUP_TABLE_BYTES + 15) / 16 * 16;
+    constexpr int ROWS = T::rows_for((LDS_LIMIT - STAGE_BASE) / 4);
+    static_assert(STAGE_BASE + 4 * T::bytes(ROWS) <= LDS_LIMIT, "LDS budget");
+    __shared__ __attribute__((aligned(16))) uint8_t smem[STAGE_BASE + 4 * T::bytes(ROWS)];
+    lds_u8* lds = (lds_u8*)smem;
+    const uint32_t lds0 = lds_addr(lds);
+    int* table = reinterpret_cast<int*>(smem + TABLE);
+    const GroupTable tb{table, table + GROUP_MAX_E + 1, table + 2 * GROUP_MAX_E + 1};
+    const int tiles_n = (int)((N + S::BN - 1) / S::BN);
+    if (threadIdx.x < 64) build_table<S::BM>(offsets, E, total_M, tiles_n, tb);
+    __syncthreads();
+
+    const int total = __builtin_amdgcn_readfirstlane(tb.first[E]);
+    const int per_xcd = (total + 7) / 8;
+    const int stride = (int)gridDim.x / 8;
+    const int t_end = min((int)(blockIdx.x % 8) * per_xcd + per_xcd, total);
+    int t = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+    if (t >= t_end) return;
+
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nkt = (int)(K / 256);             // a multiple of 4
+    const rs::Offs o = rs::offsets(K, wave);
+    GroupItem it = decode_item<S::BM>(tb, E, tiles_n, t, 0);
+    if (it.e < 0) return;
+    rs::Src cur = rs::item_src(it, x, xs, w, ws, N, K);
+    v16f acc[2][4];
+    zero_acc<S>(acc);
+    rs::Pipe p;
+    rs::prologue(lds, lds0, cur, o, wave, p);
+    int par = 0;
+    for (;;) {
+        const int tn = t + stride;
+        GroupItem nx = it;
+        bool have_next = tn < t_end;
+        if (have_next) {
+            nx = decode_item<S::BM>(tb, E, tiles_n, tn, it.e);
+            have_next = nx.e >= 0;
+            if (!have_next) nx = it;
+        }
+        const rs::Src nxt = rs::item_src(nx, x, xs, w, ws, N, K);
+        rs::item_stages(lds, lds0, cur, nxt, o, wave, nkt, it.jl, par, p, acc);
+        // keep the loads in flight plus the epilogue's stores within the
+        // 6-bit load counter
+        wait_vm<24>();
+        if constexpr (GLU)
+            store_tile_glu<S, ROWS, UOS>(acc, lds + STAGE_BASE + wave * T::bytes(ROWS),
+                                         static_cast<uint8_t*>(y), hs, it.m0, it.m_end,
+                                         (int64_t)it.tn * S::BN, N, wave, 0);
+        else
+            store_tile<S, OUT_BF16, ROWS>(acc, lds + STAGE_BASE + wave * T::bytes(ROWS), y,
+                                          it.m0, it.m_end, (int64_t)it.tn * S::BN, N, wave, 0);
+        if (!have_next) break;
+        rezero_acc<S>(acc);
+        it = nx;
+        cur = nxt;
+        t = tn;
+    }
+    wait_vm<0>();                               // the surplus loads, before the LDS is released
+}
+
 }  // namespace tiled
 
 // Buffer offsets are 32-bit: every operand must span less than 2 GiB.
@@ -1299,6 +1664,9 @@ hipError_t launch_gemm_tiled_w4a8(const uint8_t* a_codes, const uint8_t* a_scale
     return hipGetLastError();
 }
 
+// The register-streamed grouped kernel walks an item's stages four at a time.
+static bool grouped_stream_ok(int64_t K) { return K % 1024 == 0; }
+
 // One persistent workgroup per CU (the tile's LDS allows no more), never
 // more workgroups than the largest possible number of work items.
 static hipError_t grouped_grid(int64_t E, int64_t total_M, int64_t N, dim3& grid) {
@@ -1324,14 +1692,14 @@ hipError_t launch_grouped_gemm_tiled(const uint8_t* a_codes, const uint8_t* a_sc
     const hipError_t e = grouped_grid(E, total_M, N, grid);
     if (e != hipSuccess) return e;
     uint8_t* const none = nullptr;
-    if (out_bf16)
-        hipLaunchKernelGGL(tiled::grouped_tiled_kernel<true>, grid, dim3(256), 0, stream,
-                           a_codes, a_scales, b_codes, b_scales, offsets, (int)E, (int)total_M, N,
-                           K, y, none);
+    auto go = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, a_codes, a_scales, b_codes,
+                           b_scales, offsets, (int)E, (int)total_M, N, K, y, none);
+    };
+    if (grouped_stream_ok(K))
+        out_bf16 ? go(tiled::grouped_stream_kernel<true>) : go(tiled::grouped_stream_kernel<false>);
     else
-        hipLaunchKernelGGL(tiled::grouped_tiled_kernel<false>, grid, dim3(256), 0, stream,
-                           a_codes, a_scales, b_codes, b_scales, offsets, (int)E, (int)total_M, N,
-                           K, y, none);
+        out_bf16 ? go(tiled::grouped_tiled_kernel<true>) : go(tiled::grouped_tiled_kernel<false>);
     return hipGetLastError();
 }
 
@@ -1348,14 +1716,17 @@ hipError_t launch_grouped_glu_quant(const uint8_t* a_codes, const uint8_t* a_sca
     dim3 grid;
     const hipError_t e = grouped_grid(E, total_M, N, grid);
     if (e != hipSuccess) return e;
-    if (uos)
-        hipLaunchKernelGGL((tiled::grouped_tiled_kernel<true, true, true>), grid, dim3(256), 0,
-                           stream, a_codes, a_scales, b_codes, b_scales, offsets, (int)E,
-                           (int)total_M, N, K, static_cast<void*>(h_codes), h_scales);
+    auto go = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, a_codes, a_scales, b_codes,
+                           b_scales, offsets, (int)E, (int)total_M, N, K,
+                           static_cast<void*>(h_codes), h_scales);
+    };
+    if (grouped_stream_ok(K))
+        uos ? go(tiled::grouped_stream_kernel<true, true, true>)
+            : go(tiled::grouped_stream_kernel<true, true, false>);
     else
-        hipLaunchKernelGGL((tiled::grouped_tiled_kernel<true, true, false>), grid, dim3(256), 0,
-                           stream, a_codes, a_scales, b_codes, b_scales, offsets, (int)E,
-                           (int)total_M, N, K, static_cast<void*>(h_codes), h_scales);
+        uos ? go(tiled::grouped_tiled_kernel<true, true, true>)
+            : go(tiled::grouped_tiled_kernel<true, true, false>);
     return hipGetLastError();
 }
 
