@@ -1205,15 +1205,21 @@ __global__ __launch_bounds__(256, 1) void grouped_tiled_kernel(
 // ---------------------------------------------------------------------------
 namespace rs {
 
+// The activation ring: four stage buffers, each a __shared__ array of its
+// own, always named statically (the stage's position in its group of four),
+// so the compiler can tell which buffer a DMA writes and which one an LDS
+// read reads, and counts the DMA loads in the waits it places for the
+// weight registers instead of draining them before every read.
 constexpr int XBUF = 128 * BKB;               // a stage's activation codes: 128 rows x 128 B
-constexpr int NBUF = 4;
-constexpr int RING = NBUF * XBUF;             // 64 KiB
+struct Ring {
+    lds_u8* b[4];
+};
 // The scale bytes of a group of four stages, 32 a row (8 a stage): the 256
-// weight rows, then the 128 activation rows.  Two groups' buffers.
+// weight rows, then the 128 activation rows.  Two groups' buffers, at the
+// start of the kernel's other LDS array.
 constexpr int SCW = 256 * 32;
 constexpr int SC = SCW + 128 * 32;            // 12 KiB
-constexpr int SCB = RING;
-constexpr int LDS_END = SCB + 2 * SC;         // 88 KiB
+constexpr int LDS_END = 2 * SC;               // 24 KiB
 
 // The wait in stage U of a group: 20 loads were issued after stage g+1's
 // activations, 23 when the group's first stage (which also loads the next
@@ -1228,7 +1234,9 @@ struct WSet {
     v4u c[2][4];
 };
 
-// Per-lane offsets, the same for every item and stage.
+// Per-lane offsets, the same for every item and stage.  As in the LDS-staged
+// kernels, lane half h takes MX blocks 4h..4h+3 of a stage, one per K-step,
+// so its 4 scale bytes of a stage are one 32-bit word.
 struct Offs {
     uint32_t w[2];              // weight code loads of blocks i (+ 16 t)
     uint32_t x[4];              // activation code DMA
@@ -1267,8 +1275,8 @@ __device__ __forceinline__ Offs offsets(int64_t K, int wave) {
 // a buffer resource for ordinary loads, the rest as raw descriptors for the
 // DMA.
 struct Src {
-    __amdgpu_buffer_rsrc_t w;
-    v4i ws, x, xs;
+    __amdgpu_buffer_rsrc_t w, x;
+    v4i ws, xs;
 };
 
 __device__ __forceinline__ Src item_src(const GroupItem& it, const uint8_t* x, const uint8_t* xs,
@@ -1283,25 +1291,28 @@ __device__ __forceinline__ Src item_src(const GroupItem& it, const uint8_t* x, c
     s.w = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(w + wrow * ldc), (short)0,
                                             (int)(rows_w * ldc), 0x00020000);
     s.ws = make_rsrc(ws + wrow * lds_, (uint32_t)(rows_w * lds_));
-    s.x = make_rsrc(x + (int64_t)it.m0 * ldc, (uint32_t)(rows_x * ldc));
+    s.x = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(x + (int64_t)it.m0 * ldc),
+                                            (short)0, (int)(rows_x * ldc), 0x00020000);
     s.xs = make_rsrc(xs + (int64_t)it.m0 * lds_, (uint32_t)(rows_x * lds_));
     return s;
 }
 
 // Stage kt's activation codes of the item `s` into ring buffer B.
 template <int B>
-__device__ __forceinline__ void load_x(lds_u8* lds, const Src& s, const Offs& o, int wave,
+__device__ __forceinline__ void load_x(const Ring& ring, const Src& s, const Offs& o, int wave,
                                        int kt) {
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-        dma16(s.x, lds + B * XBUF + (wave * 4 + q) * 1024, o.x[q], (uint32_t)kt * BKB);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            s.x, (__attribute__((address_space(3))) void*)(ring.b[B] + (wave * 4 + q) * 1024), 16,
+            (int)o.x[q], kt * BKB, 0, 0);
 }
 
 // The scales of stages 4 grp .. 4 grp + 3 into scale buffer `par`: each wave
 // its own 64 weight rows and 32 of the activation rows, two lanes a row.
 __device__ __forceinline__ void load_sc(lds_u8* lds, int par, const Src& s, const Offs& o,
                                         int wave, int grp) {
-    lds_u8* b = lds + SCB + par * SC;
+    lds_u8* b = lds + par * SC;
     const uint32_t k = (uint32_t)grp * 32;
     dma16(s.ws, b + (2 * wave) * 1024, o.sw[0], k);
     dma16(s.ws, b + (2 * wave + 1) * 1024, o.sw[1], k);
@@ -1327,22 +1338,22 @@ struct XFrag {
     v4u x[4];
 };
 template <int B, int T>
-__device__ __forceinline__ void read_x(XFrag& f, uint32_t lds0, const Offs& o) {
+__device__ __forceinline__ void read_x(XFrag& f, const Ring& ring, const Offs& o) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-        f.x[j] = *reinterpret_cast<lds_v4u*>((uintptr_t)(lds0 + B * XBUF + j * 32 * BKB + o.rx[T]));
+        f.x[j] = *reinterpret_cast<lds_v4u*>(ring.b[B] + o.rx[T] + j * 32 * BKB);
 }
-// Stage S (of its group, in the scale buffer at `sbase`): the scale words
-// of the wave's two weight blocks and of the four activation blocks.
+// Stage S (of its group, in scale buffer `sb`): the scale words of the
+// wave's two weight blocks and of the four activation blocks.
 template <int S>
-__device__ __forceinline__ void read_scales(uint32_t (&wsc)[2], uint32_t (&sc)[4], uint32_t sbase,
+__device__ __forceinline__ void read_scales(uint32_t (&wsc)[2], uint32_t (&sc)[4], const lds_u8* sb,
                                             const Offs& o) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
-        wsc[i] = *reinterpret_cast<lds_u32*>((uintptr_t)(sbase + o.rsw + i * 32 * 32 + 8 * S));
+        wsc[i] = *reinterpret_cast<lds_u32*>(sb + o.rsw + i * 32 * 32 + 8 * S);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-        sc[j] = *reinterpret_cast<lds_u32*>((uintptr_t)(sbase + o.rsx + j * 32 * 32 + 8 * S));
+        sc[j] = *reinterpret_cast<lds_u32*>(sb + o.rsx + j * 32 * 32 + 8 * S);
 }
 
 // The MFMAs of K-step T on the activation blocks that hold rows (j < jl,
@@ -1375,7 +1386,7 @@ struct Pipe {
 // K-step 0's fragments; each K-step reads the next one's into the other
 // slot (K-step 3: stage kt+1's K-step 0, and its scale words).
 template <int U, bool LAST>
-__device__ __forceinline__ void stage(lds_u8* lds, uint32_t lds0, const Src& cur, const Src& nxt,
+__device__ __forceinline__ void stage(lds_u8* lds, const Ring& ring, const Src& cur, const Src& nxt,
                                       const Offs& o, int wave, int kt, int jl, int par, Pipe& p,
                                       v16f (&acc)[2][4]) {
     constexpr bool X_NEXT = LAST && U >= 1;
@@ -1388,10 +1399,10 @@ __device__ __forceinline__ void stage(lds_u8* lds, uint32_t lds0, const Src& cur
     // compiler neither versions the loop on it nor moves one block's MFMAs
     // out of their stage (either keeps every weight set alive far longer)
     asm volatile("" : "+s"(jl));
-    read_x<U, 1>(p.f[1], lds0, o);
+    read_x<U, 1>(p.f[1], ring, o);
     __builtin_amdgcn_sched_barrier(0);
     mfma_k<0>(acc, w, p.f[0], p.wsc, p.sc, jl);
-    read_x<U, 2>(p.f[0], lds0, o);
+    read_x<U, 2>(p.f[0], ring, o);
     __builtin_amdgcn_sched_barrier(0);
     mfma_k<1>(acc, w, p.f[1], p.wsc, p.sc, jl);
     // stage kt+1's activations (and, in the group's last stage, the next
@@ -1399,15 +1410,14 @@ __device__ __forceinline__ void stage(lds_u8* lds, uint32_t lds0, const Src& cur
     // buffers about to be reloaded
     wait_vm<wait_x<U>()>();
     __builtin_amdgcn_s_barrier();
-    load_x<(U + 3) % 4>(lds, sx, o, wave, kx);
+    load_x<(U + 3) % 4>(ring, sx, o, wave, kx);
     if constexpr (U == 0) load_sc(lds, par ^ 1, sw, o, wave, LAST ? 0 : kt / 4 + 1);
-    read_x<U, 3>(p.f[1], lds0, o);
+    read_x<U, 3>(p.f[1], ring, o);
     __builtin_amdgcn_sched_barrier(0);
     mfma_k<2>(acc, w, p.f[0], p.wsc, p.sc, jl);
     uint32_t wsc_next[2], sc_next[4];
-    read_x<(U + 1) % 4, 0>(p.f[0], lds0, o);
-    read_scales<(U + 1) % 4>(wsc_next, sc_next,
-                             lds0 + SCB + (uint32_t)((U == 3 ? par ^ 1 : par) * SC), o);
+    read_x<(U + 1) % 4, 0>(p.f[0], ring, o);
+    read_scales<(U + 1) % 4>(wsc_next, sc_next, lds + (U == 3 ? par ^ 1 : par) * SC, o);
     __builtin_amdgcn_sched_barrier(0);
     mfma_k<3>(acc, w, p.f[1], p.wsc, p.sc, jl);
     __builtin_amdgcn_sched_barrier(0);
@@ -1425,42 +1435,42 @@ __device__ __forceinline__ void stage(lds_u8* lds, uint32_t lds0, const Src& cur
 
 // All stages of item `cur`; par: the scale buffer of its first group
 // (toggled per group).
-__device__ __forceinline__ void item_stages(lds_u8* lds, uint32_t lds0, const Src& cur,
+__device__ __forceinline__ void item_stages(lds_u8* lds, const Ring& ring, const Src& cur,
                                             const Src& nxt, const Offs& o, int wave, int nkt,
                                             int jl, int& par, Pipe& p, v16f (&acc)[2][4]) {
     int kt = 0;
     for (; kt < nkt - 4; kt += 4) {
-        stage<0, false>(lds, lds0, cur, nxt, o, wave, kt, jl, par, p, acc);
-        stage<1, false>(lds, lds0, cur, nxt, o, wave, kt + 1, jl, par, p, acc);
-        stage<2, false>(lds, lds0, cur, nxt, o, wave, kt + 2, jl, par, p, acc);
-        stage<3, false>(lds, lds0, cur, nxt, o, wave, kt + 3, jl, par, p, acc);
+        stage<0, false>(lds, ring, cur, nxt, o, wave, kt, jl, par, p, acc);
+        stage<1, false>(lds, ring, cur, nxt, o, wave, kt + 1, jl, par, p, acc);
+        stage<2, false>(lds, ring, cur, nxt, o, wave, kt + 2, jl, par, p, acc);
+        stage<3, false>(lds, ring, cur, nxt, o, wave, kt + 3, jl, par, p, acc);
         par ^= 1;
     }
-    stage<0, true>(lds, lds0, cur, nxt, o, wave, kt, jl, par, p, acc);
-    stage<1, true>(lds, lds0, cur, nxt, o, wave, kt + 1, jl, par, p, acc);
-    stage<2, true>(lds, lds0, cur, nxt, o, wave, kt + 2, jl, par, p, acc);
-    stage<3, true>(lds, lds0, cur, nxt, o, wave, kt + 3, jl, par, p, acc);
+    stage<0, true>(lds, ring, cur, nxt, o, wave, kt, jl, par, p, acc);
+    stage<1, true>(lds, ring, cur, nxt, o, wave, kt + 1, jl, par, p, acc);
+    stage<2, true>(lds, ring, cur, nxt, o, wave, kt + 2, jl, par, p, acc);
+    stage<3, true>(lds, ring, cur, nxt, o, wave, kt + 3, jl, par, p, acc);
     par ^= 1;
 }
 
 // The first item's loads in the order the stages issue them (as if stages
 // -4..-1 had run, the first group's scales ahead of them), then its stage
 // 0's first fragments and scale words.
-__device__ __forceinline__ void prologue(lds_u8* lds, uint32_t lds0, const Src& s, const Offs& o,
-                                         int wave, Pipe& p) {
+__device__ __forceinline__ void prologue(lds_u8* lds, const Ring& ring, const Src& s,
+                                         const Offs& o, int wave, Pipe& p) {
     load_sc(lds, 0, s, o, wave, 0);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-        if (g == 1) load_x<0>(lds, s, o, wave, 0);
-        if (g == 2) load_x<1>(lds, s, o, wave, 1);
-        if (g == 3) load_x<2>(lds, s, o, wave, 2);
+        if (g == 1) load_x<0>(ring, s, o, wave, 0);
+        if (g == 2) load_x<1>(ring, s, o, wave, 1);
+        if (g == 3) load_x<2>(ring, s, o, wave, 2);
         load_w(p.w[g], s, o, g);
     }
     // stage 0's activations: 8 + 12 + 12 = 32 loads were issued after them
     wait_vm<32>();
     __builtin_amdgcn_s_barrier();
-    read_x<0, 0>(p.f[0], lds0, o);
-    read_scales<0>(p.wsc, p.sc, lds0 + SCB, o);
+    read_x<0, 0>(p.f[0], ring, o);
+    read_scales<0>(p.wsc, p.sc, lds, o);
 }
 
 }  // namespace rs
@@ -1477,11 +1487,13 @@ __global__ __launch_bounds__(256, 1) void grouped_stream_kernel(
     using T = Stage<S, OUT_BF16>;
     constexpr int TABLE = rs::LDS_END;
     constexpr int STAGE_BASE = (TABLE + GROUP_TABLE_BYTES + 15) / 16 * 16;
-    constexpr int ROWS = T::rows_for((LDS_LIMIT - STAGE_BASE) / 4);
-    static_assert(STAGE_BASE + 4 * T::bytes(ROWS) <= LDS_LIMIT, "LDS budget");
+    constexpr int ROWS = T::rows_for((LDS_LIMIT - 4 * rs::XBUF - STAGE_BASE) / 4);
+    static_assert(4 * rs::XBUF + STAGE_BASE + 4 * T::bytes(ROWS) <= LDS_LIMIT, "LDS budget");
     __shared__ __attribute__((aligned(16))) uint8_t smem[STAGE_BASE + 4 * T::bytes(ROWS)];
+    __shared__ __attribute__((aligned(16))) uint8_t xr0[rs::XBUF], xr1[rs::XBUF], xr2[rs::XBUF],
+        xr3[rs::XBUF];
     lds_u8* lds = (lds_u8*)smem;
-    const uint32_t lds0 = lds_addr(lds);
+    const rs::Ring ring{{(lds_u8*)xr0, (lds_u8*)xr1, (lds_u8*)xr2, (lds_u8*)xr3}};
     int* table = reinterpret_cast<int*>(smem + TABLE);
     const GroupTable tb{table, table + GROUP_MAX_E + 1, table + 2 * GROUP_MAX_E + 1};
     const int tiles_n = (int)((N + S::BN - 1) / S::BN);
@@ -1504,7 +1516,7 @@ __global__ __launch_bounds__(256, 1) void grouped_stream_kernel(
     v16f acc[2][4];
     zero_acc<S>(acc);
     rs::Pipe p;
-    rs::prologue(lds, lds0, cur, o, wave, p);
+    rs::prologue(lds, ring, cur, o, wave, p);
     int par = 0;
     for (;;) {
         const int tn = t + stride;
@@ -1516,7 +1528,7 @@ __global__ __launch_bounds__(256, 1) void grouped_stream_kernel(
             if (!have_next) nx = it;
         }
         const rs::Src nxt = rs::item_src(nx, x, xs, w, ws, N, K);
-        rs::item_stages(lds, lds0, cur, nxt, o, wave, nkt, it.jl, par, p, acc);
+        rs::item_stages(lds, ring, cur, nxt, o, wave, nkt, it.jl, par, p, acc);
         // keep the loads in flight plus the epilogue's stores within the
         // 6-bit load counter
         wait_vm<24>();
