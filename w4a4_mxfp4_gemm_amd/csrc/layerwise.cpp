@@ -180,9 +180,11 @@ int mxfp4_requant_layers_from_host(const mxfp4_load_part* parts, int64_t n_parts
         if (e == hipSuccess) e = hipEventRecord(freed[c.slot], stream);
         if (e != hipSuccess) st = MXFP4_EHIP;
     }
+    // destroying an event whose work is still pending is allowed (the
+    // runtime releases it once the work is done); a failure is still reported
     for (int64_t s = 0; s < kSlots; ++s) {
-        if (copied[s]) hipEventDestroy(copied[s]);
-        if (freed[s]) hipEventDestroy(freed[s]);
+        if (copied[s] && hipEventDestroy(copied[s]) != hipSuccess && st == MXFP4_OK) st = MXFP4_EHIP;
+        if (freed[s] && hipEventDestroy(freed[s]) != hipSuccess && st == MXFP4_OK) st = MXFP4_EHIP;
     }
     return st;
 }
