@@ -9,7 +9,7 @@ import torch
 
 import oracle
 import synth
-from gpu_util import (Guarded, assert_w4a8, bf16_bits, dev, say, u8, w4a8_block_maxima,
+from gpu_util import (Guarded, assert_w4a8, bf16_bits, dev, f32, say, u8, w4a8_block_maxima,
                       w4a8_truncation_bound)
 
 pytestmark = pytest.mark.gpu
@@ -305,6 +305,58 @@ def test_w4a8_in_block_truncation_model(mx, M, K):
     exact = np.repeat((448 + x)[:, None], 8, axis=1).reshape(-1)
     assert (np.abs(y.reshape(-1) - exact) <= bound).all()
 
+
+
+def observed_error(gpu, y, s, bound):
+    """Largest |gpu - exact| relative to S = sum_k |a_k b_k|, to the W4A8
+    bar's truncation allowance, and to |exact| (outputs above 1e-3 of the
+    largest), and the fraction of outputs beyond the W4A4 bar 1e-5 * S."""
+    err = np.abs(f32(gpu.float()).astype(np.float64).reshape(y.shape) - y)
+    big = np.abs(y) > 1e-3 * np.abs(y).max()
+    return dict(max_err_over_S=float((err / np.maximum(s, 1e-300)).max()),
+                max_err_over_allowance=float((err / np.maximum(bound, 1e-300)).max()),
+                max_rel_err=float((err[big] / np.abs(y[big])).max()),
+                frac_beyond_w4a4_bar=float((err > oracle.GEMM_FP32_RTOL * s).mean()))
+
+
+def test_w4a8_error_observed_on_the_bench_shapes(mx):
+    """The W4A8 error as it comes out on the bench's data (NVFP4-derived
+    weights N(0, 0.02), activations N(0, 1) with 1% outlier channels x50):
+    the decode layer W [12288, 4096] at M = 64 (every row, 1000 sampled
+    columns) and a [4096]^3 GEMM (16 sampled rows, every column), fp32 out.
+    Reported (run with -s), and held inside the bar; the bar itself is a
+    worst case over full-range operands, far above what such data reaches."""
+    cases = []
+    w = synth.bf16_normal((12288, 4096), 0.02, seed=11)
+    codes, scales, g = synth.nvfp4_from_bf16(w)
+    wo = oracle.requant(u8(codes), u8(scales), np.atleast_1d(g.numpy()))
+    x = synth.activations(64, 4096, seed=12, outlier_seed=13)
+    cols = np.random.default_rng(7).choice(12288, 1000, replace=False)
+    cases.append(("decode M=64 N=12288 K=4096", x, wo, np.repeat(np.arange(64), cols.size),
+                  np.tile(cols, 64)))
+    w2 = synth.bf16_normal((4096, 4096), 0.02, seed=21)
+    c2, s2, g2 = synth.nvfp4_from_bf16(w2)
+    wo2 = oracle.requant(u8(c2), u8(s2), np.atleast_1d(g2.numpy()))
+    x2 = synth.activations(4096, 4096, seed=24, outlier_seed=26)
+    rows = np.unique(np.concatenate([np.arange(0, 4096, 273), [4095]]))
+    cases.append(("prefill [4096]^3", x2, wo2, np.repeat(rows, 4096), np.tile(np.arange(4096), rows.size)))
+    for label, xx, (bc, bs), pm, pn in cases:
+        oc, os_ = oracle.quantize_act_fp8(bf16_bits(xx))
+        gy = mx.mxfp4_gemm_w4a8(torch.from_numpy(oc).to(dev()), torch.from_numpy(os_).to(dev()),
+                                torch.from_numpy(bc).to(dev()), torch.from_numpy(bs).to(dev()),
+                                out_dtype=torch.float32)
+        y, s = oracle.gemm_w4a8(oc, os_, bc, bs, pm, pn)
+        amax, bmax = w4a8_block_maxima(oc, os_, bc, bs)
+        bound = w4a8_truncation_bound(amax, bmax, pm, pn)
+        got = gy.cpu()[pm, pn]
+        assert_w4a8(got, y, s, bound, label)
+        obs = observed_error(got, y, s, bound)
+        say(f"  {label}: {obs} "
+            f"(allowance median {np.median(bound / np.maximum(s, 1e-300)):.2e} of S)")
+        # on these seeded inputs the truncation costs about 3e-5 * S at most
+        # (0.5% of its allowance): a change in the arithmetic that kept inside
+        # the worst-case bar but lost more would show here
+        assert obs["max_err_over_S"] < 1e-4, obs
 
 
 @pytest.mark.parametrize("M,N,K,ldx", [(1, 1000, 4096, 4096), (5, 300, 2048, 2048),
