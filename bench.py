@@ -429,13 +429,16 @@ def moe_workload(torch, mx, synth):
     is timed beside it, and so is the step with the gate_up stage as two
     launches (grouped GEMM to bf16, then the activation kernel).  The fused
     call reads the gate_up weights as rows interleaved by 32 (gate, up); the
-    synthetic weights are the same bytes either way."""
+    synthetic weights are the same bytes either way.  The expert weight codes
+    are pre-shuffled into the grouped GEMMs' operand order at load time."""
     E, T, TOPK = 128, 2048, 8
     d = torch.device("cuda:0")
     perm, offsets, rows, weights = synth.route_topk_full(T, E, TOPK, seed=34, device="cpu")
     perm, offsets, rows, weights = perm.to(d), offsets.to(d), rows.to(d), weights.to(d)
     tokens = synth.activations(T, 4096, seed=33, device=d)
     W = {}
+    SAMPLE_EXPERTS = (0, 41, 87, 127)              # the CPU baseline's experts
+    W_rows = {}                                    # their row-major codes, on the host
     for name, (N, K), seed in (("gate_up", (2048, 4096), 31), ("down", (4096, 1024), 32)):
         wc = torch.empty((E, N, K // 2), dtype=torch.uint8, device=d)
         ws = torch.empty((E, N, K // 32), dtype=torch.uint8, device=d)
@@ -443,7 +446,10 @@ def moe_workload(torch, mx, synth):
             w = synth.bf16_normal((N, K), 0.02, seed=seed * 1000 + e, device=d)
             c, s, g = synth.nvfp4_from_bf16(w)
             mx.mxfp4_requant_from_nvfp4(c, s, g.reshape(1), wc[e], ws[e])
-        W[name] = (N, K, wc, ws)
+        W_rows[name] = wc[list(SAMPLE_EXPERTS)].cpu()
+        # load time: the codes go into the grouped GEMMs' operand order
+        W[name] = (N, K, mx.mxfp4_preshuffle_weights(wc), ws)
+        del wc
     Mtot = T * TOPK
     R = MOE_SLOTS
     tokens = [tokens.clone() for _ in range(R)]
@@ -463,20 +469,22 @@ def moe_workload(torch, mx, synth):
 
     def gemm_gate_up(r):
         mx.mxfp4_grouped_gemm(aq1[r][0], aq1[r][1], W["gate_up"][2], W["gate_up"][3], offsets,
-                              y1[r])
+                              y1[r], b_preshuffled=True)
 
     def act_down(r):
         mx.mxfp4_silu_mul_quantize(y1[r], *aq2[r])
 
     def gemm_down(r):
-        mx.mxfp4_grouped_gemm(aq2[r][0], aq2[r][1], W["down"][2], W["down"][3], offsets, y2[r])
+        mx.mxfp4_grouped_gemm(aq2[r][0], aq2[r][1], W["down"][2], W["down"][3], offsets, y2[r],
+                              b_preshuffled=True)
 
     def combine(r):
         mx.mxfp4_moe_combine(y2[r], rows, weights, out[r])
 
     def gate_up_glu(r):
         mx.mxfp4_grouped_gemm_silu_quantize(aq1[r][0], aq1[r][1], W["gate_up"][2],
-                                            W["gate_up"][3], offsets, *aq2[r])
+                                            W["gate_up"][3], offsets, *aq2[r],
+                                            b_preshuffled=True)
 
     def step(r):
         aq_gate_up(r), gate_up_glu(r), gemm_down(r)
@@ -529,17 +537,18 @@ def moe_workload(torch, mx, synth):
         off = offsets.cpu().numpy()
         tok = tokens[0].cpu().view(torch.int16).numpy().view(np.uint16)
         pm = perm.cpu().numpy()
-        gu = [u.cpu().numpy() for u in W["gate_up"][2:]]
-        dn = [u.cpu().numpy() for u in W["down"][2:]]
+        gu_s = W["gate_up"][3].cpu().numpy()
+        dn_s = W["down"][3].cpu().numpy()
+        gu_c, dn_c = W_rows["gate_up"].numpy(), W_rows["down"].numpy()
         t0 = time.perf_counter()
         flops = 0
-        for e in (0, 41, 87, 127):
+        for i, e in enumerate(SAMPLE_EXPERTS):
             r0, r1 = int(off[e]), int(off[e + 1])
             ac, as_ = oracle.quantize_act(tok, row_index=pm[r0:r1])
-            oracle.gemm(ac, as_, gu[0][e], gu[1][e])
+            oracle.gemm(ac, as_, gu_c[i], gu_s[e])
             hc = np.zeros((r1 - r0, 512), np.uint8)
             hs = np.full((r1 - r0, 32), 127, np.uint8)
-            oracle.gemm(hc, hs, dn[0][e], dn[1][e])
+            oracle.gemm(hc, hs, dn_c[i], dn_s[e])
             flops += 2 * (r1 - r0) * (2048 * 4096 + 4096 * 1024)
         dt = time.perf_counter() - t0
         return {"TFLOPs": round(flops / dt / 1e12, 6), "cores": oracle.num_threads(),

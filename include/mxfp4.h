@@ -76,6 +76,9 @@ enum { MXFP4_REQ_INTERMEDIATE_BF16 = 1u << 0 };         /* requant flags        
  * no flag.
  */
 enum { MXFP4_SCALE_UOS = 1u << 1 };
+/* Grouped GEMM flag: b_codes are in the layout mxfp4_preshuffle_weights
+   writes (see there). */
+enum { MXFP4_B_PRESHUFFLED = 1u << 2 };
 
 /*
  * NVFP4 -> MXFP4 requant of T same-shape weight tensors, the load-time step
@@ -302,10 +305,15 @@ int mxfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
  *                       a bad table can give wrong rows but never a write
  *                       outside y.
  *   y                   [total_M][N] bf16 or fp32, device, written
- *   workspace, flags    as for mxfp4_gemm
+ *   workspace           as for mxfp4_gemm
+ *   flags               0 or MXFP4_B_PRESHUFFLED (b_codes pre-shuffled;
+ *                       MXFP4_EUNSUPPORTED unless the register-streamed
+ *                       kernel below applies and N % 32 == 0)
  * Kernel choice (same results): K % 512 == 0, E <= 2048, each operand's
- * codes under 2 GiB and both scale pointers 4-byte aligned: the LDS-tiled
- * persistent kernel that walks the offset table; else the generic kernel.
+ * codes under 2 GiB and both scale pointers 4-byte aligned: a persistent
+ * kernel that walks the offset table, with the weights streamed straight
+ * into registers when K % 1024 == 0 and staged in LDS otherwise; else the
+ * generic kernel.
  */
 int mxfp4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
                        const uint8_t* b_codes, const uint8_t* b_scales,
@@ -313,6 +321,23 @@ int mxfp4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
                        int64_t N, int64_t K, void* y, int out_dtype,
                        void* workspace, size_t workspace_bytes,
                        uint32_t flags, hipStream_t stream);
+
+/*
+ * Rewrites T MXFP4 weight tensors [T][N][K/2] of E2M1 codes into the order
+ * the grouped GEMMs' matrix-core operands are loaded in, for
+ * MXFP4_B_PRESHUFFLED (a load-time step, like the requant; the scales are
+ * unchanged).  Within each tensor, 16-byte piece p of the output is the
+ * operand of lane l = p % 64 in K-step t = (p / 64) % 4 of K-stage
+ * s = (p / 256) % (K/256) of the 32-row block b = p / (64 K): bytes
+ * 128 s + 16 (4 (l / 32) + t) .. +15 of row 32 b + l % 32.
+ *
+ *   codes   [T][N][K/2] u8, device, read; 16-byte aligned
+ *   out     [T][N][K/2] u8, device, written; 16-byte aligned, not
+ *           overlapping codes
+ *   N       a positive multiple of 32;  K  a positive multiple of 256
+ */
+int mxfp4_preshuffle_weights(const uint8_t* codes, uint8_t* out, int64_t T, int64_t N,
+                             int64_t K, hipStream_t stream);
 
 /* Workspace bytes mxfp4_gemm / mxfp4_grouped_gemm need (currently 0). */
 size_t mxfp4_gemm_workspace_size(int64_t M, int64_t N, int64_t K);
@@ -489,8 +514,10 @@ int mxfp4_silu_mul_quantize(const void* gate_up_bf16, int64_t ldg, int64_t M, in
  *   I                   columns of h; a positive multiple of 32
  *   h_codes, h_scales   [total_M][I/2], [total_M][I/32] u8, device, written
  *                       (h_codes 16-byte aligned)
- *   flags               0 or MXFP4_SCALE_UOS
- * Returns MXFP4_EUNSUPPORTED where the LDS-tiled grouped kernel does not
+ *   flags               0, MXFP4_SCALE_UOS and/or MXFP4_B_PRESHUFFLED (the
+ *                       interleaved b_codes then pre-shuffled; needs
+ *                       K % 1024 == 0)
+ * Returns MXFP4_EUNSUPPORTED where the persistent grouped kernel does not
  * apply (K % 512 != 0, more than its expert table holds, operands over 2 GiB,
  * scale pointers not 4-byte aligned); the two calls above cover those shapes.
  */

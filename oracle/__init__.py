@@ -550,6 +550,27 @@ def moe_combine(y_bits, rows, weights, H=None):
     return out, s
 
 
+# ---- pre-shuffled weight order (a layout of this library) -------------------
+def preshuffle_codes(codes):
+    """The weight-code order of mxfp4_preshuffle_weights.  It is this
+    library's own layout (defined where include/mxfp4.h declares that call),
+    not something the pages define: a permutation of each tensor's bytes so
+    that one 32x32x64 matrix-core operand load is 1 KiB contiguous.  With the
+    codes of a tensor viewed as [N/32 blocks b][32 rows q][K/256 stages s]
+    [2 halves h][4 K-steps t][16 bytes j] (row 32b + q, byte 128s + 16(4h + t)
+    + j of the row), the output lists the same bytes in the order
+    [b][s][t][h][q][j]: piece ((b S + s) 4 + t) 64 + 32h + q.  codes:
+    [..., N, K/2] uint8, N % 32 == 0, K % 256 == 0."""
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    *lead, N, half = c.shape
+    K = 2 * half
+    assert N % 32 == 0 and K % 256 == 0
+    n = len(lead)
+    v = c.reshape(*lead, N // 32, 32, K // 256, 2, 4, 16)
+    axes = list(range(n)) + [n + a for a in (0, 2, 4, 3, 1, 5)]
+    return np.ascontiguousarray(v.transpose(axes)).reshape(c.shape)
+
+
 # ---- parity bar for the GEMM ------------------------------------------------
 def gemm_fp32_ok(gpu, y, s, rtol=GEMM_FP32_RTOL) -> np.ndarray:
     """Elementwise: |gpu - y| <= rtol * s (s == 0 requires gpu == 0)."""

@@ -208,7 +208,7 @@ def test_grouped_gemm_silu_quantize_argument_checks(lib):
     assert g(I=0) == -1
     assert g(K=48) == -1                 # K % 32
     assert g(flags=1) == -1
-    assert g(flags=4) == -1
+    assert g(flags=8) == -1             # 4 is MXFP4_B_PRESHUFFLED
     assert g(off=None) == -1
     assert g(hs=None) == -1
     assert g(a=ODD) == -2
@@ -351,3 +351,34 @@ def test_layerwise_argument_checks(lib):
     assert run(P, 2, FAKE, 1 << 20, 0, None, None) == -1                   # a null source
     parts[0].T = 0
     assert run(P, 2, None, 0, 0, None, None) == 0                          # nothing to load
+
+
+def test_preshuffle_argument_checks(lib):
+    f = lib.mxfp4_preshuffle_weights
+    #         codes out        T  N   K
+    assert f(FAKE, FAKE + 4096, 1, 48, 256, None) == -1          # N % 32
+    assert f(FAKE, FAKE + 4096, 1, 32, 384, None) == -1          # K % 256
+    assert f(FAKE, FAKE + 4096, -1, 32, 256, None) == -1
+    assert f(None, FAKE + 4096, 1, 32, 256, None) == -1
+    assert f(FAKE, FAKE + 2048, 1, 32, 256, None) == -1          # overlapping (4 KiB each)
+    assert f(FAKE, FAKE, 1, 32, 256, None) == -1                 # in place
+    assert f(ODD, FAKE + 8192, 1, 32, 256, None) == -2
+    assert f(FAKE, FAKE + 4104, 1, 32, 256, None) == -2          # out alignment
+    assert f(FAKE, FAKE, 0, 32, 256, None) == 0                  # nothing to do
+
+
+def test_grouped_preshuffled_needs_the_register_streamed_kernel(lib):
+    """MXFP4_B_PRESHUFFLED is refused (before any launch) where the kernel
+    that reads that layout does not run: K % 1024 != 0 or N % 32 != 0."""
+    import w4a4_mxfp4_gemm_amd as m
+    F = m.MXFP4_B_PRESHUFFLED
+    g = lib.mxfp4_grouped_gemm
+    #        a     sa    b     sb    off   E  M   N    K     y     dt ws  wsb flags
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 64, 256, 1536, FAKE, 0, None, 0, F, None) == -3
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 64, 240, 1024, FAKE, 0, None, 0, F, None) == -3
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 64, 256, 1024, FAKE, 0, None, 0, 8, None) == -1
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 0, 256, 1536, FAKE, 0, None, 0, F, None) == 0
+    h = lib.mxfp4_grouped_gemm_silu_quantize
+    #        a     sa    b     sb    off   E  M   I    K     hc    hs    flags
+    assert h(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 64, 128, 1536, FAKE, FAKE, F, None) == -3
+    assert h(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 0, 128, 1536, FAKE, FAKE, F | 2, None) == 0

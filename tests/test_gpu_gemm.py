@@ -265,6 +265,48 @@ def test_grouped_gemm_tiled_more_than_256_experts(mx):
         assert_gemm_fp32(gy, y, s, f"grouped tiled 300 experts K={K}")
 
 
+def test_preshuffle_matches_the_definition(mx):
+    """mxfp4_preshuffle_weights equals the oracle's definition of the layout,
+    byte for byte, and writes nothing outside its output."""
+    T, N, K = 3, 96, 1536
+    say(f"preshuffle T={T} N={N} K={K}")
+    codes = torch.randint(0, 256, (T, N, K // 2), dtype=torch.uint8,
+                          generator=torch.Generator().manual_seed(5))
+    out = Guarded((T, N, K // 2), torch.uint8)
+    mx.mxfp4_preshuffle_weights(codes.to(dev()), out.view)
+    torch.cuda.synchronize()
+    assert out.intact(), "write outside the output"
+    assert np.array_equal(u8(out.view), oracle.preshuffle_codes(u8(codes)))
+
+
+@pytest.mark.parametrize("K", [1024, 3072])
+def test_grouped_gemm_preshuffled_weights(mx, K):
+    """The grouped GEMM reading pre-shuffled weight codes gives the row-major
+    call's output bit for bit (fp32 and bf16; every 32-row block of a
+    128-row tile, a partial 256-row weight tile, empty experts), and that is
+    within the oracle's bar."""
+    counts = [0, 1, 31, 32, 33, 97, 128, 129, 257, 300, 0]
+    E, N = len(counts), 320
+    say(f"grouped gemm preshuffled counts={counts} N={N} K={K}")
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    M = int(offsets[-1])
+    a, sa = synth.canonical_mxfp4(M, K, seed=K + 1)
+    b, sb = synth.canonical_mxfp4(E * N, K, seed=K + 2)
+    b, sb = b.reshape(E, N, K // 2), sb.reshape(E, N, K // 32)
+    A, SA, B, SB, OFF = to_dev(a, sa, b, sb, offsets)
+    Bs = mx.mxfp4_preshuffle_weights(B)
+    for dt in (torch.float32, torch.bfloat16):
+        ref = mx.mxfp4_grouped_gemm(A, SA, B, SB, OFF, out_dtype=dt)
+        gy = Guarded((M, N), dt)
+        mx.mxfp4_grouped_gemm(A, SA, Bs, SB, OFF, gy.view, b_preshuffled=True)
+        torch.cuda.synchronize()
+        assert gy.intact(), "write outside y"
+        assert torch.equal(gy.view, ref), dt
+        if dt == torch.float32:
+            y, s = oracle.grouped_gemm(u8(a), u8(sa), u8(b), u8(sb), offsets)
+            assert_gemm_fp32(gy.view, y, s, "grouped preshuffled")
+
+
 @pytest.mark.parametrize("K", [512, 1024])
 def test_grouped_gemm_tiled_bad_offsets_stay_inside_y(mx, K):
     say(f"grouped tiled gemm malformed offsets K={K}")

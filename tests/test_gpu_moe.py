@@ -262,6 +262,13 @@ def fused_glu_both(mx, E, counts, I, K, seed, rule):
     hc, hs = mx.mxfp4_silu_mul_quantize(y1[:, idx].contiguous(), scale_rule=rule)
     torch.cuda.synchronize()
     assert torch.equal(hc, gc.view) and torch.equal(hs, gs.view), "fused != two calls"
+    if K % 1024 == 0 and M:
+        # the same call on pre-shuffled weight codes
+        pc, ps = mx.mxfp4_grouped_gemm_silu_quantize(
+            A[0], A[1], mx.mxfp4_preshuffle_weights(A[2]), A[3], A[4], scale_rule=rule,
+            b_preshuffled=True)
+        torch.cuda.synchronize()
+        assert torch.equal(pc, gc.view) and torch.equal(ps, gs.view), "preshuffled"
 
 
 @pytest.mark.parametrize("E,counts,I,K", [
@@ -294,6 +301,11 @@ def test_grouped_gemm_silu_quantize_moe_size(mx):
     rc, rs = mx.mxfp4_silu_mul_quantize(y1[:, idx].contiguous())
     torch.cuda.synchronize()
     assert torch.equal(hc, rc) and torch.equal(hs, rs)
+    # and the same call on pre-shuffled weight codes
+    pc, ps = mx.mxfp4_grouped_gemm_silu_quantize(xc, xs, mx.mxfp4_preshuffle_weights(wc), ws, off,
+                                                 b_preshuffled=True)
+    torch.cuda.synchronize()
+    assert torch.equal(pc, hc) and torch.equal(ps, hs)
 
 
 def test_moe_layer_end_to_end(mx):

@@ -888,3 +888,35 @@ def test_quantize_act_smooth_closed_forms():
     idx = np.array([5, 0, 5], dtype=np.int32)
     g = oracle.quantize_act_smooth(xb, bf16_bits(pw), row_index=idx)
     assert np.array_equal(g[0], c[idx]) and np.array_equal(g[1], s_[idx])
+
+
+# ---- the pre-shuffled weight order --------------------------------------------------
+def test_preshuffle_piece_by_piece_and_inverse():
+    """preshuffle_codes against the piece formula the header states, one
+    16-byte piece at a time in a plain loop (lane l, K-step t, stage s, block
+    b of piece p; source row 32b + l % 32, bytes 128s + 16(4(l // 32) + t)),
+    for two tensors; and the inverse permutation restores the input."""
+    rng = np.random.default_rng(3)
+    T, N, K = 2, 64, 512
+    codes = rng.integers(0, 256, (T, N, K // 2), dtype=np.uint8)
+    out = oracle.preshuffle_codes(codes)
+    S = K // 256
+    for tt in range(T):
+        flat = out[tt].reshape(-1)
+        for p in range(N * K // 32):
+            l, t, s, b = p % 64, (p // 64) % 4, (p // 256) % S, p // (256 * S)
+            row, byte = 32 * b + l % 32, 128 * s + 16 * (4 * (l // 32) + t)
+            assert np.array_equal(flat[16 * p:16 * p + 16], codes[tt, row, byte:byte + 16]), (tt, p)
+    # a 2-D tensor is one tensor
+    assert np.array_equal(oracle.preshuffle_codes(codes[1]), out[1])
+    # the piece formula maps output bytes one to one onto input bytes, so
+    # scattering the output back through it restores the input
+    src = np.empty(N * K // 2, dtype=np.int64)
+    for p in range(N * K // 32):
+        l, t, s, b = p % 64, (p // 64) % 4, (p // 256) % S, p // (256 * S)
+        row, byte = 32 * b + l % 32, 128 * s + 16 * (4 * (l // 32) + t)
+        src[16 * p:16 * p + 16] = row * (K // 2) + byte + np.arange(16)
+    assert np.array_equal(np.sort(src), np.arange(src.size))
+    back = np.empty(N * K // 2, dtype=np.uint8)
+    back[src] = out[0].reshape(-1)
+    assert np.array_equal(back.reshape(N, K // 2), codes[0])

@@ -20,6 +20,7 @@ MXFP4_OUT_BF16 = 0
 MXFP4_OUT_FP32 = 1
 MXFP4_REQ_INTERMEDIATE_BF16 = 1
 MXFP4_SCALE_UOS = 2
+MXFP4_B_PRESHUFFLED = 4
 
 _STATUS_NAMES = {0: "MXFP4_OK", -1: "MXFP4_EINVAL", -2: "MXFP4_EALIGN",
                  -3: "MXFP4_EUNSUPPORTED", -4: "MXFP4_EHIP", -5: "MXFP4_ESCRATCH"}
@@ -84,6 +85,8 @@ def _load_library() -> ctypes.CDLL:
     lib.mxfp4_requant_layers_from_host.restype = ctypes.c_int
     lib.mxfp4_linear_bf16_noalloc.argtypes = [P, I, I, I, I, P, P, P, P, ctypes.c_int, U32, P]
     lib.mxfp4_linear_bf16_noalloc.restype = ctypes.c_int
+    lib.mxfp4_preshuffle_weights.argtypes = [P, P, I, I, I, P]
+    lib.mxfp4_preshuffle_weights.restype = ctypes.c_int
     lib.mxfp4_status_string.argtypes = [ctypes.c_int]
     lib.mxfp4_status_string.restype = ctypes.c_char_p
     lib.mxfp4_version.argtypes = []
@@ -102,7 +105,7 @@ EXPORTED_SYMBOLS = ("mxfp4_requant_from_nvfp4", "mxfp4_requant_from_nvfp4_subset
                     "mxfp4_quantize_act_smooth", "mxfp8_quantize_act_smooth",
                     "mxfp4_grouped_gemm_silu_quantize", "mxfp4_quantize_act_scatter",
                     "mxfp4_layerwise_plan", "mxfp4_requant_layers_from_host",
-                    "mxfp4_linear_bf16_noalloc",
+                    "mxfp4_linear_bf16_noalloc", "mxfp4_preshuffle_weights",
                     "mxfp4_status_string", "mxfp4_version")
 
 
@@ -616,9 +619,10 @@ def mxfp4_moe_combine(y, rows, weights, out=None, *, H=None, out_dtype=torch.bfl
 
 
 def mxfp4_grouped_gemm(a_codes, a_scales, b_codes, b_scales, offsets, y=None, *,
-                       out_dtype=torch.bfloat16, stream=None):
+                       out_dtype=torch.bfloat16, b_preshuffled=False, stream=None):
     """For each expert e: y[off[e]:off[e+1]] = A[off[e]:off[e+1]] * B[e]^T.
-    A [total_M, K/2] expert-sorted, B [E, N, K/2], offsets int32 [E+1]."""
+    A [total_M, K/2] expert-sorted, B [E, N, K/2], offsets int32 [E+1].
+    b_preshuffled: B's codes as mxfp4_preshuffle_weights wrote them."""
     _need(a_codes, "a_codes", torch.uint8)
     dev = a_codes.device
     for t, n in ((a_scales, "a_scales"), (b_codes, "b_codes"), (b_scales, "b_scales")):
@@ -638,8 +642,29 @@ def mxfp4_grouped_gemm(a_codes, a_scales, b_codes, b_scales, offsets, y=None, *,
         raise ValueError("y must be [total_M, N]")
     _check("mxfp4_grouped_gemm", _lib.mxfp4_grouped_gemm(
         _ptr(a_codes), _ptr(a_scales), _ptr(b_codes), _ptr(b_scales), _ptr(offsets),
-        E, total_M, N, K, _ptr(y), _out_dtype(y.dtype), None, 0, 0, _stream(stream, dev)))
+        E, total_M, N, K, _ptr(y), _out_dtype(y.dtype), None, 0,
+        MXFP4_B_PRESHUFFLED if b_preshuffled else 0, _stream(stream, dev)))
     return y
+
+
+def mxfp4_preshuffle_weights(codes, out=None, *, stream=None):
+    """MXFP4 weight codes [T, N, K/2] (or [N, K/2]) -> the same bytes in the
+    grouped GEMMs' operand order (for b_preshuffled=True); N % 32 == 0,
+    K % 256 == 0."""
+    _need(codes, "codes", torch.uint8)
+    dev = codes.device
+    if codes.dim() not in (2, 3):
+        raise ValueError("codes must be [N, K/2] or [T, N, K/2]")
+    T = 1 if codes.dim() == 2 else codes.shape[0]
+    N, K = codes.shape[-2], codes.shape[-1] * 2
+    if out is None:
+        out = torch.empty_like(codes)
+    _need(out, "out", torch.uint8, dev)
+    if out.shape != codes.shape:
+        raise ValueError("out must have the shape of codes")
+    _check("mxfp4_preshuffle_weights", _lib.mxfp4_preshuffle_weights(
+        _ptr(codes), _ptr(out), T, N, K, _stream(stream, dev)))
+    return out
 
 
 
@@ -672,7 +697,8 @@ def mxfp4_quantize_act_scatter(x, dest_rows, codes=None, scales=None, *, R=None,
 
 
 def mxfp4_grouped_gemm_silu_quantize(a_codes, a_scales, b_codes, b_scales, offsets,
-                                     codes=None, scales=None, *, scale_rule="ocp", stream=None):
+                                     codes=None, scales=None, *, scale_rule="ocp",
+                                     b_preshuffled=False, stream=None):
     """The MoE gate_up grouped GEMM with the expert activation and its MXFP4
     quantization fused in: A [total_M, K/2] expert-sorted, B [E, 2I, K/2] with
     each expert's rows interleaved by 32 (rows 64q..64q+31 gate, 64q+32..64q+63
@@ -703,7 +729,8 @@ def mxfp4_grouped_gemm_silu_quantize(a_codes, a_scales, b_codes, b_scales, offse
         raise ValueError("output shapes do not match [total_M, I/2] / [total_M, I/32]")
     _check("mxfp4_grouped_gemm_silu_quantize", _lib.mxfp4_grouped_gemm_silu_quantize(
         _ptr(a_codes), _ptr(a_scales), _ptr(b_codes), _ptr(b_scales), _ptr(offsets),
-        E, total_M, I, K, _ptr(codes), _ptr(scales), _rule_flag(scale_rule),
+        E, total_M, I, K, _ptr(codes), _ptr(scales),
+        _rule_flag(scale_rule) | (MXFP4_B_PRESHUFFLED if b_preshuffled else 0),
         _stream(stream, dev)))
     return codes, scales
 
@@ -714,8 +741,8 @@ __all__ = ["mxfp4_requant_from_nvfp4", "mxfp4_quantize_act", "mxfp4_gemm",
            "mxfp8_quantize_act", "mxfp4_gemm_w4a8", "mxfp4_linear_w4a8_bf16",
            "mxfp4_linear_w4a8_workspace_size", "mxfp4_quantize_act_smooth",
            "mxfp8_quantize_act_smooth", "mxfp4_grouped_gemm_silu_quantize",
-           "mxfp4_quantize_act_scatter",
+           "mxfp4_quantize_act_scatter", "mxfp4_preshuffle_weights",
            "mxfp4_status_string",
            "mxfp4_version", "Mxfp4Error", "LIBRARY_PATH", "EXPORTED_SYMBOLS",
            "MXFP4_OUT_BF16", "MXFP4_OUT_FP32", "MXFP4_REQ_INTERMEDIATE_BF16",
-           "MXFP4_SCALE_UOS"]
+           "MXFP4_SCALE_UOS", "MXFP4_B_PRESHUFFLED"]

@@ -342,10 +342,11 @@ hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const ui
 hipError_t launch_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
                                const uint8_t* b_codes, const uint8_t* b_scales,
                                const int32_t* offsets, int64_t E, int64_t total_M, int64_t N,
-                               int64_t K, void* y, bool out_bf16, hipStream_t stream) {
-    if (grouped_tiled_supported(E, total_M, N, K, a_scales, b_scales))
+                               int64_t K, void* y, bool out_bf16, bool b_shuffled,
+                               hipStream_t stream) {
+    if (b_shuffled || grouped_tiled_supported(E, total_M, N, K, a_scales, b_scales))
         return launch_grouped_gemm_tiled(a_codes, a_scales, b_codes, b_scales, offsets, E,
-                                         total_M, N, K, y, out_bf16, stream);
+                                         total_M, N, K, y, out_bf16, b_shuffled, stream);
     constexpr int WM = 2, WN = 2, KSPLIT = 1;
     constexpr int TM = 16 * WM;
     constexpr int TN = 16 * WN * (4 / KSPLIT);

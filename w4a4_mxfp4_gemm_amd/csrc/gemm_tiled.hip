@@ -52,6 +52,7 @@
 #include "mx_device.h"
 #include "launch.h"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace mx {
@@ -1236,22 +1237,39 @@ struct WSet {
 
 // Per-lane offsets, the same for every item and stage.  As in the LDS-staged
 // kernels, lane half h takes MX blocks 4h..4h+3 of a stage, one per K-step,
-// so its 4 scale bytes of a stage are one 32-bit word.
+// so its 4 scale bytes of a stage are one 32-bit word.  The weight codes are
+// read row-major ([N][K/2]: a load brings 16 bytes from each of 32 rows) or,
+// pre-shuffled, in the MFMA's operand order (each load 1 KiB contiguous:
+// a quarter of the vector L1's tag lookups); the layout only changes where a
+// lane's 16 bytes are, through the two strides.
 struct Offs {
-    uint32_t w[2];              // weight code loads of blocks i (+ 16 t)
+    uint32_t w[2];              // weight code loads of blocks i, K-step 0 of stage 0
+    uint32_t wt, wk;            // + wt per K-step, + wk per stage
     uint32_t x[4];              // activation code DMA
     uint32_t sw[2], sx;         // scale DMA: the wave's weight rows (two loads), activation rows
     uint32_t rx[4];             // LDS reads: code chunk of K-step t
     uint32_t rsw, rsx;          // LDS reads: scale words of weight / activation block 0
 };
 
-__device__ __forceinline__ Offs offsets(int64_t K, int wave) {
+__device__ __forceinline__ Offs offsets(int64_t K, int wave, bool shuffled) {
     const int lane = threadIdx.x & 63;
     const int r32 = lane & 31, h = lane >> 5;
     const uint32_t ldc = (uint32_t)(K / 2), lds_ = (uint32_t)(K / 32);
     Offs o;
+    if (shuffled) {
+        // 32-row block b of the tile, stage kt, K-step t: 1 KiB at
+        // ((b * K/256 + kt) * 4 + t) * 1024, lane l at 16 l
 #pragma unroll
-    for (int i = 0; i < 2; ++i) o.w[i] = (uint32_t)(64 * wave + 32 * i + r32) * ldc + 64 * h;
+        for (int i = 0; i < 2; ++i)
+            o.w[i] = (uint32_t)(2 * wave + i) * (uint32_t)(K / 256) * 4096u + 16u * (uint32_t)lane;
+        o.wt = 1024;
+        o.wk = 4096;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) o.w[i] = (uint32_t)(64 * wave + 32 * i + r32) * ldc + 64 * h;
+        o.wt = 16;
+        o.wk = BKB;
+    }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int row = (wave * 4 + q) * 8 + (lane >> 3);
@@ -1329,7 +1347,8 @@ __device__ __forceinline__ void load_w(WSet& w, const Src& s, const Offs& o, int
         for (int t = 0; t < 4; ++t)
             w.c[i][t] = __builtin_bit_cast(
                 v4u,
-                __builtin_amdgcn_raw_buffer_load_b128(s.w, (int)(o.w[i] + 16 * t), kt * BKB, 0));
+                __builtin_amdgcn_raw_buffer_load_b128(s.w, (int)(o.w[i] + o.wt * t),
+                                                      kt * (int)o.wk, 0));
 }
 
 // K-step T's activation fragments of the stage in ring buffer B (all four
@@ -1475,13 +1494,14 @@ __device__ __forceinline__ void prologue(lds_u8* lds, const Ring& ring, const Sr
 
 }  // namespace rs
 
-// K % 1024 == 0 (stages of an item a multiple of 4).
+// K % 1024 == 0 (stages of an item a multiple of 4).  w_shuffled: the
+// weight codes are in the order mxfp4_preshuffle_weights writes (N % 32 == 0).
 template <bool OUT_BF16, bool GLU = false, bool UOS = false>
 __global__ __launch_bounds__(256, 1) void grouped_stream_kernel(
     const uint8_t* __restrict__ x, const uint8_t* __restrict__ xs,
     const uint8_t* __restrict__ w, const uint8_t* __restrict__ ws,
     const int32_t* __restrict__ offsets, int E, int total_M, int64_t N, int64_t K,
-    void* __restrict__ y, uint8_t* __restrict__ hs) {
+    void* __restrict__ y, uint8_t* __restrict__ hs, int w_shuffled) {
     static_assert(!GLU || OUT_BF16, "the GLU epilogue parks bf16");
     using S = GroupShape;                       // the accumulator and epilogue layout
     using T = Stage<S, OUT_BF16>;
@@ -1509,7 +1529,7 @@ __global__ __launch_bounds__(256, 1) void grouped_stream_kernel(
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nkt = (int)(K / 256);             // a multiple of 4
-    const rs::Offs o = rs::offsets(K, wave);
+    const rs::Offs o = rs::offsets(K, wave, w_shuffled != 0);
     GroupItem it = decode_item<S::BM>(tb, E, tiles_n, t, 0);
     if (it.e < 0) return;
     rs::Src cur = rs::item_src(it, x, xs, w, ws, N, K);
@@ -1546,6 +1566,28 @@ __global__ __launch_bounds__(256, 1) void grouped_stream_kernel(
         t = tn;
     }
     wait_vm<0>();                               // the surplus loads, before the LDS is released
+}
+
+// The pre-shuffled weight layout: for T tensors [N][K/2] of E2M1 codes, piece
+// p (16 bytes) of a tensor is the A operand of lane l = p % 64 in K-step
+// t = (p / 64) % 4 of stage s = (p / 256) % (K/256) of 32-row block
+// b = p / (64 K): row 32 b + l % 32, bytes 128 s + 16 (4 (l / 32) + t).
+// One thread a piece: the writes are coalesced, the reads 32 bytes a row.
+__global__ __launch_bounds__(256) void preshuffle_kernel(const uint8_t* __restrict__ in,
+                                                         uint8_t* __restrict__ out, int64_t T,
+                                                         int64_t N, int64_t K) {
+    const int64_t S = K / 256, per = N * (K / 32);
+    const int64_t total = T * per;
+    for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < total;
+         p += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t tt = p / per, q = p - tt * per;
+        const int l = (int)(q % 64), t = (int)((q / 64) % 4);
+        const int64_t st = (q / 256) % S, b = q / (256 * S);
+        const int64_t row = tt * N + 32 * b + l % 32;
+        const v4u v = *reinterpret_cast<const v4u*>(in + row * (K / 2) + 128 * st +
+                                                    16 * (4 * (l / 32) + t));
+        *reinterpret_cast<v4u*>(out + 16 * p) = v;
+    }
 }
 
 }  // namespace tiled
@@ -1679,6 +1721,21 @@ hipError_t launch_gemm_tiled_w4a8(const uint8_t* a_codes, const uint8_t* a_scale
 // The register-streamed grouped kernel walks an item's stages four at a time.
 static bool grouped_stream_ok(int64_t K) { return K % 1024 == 0; }
 
+bool grouped_stream_supported(int64_t E, int64_t total_M, int64_t N, int64_t K,
+                              const void* a_scales, const void* b_scales) {
+    return grouped_stream_ok(K) && N % 32 == 0 &&
+           grouped_tiled_supported(E, total_M, N, K, a_scales, b_scales);
+}
+
+hipError_t launch_preshuffle(const uint8_t* in, uint8_t* out, int64_t T, int64_t N, int64_t K,
+                             hipStream_t stream) {
+    const int64_t pieces = T * N * (K / 32);
+    const int64_t blocks = std::min<int64_t>((pieces + 255) / 256, 256 * 32);
+    hipLaunchKernelGGL(tiled::preshuffle_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, in,
+                       out, T, N, K);
+    return hipGetLastError();
+}
+
 // One persistent workgroup per CU (the tile's LDS allows no more), never
 // more workgroups than the largest possible number of work items.
 static hipError_t grouped_grid(int64_t E, int64_t total_M, int64_t N, dim3& grid) {
@@ -1699,19 +1756,26 @@ hipError_t launch_grouped_gemm_tiled(const uint8_t* a_codes, const uint8_t* a_sc
                                      const uint8_t* b_codes, const uint8_t* b_scales,
                                      const int32_t* offsets, int64_t E, int64_t total_M,
                                      int64_t N, int64_t K, void* y, bool out_bf16,
-                                     hipStream_t stream) {
+                                     bool b_shuffled, hipStream_t stream) {
     dim3 grid;
     const hipError_t e = grouped_grid(E, total_M, N, grid);
     if (e != hipSuccess) return e;
     uint8_t* const none = nullptr;
-    auto go = [&](auto kernel) {
-        hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, a_codes, a_scales, b_codes,
-                           b_scales, offsets, (int)E, (int)total_M, N, K, y, none);
-    };
-    if (grouped_stream_ok(K))
+    if (grouped_stream_ok(K)) {
+        auto go = [&](auto kernel) {
+            hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, a_codes, a_scales, b_codes,
+                               b_scales, offsets, (int)E, (int)total_M, N, K, y, none,
+                               (int)b_shuffled);
+        };
         out_bf16 ? go(tiled::grouped_stream_kernel<true>) : go(tiled::grouped_stream_kernel<false>);
-    else
+    } else {
+        if (b_shuffled) return hipErrorInvalidValue;   // the caller checks this first
+        auto go = [&](auto kernel) {
+            hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, a_codes, a_scales, b_codes,
+                               b_scales, offsets, (int)E, (int)total_M, N, K, y, none);
+        };
         out_bf16 ? go(tiled::grouped_tiled_kernel<true>) : go(tiled::grouped_tiled_kernel<false>);
+    }
     return hipGetLastError();
 }
 
@@ -1724,21 +1788,28 @@ hipError_t launch_grouped_glu_quant(const uint8_t* a_codes, const uint8_t* a_sca
                                     const uint8_t* b_codes, const uint8_t* b_scales,
                                     const int32_t* offsets, int64_t E, int64_t total_M,
                                     int64_t N, int64_t K, uint8_t* h_codes, uint8_t* h_scales,
-                                    bool uos, hipStream_t stream) {
+                                    bool uos, bool b_shuffled, hipStream_t stream) {
     dim3 grid;
     const hipError_t e = grouped_grid(E, total_M, N, grid);
     if (e != hipSuccess) return e;
-    auto go = [&](auto kernel) {
-        hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, a_codes, a_scales, b_codes,
-                           b_scales, offsets, (int)E, (int)total_M, N, K,
-                           static_cast<void*>(h_codes), h_scales);
-    };
-    if (grouped_stream_ok(K))
+    if (grouped_stream_ok(K)) {
+        auto go = [&](auto kernel) {
+            hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, a_codes, a_scales, b_codes,
+                               b_scales, offsets, (int)E, (int)total_M, N, K,
+                               static_cast<void*>(h_codes), h_scales, (int)b_shuffled);
+        };
         uos ? go(tiled::grouped_stream_kernel<true, true, true>)
             : go(tiled::grouped_stream_kernel<true, true, false>);
-    else
+    } else {
+        if (b_shuffled) return hipErrorInvalidValue;   // the caller checks this first
+        auto go = [&](auto kernel) {
+            hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, a_codes, a_scales, b_codes,
+                               b_scales, offsets, (int)E, (int)total_M, N, K,
+                               static_cast<void*>(h_codes), h_scales);
+        };
         uos ? go(tiled::grouped_tiled_kernel<true, true, true>)
             : go(tiled::grouped_tiled_kernel<true, true, false>);
+    }
     return hipGetLastError();
 }
 

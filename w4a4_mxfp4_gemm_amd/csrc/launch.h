@@ -66,7 +66,7 @@ hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
 hipError_t launch_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
                                const uint8_t* b_codes, const uint8_t* b_scales,
                                const int32_t* offsets, int64_t E, int64_t total_M,
-                               int64_t N, int64_t K, void* y, bool out_bf16,
+                               int64_t N, int64_t K, void* y, bool out_bf16, bool b_shuffled,
                                hipStream_t stream);
 
 bool tiled_gemm_supported(int64_t M, int64_t N, int64_t K, const void* a_scales,
@@ -84,7 +84,17 @@ hipError_t launch_grouped_gemm_tiled(const uint8_t* a_codes, const uint8_t* a_sc
                                      const uint8_t* b_codes, const uint8_t* b_scales,
                                      const int32_t* offsets, int64_t E, int64_t total_M,
                                      int64_t N, int64_t K, void* y, bool out_bf16,
-                                     hipStream_t stream);
+                                     bool b_shuffled, hipStream_t stream);
+
+// The grouped kernel with the weights streamed into registers (K % 1024 ==
+// 0) on the tiled kernel's shapes, N % 32 == 0: the one that reads weights
+// pre-shuffled by launch_preshuffle (T tensors [N][K/2], N % 32 == 0,
+// K % 256 == 0).
+bool grouped_stream_supported(int64_t E, int64_t total_M, int64_t N, int64_t K,
+                              const void* a_scales, const void* b_scales);
+
+hipError_t launch_preshuffle(const uint8_t* in, uint8_t* out, int64_t T, int64_t N, int64_t K,
+                             hipStream_t stream);
 
 // The grouped gate_up GEMM with the expert activation and its MXFP4
 // quantization in the epilogue (gate/up weight rows interleaved by 32): the
@@ -96,7 +106,7 @@ hipError_t launch_grouped_glu_quant(const uint8_t* a_codes, const uint8_t* a_sca
                                     const uint8_t* b_codes, const uint8_t* b_scales,
                                     const int32_t* offsets, int64_t E, int64_t total_M,
                                     int64_t N, int64_t K, uint8_t* h_codes, uint8_t* h_scales,
-                                    bool uos, hipStream_t stream);
+                                    bool uos, bool b_shuffled, hipStream_t stream);
 
 bool skinny_gemm_supported(int64_t M, int64_t N, int64_t K, const void* x, const void* x_scales,
                            const void* w_scales);

@@ -307,7 +307,8 @@ int mxfp4_grouped_gemm_silu_quantize(const uint8_t* a_codes, const uint8_t* a_sc
                                      uint8_t* h_scales, uint32_t flags, hipStream_t stream) {
     if (E <= 0 || total_M < 0 || check_k(I) != MXFP4_OK || check_k(K) != MXFP4_OK)
         return MXFP4_EINVAL;
-    if ((flags & ~(uint32_t)MXFP4_SCALE_UOS) != 0) return MXFP4_EINVAL;
+    if ((flags & ~(uint32_t)(MXFP4_SCALE_UOS | MXFP4_B_PRESHUFFLED)) != 0) return MXFP4_EINVAL;
+    const bool shuffled = (flags & MXFP4_B_PRESHUFFLED) != 0;
     if (total_M == 0) return MXFP4_OK;
     if (!a_codes || !a_scales || !b_codes || !b_scales || !offsets || !h_codes || !h_scales)
         return MXFP4_EINVAL;
@@ -315,11 +316,13 @@ int mxfp4_grouped_gemm_silu_quantize(const uint8_t* a_codes, const uint8_t* a_sc
         !aligned(offsets, 4))
         return MXFP4_EALIGN;
     const int64_t N = 2 * I;
-    if (!mx::grouped_glu_supported(E, total_M, N, K, a_scales, b_scales))
+    if (!mx::grouped_glu_supported(E, total_M, N, K, a_scales, b_scales) ||
+        (shuffled && !mx::grouped_stream_supported(E, total_M, N, K, a_scales, b_scales)))
         return MXFP4_EUNSUPPORTED;
     return from_hip(mx::launch_grouped_glu_quant(a_codes, a_scales, b_codes, b_scales, offsets,
                                                  E, total_M, N, K, h_codes, h_scales,
-                                                 (flags & MXFP4_SCALE_UOS) != 0, stream));
+                                                 (flags & MXFP4_SCALE_UOS) != 0, shuffled,
+                                                 stream));
 }
 
 int mxfp4_moe_combine(const void* y_bf16, int64_t ldy, int64_t R, const int32_t* rows,
@@ -346,14 +349,30 @@ int mxfp4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const ui
                        void* workspace, size_t workspace_bytes, uint32_t flags,
                        hipStream_t stream) {
     if (E <= 0) return MXFP4_EINVAL;
+    const bool shuffled = (flags & MXFP4_B_PRESHUFFLED) != 0;
     const int st = check_gemm_common(a_codes, a_scales, b_codes, b_scales, total_M, N, K, y,
-                                     out_dtype, workspace, workspace_bytes, flags);
+                                     out_dtype, workspace, workspace_bytes,
+                                     flags & ~(uint32_t)MXFP4_B_PRESHUFFLED);
     if (st != MXFP4_OK || total_M == 0) return st;
     if (!offsets) return MXFP4_EINVAL;
     if (!aligned(offsets, 4)) return MXFP4_EALIGN;
+    if (shuffled && !mx::grouped_stream_supported(E, total_M, N, K, a_scales, b_scales))
+        return MXFP4_EUNSUPPORTED;
     return from_hip(mx::launch_grouped_gemm(a_codes, a_scales, b_codes, b_scales, offsets, E,
                                             total_M, N, K, y, out_dtype == MXFP4_OUT_BF16,
-                                            stream));
+                                            shuffled, stream));
+}
+
+int mxfp4_preshuffle_weights(const uint8_t* codes, uint8_t* out, int64_t T, int64_t N,
+                             int64_t K, hipStream_t stream) {
+    if (T < 0 || N <= 0 || N % 32 != 0 || K <= 0 || K % 256 != 0) return MXFP4_EINVAL;
+    if (T == 0) return MXFP4_OK;
+    if (!codes || !out) return MXFP4_EINVAL;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(codes), b = reinterpret_cast<uintptr_t>(out);
+    const uint64_t bytes = (uint64_t)T * (uint64_t)N * (uint64_t)(K / 2);
+    if (a < b + bytes && b < a + bytes) return MXFP4_EINVAL;      // overlapping buffers
+    if (!aligned(codes, 16) || !aligned(out, 16)) return MXFP4_EALIGN;
+    return from_hip(mx::launch_preshuffle(codes, out, T, N, K, stream));
 }
 
 size_t mxfp4_gemm_workspace_size(int64_t, int64_t, int64_t) { return 0; }
