@@ -211,16 +211,26 @@ def grouped_case(mx, counts, N, K, seed, out_dtype):
     return gy.view, y, s
 
 
+# Expert sizes ending in each 32-row block of a 128-row tile or spanning
+# several; the second set averages more than 96 rows an expert, which gives
+# the register-streamed kernel its 160-row tile: sizes ending in each of its
+# five blocks and spanning two and three tiles.
+ROW_BLOCK_COUNTS = {"tile128": [0, 1, 31, 32, 33, 97, 128, 129, 257, 300, 0],
+                    "tile160": [0, 1, 31, 32, 33, 97, 128, 129, 159, 160, 161, 257, 300, 320,
+                                321, 0]}
+
+
 @pytest.mark.parametrize("K", [1024, 1536, 3072])
-def test_grouped_gemm_tiled_row_blocks(mx, K):
-    """Expert sizes that end in each 32-row block of a 128-row tile, span
-    several tiles, or are empty; N with a partial 256-row weight tile.  The
-    bf16 output is the RNE of the same fp32 accumulator (random scales make
+@pytest.mark.parametrize("rows", ["tile128", "tile160"])
+def test_grouped_gemm_tiled_row_blocks(mx, K, rows):
+    """Expert sizes that end in each 32-row block of a tile, span several
+    tiles, or are empty; N with a partial 256-row weight tile.  The bf16
+    output is the RNE of the same fp32 accumulator (random scales make
     cancellation common, so the oracle bound is the fp32 one).  K = 1024 and
     3072 take the kernel with the weights streamed into registers (an item
     of 4 stages, and of 12: its steady loop), K = 1536 the one that stages
     them in LDS."""
-    counts = [0, 1, 31, 32, 33, 97, 128, 129, 257, 300, 0]
+    counts = ROW_BLOCK_COUNTS[rows]
     say(f"grouped tiled row blocks counts={counts} N=300 K={K}")
     gy, y, s = grouped_case(mx, counts, 300, K, 51, torch.float32)
     assert_gemm_fp32(gy, y, s, "grouped tiled")
@@ -280,12 +290,13 @@ def test_preshuffle_matches_the_definition(mx):
 
 
 @pytest.mark.parametrize("K", [1024, 3072])
-def test_grouped_gemm_preshuffled_weights(mx, K):
+@pytest.mark.parametrize("rows", ["tile128", "tile160"])
+def test_grouped_gemm_preshuffled_weights(mx, K, rows):
     """The grouped GEMM reading pre-shuffled weight codes gives the row-major
     call's output bit for bit (fp32 and bf16; every 32-row block of a
     128-row tile, a partial 256-row weight tile, empty experts), and that is
     within the oracle's bar."""
-    counts = [0, 1, 31, 32, 33, 97, 128, 129, 257, 300, 0]
+    counts = ROW_BLOCK_COUNTS[rows]
     E, N = len(counts), 320
     say(f"grouped gemm preshuffled counts={counts} N={N} K={K}")
     offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)

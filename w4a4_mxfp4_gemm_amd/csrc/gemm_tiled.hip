@@ -1206,29 +1206,41 @@ __global__ __launch_bounds__(256, 1) void grouped_tiled_kernel(
 // ---------------------------------------------------------------------------
 namespace rs {
 
-// The activation ring: four stage buffers, each a __shared__ array of its
-// own, always named statically (the stage's position in its group of four),
-// so the compiler can tell which buffer a DMA writes and which one an LDS
-// read reads, and counts the DMA loads in the waits it places for the
-// weight registers instead of draining them before every read.
-constexpr int XBUF = 128 * BKB;               // a stage's activation codes: 128 rows x 128 B
+// The geometry of an item: MB 32-row activation blocks (BM = 32 MB rows)
+// against the 256 weight rows of a tile, and what follows from MB.
+template <int MB_>
+struct Geo {
+    static constexpr int MB = MB_;
+    static constexpr int BM = 32 * MB;
+    using Shape = tiled::Shape<MB, 2, 1, 4>;      // the accumulator and epilogue layout
+    // The activation ring: four stage buffers, each a __shared__ array of its
+    // own, always named statically (the stage's position in its group of
+    // four), so the compiler can tell which buffer a DMA writes and which one
+    // an LDS read reads, and counts the DMA loads in the waits it places for
+    // the weight registers instead of draining them before every read.
+    static constexpr int XBUF = BM * BKB;         // a stage's activation codes
+    static constexpr int XL = MB;                 // their DMA loads a wave (8 rows each)
+    // The scale bytes of a group of four stages, 32 a row (8 a stage): the
+    // 256 weight rows, then 128 XSL activation rows.  Two groups' buffers, at
+    // the start of the kernel's other LDS array.
+    static constexpr int XSL = (MB + 3) / 4;      // activation scale DMA loads a wave (32 rows)
+    static constexpr int SL = 2 + XSL;            // all scale DMA loads of a wave, a group
+    static constexpr int SCW = 256 * 32;
+    static constexpr int SC = SCW + 128 * XSL * 32;
+    static constexpr int LDS_END = 2 * SC;
+    // The wait in stage U of a group for stage g+1's activations (loaded in
+    // stage g-2): the 8 weight loads of stage g-2 and the XL + 8 of stage g-1
+    // were issued after them, and the SL scale loads of the group's first
+    // stage when it is one of those two (they follow its activation loads).
+    template <int U>
+    static constexpr int wait_x() {
+        return 16 + XL + (U == 1 || U == 2 ? SL : 0);
+    }
+};
+
 struct Ring {
     lds_u8* b[4];
 };
-// The scale bytes of a group of four stages, 32 a row (8 a stage): the 256
-// weight rows, then the 128 activation rows.  Two groups' buffers, at the
-// start of the kernel's other LDS array.
-constexpr int SCW = 256 * 32;
-constexpr int SC = SCW + 128 * 32;            // 12 KiB
-constexpr int LDS_END = 2 * SC;               // 24 KiB
-
-// The wait in stage U of a group: 20 loads were issued after stage g+1's
-// activations, 23 when the group's first stage (which also loads the next
-// group's scales) is among the two stages before.
-template <int U>
-constexpr int wait_x() {
-    return 20 + (U == 1 || U == 2 ? 3 : 0);
-}
 
 // One stage of one wave's weight codes: blocks i (32 rows), K-steps t.
 struct WSet {
@@ -1242,20 +1254,22 @@ struct WSet {
 // pre-shuffled, in the MFMA's operand order (each load 1 KiB contiguous:
 // a quarter of the vector L1's tag lookups); the layout only changes where a
 // lane's 16 bytes are, through the two strides.
+template <class G>
 struct Offs {
     uint32_t w[2];              // weight code loads of blocks i, K-step 0 of stage 0
     uint32_t wt, wk;            // + wt per K-step, + wk per stage
-    uint32_t x[4];              // activation code DMA
-    uint32_t sw[2], sx;         // scale DMA: the wave's weight rows (two loads), activation rows
+    uint32_t x[G::XL];          // activation code DMA
+    uint32_t sw[2], sx[G::XSL]; // scale DMA: the wave's weight rows (two loads), activation rows
     uint32_t rx[4];             // LDS reads: code chunk of K-step t
     uint32_t rsw, rsx;          // LDS reads: scale words of weight / activation block 0
 };
 
-__device__ __forceinline__ Offs offsets(int64_t K, int wave, bool shuffled) {
+template <class G>
+__device__ __forceinline__ Offs<G> offsets(int64_t K, int wave, bool shuffled) {
     const int lane = threadIdx.x & 63;
     const int r32 = lane & 31, h = lane >> 5;
     const uint32_t ldc = (uint32_t)(K / 2), lds_ = (uint32_t)(K / 32);
-    Offs o;
+    Offs<G> o;
     if (shuffled) {
         // 32-row block b of the tile, stage kt, K-step t: 1 KiB at
         // ((b * K/256 + kt) * 4 + t) * 1024, lane l at 16 l
@@ -1271,27 +1285,28 @@ __device__ __forceinline__ Offs offsets(int64_t K, int wave, bool shuffled) {
         o.wk = BKB;
     }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int row = (wave * 4 + q) * 8 + (lane >> 3);
+    for (int q = 0; q < G::XL; ++q) {
+        const int row = (wave * G::XL + q) * 8 + (lane >> 3);
         const int c = (lane & 7) ^ ((row >> 1) & 7);
         o.x[q] = (uint32_t)row * ldc + 16 * c;
     }
 #pragma unroll
     for (int q = 0; q < 2; ++q)
         o.sw[q] = (uint32_t)(64 * wave + 32 * q + (lane >> 1)) * lds_ + 16 * (lane & 1);
-    o.sx = (uint32_t)(32 * wave + (lane >> 1)) * lds_ + 16 * (lane & 1);
+#pragma unroll
+    for (int q = 0; q < G::XSL; ++q)
+        o.sx[q] = (uint32_t)((wave * G::XSL + q) * 32 + (lane >> 1)) * lds_ + 16 * (lane & 1);
 #pragma unroll
     for (int t = 0; t < 4; ++t)
         o.rx[t] = (uint32_t)(r32 * BKB + 16 * ((4 * h + t) ^ ((r32 >> 1) & 7)));
     o.rsw = (uint32_t)((64 * wave + r32) * 32 + 4 * h);
-    o.rsx = (uint32_t)(SCW + r32 * 32 + 4 * h);
+    o.rsx = (uint32_t)(G::SCW + r32 * 32 + 4 * h);
     return o;
 }
 
 // Where an item's operands come from, each starting at the item's first row
 // (rows past N, or past the expert's last row, read 0): the weight codes as
-// a buffer resource for ordinary loads, the rest as raw descriptors for the
-// DMA.
+// a buffer resource for ordinary loads, the rest for the DMA.
 struct Src {
     __amdgpu_buffer_rsrc_t w, x;
     v4i ws, xs;
@@ -1316,31 +1331,35 @@ __device__ __forceinline__ Src item_src(const GroupItem& it, const uint8_t* x, c
 }
 
 // Stage kt's activation codes of the item `s` into ring buffer B.
-template <int B>
-__device__ __forceinline__ void load_x(const Ring& ring, const Src& s, const Offs& o, int wave,
+template <class G, int B>
+__device__ __forceinline__ void load_x(const Ring& ring, const Src& s, const Offs<G>& o, int wave,
                                        int kt) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int q = 0; q < G::XL; ++q)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            s.x, (__attribute__((address_space(3))) void*)(ring.b[B] + (wave * 4 + q) * 1024), 16,
-            (int)o.x[q], kt * BKB, 0, 0);
+            s.x, (__attribute__((address_space(3))) void*)(ring.b[B] + (wave * G::XL + q) * 1024),
+            16, (int)o.x[q], kt * BKB, 0, 0);
 }
 
 // The scales of stages 4 grp .. 4 grp + 3 into scale buffer `par`: each wave
-// its own 64 weight rows and 32 of the activation rows, two lanes a row.
-__device__ __forceinline__ void load_sc(lds_u8* lds, int par, const Src& s, const Offs& o,
+// its own 64 weight rows and 32 XSL of the activation rows, two lanes a row.
+template <class G>
+__device__ __forceinline__ void load_sc(lds_u8* lds, int par, const Src& s, const Offs<G>& o,
                                         int wave, int grp) {
-    lds_u8* b = lds + par * SC;
+    lds_u8* b = lds + par * G::SC;
     const uint32_t k = (uint32_t)grp * 32;
     dma16(s.ws, b + (2 * wave) * 1024, o.sw[0], k);
     dma16(s.ws, b + (2 * wave + 1) * 1024, o.sw[1], k);
-    dma16(s.xs, b + SCW + wave * 1024, o.sx, k);
+#pragma unroll
+    for (int q = 0; q < G::XSL; ++q)
+        dma16(s.xs, b + G::SCW + (wave * G::XSL + q) * 1024, o.sx[q], k);
 }
 
 // Stage kt's weight codes into a set: each 32-row block's four K-step
 // registers back to back, so each row's 128-byte line is still in L1 for
 // the three loads after the first.
-__device__ __forceinline__ void load_w(WSet& w, const Src& s, const Offs& o, int kt) {
+template <class G>
+__device__ __forceinline__ void load_w(WSet& w, const Src& s, const Offs<G>& o, int kt) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -1351,37 +1370,39 @@ __device__ __forceinline__ void load_w(WSet& w, const Src& s, const Offs& o, int
                                                       kt * (int)o.wk, 0));
 }
 
-// K-step T's activation fragments of the stage in ring buffer B (all four
+// K-step T's activation fragments of the stage in ring buffer B (all MB
 // 32-row blocks).
+template <class G>
 struct XFrag {
-    v4u x[4];
+    v4u x[G::MB];
 };
-template <int B, int T>
-__device__ __forceinline__ void read_x(XFrag& f, const Ring& ring, const Offs& o) {
+template <class G, int B, int T>
+__device__ __forceinline__ void read_x(XFrag<G>& f, const Ring& ring, const Offs<G>& o) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < G::MB; ++j)
         f.x[j] = *reinterpret_cast<lds_v4u*>(ring.b[B] + o.rx[T] + j * 32 * BKB);
 }
 // Stage S (of its group, in scale buffer `sb`): the scale words of the
-// wave's two weight blocks and of the four activation blocks.
-template <int S>
-__device__ __forceinline__ void read_scales(uint32_t (&wsc)[2], uint32_t (&sc)[4], const lds_u8* sb,
-                                            const Offs& o) {
+// wave's two weight blocks and of the MB activation blocks.
+template <class G, int S>
+__device__ __forceinline__ void read_scales(uint32_t (&wsc)[2], uint32_t (&sc)[G::MB],
+                                            const lds_u8* sb, const Offs<G>& o) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
         wsc[i] = *reinterpret_cast<lds_u32*>(sb + o.rsw + i * 32 * 32 + 8 * S);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < G::MB; ++j)
         sc[j] = *reinterpret_cast<lds_u32*>(sb + o.rsx + j * 32 * 32 + 8 * S);
 }
 
 // The MFMAs of K-step T on the activation blocks that hold rows (j < jl,
 // uniform: the blocks past an expert's last row are skipped).
-template <int T>
-__device__ __forceinline__ void mfma_k(v16f (&acc)[2][4], const WSet& w, const XFrag& f,
-                                       const uint32_t (&wsc)[2], const uint32_t (&sc)[4], int jl) {
+template <class G, int T>
+__device__ __forceinline__ void mfma_k(v16f (&acc)[2][G::MB], const WSet& w, const XFrag<G>& f,
+                                       const uint32_t (&wsc)[2], const uint32_t (&sc)[G::MB],
+                                       int jl) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < G::MB; ++j) {
         if (j == 0 || jl > j) {
 #pragma unroll
             for (int i = 0; i < 2; ++i)
@@ -1392,10 +1413,11 @@ __device__ __forceinline__ void mfma_k(v16f (&acc)[2][4], const WSet& w, const X
 
 // Pipeline registers of a wave: the four weight sets, two K-steps of
 // activation fragments, the scale words of the stage the MFMAs use.
+template <class G>
 struct Pipe {
     WSet w[4];
-    XFrag f[2];
-    uint32_t wsc[2], sc[4];
+    XFrag<G> f[2];
+    uint32_t wsc[2], sc[G::MB];
 };
 
 // Stage kt = 4q + U of item `cur`, in the group whose scales are in buffer
@@ -1404,10 +1426,10 @@ struct Pipe {
 // four stages (LAST) those belong to the next item.  On entry f[0] holds
 // K-step 0's fragments; each K-step reads the next one's into the other
 // slot (K-step 3: stage kt+1's K-step 0, and its scale words).
-template <int U, bool LAST>
+template <class G, int U, bool LAST>
 __device__ __forceinline__ void stage(lds_u8* lds, const Ring& ring, const Src& cur, const Src& nxt,
-                                      const Offs& o, int wave, int kt, int jl, int par, Pipe& p,
-                                      v16f (&acc)[2][4]) {
+                                      const Offs<G>& o, int wave, int kt, int jl, int par,
+                                      Pipe<G>& p, v16f (&acc)[2][G::MB]) {
     constexpr bool X_NEXT = LAST && U >= 1;
     const Src& sw = LAST ? nxt : cur;
     const Src& sx = X_NEXT ? nxt : cur;
@@ -1418,100 +1440,105 @@ __device__ __forceinline__ void stage(lds_u8* lds, const Ring& ring, const Src& 
     // compiler neither versions the loop on it nor moves one block's MFMAs
     // out of their stage (either keeps every weight set alive far longer)
     asm volatile("" : "+s"(jl));
-    read_x<U, 1>(p.f[1], ring, o);
+    read_x<G, U, 1>(p.f[1], ring, o);
     __builtin_amdgcn_sched_barrier(0);
-    mfma_k<0>(acc, w, p.f[0], p.wsc, p.sc, jl);
-    read_x<U, 2>(p.f[0], ring, o);
+    mfma_k<G, 0>(acc, w, p.f[0], p.wsc, p.sc, jl);
+    read_x<G, U, 2>(p.f[0], ring, o);
     __builtin_amdgcn_sched_barrier(0);
-    mfma_k<1>(acc, w, p.f[1], p.wsc, p.sc, jl);
+    mfma_k<G, 1>(acc, w, p.f[1], p.wsc, p.sc, jl);
     // stage kt+1's activations (and, in the group's last stage, the next
     // group's scales) landed in every wave; every wave is done with the
     // buffers about to be reloaded
-    wait_vm<wait_x<U>()>();
+    wait_vm<G::template wait_x<U>()>();
     __builtin_amdgcn_s_barrier();
-    load_x<(U + 3) % 4>(ring, sx, o, wave, kx);
-    if constexpr (U == 0) load_sc(lds, par ^ 1, sw, o, wave, LAST ? 0 : kt / 4 + 1);
-    read_x<U, 3>(p.f[1], ring, o);
+    load_x<G, (U + 3) % 4>(ring, sx, o, wave, kx);
+    if constexpr (U == 0) load_sc<G>(lds, par ^ 1, sw, o, wave, LAST ? 0 : kt / 4 + 1);
+    read_x<G, U, 3>(p.f[1], ring, o);
     __builtin_amdgcn_sched_barrier(0);
-    mfma_k<2>(acc, w, p.f[0], p.wsc, p.sc, jl);
-    uint32_t wsc_next[2], sc_next[4];
-    read_x<(U + 1) % 4, 0>(p.f[0], ring, o);
-    read_scales<(U + 1) % 4>(wsc_next, sc_next, lds + (U == 3 ? par ^ 1 : par) * SC, o);
+    mfma_k<G, 2>(acc, w, p.f[0], p.wsc, p.sc, jl);
+    uint32_t wsc_next[2], sc_next[G::MB];
+    read_x<G, (U + 1) % 4, 0>(p.f[0], ring, o);
+    read_scales<G, (U + 1) % 4>(wsc_next, sc_next, lds + (U == 3 ? par ^ 1 : par) * G::SC, o);
     __builtin_amdgcn_sched_barrier(0);
-    mfma_k<3>(acc, w, p.f[1], p.wsc, p.sc, jl);
+    mfma_k<G, 3>(acc, w, p.f[1], p.wsc, p.sc, jl);
     __builtin_amdgcn_sched_barrier(0);
-    load_w(w, sw, o, kw);                     // the set's registers are free
+    load_w<G>(w, sw, o, kw);                  // the set's registers are free
 #pragma unroll
     for (int i = 0; i < 2; ++i) p.wsc[i] = wsc_next[i];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) p.sc[j] = sc_next[j];
+    for (int j = 0; j < G::MB; ++j) p.sc[j] = sc_next[j];
     // this stage's MFMAs complete their chains here
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) asm volatile("" : "+a"(acc[i][j]));
+        for (int j = 0; j < G::MB; ++j) asm volatile("" : "+a"(acc[i][j]));
 }
 
 // All stages of item `cur`; par: the scale buffer of its first group
 // (toggled per group).
+template <class G>
 __device__ __forceinline__ void item_stages(lds_u8* lds, const Ring& ring, const Src& cur,
-                                            const Src& nxt, const Offs& o, int wave, int nkt,
-                                            int jl, int& par, Pipe& p, v16f (&acc)[2][4]) {
+                                            const Src& nxt, const Offs<G>& o, int wave, int nkt,
+                                            int jl, int& par, Pipe<G>& p,
+                                            v16f (&acc)[2][G::MB]) {
     int kt = 0;
     for (; kt < nkt - 4; kt += 4) {
-        stage<0, false>(lds, ring, cur, nxt, o, wave, kt, jl, par, p, acc);
-        stage<1, false>(lds, ring, cur, nxt, o, wave, kt + 1, jl, par, p, acc);
-        stage<2, false>(lds, ring, cur, nxt, o, wave, kt + 2, jl, par, p, acc);
-        stage<3, false>(lds, ring, cur, nxt, o, wave, kt + 3, jl, par, p, acc);
+        stage<G, 0, false>(lds, ring, cur, nxt, o, wave, kt, jl, par, p, acc);
+        stage<G, 1, false>(lds, ring, cur, nxt, o, wave, kt + 1, jl, par, p, acc);
+        stage<G, 2, false>(lds, ring, cur, nxt, o, wave, kt + 2, jl, par, p, acc);
+        stage<G, 3, false>(lds, ring, cur, nxt, o, wave, kt + 3, jl, par, p, acc);
         par ^= 1;
     }
-    stage<0, true>(lds, ring, cur, nxt, o, wave, kt, jl, par, p, acc);
-    stage<1, true>(lds, ring, cur, nxt, o, wave, kt + 1, jl, par, p, acc);
-    stage<2, true>(lds, ring, cur, nxt, o, wave, kt + 2, jl, par, p, acc);
-    stage<3, true>(lds, ring, cur, nxt, o, wave, kt + 3, jl, par, p, acc);
+    stage<G, 0, true>(lds, ring, cur, nxt, o, wave, kt, jl, par, p, acc);
+    stage<G, 1, true>(lds, ring, cur, nxt, o, wave, kt + 1, jl, par, p, acc);
+    stage<G, 2, true>(lds, ring, cur, nxt, o, wave, kt + 2, jl, par, p, acc);
+    stage<G, 3, true>(lds, ring, cur, nxt, o, wave, kt + 3, jl, par, p, acc);
     par ^= 1;
 }
 
 // The first item's loads in the order the stages issue them (as if stages
 // -4..-1 had run, the first group's scales ahead of them), then its stage
 // 0's first fragments and scale words.
+template <class G>
 __device__ __forceinline__ void prologue(lds_u8* lds, const Ring& ring, const Src& s,
-                                         const Offs& o, int wave, Pipe& p) {
-    load_sc(lds, 0, s, o, wave, 0);
+                                         const Offs<G>& o, int wave, Pipe<G>& p) {
+    load_sc<G>(lds, 0, s, o, wave, 0);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-        if (g == 1) load_x<0>(ring, s, o, wave, 0);
-        if (g == 2) load_x<1>(ring, s, o, wave, 1);
-        if (g == 3) load_x<2>(ring, s, o, wave, 2);
-        load_w(p.w[g], s, o, g);
+        if (g == 1) load_x<G, 0>(ring, s, o, wave, 0);
+        if (g == 2) load_x<G, 1>(ring, s, o, wave, 1);
+        if (g == 3) load_x<G, 2>(ring, s, o, wave, 2);
+        load_w<G>(p.w[g], s, o, g);
     }
-    // stage 0's activations: 8 + 12 + 12 = 32 loads were issued after them
-    wait_vm<32>();
+    // stage 0's activations: 8 + 2 (XL + 8) loads were issued after them
+    wait_vm<24 + 2 * G::XL>();
     __builtin_amdgcn_s_barrier();
-    read_x<0, 0>(p.f[0], ring, o);
-    read_scales<0>(p.wsc, p.sc, lds, o);
+    read_x<G, 0, 0>(p.f[0], ring, o);
+    read_scales<G, 0>(p.wsc, p.sc, lds, o);
 }
 
 }  // namespace rs
 
-// K % 1024 == 0 (stages of an item a multiple of 4).  w_shuffled: the
-// weight codes are in the order mxfp4_preshuffle_weights writes (N % 32 == 0).
-template <bool OUT_BF16, bool GLU = false, bool UOS = false>
+// K % 1024 == 0 (stages of an item a multiple of 4).  MB 32-row activation
+// blocks a tile (4 or 5).  w_shuffled: the weight codes are in the order
+// mxfp4_preshuffle_weights writes (N % 32 == 0).
+template <int MB, bool OUT_BF16, bool GLU = false, bool UOS = false>
 __global__ __launch_bounds__(256, 1) void grouped_stream_kernel(
     const uint8_t* __restrict__ x, const uint8_t* __restrict__ xs,
     const uint8_t* __restrict__ w, const uint8_t* __restrict__ ws,
     const int32_t* __restrict__ offsets, int E, int total_M, int64_t N, int64_t K,
     void* __restrict__ y, uint8_t* __restrict__ hs, int w_shuffled) {
     static_assert(!GLU || OUT_BF16, "the GLU epilogue parks bf16");
-    using S = GroupShape;                       // the accumulator and epilogue layout
+    using G = rs::Geo<MB>;
+    using S = typename G::Shape;
     using T = Stage<S, OUT_BF16>;
-    constexpr int TABLE = rs::LDS_END;
+    constexpr int TABLE = G::LDS_END;
     constexpr int STAGE_BASE = (TABLE + GROUP_TABLE_BYTES + 15) / 16 * 16;
-    constexpr int ROWS = T::rows_for((LDS_LIMIT - 4 * rs::XBUF - STAGE_BASE) / 4);
-    static_assert(4 * rs::XBUF + STAGE_BASE + 4 * T::bytes(ROWS) <= LDS_LIMIT, "LDS budget");
+    constexpr int ROWS = T::rows_for((LDS_LIMIT - 4 * G::XBUF - STAGE_BASE) / 4);
+    static_assert(4 * G::XBUF + STAGE_BASE + 4 * T::bytes(ROWS) <= LDS_LIMIT, "LDS budget");
     __shared__ __attribute__((aligned(16))) uint8_t smem[STAGE_BASE + 4 * T::bytes(ROWS)];
-    __shared__ __attribute__((aligned(16))) uint8_t xr0[rs::XBUF], xr1[rs::XBUF], xr2[rs::XBUF],
-        xr3[rs::XBUF];
+    __shared__ __attribute__((aligned(16))) uint8_t xr0[G::XBUF], xr1[G::XBUF], xr2[G::XBUF],
+        xr3[G::XBUF];
     lds_u8* lds = (lds_u8*)smem;
     const rs::Ring ring{{(lds_u8*)xr0, (lds_u8*)xr1, (lds_u8*)xr2, (lds_u8*)xr3}};
     int* table = reinterpret_cast<int*>(smem + TABLE);
@@ -1529,14 +1556,14 @@ __global__ __launch_bounds__(256, 1) void grouped_stream_kernel(
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nkt = (int)(K / 256);             // a multiple of 4
-    const rs::Offs o = rs::offsets(K, wave, w_shuffled != 0);
+    const rs::Offs<G> o = rs::offsets<G>(K, wave, w_shuffled != 0);
     GroupItem it = decode_item<S::BM>(tb, E, tiles_n, t, 0);
     if (it.e < 0) return;
     rs::Src cur = rs::item_src(it, x, xs, w, ws, N, K);
-    v16f acc[2][4];
+    v16f acc[2][MB];
     zero_acc<S>(acc);
-    rs::Pipe p;
-    rs::prologue(lds, ring, cur, o, wave, p);
+    rs::Pipe<G> p;
+    rs::prologue<G>(lds, ring, cur, o, wave, p);
     int par = 0;
     for (;;) {
         const int tn = t + stride;
@@ -1548,7 +1575,7 @@ __global__ __launch_bounds__(256, 1) void grouped_stream_kernel(
             if (!have_next) nx = it;
         }
         const rs::Src nxt = rs::item_src(nx, x, xs, w, ws, N, K);
-        rs::item_stages(lds, ring, cur, nxt, o, wave, nkt, it.jl, par, p, acc);
+        rs::item_stages<G>(lds, ring, cur, nxt, o, wave, nkt, it.jl, par, p, acc);
         // keep the loads in flight plus the epilogue's stores within the
         // 6-bit load counter
         wait_vm<24>();
@@ -1721,6 +1748,13 @@ hipError_t launch_gemm_tiled_w4a8(const uint8_t* a_codes, const uint8_t* a_scale
 // The register-streamed grouped kernel walks an item's stages four at a time.
 static bool grouped_stream_ok(int64_t K) { return K % 1024 == 0; }
 
+// Its activation tile: 160 rows when the experts average more than 96 rows
+// (as MoE routing gives them: a spread around the mean that 128-row tiles
+// would split, each part then reading the expert's weight tiles again),
+// else 128.  ceil(r / 160) <= ceil(r / 128), so the wider tile never makes
+// more items; the blocks past an expert's rows skip their MFMAs.
+static bool grouped_wide_tile(int64_t E, int64_t total_M) { return total_M > 96 * E; }
+
 bool grouped_stream_supported(int64_t E, int64_t total_M, int64_t N, int64_t K,
                               const void* a_scales, const void* b_scales) {
     return grouped_stream_ok(K) && N % 32 == 0 &&
@@ -1767,7 +1801,12 @@ hipError_t launch_grouped_gemm_tiled(const uint8_t* a_codes, const uint8_t* a_sc
                                b_scales, offsets, (int)E, (int)total_M, N, K, y, none,
                                (int)b_shuffled);
         };
-        out_bf16 ? go(tiled::grouped_stream_kernel<true>) : go(tiled::grouped_stream_kernel<false>);
+        if (grouped_wide_tile(E, total_M))
+            out_bf16 ? go(tiled::grouped_stream_kernel<5, true>)
+                     : go(tiled::grouped_stream_kernel<5, false>);
+        else
+            out_bf16 ? go(tiled::grouped_stream_kernel<4, true>)
+                     : go(tiled::grouped_stream_kernel<4, false>);
     } else {
         if (b_shuffled) return hipErrorInvalidValue;   // the caller checks this first
         auto go = [&](auto kernel) {
@@ -1798,8 +1837,12 @@ hipError_t launch_grouped_glu_quant(const uint8_t* a_codes, const uint8_t* a_sca
                                b_scales, offsets, (int)E, (int)total_M, N, K,
                                static_cast<void*>(h_codes), h_scales, (int)b_shuffled);
         };
-        uos ? go(tiled::grouped_stream_kernel<true, true, true>)
-            : go(tiled::grouped_stream_kernel<true, true, false>);
+        if (grouped_wide_tile(E, total_M))
+            uos ? go(tiled::grouped_stream_kernel<5, true, true, true>)
+                : go(tiled::grouped_stream_kernel<5, true, true, false>);
+        else
+            uos ? go(tiled::grouped_stream_kernel<4, true, true, true>)
+                : go(tiled::grouped_stream_kernel<4, true, true, false>);
     } else {
         if (b_shuffled) return hipErrorInvalidValue;   // the caller checks this first
         auto go = [&](auto kernel) {
