@@ -1207,10 +1207,12 @@ __global__ __launch_bounds__(256, 1) void grouped_tiled_kernel(
 namespace rs {
 
 // The geometry of an item: MB 32-row activation blocks (BM = 32 MB rows)
-// against the 256 weight rows of a tile, and what follows from MB.
-template <int MB_>
+// against the 256 weight rows of a tile, and what follows from MB; SHUF: the
+// weight codes are pre-shuffled (mxfp4_preshuffle_weights' order).
+template <int MB_, bool SHUF_>
 struct Geo {
     static constexpr int MB = MB_;
+    static constexpr bool SHUF = SHUF_;
     static constexpr int BM = 32 * MB;
     using Shape = tiled::Shape<MB, 2, 1, 4>;      // the accumulator and epilogue layout
     // The activation ring: four stage buffers, each a __shared__ array of its
@@ -1265,12 +1267,12 @@ struct Offs {
 };
 
 template <class G>
-__device__ __forceinline__ Offs<G> offsets(int64_t K, int wave, bool shuffled) {
+__device__ __forceinline__ Offs<G> offsets(int64_t K, int wave) {
     const int lane = threadIdx.x & 63;
     const int r32 = lane & 31, h = lane >> 5;
     const uint32_t ldc = (uint32_t)(K / 2), lds_ = (uint32_t)(K / 32);
     Offs<G> o;
-    if (shuffled) {
+    if constexpr (G::SHUF) {
         // 32-row block b of the tile, stage kt, K-step t: 1 KiB at
         // ((b * K/256 + kt) * 4 + t) * 1024, lane l at 16 l
 #pragma unroll
@@ -1360,6 +1362,13 @@ __device__ __forceinline__ void load_sc(lds_u8* lds, int par, const Src& s, cons
 // the three loads after the first.
 template <class G>
 __device__ __forceinline__ void load_w(WSet& w, const Src& s, const Offs<G>& o, int kt) {
+    // Pre-shuffled, a load fills 8 whole 128-byte lines that nothing reads
+    // again: the non-temporal hint keeps them from pushing the activation
+    // rows, which the expert's other weight tiles read, out of L2 (measured
+    // 5% faster).  Row-major, a load takes 32 bytes of each of 32 lines and
+    // the next K-steps take the rest: there the hint made every GEMM ~40%
+    // slower, so row-major loads stay plain.
+    constexpr int CPOL = G::SHUF ? 2 : 0;   // nt
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -1367,7 +1376,7 @@ __device__ __forceinline__ void load_w(WSet& w, const Src& s, const Offs<G>& o, 
             w.c[i][t] = __builtin_bit_cast(
                 v4u,
                 __builtin_amdgcn_raw_buffer_load_b128(s.w, (int)(o.w[i] + o.wt * t),
-                                                      kt * (int)o.wk, 0));
+                                                      kt * (int)o.wk, CPOL));
 }
 
 // K-step T's activation fragments of the stage in ring buffer B (all MB
@@ -1520,16 +1529,16 @@ __device__ __forceinline__ void prologue(lds_u8* lds, const Ring& ring, const Sr
 }  // namespace rs
 
 // K % 1024 == 0 (stages of an item a multiple of 4).  MB 32-row activation
-// blocks a tile (4 or 5).  w_shuffled: the weight codes are in the order
+// blocks a tile (4 or 5).  SHUF: the weight codes are in the order
 // mxfp4_preshuffle_weights writes (N % 32 == 0).
-template <int MB, bool OUT_BF16, bool GLU = false, bool UOS = false>
+template <int MB, bool OUT_BF16, bool GLU, bool UOS, bool SHUF>
 __global__ __launch_bounds__(256, 1) void grouped_stream_kernel(
     const uint8_t* __restrict__ x, const uint8_t* __restrict__ xs,
     const uint8_t* __restrict__ w, const uint8_t* __restrict__ ws,
     const int32_t* __restrict__ offsets, int E, int total_M, int64_t N, int64_t K,
-    void* __restrict__ y, uint8_t* __restrict__ hs, int w_shuffled) {
+    void* __restrict__ y, uint8_t* __restrict__ hs) {
     static_assert(!GLU || OUT_BF16, "the GLU epilogue parks bf16");
-    using G = rs::Geo<MB>;
+    using G = rs::Geo<MB, SHUF>;
     using S = typename G::Shape;
     using T = Stage<S, OUT_BF16>;
     constexpr int TABLE = G::LDS_END;
@@ -1556,7 +1565,7 @@ __global__ __launch_bounds__(256, 1) void grouped_stream_kernel(
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nkt = (int)(K / 256);             // a multiple of 4
-    const rs::Offs<G> o = rs::offsets<G>(K, wave, w_shuffled != 0);
+    const rs::Offs<G> o = rs::offsets<G>(K, wave);
     GroupItem it = decode_item<S::BM>(tb, E, tiles_n, t, 0);
     if (it.e < 0) return;
     rs::Src cur = rs::item_src(it, x, xs, w, ws, N, K);
@@ -1798,15 +1807,25 @@ hipError_t launch_grouped_gemm_tiled(const uint8_t* a_codes, const uint8_t* a_sc
     if (grouped_stream_ok(K)) {
         auto go = [&](auto kernel) {
             hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, a_codes, a_scales, b_codes,
-                               b_scales, offsets, (int)E, (int)total_M, N, K, y, none,
-                               (int)b_shuffled);
+                               b_scales, offsets, (int)E, (int)total_M, N, K, y, none);
         };
-        if (grouped_wide_tile(E, total_M))
-            out_bf16 ? go(tiled::grouped_stream_kernel<5, true>)
-                     : go(tiled::grouped_stream_kernel<5, false>);
-        else
-            out_bf16 ? go(tiled::grouped_stream_kernel<4, true>)
-                     : go(tiled::grouped_stream_kernel<4, false>);
+        using tiled::grouped_stream_kernel;
+        const bool wide = grouped_wide_tile(E, total_M);
+        if (b_shuffled) {
+            if (wide)
+                out_bf16 ? go(grouped_stream_kernel<5, true, false, false, true>)
+                         : go(grouped_stream_kernel<5, false, false, false, true>);
+            else
+                out_bf16 ? go(grouped_stream_kernel<4, true, false, false, true>)
+                         : go(grouped_stream_kernel<4, false, false, false, true>);
+        } else {
+            if (wide)
+                out_bf16 ? go(grouped_stream_kernel<5, true, false, false, false>)
+                         : go(grouped_stream_kernel<5, false, false, false, false>);
+            else
+                out_bf16 ? go(grouped_stream_kernel<4, true, false, false, false>)
+                         : go(grouped_stream_kernel<4, false, false, false, false>);
+        }
     } else {
         if (b_shuffled) return hipErrorInvalidValue;   // the caller checks this first
         auto go = [&](auto kernel) {
@@ -1835,14 +1854,25 @@ hipError_t launch_grouped_glu_quant(const uint8_t* a_codes, const uint8_t* a_sca
         auto go = [&](auto kernel) {
             hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, a_codes, a_scales, b_codes,
                                b_scales, offsets, (int)E, (int)total_M, N, K,
-                               static_cast<void*>(h_codes), h_scales, (int)b_shuffled);
+                               static_cast<void*>(h_codes), h_scales);
         };
-        if (grouped_wide_tile(E, total_M))
-            uos ? go(tiled::grouped_stream_kernel<5, true, true, true>)
-                : go(tiled::grouped_stream_kernel<5, true, true, false>);
-        else
-            uos ? go(tiled::grouped_stream_kernel<4, true, true, true>)
-                : go(tiled::grouped_stream_kernel<4, true, true, false>);
+        using tiled::grouped_stream_kernel;
+        const bool wide = grouped_wide_tile(E, total_M);
+        if (b_shuffled) {
+            if (wide)
+                uos ? go(grouped_stream_kernel<5, true, true, true, true>)
+                    : go(grouped_stream_kernel<5, true, true, false, true>);
+            else
+                uos ? go(grouped_stream_kernel<4, true, true, true, true>)
+                    : go(grouped_stream_kernel<4, true, true, false, true>);
+        } else {
+            if (wide)
+                uos ? go(grouped_stream_kernel<5, true, true, true, false>)
+                    : go(grouped_stream_kernel<5, true, true, false, false>);
+            else
+                uos ? go(grouped_stream_kernel<4, true, true, true, false>)
+                    : go(grouped_stream_kernel<4, true, true, false, false>);
+        }
     } else {
         if (b_shuffled) return hipErrorInvalidValue;   // the caller checks this first
         auto go = [&](auto kernel) {
