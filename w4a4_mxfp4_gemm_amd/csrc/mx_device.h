@@ -22,11 +22,13 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// Two fp32 -> packed bf16 (RNE; gfx950 v_cvt_pk_bf16_f32), a in the low half.
+// Two fp32 -> packed bf16 (RNE), a in the low half: one v_cvt_pk_bf16_f32.
+// (Two scalar casts compile to two of them, each with a zero partner, plus a
+// shift and an OR.)
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-    const __bf16 lo = (__bf16)a, hi = (__bf16)b;
-    return (uint32_t)__builtin_bit_cast(uint16_t, lo) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+    typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+    typedef float f32x2_v __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_v{a, b}, bf16x2_v));
 }
 
 // float8_e4m3fn byte -> fp32 (exact): bias 7, exponent field 0 subnormal,
