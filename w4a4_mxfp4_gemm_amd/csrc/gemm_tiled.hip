@@ -473,8 +473,9 @@ __device__ __forceinline__ v4f bias4(const uint16_t* __restrict__ bias, int64_t 
     return r;
 }
 
-// BIAS: bias[n] (bf16) joins each fp32 sum before its one rounding.
-template <class S, bool OUT_BF16, int ROWS, bool BIAS = false>
+// BIAS: bias[n] (bf16) joins each fp32 sum before its one rounding.  BUF:
+// whole pieces through a buffer descriptor (below).
+template <class S, bool OUT_BF16, int ROWS, bool BIAS = false, bool BUF = false>
 __device__ __forceinline__ void store_tile(const v16f (&acc)[S::NB][S::MB], lds_u8* stage,
                                            void* __restrict__ y, int64_t m0, int64_t m_end,
                                            int64_t n0, int64_t N, int wn, int wm,
@@ -490,6 +491,16 @@ __device__ __forceinline__ void store_tile(const v16f (&acc)[S::NB][S::MB], lds_
     const int r32 = lane & 31, h = lane >> 5;
     const bool vec_ok = (N % T::EPC) == 0 && (reinterpret_cast<uintptr_t>(y) % 16) == 0;
     const int64_t col0 = n0 + wn * 32 * S::NB;
+    // BUF: whole 16-byte pieces go through a buffer descriptor over the
+    // pass's rows: its range drops the rows past m_end, and a piece past N
+    // gets an offset beyond any range.  Each store is then one 32-bit offset,
+    // not a 64-bit address, two 64-bit compares and a branch.  The wave's
+    // rows must span under 2 GiB of y.  Measured 1-2% faster for the grouped
+    // GEMMs, whose epilogues nothing overlaps; no gain for the dense tiles.
+    const int64_t pitch = N * T::ESIZE;
+    const bool fast =
+        BUF && vec_ok && col0 < N && pitch * (32 * S::MB) < ((int64_t)1 << 31);
+    const int cols_left = (int)min(N - col0, (int64_t)(32 * S::NB));
 #pragma unroll
     for (int j = 0; j < S::MB; ++j) {
 #pragma unroll
@@ -521,6 +532,26 @@ __device__ __forceinline__ void store_tile(const v16f (&acc)[S::NB][S::MB], lds_
                 }
             }
             asm volatile("" ::: "memory");         // reads after the writes
+            if (fast) {
+                const int64_t rows_left = m_end - row0;   // > 0
+                const int ipitch = (int)pitch;
+                const __amdgpu_buffer_rsrc_t out = __builtin_amdgcn_make_buffer_rsrc(
+                    reinterpret_cast<uint8_t*>(y) + row0 * pitch + col0 * T::ESIZE, (short)0,
+                    (int)(min(rows_left, (int64_t)ROWS) * pitch - col0 * T::ESIZE), 0x00020000);
+#pragma unroll
+                for (int q = 0; q < ROWS * T::CHUNKS / 64; ++q) {
+                    const int c = q * 64 + lane;
+                    const int rr = c / T::CHUNKS, cc = c % T::CHUNKS;
+                    const v4u v = *reinterpret_cast<const __attribute__((address_space(3))) v4u*>(
+                        stage + rr * T::PITCH + cc * 16);
+                    const int off = cc * T::EPC < cols_left ? rr * ipitch + cc * 16 : 0x7FFFFFF0;
+                    // non-temporal, as below
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, v), out, off,
+                                                           0, 2);
+                }
+                asm volatile("" ::: "memory");     // next writes after the reads
+                continue;
+            }
 #pragma unroll
             for (int q = 0; q < ROWS * T::CHUNKS / 64; ++q) {
                 const int c = q * 64 + lane;
@@ -1593,8 +1624,9 @@ __global__ __launch_bounds__(256, 1) void grouped_stream_kernel(
                                          static_cast<uint8_t*>(y), hs, it.m0, it.m_end,
                                          (int64_t)it.tn * S::BN, N, wave, 0);
         else
-            store_tile<S, OUT_BF16, ROWS>(acc, lds + STAGE_BASE + wave * T::bytes(ROWS), y,
-                                          it.m0, it.m_end, (int64_t)it.tn * S::BN, N, wave, 0);
+            store_tile<S, OUT_BF16, ROWS, false, true>(acc, lds + STAGE_BASE + wave * T::bytes(ROWS),
+                                                       y, it.m0, it.m_end, (int64_t)it.tn * S::BN,
+                                                       N, wave, 0);
         if (!have_next) break;
         rezero_acc<S>(acc);
         it = nx;
