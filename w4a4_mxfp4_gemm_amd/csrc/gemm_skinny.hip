@@ -537,8 +537,12 @@ static hipError_t launch_k(const uint8_t* a, const uint8_t* as, int64_t ldx, con
     if (M <= 48)
         return launch_mt<3, SPW, NW4096, A8>(a, as, ldx, b, bs, M, N, K, y, bias, out_bf16,
                                                 stream);
-    return launch_mt<4, SPW, NW4096, A8>(a, as, ldx, b, bs, M, N, K, y, bias, out_bf16,
-                                            stream);
+    // four activation blocks of E4M3 (twice the E2M1 registers) spill at two
+    // wavefronts per SIMD: one wavefront per SIMD, two super-steps each
+    if constexpr (A8)
+        return launch_mt<4, 2, 4, true>(a, as, ldx, b, bs, M, N, K, y, bias, out_bf16, stream);
+    else
+        return launch_mt<4, SPW, NW4096>(a, as, ldx, b, bs, M, N, K, y, bias, out_bf16, stream);
 }
 
 // two wavefronts per SIMD (at K = 4096; measured 0.3-0.5 us less than one
@@ -555,11 +559,6 @@ hipError_t launch_gemm_skinny_w4a8(const uint8_t* a_codes, const uint8_t* a_scal
                                    const uint8_t* b_codes, const uint8_t* b_scales, int64_t M,
                                    int64_t N, int64_t K, void* y, const uint16_t* bias,
                                    bool out_bf16, hipStream_t stream) {
-    // four activation blocks of E4M3 (twice the E2M1 registers) spill at two
-    // wavefronts per SIMD: one wavefront per SIMD, two super-steps each
-    if (M > 48 && K == 4096)
-        return launch_mt<4, 2, 4, true>(a_codes, a_scales, 0, b_codes, b_scales, M, N, K, y,
-                                        bias, out_bf16, stream);
     return launch_k<8, true>(a_codes, a_scales, 0, b_codes, b_scales, M, N, K, y, bias, out_bf16,
                              stream);
 }
