@@ -422,6 +422,19 @@ hipError_t launch_silu_mul_quantize(const uint16_t* gate_up, int64_t ldg, int64_
     return hipGetLastError();
 }
 
+// Workgroups of the whole-batch requant kernel resident on the current
+// device at once (0 if the runtime cannot say).
+static int64_t requant_resident_workgroups() {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void*>(requant_kernel<false, 1, false>), 256, 0) !=
+            hipSuccess)
+        return 0;
+    return (int64_t)cus * per_cu;
+}
+
 hipError_t launch_requant(const uint8_t* nv_codes, const uint8_t* nv_scales,
                           const float* nv_global, int64_t T, int64_t N, int64_t K,
                           const int32_t* tensors, int64_t n_tensors, uint8_t* mx_codes,
@@ -430,6 +443,14 @@ hipError_t launch_requant(const uint8_t* nv_codes, const uint8_t* nv_scales,
     const int64_t bpt = N * (K / 32);
     int64_t gx = (bpt + 511) / 512;
     if (gx > 8192) gx = 8192;
+    // One tensor: at most one round of resident workgroups, each walking
+    // the tensor's blocks, rather than a second, partly filled round.  For
+    // a [12288, 4096] weight (3072 workgroup steps of 512 blocks) measured
+    // 12.9 -> 11.9 us.
+    if (!tensors && T == 1) {
+        static const int64_t resident = requant_resident_workgroups();
+        if (resident > 0 && gx > resident) gx = resident;
+    }
     auto grid = [&](int64_t count) {
         return dim3((unsigned)gx, (unsigned)(count > 65535 ? 65535 : count));
     };
