@@ -343,6 +343,17 @@ __global__ __launch_bounds__(256) void requant_kernel(
     }
 }
 
+// 256-thread workgroups of `kernel` resident on the current device at once
+// (0 if the runtime cannot say).
+static int64_t resident_workgroups(const void* kernel) {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess)
+        return 0;
+    return (int64_t)cus * per_cu;
+}
+
 hipError_t launch_act_quant(const uint16_t* x, int64_t ldx, const int32_t* row_index,
                             int64_t M, int64_t K, uint8_t* codes, uint8_t* scales, bool uos,
                             hipStream_t stream, const uint16_t* smooth) {
@@ -351,6 +362,16 @@ hipError_t launch_act_quant(const uint16_t* x, int64_t ldx, const int32_t* row_i
     const int64_t gx = (chunks + 255) / 256;
     int64_t gy = (M + ROWS - 1) / ROWS;
     if (gy > 65535) gy = 65535;
+    // Between one and two rounds of resident workgroups: three quarters of
+    // one round, each walking more rows, rather than a second partial round
+    // ([4096, 4096]: 8.82 -> 8.37 us; one quarter of a round, or capping the
+    // seven rounds of [4096, 14336], measured slower).
+    {
+        static const int64_t resident = resident_workgroups(
+            reinterpret_cast<const void*>(act_quant_kernel<ROWS, false, false>));
+        if (resident > 0 && gx * gy > resident && gx * gy <= 2 * resident)
+            gy = (resident * 3 / 4 + gx - 1) / gx;
+    }
     // codes past 16 MiB (more than the next GEMM finds in L2) go out
     // non-temporally unless gathered (a gathered batch is the MoE one, whose
     // GEMM re-reads each expert's rows): measured 7% faster at [4096,14336],
@@ -422,19 +443,6 @@ hipError_t launch_silu_mul_quantize(const uint16_t* gate_up, int64_t ldg, int64_
     return hipGetLastError();
 }
 
-// Workgroups of the whole-batch requant kernel resident on the current
-// device at once (0 if the runtime cannot say).
-static int64_t requant_resident_workgroups() {
-    int dev = 0, cus = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void*>(requant_kernel<false, 1, false>), 256, 0) !=
-            hipSuccess)
-        return 0;
-    return (int64_t)cus * per_cu;
-}
-
 hipError_t launch_requant(const uint8_t* nv_codes, const uint8_t* nv_scales,
                           const float* nv_global, int64_t T, int64_t N, int64_t K,
                           const int32_t* tensors, int64_t n_tensors, uint8_t* mx_codes,
@@ -448,7 +456,8 @@ hipError_t launch_requant(const uint8_t* nv_codes, const uint8_t* nv_scales,
     // a [12288, 4096] weight (3072 workgroup steps of 512 blocks) measured
     // 12.9 -> 11.9 us.
     if (!tensors && T == 1) {
-        static const int64_t resident = requant_resident_workgroups();
+        static const int64_t resident =
+            resident_workgroups(reinterpret_cast<const void*>(requant_kernel<false, 1, false>));
         if (resident > 0 && gx > resident) gx = resident;
     }
     auto grid = [&](int64_t count) {
