@@ -187,7 +187,8 @@ def grouped_exact_at(ac, as_, wc, ws, offsets):
 
 def test_moe_grouped_gemms_every_output(mx, moe):
     """Both grouped GEMMs over every routed row: gate_up on the gathered token
-    rows, down on a synthetic bf16 [16384, 1024] input N(0, 1)."""
+    rows, down on a synthetic bf16 [16384, 1024] input N(0, 1).  The bench
+    runs them on pre-shuffled weights: that call must give the same bytes."""
     d = dev()
     off = moe["offsets"]
     cases = [("gate_up", moe["tokens"], moe["perm"], 35), ("down", None, None, 35)]
@@ -203,7 +204,12 @@ def test_moe_grouped_gemms_every_output(mx, moe):
         wc, ws = moe["gpu"][name]
         y = mx.mxfp4_grouped_gemm(xc, xs, wc, ws, torch.from_numpy(off).to(d),
                                   out_dtype=torch.bfloat16)
+        ysh = mx.mxfp4_grouped_gemm(xc, xs, mx.mxfp4_preshuffle_weights(wc), ws,
+                                    torch.from_numpy(off).to(d), out_dtype=torch.bfloat16,
+                                    b_preshuffled=True)
         torch.cuda.synchronize()
+        assert torch.equal(ysh, y), f"{name}: pre-shuffled weights"
+        del ysh
         assert np.array_equal(u8(xc), ac) and np.array_equal(u8(xs), as_), f"{name} act-quant"
         owc, ows = moe["orc"][name]
         yo, _ = grouped_blas(ac, as_, owc, ows, off)
@@ -319,7 +325,16 @@ def test_moe_layer_every_output(mx, moe, gate_up_oracle):
     y2 = mx.mxfp4_grouped_gemm(hc, hs, *moe["gpu"]["down"], off, out_dtype=torch.bfloat16)
     out = mx.mxfp4_moe_combine(y2, rows, torch.from_numpy(moe["weights"]).to(d),
                                out_dtype=torch.float32)
+    # the bench's configuration: both grouped GEMMs on pre-shuffled weights
+    (gwc, gws), (dwc, dws) = moe["gpu"]["gate_up"], moe["gpu"]["down"]
+    hcs, hss = mx.mxfp4_grouped_gemm_silu_quantize(xc, xs, mx.mxfp4_preshuffle_weights(gwc), gws,
+                                                   off, b_preshuffled=True)
+    y2s = mx.mxfp4_grouped_gemm(hc, hs, mx.mxfp4_preshuffle_weights(dwc), dws, off,
+                                out_dtype=torch.bfloat16, b_preshuffled=True)
     torch.cuda.synchronize()
+    assert torch.equal(hcs, hc) and torch.equal(hss, hs), "gate_up: pre-shuffled weights"
+    assert torch.equal(y2s, y2), "down: pre-shuffled weights"
+    del hcs, hss, y2s
     assert np.array_equal(u8(xc), moe["ac"]) and np.array_equal(u8(xs), moe["as"]), "dispatch"
 
     nominal, hmin, hmax = h_range(*gate_up_oracle)
