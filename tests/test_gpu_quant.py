@@ -437,3 +437,54 @@ def test_act_quant_scatter_clamps_bad_rows(mx):
             d = clamped[t, j]
             if owners[d] == 1 and dest[t, j] == d:
                 assert np.array_equal(u8(gc.view)[d], oc[t]) and np.array_equal(u8(gs.view)[d], os_[t])
+
+
+_FIRST_CALLS_IN_CAPTURE = r"""
+import sys, torch
+sys.path.insert(0, sys.argv[1])
+import w4a4_mxfp4_gemm_amd as mx
+d = torch.device("cuda:0")
+g = torch.Generator().manual_seed(5)
+x = torch.randn((4096, 4096), generator=g).to(torch.bfloat16).to(d)
+nc = torch.randint(0, 256, (12288, 2048), dtype=torch.uint8, generator=g).to(d)
+ns = torch.randint(0, 127, (12288, 256), dtype=torch.uint8, generator=g).to(d)
+ng = torch.tensor([0.25], dtype=torch.float32).to(d)
+c, s = torch.empty((4096, 2048), dtype=torch.uint8, device=d), torch.empty((4096, 128), dtype=torch.uint8, device=d)
+oc, os_ = torch.empty((12288, 2048), dtype=torch.uint8, device=d), torch.empty((12288, 128), dtype=torch.uint8, device=d)
+stream = torch.cuda.Stream()
+graph = torch.cuda.CUDAGraph()
+with torch.cuda.stream(stream):
+    with torch.cuda.graph(graph, stream=stream):
+        mx.mxfp4_quantize_act(x, codes=c, scales=s)
+        mx.mxfp4_requant_from_nvfp4(nc, ns, ng, mx_codes=oc, mx_scales=os_)
+for _ in range(3):
+    c.zero_(); oc.zero_()
+    graph.replay()
+    torch.cuda.synchronize()
+    ec, es = mx.mxfp4_quantize_act(x)
+    rc, rs = mx.mxfp4_requant_from_nvfp4(nc, ns, ng)
+    torch.cuda.synchronize()
+    assert torch.equal(c, ec) and torch.equal(s, es), "act-quant replay"
+    assert torch.equal(oc, rc) and torch.equal(os_, rs), "requant replay"
+print("first calls inside capture ok", flush=True)
+"""
+
+
+def test_first_quantizer_calls_inside_graph_capture(mx, tmp_path):
+    """The grid sizing of the act-quant and single-tensor requant queries the
+    runtime once, at the first call.  In a fresh process whose first such
+    calls are made during HIP graph capture, the calls still succeed, and
+    every replay equals the eager result bit for bit (the shapes are the ones
+    whose grids are resized: [4096, 4096] activations, one [12288, 4096]
+    weight)."""
+    import pathlib
+    import subprocess
+    import sys
+    say("first act-quant / requant calls inside graph capture (fresh process)")
+    script = tmp_path / "first_calls.py"
+    script.write_text(_FIRST_CALLS_IN_CAPTURE)
+    root = pathlib.Path(__file__).resolve().parent.parent
+    r = subprocess.run([sys.executable, str(script), str(root)], capture_output=True, text=True,
+                       timeout=240)
+    assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-3000:]
+    assert "first calls inside capture ok" in r.stdout

@@ -344,13 +344,16 @@ __global__ __launch_bounds__(256) void requant_kernel(
 }
 
 // 256-thread workgroups of `kernel` resident on the current device at once
-// (0 if the runtime cannot say).
+// (0 if the runtime cannot say; the failed query's error is then cleared,
+// so that the launch that follows reports only its own).
 static int64_t resident_workgroups(const void* kernel) {
     int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess)
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess) {
+        (void)hipGetLastError();
         return 0;
+    }
     return (int64_t)cus * per_cu;
 }
 
