@@ -170,8 +170,10 @@ class Phases:
             self.graphs[name] = gs
         torch.cuda.synchronize()
 
-    def time(self, name, reps, warmup):
-        """Average milliseconds per slot (per step for the step phase)."""
+    def time(self, name, reps, warmup, per_rep=None):
+        """Average milliseconds per slot (per step for the step phase).  With
+        `per_rep` (a list), an event after each replay also appends each
+        replay's milliseconds to it; the average still spans all replays."""
         torch = self.torch
         gs = self.graphs[name]
         per_replay = 1 if name == "step" else self.slots * self.rounds
@@ -180,11 +182,20 @@ class Phases:
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
+        marks = []
         e0.record()
         for i in range(reps):
             gs[i % len(gs)].replay()
+            if per_rep is not None:
+                marks.append(torch.cuda.Event(enable_timing=True))
+                marks[-1].record()
         e1.record()
         torch.cuda.synchronize()
+        if per_rep is not None:
+            prev = e0
+            for m in marks:
+                per_rep.append(prev.elapsed_time(m) / per_replay)
+                prev = m
         return e0.elapsed_time(e1) / (reps * per_replay)
 
     def time_all(self, reps):
@@ -843,8 +854,11 @@ def main():
     ph.capture()
     # the contract's timed region: exactly `steps` steps after `warmup` untimed ones,
     # synchronised on both sides (one process, one GPU)
-    t = {"step": ph.time("step", args.steps, args.warmup)}
+    per_step = []
+    t = {"step": ph.time("step", args.steps, args.warmup, per_step)}
     total_ms = t["step"] * args.steps
+    q = sorted(per_step)
+    pick = lambda f: q[min(len(q) - 1, int(round(f * (len(q) - 1))))]
     reps = max(3, args.steps // max(1, ph.slots))
     t.update(ph.time_all(reps))
     value, unit, roof, extra, cfg = report(t, peaks)
@@ -868,7 +882,9 @@ def main():
 
     out = {"metric": METRIC, "value": round(value, 4), "unit": unit, "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup,
-           "ms_per_step": round(total_ms / args.steps, 4), "higher_is_better": True,
+           "ms_per_step": round(total_ms / args.steps, 4),
+           "step_ms_median_p10_p90": [round(pick(0.5), 4), round(pick(0.1), 4), round(pick(0.9), 4)],
+           "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": "mxfp4 (e2m1 x e8m0, fp32 acc)",
            "data": "synthetic (seeded; NVFP4 weights from bf16 N(0,0.02), bf16 activations "
                    "N(0,1) with 1% outlier channels x50)",
