@@ -238,6 +238,22 @@ def test_grouped_gemm_tiled_row_blocks(mx, K, rows):
     assert np.array_equal(bf16_bits(yb), bf16_bits(gy.to(torch.bfloat16)))
 
 
+@pytest.mark.parametrize("N", [296, 352])
+def test_grouped_gemm_stream_partial_wave_columns(mx, N):
+    """bf16 and fp32 out with N a multiple of 8 but not of 64, so that in the
+    last weight tile one wave owns 40 (N = 296) or 32 (N = 352) valid columns
+    and the waves past it none: the register-streamed kernel's epilogue
+    drops the pieces past N through its store descriptor.  Expert sizes as
+    in the 160-row tile case, K = 1024; fp32 against the oracle, bf16 equal
+    to the RNE of the fp32 result."""
+    counts = ROW_BLOCK_COUNTS["tile160"]
+    say(f"grouped stream partial wave columns N={N}")
+    gy, y, s = grouped_case(mx, counts, N, 1024, 57, torch.float32)
+    assert_gemm_fp32(gy, y, s, "grouped stream")
+    yb, _, _ = grouped_case(mx, counts, N, 1024, 57, torch.bfloat16)
+    assert np.array_equal(bf16_bits(yb), bf16_bits(gy.to(torch.bfloat16)))
+
+
 def test_grouped_gemm_stream_many_items(mx):
     """More work items than workgroups (480 items of 4 stages over 96 experts),
     so the workgroups walk several: each item's first stages arrive during
