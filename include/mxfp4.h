@@ -55,7 +55,7 @@ typedef enum {
     MXFP4_OK = 0,
     MXFP4_EINVAL = -1,       /* bad size, null pointer, unknown flag/dtype    */
     MXFP4_EALIGN = -2,       /* a pointer or leading dimension misaligned     */
-    MXFP4_EUNSUPPORTED = -3, /* valid request this build does not implement   */
+    MXFP4_EUNSUPPORTED = -3, /* valid request the library does not implement  */
     MXFP4_EHIP = -4,         /* the HIP runtime refused a launch              */
     MXFP4_ESCRATCH = -5      /* needs more than mxfp4_linear_bf16_noalloc's
                                 static scratch (MXFP4_NOALLOC_SCRATCH_BYTES)  */
