@@ -132,10 +132,13 @@ class Phases:
     """Named launch sequences captured into HIP graphs and timed by replaying
     the graphs back to back between two HIP events recorded on the stream the
     kernels run on.  The step phase gets one graph per rotation slot (one
-    replay = one step); every other phase gets a single graph holding all slots
-    in turn, repeated until it holds at least `min_launches` passes, so short
-    kernels run back to back on the GPU and the time per pass is not bounded
-    by the host's graph-launch rate."""
+    replay = one step) for the warm-up and the per-step distribution, and its
+    timed steps replay graphs that each hold G consecutive steps (G = gcd of
+    the step count and the slot count), since each graph launch leaves the GPU
+    idle for a few microseconds.  Every other phase gets a single graph holding
+    all slots in turn, repeated until it holds at least `min_launches` passes,
+    so short kernels run back to back on the GPU and the time per pass is not
+    bounded by the host's graph-launch rate."""
 
     def __init__(self, torch, slots, min_launches=20):
         self.torch = torch
@@ -170,32 +173,52 @@ class Phases:
             self.graphs[name] = gs
         torch.cuda.synchronize()
 
+    def chained_steps(self, g):
+        """Graphs of g consecutive steps, slots / g of them, covering the slots
+        in order (g divides the slot count)."""
+        torch = self.torch
+        fn = self.fns["step"]
+        gs = []
+        for b in range(self.slots // g):
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for r in range(b * g, b * g + g):
+                    fn(r)
+            gs.append(graph)
+        torch.cuda.synchronize()
+        return gs
+
     def time(self, name, reps, warmup, per_rep=None):
         """Average milliseconds per slot (per step for the step phase).  With
-        `per_rep` (a list), an event after each replay also appends each
-        replay's milliseconds to it; the average still spans all replays."""
+        `per_rep` (a list, step phase only), a second pass of `reps` steps, one
+        graph and one event per step, appends each step's milliseconds to it;
+        the average comes from the first pass alone."""
         torch = self.torch
         gs = self.graphs[name]
         per_replay = 1 if name == "step" else self.slots * self.rounds
+        timed, n = gs, reps
+        if name == "step":
+            self.steps_per_graph = g = math.gcd(reps, self.slots)
+            if g > 1:
+                timed, n = self.chained_steps(g), reps // g
         for i in range(warmup):
             gs[i % len(gs)].replay()
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
-        marks = []
         e0.record()
-        for i in range(reps):
-            gs[i % len(gs)].replay()
-            if per_rep is not None:
-                marks.append(torch.cuda.Event(enable_timing=True))
-                marks[-1].record()
+        for i in range(n):
+            timed[i % len(timed)].replay()
         e1.record()
         torch.cuda.synchronize()
         if per_rep is not None:
-            prev = e0
-            for m in marks:
-                per_rep.append(prev.elapsed_time(m) / per_replay)
-                prev = m
+            marks = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+            marks[0].record()
+            for i in range(reps):
+                gs[i % len(gs)].replay()
+                marks[i + 1].record()
+            torch.cuda.synchronize()
+            per_rep.extend(a.elapsed_time(b) / per_replay for a, b in zip(marks, marks[1:]))
         return e0.elapsed_time(e1) / (reps * per_replay)
 
     def time_all(self, reps):
@@ -856,6 +879,7 @@ def main():
     # synchronised on both sides (one process, one GPU)
     per_step = []
     t = {"step": ph.time("step", args.steps, args.warmup, per_step)}
+    steps_per_graph = ph.steps_per_graph
     total_ms = t["step"] * args.steps
     q = sorted(per_step)
     pick = lambda f: q[min(len(q) - 1, int(round(f * (len(q) - 1))))]
@@ -883,7 +907,10 @@ def main():
     out = {"metric": METRIC, "value": round(value, 4), "unit": unit, "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": round(total_ms / args.steps, 4),
+           "steps_per_graph": steps_per_graph,
            "step_ms_median_p10_p90": [round(pick(0.5), 4), round(pick(0.1), 4), round(pick(0.9), 4)],
+           "step_ms_median_p10_p90_pass": "a second pass of the same steps, one graph and "
+                                          "one event per step",
            "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": "mxfp4 (e2m1 x e8m0, fp32 acc)",
            "data": "synthetic (seeded; NVFP4 weights from bf16 N(0,0.02), bf16 activations "
