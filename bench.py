@@ -304,11 +304,11 @@ def prefill_workload(torch, mx, synth):
                 "gemm_TFLOPs": round(2 * M * N * K / (tg * 1e-3) / 1e12, 1),
                 "TFLOPs_incl_act_quant": round(2 * M * N * K / ((ta + tg) * 1e-3) / 1e12, 1),
                 "act_quant_GBps": round(gb, 1), "act_quant_frac_hbm": round(gb / HBM_PEAK_GBPS, 4)}
-        # the dominant kernel: the 28672 x 4096 GEMM (persistent tile walk)
+        # the dominant kernel: the 28672 x 4096 GEMM (seven rounds of 256 x 256 tiles)
         N, K = 28672, 4096
         tg = t[f"gemm_{N}x{K}"]
         ach = 2 * M * N * K / (tg * 1e-3) / 1e12
-        roof = roofline("mxfp4_gemm M=4096 N=28672 K=4096 (gemm_persistent_kernel), bf16 out",
+        roof = roofline("mxfp4_gemm M=4096 N=28672 K=4096 (gemm_dense_kernel), bf16 out",
                         "mfma", ach, MXFP4_PEAK_TFLOPS, "TFLOP/s",
                         recorded_traffic("gemm_prefill", "hbm_bytes_per_dispatch_28672x4096"),
                         {"flop": 2 * M * N * K, "bytes": gemm_bytes(M, N, K)}, tg * 1e3,

@@ -39,8 +39,8 @@ SHAPES = [(1, 1, 32), (1, 300, 4096), (7, 17, 96), (16, 256, 512), (33, 200, 544
           # more weight tiles than a grid's slots hold at once (over 16 x 3 x 256
           # rows): each slot is refilled as it is consumed
           (3, 13000, 2048), (64, 12352, 2048),
-          # more tiles than one round on the chip (persistent walk, ragged M and
-          # N), with and without the next tile's stages streamed early
+          # more tiles than one round on the chip (ragged M and N), K of 4 and 2
+          # stages (the 8-wave pipeline's loads past the last stage)
           (2200, 7700, 1024), (2200, 7700, 512)]
 
 
@@ -500,7 +500,7 @@ def test_linear_bf16_uos_against_oracle(mx):
 def test_linear_bf16_row_bias(mx, M, N, K):
     """A bf16 row bias through every GEMM path (one-launch decode, skinny, with
     its slots refilled past 12288 rows, generic, tiled with a ragged N,
-    persistent), against the oracle's act-quant,
+    several rounds of tiles), against the oracle's act-quant,
     requant and GEMM plus the bias before the one rounding.  Sizes the oracle
     cannot finish whole are checked on sampled rows."""
     say(f"linear bf16 + bias M={M} N={N} K={K}")

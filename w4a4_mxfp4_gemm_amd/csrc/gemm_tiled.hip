@@ -1,15 +1,17 @@
 // gemm_tiled.hip -- MFMA-bound MXFP4 GEMM for many activation rows (prefill)
-// and its grouped form for MoE experts.  A workgroup of 4 wavefronts owns one
-// output tile; operands are staged in LDS by gfx950's buffer loads with LDS
-// destination and multiplied with v_mfma_scale_f32_32x32x64_f8f6f4.  (One
-// wavefront per SIMD keeps the matrix core busy with back-to-back 32x32x64
-// scaled MFMAs, but not with 16x16x128 ones, which is why the tiles use the
-// larger shape.)
+// and its grouped form for MoE experts.  A workgroup of 4 or 8 wavefronts
+// owns one output tile; operands are staged in LDS by gfx950's buffer loads
+// with LDS destination and multiplied with v_mfma_scale_f32_32x32x64_f8f6f4.
+// (One wavefront per SIMD keeps the matrix core busy with back-to-back
+// 32x32x64 scaled MFMAs, but not with 16x16x128 ones, which is why the tiles
+// use the larger shape.)
 //
 // Tile shapes (Shape<MB, NB, WGM, WGN>: each wave owns MB x NB blocks of
-// 32 x 32 outputs, the 4 waves form a WGM x WGN grid):
-//   dense    256 activation rows x 256 weight rows, waves 2 x 2, 128 x 128 each
-//   grouped  128 activation rows x 256 weight rows, waves 1 x 4, 128 x 64 each
+// 32 x 32 outputs, the waves form a WGM x WGN grid):
+//   dense    256 activation rows x 256 weight rows, 8 waves 2 x 4, 128 x 64 each
+//            (two per SIMD; its own K-step pipeline, gemm_dense_kernel)
+//   W4A8     128 activation rows x 256 weight rows, 4 waves 2 x 2, 64 x 128 each
+//   grouped  128 activation rows x 256 weight rows, 4 waves 1 x 4, 128 x 64 each
 // The grouped tile matches MoE expert groups of ~128 tokens: all four waves
 // stay busy, and 32-row blocks past the expert's last row skip their MFMAs.
 //
@@ -40,7 +42,7 @@
 // load instruction writes 1 KiB of consecutive LDS (8 rows), so the swizzle is
 // applied to the global address each lane fetches.
 //
-// Pipeline, per stage kt (one barrier per stage):
+// Pipeline of the 4-wave tiles, per stage kt (one barrier per stage):
 //   read half 1 of stage kt;  MFMAs on half 0;  wait for the reads
 //   wait for stage kt+1's loads; barrier; load stage kt+2 (+ one scale half-chunk)
 //   read half 0 of stage kt+1;  MFMAs on half 1;  wait for the reads
@@ -54,6 +56,7 @@
 
 #include <algorithm>
 #include <type_traits>
+#include <utility>
 
 namespace mx {
 namespace tiled {
@@ -73,7 +76,8 @@ constexpr int SCALE_CHUNK = 2 * SCALE_OPERAND;
 // fragment is two 16-byte reads (see read_offsets).
 template <int MB_, int NB_, int WGM_, int WGN_, bool A8_ = false>
 struct Shape {
-    static_assert(WGM_ * WGN_ == 4, "four wavefronts per workgroup");
+    static constexpr int NW = WGM_ * WGN_;                // wavefronts per workgroup
+    static_assert(NW == 4 || NW == 8, "four or eight wavefronts per workgroup");
     static constexpr int MB = MB_, NB = NB_, WGM = WGM_, WGN = WGN_;
     static constexpr bool A8 = A8_;
     static constexpr int BM = 32 * MB * WGM;              // activation rows per tile
@@ -81,8 +85,8 @@ struct Shape {
     static_assert(BM <= 256 && BN == 256, "scale staging holds 256 rows per operand");
     static constexpr int XBKB = A8 ? 2 * BKB : BKB;       // activation code bytes per row, stage
     static constexpr int XPARTS = A8 ? 2 : 1;             // 16-byte reads per activation fragment
-    static constexpr int WLOADS = BN / 32;                // 1 KiB code loads per thread per stage
-    static constexpr int XLOADS = BM * XBKB / 4096;
+    static constexpr int WLOADS = BN * BKB / 1024 / NW;   // 1 KiB code loads per thread per stage
+    static constexpr int XLOADS = BM * XBKB / 1024 / NW;
     static constexpr int W_OPERAND = BN * BKB;
     static constexpr int CODE_STAGE = BN * BKB + BM * XBKB;   // W then X
     static constexpr int SCALE_BASE = 2 * CODE_STAGE;     // after the two code stages
@@ -95,7 +99,7 @@ struct Shape {
     static_assert(LOADS_PER_STAGE <= 2 * SLOTS && CODE_READS <= SLOTS, "slot budget");
 };
 
-using DenseShape = Shape<4, 4, 2, 2>;
+using DenseShape = Shape<4, 2, 2, 4>;
 using GroupShape = Shape<4, 2, 1, 4>;
 // W4A8: 128 activation rows, so that two stages of 256-byte rows fit the LDS
 using W4A8Shape = Shape<2, 4, 2, 2, true>;
@@ -197,12 +201,13 @@ __device__ __forceinline__ void load_codes(lds_u8* lds, const Operands& op,
 
 // One operand's scales for chunk c (stages 2c, 2c+1) into ring slot `slot`:
 // 16 bytes per row, 256 rows (an activation tile of fewer rows repeats its
-// last row).
+// last row), one load by each of the first four wavefronts.
 template <class S>
 __device__ __forceinline__ void load_scales(lds_u8* lds, const Operands& op,
                                             const LoadOffsets<S>& o, bool weights, int c,
                                             int slot) {
     const int wave = wave_id();
+    if (S::NW > 4 && wave >= 4) return;       // wave-uniform
     lds_u8* dst = lds + S::SCALE_BASE + slot * SCALE_CHUNK + (weights ? 0 : SCALE_OPERAND) +
                   wave * 1024;
     dma16(weights ? op.ws : op.xs, dst, weights ? o.ws : o.xs, (uint32_t)c * 16);
@@ -870,11 +875,12 @@ __device__ __forceinline__ void store_tile_glu(const v16f (&acc)[S::NB][S::MB], 
     }
 }
 
-template <bool OUT_BF16, bool BIAS, class S = DenseShape>
+template <bool OUT_BF16, bool BIAS, class S>
 __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(
     const uint8_t* __restrict__ x, const uint8_t* __restrict__ xs,
     const uint8_t* __restrict__ w, const uint8_t* __restrict__ ws, int64_t M, int64_t N,
     int64_t K, void* __restrict__ y, int gm, const uint16_t* __restrict__ bias) {
+    static_assert(S::NW == 4, "the half-stage pipeline of four wavefronts");
     __shared__ __attribute__((aligned(16))) uint8_t smem[S::LDS_BYTES];
     const int tiles_m = (int)((M + S::BM - 1) / S::BM);
     const int tiles_n = (int)((N + S::BN - 1) / S::BN);
@@ -904,8 +910,8 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Dense GEMM, persistent, for more than one round of tiles and K >= 1024: one
-// workgroup per CU walks the tiles
+// Dense GEMM of a 4-wave shape (the W4A8 tile), persistent, for more than one
+// round of tiles and K >= 1024: one workgroup per CU walks the tiles
 //   t = xcd * ceil(total / 8) + local + k * (grid / 8)   (xcd = id % 8, local = id / 8)
 // (the XCD-contiguous runs above, now visited by the XCD's workgroups side by
 // side).  While a tile's last two stages run, the next tile's first stage
@@ -917,11 +923,12 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(
 // ---------------------------------------------------------------------------
 constexpr int LDS_LIMIT = 160 * 1024;           // LDS a workgroup may hold
 
-template <bool OUT_BF16, bool BIAS, class S = DenseShape>
+template <bool OUT_BF16, bool BIAS, class S>
 __global__ __launch_bounds__(256, 1) void gemm_persistent_kernel(
     const uint8_t* __restrict__ x, const uint8_t* __restrict__ xs,
     const uint8_t* __restrict__ w, const uint8_t* __restrict__ ws, int64_t M, int64_t N,
     int64_t K, void* __restrict__ y, int gm, const uint16_t* __restrict__ bias) {
+    static_assert(S::NW == 4, "the half-stage pipeline of four wavefronts");
     using T = Stage<S, OUT_BF16>;
     constexpr int ROWS = T::rows_for(S::WLOADS * 1024);   // a wave's weight rows of a stage
     __shared__ __attribute__((aligned(16))) uint8_t smem[S::LDS_BYTES];
@@ -974,6 +981,216 @@ __global__ __launch_bounds__(256, 1) void gemm_persistent_kernel(
         tn = tn_next;
     }
     wait_vm<0>();
+}
+
+// ---------------------------------------------------------------------------
+// Dense GEMM, 8 wavefronts: the 256 x 256 tile of DenseShape, each wave
+// 128 activation rows x 64 weight rows, two waves on every SIMD.  Whenever
+// one of a SIMD's waves stalls issuing a load or waiting on LDS, the other
+// can issue its MFMAs.  Its accumulators (128 registers) leave room for
+// only one K-step's fragments ahead, so the register pipeline runs at
+// K-step granularity; the LDS layout and the operand order are those of
+// the 4-wave tiles, and the outputs are bit-identical to theirs.
+//
+// Per stage kt (4 K-steps, one barrier):
+//   K-step 0: MFMAs on f0;  read K-step 1 into f1;  DMA group B of stage kt+1
+//   K-step 1: MFMAs on f1;  read K-step 2 into f0;  DMA group C of stage kt+1
+//   K-step 2: MFMAs on f0;  read K-step 3 into f1
+//   wait for this wave's loads (stage kt+1 landed); barrier
+//   K-step 3: MFMAs on f1;  read stage kt+1's K-step 0 into f0 and its scale
+//             words;  DMA group A of stage kt+2 (into stage kt's buffer,
+//             which no wave reads after the barrier) and its scale half-chunk
+// A stage's 8 code loads a wave are split into groups A, B, C of 4, 4, 0:
+// group A waits behind the barrier, B and C ride on the next stage's
+// K-steps.  Past the last stage the loads repeat the last stage (into a
+// buffer nothing reads again) and the reads fetch unused values, so every
+// stage issues the same instructions; the surplus loads drain at the end.
+// ---------------------------------------------------------------------------
+namespace d8 {
+
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// One K-step of one wave's operands: NB weight and MB activation fragments.
+template <class S>
+struct KFrag {
+    v4u w[S::NB], x[S::MB];
+};
+
+// Read R of K-step T of the stage at `codes`: weight fragments first.
+template <class S, int T, int R>
+__device__ __forceinline__ void kread(KFrag<S>& f, uint32_t codes, const ReadOffsets<S>& ro) {
+    if constexpr (R < S::NB)
+        ds_read_b128<R * 32 * BKB>(f.w[R], codes + ro.w[T]);
+    else
+        ds_read_b128<(R - S::NB) * 32 * BKB>(f.x[R - S::NB], codes + ro.x[T]);
+}
+template <class S, int R>
+__device__ __forceinline__ void sread(Scales<S>& sc, uint32_t scales, const ReadOffsets<S>& ro) {
+    if constexpr (R < S::NB)
+        ds_read_b32<R * 32 * 16>(sc.w[R], scales + ro.ws);
+    else
+        ds_read_b32<(R - S::NB) * 32 * 16>(sc.x[R - S::NB], scales + ro.xs);
+}
+
+// The MFMAs of K-step T; after MFMA q, step(q) issues that slot's reads and
+// loads.  Each MFMA is pinned in program order: left free, the compiler sank
+// them below the reads threaded between them, which kept several K-steps'
+// fragments alive at once and spilled.
+template <class S, int T, int Q = 0, typename Step>
+__device__ __forceinline__ void kmfma(const KFrag<S>& f, const Scales<S>& sc,
+                                      v16f (&acc)[S::NB][S::MB], Step&& step) {
+    if constexpr (Q < S::NB * S::MB) {
+        constexpr int i = Q / S::MB, j = Q % S::MB;
+        acc[i][j] = mfma<T>(f.w[i], f.x[j], acc[i][j], sc.w[i], sc.x[j]);
+        asm volatile("" ::"v"(acc[i][j]));
+        step(std::integral_constant<int, Q>{});
+        __builtin_amdgcn_sched_barrier(0);
+        kmfma<S, T, Q + 1>(f, sc, acc, step);
+    }
+}
+
+// Code load l of a stage (0 .. WLOADS + XLOADS - 1) in group [L0, L1),
+// spread over the K-step's MFMA slots: the load slot q issues, or -1.
+template <int L0, int L1, int SLOTS>
+constexpr int slot_load(int q) {
+    const int n = L1 - L0;
+    for (int k = 0; k < n; ++k)
+        if (q == k * SLOTS / n) return L0 + k;
+    return -1;
+}
+
+template <class S>
+struct Groups {
+    static constexpr int NL = S::WLOADS + S::XLOADS;   // code loads a wave, a stage
+    static constexpr int A = NL / 2;                   // [0, A) behind the barrier
+    static constexpr int B1 = NL;                      // [A, B1) in the next K-step 0
+    static_assert(A + 1 <= S::NB * S::MB, "group A and the scale load fit the slots");
+};
+
+// Stage 0, the scale chunks of stages 0-3 and stage 1's group A; then stage
+// 0's K-step 0 fragments and scale words.
+template <class S>
+__device__ __forceinline__ void prologue(lds_u8* lds, const TileSrc<S>& src,
+                                         const LoadOffsets<S>& lo, int nkt, KFrag<S>& f0,
+                                         Scales<S>& sc, const ReadOffsets<S>& ro) {
+    using G = Groups<S>;
+    const int c1 = nkt / 2 - 1 >= 1 ? 1 : 0;
+    load_codes<S>(lds, src.op, lo, 0, 0);
+    load_scales<S>(lds, src.op, lo, true, 0, 0);
+    load_scales<S>(lds, src.op, lo, false, 0, 0);
+    load_scales<S>(lds, src.op, lo, true, c1, c1);
+    load_scales<S>(lds, src.op, lo, false, c1, c1);
+    static_for<G::A>([&](auto l) {
+        load_op<S, decltype(l)::value>(lds, src, src, lo, 1, 1, true, 0, 0);
+    });
+    wait_vm<G::A>();                          // all but stage 1's group A
+    __builtin_amdgcn_s_barrier();
+    const uint32_t lds0 = lds_addr(lds);
+    static_for<S::NB + S::MB>([&](auto r) {
+        kread<S, 0, decltype(r)::value>(f0, code_addr(lds0, 0, S::CODE_STAGE), ro);
+        sread<S, decltype(r)::value>(sc, scale_addr<S>(lds0, 0, 0), ro);
+    });
+}
+
+template <class S>
+__device__ __forceinline__ void main_loop(lds_u8* lds, const TileSrc<S>& src,
+                                          const LoadOffsets<S>& lo, int nkt, KFrag<S>& f0,
+                                          KFrag<S>& f1, Scales<S>& sc,
+                                          v16f (&acc)[S::NB][S::MB], const ReadOffsets<S>& ro) {
+    using G = Groups<S>;
+    constexpr int SL = S::NB * S::MB;        // MFMA slots of a K-step
+    constexpr int NR = S::NB + S::MB;        // fragment reads of a K-step
+    static_assert(NR <= SL, "one fragment read and one scale read a slot");
+    const int last_chunk = nkt / 2 - 1;
+    const uint32_t lds0 = lds_addr(lds);
+    for (int kt = 0; kt < nkt; ++kt) {
+        const uint32_t codes = code_addr(lds0, kt, S::CODE_STAGE);
+        const int k1 = kt + 1;
+        const int ks1 = k1 < nkt ? k1 : nkt - 1;
+        kmfma<S, 0>(f0, sc, acc, [&](auto q) {
+            constexpr int Q = decltype(q)::value;
+            if constexpr (Q < NR) kread<S, 1, Q>(f1, codes, ro);
+            constexpr int L = slot_load<G::A, G::B1, SL>(Q);
+            if constexpr (L >= 0) load_op<S, L>(lds, src, src, lo, k1 & 1, ks1, true, 0, 0);
+        });
+        kmfma<S, 1>(f1, sc, acc, [&](auto q) {
+            constexpr int Q = decltype(q)::value;
+            if constexpr (Q < NR) kread<S, 2, Q>(f0, codes, ro);
+        });
+        kmfma<S, 2>(f0, sc, acc, [&](auto q) {
+            constexpr int Q = decltype(q)::value;
+            if constexpr (Q < NR) kread<S, 3, Q>(f1, codes, ro);
+        });
+        // stage kt+1 landed for every wave; every wave has issued its reads
+        // of stage kt (LDS reads finish long before a DMA's data arrives)
+        wait_vm<0>();
+        __builtin_amdgcn_s_barrier();
+        const int s2 = kt + 2;
+        const int ks2 = s2 < nkt ? s2 : nkt - 1;
+        const int c = min(s2 / 2 + 1, last_chunk);   // past the last: that chunk again
+        const bool scale_w = (s2 & 1) == 0;
+        const uint32_t ncodes = code_addr(lds0, k1, S::CODE_STAGE);
+        const uint32_t nscales = scale_addr<S>(lds0, 0, k1);
+        Scales<S> sn;
+        kmfma<S, 3>(f1, sc, acc, [&](auto q) {
+            constexpr int Q = decltype(q)::value;
+            if constexpr (Q < NR) {
+                kread<S, 0, Q>(f0, ncodes, ro);
+                sread<S, Q>(sn, nscales, ro);
+            }
+            constexpr int L = slot_load<0, G::A + 1, SL>(Q);   // group A, then the scales
+            if constexpr (L >= 0 && L < G::A)
+                load_op<S, L>(lds, src, src, lo, s2 & 1, ks2, true, 0, 0);
+            else if constexpr (L == G::A)
+                load_op<S, G::NL>(lds, src, src, lo, 0, 0, scale_w, c, c % 3);
+        });
+        sc = sn;
+    }
+}
+
+}  // namespace d8
+
+template <bool OUT_BF16, bool BIAS>
+__global__ __launch_bounds__(512, 1) void gemm_dense_kernel(
+    const uint8_t* __restrict__ x, const uint8_t* __restrict__ xs,
+    const uint8_t* __restrict__ w, const uint8_t* __restrict__ ws, int64_t M, int64_t N,
+    int64_t K, void* __restrict__ y, int gm, const uint16_t* __restrict__ bias) {
+    using S = DenseShape;
+    static_assert(S::NW == 8, "two wavefronts a SIMD");
+    __shared__ __attribute__((aligned(16))) uint8_t smem[S::LDS_BYTES];
+    const int tiles_m = (int)((M + S::BM - 1) / S::BM);
+    const int tiles_n = (int)((N + S::BN - 1) / S::BN);
+    int tm, tn;
+    if (!tile_coords(tiles_m, tiles_n, gm, tm, tn)) return;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wn = wave % S::WGN, wm = wave / S::WGN;
+    const int64_t m0 = (int64_t)tm * S::BM, n0 = (int64_t)tn * S::BN;
+    const int nkt = (int)(K / 256);           // even: K % 512 == 0
+    lds_u8* lds = (lds_u8*)smem;
+    const TileSrc<S> src = tile_src<S>(x, xs, w, ws, m0, M, n0, N, K);
+    const ReadOffsets<S> ro = read_offsets<S>(wn, wm);
+    const LoadOffsets<S> lo = load_offsets<S>(K / 2, K / 2, K / 32);
+    v16f acc[S::NB][S::MB];
+    zero_acc<S>(acc);
+    d8::KFrag<S> f0, f1;
+    Scales<S> sc;
+    d8::prologue<S>(lds, src, lo, nkt, f0, sc, ro);
+    d8::main_loop<S>(lds, src, lo, nkt, f0, f1, sc, acc, ro);
+    wait_vm<0>();                             // drain the surplus loads
+    // every wave is past its last read of the stage buffers, which now hold
+    // the eight waves' epilogue regions
+    __syncthreads();
+    using T = Stage<S, OUT_BF16>;
+    constexpr int ROWS = T::rows_for(S::SCALE_BASE / S::NW);
+    store_tile<S, OUT_BF16, ROWS, BIAS>(acc, lds + wave * T::bytes(ROWS), y, m0, M, n0, N, wn,
+                                        wm, bias);
 }
 
 // ---------------------------------------------------------------------------
@@ -1692,45 +1909,30 @@ hipError_t launch_gemm_tiled(const uint8_t* a_codes, const uint8_t* a_scales,
                              const uint8_t* b_codes, const uint8_t* b_scales, int64_t M,
                              int64_t N, int64_t K, void* y, const uint16_t* bias,
                              bool out_bf16, hipStream_t stream) {
+    // one 8-wave workgroup a tile, XCD-aware tile order (tile_coords): the
+    // tiles a round of resident workgroups covers on an XCD form a compact
+    // block, so its operand rows are read into that XCD's L2 once
     using S = tiled::DenseShape;
     const int tiles_m = (int)((M + S::BM - 1) / S::BM);
     const int tiles_n = (int)((N + S::BN - 1) / S::BN);
-    const int total = tiles_m * tiles_n;
-    const int per_xcd = (total + 7) / 8;
+    const int per_xcd = (tiles_m * tiles_n + 7) / 8;
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return hipErrorInvalidDevice;
     const int slots = cus / 8 > 0 ? cus / 8 : 1;   // resident workgroups per XCD
-    if (per_xcd > slots && K >= 1024) {
-        // more than one round: persistent, each XCD's workgroups walking its
-        // run side by side in compact blocks
-        const int gm = group_rows(tiles_m, slots);
-        const dim3 grid((unsigned)(slots * 8));
-        auto go = [&](auto kernel) {
-            hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, a_codes, a_scales, b_codes,
-                               b_scales, M, N, K, y, gm, bias);
-        };
-        if (bias)
-            out_bf16 ? go(tiled::gemm_persistent_kernel<true, true>)
-                     : go(tiled::gemm_persistent_kernel<false, true>);
-        else
-            out_bf16 ? go(tiled::gemm_persistent_kernel<true, false>)
-                     : go(tiled::gemm_persistent_kernel<false, false>);
-        return hipGetLastError();
-    }
-    const int gm = group_rows(tiles_m, per_xcd);
+    const int gm = group_rows(tiles_m, per_xcd < slots ? per_xcd : slots);
     const dim3 grid((unsigned)(per_xcd * 8));
     auto go = [&](auto kernel) {
-        hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, a_codes, a_scales, b_codes,
+        hipLaunchKernelGGL(kernel, grid, dim3(512), 0, stream, a_codes, a_scales, b_codes,
                            b_scales, M, N, K, y, gm, bias);
     };
     if (bias)
-        out_bf16 ? go(tiled::gemm_tiled_kernel<true, true>)
-                 : go(tiled::gemm_tiled_kernel<false, true>);
+        out_bf16 ? go(tiled::gemm_dense_kernel<true, true>)
+                 : go(tiled::gemm_dense_kernel<false, true>);
     else
-        out_bf16 ? go(tiled::gemm_tiled_kernel<true, false>)
-                 : go(tiled::gemm_tiled_kernel<false, false>);
+        out_bf16 ? go(tiled::gemm_dense_kernel<true, false>)
+                 : go(tiled::gemm_dense_kernel<false, false>);
     return hipGetLastError();
 }
 
@@ -1756,7 +1958,7 @@ hipError_t launch_gemm_tiled_w4a8(const uint8_t* a_codes, const uint8_t* a_scale
         return hipErrorInvalidDevice;
     const int slots = cus / 8 > 0 ? cus / 8 : 1;   // resident workgroups per XCD
     if (per_xcd > slots && K >= 1024) {
-        // more than one round: the persistent walk of the W4A4 prefill
+        // more than one round: the persistent walk
         const int gm = group_rows(tiles_m, slots);
         const dim3 grid((unsigned)(slots * 8));
         auto go = [&](auto kernel) {
