@@ -290,6 +290,49 @@ def prefill_workload(torch, mx, synth):
         ph.add(f"gemm_{N}x{K}", lambda r, xq=xq, wc=wc, wsc=wsc, y=y:
                mx.mxfp4_gemm(xq[r][0], xq[r][1], wc, wsc, y))
 
+    def vendor_library():
+        """The platform's MXFP4 GEMM (hipBLASLt, through torch._scaled_mm with
+        E2M1 operands and E8M0 scales) on the same quantized operands, beside
+        this library's GEMM, both timed the same way: eager launches between
+        two events, after a warm-up, interleaved.  Context only, outside the
+        timed region: hipBLASLt reads the scale tensors in a layout of its own,
+        so its outputs differ (max_rel_diff) and only its time compares."""
+        out = {"how": "torch._scaled_mm (hipBLASLt) vs mxfp4_gemm, 10 eager launches "
+                      "between events after 3, medians of 5 interleaved rounds; timing only"}
+        try:
+            f4, e8 = torch.float4_e2m1fn_x2, torch.float8_e8m0fnu
+            for N, K, wc, wsc, x, xq, y in data:
+                a, sa = xq[0]
+                lt = lambda: torch._scaled_mm(a.view(f4), wc.view(f4).t(), scale_a=sa.view(e8),
+                                              scale_b=wsc.view(e8), out_dtype=torch.bfloat16)
+                ours = lambda: mx.mxfp4_gemm(a, sa, wc, wsc, y)
+                times = {"hipblaslt": [], "ours": []}
+                for fn in (lt, ours):
+                    for _ in range(3):
+                        fn()
+                for _ in range(5):
+                    for name, fn in (("hipblaslt", lt), ("ours", ours)):
+                        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                        e0.record()
+                        for _ in range(10):
+                            fn()
+                        e1.record()
+                        torch.cuda.synchronize()
+                        times[name].append(e0.elapsed_time(e1) / 10 * 1e3)
+                yl = lt().float()
+                ours()
+                torch.cuda.synchronize()
+                tl, to = sorted(times["hipblaslt"])[2], sorted(times["ours"])[2]
+                out[f"{N}x{K}"] = {
+                    "hipblaslt_us": round(tl, 2), "ours_us": round(to, 2),
+                    "hipblaslt_TFLOPs": round(2 * M * N * K / (tl * 1e-6) / 1e12, 1),
+                    "ours_TFLOPs": round(2 * M * N * K / (to * 1e-6) / 1e12, 1),
+                    "max_rel_diff": float(((yl - y.float()).abs().max() / y.float().abs().max()).item())}
+                del yl
+        except Exception as ex:                 # the vendor path is optional context
+            out["error"] = repr(ex)[:300]
+        return out
+
     def report(t, peaks):
         flops = sum(2 * M * N * K for N, K in shapes)
         value = flops / (t["step"] * 1e-3) / 1e12
@@ -318,6 +361,7 @@ def prefill_workload(torch, mx, synth):
                  "step_frac_mfma_peak": round(value / MXFP4_PEAK_TFLOPS, 4)}
         if peaks.get("mfma_TFLOPs"):
             extra["step_frac_of_measured_mfma_peak"] = round(value / peaks["mfma_TFLOPs"], 4)
+        extra["vendor_library"] = vendor_library()
         cfg = {"workload": "prefill dense linears M=4096, (N,K) in (4096,4096),(28672,4096),"
                            "(4096,14336): act-quant + W4A4 GEMM, bf16 out",
                "M": M, "NK": [list(s) for s in shapes]}
