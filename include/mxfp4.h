@@ -35,8 +35,9 @@
  *     vectors 16 bytes.  Other scale pointers may have any alignment, but
  *     the fast GEMM kernels need them aligned (16 bytes for the decode
  *     kernel, 4 for the tiled ones) and a call whose scale pointers are not
- *     falls back to the generic kernel: the same results, slower.  Each GEMM
- *     call lists its kernel choice.
+ *     falls back to the generic kernel: results within the same tolerance
+ *     (the fp32 sums may round differently), slower.  Each GEMM call lists
+ *     its kernel choice.
  *   - Results are bitwise reproducible from run to run (no atomics, fixed
  *     reduction order).
  */
@@ -277,12 +278,15 @@ int mxfp4_quantize_act_smooth(const void* x_bf16, int64_t ldx, const int32_t* ro
  *   workspace           reserved: the current kernels need none; pass NULL
  *                       and 0 (mxfp4_gemm_workspace_size returns 0)
  *   flags               must be 0
- * Kernel choice (every kernel gives the same results):
+ * Kernel choice (every kernel meets the same tolerance; each is deterministic):
  *   M <= 64, K = 2048 or 4096, N >= 16, a_codes/a_scales/b_scales 16-byte
  *     aligned: the weight-streaming decode kernel;
+ *   else K % 512 == 0 with K <= 16384, the same alignment, N >= 16 and
+ *     M <= 64 (K <= 8192), 32 (K <= 12288) or 16 (K <= 16384): the
+ *     weight-streaming kernel with ceil(K / 4096) super-steps a wave;
  *   else M >= 128, K % 512 == 0, each operand's codes under 2 GiB, both scale
- *     pointers 4-byte aligned: the LDS-tiled MFMA kernel (persistent tile walk
- *     when there is more than one round of tiles);
+ *     pointers 4-byte aligned: the LDS-tiled MFMA kernel (8 wavefronts, one
+ *     256 x 256 tile each);
  *   else the generic 16x16x128 MFMA kernel.
  */
 int mxfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales,

@@ -39,6 +39,12 @@ SHAPES = [(1, 1, 32), (1, 300, 4096), (7, 17, 96), (16, 256, 512), (33, 200, 544
           # more weight tiles than a grid's slots hold at once (over 16 x 3 x 256
           # rows): each slot is refilled as it is consumed
           (3, 13000, 2048), (64, 12352, 2048),
+          # the weight-streaming kernel at other K: 1..4 super-steps a wave, those
+          # past K masked off (K = 512: seven of eight waves idle), 1..3 tiles in
+          # flight, refilled slots past 256 tiles
+          (1, 300, 512), (64, 1040, 512), (40, 200, 1536), (17, 333, 3584), (64, 1000, 4608),
+          (33, 520, 8192), (32, 260, 12288), (5, 4200, 10240), (16, 4200, 14336),
+          (9, 300, 16384),
           # more tiles than one round on the chip (ragged M and N), K of 4 and 2
           # stages (the 8-wave pipeline's loads past the last stage)
           (2200, 7700, 1024), (2200, 7700, 512)]

@@ -323,6 +323,9 @@ hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const ui
     if (skinny_gemm_supported(M, N, K, a_codes, a_scales, b_scales))
         return launch_gemm_skinny(a_codes, a_scales, b_codes, b_scales, M, N, K, y, bias,
                                   out_bf16, stream);
+    if (skinny_any_k_supported(M, N, K, a_codes, a_scales, b_scales))
+        return launch_gemm_skinny_any_k(a_codes, a_scales, b_codes, b_scales, M, N, K, y, bias,
+                                        out_bf16, stream);
     if (tiled_gemm_supported(M, N, K, a_scales, b_scales))
         return launch_gemm_tiled(a_codes, a_scales, b_codes, b_scales, M, N, K, y, bias,
                                  out_bf16, stream);

@@ -70,16 +70,19 @@ __device__ __forceinline__ void lds_barrier() {
 // with row stride K/2 code bytes and K/32 scale bytes): super-step
 // ss = wave + NW j, load q brings blocks 4q..4q+3 (lane group g: block
 // 4q+g).  Plain (cached) loads: non-temporal ones measured slower here.
-template <int SPW, int NW>
+// MASK: K covers only nss = K / 512 of the NW x SPW super-steps; this wave's
+// super-steps past the last are neither loaded nor multiplied.
+template <int SPW, int NW, bool MASK = false>
 __device__ __forceinline__ void load_block(Frag<SPW>& f, const uint8_t* codes,
                                            const uint8_t* scales, int64_t row, int nkb) {
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = MASK ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : threadIdx.x >> 6;
     const int g = lane >> 4;
     const uint8_t* crow = codes + row * (int64_t)nkb * 16;
     const uint8_t* srow = scales + row * (int64_t)nkb;
 #pragma unroll
     for (int j = 0; j < SPW; ++j) {
+        if (MASK && (wave + NW * j) * 16 >= nkb) break;   // wave-uniform
         const int kb0 = (wave + NW * j) * 16;
         const v4u* p = reinterpret_cast<const v4u*>(crow + (int64_t)kb0 * 16 + 16 * g);
         const v4u* ps = reinterpret_cast<const v4u*>(srow + kb0);
@@ -263,7 +266,7 @@ __device__ __forceinline__ void quant_raw8(Frag8<SPW>& f, const RawX<SPW>& r) {
 // the activations itself while its weight loads stream (UOS: by the Qmax =
 // 7.25 exponent rule).  A8: x is MXFP8 (the W4A8 activations).
 template <int MT, int SPW, int NW, int TPW, bool OUT_BF16, bool BF16A, bool UOS = false,
-          bool A8 = false>
+          bool A8 = false, bool MASK = false>
 __global__ __launch_bounds__(64 * NW, 1) void gemm_skinny_kernel(
     // no __restrict__ on the operands: with it the compiler may move their loads
     // across the points that order them (below the first MFMA, or the bf16
@@ -271,12 +274,16 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_skinny_kernel(
     const uint8_t* x, const uint8_t* xs, int64_t ldx, const uint8_t* w, const uint8_t* ws,
     int M, int N, int K, void* __restrict__ y, const uint16_t* __restrict__ bias) {
     __shared__ __attribute__((aligned(16))) Smem<MT, NW> sm;
+    static_assert(!MASK || (!BF16A && !A8), "a partial super-step count for MXFP4 operands");
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int r16 = lane & 15, g = lane >> 4;
     const int nkb = K / 32;
     const int ntiles = (N + 15) / 16;
     const int stride = gridDim.x;
+    // MASK: super-step j of this wave holds data only below nkb
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    auto live = [&](int j) { return !MASK || (wave_u + NW * j) * 16 < nkb; };
 
     auto tile_row = [&](int t) {
         const int tt = t < ntiles ? t : ntiles - 1;     // surplus loads: any valid row
@@ -299,7 +306,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_skinny_kernel(
         else if constexpr (A8)
             load_block8<SPW, NW>(a[mt], x, xs, row, nkb);
         else
-            load_block<SPW, NW>(a[mt], x, xs, row, nkb);
+            load_block<SPW, NW, MASK>(a[mt], x, xs, row, nkb);
     }
     // the activation loads stay ahead of the weight loads (a memory clobber
     // is a point no load moves across)
@@ -328,7 +335,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_skinny_kernel(
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
         bslot[i] = load_bias(blockIdx.x + i * stride);
-        load_block<SPW, NW>(slot[i], w, ws, tile_row(blockIdx.x + i * stride), nkb);
+        load_block<SPW, NW, MASK>(slot[i], w, ws, tile_row(blockIdx.x + i * stride), nkb);
     }
     __builtin_amdgcn_sched_barrier(0);   // issue every load before the first use
     if constexpr (BF16A) {
@@ -348,6 +355,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_skinny_kernel(
         for (int mt = 0; mt < MT; ++mt) acc[mt] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < SPW; ++j) {
+            if (!live(j)) break;                  // wave-uniform
             // this lane's weight scale byte for MFMA q is byte 4q+g: word q >> 8g
             const uint32_t s0 = f.s[j][0] >> sh, s1 = f.s[j][1] >> sh;
             const uint32_t s2 = f.s[j][2] >> sh, s3 = f.s[j][3] >> sh;
@@ -444,7 +452,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_skinny_kernel(
             const uint2 bv = bslot[i];
             if (t + TPW * stride < ntiles) {
                 bslot[i] = load_bias(t + TPW * stride);
-                load_block<SPW, NW>(slot[i], w, ws, tile_row(t + TPW * stride), nkb);
+                load_block<SPW, NW, MASK>(slot[i], w, ws, tile_row(t + TPW * stride), nkb);
             }
             finish(t, k & 1, acc, bv);
         }
@@ -461,6 +469,33 @@ bool skinny_gemm_supported(int64_t M, int64_t N, int64_t K, const void* x, const
     return M >= 1 && M <= 64 && (K == 2048 || K == 4096) && N >= 16 && aligned;
 }
 
+// Other K (a multiple of 512 up to 16384): eight wavefronts, SPW = ceil(K /
+// 4096) super-steps each, those past K masked off; the register file holds
+// SPW x (MT activation blocks + TPW weight tiles) x 20 registers, which sets
+// the largest M and the tiles in flight per SPW (any_k_config).
+struct AnyK {
+    int spw, mt_max;
+};
+static AnyK any_k_config(int64_t K) {
+    const int nss = (int)(K / 512);
+    const int spw = (nss + 7) / 8;
+    static const int mt_max[5] = {0, 4, 4, 2, 1};
+    return AnyK{spw, spw >= 1 && spw <= 4 ? mt_max[spw] : 0};
+}
+
+bool skinny_any_k_supported(int64_t M, int64_t N, int64_t K, const void* x, const void* x_scales,
+                            const void* w_scales) {
+    const bool aligned = (reinterpret_cast<uintptr_t>(x_scales) % 16) == 0 &&
+                         (reinterpret_cast<uintptr_t>(w_scales) % 16) == 0 &&
+                         (reinterpret_cast<uintptr_t>(x) % 16) == 0;
+    // K <= 2048 keeps most of the eight waves idle (K = 1024, N = 4096, M = 16:
+    // 4.2 us against the generic kernel's 3.8); K = 2048 and 4096 have kernels
+    // of their own
+    if (K % 512 != 0 || K < 2560 || K > 16384 || K == 4096 || N < 16 || M < 1 || !aligned)
+        return false;
+    return M <= 16 * any_k_config(K).mt_max;
+}
+
 // ldx > 0: `a` is bf16 activations [M][ldx] (as unused), quantized in the kernel.
 // Shapes the act-quant + GEMM launch serves: those of the skinny GEMM with
 // one 16-row activation block (the raw bf16 share of a wave, 64 registers a
@@ -472,13 +507,21 @@ bool linear_skinny_shape(int64_t M, int64_t N, int64_t K) {
     return M >= 1 && M <= LINEAR_FUSED_MAX && (K == 2048 || K == 4096) && N >= 16;
 }
 
-template <int MT, int SPW, int NW, bool A8 = false>
-static hipError_t launch_mt(const uint8_t* a, const uint8_t* as, int64_t ldx, const uint8_t* b,
-                            const uint8_t* bs, int64_t M, int64_t N, int64_t K, void* y,
-                            const uint16_t* bias, bool out_bf16, hipStream_t stream,
-                            bool uos = false) {
-    // tiles in flight per wave: all of a workgroup's tiles when they fit
-    constexpr int TPW = 3;
+// Weight tiles in flight per wave: enough that 256 workgroups cover the
+// tiles (one each up to 4096 rows, two up to 8192, else three).  Fewer
+// workgroups, each with more tiles in flight, measured slower: 6.15 against
+// 4.31 us at N = 4096, K = 4096, M = 1.
+static int tiles_per_wave(int64_t N, int tpw_max) {
+    const int64_t ntiles = (N + 15) / 16;
+    const int tpw = ntiles <= 256 ? 1 : ntiles <= 512 ? 2 : 3;
+    return tpw < tpw_max ? tpw : tpw_max;
+}
+
+template <int MT, int SPW, int NW, int TPW, bool A8>
+static hipError_t launch_tpw(const uint8_t* a, const uint8_t* as, int64_t ldx, const uint8_t* b,
+                             const uint8_t* bs, int64_t M, int64_t N, int64_t K, void* y,
+                             const uint16_t* bias, bool out_bf16, hipStream_t stream,
+                             bool uos) {
     const int ntiles = (int)((N + 15) / 16);
     int grid = (ntiles + TPW - 1) / TPW;
     if (grid > 256) grid = 256;
@@ -507,6 +550,21 @@ static hipError_t launch_mt(const uint8_t* a, const uint8_t* as, int64_t ldx, co
                         : go(gemm_skinny_kernel<MT, SPW, NW, TPW, false, false, false, true>);
     return out_bf16 ? go(gemm_skinny_kernel<MT, SPW, NW, TPW, true, false>)
                     : go(gemm_skinny_kernel<MT, SPW, NW, TPW, false, false>);
+}
+
+template <int MT, int SPW, int NW, bool A8 = false>
+static hipError_t launch_mt(const uint8_t* a, const uint8_t* as, int64_t ldx, const uint8_t* b,
+                            const uint8_t* bs, int64_t M, int64_t N, int64_t K, void* y,
+                            const uint16_t* bias, bool out_bf16, hipStream_t stream,
+                            bool uos = false) {
+    switch (tiles_per_wave(N, 3)) {
+        case 1: return launch_tpw<MT, SPW, NW, 1, A8>(a, as, ldx, b, bs, M, N, K, y, bias,
+                                                       out_bf16, stream, uos);
+        case 2: return launch_tpw<MT, SPW, NW, 2, A8>(a, as, ldx, b, bs, M, N, K, y, bias,
+                                                       out_bf16, stream, uos);
+        default: return launch_tpw<MT, SPW, NW, 3, A8>(a, as, ldx, b, bs, M, N, K, y, bias,
+                                                        out_bf16, stream, uos);
+    }
 }
 
 // K = 4096: NW super-steps of 512 K per wave pass (SPW = 8 / NW each);
@@ -543,6 +601,62 @@ static hipError_t launch_k(const uint8_t* a, const uint8_t* as, int64_t ldx, con
         return launch_mt<4, 2, 4, true>(a, as, ldx, b, bs, M, N, K, y, bias, out_bf16, stream);
     else
         return launch_mt<4, SPW, NW4096>(a, as, ldx, b, bs, M, N, K, y, bias, out_bf16, stream);
+}
+
+template <int MT, int SPW, int TPW>
+static hipError_t launch_masked_tpw(const uint8_t* a, const uint8_t* as, const uint8_t* b,
+                                    const uint8_t* bs, int64_t M, int64_t N, int64_t K, void* y,
+                                    const uint16_t* bias, bool out_bf16, hipStream_t stream) {
+    const int ntiles = (int)((N + 15) / 16);
+    int grid = (ntiles + TPW - 1) / TPW;
+    if (grid > 256) grid = 256;
+    auto go = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, dim3(grid), dim3(512), 0, stream, a, as, (int64_t)0, b, bs,
+                           (int)M, (int)N, (int)K, y, bias);
+        return hipGetLastError();
+    };
+    using namespace skinny;
+    return out_bf16 ? go(gemm_skinny_kernel<MT, SPW, 8, TPW, true, false, false, false, true>)
+                    : go(gemm_skinny_kernel<MT, SPW, 8, TPW, false, false, false, false, true>);
+}
+
+// TPW_MAX: the most tiles in flight the register file holds at this MT, SPW
+template <int MT, int SPW, int TPW_MAX>
+static hipError_t launch_masked(const uint8_t* a, const uint8_t* as, const uint8_t* b,
+                                const uint8_t* bs, int64_t M, int64_t N, int64_t K, void* y,
+                                const uint16_t* bias, bool out_bf16, hipStream_t stream) {
+    const int tpw = tiles_per_wave(N, TPW_MAX);
+    if constexpr (TPW_MAX >= 3)
+        if (tpw == 3)
+            return launch_masked_tpw<MT, SPW, 3>(a, as, b, bs, M, N, K, y, bias, out_bf16, stream);
+    if constexpr (TPW_MAX >= 2)
+        if (tpw == 2)
+            return launch_masked_tpw<MT, SPW, 2>(a, as, b, bs, M, N, K, y, bias, out_bf16, stream);
+    return launch_masked_tpw<MT, SPW, 1>(a, as, b, bs, M, N, K, y, bias, out_bf16, stream);
+}
+
+hipError_t launch_gemm_skinny_any_k(const uint8_t* a_codes, const uint8_t* a_scales,
+                                    const uint8_t* b_codes, const uint8_t* b_scales, int64_t M,
+                                    int64_t N, int64_t K, void* y, const uint16_t* bias,
+                                    bool out_bf16, hipStream_t stream) {
+    const int mt = (int)((M + 15) / 16);
+    auto go = [&](auto launch) {
+        return launch(a_codes, a_scales, b_codes, b_scales, M, N, K, y, bias, out_bf16, stream);
+    };
+    switch (any_k_config(K).spw * 8 + mt) {
+        case 1 * 8 + 1: return go(launch_masked<1, 1, 3>);
+        case 1 * 8 + 2: return go(launch_masked<2, 1, 3>);
+        case 1 * 8 + 3: return go(launch_masked<3, 1, 3>);
+        case 1 * 8 + 4: return go(launch_masked<4, 1, 3>);
+        case 2 * 8 + 1: return go(launch_masked<1, 2, 3>);
+        case 2 * 8 + 2: return go(launch_masked<2, 2, 3>);
+        case 2 * 8 + 3: return go(launch_masked<3, 2, 2>);
+        case 2 * 8 + 4: return go(launch_masked<4, 2, 1>);
+        case 3 * 8 + 1: return go(launch_masked<1, 3, 2>);
+        case 3 * 8 + 2: return go(launch_masked<2, 3, 1>);
+        case 4 * 8 + 1: return go(launch_masked<1, 4, 1>);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 // two wavefronts per SIMD (at K = 4096; measured 0.3-0.5 us less than one

@@ -110,6 +110,14 @@ hipError_t launch_grouped_glu_quant(const uint8_t* a_codes, const uint8_t* a_sca
 
 bool skinny_gemm_supported(int64_t M, int64_t N, int64_t K, const void* x, const void* x_scales,
                            const void* w_scales);
+// the weight-streaming kernel for other K (a multiple of 512 up to 16384) at
+// the M its register file allows (W4A4 only)
+bool skinny_any_k_supported(int64_t M, int64_t N, int64_t K, const void* x, const void* x_scales,
+                            const void* w_scales);
+hipError_t launch_gemm_skinny_any_k(const uint8_t* a_codes, const uint8_t* a_scales,
+                                    const uint8_t* b_codes, const uint8_t* b_scales, int64_t M,
+                                    int64_t N, int64_t K, void* y, const uint16_t* bias,
+                                    bool out_bf16, hipStream_t stream);
 
 // W4A8: A is MXFP8 (E4M3 codes [M][K], E8M0 [M][K/32]), B MXFP4.
 hipError_t launch_act_quant_fp8(const uint16_t* x, int64_t ldx, const int32_t* row_index,
