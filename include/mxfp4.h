@@ -284,6 +284,8 @@ int mxfp4_quantize_act_smooth(const void* x_bf16, int64_t ldx, const int32_t* ro
  *   else K % 512 == 0 with K <= 16384, the same alignment, N >= 16 and
  *     M <= 64 (K <= 8192), 32 (K <= 12288) or 16 (K <= 16384): the
  *     weight-streaming kernel with ceil(K / 4096) super-steps a wave;
+ *   64 < M <= 128 (M = 128 only under 64 tiles of 256 columns) at the K the
+ *     two rules above take with 64 rows: those kernels once per 64-row slice;
  *   else M >= 128, K % 512 == 0, each operand's codes under 2 GiB, both scale
  *     pointers 4-byte aligned: the LDS-tiled MFMA kernel (8 wavefronts, one
  *     256 x 256 tile each);

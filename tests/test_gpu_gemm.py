@@ -45,6 +45,8 @@ SHAPES = [(1, 1, 32), (1, 300, 4096), (7, 17, 96), (16, 256, 512), (33, 200, 544
           (1, 300, 512), (64, 1040, 512), (40, 200, 1536), (17, 333, 3584), (64, 1000, 4608),
           (33, 520, 8192), (32, 260, 12288), (5, 4200, 10240), (16, 4200, 14336),
           (9, 300, 16384),
+          # 64 < M <= 128: the decode kernel once per 64-row slice
+          (96, 300, 4096), (128, 520, 2048), (127, 1000, 8192), (65, 4200, 4096),
           # more tiles than one round on the chip (ragged M and N), K of 4 and 2
           # stages (the 8-wave pipeline's loads past the last stage)
           (2200, 7700, 1024), (2200, 7700, 512)]
