@@ -929,7 +929,19 @@ def main():
     pick = lambda f: q[min(len(q) - 1, int(round(f * (len(q) - 1))))]
     reps = max(3, args.steps // max(1, ph.slots))
     t.update(ph.time_all(reps))
-    value, unit, roof, extra, cfg = report(t, peaks)
+    rep = report(t, peaks)
+    if isinstance(rep, dict):
+        # another workload as the headline (--workload decode, moe, ...): its
+        # report's own rate and roofline
+        roof = rep["roofline"]
+        value = rep.get("TFLOPs_incl_act_quant")
+        unit = "TFLOP/s"
+        if value is None:
+            value, unit = roof["achieved"], roof["unit"]
+        cfg = {"workload": rep["workload"]}
+        extra = {k: v for k, v in rep.items() if k not in ("roofline", "workload")}
+    else:
+        value, unit, roof, extra, cfg = rep
     say(f"{headline}: {value:.1f} {unit}")
     del ph
     torch.cuda.synchronize()
