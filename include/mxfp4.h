@@ -288,7 +288,8 @@ int mxfp4_quantize_act_smooth(const void* x_bf16, int64_t ldx, const int32_t* ro
  *     two rules above take with 64 rows: those kernels once per 64-row slice;
  *   else M >= 128, K % 512 == 0, each operand's codes under 2 GiB, both scale
  *     pointers 4-byte aligned: the LDS-tiled MFMA kernel (8 wavefronts, one
- *     256 x 256 tile each);
+ *     256 x 256 tile each; 128 x 256 tiles when the 256 x 256 ones would
+ *     number at most half the CUs);
  *   else the generic 16x16x128 MFMA kernel.
  */
 int mxfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales,

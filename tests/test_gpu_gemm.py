@@ -45,6 +45,9 @@ SHAPES = [(1, 1, 32), (1, 300, 4096), (7, 17, 96), (16, 256, 512), (33, 200, 544
           (1, 300, 512), (64, 1040, 512), (40, 200, 1536), (17, 333, 3584), (64, 1000, 4608),
           (33, 520, 8192), (32, 260, 12288), (5, 4200, 10240), (16, 4200, 14336),
           (9, 300, 16384),
+          # too few 256 x 256 tiles to fill the chip: 128-row tiles (ragged M and
+          # N, K of 2, 3 and 16 stages)
+          (520, 520, 2048), (1000, 2000, 1536), (256, 1030, 4096),
           # 64 < M <= 128: the decode kernel once per 64-row slice
           (96, 300, 4096), (128, 520, 2048), (127, 1000, 8192), (65, 4200, 4096),
           # more tiles than one round on the chip (ragged M and N), K of 4 and 2

@@ -100,6 +100,9 @@ struct Shape {
 };
 
 using DenseShape = Shape<4, 2, 2, 4>;
+// 128 activation rows x 256 weight rows, 8 waves of 64 x 64: for shapes with
+// too few 256 x 256 tiles to fill the chip
+using DenseHalfShape = Shape<2, 2, 2, 4>;
 using GroupShape = Shape<4, 2, 1, 4>;
 // W4A8: 128 activation rows, so that two stages of 256-byte rows fit the LDS
 using W4A8Shape = Shape<2, 4, 2, 2, true>;
@@ -1157,12 +1160,11 @@ __device__ __forceinline__ void main_loop(lds_u8* lds, const TileSrc<S>& src,
 
 }  // namespace d8
 
-template <bool OUT_BF16, bool BIAS>
+template <bool OUT_BF16, bool BIAS, class S = DenseShape>
 __global__ __launch_bounds__(512, 1) void gemm_dense_kernel(
     const uint8_t* __restrict__ x, const uint8_t* __restrict__ xs,
     const uint8_t* __restrict__ w, const uint8_t* __restrict__ ws, int64_t M, int64_t N,
     int64_t K, void* __restrict__ y, int gm, const uint16_t* __restrict__ bias) {
-    using S = DenseShape;
     static_assert(S::NW == 8, "two wavefronts a SIMD");
     __shared__ __attribute__((aligned(16))) uint8_t smem[S::LDS_BYTES];
     const int tiles_m = (int)((M + S::BM - 1) / S::BM);
@@ -1912,28 +1914,36 @@ hipError_t launch_gemm_tiled(const uint8_t* a_codes, const uint8_t* a_scales,
     // one 8-wave workgroup a tile, XCD-aware tile order (tile_coords): the
     // tiles a round of resident workgroups covers on an XCD form a compact
     // block, so its operand rows are read into that XCD's L2 once
-    using S = tiled::DenseShape;
-    const int tiles_m = (int)((M + S::BM - 1) / S::BM);
-    const int tiles_n = (int)((N + S::BN - 1) / S::BN);
-    const int per_xcd = (tiles_m * tiles_n + 7) / 8;
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return hipErrorInvalidDevice;
     const int slots = cus / 8 > 0 ? cus / 8 : 1;   // resident workgroups per XCD
-    const int gm = group_rows(tiles_m, per_xcd < slots ? per_xcd : slots);
-    const dim3 grid((unsigned)(per_xcd * 8));
-    auto go = [&](auto kernel) {
-        hipLaunchKernelGGL(kernel, grid, dim3(512), 0, stream, a_codes, a_scales, b_codes,
-                           b_scales, M, N, K, y, gm, bias);
+    auto run = [&](auto shape) {
+        using S = decltype(shape);
+        const int tiles_m = (int)((M + S::BM - 1) / S::BM);
+        const int tiles_n = (int)((N + S::BN - 1) / S::BN);
+        const int per_xcd = (tiles_m * tiles_n + 7) / 8;
+        const int gm = group_rows(tiles_m, per_xcd < slots ? per_xcd : slots);
+        const dim3 grid((unsigned)(per_xcd * 8));
+        auto go = [&](auto kernel) {
+            hipLaunchKernelGGL(kernel, grid, dim3(512), 0, stream, a_codes, a_scales, b_codes,
+                               b_scales, M, N, K, y, gm, bias);
+        };
+        if (bias)
+            out_bf16 ? go(tiled::gemm_dense_kernel<true, true, S>)
+                     : go(tiled::gemm_dense_kernel<false, true, S>);
+        else
+            out_bf16 ? go(tiled::gemm_dense_kernel<true, false, S>)
+                     : go(tiled::gemm_dense_kernel<false, false, S>);
+        return hipGetLastError();
     };
-    if (bias)
-        out_bf16 ? go(tiled::gemm_dense_kernel<true, true>)
-                 : go(tiled::gemm_dense_kernel<false, true>);
-    else
-        out_bf16 ? go(tiled::gemm_dense_kernel<true, false>)
-                 : go(tiled::gemm_dense_kernel<false, false>);
-    return hipGetLastError();
+    // at most half the CUs' worth of 256 x 256 tiles: 128-row tiles, twice as
+    // many (measured at K = 4096: M = 1024, N = 4096 25.3 -> 18.3 us; M = 2048
+    // 28.6 -> 25.9 us; from 192 big tiles on the 256-row tiles are faster)
+    const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
+    if (2 * big_tiles <= (int64_t)cus) return run(tiled::DenseHalfShape{});
+    return run(tiled::DenseShape{});
 }
 
 // W4A8: MXFP8 activations [M][K] (one byte per element), MXFP4 weights.
