@@ -987,27 +987,29 @@ __global__ __launch_bounds__(256, 1) void gemm_persistent_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Dense GEMM, 8 wavefronts: the 256 x 256 tile of DenseShape, each wave
-// 128 activation rows x 64 weight rows, two waves on every SIMD.  Whenever
-// one of a SIMD's waves stalls issuing a load or waiting on LDS, the other
-// can issue its MFMAs.  Its accumulators (128 registers) leave room for
-// only one K-step's fragments ahead, so the register pipeline runs at
-// K-step granularity; the LDS layout and the operand order are those of
-// the 4-wave tiles, and the outputs are bit-identical to theirs.
+// Dense GEMM, 8 wavefronts, two on every SIMD: the 256 x 256 tile of
+// DenseShape (each wave 128 activation rows x 64 weight rows) or the 128 x
+// 256 tile of DenseHalfShape (64 x 64 a wave).  Whenever one of a SIMD's
+// waves stalls issuing a load or waiting on LDS, the other can issue its
+// MFMAs.  Its accumulators (128 registers at DenseShape) leave room for only
+// one K-step's fragments ahead, so the register pipeline runs at K-step
+// granularity; the LDS layout and the operand order are those of the 4-wave
+// tiles, and the outputs are bit-identical to theirs.
 //
 // Per stage kt (4 K-steps, one barrier):
 //   K-step 0: MFMAs on f0;  read K-step 1 into f1;  DMA group B of stage kt+1
-//   K-step 1: MFMAs on f1;  read K-step 2 into f0;  DMA group C of stage kt+1
+//   K-step 1: MFMAs on f1;  read K-step 2 into f0
 //   K-step 2: MFMAs on f0;  read K-step 3 into f1
 //   wait for this wave's loads (stage kt+1 landed); barrier
 //   K-step 3: MFMAs on f1;  read stage kt+1's K-step 0 into f0 and its scale
 //             words;  DMA group A of stage kt+2 (into stage kt's buffer,
 //             which no wave reads after the barrier) and its scale half-chunk
-// A stage's 8 code loads a wave are split into groups A, B, C of 4, 4, 0:
-// group A waits behind the barrier, B and C ride on the next stage's
-// K-steps.  Past the last stage the loads repeat the last stage (into a
-// buffer nothing reads again) and the reads fetch unused values, so every
-// stage issues the same instructions; the surplus loads drain at the end.
+// A stage's code loads a wave (8, or 6 at DenseHalfShape) are split into two
+// halves: group A waits behind the barrier, group B rides on the next
+// stage's first K-step.  Past the last stage the loads repeat the last stage
+// (into a buffer nothing reads again) and the reads fetch unused values, so
+// every stage issues the same instructions; the surplus loads drain at the
+// end.
 // ---------------------------------------------------------------------------
 namespace d8 {
 
