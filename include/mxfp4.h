@@ -289,7 +289,9 @@ int mxfp4_quantize_act_smooth(const void* x_bf16, int64_t ldx, const int32_t* ro
  *   else M >= 128, K % 512 == 0, each operand's codes under 2 GiB, both scale
  *     pointers 4-byte aligned: the LDS-tiled MFMA kernel (8 wavefronts, one
  *     256 x 256 tile each; 128 x 256 tiles when the 256 x 256 ones would
- *     number at most half the CUs);
+ *     number at most half the CUs; when the tiles take more than one round
+ *     of the CUs and the last round is at most half full, some tiles run
+ *     as two 128-row halves, which changes no output bit);
  *   else the generic 16x16x128 MFMA kernel.
  */
 int mxfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales,

@@ -51,8 +51,13 @@ SHAPES = [(1, 1, 32), (1, 300, 4096), (7, 17, 96), (16, 256, 512), (33, 200, 544
           # 64 < M <= 128: the decode kernel once per 64-row slice
           (96, 300, 4096), (128, 520, 2048), (127, 1000, 8192), (65, 4200, 4096),
           # more tiles than one round on the chip (ragged M and N), K of 4 and 2
-          # stages (the 8-wave pipeline's loads past the last stage)
-          (2200, 7700, 1024), (2200, 7700, 512)]
+          # stages (the 8-wave pipeline's loads past the last stage); the last
+          # round at most half full, so the tiles of each XCD's first slots run
+          # as half tiles: ragged last tile row (its bottom half partly, or
+          # wholly, past M) and whole tile rows
+          (2200, 7700, 1024), (2200, 7700, 512), (1400, 12288, 512), (1536, 12288, 512),
+          # the last round more than half full: whole tiles only
+          (2500, 12288, 512)]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)
@@ -507,13 +512,15 @@ def test_linear_bf16_uos_against_oracle(mx):
 
 @pytest.mark.parametrize("M,N,K", [(1, 1000, 4096), (8, 2048, 4096), (5, 300, 2048),
                                    (33, 1040, 2048), (100, 300, 1024), (150, 260, 800),
-                                   (300, 1000, 1024), (4096, 8192, 4096), (20, 13001, 2048)])
+                                   (300, 1000, 1024), (4096, 8192, 4096), (20, 13001, 2048),
+                                   (1400, 12288, 1024)])
 def test_linear_bf16_row_bias(mx, M, N, K):
     """A bf16 row bias through every GEMM path (one-launch decode, skinny, with
     its slots refilled past 12288 rows, generic, tiled with a ragged N,
-    several rounds of tiles), against the oracle's act-quant,
-    requant and GEMM plus the bias before the one rounding.  Sizes the oracle
-    cannot finish whole are checked on sampled rows."""
+    several rounds of tiles, half tiles in the last round), against the
+    oracle's act-quant, requant and GEMM plus the bias before the one
+    rounding.  Sizes the oracle cannot finish whole are checked on sampled
+    rows."""
     say(f"linear bf16 + bias M={M} N={N} K={K}")
     x = synth.activations(M, K, seed=M + 7, outlier_seed=K + 7)
     w = synth.bf16_normal((N, K), 0.02, seed=N + 7)

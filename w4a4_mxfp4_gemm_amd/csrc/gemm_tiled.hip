@@ -1047,17 +1047,20 @@ __device__ __forceinline__ void sread(Scales<S>& sc, uint32_t scales, const Read
 // The MFMAs of K-step T; after MFMA q, step(q) issues that slot's reads and
 // loads.  Each MFMA is pinned in program order: left free, the compiler sank
 // them below the reads threaded between them, which kept several K-steps'
-// fragments alive at once and spilled.
-template <class S, int T, int Q = 0, typename Step>
+// fragments alive at once and spilled.  MF = false: a wave with no rows to
+// multiply (half tiles) keeps the slots' loads and drops its MFMAs.
+template <class S, int T, bool MF, int Q = 0, typename Step>
 __device__ __forceinline__ void kmfma(const KFrag<S>& f, const Scales<S>& sc,
                                       v16f (&acc)[S::NB][S::MB], Step&& step) {
     if constexpr (Q < S::NB * S::MB) {
         constexpr int i = Q / S::MB, j = Q % S::MB;
-        acc[i][j] = mfma<T>(f.w[i], f.x[j], acc[i][j], sc.w[i], sc.x[j]);
-        asm volatile("" ::"v"(acc[i][j]));
+        if constexpr (MF) {
+            acc[i][j] = mfma<T>(f.w[i], f.x[j], acc[i][j], sc.w[i], sc.x[j]);
+            asm volatile("" ::"v"(acc[i][j]));
+        }
         step(std::integral_constant<int, Q>{});
         __builtin_amdgcn_sched_barrier(0);
-        kmfma<S, T, Q + 1>(f, sc, acc, step);
+        kmfma<S, T, MF, Q + 1>(f, sc, acc, step);
     }
 }
 
@@ -1080,8 +1083,8 @@ struct Groups {
 };
 
 // Stage 0, the scale chunks of stages 0-3 and stage 1's group A; then stage
-// 0's K-step 0 fragments and scale words.
-template <class S>
+// 0's K-step 0 fragments and scale words (MF: the wave multiplies).
+template <class S, bool MF>
 __device__ __forceinline__ void prologue(lds_u8* lds, const TileSrc<S>& src,
                                          const LoadOffsets<S>& lo, int nkt, KFrag<S>& f0,
                                          Scales<S>& sc, const ReadOffsets<S>& ro) {
@@ -1098,13 +1101,14 @@ __device__ __forceinline__ void prologue(lds_u8* lds, const TileSrc<S>& src,
     wait_vm<G::A>();                          // all but stage 1's group A
     __builtin_amdgcn_s_barrier();
     const uint32_t lds0 = lds_addr(lds);
-    static_for<S::NB + S::MB>([&](auto r) {
-        kread<S, 0, decltype(r)::value>(f0, code_addr(lds0, 0, S::CODE_STAGE), ro);
-        sread<S, decltype(r)::value>(sc, scale_addr<S>(lds0, 0, 0), ro);
-    });
+    if constexpr (MF)
+        static_for<S::NB + S::MB>([&](auto r) {
+            kread<S, 0, decltype(r)::value>(f0, code_addr(lds0, 0, S::CODE_STAGE), ro);
+            sread<S, decltype(r)::value>(sc, scale_addr<S>(lds0, 0, 0), ro);
+        });
 }
 
-template <class S>
+template <class S, bool MF>
 __device__ __forceinline__ void main_loop(lds_u8* lds, const TileSrc<S>& src,
                                           const LoadOffsets<S>& lo, int nkt, KFrag<S>& f0,
                                           KFrag<S>& f1, Scales<S>& sc,
@@ -1119,19 +1123,19 @@ __device__ __forceinline__ void main_loop(lds_u8* lds, const TileSrc<S>& src,
         const uint32_t codes = code_addr(lds0, kt, S::CODE_STAGE);
         const int k1 = kt + 1;
         const int ks1 = k1 < nkt ? k1 : nkt - 1;
-        kmfma<S, 0>(f0, sc, acc, [&](auto q) {
+        kmfma<S, 0, MF>(f0, sc, acc, [&](auto q) {
             constexpr int Q = decltype(q)::value;
-            if constexpr (Q < NR) kread<S, 1, Q>(f1, codes, ro);
+            if constexpr (MF && Q < NR) kread<S, 1, Q>(f1, codes, ro);
             constexpr int L = slot_load<G::A, G::B1, SL>(Q);
             if constexpr (L >= 0) load_op<S, L>(lds, src, src, lo, k1 & 1, ks1, true, 0, 0);
         });
-        kmfma<S, 1>(f1, sc, acc, [&](auto q) {
+        kmfma<S, 1, MF>(f1, sc, acc, [&](auto q) {
             constexpr int Q = decltype(q)::value;
-            if constexpr (Q < NR) kread<S, 2, Q>(f0, codes, ro);
+            if constexpr (MF && Q < NR) kread<S, 2, Q>(f0, codes, ro);
         });
-        kmfma<S, 2>(f0, sc, acc, [&](auto q) {
+        kmfma<S, 2, MF>(f0, sc, acc, [&](auto q) {
             constexpr int Q = decltype(q)::value;
-            if constexpr (Q < NR) kread<S, 3, Q>(f1, codes, ro);
+            if constexpr (MF && Q < NR) kread<S, 3, Q>(f1, codes, ro);
         });
         // stage kt+1 landed for every wave; every wave has issued its reads
         // of stage kt (LDS reads finish long before a DMA's data arrives)
@@ -1144,9 +1148,9 @@ __device__ __forceinline__ void main_loop(lds_u8* lds, const TileSrc<S>& src,
         const uint32_t ncodes = code_addr(lds0, k1, S::CODE_STAGE);
         const uint32_t nscales = scale_addr<S>(lds0, 0, k1);
         Scales<S> sn;
-        kmfma<S, 3>(f1, sc, acc, [&](auto q) {
+        kmfma<S, 3, MF>(f1, sc, acc, [&](auto q) {
             constexpr int Q = decltype(q)::value;
-            if constexpr (Q < NR) {
+            if constexpr (MF && Q < NR) {
                 kread<S, 0, Q>(f0, ncodes, ro);
                 sread<S, Q>(sn, nscales, ro);
             }
@@ -1162,38 +1166,65 @@ __device__ __forceinline__ void main_loop(lds_u8* lds, const TileSrc<S>& src,
 
 }  // namespace d8
 
-template <bool OUT_BF16, bool BIAS, class S = DenseShape>
+//
+// HALVES: the last round of tiles is at most half full, so the workgroups of
+// each XCD are laid out as `halves` top halves of its first tiles, then its
+// whole tiles, then the bottom halves of those first tiles.  The CUs that
+// start on a half tile run half a tile out of phase with the others, and the
+// bottom halves fill the last round; every tile is still summed the same way
+// (bit-identical output).  A half tile (128 rows, rows past it outside the
+// activation descriptor) is multiplied by the four waves of its rows; the
+// other four only load and wait.
+template <bool OUT_BF16, bool BIAS, class S = DenseShape, bool HALVES = false>
 __global__ __launch_bounds__(512, 1) void gemm_dense_kernel(
     const uint8_t* __restrict__ x, const uint8_t* __restrict__ xs,
     const uint8_t* __restrict__ w, const uint8_t* __restrict__ ws, int64_t M, int64_t N,
-    int64_t K, void* __restrict__ y, int gm, const uint16_t* __restrict__ bias) {
+    int64_t K, void* __restrict__ y, int gm, const uint16_t* __restrict__ bias, int halves) {
     static_assert(S::NW == 8, "two wavefronts a SIMD");
+    static_assert(!HALVES || S::MB * S::WGM == 8, "half tiles split the 256-row tile");
     __shared__ __attribute__((aligned(16))) uint8_t smem[S::LDS_BYTES];
     const int tiles_m = (int)((M + S::BM - 1) / S::BM);
     const int tiles_n = (int)((N + S::BN - 1) / S::BN);
-    int tm, tn;
-    if (!tile_coords(tiles_m, tiles_n, gm, tm, tn)) return;
+    int tm, tn, part = 0;                     // part: 0 whole tile, 1 top half, 2 bottom half
+    if constexpr (HALVES) {
+        const int per_xcd = (int)gridDim.x / 8 - halves;
+        const int id = (int)blockIdx.x, j = id / 8;
+        part = j < halves ? 1 : (j < per_xcd ? 0 : 2);
+        const int t = (id % 8) * per_xcd + (part == 2 ? j - per_xcd : j);
+        if (t >= tiles_m * tiles_n) return;
+        tile_of(t, tiles_m, tiles_n, gm, tm, tn);
+    } else {
+        if (!tile_coords(tiles_m, tiles_n, gm, tm, tn)) return;
+    }
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wn = wave % S::WGN, wm = wave / S::WGN;
-    const int64_t m0 = (int64_t)tm * S::BM, n0 = (int64_t)tn * S::BN;
+    const int64_t m0 = (int64_t)tm * S::BM + (part == 2 ? S::BM / 2 : 0);
+    const int64_t n0 = (int64_t)tn * S::BN;
+    if (m0 >= M) return;                      // a bottom half past the last row
+    const int64_t m_end = part != 0 ? min(M, m0 + S::BM / 2) : M;
     const int nkt = (int)(K / 256);           // even: K % 512 == 0
     lds_u8* lds = (lds_u8*)smem;
-    const TileSrc<S> src = tile_src<S>(x, xs, w, ws, m0, M, n0, N, K);
+    const TileSrc<S> src = tile_src<S>(x, xs, w, ws, m0, m_end, n0, N, K);
     const ReadOffsets<S> ro = read_offsets<S>(wn, wm);
     const LoadOffsets<S> lo = load_offsets<S>(K / 2, K / 2, K / 32);
     v16f acc[S::NB][S::MB];
     zero_acc<S>(acc);
     d8::KFrag<S> f0, f1;
     Scales<S> sc;
-    d8::prologue<S>(lds, src, lo, nkt, f0, sc, ro);
-    d8::main_loop<S>(lds, src, lo, nkt, f0, f1, sc, acc, ro);
+    if (HALVES && part != 0 && wm == 1) {     // no rows of this half tile
+        d8::prologue<S, false>(lds, src, lo, nkt, f0, sc, ro);
+        d8::main_loop<S, false>(lds, src, lo, nkt, f0, f1, sc, acc, ro);
+    } else {
+        d8::prologue<S, true>(lds, src, lo, nkt, f0, sc, ro);
+        d8::main_loop<S, true>(lds, src, lo, nkt, f0, f1, sc, acc, ro);
+    }
     wait_vm<0>();                             // drain the surplus loads
     // every wave is past its last read of the stage buffers, which now hold
     // the eight waves' epilogue regions
     __syncthreads();
     using T = Stage<S, OUT_BF16>;
     constexpr int ROWS = T::rows_for(S::SCALE_BASE / S::NW);
-    store_tile<S, OUT_BF16, ROWS, BIAS>(acc, lds + wave * T::bytes(ROWS), y, m0, M, n0, N, wn,
+    store_tile<S, OUT_BF16, ROWS, BIAS>(acc, lds + wave * T::bytes(ROWS), y, m0, m_end, n0, N, wn,
                                         wm, bias);
 }
 
@@ -1921,31 +1952,41 @@ hipError_t launch_gemm_tiled(const uint8_t* a_codes, const uint8_t* a_scales,
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return hipErrorInvalidDevice;
     const int slots = cus / 8 > 0 ? cus / 8 : 1;   // resident workgroups per XCD
-    auto run = [&](auto shape) {
+    auto run = [&](auto shape, auto halves_on) {
         using S = decltype(shape);
+        constexpr bool H = decltype(halves_on)::value;
         const int tiles_m = (int)((M + S::BM - 1) / S::BM);
         const int tiles_n = (int)((N + S::BN - 1) / S::BN);
         const int per_xcd = (tiles_m * tiles_n + 7) / 8;
         const int gm = group_rows(tiles_m, per_xcd < slots ? per_xcd : slots);
-        const dim3 grid((unsigned)(per_xcd * 8));
+        const int halves = H ? slots / 2 : 0;
+        const dim3 grid((unsigned)((per_xcd + halves) * 8));
         auto go = [&](auto kernel) {
             hipLaunchKernelGGL(kernel, grid, dim3(512), 0, stream, a_codes, a_scales, b_codes,
-                               b_scales, M, N, K, y, gm, bias);
+                               b_scales, M, N, K, y, gm, bias, halves);
         };
         if (bias)
-            out_bf16 ? go(tiled::gemm_dense_kernel<true, true, S>)
-                     : go(tiled::gemm_dense_kernel<false, true, S>);
+            out_bf16 ? go(tiled::gemm_dense_kernel<true, true, S, H>)
+                     : go(tiled::gemm_dense_kernel<false, true, S, H>);
         else
-            out_bf16 ? go(tiled::gemm_dense_kernel<true, false, S>)
-                     : go(tiled::gemm_dense_kernel<false, false, S>);
+            out_bf16 ? go(tiled::gemm_dense_kernel<true, false, S, H>)
+                     : go(tiled::gemm_dense_kernel<false, false, S, H>);
         return hipGetLastError();
     };
+    using Off = std::false_type;
     // at most half the CUs' worth of 256 x 256 tiles: 128-row tiles, twice as
     // many (measured at K = 4096: M = 1024, N = 4096 25.3 -> 18.3 us; M = 2048
     // 28.6 -> 25.9 us; from 192 big tiles on the 256-row tiles are faster)
     const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
-    if (2 * big_tiles <= (int64_t)cus) return run(tiled::DenseHalfShape{});
-    return run(tiled::DenseShape{});
+    if (2 * big_tiles <= (int64_t)cus) return run(tiled::DenseHalfShape{}, Off{});
+    // more than one round with the last one at most half full: half tiles
+    // (measured at K = 4096: M = 1536, N = 12288 58.5 -> 50.6 us; M = 5000,
+    // N = 4096 59.7 -> 51.7 us; M = 3000, N = 28672 192.0 -> 181.5 us; with
+    // the last round more than half full they were slower)
+    const int64_t per_xcd = (big_tiles + 7) / 8, tail = per_xcd % slots;
+    if (per_xcd > slots && tail != 0 && 2 * tail <= slots)
+        return run(tiled::DenseShape{}, std::true_type{});
+    return run(tiled::DenseShape{}, Off{});
 }
 
 // W4A8: MXFP8 activations [M][K] (one byte per element), MXFP4 weights.
