@@ -1959,9 +1959,8 @@ hipError_t launch_gemm_tiled(const uint8_t* a_codes, const uint8_t* a_scales,
         const int tiles_n = (int)((N + S::BN - 1) / S::BN);
         const int per_xcd = (tiles_m * tiles_n + 7) / 8;
         // one round: the squarest block of tiles, rows first (8 x 4 at 32
-        // slots); several rounds: half as many rows (4 x 8), so the activation
-        // rows a round shares (2 MiB at K = 4096) stay in the XCD's 4 MiB L2
-        // for the next round's columns (28672 x 4096: 239 -> 234 us)
+        // slots); several rounds: half as many rows (4 x 8), measured faster
+        // (28672 x 4096: 239 -> 234 us) at about the same L2 miss traffic
         const int gm = per_xcd > slots ? group_rows(tiles_m, slots / 4)
                                        : group_rows(tiles_m, per_xcd < slots ? per_xcd : slots);
         const int halves = H ? slots / 2 : 0;
